@@ -1,0 +1,213 @@
+"""Python binding of the CPU oracle (``oracle.c``).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this module.  It never touches the
+GPU library and the GPU library never touches it.
+
+Arrays in and out are numpy; inputs are the float32 arrays of
+``evaluation_nonlinear_rnns_amd.inputs``.  ``precision`` selects the double
+(``"f64"``) or single (``"f32"``) precision instantiation of the oracle.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_SOURCES = [os.path.join(_HERE, "oracle.c"), os.path.join(_HERE, "orc_impl.h")]
+
+CELLS = {"tanh": 0, "gru": 1, "linear": 2}
+MODES = {"dense": 0, "diag": 1}
+STATUS = {0: "converged", 1: "not_converged", 2: "nonfinite"}
+
+
+def build(force: bool = True) -> str:
+    """Compile ``liboracle.so`` with gcc (no fast-math, no FMA contraction)."""
+    if not force and os.path.exists(_LIB_PATH):
+        return _LIB_PATH
+    cmd = ["gcc", "-O2", "-std=gnu11", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
+           "-Wall", "-o", _LIB_PATH + ".tmp", _SOURCES[0], "-lm"]
+    subprocess.run(cmd, check=True, cwd=_HERE)
+    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
+    return _LIB_PATH
+
+
+class _Cell(ctypes.Structure):
+    _fields_ = [("cell", ctypes.c_int), ("D", ctypes.c_int), ("M", ctypes.c_int),
+                ("W", ctypes.c_void_p), ("U", ctypes.c_void_p), ("b", ctypes.c_void_p),
+                ("b2", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        _lib = ctypes.CDLL(_LIB_PATH)
+        for name in ("orc_step", "orc_rollout", "orc_solve_diag", "orc_solve_dense", "orc_newton",
+                     "orc_lle"):
+            for suf in ("_f64", "_f32"):
+                getattr(_lib, name + suf).restype = ctypes.c_int
+        _lib.orc_max_threads.restype = ctypes.c_int
+    return _lib
+
+
+def max_threads() -> int:
+    return int(lib().orc_max_threads())
+
+
+def _f32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def _dt(precision: str):
+    if precision not in ("f64", "f32"):
+        raise ValueError("precision must be 'f64' or 'f32'")
+    return np.float64 if precision == "f64" else np.float32
+
+
+class Cell:
+    """A cell's parameters (float32) held alive for the C calls.
+
+    tanh / linear: ``W [D,D]``, ``U [D,M]``, ``b [D]``.
+    GRU: ``W`` = W_hh ``[3D,D]``, ``U`` = W_ih ``[3D,M]``, ``b`` = b_ih, ``b2`` = b_hh.
+    """
+
+    def __init__(self, cell: str, W, U, b=None, b2=None):
+        self.cell = cell
+        self.W = _f32(W)
+        self.U = _f32(U)
+        self.b = None if b is None else _f32(b)
+        self.b2 = None if b2 is None else _f32(b2)
+        rows = self.W.shape[0]
+        self.D = self.W.shape[1]
+        self.M = self.U.shape[1]
+        if cell == "gru":
+            assert rows == 3 * self.D and self.U.shape[0] == 3 * self.D
+        else:
+            assert rows == self.D and self.U.shape[0] == self.D
+        self._c = _Cell(CELLS[cell], self.D, self.M, _ptr(self.W), _ptr(self.U), _ptr(self.b),
+                        _ptr(self.b2))
+
+    @classmethod
+    def from_problem(cls, p: dict, cell: Optional[str] = None) -> "Cell":
+        return cls(cell or p["cell"], p["W"], p["U"], p.get("b"), p.get("b2"))
+
+    @property
+    def ref(self):
+        return ctypes.byref(self._c)
+
+
+def step(cell: Cell, s, x, precision: str = "f64"):
+    """One transition: returns ``(f [D], J [D,D])`` at state ``s`` and input ``x``."""
+    dt = _dt(precision)
+    s = np.ascontiguousarray(s, dtype=dt)
+    x = _f32(x)
+    f = np.empty(cell.D, dt)
+    J = np.empty((cell.D, cell.D), dt)
+    jd = np.empty(cell.D, dt)
+    rc = getattr(lib(), "orc_step" + "_" + precision)(cell.ref, _ptr(s), _ptr(x), _ptr(f), _ptr(J),
+                                                      _ptr(jd))
+    if rc != 0:
+        raise RuntimeError("orc_step failed")
+    return f, J, jd
+
+
+def rollout(cell: Cell, x, s0=None, precision: str = "f64", threads: int = 0) -> np.ndarray:
+    """Sequential rollout ``s_t = f(s_{t-1}, x_t)``; returns ``[B, T, D]``."""
+    dt = _dt(precision)
+    x = _f32(x)
+    B, T = x.shape[0], x.shape[1]
+    s0 = None if s0 is None else _f32(s0)
+    out = np.empty((B, T, cell.D), dt)
+    rc = getattr(lib(), "orc_rollout_" + precision)(cell.ref, _ptr(x), _ptr(s0), B, T, _ptr(out),
+                                                    threads)
+    if rc != 0:
+        raise RuntimeError("orc_rollout failed")
+    return out
+
+
+def solve_diag(a, b, s0=None, precision: str = "f64", threads: int = 0) -> np.ndarray:
+    """Forward substitution of ``s_t = a_t * s_{t-1} + b_t``; arrays ``[B, T, D]``."""
+    dt = _dt(precision)
+    a = _f32(a)
+    b = _f32(b)
+    B, T, D = a.shape
+    s0 = None if s0 is None else _f32(s0)
+    out = np.empty((B, T, D), dt)
+    rc = getattr(lib(), "orc_solve_diag_" + precision)(_ptr(a), _ptr(b), _ptr(s0), B, T, D,
+                                                       _ptr(out), threads)
+    if rc != 0:
+        raise RuntimeError("orc_solve_diag failed")
+    return out
+
+
+def solve_dense(A, b, s0=None, precision: str = "f64", threads: int = 0) -> np.ndarray:
+    """Forward substitution of ``s_t = A_t s_{t-1} + b_t``; ``A [B,T,D,D]``, ``b [B,T,D]``."""
+    dt = _dt(precision)
+    A = _f32(A)
+    b = _f32(b)
+    B, T, D = b.shape
+    s0 = None if s0 is None else _f32(s0)
+    out = np.empty((B, T, D), dt)
+    rc = getattr(lib(), "orc_solve_dense_" + precision)(_ptr(A), _ptr(b), _ptr(s0), B, T, D,
+                                                        _ptr(out), threads)
+    if rc != 0:
+        raise RuntimeError("orc_solve_dense failed")
+    return out
+
+
+def newton(cell: Cell, x, s0=None, mode: str = "dense", tol: float = 1e-6, max_iter: int = 100,
+           precision: str = "f32", init=None, threads: int = 0, history: bool = False):
+    """Parallel Newton (``mode="dense"``) or diagonal quasi-Newton (``"diag"``).
+
+    Returns ``(traj [B,T,D], iters [B], resid [B], status [B])`` and, with
+    ``history=True``, the residual at every iteration ``[B, max_iter+1]``.
+    ``tol < 0`` never passes, which returns the iterate ``s^(max_iter)``.
+    """
+    dt = _dt(precision)
+    x = _f32(x)
+    B, T = x.shape[0], x.shape[1]
+    s0 = None if s0 is None else _f32(s0)
+    init = None if init is None else _f32(init)
+    traj = np.empty((B, T, cell.D), dt)
+    iters = np.zeros(B, np.int32)
+    resid = np.zeros(B, np.float64)
+    status = np.zeros(B, np.int32)
+    hist = np.full((B, max_iter + 1), np.nan) if history else None
+    rc = getattr(lib(), "orc_newton_" + precision)(
+        cell.ref, _ptr(x), _ptr(s0), B, T, MODES[mode], ctypes.c_double(tol), int(max_iter),
+        _ptr(init), _ptr(traj), _ptr(iters), _ptr(resid), _ptr(status), _ptr(hist), threads)
+    if rc != 0:
+        raise RuntimeError("orc_newton failed")
+    if history:
+        return traj, iters, resid, status, hist
+    return traj, iters, resid, status
+
+
+def lle(cell: Cell, x, traj, v0, s0=None, precision: str = "f64", threads: int = 0) -> np.ndarray:
+    """Largest Lyapunov exponent per sequence along ``traj`` (``[B,T,D]``)."""
+    dt = _dt(precision)
+    x = _f32(x)
+    traj = np.ascontiguousarray(traj, dtype=dt)
+    v0 = _f32(v0)
+    B, T = x.shape[0], x.shape[1]
+    s0 = None if s0 is None else _f32(s0)
+    out = np.empty(B, np.float64)
+    rc = getattr(lib(), "orc_lle_" + precision)(cell.ref, _ptr(x), _ptr(s0), _ptr(traj), B, T,
+                                                _ptr(v0), _ptr(out), threads)
+    if rc != 0:
+        raise RuntimeError("orc_lle failed")
+    return out

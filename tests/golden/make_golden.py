@@ -1,0 +1,89 @@
+"""Write the oracle's reference values for the full-size workloads.
+
+Calls only the CPU oracle (``oracle/``) and the seeded input generator.  The
+output, ``oracle_full_workloads.json``, holds per-sequence iteration counts,
+final residuals and statuses of the oracle's float32 Newton / quasi-Newton run
+(the count the GPU solver must match within one iteration), the largest
+Lyapunov exponent of every sequence along its float64 rollout (Algorithm 1 of
+the "Predictability Enables Parallelization" page's appendix, as described in
+its rebuttal), and the gap between the oracle's float32 and float64 rollouts
+with the predictability horizon (the last step at which that gap stays within
+1e-5).  These full sizes take minutes on a CPU, which is why they are stored.
+
+Usage: python tests/golden/make_golden.py [workload ...]
+"""
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+sys.path.insert(0, ROOT)
+
+from oracle import oracle as O  # noqa: E402
+from evaluation_nonlinear_rnns_amd import inputs as I  # noqa: E402
+
+OUT = os.path.join(HERE, "oracle_full_workloads.json")
+HORIZON_TOL = 1e-5
+
+
+def _horizon(r32, r64):
+    """Per sequence: last time step index t with max_{t' <= t} gap <= HORIZON_TOL (T if never exceeded)."""
+    gap = np.abs(r32.astype(np.float64) - r64).max(axis=2)          # [B, T]
+    run = np.maximum.accumulate(gap, axis=1)
+    over = run > HORIZON_TOL
+    T = gap.shape[1]
+    return [int(np.argmax(o)) if o.any() else T for o in over], float(gap.max())
+
+
+def run_one(name, gain=None):
+    w = I.WORKLOADS[name]
+    p = I.workload_problem(name, gain=gain)
+    c = O.Cell.from_problem(p)
+    t0 = time.time()
+    r64 = O.rollout(c, p["x"], p["s0"], precision="f64")
+    r32 = O.rollout(c, p["x"], p["s0"], precision="f32")
+    horizon, gap = _horizon(r32, r64)
+    lle = O.lle(c, p["x"], r64, I.lle_probe(10000 + w.seed, w.B, w.D), p["s0"]).tolist()
+    t1 = time.time()
+    _, iters, resid, status = O.newton(c, p["x"], p["s0"], mode=w.mode, tol=w.tol,
+                                       max_iter=w.max_iter, precision="f32")
+    t2 = time.time()
+    rec = {
+        "workload": name, "cell": w.cell, "mode": w.mode, "D": w.D, "M": w.M, "T": w.T, "B": w.B,
+        "gain": w.gain if gain is None else gain, "tol": w.tol, "max_iter": w.max_iter,
+        "seed": w.seed,
+        "iters_f32": [int(v) for v in iters], "resid_f32": [float(v) for v in resid],
+        "status_f32": [int(v) for v in status],
+        "lle_f64": lle, "rollout_gap_f32_f64": gap, "horizon_1e-5": horizon,
+        "seconds_rollouts": round(t1 - t0, 2), "seconds_newton_f32": round(t2 - t1, 2),
+    }
+    print(f"{name} gain={rec['gain']}: iters {min(iters)}..{max(iters)} (median {np.median(iters)}), "
+          f"status {sorted(set(rec['status_f32']))}, lle {np.mean(lle):.4f}, gap {gap:.2e}, "
+          f"newton {t2 - t1:.1f}s", flush=True)
+    return rec
+
+
+def main(argv):
+    names = argv or ["tanh_d4_t1024", "gru_d64_t65536", "tanh_d32_t16384", "tanh_d16_t4096_sweep"]
+    data = {}
+    if os.path.exists(OUT):
+        with open(OUT) as f:
+            data = json.load(f)
+    data["_about"] = ("Oracle reference values for the full-size workloads, written by "
+                      "tests/golden/make_golden.py from oracle/ only.")
+    for name in names:
+        w = I.WORKLOADS[name]
+        if w.gains:
+            data[name] = {f"{g:g}": run_one(name, gain=g) for g in w.gains}
+        else:
+            data[name] = run_one(name)
+        with open(OUT, "w") as f:
+            json.dump(data, f, indent=1)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])

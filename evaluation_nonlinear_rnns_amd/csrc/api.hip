@@ -1,0 +1,537 @@
+// C entry points of libdeer (declared in include/deer.h): argument checks,
+// workspace layout, the device-driven Newton loop and error reporting.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+namespace deer {
+
+// ------------------------------------------------------------------ errors
+namespace {
+thread_local std::string g_last_error = "no error";
+}
+
+void set_error(const std::string &msg) { g_last_error = msg; }
+
+int fail(int code, const std::string &msg)
+{
+    set_error(msg);
+    return code;
+}
+
+int hip_fail(hipError_t e, const char *what)
+{
+    set_error(std::string("HIP error ") + hipGetErrorName(e) + " (" + hipGetErrorString(e) + ") in " + what);
+    return DEER_ERR_HIP;
+}
+
+// --------------------------------------------------------------- profiling
+namespace {
+constexpr int kProfKinds = 4;
+std::atomic<int> g_prof_enabled{0};
+std::mutex g_prof_mu;
+long long g_prof_launches[kProfKinds] = {0, 0, 0, 0};
+double g_prof_ms[kProfKinds] = {0, 0, 0, 0};
+
+// Event pairs recorded around launches of one deer_solve call.
+struct ProfScope {
+    bool on = false;
+    hipStream_t stream = nullptr;
+    std::vector<std::pair<int, std::pair<hipEvent_t, hipEvent_t>>> marks;
+    int open_kind = -1;
+    hipEvent_t open_start = nullptr;
+
+    explicit ProfScope(hipStream_t s) : on(g_prof_enabled.load() != 0), stream(s) {}
+    void begin(int kind)
+    {
+        if (!on) return;
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) { on = false; return; }
+        (void)hipEventRecord(e, stream);
+        open_kind = kind;
+        open_start = e;
+    }
+    void end()
+    {
+        if (!on || open_kind < 0) return;
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) { on = false; return; }
+        (void)hipEventRecord(e, stream);
+        marks.push_back({open_kind, {open_start, e}});
+        open_kind = -1;
+    }
+    // Call after the stream has been synchronised.  Only the first limit[k]
+    // launches of each kind did work; launches enqueued after convergence exit
+    // at once and are not counted.
+    void collect(const long long limit[kProfKinds])
+    {
+        std::lock_guard<std::mutex> lock(g_prof_mu);
+        long long seen[kProfKinds] = {0, 0, 0, 0};
+        for (auto &m : marks) {
+            if (seen[m.first]++ >= limit[m.first]) continue;
+            float ms = 0.0f;
+            if (hipEventElapsedTime(&ms, m.second.first, m.second.second) == hipSuccess) {
+                g_prof_launches[m.first] += 1;
+                g_prof_ms[m.first] += ms;
+            }
+        }
+        release();
+    }
+    void release()
+    {
+        for (auto &m : marks) {
+            (void)hipEventDestroy(m.second.first);
+            (void)hipEventDestroy(m.second.second);
+        }
+        marks.clear();
+    }
+    ~ProfScope() { release(); }
+};
+
+// Pinned host words for polling the device's all-done flag, one set per host thread.
+struct PollSlots {
+    int *host = nullptr;
+    PollSlots()
+    {
+        if (hipHostMalloc(reinterpret_cast<void **>(&host), 64 * sizeof(int), hipHostMallocDefault) != hipSuccess)
+            host = nullptr;
+    }
+};
+thread_local PollSlots g_poll;
+
+// ------------------------------------------------------ small device kernels
+struct SolveControl {
+    int iter;       // current iteration index i (iterate s^(i) lives in buffer i % 2)
+    int all_done;   // 1 once every sequence has stopped
+    int pad[62];
+};
+
+__global__ void init_control_kernel(SolveControl *ctl, int *done, int *iters, int *status, float *resid,
+                                    unsigned *res_bits, int B)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i == 0) { ctl->iter = 0; ctl->all_done = 0; }
+    if (i < B) { done[i] = 0; iters[i] = 0; status[i] = 0; resid[i] = 0.0f; res_bits[i] = 0u; }
+}
+
+__global__ void fill_kernel(float *__restrict__ p, size_t n, float v)
+{
+    size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+    for (; i < n; i += stride) p[i] = v;
+}
+
+__global__ void copy_kernel(float *__restrict__ dst, const float *__restrict__ src, size_t n)
+{
+    size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+    for (; i < n; i += stride) dst[i] = src[i];
+}
+
+__global__ void zero_words_kernel(unsigned *__restrict__ p, size_t nwords)
+{
+    size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+    for (; i < nwords; i += stride) p[i] = 0u;
+}
+
+// Convergence test for iteration i = ctl->iter, per sequence, on the residual
+// of the current iterate: converged sequences are frozen with iters = i; at
+// the cap they stop as not converged (or non-finite for a NaN / Inf residual).
+__global__ void check_kernel(SolveControl *ctl, unsigned *res_bits, int *done, int *iters, int *status,
+                             float *resid, int B, float tol, int max_iter)
+{
+    if (ctl->all_done) return;
+    const int i = ctl->iter;
+    int active = 0;
+    for (int b = threadIdx.x; b < B; b += blockDim.x) {
+        if (done[b]) continue;
+        const float r = __uint_as_float(res_bits[b]);
+        res_bits[b] = 0u;
+        if (r <= tol) {
+            done[b] = 1;
+            iters[b] = i;
+            status[b] = DEER_SEQ_CONVERGED;
+            resid[b] = r;
+        } else if (i >= max_iter) {
+            done[b] = 1;
+            iters[b] = max_iter;
+            status[b] = __builtin_isfinite(r) ? DEER_SEQ_NOT_CONVERGED : DEER_SEQ_NONFINITE;
+            resid[b] = r;
+        } else {
+            active = 1;
+        }
+    }
+    active = __syncthreads_or(active);
+    if (threadIdx.x == 0) {
+        if (active) ctl->iter = i + 1;
+        else ctl->all_done = 1;
+    }
+}
+
+// Sequences whose final iterate sits in the second buffer are copied out.
+__global__ void gather_kernel(float *__restrict__ traj, const float *__restrict__ buf1, const int *__restrict__ iters,
+                              size_t per_seq, int B)
+{
+    const int bseq = blockIdx.y;
+    if (bseq >= B || (iters[bseq] & 1) == 0) return;
+    const size_t base = static_cast<size_t>(bseq) * per_seq;
+    for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < per_seq;
+         i += static_cast<size_t>(gridDim.x) * blockDim.x)
+        traj[base + i] = buf1[base + i];
+}
+
+unsigned grid_for(size_t n, unsigned threads = 256, unsigned cap = 8192)
+{
+    size_t g = (n + threads - 1) / threads;
+    if (g < 1) g = 1;
+    if (g > cap) g = cap;
+    return static_cast<unsigned>(g);
+}
+
+// ------------------------------------------------------ argument checks
+int check_cell(const deer_cell_params_t *p, int mode)
+{
+    if (!p) return fail(DEER_ERR_INVALID, "cell parameters: null pointer");
+    if (p->cell != DEER_CELL_TANH && p->cell != DEER_CELL_GRU)
+        return fail(DEER_ERR_INVALID, "cell parameters: unknown cell " + std::to_string(p->cell));
+    if (mode != DEER_MODE_DENSE && mode != DEER_MODE_DIAG)
+        return fail(DEER_ERR_INVALID, "unknown mode " + std::to_string(mode));
+    if (p->D < 1 || p->D > kMaxD)
+        return fail(DEER_ERR_UNSUPPORTED, "state size D=" + std::to_string(p->D) + " outside 1..64");
+    if (p->M < 1 || p->M > kMaxM)
+        return fail(DEER_ERR_UNSUPPORTED, "input size M=" + std::to_string(p->M) + " outside 1..1024");
+    if (p->cell == DEER_CELL_GRU && mode != DEER_MODE_DIAG)
+        return fail(DEER_ERR_UNSUPPORTED, "the GRU cell is supported in diag mode only");
+    if (!p->W || !p->U) return fail(DEER_ERR_INVALID, "cell parameters: W and U are required");
+    return DEER_OK;
+}
+
+int check_sizes(int B, int T)
+{
+    if (B < 0 || T < 0) return fail(DEER_ERR_INVALID, "negative batch or length");
+    if (static_cast<long long>(B) * T > (1ll << 31))
+        return fail(DEER_ERR_UNSUPPORTED, "B*T above 2^31 positions");
+    return DEER_OK;
+}
+
+// Layout of the deer_solve workspace.
+struct SolveLayout {
+    void *scan = nullptr;       // scan state (diag: look-back header + descriptors; dense: chunk aggregates)
+    SolveControl *ctl = nullptr;
+    unsigned *res_bits = nullptr;
+    int *done = nullptr, *iters = nullptr, *status = nullptr;
+    float *resid = nullptr;
+    float *buf1 = nullptr;      // second trajectory buffer [B,T,D]
+    float *lin = nullptr;       // a_t (diag) or d_t (dense, factored leaf) [B,T,D]
+    float *bvec = nullptr;      // b_t [B,T,D]
+    float *proj = nullptr;      // input projection [B,T,PD]
+    size_t bytes = 0;
+};
+
+SolveLayout solve_layout(void *ws, const deer_cell_params_t *p, int B, int T, int mode)
+{
+    const size_t BTD = static_cast<size_t>(B) * T * p->D;
+    const int PD = (p->cell == DEER_CELL_GRU) ? 3 * p->D : p->D;
+    Carve c(ws);
+    SolveLayout L;
+    // the scan state comes first so that its header keeps a fixed place
+    const size_t scan_bytes = (mode == DEER_MODE_DIAG) ? diag_scan_state_bytes(B, T, p->D)
+                                                       : dense_scan_state_bytes(B, T, p->D);
+    L.scan = c.take<char>(scan_bytes);
+    L.ctl = c.take<SolveControl>(1);
+    L.res_bits = c.take<unsigned>(B);
+    L.done = c.take<int>(B);
+    L.iters = c.take<int>(B);
+    L.status = c.take<int>(B);
+    L.resid = c.take<float>(B);
+    L.buf1 = c.take<float>(BTD);
+    L.lin = c.take<float>(BTD);
+    L.bvec = c.take<float>(BTD);
+    L.proj = c.take<float>(static_cast<size_t>(B) * T * PD);
+    L.bytes = c.off;
+    return L;
+}
+
+int check_workspace(void *ws, size_t have, size_t need, const char *who)
+{
+    if (!ws || have < need)
+        return fail(DEER_ERR_WORKSPACE, std::string(who) + ": workspace of " + std::to_string(need) + " bytes required");
+    if (reinterpret_cast<uintptr_t>(ws) % kAlign != 0)
+        return fail(DEER_ERR_WORKSPACE, std::string(who) + ": workspace not 256-byte aligned");
+    return DEER_OK;
+}
+
+}  // namespace
+}  // namespace deer
+
+using namespace deer;
+
+extern "C" {
+
+const char *deer_last_error(void) { return g_last_error.c_str(); }
+
+int deer_profile_enable(int enable)
+{
+    g_prof_enabled.store(enable ? 1 : 0);
+    return DEER_OK;
+}
+
+int deer_profile_read(int which, long long *launches, double *milliseconds)
+{
+    if (which < 0 || which >= kProfKinds || !launches || !milliseconds)
+        return fail(DEER_ERR_INVALID, "deer_profile_read: bad argument");
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    *launches = g_prof_launches[which];
+    *milliseconds = g_prof_ms[which];
+    g_prof_launches[which] = 0;
+    g_prof_ms[which] = 0.0;
+    return DEER_OK;
+}
+
+int deer_workspace_init(void *workspace, size_t ws_bytes, void *stream)
+{
+    if (!workspace) return fail(DEER_ERR_WORKSPACE, "workspace: null pointer");
+    if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+        return fail(DEER_ERR_WORKSPACE, "workspace: not 256-byte aligned");
+    const size_t words = ws_bytes / 4;
+    if (words == 0) return DEER_OK;
+    hipLaunchKernelGGL(zero_words_kernel, dim3(grid_for(words)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<unsigned *>(workspace), words);
+    DEER_HIP(hipGetLastError());
+    return DEER_OK;
+}
+
+int linear_scan_workspace_size(int B, int T, int D, int dense, size_t *bytes_out)
+{
+    if (!bytes_out) return fail(DEER_ERR_INVALID, "linear_scan_workspace_size: null output");
+    int rc = check_sizes(B, T);
+    if (rc) return rc;
+    if (D < 1) return fail(DEER_ERR_INVALID, "D must be >= 1");
+    if (dense && D > kMaxD) return fail(DEER_ERR_UNSUPPORTED, "dense scan: D above 64");
+    *bytes_out = dense ? dense_scan_state_bytes(B, T, D) : diag_scan_state_bytes(B, T, D);
+    return DEER_OK;
+}
+
+int linear_scan_diag(const float *a, const float *b, const float *s0, float *s, int B, int T, int D,
+                     void *workspace, size_t ws_bytes, void *stream)
+{
+    int rc = check_sizes(B, T);
+    if (rc) return rc;
+    if (D < 1) return fail(DEER_ERR_INVALID, "linear_scan_diag: D must be >= 1");
+    if (B == 0 || T == 0) return DEER_OK;
+    if (!a || !b || !s) return fail(DEER_ERR_INVALID, "linear_scan_diag: null a, b or s");
+    if (s == a || s == b) return fail(DEER_ERR_INVALID, "linear_scan_diag: s must not alias a or b");
+    if (D % 4 == 0 && ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b) |
+                        reinterpret_cast<uintptr_t>(s)) % 16 != 0))
+        return fail(DEER_ERR_INVALID, "linear_scan_diag: a, b and s must be 16-byte aligned");
+    rc = check_workspace(workspace, ws_bytes, diag_scan_state_bytes(B, T, D), "linear_scan_diag");
+    if (rc) return rc;
+    return launch_diag_scan(a, b, s0, s, s, nullptr, nullptr, nullptr, B, T, D, workspace,
+                            static_cast<hipStream_t>(stream));
+}
+
+int linear_scan_dense(const float *A, const float *b, const float *s0, float *s, int B, int T, int D,
+                      void *workspace, size_t ws_bytes, void *stream)
+{
+    int rc = check_sizes(B, T);
+    if (rc) return rc;
+    if (D < 1 || D > kMaxD) return fail(DEER_ERR_UNSUPPORTED, "linear_scan_dense: D outside 1..64");
+    if (B == 0 || T == 0) return DEER_OK;
+    if (!A || !b || !s) return fail(DEER_ERR_INVALID, "linear_scan_dense: null A, b or s");
+    if (s == b || s == A) return fail(DEER_ERR_INVALID, "linear_scan_dense: s must not alias A or b");
+    rc = check_workspace(workspace, ws_bytes, dense_scan_state_bytes(B, T, D), "linear_scan_dense");
+    if (rc) return rc;
+    return launch_dense_scan(A, nullptr, nullptr, b, s0, s, s, nullptr, nullptr, nullptr, B, T, D, workspace,
+                             static_cast<hipStream_t>(stream));
+}
+
+int deer_workspace_size(const deer_cell_params_t *p, int B, int T, int mode, size_t *bytes_out)
+{
+    if (!bytes_out) return fail(DEER_ERR_INVALID, "deer_workspace_size: null output");
+    int rc = check_cell(p, mode);
+    if (rc) return rc;
+    rc = check_sizes(B, T);
+    if (rc) return rc;
+    *bytes_out = solve_layout(nullptr, p, B, T, mode).bytes;
+    return DEER_OK;
+}
+
+int deer_rollout(const deer_cell_params_t *p, const float *x, const float *s0, int B, int T, float *traj_out,
+                 void *stream)
+{
+    if (!p) return fail(DEER_ERR_INVALID, "cell parameters: null pointer");
+    int rc = check_cell(p, p->cell == DEER_CELL_GRU ? DEER_MODE_DIAG : DEER_MODE_DENSE);
+    if (rc) return rc;
+    rc = check_sizes(B, T);
+    if (rc) return rc;
+    if (B == 0 || T == 0) return DEER_OK;
+    if (!x || !traj_out) return fail(DEER_ERR_INVALID, "deer_rollout: null x or traj_out");
+    return launch_rollout(p, x, s0, B, T, traj_out, static_cast<hipStream_t>(stream));
+}
+
+int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int B, int T, int mode, float tol,
+               int max_iter, const float *init_guess, float *traj_out, int *iters_out, float *resid_out,
+               int *status_out, void *workspace, size_t ws_bytes, void *stream_)
+{
+    int rc = check_cell(p, mode);
+    if (rc) return rc;
+    rc = check_sizes(B, T);
+    if (rc) return rc;
+    if (max_iter < 0) return fail(DEER_ERR_INVALID, "max_iter must be >= 0");
+    if (std::isnan(tol)) return fail(DEER_ERR_INVALID, "tol is NaN");
+    if (B == 0) return DEER_OK;
+    if (!iters_out) return fail(DEER_ERR_INVALID, "iters_out: null pointer");
+    if (T == 0) {
+        // an empty trajectory has residual 0: it passes iff 0 <= tol, else it stops at the cap
+        const bool pass = 0.0f <= tol;
+        for (int b = 0; b < B; ++b) {
+            iters_out[b] = pass ? 0 : max_iter;
+            if (resid_out) resid_out[b] = 0.0f;
+            if (status_out) status_out[b] = pass ? DEER_SEQ_CONVERGED : DEER_SEQ_NOT_CONVERGED;
+        }
+        return pass ? DEER_OK : DEER_NOT_CONVERGED;
+    }
+    if (!x || !traj_out) return fail(DEER_ERR_INVALID, "x and traj_out are required");
+    rc = check_workspace(workspace, ws_bytes, solve_layout(nullptr, p, B, T, mode).bytes, "deer_solve");
+    if (rc) return rc;
+    if (!g_poll.host) return fail(DEER_ERR_HIP, "deer_solve: pinned host memory unavailable");
+
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    const SolveLayout L = solve_layout(workspace, p, B, T, mode);
+    const int D = p->D;
+    const size_t BTD = static_cast<size_t>(B) * T * D;
+    const bool gru = p->cell == DEER_CELL_GRU;
+    const int PD = gru ? 3 * D : D;
+    ProfScope prof(stream);
+
+    // per-solve control state and the starting iterate s^(0) in traj_out
+    hipLaunchKernelGGL(init_control_kernel, dim3(grid_for(static_cast<size_t>(B) + 1)), dim3(256), 0, stream, L.ctl,
+                       L.done, L.iters, L.status, L.resid, L.res_bits, B);
+    DEER_HIP(hipGetLastError());
+    if (init_guess) {
+        if (init_guess != traj_out)
+            hipLaunchKernelGGL(copy_kernel, dim3(grid_for(BTD)), dim3(256), 0, stream, traj_out, init_guess, BTD);
+    } else {
+        hipLaunchKernelGGL(fill_kernel, dim3(grid_for(BTD)), dim3(256), 0, stream, traj_out, BTD, 0.0f);
+    }
+    DEER_HIP(hipGetLastError());
+
+    // iteration-invariant input projection (W_ih x + b_ih for the GRU, U x + b for tanh)
+    prof.begin(2);
+    rc = launch_projection(x, p->U, p->b, L.proj, B * T, p->M, PD, stream);
+    prof.end();
+    if (rc) return rc;
+
+    const int *sel = &L.ctl->iter;
+    const int *all_done = &L.ctl->all_done;
+    auto enqueue_iteration = [&]() -> int {
+        int r;
+        prof.begin(0);
+        if (gru)
+            r = launch_gru_eval(p->W, p->b2, L.proj, s0, traj_out, L.buf1, sel, L.done, all_done, L.lin, L.bvec,
+                                L.res_bits, B, T, D, stream);
+        else
+            r = launch_tanh_eval(p->W, L.proj, s0, traj_out, L.buf1, sel, L.done, all_done, L.lin, L.bvec,
+                                 L.res_bits, B, T, D, mode == DEER_MODE_DENSE, stream);
+        prof.end();
+        if (r) return r;
+        prof.begin(3);
+        hipLaunchKernelGGL(check_kernel, dim3(1), dim3(256), 0, stream, L.ctl, L.res_bits, L.done, L.iters,
+                           L.status, L.resid, B, tol, max_iter);
+        prof.end();
+        DEER_HIP(hipGetLastError());
+        prof.begin(1);
+        if (mode == DEER_MODE_DIAG)
+            r = launch_diag_scan(L.lin, L.bvec, s0, traj_out, L.buf1, sel, L.done, all_done, B, T, D, L.scan, stream);
+        else
+            r = launch_dense_scan(nullptr, L.lin, p->W, L.bvec, s0, traj_out, L.buf1, sel, L.done, all_done, B, T, D,
+                                  L.scan, stream);
+        prof.end();
+        return r;
+    };
+
+    // Enqueue batches of iterations and poll the device flag of the previous
+    // batch while the current one runs.  Kernels after convergence exit at once.
+    const long long total = static_cast<long long>(max_iter) + 1;   // evaluations needed at most
+    long long launched = 0;
+    int batch = 1;
+    int slot = 0;
+    hipEvent_t ev[2] = {nullptr, nullptr};
+    DEER_HIP(hipEventCreateWithFlags(&ev[0], hipEventDisableTiming));
+    DEER_HIP(hipEventCreateWithFlags(&ev[1], hipEventDisableTiming));
+    bool pending = false;
+    int pending_slot = 0;
+    volatile int *h = g_poll.host;
+    while (launched < total) {
+        const long long n = std::min<long long>(batch, total - launched);
+        for (long long k = 0; k < n && rc == DEER_OK; ++k) rc = enqueue_iteration();
+        if (rc) break;
+        launched += n;
+        h[slot] = 0;
+        if (hipMemcpyAsync(g_poll.host + slot, all_done, sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+            hipEventRecord(ev[slot], stream) != hipSuccess) {
+            rc = fail(DEER_ERR_HIP, "deer_solve: polling copy failed");
+            break;
+        }
+        if (pending) {
+            if (hipEventSynchronize(ev[pending_slot]) != hipSuccess) {
+                rc = fail(DEER_ERR_HIP, "deer_solve: event wait failed");
+                break;
+            }
+            if (h[pending_slot]) break;
+        }
+        pending = true;
+        pending_slot = slot;
+        slot ^= 1;
+        if (batch < 4) batch *= 2;
+    }
+    if (rc == DEER_OK) {
+        const size_t per_seq = static_cast<size_t>(T) * D;
+        hipLaunchKernelGGL(gather_kernel, dim3(grid_for(per_seq, 256, 1024), B), dim3(256), 0, stream, traj_out,
+                           L.buf1, L.iters, per_seq, B);
+        if (hipGetLastError() != hipSuccess) rc = fail(DEER_ERR_HIP, "deer_solve: gather launch failed");
+    }
+    std::vector<int> status_h(B, 0);
+    unsigned abort_flag = 0;
+    if (rc == DEER_OK) {
+        if (hipMemcpyAsync(iters_out, L.iters, sizeof(int) * B, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+            (resid_out && hipMemcpyAsync(resid_out, L.resid, sizeof(float) * B, hipMemcpyDeviceToHost, stream) != hipSuccess) ||
+            hipMemcpyAsync(status_h.data(), L.status, sizeof(int) * B, hipMemcpyDeviceToHost, stream) != hipSuccess)
+            rc = fail(DEER_ERR_HIP, "deer_solve: result copy failed");
+    }
+    if (rc == DEER_OK && mode == DEER_MODE_DIAG) {
+        if (hipMemcpyAsync(&abort_flag, &static_cast<ScanHeader *>(L.scan)->abort, sizeof(unsigned),
+                           hipMemcpyDeviceToHost, stream) != hipSuccess)
+            rc = fail(DEER_ERR_HIP, "deer_solve: flag copy failed");
+    }
+    const hipError_t se = hipStreamSynchronize(stream);
+    (void)hipEventDestroy(ev[0]);
+    (void)hipEventDestroy(ev[1]);
+    if (se != hipSuccess && rc == DEER_OK) rc = hip_fail(se, "hipStreamSynchronize(deer_solve)");
+    if (rc) return rc;
+    {
+        int last = 0;
+        for (int b = 0; b < B; ++b) last = std::max(last, iters_out[b]);
+        const long long limit[kProfKinds] = {last + 1, last, 1, last + 1};
+        prof.collect(limit);
+    }
+    if (abort_flag) return fail(DEER_ERR_DEVICE, "deer_solve: the scan look-back wait hit its bound");
+    bool any_nc = false;
+    for (int b = 0; b < B; ++b) {
+        if (status_out) status_out[b] = status_h[b];
+        any_nc |= status_h[b] != DEER_SEQ_CONVERGED;
+    }
+    return any_nc ? DEER_NOT_CONVERGED : DEER_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,412 @@
+// Cell kernels: the iteration-invariant input projection, the per-iteration
+// evaluation of f and its Jacobian at every (sequence, step) of the current
+// trajectory guess, and the plain sequential rollout.
+//
+// Evaluation at the guess s^(i) ("Parallel Broyden Methods", section 2;
+// residual as restated in the "Predictability" rebuttal, its equation 2):
+//   f_t = f(s_{t-1}, x_t)   (s_{-1} = s0)
+//   r_t = s_t - f_t         -> per-sequence max |r_t| (atomic max on the float bits)
+//   A_t = J_t or diag(J_t),  b_t = f_t - A_t s_{t-1}
+// so that s^(i+1) solves s_t = A_t s_{t-1} + b_t.
+//
+// Layout: a workgroup owns TP consecutive steps of one sequence.  The TP+1
+// state rows it needs (s_{t0-1} .. s_{t0+TP-1}) and the transposed recurrent
+// weights sit in LDS; lane c of a lane group handles channel c, so every global
+// access is a contiguous row segment.
+#include "internal.h"
+
+namespace deer {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTP = 64;   // steps per workgroup in the evaluation kernels
+
+__device__ __forceinline__ float sigmoidf_(float u) { return 1.0f / (1.0f + expf(-u)); }
+
+// max over the workgroup of unsigned bit patterns (non-negative floats order as
+// integers; NaN patterns sit above +Inf), then one atomic per workgroup
+__device__ __forceinline__ void block_max_to(unsigned v, unsigned *dst)
+{
+    __shared__ unsigned red[kThreads / 64];
+    for (int o = 32; o > 0; o >>= 1) v = max(v, static_cast<unsigned>(__shfl_xor(static_cast<int>(v), o, 64)));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        unsigned m = red[0];
+        for (int w = 1; w < kThreads / 64; ++w) m = max(m, red[w]);
+        atomicMax(dst, m);
+    }
+}
+
+// ------------------------------------------------------------- projection
+// out[n][o] = sum_j U[o][j] x[n][j] + bias[o], for OG groups of 64 outputs.
+template <int OG>
+__global__ __launch_bounds__(kThreads) void projection_kernel(const float *__restrict__ x, const float *__restrict__ U,
+                                                              const float *__restrict__ bias, float *__restrict__ out,
+                                                              int N, int M, int O, int row_tiles)
+{
+    constexpr int RT = 32;                   // rows per tile
+    __shared__ float Ut[64][64 * OG];        // Ut[k][o] = U[o][k0 + k]
+    __shared__ float xs[RT][65];
+    const int ol = threadIdx.x & 63, pg = threadIdx.x >> 6;
+    const int nkt = (M + 63) / 64;
+    float bo[OG];
+#pragma unroll
+    for (int g = 0; g < OG; ++g) {
+        const int o = ol + 64 * g;
+        bo[g] = (bias && o < O) ? bias[o] : 0.0f;
+    }
+    auto load_U = [&](int k0) {
+        for (int e = threadIdx.x; e < 64 * 64 * OG; e += kThreads) {
+            const int o = e / 64, k = e % 64;
+            Ut[k][o] = (o < O && k0 + k < M) ? U[static_cast<size_t>(o) * M + k0 + k] : 0.0f;
+        }
+    };
+    if (nkt == 1) load_U(0);
+    for (int rt = 0; rt < row_tiles; ++rt) {
+        const long long n0 = (static_cast<long long>(blockIdx.x) * row_tiles + rt) * RT;
+        if (n0 >= N) break;
+        float acc[RT / 4][OG];
+#pragma unroll
+        for (int r = 0; r < RT / 4; ++r)
+#pragma unroll
+            for (int g = 0; g < OG; ++g) acc[r][g] = 0.0f;
+        for (int kt = 0; kt < nkt; ++kt) {
+            const int k0 = kt * 64;
+            __syncthreads();
+            if (nkt > 1) load_U(k0);
+            for (int e = threadIdx.x; e < RT * 64; e += kThreads) {
+                const int r = e / 64, k = e % 64;
+                const long long n = n0 + r;
+                xs[r][k] = (n < N && k0 + k < M) ? x[static_cast<size_t>(n) * M + k0 + k] : 0.0f;
+            }
+            __syncthreads();
+#pragma unroll 8
+            for (int k = 0; k < 64; ++k) {
+                float u[OG];
+#pragma unroll
+                for (int g = 0; g < OG; ++g) u[g] = Ut[k][ol + 64 * g];
+#pragma unroll
+                for (int r = 0; r < RT / 4; ++r) {
+                    const float xv = xs[pg + 4 * r][k];
+#pragma unroll
+                    for (int g = 0; g < OG; ++g) acc[r][g] += u[g] * xv;
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < RT / 4; ++r) {
+            const long long n = n0 + pg + 4 * r;
+            if (n >= N) continue;
+#pragma unroll
+            for (int g = 0; g < OG; ++g) {
+                const int o = ol + 64 * g;
+                if (o < O) out[static_cast<size_t>(n) * O + o] = acc[r][g] + bo[g];
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------- tanh cell
+// f = tanh(W s + p); dense: lin = d = 1 - f^2, b = f - d * (W s)  (A_t = diag(d) W)
+//                    diag:  lin = a = d * W_cc, b = f - a * s_c
+template <int DP>
+__global__ __launch_bounds__(kThreads) void tanh_eval_kernel(
+    const float *__restrict__ W, const float *__restrict__ p, const float *__restrict__ s0,
+    const float *s_even, const float *s_odd, const int *__restrict__ sel, const int *__restrict__ skip,
+    const int *__restrict__ all_done, float *__restrict__ lin, float *__restrict__ bout, unsigned *__restrict__ res_bits,
+    int T, int D, int tiles, int dense)
+{
+    if (all_done && *all_done) return;
+    const int bseq = blockIdx.x / tiles, tile = blockIdx.x % tiles;
+    if (skip && skip[bseq]) return;
+    constexpr int PPP = kThreads / DP;   // positions per pass
+    __shared__ float Wt[DP][DP + 1];     // Wt[k][c] = W[c][k]
+    __shared__ float srow[kTP + 1][DP];  // srow[r] = s_{t0 - 1 + r}
+    const float *s = (sel && (*sel & 1)) ? s_odd : s_even;
+    const int t0 = tile * kTP;
+    const size_t seq = static_cast<size_t>(bseq) * T;
+    for (int e = threadIdx.x; e < DP * DP; e += kThreads) {
+        const int k = e / DP, c = e % DP;
+        Wt[k][c] = (k < D && c < D) ? W[c * D + k] : 0.0f;
+    }
+    for (int e = threadIdx.x; e < (kTP + 1) * DP; e += kThreads) {
+        const int r = e / DP, c = e % DP;
+        const int t = t0 - 1 + r;
+        float v = 0.0f;
+        if (c < D && t < T) {
+            if (t < 0) v = s0 ? s0[static_cast<size_t>(bseq) * D + c] : 0.0f;
+            else v = s[(seq + t) * D + c];
+        }
+        srow[r][c] = v;
+    }
+    __syncthreads();
+    const int c = threadIdx.x % DP, ps = threadIdx.x / DP;
+    const bool cv = c < D;
+    const float wcc = cv ? Wt[c][c] : 0.0f;
+    unsigned rmax = 0u;
+    for (int r = ps; r < kTP; r += PPP) {
+        const int t = t0 + r;
+        if (t >= T) break;
+        float ws = 0.0f;
+#pragma unroll 8
+        for (int k = 0; k < DP; ++k) ws += Wt[k][c] * srow[r][k];
+        if (!cv) continue;
+        const size_t o = (seq + t) * D + c;
+        const float h = ws + p[o];
+        const float f = tanhf(h);
+        const float d = 1.0f - f * f;
+        if (dense) {
+            lin[o] = d;
+            bout[o] = f - d * ws;
+        } else {
+            const float a = d * wcc;
+            lin[o] = a;
+            bout[o] = f - a * srow[r][c];
+        }
+        rmax = max(rmax, __float_as_uint(fabsf(srow[r + 1][c] - f)));
+    }
+    block_max_to(rmax, res_bits + bseq);
+}
+
+// -------------------------------------------------------------- GRU cell
+// Gate order (r, z, n); p = W_ih x + b_ih precomputed, q = W_hh h + b_hh here.
+//   a = d f / d h (diagonal) = z + (h - n) z (1 - z) Wz_cc
+//                            + (1 - z)(1 - n^2)(r Wn_cc + r (1 - r) Wr_cc q_n)
+//   b = f - a h
+template <int DP>
+__global__ __launch_bounds__(kThreads) void gru_eval_kernel(
+    const float *__restrict__ Whh, const float *__restrict__ bhh, const float *__restrict__ p,
+    const float *__restrict__ s0, const float *s_even, const float *s_odd, const int *__restrict__ sel,
+    const int *__restrict__ skip, const int *__restrict__ all_done, float *__restrict__ aout,
+    float *__restrict__ bout, unsigned *__restrict__ res_bits, int T, int D, int tiles)
+{
+    if (all_done && *all_done) return;
+    const int bseq = blockIdx.x / tiles, tile = blockIdx.x % tiles;
+    if (skip && skip[bseq]) return;
+    constexpr int PPP = kThreads / DP;
+    __shared__ float Wt[DP][3 * DP];     // Wt[k][g*DP + c] = W_hh[g*D + c][k]
+    __shared__ float srow[kTP + 1][DP];
+    const float *s = (sel && (*sel & 1)) ? s_odd : s_even;
+    const int t0 = tile * kTP;
+    const size_t seq = static_cast<size_t>(bseq) * T;
+    for (int e = threadIdx.x; e < 3 * DP * DP; e += kThreads) {
+        const int row = e / DP, k = e % DP;     // row = g*DP + c
+        const int g = row / DP, c = row % DP;
+        Wt[k][row] = (k < D && c < D) ? Whh[static_cast<size_t>(g * D + c) * D + k] : 0.0f;
+    }
+    for (int e = threadIdx.x; e < (kTP + 1) * DP; e += kThreads) {
+        const int r = e / DP, c = e % DP;
+        const int t = t0 - 1 + r;
+        float v = 0.0f;
+        if (c < D && t < T) {
+            if (t < 0) v = s0 ? s0[static_cast<size_t>(bseq) * D + c] : 0.0f;
+            else v = s[(seq + t) * D + c];
+        }
+        srow[r][c] = v;
+    }
+    __syncthreads();
+    const int c = threadIdx.x % DP, ps = threadIdx.x / DP;
+    const bool cv = c < D;
+    const float wr = cv ? Wt[c][c] : 0.0f, wz = cv ? Wt[c][DP + c] : 0.0f, wn = cv ? Wt[c][2 * DP + c] : 0.0f;
+    const float br = (cv && bhh) ? bhh[c] : 0.0f;
+    const float bz = (cv && bhh) ? bhh[D + c] : 0.0f;
+    const float bn = (cv && bhh) ? bhh[2 * D + c] : 0.0f;
+    unsigned rmax = 0u;
+    for (int r = ps; r < kTP; r += PPP) {
+        const int t = t0 + r;
+        if (t >= T) break;
+        float qr = br, qz = bz, qn = bn;
+#pragma unroll 8
+        for (int k = 0; k < DP; ++k) {
+            const float hk = srow[r][k];
+            qr += Wt[k][c] * hk;
+            qz += Wt[k][DP + c] * hk;
+            qn += Wt[k][2 * DP + c] * hk;
+        }
+        if (!cv) continue;
+        const size_t pb = (seq + t) * (3 * static_cast<size_t>(D));
+        const float rg = sigmoidf_(p[pb + c] + qr);
+        const float zg = sigmoidf_(p[pb + D + c] + qz);
+        const float ng = tanhf(p[pb + 2 * D + c] + rg * qn);
+        const float h = srow[r][c];
+        const float f = (1.0f - zg) * ng + zg * h;
+        const float a = zg + (h - ng) * zg * (1.0f - zg) * wz +
+                        (1.0f - zg) * (1.0f - ng * ng) * (rg * wn + rg * (1.0f - rg) * wr * qn);
+        const size_t o = (seq + t) * D + c;
+        aout[o] = a;
+        bout[o] = f - a * h;
+        rmax = max(rmax, __float_as_uint(fabsf(srow[r + 1][c] - f)));
+    }
+    block_max_to(rmax, res_bits + bseq);
+}
+
+// ------------------------------------------------------ sequential rollout
+// One wavefront per sequence steps s_t = f(s_{t-1}, x_t) forward; weights in LDS.
+template <int DP, bool GRU>
+__global__ __launch_bounds__(kThreads) void rollout_kernel(const float *__restrict__ W, const float *__restrict__ U,
+                                                           const float *__restrict__ b, const float *__restrict__ b2,
+                                                           const float *__restrict__ x, const float *__restrict__ s0,
+                                                           float *__restrict__ traj, int B, int T, int D, int M)
+{
+    constexpr int NG = GRU ? 3 : 1;
+    __shared__ float Wt[DP][NG * DP];    // Wt[k][g*DP + c] = W[g*D + c][k]
+    __shared__ float Ut[64][NG * DP];    // Ut[j][g*DP + c] = U[g*D + c][j]  (M <= 64)
+    for (int e = threadIdx.x; e < NG * DP * DP; e += kThreads) {
+        const int row = e / DP, k = e % DP, g = row / DP, c = row % DP;
+        Wt[k][row] = (k < D && c < D) ? W[static_cast<size_t>(g * D + c) * D + k] : 0.0f;
+    }
+    for (int e = threadIdx.x; e < NG * DP * 64; e += kThreads) {
+        const int row = e / 64, j = e % 64, g = row / DP, c = row % DP;
+        Ut[j][row] = (j < M && c < D) ? U[static_cast<size_t>(g * D + c) * M + j] : 0.0f;
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const int bseq = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    if (bseq >= B) return;
+    const bool cv = lane < D;
+    const int c = lane < DP ? lane : 0;
+    float bi[NG], bh[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        bi[g] = (cv && b) ? b[g * D + c] : 0.0f;
+        bh[g] = (cv && b2) ? b2[g * D + c] : 0.0f;
+    }
+    float st = (cv && s0) ? s0[static_cast<size_t>(bseq) * D + lane] : 0.0f;
+    const size_t xb = static_cast<size_t>(bseq) * T * M;
+    const size_t ob = static_cast<size_t>(bseq) * T * D;
+    for (int t = 0; t < T; ++t) {
+        const float xl = (lane < M) ? x[xb + static_cast<size_t>(t) * M + lane] : 0.0f;
+        float gi[NG], gh[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) { gi[g] = bi[g]; gh[g] = bh[g]; }
+        for (int j = 0; j < M; ++j) {
+            const float xj = __shfl(xl, j, 64);
+#pragma unroll
+            for (int g = 0; g < NG; ++g) gi[g] += Ut[j][g * DP + c] * xj;
+        }
+#pragma unroll
+        for (int k = 0; k < DP; ++k) {
+            const float sk = __shfl(st, k, 64);
+#pragma unroll
+            for (int g = 0; g < NG; ++g) gh[g] += Wt[k][g * DP + c] * sk;
+        }
+        float f;
+        if constexpr (GRU) {
+            const float rg = sigmoidf_(gi[0] + gh[0]);
+            const float zg = sigmoidf_(gi[1] + gh[1]);
+            const float ng = tanhf(gi[2] + rg * gh[2]);
+            f = (1.0f - zg) * ng + zg * st;
+        } else {
+            f = tanhf(gi[0] + gh[0]);
+        }
+        st = cv ? f : 0.0f;
+        if (cv) traj[ob + static_cast<size_t>(t) * D + lane] = st;
+    }
+}
+
+int pick_dp(int D) { return D <= 4 ? 4 : D <= 8 ? 8 : D <= 16 ? 16 : D <= 32 ? 32 : 64; }
+
+unsigned eval_blocks(int B, int T, int &tiles)
+{
+    tiles = (T + kTP - 1) / kTP;
+    return static_cast<unsigned>(static_cast<long long>(B) * tiles);
+}
+
+}  // namespace
+
+int launch_projection(const float *x, const float *U, const float *bias, float *p, int N, int M, int O,
+                      hipStream_t stream)
+{
+    if (N == 0) return DEER_OK;
+    if (O > 192) return fail(DEER_ERR_UNSUPPORTED, "projection: more than 192 outputs");
+    const int row_tiles = 4;
+    const long long rows_per_block = 32ll * row_tiles;
+    const unsigned blocks = static_cast<unsigned>((N + rows_per_block - 1) / rows_per_block);
+    const int og = (O + 63) / 64;
+    if (og == 1)
+        hipLaunchKernelGGL((projection_kernel<1>), dim3(blocks), dim3(kThreads), 0, stream, x, U, bias, p, N, M, O, row_tiles);
+    else if (og == 2)
+        hipLaunchKernelGGL((projection_kernel<2>), dim3(blocks), dim3(kThreads), 0, stream, x, U, bias, p, N, M, O, row_tiles);
+    else
+        hipLaunchKernelGGL((projection_kernel<3>), dim3(blocks), dim3(kThreads), 0, stream, x, U, bias, p, N, M, O, row_tiles);
+    DEER_HIP(hipGetLastError());
+    return DEER_OK;
+}
+
+#define DEER_TANH_CASE(DPV)                                                                                     \
+    case DPV:                                                                                                   \
+        hipLaunchKernelGGL((tanh_eval_kernel<DPV>), dim3(blocks), dim3(kThreads), 0, stream, W, p, s0, s_even,  \
+                           s_odd, sel, skip, all_done, lin, bvec, res_bits, T, D, tiles, dense);                \
+        break;
+
+int launch_tanh_eval(const float *W, const float *p, const float *s0, const float *s_even, const float *s_odd,
+                     const int *sel, const int *skip, const int *all_done, float *lin, float *bvec, unsigned *res_bits,
+                     int B, int T, int D, int dense, hipStream_t stream)
+{
+    int tiles;
+    const unsigned blocks = eval_blocks(B, T, tiles);
+    if (blocks == 0) return DEER_OK;
+    switch (pick_dp(D)) {
+        DEER_TANH_CASE(4)
+        DEER_TANH_CASE(8)
+        DEER_TANH_CASE(16)
+        DEER_TANH_CASE(32)
+        DEER_TANH_CASE(64)
+    }
+    DEER_HIP(hipGetLastError());
+    return DEER_OK;
+}
+
+#define DEER_GRU_CASE(DPV)                                                                                      \
+    case DPV:                                                                                                   \
+        hipLaunchKernelGGL((gru_eval_kernel<DPV>), dim3(blocks), dim3(kThreads), 0, stream, Whh, bhh, p, s0,    \
+                           s_even, s_odd, sel, skip, all_done, a, bvec, res_bits, T, D, tiles);                 \
+        break;
+
+int launch_gru_eval(const float *Whh, const float *bhh, const float *p, const float *s0, const float *s_even,
+                    const float *s_odd, const int *sel, const int *skip, const int *all_done, float *a, float *bvec,
+                    unsigned *res_bits, int B, int T, int D, hipStream_t stream)
+{
+    int tiles;
+    const unsigned blocks = eval_blocks(B, T, tiles);
+    if (blocks == 0) return DEER_OK;
+    switch (pick_dp(D)) {
+        DEER_GRU_CASE(4)
+        DEER_GRU_CASE(8)
+        DEER_GRU_CASE(16)
+        DEER_GRU_CASE(32)
+        DEER_GRU_CASE(64)
+    }
+    DEER_HIP(hipGetLastError());
+    return DEER_OK;
+}
+
+#define DEER_ROLL_CASE(DPV)                                                                                      \
+    case DPV:                                                                                                    \
+        if (gru)                                                                                                 \
+            hipLaunchKernelGGL((rollout_kernel<DPV, true>), dim3(blocks), dim3(kThreads), 0, stream, p->W, p->U, \
+                               p->b, p->b2, x, s0, traj, B, T, p->D, p->M);                                      \
+        else                                                                                                     \
+            hipLaunchKernelGGL((rollout_kernel<DPV, false>), dim3(blocks), dim3(kThreads), 0, stream, p->W,      \
+                               p->U, p->b, p->b2, x, s0, traj, B, T, p->D, p->M);                                \
+        break;
+
+int launch_rollout(const deer_cell_params_t *p, const float *x, const float *s0, int B, int T, float *traj,
+                   hipStream_t stream)
+{
+    if (p->M > 64) return fail(DEER_ERR_UNSUPPORTED, "deer_rollout: input size above 64");
+    const bool gru = p->cell == DEER_CELL_GRU;
+    const unsigned blocks = static_cast<unsigned>((B + 3) / 4);
+    switch (pick_dp(p->D)) {
+        DEER_ROLL_CASE(4)
+        DEER_ROLL_CASE(8)
+        DEER_ROLL_CASE(16)
+        DEER_ROLL_CASE(32)
+        DEER_ROLL_CASE(64)
+    }
+    DEER_HIP(hipGetLastError());
+    return DEER_OK;
+}
+
+}  // namespace deer

@@ -1,0 +1,284 @@
+// Single-pass scan of the diagonal affine recurrence s_t = a_t * s_{t-1} + b_t.
+//
+// Diagonal blocks stay diagonal when composed, so every channel (b, d) is an
+// independent scalar recurrence ("Parallel Broyden Methods", section 2,
+// diagonal quasi-Newton).  Two affine maps merge as
+//     (a_j, b_j) o (a_i, b_i) = (a_j a_i, a_j b_i + b_j)   (i before j),
+// the later map acting on the left (same page, appendix C.2).
+//
+// Layout [B, T, D], D fastest.  A workgroup owns one tile of 64 channels x L
+// time steps of one sequence (a "chunk"):
+//   1. every thread loads LT consecutive steps of VEC channels into registers
+//      (non-temporal 16-byte loads, 256-byte contiguous row segments) and folds
+//      them into one affine pair per channel;
+//   2. the time slots of the workgroup are combined through LDS (exclusive
+//      prefix per slot, chunk aggregate per channel);
+//   3. wave 0 publishes the chunk aggregate, looks back over earlier chunks of
+//      the same channels (decoupled look-back) until it meets an inclusive
+//      prefix, and publishes its own inclusive prefix (the state at the
+//      chunk's last step);
+//   4. every thread replays its registers from the carried-in state and
+//      streams s out (non-temporal stores).
+// a and b are read once and s written once: 12 bytes per element.
+//
+// Look-back descriptors are 64-bit words holding a float and a 32-bit tag
+// (epoch * 4 + kind), written and read with agent-scope atomics, so a word is
+// valid on its own and no fences are needed.  Chunks are numbered by an atomic
+// ticket taken at workgroup start, so every chunk's predecessors are already
+// resident or finished: the look-back always makes progress.  Its wait is
+// bounded all the same; if the bound is hit the header's abort flag is set and
+// the chunk's carry becomes NaN.
+#include "internal.h"
+
+namespace deer {
+namespace {
+
+constexpr int kCH = 64;          // channels per chunk tile
+constexpr int kThreads = 256;
+constexpr unsigned kSpinLimit = 1u << 22;
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ unsigned long long pack_word(float v, unsigned tag) {
+    return (static_cast<unsigned long long>(tag) << 32) | __float_as_uint(v);
+}
+__device__ __forceinline__ unsigned word_tag(unsigned long long w) { return static_cast<unsigned>(w >> 32); }
+__device__ __forceinline__ float word_val(unsigned long long w) { return __uint_as_float(static_cast<unsigned>(w)); }
+
+__device__ __forceinline__ unsigned long long load_word(const unsigned long long *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_word(unsigned long long *p, unsigned long long v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int VEC, int LT>
+struct DiagGeom {
+    static constexpr int LD = kCH / VEC;       // threads across a tile row
+    static constexpr int NS = kThreads / LD;   // time slots per workgroup
+    static constexpr int L = NS * LT;          // time steps per chunk
+};
+
+template <int VEC, int LT>
+__global__ __launch_bounds__(kThreads) void diag_scan_kernel(
+    const float *__restrict__ a, const float *__restrict__ b, const float *__restrict__ s0,
+    float *out0, float *out1, const int *__restrict__ out_sel, const int *__restrict__ skip,
+    const int *__restrict__ all_done, int T, int D, int groups, int chains, int nchunk,
+    ScanHeader *__restrict__ hdr, unsigned long long *__restrict__ desc)
+{
+    using G = DiagGeom<VEC, LT>;
+    constexpr int LD = G::LD, NS = G::NS, L = G::L;
+
+    if (all_done && *all_done) return;   // same value for every workgroup of the launch
+
+    __shared__ unsigned sh_ticket, sh_epoch;
+    __shared__ float shA[NS][kCH];
+    __shared__ float shB[NS][kCH];
+    __shared__ float shC[kCH];
+
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        sh_ticket = __hip_atomic_fetch_add(&hdr->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sh_epoch = __hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    const unsigned ticket = sh_ticket;
+    const unsigned epoch = sh_epoch;
+    const unsigned tag_agg = epoch * 4u + 1u, tag_inc = epoch * 4u + 2u;
+    const int tchunk = static_cast<int>(ticket / static_cast<unsigned>(chains));
+    const int chain = static_cast<int>(ticket % static_cast<unsigned>(chains));
+    const int bseq = chain / groups;
+    const int grp = chain % groups;
+
+    if (!(skip && skip[bseq])) {
+        float *out = (out_sel && (*out_sel & 1)) ? out1 : out0;
+        const int slot = tid / LD;
+        const int lc = (tid % LD) * VEC;          // channel offset inside the tile
+        const int c0 = grp * kCH + lc;            // first channel of this thread
+        const bool cvalid = c0 < D;               // VEC == 4 implies D % 4 == 0
+        const int t0 = tchunk * L + slot * LT;
+        const size_t seq = static_cast<size_t>(bseq) * T * D;
+
+        float av[LT][VEC], bv[LT][VEC];
+#pragma unroll
+        for (int j = 0; j < LT; ++j) {
+            const int t = t0 + j;
+            if (cvalid && t < T) {
+                const size_t off = seq + static_cast<size_t>(t) * D + c0;
+                if constexpr (VEC == 4) {
+                    const v4f x = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(a + off));
+                    const v4f y = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(b + off));
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) { av[j][v] = x[v]; bv[j][v] = y[v]; }
+                } else {
+                    av[j][0] = __builtin_nontemporal_load(a + off);
+                    bv[j][0] = __builtin_nontemporal_load(b + off);
+                }
+            } else {
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) { av[j][v] = 1.0f; bv[j][v] = 0.0f; }
+            }
+        }
+
+        // fold this thread's LT steps into one affine pair per channel
+        float A[VEC], Bq[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) { A[v] = 1.0f; Bq[v] = 0.0f; }
+#pragma unroll
+        for (int j = 0; j < LT; ++j)
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+                Bq[v] = av[j][v] * Bq[v] + bv[j][v];
+                A[v] = av[j][v] * A[v];
+            }
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) { shA[slot][lc + v] = A[v]; shB[slot][lc + v] = Bq[v]; }
+        __syncthreads();
+
+        // exclusive prefix over the earlier time slots of this chunk
+        float PA[VEC], PB[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) { PA[v] = 1.0f; PB[v] = 0.0f; }
+        for (int k = 0; k < slot; ++k)
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+                const float ak = shA[k][lc + v];
+                PB[v] = ak * PB[v] + shB[k][lc + v];
+                PA[v] = ak * PA[v];
+            }
+
+        if (tid < kCH) {   // wave 0: one channel per lane
+            const int c = tid;
+            const int ch = grp * kCH + c;
+            float carry = 0.0f;
+            if (ch < D) {
+                float GA = 1.0f, GB = 0.0f;
+                for (int k = 0; k < NS; ++k) {
+                    const float ak = shA[k][c];
+                    GB = ak * GB + shB[k][c];
+                    GA = ak * GA;
+                }
+                unsigned long long *mine = desc + (static_cast<size_t>(chain) * nchunk + tchunk) * 3 * kCH;
+                if (tchunk == 0) {
+                    carry = s0 ? s0[static_cast<size_t>(bseq) * D + ch] : 0.0f;
+                } else {
+                    store_word(mine + c, pack_word(GA, tag_agg));
+                    store_word(mine + kCH + c, pack_word(GB, tag_agg));
+                    float accA = 1.0f, accB = 0.0f;   // maps s_end(j) to s_end(tchunk - 1)
+                    int j = tchunk - 1;
+                    unsigned spins = 0;
+                    while (true) {
+                        const unsigned long long *pj = desc + (static_cast<size_t>(chain) * nchunk + j) * 3 * kCH;
+                        const unsigned long long wi = load_word(pj + 2 * kCH + c);
+                        if (word_tag(wi) == tag_inc) {
+                            carry = accA * word_val(wi) + accB;
+                            break;
+                        }
+                        const unsigned long long wa = load_word(pj + c);
+                        const unsigned long long wb = load_word(pj + kCH + c);
+                        if (word_tag(wa) == tag_agg && word_tag(wb) == tag_agg) {
+                            accB = accA * word_val(wb) + accB;
+                            accA = accA * word_val(wa);
+                            --j;
+                            continue;
+                        }
+                        ++spins;
+                        if (spins > kSpinLimit ||
+                            ((spins & 1023u) == 0u &&
+                             __hip_atomic_load(&hdr->abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
+                            __hip_atomic_store(&hdr->abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            carry = __builtin_nanf("");
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(1);
+                    }
+                }
+                store_word(mine + 2 * kCH + c, pack_word(GA * carry + GB, tag_inc));
+            }
+            shC[c] = carry;
+        }
+        __syncthreads();
+
+        float st[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) st[v] = PA[v] * shC[lc + v] + PB[v];
+#pragma unroll
+        for (int j = 0; j < LT; ++j) {
+            const int t = t0 + j;
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) st[v] = av[j][v] * st[v] + bv[j][v];
+            if (cvalid && t < T) {
+                const size_t off = seq + static_cast<size_t>(t) * D + c0;
+                if constexpr (VEC == 4) {
+                    v4f y;
+                    y[0] = st[0]; y[1] = st[1]; y[2] = st[2]; y[3] = st[3];
+                    __builtin_nontemporal_store(y, reinterpret_cast<v4f *>(out + off));
+                } else {
+                    __builtin_nontemporal_store(st[0], out + off);
+                }
+            }
+        }
+    }
+
+    // Last workgroup out resets the ticket/done counters and advances the epoch.
+    __syncthreads();
+    if (tid == 0) {
+        const unsigned prev = __hip_atomic_fetch_add(&hdr->done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        if (prev == gridDim.x - 1) {
+            __hip_atomic_store(&hdr->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&hdr->epoch, epoch + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+constexpr int kLT4 = 16;   // VEC = 4: 16 slots x 16 steps = 256 steps per chunk
+constexpr int kLT1 = 32;   // VEC = 1: 4 slots x 32 steps = 128 steps per chunk
+
+}  // namespace
+
+DiagScanPlan diag_scan_plan(int B, int T, int D)
+{
+    DiagScanPlan p{};
+    p.B = B;
+    p.T = T;
+    p.D = D;
+    p.vec = (D % 4 == 0) ? 4 : 1;
+    p.chunk_len = (p.vec == 4) ? DiagGeom<4, kLT4>::L : DiagGeom<1, kLT1>::L;
+    p.groups = (D + kCH - 1) / kCH;
+    p.chains = B * p.groups;
+    p.nchunk = (T + p.chunk_len - 1) / p.chunk_len;
+    p.desc_words = static_cast<size_t>(p.chains) * p.nchunk * 3 * kCH;
+    return p;
+}
+
+size_t diag_scan_state_bytes(int B, int T, int D)
+{
+    const DiagScanPlan p = diag_scan_plan(B, T, D);
+    return sizeof(ScanHeader) + align_up(p.desc_words * sizeof(unsigned long long));
+}
+
+int launch_diag_scan(const float *a, const float *b, const float *s0, float *out0, float *out1,
+                     const int *out_sel, const int *skip, const int *all_done, int B, int T, int D,
+                     void *state, hipStream_t stream)
+{
+    const DiagScanPlan p = diag_scan_plan(B, T, D);
+    if (B == 0 || T == 0) return DEER_OK;
+    const size_t blocks = static_cast<size_t>(p.chains) * p.nchunk;
+    if (blocks > 0x7fffffffull) return fail(DEER_ERR_UNSUPPORTED, "linear scan: problem too large for one launch");
+    auto *hdr = static_cast<ScanHeader *>(state);
+    auto *desc = reinterpret_cast<unsigned long long *>(static_cast<char *>(state) + sizeof(ScanHeader));
+    if (p.vec == 4) {
+        hipLaunchKernelGGL((diag_scan_kernel<4, kLT4>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                           stream, a, b, s0, out0, out1, out_sel, skip, all_done, T, D, p.groups, p.chains,
+                           p.nchunk, hdr, desc);
+    } else {
+        hipLaunchKernelGGL((diag_scan_kernel<1, kLT1>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                           stream, a, b, s0, out0, out1, out_sel, skip, all_done, T, D, p.groups, p.chains,
+                           p.nchunk, hdr, desc);
+    }
+    DEER_HIP(hipGetLastError());
+    return DEER_OK;
+}
+
+}  // namespace deer

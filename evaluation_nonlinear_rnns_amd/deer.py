@@ -1,0 +1,280 @@
+"""Python binding of libdeer (include/deer.h).
+
+Argument marshalling only: torch supplies device memory and the current HIP
+stream; every step of the solver runs in the library's HIP kernels.  The
+functions keep the C names.  Loading fails loudly when the library has not
+been built (``python -m evaluation_nonlinear_rnns_amd.build``) -- there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdeer.so")
+
+DEER_MODE_DENSE = 0
+DEER_MODE_DIAG = 1
+DEER_CELL_TANH = 0
+DEER_CELL_GRU = 1
+MODES = {"dense": DEER_MODE_DENSE, "diag": DEER_MODE_DIAG}
+CELLS = {"tanh": DEER_CELL_TANH, "gru": DEER_CELL_GRU}
+
+DEER_OK = 0
+DEER_NOT_CONVERGED = 1
+ERRORS = {-1: "DEER_ERR_INVALID", -2: "DEER_ERR_UNSUPPORTED", -3: "DEER_ERR_WORKSPACE",
+          -4: "DEER_ERR_HIP", -5: "DEER_ERR_DEVICE"}
+
+# Every symbol include/deer.h declares.
+EXPORTS = ("deer_workspace_size", "deer_workspace_init", "deer_solve", "linear_scan_workspace_size",
+           "linear_scan_diag", "linear_scan_dense", "deer_rollout", "deer_profile_enable",
+           "deer_profile_read", "deer_last_error")
+
+
+class DeerError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{ERRORS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class CellParams(ctypes.Structure):
+    _fields_ = [("cell", ctypes.c_int), ("D", ctypes.c_int), ("M", ctypes.c_int),
+                ("W", ctypes.c_void_p), ("U", ctypes.c_void_p), ("b", ctypes.c_void_p),
+                ("b2", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load_library():
+    """Load libdeer.so (after torch, so both share one HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    import torch  # noqa: F401  -- loads the HIP runtime torch uses first
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m evaluation_nonlinear_rnns_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    c_int, c_size, vp, fp = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+    sig = {
+        "deer_workspace_size": ([ctypes.POINTER(CellParams), c_int, c_int, c_int, ctypes.POINTER(c_size)], c_int),
+        "deer_workspace_init": ([vp, c_size, vp], c_int),
+        "deer_solve": ([ctypes.POINTER(CellParams), vp, vp, c_int, c_int, c_int, fp, c_int, vp, vp, vp, vp, vp,
+                        vp, c_size, vp], c_int),
+        "linear_scan_workspace_size": ([c_int, c_int, c_int, c_int, ctypes.POINTER(c_size)], c_int),
+        "linear_scan_diag": ([vp, vp, vp, vp, c_int, c_int, c_int, vp, c_size, vp], c_int),
+        "linear_scan_dense": ([vp, vp, vp, vp, c_int, c_int, c_int, vp, c_size, vp], c_int),
+        "deer_rollout": ([ctypes.POINTER(CellParams), vp, vp, c_int, c_int, vp, vp], c_int),
+        "deer_profile_enable": ([c_int], c_int),
+        "deer_profile_read": ([c_int, ctypes.POINTER(ctypes.c_longlong), ctypes.POINTER(ctypes.c_double)], c_int),
+        "deer_last_error": ([], ctypes.c_char_p),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    _lib = lib
+    return lib
+
+
+def _check(rc: int, allow_nc: bool = False) -> int:
+    if rc == DEER_OK or (allow_nc and rc == DEER_NOT_CONVERGED):
+        return rc
+    raise DeerError(rc, load_library().deer_last_error().decode())
+
+
+def _stream(stream=None):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t, name, dtype=None, shape=None):
+    """Device pointer of a contiguous float32 CUDA tensor (or None)."""
+    import torch
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != (dtype or torch.float32):
+        raise TypeError(f"{name} must be {dtype or torch.float32}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+@dataclass
+class Cell:
+    """Cell parameters on the device (float32, contiguous).
+
+    tanh: ``W [D,D]``, ``U [D,M]``, ``b [D]`` or None.
+    GRU:  ``W`` = W_hh ``[3D,D]``, ``U`` = W_ih ``[3D,M]``, ``b`` = b_ih, ``b2`` = b_hh.
+    """
+
+    cell: str
+    W: "object"
+    U: "object"
+    b: "object" = None
+    b2: "object" = None
+
+    @property
+    def D(self) -> int:
+        return int(self.W.shape[1])
+
+    @property
+    def M(self) -> int:
+        return int(self.U.shape[1])
+
+    def params(self) -> CellParams:
+        rows = 3 * self.D if self.cell == "gru" else self.D
+        _dev(self.W, "W", shape=(rows, self.D))
+        _dev(self.U, "U", shape=(rows, self.M))
+        _dev(self.b, "b", shape=(rows,))
+        if self.cell == "gru":
+            _dev(self.b2, "b2", shape=(rows,))
+        return CellParams(CELLS[self.cell], self.D, self.M, _dev(self.W, "W"), _dev(self.U, "U"),
+                          _dev(self.b, "b"), _dev(self.b2, "b2") if self.cell == "gru" else None)
+
+
+# ------------------------------------------------------------- workspaces
+
+def deer_workspace_size(cell: Cell, B: int, T: int, mode: str) -> int:
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    p = cell.params()
+    _check(lib.deer_workspace_size(ctypes.byref(p), B, T, MODES[mode], ctypes.byref(n)))
+    return int(n.value)
+
+
+def linear_scan_workspace_size(B: int, T: int, D: int, dense: bool = False) -> int:
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    _check(lib.linear_scan_workspace_size(B, T, D, int(dense), ctypes.byref(n)))
+    return int(n.value)
+
+
+def new_workspace(nbytes: int, device=None):
+    """A zero-filled, 256-byte aligned device workspace (torch allocation)."""
+    import torch
+    n = max(int(nbytes), 256)
+    ws = torch.zeros(n, dtype=torch.uint8, device=device or "cuda")
+    if ws.data_ptr() % 256 != 0:
+        raise RuntimeError("workspace allocation is not 256-byte aligned")
+    return ws
+
+
+def deer_workspace_init(ws, stream=None) -> None:
+    lib = load_library()
+    _check(lib.deer_workspace_init(_dev(ws, "workspace", dtype=ws.dtype), ws.numel() * ws.element_size(),
+                                   _stream(stream)))
+
+
+# ---------------------------------------------------------------- solvers
+
+def deer_solve(cell: Cell, x, s0=None, mode: str = "dense", tol: float = 1e-6, max_iter: int = 100,
+               init_guess=None, out=None, workspace=None, stream=None):
+    """Parallel Newton / quasi-Newton solve; returns ``(traj, iters, resid, status, rc)``.
+
+    ``traj`` is a ``[B,T,D]`` CUDA tensor; ``iters``, ``status`` are numpy int32
+    ``[B]``, ``resid`` numpy float32 ``[B]``; ``rc`` is DEER_OK or
+    DEER_NOT_CONVERGED.
+    """
+    import numpy as np
+    import torch
+    lib = load_library()
+    B, T, M = (int(v) for v in x.shape)
+    D = cell.D
+    if M != cell.M:
+        raise ValueError(f"x has input size {M}, the cell expects {cell.M}")
+    p = cell.params()
+    if out is None:
+        out = torch.empty((B, T, D), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = new_workspace(deer_workspace_size(cell, B, T, mode), device=x.device)
+    iters = np.zeros(B, np.int32)
+    resid = np.zeros(B, np.float32)
+    status = np.zeros(B, np.int32)
+    rc = lib.deer_solve(ctypes.byref(p), _dev(x, "x", shape=(B, T, M)), _dev(s0, "s0", shape=(B, D)), B, T,
+                        MODES[mode], ctypes.c_float(tol), int(max_iter),
+                        _dev(init_guess, "init_guess", shape=(B, T, D)), _dev(out, "out", shape=(B, T, D)),
+                        iters.ctypes.data_as(ctypes.c_void_p), resid.ctypes.data_as(ctypes.c_void_p),
+                        status.ctypes.data_as(ctypes.c_void_p),
+                        _dev(workspace, "workspace", dtype=workspace.dtype),
+                        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, allow_nc=True)
+    return out, iters, resid, status, rc
+
+
+def linear_scan_diag(a, b, s0=None, out=None, workspace=None, stream=None):
+    """``s_t = a_t * s_{t-1} + b_t`` over ``[B,T,D]`` tensors; returns ``s``."""
+    import torch
+    lib = load_library()
+    B, T, D = (int(v) for v in a.shape)
+    if out is None:
+        out = torch.empty_like(a)
+    if workspace is None:
+        workspace = new_workspace(linear_scan_workspace_size(B, T, D), device=a.device)
+    _check(lib.linear_scan_diag(_dev(a, "a"), _dev(b, "b", shape=(B, T, D)), _dev(s0, "s0", shape=(B, D)),
+                                _dev(out, "out", shape=(B, T, D)), B, T, D,
+                                _dev(workspace, "workspace", dtype=workspace.dtype),
+                                workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def linear_scan_dense(A, b, s0=None, out=None, workspace=None, stream=None):
+    """``s_t = A_t s_{t-1} + b_t`` with ``A [B,T,D,D]``; returns ``s [B,T,D]``."""
+    import torch
+    lib = load_library()
+    B, T, D = (int(v) for v in b.shape)
+    if out is None:
+        out = torch.empty_like(b)
+    if workspace is None:
+        workspace = new_workspace(linear_scan_workspace_size(B, T, D, dense=True), device=b.device)
+    _check(lib.linear_scan_dense(_dev(A, "A", shape=(B, T, D, D)), _dev(b, "b"), _dev(s0, "s0", shape=(B, D)),
+                                 _dev(out, "out", shape=(B, T, D)), B, T, D,
+                                 _dev(workspace, "workspace", dtype=workspace.dtype),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def deer_rollout(cell: Cell, x, s0=None, out=None, stream=None):
+    """Sequential rollout on the GPU; returns ``traj [B,T,D]``."""
+    import torch
+    lib = load_library()
+    B, T, M = (int(v) for v in x.shape)
+    p = cell.params()
+    if out is None:
+        out = torch.empty((B, T, cell.D), dtype=torch.float32, device=x.device)
+    _check(lib.deer_rollout(ctypes.byref(p), _dev(x, "x", shape=(B, T, M)), _dev(s0, "s0", shape=(B, cell.D)),
+                            B, T, _dev(out, "out", shape=(B, T, cell.D)), _stream(stream)))
+    return out
+
+
+def deer_profile_enable(enable: bool = True) -> None:
+    _check(load_library().deer_profile_enable(int(enable)))
+
+
+def deer_profile_read(which: int) -> Tuple[int, float]:
+    """``(launches, milliseconds)`` timed for a kernel class since the last read."""
+    n = ctypes.c_longlong(0)
+    ms = ctypes.c_double(0.0)
+    _check(load_library().deer_profile_read(int(which), ctypes.byref(n), ctypes.byref(ms)))
+    return int(n.value), float(ms.value)
+
+
+PROFILE_EVAL, PROFILE_SCAN, PROFILE_PROJECTION, PROFILE_CHECK = 0, 1, 2, 3
+
+
+def cell_from_problem(p: dict, device="cuda") -> Cell:
+    """Move a problem's float32 parameters (``inputs`` module) to the device."""
+    import torch
+
+    def t(a):
+        return None if a is None else torch.from_numpy(a).to(device)
+
+    return Cell(p["cell"], t(p["W"]), t(p["U"]), t(p.get("b")), t(p.get("b2")) if p["cell"] == "gru" else None)

@@ -1,0 +1,189 @@
+/*
+ * deer.h -- C interface of the MI355X (gfx950) parallel Newton solver for
+ * nonlinear recurrences.
+ *
+ * The problem ("Parallel Broyden Methods for Efficiently Evaluating Nonlinear
+ * State Space Models", section 2, problem statement): given a transition
+ * s_t = f(s_{t-1}, x_t), inputs x_1..x_T and a fixed s_0, find the trajectory
+ * s_1..s_T as the root of the residual r_t(s) = s_t - f(s_{t-1}, x_t)
+ * ("Predictability Enables Parallelization of Nonlinear State Space Models",
+ * rebuttal, its equation 2).  Each Newton iteration linearises f around the
+ * current guess, s_t ~ A_t s_{t-1} + b_t, and solves that linear recurrence
+ * with a parallel associative scan; A_t is the full Jacobian (DEER, dense
+ * mode) or its diagonal (quasi-DEER, diag mode).
+ *
+ * Conventions for every call:
+ *   - float32, row-major, contiguous; sequences are laid out [B, T, D] with D
+ *     fastest.  Time index t = 0..T-1 holds the state after step t+1.
+ *   - Pointers named "device" must be device memory of the current HIP device
+ *     (hipMalloc / torch CUDA tensors); "host" pointers are ordinary memory.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  All work
+ *     is enqueued on it; outputs are complete once the stream is synchronised.
+ *   - The library never allocates or frees caller memory and keeps no pointer
+ *     after a call returns.  Scratch memory comes from the caller's workspace.
+ *   - Return value: DEER_OK (0) on success, DEER_NOT_CONVERGED (1) when
+ *     deer_solve ran to max_iter for at least one sequence (a result, not an
+ *     error), a negative DEER_ERR_* code otherwise.  After a negative return
+ *     deer_last_error() describes the problem.  Nothing is thrown across the
+ *     interface.
+ *   - One workspace must not be used by two calls that may run at the same
+ *     time (different streams or threads).
+ */
+#ifndef DEER_H_
+#define DEER_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum deer_mode { DEER_MODE_DENSE = 0, DEER_MODE_DIAG = 1 };
+enum deer_cell { DEER_CELL_TANH = 0, DEER_CELL_GRU = 1 };
+
+enum deer_status {
+    DEER_OK = 0,
+    DEER_NOT_CONVERGED = 1,
+    DEER_ERR_INVALID = -1,      /* bad pointer, size or flag */
+    DEER_ERR_UNSUPPORTED = -2,  /* shape or cell/mode pair outside the supported set */
+    DEER_ERR_WORKSPACE = -3,    /* workspace missing, too small or misaligned */
+    DEER_ERR_HIP = -4,          /* a HIP runtime call failed */
+    DEER_ERR_DEVICE = -5        /* a kernel reported an internal failure (see deer_last_error) */
+};
+
+/* Per-sequence outcome written to status_out[b] by deer_solve. */
+enum deer_seq_status {
+    DEER_SEQ_CONVERGED = 0,      /* residual <= tol after iters_out[b] iterations */
+    DEER_SEQ_NOT_CONVERGED = 1,  /* max_iter reached with a finite residual */
+    DEER_SEQ_NONFINITE = 2       /* max_iter reached with a NaN / Inf residual */
+};
+
+/*
+ * Cell parameters (device pointers, float32).
+ *   tanh:  f(s, x) = tanh(W s + U x + b)   -- the vector form of the scalar
+ *          tanh model on the "Predictability" page (rebuttal, "Application to
+ *          RNN training efficiency").  W [D,D], U [D,M], b [D] or NULL (zeros);
+ *          b2 unused.
+ *   GRU:   gate order (r, z, n); W = W_hh [3D,D], U = W_ih [3D,M],
+ *          b = b_ih [3D] or NULL, b2 = b_hh [3D] or NULL:
+ *            r = sigmoid(W_ih,r x + b_ih,r + W_hh,r s + b_hh,r)
+ *            z = sigmoid(W_ih,z x + b_ih,z + W_hh,z s + b_hh,z)
+ *            n = tanh(W_ih,n x + b_ih,n + r * (W_hh,n s + b_hh,n))
+ *            f = (1 - z) * n + z * s
+ *          (the GRU is only cited on the pages; these are its textbook
+ *          equations).
+ * Supported: 1 <= D <= 64, 1 <= M <= 1024.  tanh in dense or diag mode, GRU in
+ * diag mode.
+ */
+typedef struct {
+    int cell;        /* enum deer_cell */
+    int D;           /* state size */
+    int M;           /* input size */
+    const float *W;
+    const float *U;
+    const float *b;
+    const float *b2;
+} deer_cell_params_t;
+
+/*
+ * Bytes of device workspace deer_solve needs for this problem (host output).
+ * Returns DEER_OK, or an error for an unsupported problem.
+ */
+int deer_workspace_size(const deer_cell_params_t *p, int B, int T, int mode, size_t *bytes_out);
+
+/*
+ * Zero-fill a workspace on `stream`.  Every workspace (for deer_solve,
+ * linear_scan_diag or linear_scan_dense) must be zero-filled once before its
+ * first use -- by this call or any other zero fill; the calls themselves leave
+ * it ready for the next call.  `workspace` device, 256-byte aligned.
+ */
+int deer_workspace_init(void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Solve for the trajectory by parallel Newton (mode DEER_MODE_DENSE) or
+ * diagonal quasi-Newton (DEER_MODE_DIAG) iterations ("Parallel Broyden
+ * Methods", section 2: exact parallel Newton and diagonal quasi-Newton;
+ * finite-step recovery, Theorem 1 of section 3.2).
+ *
+ *   p           cell parameters (host struct holding device pointers)
+ *   x           device [B,T,M] inputs
+ *   s0          device [B,D] initial states, or NULL for zeros
+ *   tol         stop when max_{t,d} |s_t - f(s_{t-1}, x_t)| <= tol for a
+ *               sequence (absolute L-infinity residual, tested on each iterate
+ *               before it is refined; NaN never passes)
+ *   max_iter    iteration cap (>= 0); at most T iterations are ever needed in
+ *               exact arithmetic
+ *   init_guess  device [B,T,D] starting trajectory, or NULL for zeros
+ *   traj_out    device [B,T,D]: per sequence the first iterate that passed the
+ *               test, or the iterate after max_iter iterations
+ *   iters_out   host [B]: iterations (linearise + solve steps) applied
+ *   resid_out   host [B] or NULL: the residual of the returned iterate
+ *   status_out  host [B] or NULL: enum deer_seq_status per sequence
+ *   workspace   device, >= deer_workspace_size bytes, 256-byte aligned,
+ *               zero-filled before its first use (deer_workspace_init)
+ * Sequences are independent: each stops on its own and is frozen there.
+ * The call enqueues its kernels on `stream`, polls a convergence flag on the
+ * device once per batch of iterations (no per-iteration host sync), and
+ * returns after the outputs are complete.
+ */
+int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int B, int T,
+               int mode, float tol, int max_iter, const float *init_guess, float *traj_out,
+               int *iters_out, float *resid_out, int *status_out, void *workspace, size_t ws_bytes,
+               void *stream);
+
+/*
+ * Bytes of workspace linear_scan_diag / linear_scan_dense need (host output).
+ */
+int linear_scan_workspace_size(int B, int T, int D, int dense, size_t *bytes_out);
+
+/*
+ * Inclusive scan of the diagonal affine recurrence s_t = a_t * s_{t-1} + b_t
+ * (elementwise per channel), s_{-1} = s0 ("Parallel Broyden Methods",
+ * section 2, diagonal quasi-Newton: diagonal blocks stay diagonal under
+ * composition; merge rule of appendix C.2).
+ *   a, b   device [B,T,D];  s0 device [B,D] or NULL (zeros);  s device [B,T,D]
+ *   (s may alias neither a nor b).  One pass: reads a and b once, writes s once.
+ *   Any B, T >= 0, 1 <= D.
+ */
+int linear_scan_diag(const float *a, const float *b, const float *s0, float *s, int B, int T, int D,
+                     void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Scan of the dense affine recurrence s_t = A_t s_{t-1} + b_t, s_{-1} = s0,
+ * with D x D blocks A_t (row-major, A_t[i][k] multiplies s_{t-1}[k]); later
+ * blocks multiply on the left when segments merge ("Parallel Broyden
+ * Methods", appendix C.2).
+ *   A device [B,T,D,D];  b device [B,T,D];  s0 device [B,D] or NULL;
+ *   s device [B,T,D].  1 <= D <= 64.
+ */
+int linear_scan_dense(const float *A, const float *b, const float *s0, float *s, int B, int T,
+                      int D, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Sequential rollout s_t = f(s_{t-1}, x_t) on the GPU, one step after the
+ * other (the evaluation the parallel methods are timed against on the
+ * "Predictability" page, rebuttal "Comparison with sequential speed").
+ *   x device [B,T,M];  s0 device [B,D] or NULL;  traj_out device [B,T,D].
+ */
+int deer_rollout(const deer_cell_params_t *p, const float *x, const float *s0, int B, int T,
+                 float *traj_out, void *stream);
+
+/*
+ * Per-kernel timing of deer_solve, for measurement.  While enabled, deer_solve
+ * records a pair of HIP events on its stream around every launch of the named
+ * kernel class and accumulates the elapsed time; reading returns the number of
+ * launches timed and their summed milliseconds and resets the counters.
+ *   which: 0 = cell evaluation (f and Jacobian), 1 = linear scan,
+ *          2 = input projection, 3 = convergence check.
+ */
+int deer_profile_enable(int enable);
+int deer_profile_read(int which, long long *launches, double *milliseconds);
+
+/* Thread-local description of the last failure (never NULL). */
+const char *deer_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DEER_H_ */

@@ -46,9 +46,9 @@ struct Carve {
 
 // ------------------------------------------------------ diagonal scan state
 // Look-back state kept in a workspace between launches.  Zero-filled once by
-// the caller; every launch leaves ticket = done = 0 and advances epoch.
+// the caller; every launch leaves done = 0 and advances epoch.
 struct ScanHeader {
-    unsigned ticket;   // next chunk ticket (launch order of workgroups)
+    unsigned reserved;
     unsigned done;     // workgroups finished in the current launch
     unsigned epoch;    // tags descriptors of the current launch
     unsigned abort;    // set if a bounded wait gave up (should never happen)
@@ -60,8 +60,9 @@ static_assert(sizeof(ScanHeader) == 256, "header is one alignment unit");
 struct DiagScanPlan {
     int B, T, D;
     int vec;        // 4 when D % 4 == 0, else 1
+    int ch;         // channels per tile
     int chunk_len;  // time steps per chunk
-    int groups;     // channel groups of 64 per sequence
+    int groups;     // channel tiles per sequence
     int chains;     // B * groups
     int nchunk;     // chunks per chain
     size_t desc_words;
@@ -113,7 +114,7 @@ int launch_gru_eval(const float *Whh, const float *bhh, const float *p, const fl
                     const int *all_done, float *a, float *bvec, unsigned *res_bits, int B, int T,
                     int D, hipStream_t stream);
 
-int launch_rollout(const deer_cell_params_t *p, const float *proj, const float *s0, int B, int T,
+int launch_rollout(const deer_cell_params_t *p, const float *x, const float *s0, int B, int T,
                    float *traj, hipStream_t stream);
 
 }  // namespace deer

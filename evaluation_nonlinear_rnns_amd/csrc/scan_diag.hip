@@ -6,34 +6,42 @@
 //     (a_j, b_j) o (a_i, b_i) = (a_j a_i, a_j b_i + b_j)   (i before j),
 // the later map acting on the left (same page, appendix C.2).
 //
-// Layout [B, T, D], D fastest.  A workgroup owns one tile of 64 channels x L
-// time steps of one sequence (a "chunk"):
+// Layout [B, T, D], D fastest.  The grid is persistent: one workgroup per
+// compute unit (more if occupancy allows), each walking the chunks
+// blockIdx.x, blockIdx.x + G, ... in order.  A chunk is a tile of CH
+// channels x L time steps of one sequence:
 //   1. every thread loads LT consecutive steps of VEC channels into registers
-//      (non-temporal 16-byte loads, 256-byte contiguous row segments) and folds
-//      them into one affine pair per channel;
+//      (non-temporal 16-byte loads; a wavefront reads whole contiguous row
+//      segments, 1 KB for 256-channel tiles) and folds them into one affine
+//      pair per channel;
 //   2. the time slots of the workgroup are combined through LDS (exclusive
 //      prefix per slot, chunk aggregate per channel);
-//   3. wave 0 publishes the chunk aggregate, looks back over earlier chunks of
-//      the same channels (decoupled look-back) until it meets an inclusive
+//   3. the chunk publishes its aggregate, looks back over the earlier chunks
+//      of the same channels (decoupled look-back) until it meets an inclusive
 //      prefix, and publishes its own inclusive prefix (the state at the
 //      chunk's last step);
 //   4. every thread replays its registers from the carried-in state and
 //      streams s out (non-temporal stores).
-// a and b are read once and s written once: 12 bytes per element.
+// a and b are read once and s written once: 12 bytes per element.  Holding
+// 32 steps per thread keeps about 1 KB of loads in flight per thread, which
+// is what it takes to approach the HBM roofline on this part; with one
+// workgroup per compute unit there are no per-chunk atomics at all.
 //
 // Look-back descriptors are 64-bit words holding a float and a 32-bit tag
 // (epoch * 4 + kind), written and read with agent-scope atomics, so a word is
-// valid on its own and no fences are needed.  Chunks are numbered by an atomic
-// ticket taken at workgroup start, so every chunk's predecessors are already
-// resident or finished: the look-back always makes progress.  Its wait is
-// bounded all the same; if the bound is hit the header's abort flag is set and
-// the chunk's carry becomes NaN.
+// valid on its own and no fences are needed.  Forward progress: a workgroup
+// only waits on chunks with smaller indices, each workgroup takes its chunks
+// in increasing order, and all workgroups of the persistent grid are resident
+// together, so the smallest waiting chunk's predecessor is always being
+// processed.  The wait is bounded all the same; if the bound is hit the
+// header's abort flag is set and the chunk's carry becomes NaN.
+#include <algorithm>
+
 #include "internal.h"
 
 namespace deer {
 namespace {
 
-constexpr int kCH = 64;          // channels per chunk tile
 constexpr int kThreads = 256;
 constexpr unsigned kSpinLimit = 1u << 22;
 
@@ -52,49 +60,44 @@ __device__ __forceinline__ void store_word(unsigned long long *p, unsigned long 
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int VEC, int LT>
+template <int VEC, int CH, int LT>
 struct DiagGeom {
-    static constexpr int LD = kCH / VEC;       // threads across a tile row
+    static constexpr int LD = CH / VEC;        // threads across a tile row
     static constexpr int NS = kThreads / LD;   // time slots per workgroup
     static constexpr int L = NS * LT;          // time steps per chunk
 };
 
-template <int VEC, int LT>
+template <int VEC, int CH, int LT>
 __global__ __launch_bounds__(kThreads) void diag_scan_kernel(
     const float *__restrict__ a, const float *__restrict__ b, const float *__restrict__ s0,
     float *out0, float *out1, const int *__restrict__ out_sel, const int *__restrict__ skip,
     const int *__restrict__ all_done, int T, int D, int groups, int chains, int nchunk,
     ScanHeader *__restrict__ hdr, unsigned long long *__restrict__ desc)
 {
-    using G = DiagGeom<VEC, LT>;
+    using G = DiagGeom<VEC, CH, LT>;
     constexpr int LD = G::LD, NS = G::NS, L = G::L;
 
     if (all_done && *all_done) return;   // same value for every workgroup of the launch
 
-    __shared__ unsigned sh_ticket, sh_epoch;
-    __shared__ float shA[NS][kCH];
-    __shared__ float shB[NS][kCH];
-    __shared__ float shC[kCH];
+    __shared__ float shA[NS][CH];
+    __shared__ float shB[NS][CH];
+    __shared__ float shC[CH];
 
     const int tid = threadIdx.x;
-    if (tid == 0) {
-        sh_ticket = __hip_atomic_fetch_add(&hdr->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        sh_epoch = __hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    const unsigned ticket = sh_ticket;
-    const unsigned epoch = sh_epoch;
+    const unsigned epoch = __hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const unsigned tag_agg = epoch * 4u + 1u, tag_inc = epoch * 4u + 2u;
-    const int tchunk = static_cast<int>(ticket / static_cast<unsigned>(chains));
-    const int chain = static_cast<int>(ticket % static_cast<unsigned>(chains));
-    const int bseq = chain / groups;
-    const int grp = chain % groups;
+    float *out = (out_sel && (*out_sel & 1)) ? out1 : out0;
+    const int slot = tid / LD;
+    const int lc = (tid % LD) * VEC;              // channel offset inside the tile
+    const long long total = static_cast<long long>(chains) * nchunk;
 
-    if (!(skip && skip[bseq])) {
-        float *out = (out_sel && (*out_sel & 1)) ? out1 : out0;
-        const int slot = tid / LD;
-        const int lc = (tid % LD) * VEC;          // channel offset inside the tile
-        const int c0 = grp * kCH + lc;            // first channel of this thread
+    for (long long cidx = blockIdx.x; cidx < total; cidx += gridDim.x) {
+        const int tchunk = static_cast<int>(cidx / chains);
+        const int chain = static_cast<int>(cidx % chains);
+        const int bseq = chain / groups;
+        const int grp = chain % groups;
+        if (skip && skip[bseq]) continue;         // uniform over the workgroup
+        const int c0 = grp * CH + lc;             // first channel of this thread
         const bool cvalid = c0 < D;               // VEC == 4 implies D % 4 == 0
         const int t0 = tchunk * L + slot * LT;
         const size_t seq = static_cast<size_t>(bseq) * T * D;
@@ -131,6 +134,7 @@ __global__ __launch_bounds__(kThreads) void diag_scan_kernel(
                 Bq[v] = av[j][v] * Bq[v] + bv[j][v];
                 A[v] = av[j][v] * A[v];
             }
+        __syncthreads();   // the previous chunk is done with the LDS tiles
 #pragma unroll
         for (int v = 0; v < VEC; ++v) { shA[slot][lc + v] = A[v]; shB[slot][lc + v] = Bq[v]; }
         __syncthreads();
@@ -147,9 +151,9 @@ __global__ __launch_bounds__(kThreads) void diag_scan_kernel(
                 PA[v] = ak * PA[v];
             }
 
-        if (tid < kCH) {   // wave 0: one channel per lane
-            const int c = tid;
-            const int ch = grp * kCH + c;
+        // one channel per thread: publish, look back, publish
+        for (int c = tid; c < CH; c += kThreads) {
+            const int ch = grp * CH + c;
             float carry = 0.0f;
             if (ch < D) {
                 float GA = 1.0f, GB = 0.0f;
@@ -158,24 +162,24 @@ __global__ __launch_bounds__(kThreads) void diag_scan_kernel(
                     GB = ak * GB + shB[k][c];
                     GA = ak * GA;
                 }
-                unsigned long long *mine = desc + (static_cast<size_t>(chain) * nchunk + tchunk) * 3 * kCH;
+                unsigned long long *mine = desc + (static_cast<size_t>(chain) * nchunk + tchunk) * 3 * CH;
                 if (tchunk == 0) {
                     carry = s0 ? s0[static_cast<size_t>(bseq) * D + ch] : 0.0f;
                 } else {
                     store_word(mine + c, pack_word(GA, tag_agg));
-                    store_word(mine + kCH + c, pack_word(GB, tag_agg));
+                    store_word(mine + CH + c, pack_word(GB, tag_agg));
                     float accA = 1.0f, accB = 0.0f;   // maps s_end(j) to s_end(tchunk - 1)
                     int j = tchunk - 1;
                     unsigned spins = 0;
                     while (true) {
-                        const unsigned long long *pj = desc + (static_cast<size_t>(chain) * nchunk + j) * 3 * kCH;
-                        const unsigned long long wi = load_word(pj + 2 * kCH + c);
+                        const unsigned long long *pj = desc + (static_cast<size_t>(chain) * nchunk + j) * 3 * CH;
+                        const unsigned long long wi = load_word(pj + 2 * CH + c);
+                        const unsigned long long wa = load_word(pj + c);
+                        const unsigned long long wb = load_word(pj + CH + c);
                         if (word_tag(wi) == tag_inc) {
                             carry = accA * word_val(wi) + accB;
                             break;
                         }
-                        const unsigned long long wa = load_word(pj + c);
-                        const unsigned long long wb = load_word(pj + kCH + c);
                         if (word_tag(wa) == tag_agg && word_tag(wb) == tag_agg) {
                             accB = accA * word_val(wb) + accB;
                             accA = accA * word_val(wa);
@@ -193,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void diag_scan_kernel(
                         __builtin_amdgcn_s_sleep(1);
                     }
                 }
-                store_word(mine + 2 * kCH + c, pack_word(GA * carry + GB, tag_inc));
+                store_word(mine + 2 * CH + c, pack_word(GA * carry + GB, tag_inc));
             }
             shC[c] = carry;
         }
@@ -220,16 +224,52 @@ __global__ __launch_bounds__(kThreads) void diag_scan_kernel(
         }
     }
 
-    // Last workgroup out resets the ticket/done counters and advances the epoch.
+    // Last workgroup out resets the done counter and advances the epoch.
     __syncthreads();
     if (tid == 0) {
         const unsigned prev = __hip_atomic_fetch_add(&hdr->done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
         if (prev == gridDim.x - 1) {
-            __hip_atomic_store(&hdr->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(&hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(&hdr->epoch, epoch + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
+}
+
+// Tile shapes: 256-channel tiles (a wavefront reads 1 KB rows) for wide
+// states, 64-channel tiles otherwise; scalar lanes when D is not a multiple of 4.
+enum DiagKind { kWide = 0, kNarrow = 1, kScalar = 2 };
+constexpr int kLT = 32;
+using GeomWide = DiagGeom<4, 256, kLT>;
+using GeomNarrow = DiagGeom<4, 64, kLT>;
+using GeomScalar = DiagGeom<1, 64, kLT>;
+
+DiagKind diag_kind(int D)
+{
+    if (D % 4 != 0) return kScalar;
+    return (D >= 256 || D % 256 == 0) ? kWide : kNarrow;
+}
+
+// Resident workgroups per compute unit, times compute units (cached per device).
+int persistent_capacity(DiagKind k)
+{
+    static int cache[64][3] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int &slot = cache[dev][k];
+    if (slot == 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+        hipError_t e = hipSuccess;
+        if (k == kWide)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, diag_scan_kernel<4, 256, kLT>, kThreads, 0);
+        else if (k == kNarrow)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, diag_scan_kernel<4, 64, kLT>, kThreads, 0);
+        else
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, diag_scan_kernel<1, 64, kLT>, kThreads, 0);
+        if (e != hipSuccess || per_cu < 1) per_cu = 1;
+        slot = cus * per_cu;
+    }
+    return slot;
 }
 
 constexpr int kLT4 = 16;   // VEC = 4: 16 slots x 16 steps = 256 steps per chunk
@@ -243,12 +283,14 @@ DiagScanPlan diag_scan_plan(int B, int T, int D)
     p.B = B;
     p.T = T;
     p.D = D;
-    p.vec = (D % 4 == 0) ? 4 : 1;
-    p.chunk_len = (p.vec == 4) ? DiagGeom<4, kLT4>::L : DiagGeom<1, kLT1>::L;
-    p.groups = (D + kCH - 1) / kCH;
+    const DiagKind k = diag_kind(D);
+    p.vec = (k == kScalar) ? 1 : 4;
+    p.ch = (k == kWide) ? 256 : 64;
+    p.chunk_len = (k == kWide) ? GeomWide::L : (k == kNarrow) ? GeomNarrow::L : GeomScalar::L;
+    p.groups = (D + p.ch - 1) / p.ch;
     p.chains = B * p.groups;
     p.nchunk = (T + p.chunk_len - 1) / p.chunk_len;
-    p.desc_words = static_cast<size_t>(p.chains) * p.nchunk * 3 * kCH;
+    p.desc_words = static_cast<size_t>(p.chains) * p.nchunk * 3 * p.ch;
     return p;
 }
 
@@ -262,21 +304,22 @@ int launch_diag_scan(const float *a, const float *b, const float *s0, float *out
                      const int *out_sel, const int *skip, const int *all_done, int B, int T, int D,
                      void *state, hipStream_t stream)
 {
-    const DiagScanPlan p = diag_scan_plan(B, T, D);
     if (B == 0 || T == 0) return DEER_OK;
-    const size_t blocks = static_cast<size_t>(p.chains) * p.nchunk;
-    if (blocks > 0x7fffffffull) return fail(DEER_ERR_UNSUPPORTED, "linear scan: problem too large for one launch");
+    const DiagScanPlan p = diag_scan_plan(B, T, D);
+    const long long total = static_cast<long long>(p.chains) * p.nchunk;
+    const DiagKind k = diag_kind(D);
+    const unsigned grid = static_cast<unsigned>(std::min<long long>(total, persistent_capacity(k)));
     auto *hdr = static_cast<ScanHeader *>(state);
     auto *desc = reinterpret_cast<unsigned long long *>(static_cast<char *>(state) + sizeof(ScanHeader));
-    if (p.vec == 4) {
-        hipLaunchKernelGGL((diag_scan_kernel<4, kLT4>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
-                           stream, a, b, s0, out0, out1, out_sel, skip, all_done, T, D, p.groups, p.chains,
-                           p.nchunk, hdr, desc);
-    } else {
-        hipLaunchKernelGGL((diag_scan_kernel<1, kLT1>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
-                           stream, a, b, s0, out0, out1, out_sel, skip, all_done, T, D, p.groups, p.chains,
-                           p.nchunk, hdr, desc);
-    }
+    if (k == kWide)
+        hipLaunchKernelGGL((diag_scan_kernel<4, 256, kLT>), dim3(grid), dim3(kThreads), 0, stream, a, b, s0, out0,
+                           out1, out_sel, skip, all_done, T, D, p.groups, p.chains, p.nchunk, hdr, desc);
+    else if (k == kNarrow)
+        hipLaunchKernelGGL((diag_scan_kernel<4, 64, kLT>), dim3(grid), dim3(kThreads), 0, stream, a, b, s0, out0,
+                           out1, out_sel, skip, all_done, T, D, p.groups, p.chains, p.nchunk, hdr, desc);
+    else
+        hipLaunchKernelGGL((diag_scan_kernel<1, 64, kLT>), dim3(grid), dim3(kThreads), 0, stream, a, b, s0, out0,
+                           out1, out_sel, skip, all_done, T, D, p.groups, p.chains, p.nchunk, hdr, desc);
     DEER_HIP(hipGetLastError());
     return DEER_OK;
 }

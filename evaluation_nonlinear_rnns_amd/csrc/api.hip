@@ -257,7 +257,7 @@ SolveLayout solve_layout(void *ws, const deer_cell_params_t *p, int B, int T, in
     L.buf1 = c.take<float>(BTD);
     L.lin = c.take<float>(BTD);
     L.bvec = c.take<float>(BTD);
-    L.proj = c.take<float>(static_cast<size_t>(B) * T * PD);
+    L.proj = c.take<float>(projection_floats(B, T, PD));
     L.bytes = c.off;
     return L;
 }
@@ -428,7 +428,7 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
 
     // iteration-invariant input projection (W_ih x + b_ih for the GRU, U x + b for tanh)
     prof.begin(2);
-    rc = launch_projection(x, p->U, p->b, L.proj, B * T, p->M, PD, stream);
+    rc = launch_projection(x, p->U, p->b, L.proj, B, T, p->M, PD, gru && gru_fast_path(D, p->M), stream);
     prof.end();
     if (rc) return rc;
 
@@ -439,7 +439,7 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
         prof.begin(0);
         if (gru)
             r = launch_gru_eval(p->W, p->b2, L.proj, s0, traj_out, L.buf1, sel, L.done, all_done, L.lin, L.bvec,
-                                L.res_bits, B, T, D, stream);
+                                L.res_bits, B, T, D, p->M, stream);
         else
             r = launch_tanh_eval(p->W, L.proj, s0, traj_out, L.buf1, sel, L.done, all_done, L.lin, L.bvec,
                                  L.res_bits, B, T, D, mode == DEER_MODE_DENSE, stream);

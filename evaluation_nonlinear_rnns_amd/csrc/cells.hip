@@ -13,6 +13,8 @@
 // state rows it needs (s_{t0-1} .. s_{t0+TP-1}) and the transposed recurrent
 // weights sit in LDS; lane c of a lane group handles channel c, so every global
 // access is a contiguous row segment.
+#include <algorithm>
+
 #include "internal.h"
 
 namespace deer {
@@ -315,11 +317,20 @@ unsigned eval_blocks(int B, int T, int &tiles)
 
 }  // namespace
 
-int launch_projection(const float *x, const float *U, const float *bias, float *p, int N, int M, int O,
-                      hipStream_t stream)
+size_t projection_floats(int B, int T, int O)
 {
-    if (N == 0) return DEER_OK;
+    return std::max(static_cast<size_t>(B) * T * O, proj_tiled_floats(B, T, O));
+}
+
+bool gru_fast_path(int D, int M) { return gru_mfma_supported(D) && proj_mfma_supported(M, 3 * D); }
+
+int launch_projection(const float *x, const float *U, const float *bias, float *p, int B, int T, int M, int O,
+                      bool tiled, hipStream_t stream)
+{
+    if (B == 0 || T == 0) return DEER_OK;
+    if (tiled || proj_mfma_supported(M, O)) return launch_projection_mfma(x, U, bias, p, B, T, M, O, tiled, stream);
     if (O > 192) return fail(DEER_ERR_UNSUPPORTED, "projection: more than 192 outputs");
+    const int N = B * T;
     const int row_tiles = 4;
     const long long rows_per_block = 32ll * row_tiles;
     const unsigned blocks = static_cast<unsigned>((N + rows_per_block - 1) / rows_per_block);
@@ -366,8 +377,11 @@ int launch_tanh_eval(const float *W, const float *p, const float *s0, const floa
 
 int launch_gru_eval(const float *Whh, const float *bhh, const float *p, const float *s0, const float *s_even,
                     const float *s_odd, const int *sel, const int *skip, const int *all_done, float *a, float *bvec,
-                    unsigned *res_bits, int B, int T, int D, hipStream_t stream)
+                    unsigned *res_bits, int B, int T, int D, int M, hipStream_t stream)
 {
+    if (gru_fast_path(D, M))
+        return launch_gru_eval_mfma(Whh, bhh, p, s0, s_even, s_odd, sel, skip, all_done, a, bvec, res_bits, B, T, D,
+                                    stream);
     int tiles;
     const unsigned blocks = eval_blocks(B, T, tiles);
     if (blocks == 0) return DEER_OK;

@@ -95,8 +95,12 @@ int launch_dense_scan(const float *A, const float *d, const float *W, const floa
                       hipStream_t stream);
 
 // ---------------------------------------------------------- cell kernels
-int launch_projection(const float *x, const float *U, const float *bias, float *p, int N, int M,
-                      int O, hipStream_t stream);
+// p = U x + bias for every position, O outputs.  `tiled` writes the layout
+// the matrix-core GRU evaluation reads (see cell_mfma.hip); row-major [B,T,O]
+// otherwise.
+int launch_projection(const float *x, const float *U, const float *bias, float *p, int B, int T, int M,
+                      int O, bool tiled, hipStream_t stream);
+size_t projection_floats(int B, int T, int O);
 
 // tanh cell: f_t = tanh(W s_{t-1} + p_t).  Dense mode writes the factored
 // leaf d_t = 1 - f_t^2 into `lin` and b_t = f_t - d_t * (W s_{t-1}); diag mode
@@ -108,11 +112,24 @@ int launch_tanh_eval(const float *W, const float *p, const float *s0, const floa
                      hipStream_t stream);
 
 // GRU cell, diagonal Jacobian: writes a_t = diag(d f / d s) and
-// b_t = f_t - a_t * s_{t-1}.
+// b_t = f_t - a_t * s_{t-1}.  With gru_fast_path(D, M) the projection is
+// tiled and the evaluation runs on the matrix cores.
+bool gru_fast_path(int D, int M);
 int launch_gru_eval(const float *Whh, const float *bhh, const float *p, const float *s0,
                     const float *s_even, const float *s_odd, const int *sel, const int *skip,
                     const int *all_done, float *a, float *bvec, unsigned *res_bits, int B, int T,
-                    int D, hipStream_t stream);
+                    int D, int M, hipStream_t stream);
+
+// Matrix-core versions (cell_mfma.hip) for the supported sizes.
+bool gru_mfma_supported(int D);
+int launch_gru_eval_mfma(const float *Whh, const float *bhh, const float *p, const float *s0,
+                         const float *s_even, const float *s_odd, const int *sel, const int *skip,
+                         const int *all_done, float *a, float *bvec, unsigned *res_bits, int B, int T,
+                         int D, hipStream_t stream);
+bool proj_mfma_supported(int M, int O);
+size_t proj_tiled_floats(int B, int T, int O);
+int launch_projection_mfma(const float *x, const float *U, const float *bias, float *p, int B, int T,
+                           int M, int O, bool tiled, hipStream_t stream);
 
 int launch_rollout(const deer_cell_params_t *p, const float *x, const float *s0, int B, int T,
                    float *traj, hipStream_t stream);

@@ -147,28 +147,45 @@ __global__ void zero_words_kernel(unsigned *__restrict__ p, size_t nwords)
 // Convergence test for iteration i = ctl->iter, per sequence, on the residual
 // of the current iterate: converged sequences are frozen with iters = i; at
 // the cap they stop as not converged (or non-finite for a NaN / Inf residual).
-__global__ void check_kernel(SolveControl *ctl, unsigned *res_bits, int *done, int *iters, int *status,
-                             float *resid, int B, float tol, int max_iter)
+// The residual comes either as one word per sequence (res_bits, reset here)
+// or as per-tile maxima (res_tile, tps words per sequence).
+__global__ void check_kernel(SolveControl *ctl, unsigned *res_bits, const unsigned *res_tile, int tps, int *done,
+                             int *iters, int *status, float *resid, int B, float tol, int max_iter)
 {
     if (ctl->all_done) return;
+    __shared__ unsigned red[256 / 64];
     const int i = ctl->iter;
     int active = 0;
-    for (int b = threadIdx.x; b < B; b += blockDim.x) {
-        if (done[b]) continue;
-        const float r = __uint_as_float(res_bits[b]);
-        res_bits[b] = 0u;
-        if (r <= tol) {
-            done[b] = 1;
-            iters[b] = i;
-            status[b] = DEER_SEQ_CONVERGED;
-            resid[b] = r;
-        } else if (i >= max_iter) {
-            done[b] = 1;
-            iters[b] = max_iter;
-            status[b] = __builtin_isfinite(r) ? DEER_SEQ_NOT_CONVERGED : DEER_SEQ_NONFINITE;
-            resid[b] = r;
+    for (int b = 0; b < B; ++b) {
+        if (done[b]) continue;                    // same for every thread
+        unsigned m = 0u;
+        if (res_tile) {
+            for (int k = threadIdx.x; k < tps; k += blockDim.x) m = max(m, res_tile[static_cast<size_t>(b) * tps + k]);
+            for (int o = 32; o > 0; o >>= 1) m = max(m, static_cast<unsigned>(__shfl_xor(static_cast<int>(m), o, 64)));
+            if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+            __syncthreads();
+            m = red[0];
+            for (int w = 1; w < static_cast<int>(blockDim.x / 64); ++w) m = max(m, red[w]);
+            __syncthreads();
         } else {
-            active = 1;
+            m = res_bits[b];
+        }
+        if (threadIdx.x == 0) {
+            const float r = __uint_as_float(m);
+            if (!res_tile) res_bits[b] = 0u;
+            if (r <= tol) {
+                done[b] = 1;
+                iters[b] = i;
+                status[b] = DEER_SEQ_CONVERGED;
+                resid[b] = r;
+            } else if (i >= max_iter) {
+                done[b] = 1;
+                iters[b] = max_iter;
+                status[b] = __builtin_isfinite(r) ? DEER_SEQ_NOT_CONVERGED : DEER_SEQ_NONFINITE;
+                resid[b] = r;
+            } else {
+                active = 1;
+            }
         }
     }
     active = __syncthreads_or(active);
@@ -224,11 +241,20 @@ int check_sizes(int B, int T)
     return DEER_OK;
 }
 
+// The GRU in diag mode at D = 32 / 64 runs one fused evaluation + scan launch
+// per iteration; everything else runs evaluation and scan as two launches.
+bool fused_gru_step(const deer_cell_params_t *p, int mode)
+{
+    return p->cell == DEER_CELL_GRU && mode == DEER_MODE_DIAG && gru_fast_path(p->D, p->M);
+}
+
 // Layout of the deer_solve workspace.
 struct SolveLayout {
     void *scan = nullptr;       // scan state (diag: look-back header + descriptors; dense: chunk aggregates)
     SolveControl *ctl = nullptr;
     unsigned *res_bits = nullptr;
+    unsigned *res_tile = nullptr;  // per-tile residual maxima (fused GRU step)
+    int tps = 0;                   // tiles per sequence for res_tile
     int *done = nullptr, *iters = nullptr, *status = nullptr;
     float *resid = nullptr;
     float *buf1 = nullptr;      // second trajectory buffer [B,T,D]
@@ -245,11 +271,17 @@ SolveLayout solve_layout(void *ws, const deer_cell_params_t *p, int B, int T, in
     Carve c(ws);
     SolveLayout L;
     // the scan state comes first so that its header keeps a fixed place
-    const size_t scan_bytes = (mode == DEER_MODE_DIAG) ? diag_scan_state_bytes(B, T, p->D)
-                                                       : dense_scan_state_bytes(B, T, p->D);
+    const bool fused = fused_gru_step(p, mode);
+    const size_t scan_bytes = fused ? gru_step_state_bytes(B, T, p->D)
+                              : (mode == DEER_MODE_DIAG) ? diag_scan_state_bytes(B, T, p->D)
+                                                         : dense_scan_state_bytes(B, T, p->D);
     L.scan = c.take<char>(scan_bytes);
     L.ctl = c.take<SolveControl>(1);
     L.res_bits = c.take<unsigned>(B);
+    if (fused) {
+        L.tps = (T + gru_step_tile(p->D) - 1) / gru_step_tile(p->D);
+        L.res_tile = c.take<unsigned>(static_cast<size_t>(B) * L.tps);
+    }
     L.done = c.take<int>(B);
     L.iters = c.take<int>(B);
     L.status = c.take<int>(B);
@@ -434,8 +466,22 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
 
     const int *sel = &L.ctl->iter;
     const int *all_done = &L.ctl->all_done;
+    const bool fused = fused_gru_step(p, mode);
     auto enqueue_iteration = [&]() -> int {
         int r;
+        if (fused) {
+            prof.begin(0);
+            r = launch_gru_quasi_step(p->W, p->b2, L.proj, s0, traj_out, L.buf1, sel, L.done, all_done, L.res_tile,
+                                      B, T, D, L.scan, stream);
+            prof.end();
+            if (r) return r;
+            prof.begin(3);
+            hipLaunchKernelGGL(check_kernel, dim3(1), dim3(256), 0, stream, L.ctl, L.res_bits, L.res_tile, L.tps,
+                               L.done, L.iters, L.status, L.resid, B, tol, max_iter);
+            prof.end();
+            DEER_HIP(hipGetLastError());
+            return DEER_OK;
+        }
         prof.begin(0);
         if (gru)
             r = launch_gru_eval(p->W, p->b2, L.proj, s0, traj_out, L.buf1, sel, L.done, all_done, L.lin, L.bvec,
@@ -446,7 +492,7 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
         prof.end();
         if (r) return r;
         prof.begin(3);
-        hipLaunchKernelGGL(check_kernel, dim3(1), dim3(256), 0, stream, L.ctl, L.res_bits, L.done, L.iters,
+        hipLaunchKernelGGL(check_kernel, dim3(1), dim3(256), 0, stream, L.ctl, L.res_bits, nullptr, 0, L.done, L.iters,
                            L.status, L.resid, B, tol, max_iter);
         prof.end();
         DEER_HIP(hipGetLastError());
@@ -509,7 +555,7 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
             hipMemcpyAsync(status_h.data(), L.status, sizeof(int) * B, hipMemcpyDeviceToHost, stream) != hipSuccess)
             rc = fail(DEER_ERR_HIP, "deer_solve: result copy failed");
     }
-    if (rc == DEER_OK && mode == DEER_MODE_DIAG) {
+    if (rc == DEER_OK && (mode == DEER_MODE_DIAG || fused)) {
         if (hipMemcpyAsync(&abort_flag, &static_cast<ScanHeader *>(L.scan)->abort, sizeof(unsigned),
                            hipMemcpyDeviceToHost, stream) != hipSuccess)
             rc = fail(DEER_ERR_HIP, "deer_solve: flag copy failed");

@@ -41,6 +41,24 @@ __device__ __forceinline__ void wave_max_atomic(unsigned v, unsigned *dst)
     if ((threadIdx.x & 63) == 0 && v != 0u) atomicMax(dst, v);
 }
 
+// Self-validating look-back descriptor words: float value | 32-bit tag.
+constexpr unsigned kDescSpinLimit = 1u << 22;
+constexpr int kWin = 4;   // predecessors read per look-back round trip
+__device__ __forceinline__ unsigned long long pack_desc(float v, unsigned tag)
+{
+    return (static_cast<unsigned long long>(tag) << 32) | __float_as_uint(v);
+}
+__device__ __forceinline__ unsigned desc_tag(unsigned long long w) { return static_cast<unsigned>(w >> 32); }
+__device__ __forceinline__ float desc_val(unsigned long long w) { return __uint_as_float(static_cast<unsigned>(w)); }
+__device__ __forceinline__ unsigned long long load_desc(const unsigned long long *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_desc(unsigned long long *p, unsigned long long v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ------------------------------------------------------------ GRU evaluation
 template <int D>
 struct GruGeom {
@@ -199,6 +217,260 @@ __global__ __launch_bounds__(kThreads) void gru_eval_mfma_kernel(
     if (cur >= 0) wave_max_atomic(rmax, res_bits + cur);
 }
 
+// ------------------------------------------------- fused quasi-DEER GRU step
+// One launch per Newton iteration: the evaluation above, followed in the same
+// workgroup by the diagonal scan of the (a_t, b_t) it just produced, so that
+// s^(i+1) is written directly and a, b never reach HBM.  Per position the
+// launch reads s^(i) and the projection and writes s^(i+1): (D + 3D + D) words.
+//
+// The scan composes (a_j, b_j) o (a_i, b_i) = (a_j a_i, a_j b_i + b_j), the
+// later map on the left ("Parallel Broyden Methods", appendix C.2), at four
+// levels: the 4 consecutive positions a lane holds, the 8 position groups of
+// a 32-position sub-tile (exchanged between the lane pair l, l ^ 32), the
+// sub-tiles of the workgroup's tile (LDS), and the tiles of a sequence
+// (decoupled look-back with self-validating 64-bit descriptors, as in the
+// standalone diagonal scan).  Tiles are taken in the strided order blockIdx.x,
+// blockIdx.x + G, ...; with the whole persistent grid resident the smallest
+// waiting tile's predecessor is always in progress.
+//
+// The residual of the iterate is reduced per tile into res_tile[tile] (plain
+// stores; the convergence test takes the max over a sequence's tiles).
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void gru_quasi_step_kernel(
+    const float *__restrict__ Whh, const float *__restrict__ bhh, const float *__restrict__ pt,
+    const float *__restrict__ s0, float *s_even, float *s_odd, const int *__restrict__ sel,
+    const int *__restrict__ skip, const int *__restrict__ all_done, unsigned *__restrict__ res_tile, int T,
+    int tiles_per_seq, int nseq, long long ntiles, ScanHeader *__restrict__ hdr,
+    unsigned long long *__restrict__ desc)
+{
+    using G = GruGeom<D>;
+    if (all_done && *all_done) return;           // same value for every workgroup of the launch
+    __shared__ float H[(G::TP + 1) * G::LDH];    // H[r] = s_{t0 - 1 + r}
+    __shared__ float Ws[3 * D * G::LDH];         // Ws[g D + c][k] = W_hh[g D + c][k]
+    __shared__ float shA[G::PSUB][D], shB[G::PSUB][D], shC[D];
+    __shared__ unsigned red[kThreads / 64];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int cb = wave % G::NCB, ps = wave / G::NCB;
+    const int r32 = lane & 31, hf = lane >> 5;
+    const int c = cb * 32 + r32;
+    const int tps32 = (T + 31) / 32;
+
+    for (int e = tid; e < 3 * D * D; e += kThreads) {
+        const int o = e / D, k = e % D;
+        Ws[o * G::LDH + k] = Whh[e];
+    }
+    const float br = bhh ? bhh[c] : 0.0f, bz = bhh ? bhh[D + c] : 0.0f, bn = bhh ? bhh[2 * D + c] : 0.0f;
+    const float wr = Whh[static_cast<size_t>(c) * D + c];
+    const float wz = Whh[static_cast<size_t>(D + c) * D + c];
+    const float wn = Whh[static_cast<size_t>(2 * D + c) * D + c];
+    const bool odd = sel && (*sel & 1);
+    const float *s = odd ? s_odd : s_even;       // the iterate s^(i)
+    float *out = odd ? s_even : s_odd;           // s^(i+1)
+    const unsigned epoch = __hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned tag_agg = epoch * 4u + 1u, tag_inc = epoch * 4u + 2u;
+
+    v4f hv[GruTile<D>::NH];
+    v4f pv[3][4];
+    long long tile = blockIdx.x;
+    // tiles are numbered time-major (k -> sequence k % nseq, tile k / nseq) so that
+    // the tiles in flight at once spread over the sequences and look-back walks stay short
+    auto seq_major = [&](long long k) { return (k % nseq) * tiles_per_seq + k / nseq; };
+    if (tile < ntiles) gru_fetch<D>(s, s0, pt, T, tiles_per_seq, tps32, seq_major(tile), ps, hf, c, hv, pv);
+    for (; tile < ntiles; tile += gridDim.x) {
+        const int bseq = static_cast<int>(tile % nseq);
+        const int tt = static_cast<int>(tile / nseq);
+        const int t0 = tt * G::TP;
+        const bool live = !(skip && skip[bseq]);  // uniform over the workgroup
+        __syncthreads();                          // the previous tile is done with H and the exchange arrays
+#pragma unroll
+        for (int i = 0; i < GruTile<D>::NH; ++i) {
+            const int e = tid + i * kThreads;
+            if (e < (G::TP + 1) * (D / 4)) {
+                const int r = e / (D / 4), q = (e % (D / 4)) * 4;
+                float *hrow = H + r * G::LDH + q;
+                hrow[0] = hv[i][0]; hrow[1] = hv[i][1]; hrow[2] = hv[i][2]; hrow[3] = hv[i][3];
+            }
+        }
+        __syncthreads();
+        v4f pc[3][4];
+#pragma unroll
+        for (int g = 0; g < 3; ++g)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) pc[g][q] = pv[g][q];
+        const long long next = tile + gridDim.x;
+        if (next < ntiles) gru_fetch<D>(s, s0, pt, T, tiles_per_seq, tps32, seq_major(next), ps, hf, c, hv, pv);
+        if (!live) continue;
+
+        v16f accR = {}, accZ = {}, accN = {};
+        const float *arow = H + (ps * 32 + r32) * G::LDH + hf;
+        const float *wrow = Ws + c * G::LDH + hf;
+#pragma unroll
+        for (int kk = 0; kk < G::KK; ++kk) {
+            const float av = arow[2 * kk];
+            accR = __builtin_amdgcn_mfma_f32_32x32x2f32(av, wrow[2 * kk], accR, 0, 0, 0);
+            accZ = __builtin_amdgcn_mfma_f32_32x32x2f32(av, wrow[D * G::LDH + 2 * kk], accZ, 0, 0, 0);
+            accN = __builtin_amdgcn_mfma_f32_32x32x2f32(av, wrow[2 * D * G::LDH + 2 * kk], accN, 0, 0, 0);
+        }
+
+        // gates, Jacobian diagonal and offsets at the lane's 16 positions
+        const bool full = t0 + ps * 32 + 32 <= T;
+        float la[16], lb[16];
+        unsigned rmax = 0u;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int pos = ps * 32 + acc_row(v, hf);
+            const int t = t0 + pos;
+            const float qr = accR[v] + br, qz = accZ[v] + bz, qn = accN[v] + bn;
+            const float h = H[pos * G::LDH + c];
+            const float st = H[(pos + 1) * G::LDH + c];
+            const float rg = sigmoid_fast(pc[0][v >> 2][v & 3] + qr);
+            const float zg = sigmoid_fast(pc[1][v >> 2][v & 3] + qz);
+            const float ng = tanh_fast(pc[2][v >> 2][v & 3] + rg * qn);
+            const float f = (1.0f - zg) * ng + zg * h;
+            const float a = zg + (h - ng) * zg * (1.0f - zg) * wz +
+                            (1.0f - zg) * (1.0f - ng * ng) * (rg * wn + rg * (1.0f - rg) * wr * qn);
+            const bool in = full || t < T;
+            la[v] = in ? a : 1.0f;
+            lb[v] = in ? f - a * h : 0.0f;
+            if (in) rmax = max(rmax, __float_as_uint(fabsf(st - f)));
+        }
+
+        // level 1: the lane's four runs of 4 consecutive positions
+        float GA[4], GB[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            GA[q] = 1.0f;
+            GB[q] = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                GB[q] = la[4 * q + r] * GB[q] + lb[4 * q + r];
+                GA[q] = la[4 * q + r] * GA[q];
+            }
+        }
+        // level 2: runs alternate between the lane pair (l, l ^ 32) in position order
+        float EA[4], EB[4];
+        float accA = 1.0f, accB = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float oA = __shfl_xor(GA[q], 32, 64), oB = __shfl_xor(GB[q], 32, 64);
+            const float fA = hf ? oA : GA[q], fB = hf ? oB : GB[q];   // earlier run of the pair
+            const float sA = hf ? GA[q] : oA, sB = hf ? GB[q] : oB;   // later run
+            const float midA = fA * accA, midB = fA * accB + fB;
+            EA[q] = hf ? midA : accA;
+            EB[q] = hf ? midB : accB;
+            accB = sA * midB + sB;
+            accA = sA * midA;
+        }
+        for (int o = 32; o > 0; o >>= 1) rmax = max(rmax, static_cast<unsigned>(__shfl_xor(static_cast<int>(rmax), o, 64)));
+        if (lane == 0) red[wave] = rmax;
+        if (hf == 0) { shA[ps][c] = accA; shB[ps][c] = accB; }
+        __syncthreads();
+
+        // level 4: tile aggregate per channel, look-back over the sequence's earlier tiles
+        if (tid == 0) {
+            unsigned m = red[0];
+            for (int w = 1; w < kThreads / 64; ++w) m = max(m, red[w]);
+            res_tile[static_cast<size_t>(bseq) * tiles_per_seq + tt] = m;
+        }
+        if (tid < D) {
+            const int cc = tid;
+            float TA = 1.0f, TB = 0.0f;
+#pragma unroll
+            for (int k = 0; k < G::PSUB; ++k) {
+                TB = shA[k][cc] * TB + shB[k][cc];
+                TA = shA[k][cc] * TA;
+            }
+            unsigned long long *mine = desc + (static_cast<size_t>(bseq) * tiles_per_seq + tt) * 3 * D;
+            float carry;
+            if (tt == 0) {
+                carry = s0 ? s0[static_cast<size_t>(bseq) * D + cc] : 0.0f;
+            } else {
+                store_desc(mine + cc, pack_desc(TA, tag_agg));
+                store_desc(mine + D + cc, pack_desc(TB, tag_agg));
+                // walk back in windows of kWin predecessors whose descriptors are read together
+                float kA = 1.0f, kB = 0.0f;      // maps s_end(j) to s_end(tt - 1)
+                int j = tt - 1;
+                unsigned spins = 0;
+                bool found = false;
+                while (!found) {
+                    unsigned long long wi[kWin], wa[kWin], wb[kWin];
+#pragma unroll
+                    for (int u = 0; u < kWin; ++u) {
+                        const int jj = max(j - u, 0);
+                        const unsigned long long *pj = desc + (static_cast<size_t>(bseq) * tiles_per_seq + jj) * 3 * D;
+                        wi[u] = load_desc(pj + 2 * D + cc);
+                        wa[u] = load_desc(pj + cc);
+                        wb[u] = load_desc(pj + D + cc);
+                    }
+                    bool stalled = false;
+#pragma unroll
+                    for (int u = 0; u < kWin; ++u) {
+                        if (found || stalled || j - u < 0) continue;
+                        if (desc_tag(wi[u]) == tag_inc) {
+                            carry = kA * desc_val(wi[u]) + kB;
+                            found = true;
+                        } else if (desc_tag(wa[u]) == tag_agg && desc_tag(wb[u]) == tag_agg) {
+                            kB = kA * desc_val(wb[u]) + kB;
+                            kA = kA * desc_val(wa[u]);
+                        } else {
+                            stalled = true;
+                            j -= u;              // resume at the first tile not yet published
+                        }
+                    }
+                    if (found) break;
+                    if (!stalled) {
+                        j -= kWin;
+                        continue;
+                    }
+                    ++spins;
+                    if (spins > kDescSpinLimit ||
+                        ((spins & 1023u) == 0u &&
+                         __hip_atomic_load(&hdr->abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
+                        __hip_atomic_store(&hdr->abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        carry = __builtin_nanf("");
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+            }
+            store_desc(mine + 2 * D + cc, pack_desc(TA * carry + TB, tag_inc));
+            shC[cc] = carry;
+        }
+        __syncthreads();
+
+        // replay: state entering the sub-tile, then the lane's runs
+        float PA = 1.0f, PB = 0.0f;
+        for (int k = 0; k < ps; ++k) {
+            PB = shA[k][c] * PB + shB[k][c];
+            PA = shA[k][c] * PA;
+        }
+        const float x0 = PA * shC[c] + PB;
+        const size_t seq = static_cast<size_t>(bseq) * T;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float xs = EA[q] * x0 + EB[q];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int v = 4 * q + r;
+                xs = la[v] * xs + lb[v];
+                const int t = t0 + ps * 32 + acc_row(v, hf);
+                if (full || t < T) __builtin_nontemporal_store(xs, out + (seq + t) * D + c);
+            }
+        }
+    }
+
+    // last workgroup out resets the done counter and advances the epoch
+    __syncthreads();
+    if (tid == 0) {
+        const unsigned prev = __hip_atomic_fetch_add(&hdr->done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        if (prev == gridDim.x - 1) {
+            __hip_atomic_store(&hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&hdr->epoch, epoch + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
 // ------------------------------------------------------------ input projection
 // out[n][o] = sum_k U[o][k] x[n][k] + bias[o] for O = 32 NOB outputs, K <= KP.
 // Row-major output ([B,T,O]) or, with TILED, the layout the GRU evaluation
@@ -331,6 +603,25 @@ int launch_proj_mfma(const float *x, const float *U, const float *bias, float *p
     return DEER_OK;
 }
 
+template <int D>
+int launch_gru_step(const float *Whh, const float *bhh, const float *pt, const float *s0, float *s_even, float *s_odd,
+                    const int *sel, const int *skip, const int *all_done, unsigned *res_tile, int B, int T,
+                    void *state, hipStream_t stream)
+{
+    using G = GruGeom<D>;
+    static int cap = 0;
+    if (cap == 0) cap = capacity_of(gru_quasi_step_kernel<D>, 0);
+    const int tps = (T + G::TP - 1) / G::TP;
+    const long long ntiles = static_cast<long long>(B) * tps;
+    const unsigned grid = static_cast<unsigned>(std::max<long long>(1, std::min<long long>(ntiles, cap)));
+    auto *hdr = static_cast<ScanHeader *>(state);
+    auto *desc = reinterpret_cast<unsigned long long *>(static_cast<char *>(state) + sizeof(ScanHeader));
+    hipLaunchKernelGGL((gru_quasi_step_kernel<D>), dim3(grid), dim3(kThreads), 0, stream, Whh, bhh, pt, s0, s_even,
+                       s_odd, sel, skip, all_done, res_tile, T, tps, B, ntiles, hdr, desc);
+    DEER_HIP(hipGetLastError());
+    return DEER_OK;
+}
+
 }  // namespace
 
 bool gru_mfma_supported(int D) { return D == 32 || D == 64; }
@@ -370,6 +661,26 @@ int launch_projection_mfma(const float *x, const float *U, const float *bias, fl
     default: return fail(DEER_ERR_UNSUPPORTED, "projection: output size not a supported multiple of 32");
     }
 #undef DEER_PROJ
+}
+
+int gru_step_tile(int D) { return D == 64 ? GruGeom<64>::TP : GruGeom<32>::TP; }
+
+size_t gru_step_state_bytes(int B, int T, int D)
+{
+    const int tps = (T + gru_step_tile(D) - 1) / gru_step_tile(D);
+    return sizeof(ScanHeader) + align_up(static_cast<size_t>(B) * tps * 3 * D * sizeof(unsigned long long));
+}
+
+int launch_gru_quasi_step(const float *Whh, const float *bhh, const float *pt, const float *s0, float *s_even,
+                          float *s_odd, const int *sel, const int *skip, const int *all_done, unsigned *res_tile,
+                          int B, int T, int D, void *state, hipStream_t stream)
+{
+    if (B == 0 || T == 0) return DEER_OK;
+    if (D == 64)
+        return launch_gru_step<64>(Whh, bhh, pt, s0, s_even, s_odd, sel, skip, all_done, res_tile, B, T, state, stream);
+    if (D == 32)
+        return launch_gru_step<32>(Whh, bhh, pt, s0, s_even, s_odd, sel, skip, all_done, res_tile, B, T, state, stream);
+    return fail(DEER_ERR_UNSUPPORTED, "fused GRU step needs D = 32 or 64");
 }
 
 }  // namespace deer

@@ -131,6 +131,16 @@ size_t proj_tiled_floats(int B, int T, int O);
 int launch_projection_mfma(const float *x, const float *U, const float *bias, float *p, int B, int T,
                            int M, int O, bool tiled, hipStream_t stream);
 
+// Fused quasi-DEER iteration for the GRU on the matrix cores: evaluation and
+// diagonal scan in one persistent launch, writing s^(i+1) into the buffer
+// that does not hold s^(i).  res_tile[tile] receives the residual maximum of
+// every TP-position tile (gru_step_tile(D) positions).
+int gru_step_tile(int D);
+size_t gru_step_state_bytes(int B, int T, int D);
+int launch_gru_quasi_step(const float *Whh, const float *bhh, const float *pt, const float *s0, float *s_even,
+                          float *s_odd, const int *sel, const int *skip, const int *all_done,
+                          unsigned *res_tile, int B, int T, int D, void *state, hipStream_t stream);
+
 int launch_rollout(const deer_cell_params_t *p, const float *x, const float *s0, int B, int T,
                    float *traj, hipStream_t stream);
 

@@ -109,12 +109,6 @@ struct PollSlots {
 thread_local PollSlots g_poll;
 
 // ------------------------------------------------------ small device kernels
-struct SolveControl {
-    int iter;       // current iteration index i (iterate s^(i) lives in buffer i % 2)
-    int all_done;   // 1 once every sequence has stopped
-    int pad[62];
-};
-
 __global__ void init_control_kernel(SolveControl *ctl, int *done, int *iters, int *status, float *resid,
                                     unsigned *res_bits, int B)
 {
@@ -144,67 +138,30 @@ __global__ void zero_words_kernel(unsigned *__restrict__ p, size_t nwords)
     for (; i < nwords; i += stride) p[i] = 0u;
 }
 
-// Convergence test for iteration i = ctl->iter, per sequence, on the residual
-// of the current iterate: converged sequences are frozen with iters = i; at
-// the cap they stop as not converged (or non-finite for a NaN / Inf residual).
-// The residual comes either as one word per sequence (res_bits, reset here)
-// or as per-tile maxima (res_tile, tps words per sequence).
+// Convergence test of the current iteration (see finalize_iteration).
 __global__ void check_kernel(SolveControl *ctl, unsigned *res_bits, const unsigned *res_tile, int tps, int *done,
                              int *iters, int *status, float *resid, int B, float tol, int max_iter)
 {
-    if (ctl->all_done) return;
     __shared__ unsigned red[256 / 64];
-    const int i = ctl->iter;
-    int active = 0;
-    for (int b = 0; b < B; ++b) {
-        if (done[b]) continue;                    // same for every thread
-        unsigned m = 0u;
-        if (res_tile) {
-            for (int k = threadIdx.x; k < tps; k += blockDim.x) m = max(m, res_tile[static_cast<size_t>(b) * tps + k]);
-            for (int o = 32; o > 0; o >>= 1) m = max(m, static_cast<unsigned>(__shfl_xor(static_cast<int>(m), o, 64)));
-            if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-            __syncthreads();
-            m = red[0];
-            for (int w = 1; w < static_cast<int>(blockDim.x / 64); ++w) m = max(m, red[w]);
-            __syncthreads();
-        } else {
-            m = res_bits[b];
-        }
-        if (threadIdx.x == 0) {
-            const float r = __uint_as_float(m);
-            if (!res_tile) res_bits[b] = 0u;
-            if (r <= tol) {
-                done[b] = 1;
-                iters[b] = i;
-                status[b] = DEER_SEQ_CONVERGED;
-                resid[b] = r;
-            } else if (i >= max_iter) {
-                done[b] = 1;
-                iters[b] = max_iter;
-                status[b] = __builtin_isfinite(r) ? DEER_SEQ_NOT_CONVERGED : DEER_SEQ_NONFINITE;
-                resid[b] = r;
-            } else {
-                active = 1;
-            }
-        }
-    }
-    active = __syncthreads_or(active);
-    if (threadIdx.x == 0) {
-        if (active) ctl->iter = i + 1;
-        else ctl->all_done = 1;
-    }
+    if (ctl->all_done) return;
+    finalize_iteration(ctl, res_bits, res_tile, tps, done, iters, status, resid, B, tol, max_iter, red);
 }
 
-// Sequences whose final iterate sits in the second buffer are copied out.
+// Sequences whose final iterate sits in the second buffer are copied out.  With
+// zero_start, traj was never written for sequences that stopped at iteration
+// 0; their iterate is the all-zero start.
 __global__ void gather_kernel(float *__restrict__ traj, const float *__restrict__ buf1, const int *__restrict__ iters,
-                              size_t per_seq, int B)
+                              size_t per_seq, int B, int zero_start)
 {
     const int bseq = blockIdx.y;
-    if (bseq >= B || (iters[bseq] & 1) == 0) return;
+    if (bseq >= B) return;
+    const int it = iters[bseq];
+    const bool copy = (it & 1) != 0, zero = zero_start && it == 0;
+    if (!copy && !zero) return;
     const size_t base = static_cast<size_t>(bseq) * per_seq;
     for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < per_seq;
          i += static_cast<size_t>(gridDim.x) * blockDim.x)
-        traj[base + i] = buf1[base + i];
+        traj[base + i] = copy ? buf1[base + i] : 0.0f;
 }
 
 unsigned grid_for(size_t n, unsigned threads = 256, unsigned cap = 8192)
@@ -450,10 +407,12 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
     hipLaunchKernelGGL(init_control_kernel, dim3(grid_for(static_cast<size_t>(B) + 1)), dim3(256), 0, stream, L.ctl,
                        L.done, L.iters, L.status, L.resid, L.res_bits, B);
     DEER_HIP(hipGetLastError());
+    const bool fused = fused_gru_step(p, mode);
+    const bool zero_start = fused && !init_guess;   // the fused step reads no s^(0) when it is all zeros
     if (init_guess) {
         if (init_guess != traj_out)
             hipLaunchKernelGGL(copy_kernel, dim3(grid_for(BTD)), dim3(256), 0, stream, traj_out, init_guess, BTD);
-    } else {
+    } else if (!zero_start) {
         hipLaunchKernelGGL(fill_kernel, dim3(grid_for(BTD)), dim3(256), 0, stream, traj_out, BTD, 0.0f);
     }
     DEER_HIP(hipGetLastError());
@@ -466,21 +425,15 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
 
     const int *sel = &L.ctl->iter;
     const int *all_done = &L.ctl->all_done;
-    const bool fused = fused_gru_step(p, mode);
     auto enqueue_iteration = [&]() -> int {
         int r;
         if (fused) {
             prof.begin(0);
-            r = launch_gru_quasi_step(p->W, p->b2, L.proj, s0, traj_out, L.buf1, sel, L.done, all_done, L.res_tile,
-                                      B, T, D, L.scan, stream);
+            r = launch_gru_quasi_step(p->W, p->b2, L.proj, s0, traj_out, L.buf1, L.ctl, L.done, L.iters, L.status,
+                                      L.resid, tol, max_iter, L.res_bits, L.res_tile, B, T, D, zero_start, L.scan,
+                                      stream);
             prof.end();
-            if (r) return r;
-            prof.begin(3);
-            hipLaunchKernelGGL(check_kernel, dim3(1), dim3(256), 0, stream, L.ctl, L.res_bits, L.res_tile, L.tps,
-                               L.done, L.iters, L.status, L.resid, B, tol, max_iter);
-            prof.end();
-            DEER_HIP(hipGetLastError());
-            return DEER_OK;
+            return r;
         }
         prof.begin(0);
         if (gru)
@@ -544,7 +497,7 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
     if (rc == DEER_OK) {
         const size_t per_seq = static_cast<size_t>(T) * D;
         hipLaunchKernelGGL(gather_kernel, dim3(grid_for(per_seq, 256, 1024), B), dim3(256), 0, stream, traj_out,
-                           L.buf1, L.iters, per_seq, B);
+                           L.buf1, L.iters, per_seq, B, zero_start ? 1 : 0);
         if (hipGetLastError() != hipSuccess) rc = fail(DEER_ERR_HIP, "deer_solve: gather launch failed");
     }
     std::vector<int> status_h(B, 0);

@@ -44,6 +44,7 @@ __device__ __forceinline__ void wave_max_atomic(unsigned v, unsigned *dst)
 // Self-validating look-back descriptor words: float value | 32-bit tag.
 constexpr unsigned kDescSpinLimit = 1u << 22;
 constexpr int kWin = 4;   // predecessors read per look-back round trip
+constexpr int kSeqLds = 256;   // sequences whose residual maxima a workgroup keeps in LDS
 __device__ __forceinline__ unsigned long long pack_desc(float v, unsigned tag)
 {
     return (static_cast<unsigned long long>(tag) << 32) | __float_as_uint(v);
@@ -103,7 +104,7 @@ __device__ __forceinline__ void gru_fetch(const float *__restrict__ s, const flo
             const int t = t0 - 1 + r;
             if (t < 0) {
                 if (s0) v = *reinterpret_cast<const v4f *>(s0 + static_cast<size_t>(bseq) * D + q);
-            } else if (t < T) {
+            } else if (t < T && s) {
                 v = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(s + (seq + t) * D + q));
             }
         }
@@ -238,23 +239,28 @@ __global__ __launch_bounds__(kThreads) void gru_eval_mfma_kernel(
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void gru_quasi_step_kernel(
     const float *__restrict__ Whh, const float *__restrict__ bhh, const float *__restrict__ pt,
-    const float *__restrict__ s0, float *s_even, float *s_odd, const int *__restrict__ sel,
-    const int *__restrict__ skip, const int *__restrict__ all_done, unsigned *__restrict__ res_tile, int T,
-    int tiles_per_seq, int nseq, long long ntiles, ScanHeader *__restrict__ hdr,
-    unsigned long long *__restrict__ desc)
+    const float *__restrict__ s0, float *s_even, float *s_odd, SolveControl *ctl, int *done, int *iters,
+    int *status, float *resid, float tol, int max_iter, unsigned *res_bits, unsigned *__restrict__ res_tile, int T,
+    int tiles_per_seq,
+    int nseq, long long ntiles, int zero_start, ScanHeader *__restrict__ hdr, unsigned long long *__restrict__ desc)
 {
     using G = GruGeom<D>;
-    if (all_done && *all_done) return;           // same value for every workgroup of the launch
+    if (ctl->all_done) return;                   // same value for every workgroup of the launch
+    const int *sel = &ctl->iter;
+    const int *skip = done;
     __shared__ float H[(G::TP + 1) * G::LDH];    // H[r] = s_{t0 - 1 + r}
     __shared__ float Ws[3 * D * G::LDH];         // Ws[g D + c][k] = W_hh[g D + c][k]
     __shared__ float shA[G::PSUB][D], shB[G::PSUB][D], shC[D];
     __shared__ unsigned red[kThreads / 64];
+    __shared__ unsigned seqmax[kSeqLds];         // this workgroup's residual maxima per sequence
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int cb = wave % G::NCB, ps = wave / G::NCB;
     const int r32 = lane & 31, hf = lane >> 5;
     const int c = cb * 32 + r32;
     const int tps32 = (T + 31) / 32;
+    const bool per_seq = nseq <= kSeqLds;        // else per-tile maxima go to res_tile
+    for (int b = tid; b < kSeqLds; b += kThreads) seqmax[b] = 0u;
 
     for (int e = tid; e < 3 * D * D; e += kThreads) {
         const int o = e / D, k = e % D;
@@ -264,8 +270,9 @@ __global__ __launch_bounds__(kThreads, 2) void gru_quasi_step_kernel(
     const float wr = Whh[static_cast<size_t>(c) * D + c];
     const float wz = Whh[static_cast<size_t>(D + c) * D + c];
     const float wn = Whh[static_cast<size_t>(2 * D + c) * D + c];
-    const bool odd = sel && (*sel & 1);
-    const float *s = odd ? s_odd : s_even;       // the iterate s^(i)
+    const int iter = *sel;
+    const bool odd = (iter & 1) != 0;
+    const float *s = (zero_start && iter == 0) ? nullptr : (odd ? s_odd : s_even);   // the iterate s^(i)
     float *out = odd ? s_even : s_odd;           // s^(i+1)
     const unsigned epoch = __hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const unsigned tag_agg = epoch * 4u + 1u, tag_inc = epoch * 4u + 2u;
@@ -371,7 +378,8 @@ __global__ __launch_bounds__(kThreads, 2) void gru_quasi_step_kernel(
         if (tid == 0) {
             unsigned m = red[0];
             for (int w = 1; w < kThreads / 64; ++w) m = max(m, red[w]);
-            res_tile[static_cast<size_t>(bseq) * tiles_per_seq + tt] = m;
+            if (per_seq) seqmax[bseq] = max(seqmax[bseq], m);
+            else res_tile[static_cast<size_t>(bseq) * tiles_per_seq + tt] = m;
         }
         if (tid < D) {
             const int cc = tid;
@@ -460,15 +468,29 @@ __global__ __launch_bounds__(kThreads, 2) void gru_quasi_step_kernel(
         }
     }
 
-    // last workgroup out resets the done counter and advances the epoch
+    // The last workgroup out resets the done counter, advances the epoch and
+    // runs the convergence test of this iteration on the residual maxima.
+    __shared__ int sh_last;
+    __syncthreads();
+    if (per_seq)
+        for (int b = tid; b < nseq; b += kThreads)
+            if (seqmax[b]) atomicMax(res_bits + b, seqmax[b]);
     __syncthreads();
     if (tid == 0) {
         const unsigned prev = __hip_atomic_fetch_add(&hdr->done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        if (prev == gridDim.x - 1) {
-            __hip_atomic_store(&hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&hdr->epoch, epoch + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        sh_last = (prev == gridDim.x - 1) ? 1 : 0;
     }
+    __syncthreads();
+    if (!sh_last) return;
+    __threadfence();
+    if (tid == 0) {
+        __hip_atomic_store(&hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&hdr->epoch, epoch + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (per_seq)
+        finalize_iteration(ctl, res_bits, nullptr, 0, done, iters, status, resid, nseq, tol, max_iter, red);
+    else
+        finalize_iteration(ctl, nullptr, res_tile, tiles_per_seq, done, iters, status, resid, nseq, tol, max_iter, red);
 }
 
 // ------------------------------------------------------------ input projection
@@ -486,6 +508,43 @@ struct ProjGeom {
     static constexpr int PAIRS = PS * NOB / 4;                               // (sub-tile, block) pairs per wave
     static constexpr int LDX = KP + 2;
 };
+
+template <int KP, int NOB>
+struct ProjTile {
+    static constexpr int NX = (ProjGeom<KP, NOB>::TP * KP / 4 + kThreads - 1) / kThreads;   // float4 per thread
+};
+
+// x rows of one tile (sub-tiles of 32 positions never straddle sequences).
+// Rows past the end of a sequence and columns past M read as zero.
+template <int KP, int NOB>
+__device__ __forceinline__ void proj_fetch(const float *__restrict__ x, int T, int M, int tps32, long long nsub,
+                                           long long tile, v4f (&xv)[ProjTile<KP, NOB>::NX])
+{
+    using G = ProjGeom<KP, NOB>;
+#pragma unroll
+    for (int i = 0; i < ProjTile<KP, NOB>::NX; ++i) {
+        const int e = threadIdx.x + i * kThreads;
+        v4f v = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (e < G::TP * KP / 4) {
+            const int r = e / (KP / 4), k = (e % (KP / 4)) * 4;
+            const long long u = tile * G::PS + r / 32;
+            if (u < nsub) {
+                const long long bseq = u / tps32;
+                const int t = static_cast<int>(u - bseq * tps32) * 32 + (r % 32);
+                if (t < T) {
+                    const float *src = x + (static_cast<size_t>(bseq) * T + t) * M + k;
+                    if ((M & 3) == 0 && k + 4 <= M) {
+                        v = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(src));
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) v[j] = (k + j < M) ? src[j] : 0.0f;
+                    }
+                }
+            }
+        }
+        xv[i] = v;
+    }
+}
 
 template <int KP, int NOB, bool TILED>
 __global__ __launch_bounds__(kThreads) void projection_mfma_kernel(const float *__restrict__ x,
@@ -505,23 +564,24 @@ __global__ __launch_bounds__(kThreads) void projection_mfma_kernel(const float *
         const int o = e / KP, k = e % KP;
         Ws[o * G::LDX + k] = (k < M) ? U[static_cast<size_t>(o) * M + k] : 0.0f;
     }
-    // sub-tiles of 32 positions never straddle sequences: u -> (sequence, block)
     const long long ntiles = (nsub + G::PS - 1) / G::PS;
     const long long tb = ntiles * blockIdx.x / gridDim.x, te = ntiles * (blockIdx.x + 1) / gridDim.x;
+    if (tb >= te) return;
+    v4f xv[ProjTile<KP, NOB>::NX];
+    proj_fetch<KP, NOB>(x, T, M, tps32, nsub, tb, xv);
     for (long long tile = tb; tile < te; ++tile) {
-        __syncthreads();
-        for (int e = tid; e < G::TP * KP; e += kThreads) {
-            const int r = e / KP, k = e % KP;
-            const long long u = tile * G::PS + r / 32;
-            float v = 0.0f;
-            if (u < nsub && k < M) {
-                const long long bseq = u / tps32;
-                const int t = static_cast<int>(u % tps32) * 32 + (r % 32);
-                if (t < T) v = x[(static_cast<size_t>(bseq) * T + t) * M + k];
+        __syncthreads();                         // the previous tile is done with Xs
+#pragma unroll
+        for (int i = 0; i < ProjTile<KP, NOB>::NX; ++i) {
+            const int e = tid + i * kThreads;
+            if (e < G::TP * KP / 4) {
+                const int r = e / (KP / 4), k = (e % (KP / 4)) * 4;
+                float *dst = Xs + r * G::LDX + k;
+                dst[0] = xv[i][0]; dst[1] = xv[i][1]; dst[2] = xv[i][2]; dst[3] = xv[i][3];
             }
-            Xs[r * G::LDX + k] = v;
         }
         __syncthreads();
+        if (tile + 1 < te) proj_fetch<KP, NOB>(x, T, M, tps32, nsub, tile + 1, xv);
 #pragma unroll
         for (int pi = 0; pi < G::PAIRS; ++pi) {
             const int pair = wave * G::PAIRS + pi;
@@ -536,8 +596,6 @@ __global__ __launch_bounds__(kThreads) void projection_mfma_kernel(const float *
                 acc = __builtin_amdgcn_mfma_f32_32x32x2f32(arow[2 * kk], brow[2 * kk], acc, 0, 0, 0);
             const int o = ob * 32 + r32;
             const float bo = bias ? bias[o] : 0.0f;
-            const long long bseq = u / tps32;
-            const int tb32 = static_cast<int>(u % tps32) * 32;
             if constexpr (TILED) {
                 const int g = o / DG, cch = o % DG;
                 v4f *dst = reinterpret_cast<v4f *>(out + static_cast<size_t>(u) * (32 * O));
@@ -545,9 +603,11 @@ __global__ __launch_bounds__(kThreads) void projection_mfma_kernel(const float *
                 for (int q = 0; q < 4; ++q) {
                     v4f w;
                     w[0] = acc[4 * q] + bo; w[1] = acc[4 * q + 1] + bo; w[2] = acc[4 * q + 2] + bo; w[3] = acc[4 * q + 3] + bo;
-                    dst[((g * 4 + q) * 2 + hf) * DG + cch] = w;
+                    __builtin_nontemporal_store(w, dst + ((g * 4 + q) * 2 + hf) * DG + cch);
                 }
             } else {
+                const long long bseq = u / tps32;
+                const int tb32 = static_cast<int>(u - bseq * tps32) * 32;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int t = tb32 + acc_row(v, hf);
@@ -605,8 +665,9 @@ int launch_proj_mfma(const float *x, const float *U, const float *bias, float *p
 
 template <int D>
 int launch_gru_step(const float *Whh, const float *bhh, const float *pt, const float *s0, float *s_even, float *s_odd,
-                    const int *sel, const int *skip, const int *all_done, unsigned *res_tile, int B, int T,
-                    void *state, hipStream_t stream)
+                    SolveControl *ctl, int *done, int *iters, int *status, float *resid, float tol, int max_iter,
+                    unsigned *res_bits, unsigned *res_tile, int B, int T, bool zero_start, void *state,
+                    hipStream_t stream)
 {
     using G = GruGeom<D>;
     static int cap = 0;
@@ -617,7 +678,8 @@ int launch_gru_step(const float *Whh, const float *bhh, const float *pt, const f
     auto *hdr = static_cast<ScanHeader *>(state);
     auto *desc = reinterpret_cast<unsigned long long *>(static_cast<char *>(state) + sizeof(ScanHeader));
     hipLaunchKernelGGL((gru_quasi_step_kernel<D>), dim3(grid), dim3(kThreads), 0, stream, Whh, bhh, pt, s0, s_even,
-                       s_odd, sel, skip, all_done, res_tile, T, tps, B, ntiles, hdr, desc);
+                       s_odd, ctl, done, iters, status, resid, tol, max_iter, res_bits, res_tile, T, tps, B, ntiles,
+                       zero_start ? 1 : 0, hdr, desc);
     DEER_HIP(hipGetLastError());
     return DEER_OK;
 }
@@ -672,14 +734,17 @@ size_t gru_step_state_bytes(int B, int T, int D)
 }
 
 int launch_gru_quasi_step(const float *Whh, const float *bhh, const float *pt, const float *s0, float *s_even,
-                          float *s_odd, const int *sel, const int *skip, const int *all_done, unsigned *res_tile,
-                          int B, int T, int D, void *state, hipStream_t stream)
+                          float *s_odd, SolveControl *ctl, int *done, int *iters, int *status, float *resid,
+                          float tol, int max_iter, unsigned *res_bits, unsigned *res_tile, int B, int T, int D,
+                          bool zero_start, void *state, hipStream_t stream)
 {
     if (B == 0 || T == 0) return DEER_OK;
     if (D == 64)
-        return launch_gru_step<64>(Whh, bhh, pt, s0, s_even, s_odd, sel, skip, all_done, res_tile, B, T, state, stream);
+        return launch_gru_step<64>(Whh, bhh, pt, s0, s_even, s_odd, ctl, done, iters, status, resid, tol, max_iter,
+                                   res_bits, res_tile, B, T, zero_start, state, stream);
     if (D == 32)
-        return launch_gru_step<32>(Whh, bhh, pt, s0, s_even, s_odd, sel, skip, all_done, res_tile, B, T, state, stream);
+        return launch_gru_step<32>(Whh, bhh, pt, s0, s_even, s_odd, ctl, done, iters, status, resid, tol, max_iter,
+                                   res_bits, res_tile, B, T, zero_start, state, stream);
     return fail(DEER_ERR_UNSUPPORTED, "fused GRU step needs D = 32 or 64");
 }
 

@@ -44,6 +44,67 @@ struct Carve {
     }
 };
 
+// ------------------------------------------------------------ solve control
+// Device-side state of one deer_solve call.
+struct SolveControl {
+    int iter;       // current iteration index i (iterate s^(i) lives in buffer i % 2)
+    int all_done;   // 1 once every sequence has stopped
+    int pad[62];
+};
+
+// Convergence test of iteration i = ctl->iter for every sequence, run by one
+// whole workgroup (blockDim.x a multiple of 64, at most 1024; `red` is a
+// __shared__ array of blockDim.x / 64 words).  A sequence passes when the max
+// residual of its iterate is <= tol and is then frozen with iters = i; at the
+// cap it stops as not converged, or non-finite for a NaN / Inf residual.  The
+// residual is one word per sequence (res_bits, reset here) or per-tile maxima
+// (res_tile, tps words per sequence).  Non-negative floats order like their
+// bit patterns and NaN patterns sit above +Inf, so maxima are taken on bits.
+__device__ inline void finalize_iteration(SolveControl *ctl, unsigned *res_bits, const unsigned *res_tile, int tps,
+                                          int *done, int *iters, int *status, float *resid, int B, float tol,
+                                          int max_iter, unsigned *red)
+{
+    const int i = ctl->iter;
+    int active = 0;
+    for (int b = 0; b < B; ++b) {
+        if (done[b]) continue;                    // same for every thread
+        unsigned m = 0u;
+        if (res_tile) {
+            for (int k = threadIdx.x; k < tps; k += blockDim.x) m = max(m, res_tile[static_cast<size_t>(b) * tps + k]);
+            for (int o = 32; o > 0; o >>= 1) m = max(m, static_cast<unsigned>(__shfl_xor(static_cast<int>(m), o, 64)));
+            if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+            __syncthreads();
+            m = red[0];
+            for (int w = 1; w < static_cast<int>(blockDim.x / 64); ++w) m = max(m, red[w]);
+            __syncthreads();
+        } else {
+            m = res_bits[b];
+        }
+        if (threadIdx.x == 0) {
+            const float r = __uint_as_float(m);
+            if (!res_tile) res_bits[b] = 0u;
+            if (r <= tol) {
+                done[b] = 1;
+                iters[b] = i;
+                status[b] = DEER_SEQ_CONVERGED;
+                resid[b] = r;
+            } else if (i >= max_iter) {
+                done[b] = 1;
+                iters[b] = max_iter;
+                status[b] = __builtin_isfinite(r) ? DEER_SEQ_NOT_CONVERGED : DEER_SEQ_NONFINITE;
+                resid[b] = r;
+            } else {
+                active = 1;
+            }
+        }
+    }
+    active = __syncthreads_or(active);
+    if (threadIdx.x == 0) {
+        if (active) ctl->iter = i + 1;
+        else ctl->all_done = 1;
+    }
+}
+
 // ------------------------------------------------------ diagonal scan state
 // Look-back state kept in a workspace between launches.  Zero-filled once by
 // the caller; every launch leaves done = 0 and advances epoch.
@@ -137,9 +198,14 @@ int launch_projection_mfma(const float *x, const float *U, const float *bias, fl
 // every TP-position tile (gru_step_tile(D) positions).
 int gru_step_tile(int D);
 size_t gru_step_state_bytes(int B, int T, int D);
+// The workgroup that finishes last also runs finalize_iteration(), so one
+// launch is a whole iteration.  Residual maxima go to res_bits (one word per
+// sequence, zero on entry) for up to 256 sequences, else to res_tile.  zero_start: the iterate s^(0) is all zeros and
+// is not read from memory at iteration 0.
 int launch_gru_quasi_step(const float *Whh, const float *bhh, const float *pt, const float *s0, float *s_even,
-                          float *s_odd, const int *sel, const int *skip, const int *all_done,
-                          unsigned *res_tile, int B, int T, int D, void *state, hipStream_t stream);
+                          float *s_odd, SolveControl *ctl, int *done, int *iters, int *status, float *resid,
+                          float tol, int max_iter, unsigned *res_bits, unsigned *res_tile, int B, int T, int D,
+                          bool zero_start, void *state, hipStream_t stream);
 
 int launch_rollout(const deer_cell_params_t *p, const float *x, const float *s0, int B, int T,
                    float *traj, hipStream_t stream);

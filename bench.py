@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-scan", action="store_true", help="skip the standalone scan measurement")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work for the baseline sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="first run a plain 1 GiB device copy (the reference kernel for HBM counter scaling)")
     return ap.parse_args()
 
 
@@ -80,30 +82,54 @@ def solve_workload(args, dev):
     return w, p, ms_per_step, start.elapsed_time(stop) / args.steps, prof, np.array(iters_seen)
 
 
+def _source_sha(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic(kernel, source):
+    """HBM bytes per launch from committed rocprofv3 counters, if they were taken on this source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha") != _source_sha(source):
+        return None                       # the kernel changed since the counters were taken
+    return rec.get("bytes_per_launch")
+
+
 def roofline_of(w, prof):
-    """Dominant kernel of the solve and its algorithmic rate per launch."""
+    """Dominant kernel of the solve and its algorithmic rate per launch.
+
+    The quasi-DEER GRU iteration is one fused launch: per position it reads the
+    iterate s^(i) (D words) and the input projection (3D words) and writes
+    s^(i+1) (D words), and it runs the 3D x D recurrent product on the matrix
+    cores (2 * 3D * D flops).
+    """
     from evaluation_nonlinear_rnns_amd import deer
     BT = w.B * w.T
-    # GRU evaluation: read s (D) and the projection (3D), write a and b (2D) per position
-    eval_bytes = BT * w.D * 4 * (1 + 3 + 2)
-    eval_flops = BT * 2 * 3 * w.D * w.D
-    # diagonal scan: read a, b, write s
-    scan_bytes = BT * w.D * 4 * 3
+    step_bytes = BT * w.D * 4 * (1 + 3 + 1)
+    step_flops = BT * 2 * 3 * w.D * w.D
     n_e, ms_e = prof[deer.PROFILE_EVAL]
-    n_s, ms_s = prof[deer.PROFILE_SCAN]
+    n_p, ms_p = prof[deer.PROFILE_PROJECTION]
     kernels = {
-        "gru_eval": {"launches": n_e, "avg_ms": ms_e / max(n_e, 1), "bytes": eval_bytes, "flops": eval_flops},
-        "diag_scan": {"launches": n_s, "avg_ms": ms_s / max(n_s, 1), "bytes": scan_bytes, "flops": 2 * BT * w.D},
+        "gru_quasi_step": {"launches": n_e, "avg_ms": ms_e / max(n_e, 1), "bytes": step_bytes, "flops": step_flops},
+        "input_projection": {"launches": n_p, "avg_ms": ms_p / max(n_p, 1),
+                             "bytes": BT * 4 * (w.M + 3 * w.D), "flops": BT * 2 * 3 * w.D * w.M},
     }
-    # over-enqueued launches after convergence exit at once; time only counts real work
-    dom = "gru_eval" if ms_e >= ms_s else "diag_scan"
-    k = kernels[dom]
-    achieved = k["bytes"] / (k["avg_ms"] * 1e-3) / 1e9
-    return dom, kernels, {
+    k = kernels["gru_quasi_step"]
+    sec = k["avg_ms"] * 1e-3
+    achieved = k["bytes"] / sec / 1e9
+    tflops = k["flops"] / sec / 1e12
+    src = os.path.join(ROOT, "evaluation_nonlinear_rnns_amd", "csrc", "cell_mfma.hip")
+    return "gru_quasi_step", kernels, {
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-        "kernel": dom, "avg_launch_ms": round(k["avg_ms"], 4),
+        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": _traffic("gru_quasi_step", src),
+        "kernel": "gru_quasi_step", "avg_launch_ms": round(k["avg_ms"], 4),
         "algorithmic_bytes_per_launch": k["bytes"],
+        "mfma_tflops": round(tflops, 2), "mfma_frac": round(tflops / MFMA_F32_PEAK_TFLOPS, 4),
     }
 
 
@@ -174,6 +200,12 @@ def main():
         hb.build()
     dev = torch.device("cuda:0")
     deer.load_library()
+    if args.copy_probe:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     w, p, ms_per_step, ms_events, prof, iters = solve_workload(args, dev)
     dom, kernels, roof = roofline_of(w, prof)

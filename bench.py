@@ -9,8 +9,11 @@ every sequence has converged.  Inputs are resident in HBM before timing.
 Prints one JSON line: converged trajectory steps per second (B*T / time per
 solve), the roofline of the dominant kernel (timed live with HIP events on
 the solver's stream), the oracle's sequential CPU rollout of the same
-workload as a reported baseline, and the standalone diagonal linear scan
-(B=32, T=131072, D=256) in GB/s against the HBM peak.
+workload as a reported baseline, the standalone diagonal linear scan
+(B=32, T=131072, D=256) in GB/s against the HBM peak, the dense-Jacobian DEER
+solve of the tanh RNN (B=64, T=16384, D=32) with its chunk-compose rate on the
+matrix cores, and the gain sweep of the D=16 tanh RNN (B=32, T=4096) against
+the sequential GPU rollout.
 """
 import argparse
 import json
@@ -35,6 +38,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-scan", action="store_true", help="skip the standalone scan measurement")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the dense-DEER and gain-sweep measurements")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work for the baseline sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run a plain 1 GiB device copy (the reference kernel for HBM counter scaling)")
@@ -163,6 +168,104 @@ def scan_bandwidth(args, dev):
             "elements_per_s": w.B * w.T * w.D / (ms * 1e-3)}
 
 
+def _time_solves(step, reps, stream):
+    import torch
+    from evaluation_nonlinear_rnns_amd import deer
+    step()
+    torch.cuda.synchronize()
+    for k in range(4):
+        deer.deer_profile_read(k)
+    deer.deer_profile_enable(True)
+    t0 = time.perf_counter()
+    out = None
+    for _ in range(reps):
+        out = step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / reps
+    deer.deer_profile_enable(False)
+    prof = {k: deer.deer_profile_read(k) for k in range(4)}
+    return ms, prof, out
+
+
+def dense_solve(args, dev):
+    """Dense-Jacobian DEER on the tanh RNN (B=64, T=16384, D=32).
+
+    Per iteration the linear solve composes the factored Jacobians
+    A_t = diag(1 - s_t^2) W inside chunks: one D x D x D product per position,
+    2 D^3 flops, on the matrix cores; that figure over the whole linear-solve
+    time (compose, carry and replay launches) is the reported compose rate.
+    """
+    import torch
+    from evaluation_nonlinear_rnns_amd import deer, inputs as I
+
+    w = I.WORKLOADS["tanh_d32_t16384"]
+    p = I.workload_problem(w.name)
+    cell = deer.cell_from_problem(p, dev)
+    x = torch.from_numpy(p["x"]).to(dev)
+    out = torch.empty((w.B, w.T, w.D), dtype=torch.float32, device=dev)
+    ws = deer.new_workspace(deer.deer_workspace_size(cell, w.B, w.T, w.mode), device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        return deer.deer_solve(cell, x, None, mode=w.mode, tol=w.tol, max_iter=w.max_iter, out=out, workspace=ws,
+                               stream=stream)
+
+    ms, prof, res = _time_solves(step, max(3, args.steps // 2), stream)
+    _, iters, _, status, rc = res
+    n_s, ms_s = prof[deer.PROFILE_SCAN]
+    n_e, ms_e = prof[deer.PROFILE_EVAL]
+    scan_ms = ms_s / max(n_s, 1)
+    flops = 2 * w.B * w.T * w.D ** 3
+    tflops = flops / (scan_ms * 1e-3) / 1e12
+    return {"workload": w.name, "B": w.B, "T": w.T, "D": w.D, "rc": int(rc),
+            "iterations": sorted(set(int(v) for v in iters)),
+            "ms_per_solve": round(ms, 3), "B*T/s": round(w.B * w.T / (ms * 1e-3), 1),
+            "linear_solve_avg_ms": round(scan_ms, 4), "eval_avg_ms": round(ms_e / max(n_e, 1), 4),
+            "compose_flops_per_launch": flops, "compose_tflops": round(tflops, 2),
+            "compose_frac_of_fp32_mfma_peak": round(tflops / MFMA_F32_PEAK_TFLOPS, 4)}
+
+
+def gain_sweep(args, dev):
+    """Dense DEER against the sequential GPU rollout across the recurrent gain g.
+
+    The gain sets the largest Lyapunov exponent; the sweep locates the g where
+    the parallel solve stops beating the sequential evaluation.  At g = 2 the
+    linear solve accumulates in double (float32 chunk products are too large).
+    """
+    import torch
+    from evaluation_nonlinear_rnns_amd import deer, inputs as I
+
+    w = I.WORKLOADS["tanh_d16_t4096_sweep"]
+    stream = torch.cuda.current_stream()
+    rows = []
+    for g in w.gains:
+        p = I.workload_problem(w.name, gain=g)
+        cell = deer.cell_from_problem(p, dev)
+        x = torch.from_numpy(p["x"]).to(dev)
+        f64 = g >= 2.0
+        out = torch.empty((w.B, w.T, w.D), dtype=torch.float32, device=dev)
+        ws = deer.new_workspace(deer.deer_workspace_size(cell, w.B, w.T, w.mode, scan_f64=f64), device=dev)
+
+        def step():
+            return deer.deer_solve(cell, x, None, mode=w.mode, tol=w.tol, max_iter=w.max_iter, out=out,
+                                   workspace=ws, stream=stream, scan_f64=f64)
+
+        ms, _, res = _time_solves(step, 3, stream)
+        _, iters, _, status, rc = res
+        seq = torch.empty_like(out)
+
+        def roll():
+            return deer.deer_rollout(cell, x, None, out=seq, stream=stream)
+
+        ms_seq, _, _ = _time_solves(roll, 3, stream)
+        rows.append({"gain": g, "scan_f64": f64, "rc": int(rc), "iterations_max": int(iters.max()),
+                     "iterations_median": float(np.median(iters)), "deer_ms": round(ms, 3),
+                     "rollout_ms": round(ms_seq, 3), "speedup_vs_rollout": round(ms_seq / ms, 3)})
+    slower = [r["gain"] for r in rows if r["speedup_vs_rollout"] < 1.0]
+    return {"workload": w.name, "B": w.B, "T": w.T, "D": w.D, "rows": rows,
+            "crossover_gain": min(slower) if slower else None}
+
+
 def cpu_baseline(args, w, p):
     """The oracle's float32 sequential rollout of the same workload on the host cores."""
     from oracle import oracle as O
@@ -233,6 +336,9 @@ def main():
     }
     if not args.no_scan:
         line["linear_scan"] = scan_bandwidth(args, dev)
+    if not args.no_dense:
+        line["dense_deer"] = dense_solve(args, dev)
+        line["gain_sweep"] = gain_sweep(args, dev)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(args, w, p)
     print(json.dumps(line), flush=True)

@@ -173,8 +173,11 @@ unsigned grid_for(size_t n, unsigned threads = 256, unsigned cap = 8192)
 }
 
 // ------------------------------------------------------ argument checks
-int check_cell(const deer_cell_params_t *p, int mode)
+int check_cell(const deer_cell_params_t *p, int mode_flags)
 {
+    const int mode = mode_flags & ~DEER_SCAN_F64;
+    if ((mode_flags & DEER_SCAN_F64) && mode != DEER_MODE_DENSE)
+        return fail(DEER_ERR_UNSUPPORTED, "DEER_SCAN_F64 applies to dense mode only");
     if (!p) return fail(DEER_ERR_INVALID, "cell parameters: null pointer");
     if (p->cell != DEER_CELL_TANH && p->cell != DEER_CELL_GRU)
         return fail(DEER_ERR_INVALID, "cell parameters: unknown cell " + std::to_string(p->cell));
@@ -221,8 +224,10 @@ struct SolveLayout {
     size_t bytes = 0;
 };
 
-SolveLayout solve_layout(void *ws, const deer_cell_params_t *p, int B, int T, int mode)
+SolveLayout solve_layout(void *ws, const deer_cell_params_t *p, int B, int T, int mode_flags)
 {
+    const int mode = mode_flags & ~DEER_SCAN_F64;
+    const bool f64 = (mode_flags & DEER_SCAN_F64) != 0;
     const size_t BTD = static_cast<size_t>(B) * T * p->D;
     const int PD = (p->cell == DEER_CELL_GRU) ? 3 * p->D : p->D;
     Carve c(ws);
@@ -231,7 +236,7 @@ SolveLayout solve_layout(void *ws, const deer_cell_params_t *p, int B, int T, in
     const bool fused = fused_gru_step(p, mode);
     const size_t scan_bytes = fused ? gru_step_state_bytes(B, T, p->D)
                               : (mode == DEER_MODE_DIAG) ? diag_scan_state_bytes(B, T, p->D)
-                                                         : dense_scan_state_bytes(B, T, p->D);
+                                                         : dense_scan_state_bytes(B, T, p->D, f64);
     L.scan = c.take<char>(scan_bytes);
     L.ctl = c.take<SolveControl>(1);
     L.res_bits = c.take<unsigned>(B);
@@ -340,18 +345,18 @@ int linear_scan_dense(const float *A, const float *b, const float *s0, float *s,
     if (s == b || s == A) return fail(DEER_ERR_INVALID, "linear_scan_dense: s must not alias A or b");
     rc = check_workspace(workspace, ws_bytes, dense_scan_state_bytes(B, T, D), "linear_scan_dense");
     if (rc) return rc;
-    return launch_dense_scan(A, nullptr, nullptr, b, s0, s, s, nullptr, nullptr, nullptr, B, T, D, workspace,
+    return launch_dense_scan(A, nullptr, nullptr, b, s0, s, s, nullptr, nullptr, nullptr, B, T, D, false, workspace,
                              static_cast<hipStream_t>(stream));
 }
 
-int deer_workspace_size(const deer_cell_params_t *p, int B, int T, int mode, size_t *bytes_out)
+int deer_workspace_size(const deer_cell_params_t *p, int B, int T, int mode_flags, size_t *bytes_out)
 {
     if (!bytes_out) return fail(DEER_ERR_INVALID, "deer_workspace_size: null output");
-    int rc = check_cell(p, mode);
+    int rc = check_cell(p, mode_flags);
     if (rc) return rc;
     rc = check_sizes(B, T);
     if (rc) return rc;
-    *bytes_out = solve_layout(nullptr, p, B, T, mode).bytes;
+    *bytes_out = solve_layout(nullptr, p, B, T, mode_flags).bytes;
     return DEER_OK;
 }
 
@@ -368,11 +373,13 @@ int deer_rollout(const deer_cell_params_t *p, const float *x, const float *s0, i
     return launch_rollout(p, x, s0, B, T, traj_out, static_cast<hipStream_t>(stream));
 }
 
-int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int B, int T, int mode, float tol,
-               int max_iter, const float *init_guess, float *traj_out, int *iters_out, float *resid_out,
+int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int B, int T, int mode_flags,
+               float tol, int max_iter, const float *init_guess, float *traj_out, int *iters_out, float *resid_out,
                int *status_out, void *workspace, size_t ws_bytes, void *stream_)
 {
-    int rc = check_cell(p, mode);
+    int rc = check_cell(p, mode_flags);
+    const int mode = mode_flags & ~DEER_SCAN_F64;
+    const bool scan_f64 = (mode_flags & DEER_SCAN_F64) != 0;
     if (rc) return rc;
     rc = check_sizes(B, T);
     if (rc) return rc;
@@ -391,12 +398,12 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
         return pass ? DEER_OK : DEER_NOT_CONVERGED;
     }
     if (!x || !traj_out) return fail(DEER_ERR_INVALID, "x and traj_out are required");
-    rc = check_workspace(workspace, ws_bytes, solve_layout(nullptr, p, B, T, mode).bytes, "deer_solve");
+    rc = check_workspace(workspace, ws_bytes, solve_layout(nullptr, p, B, T, mode_flags).bytes, "deer_solve");
     if (rc) return rc;
     if (!g_poll.host) return fail(DEER_ERR_HIP, "deer_solve: pinned host memory unavailable");
 
     hipStream_t stream = static_cast<hipStream_t>(stream_);
-    const SolveLayout L = solve_layout(workspace, p, B, T, mode);
+    const SolveLayout L = solve_layout(workspace, p, B, T, mode_flags);
     const int D = p->D;
     const size_t BTD = static_cast<size_t>(B) * T * D;
     const bool gru = p->cell == DEER_CELL_GRU;
@@ -454,7 +461,7 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
             r = launch_diag_scan(L.lin, L.bvec, s0, traj_out, L.buf1, sel, L.done, all_done, B, T, D, L.scan, stream);
         else
             r = launch_dense_scan(nullptr, L.lin, p->W, L.bvec, s0, traj_out, L.buf1, sel, L.done, all_done, B, T, D,
-                                  L.scan, stream);
+                                  scan_f64, L.scan, stream);
         prof.end();
         return r;
     };

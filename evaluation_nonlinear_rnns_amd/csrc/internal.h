@@ -146,13 +146,14 @@ struct DenseScanPlan {
     int nchunk;     // chunks per sequence
 };
 DenseScanPlan dense_scan_plan(int B, int T, int D);
-size_t dense_scan_state_bytes(int B, int T, int D);
+size_t dense_scan_state_bytes(int B, int T, int D, bool f64 = false);
 
 // Dense scan s_t = A_t s_{t-1} + b_t.  Either A (materialised [B,T,D,D]) or
-// the factored form A_t = diag(d_t) W (d [B,T,D], W [D,D]) is given.
+// the factored form A_t = diag(d_t) W (d [B,T,D], W [D,D]) is given.  f64:
+// products, offsets, carries and replayed states accumulate in double.
 int launch_dense_scan(const float *A, const float *d, const float *W, const float *b,
                       const float *s0, float *out0, float *out1, const int *out_sel,
-                      const int *skip, const int *all_done, int B, int T, int D, void *state,
+                      const int *skip, const int *all_done, int B, int T, int D, bool f64, void *state,
                       hipStream_t stream);
 
 // ---------------------------------------------------------- cell kernels

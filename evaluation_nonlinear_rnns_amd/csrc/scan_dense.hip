@@ -12,27 +12,35 @@
 // A_t is either materialised ([B,T,D,D]) or given in the factored form
 // A_t = diag(d_t) W of a tanh cell's Jacobian, so W stays on chip.
 //
-// One wavefront handles 64 / DP chunks at once (DP = D rounded up to a power
-// of two): lane j of a chunk's lane group holds column j of the running
-// product P and component j of the running offset.
+// The products P_c are the one dense contraction of the path (2 D^3 flops per
+// step).  For factored leaves with D = 32 (and D = 16) they run on the matrix
+// cores: P <- diag(d_t) (W P) is one 32 x 32 x 32 product per step, and with
+// the K order permuted to follow the accumulator layout, the accumulators of
+// one step are the B operands of the next -- the product never leaves the
+// registers of the wavefront that owns the chunk.
+//
+// ACC is the accumulation type of the products, offsets, carries and replayed
+// states (float, or double for unpredictable dynamics where chunk products
+// grow large enough that float32 rounding breaks the consistency of the
+// solution at chunk boundaries); inputs and outputs are float32.
 #include "internal.h"
 
 namespace deer {
 namespace {
 
 constexpr int kThreads = 256;
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef double v4d __attribute__((ext_vector_type(4)));
 
-template <int DP>
-__device__ __forceinline__ float group_shfl(float v, int gbase, int k)
-{
-    return __shfl(v, gbase + k, 64);
-}
-
-template <int DP, bool FACT>
+// --------------------------------------------------------- generic (VALU)
+// One wavefront handles 64 / DP chunks: lane j of a chunk's lane group holds
+// column j of the running product and component j of the running offset.
+template <int DP, bool FACT, class ACC>
 __global__ __launch_bounds__(kThreads) void dense_agg_kernel(
     const float *__restrict__ A, const float *__restrict__ dv, const float *__restrict__ W,
     const float *__restrict__ bv, const int *__restrict__ skip, const int *__restrict__ all_done, int B,
-    int T, int D, int L, int nchunk, float *__restrict__ Pout, float *__restrict__ Bout)
+    int T, int D, int L, int nchunk, ACC *__restrict__ Pout, ACC *__restrict__ Bout)
 {
     if (all_done && *all_done) return;
     constexpr int G = 64 / DP;
@@ -59,58 +67,57 @@ __global__ __launch_bounds__(kThreads) void dense_agg_kernel(
     const size_t seq = static_cast<size_t>(bseq) * T;
     const bool jv = j < D;
 
-    auto Aget = [&](int t, int i, int k) -> float {
-        return (i < D && k < D) ? A[((seq + t) * D + i) * D + k] : 0.0f;
+    auto Aget = [&](int t, int i, int k) -> ACC {
+        return (i < D && k < D) ? static_cast<ACC>(A[((seq + t) * D + i) * D + k]) : ACC(0);
     };
 
-    float P[DP];
-    float Bq;
+    ACC P[DP];
+    ACC Bq;
     {
         const int t = t0;
         if constexpr (FACT) {
-            const float dj = jv ? dv[(seq + t) * D + j] : 0.0f;
+            const ACC dj = jv ? static_cast<ACC>(dv[(seq + t) * D + j]) : ACC(0);
 #pragma unroll
-            for (int i = 0; i < DP; ++i) P[i] = group_shfl<DP>(dj, gbase, i) * Wr[i][j];
+            for (int i = 0; i < DP; ++i) P[i] = __shfl(dj, gbase + i, 64) * static_cast<ACC>(Wr[i][j]);
         } else {
 #pragma unroll
             for (int i = 0; i < DP; ++i) P[i] = Aget(t, i, j);
         }
-        Bq = jv ? bv[(seq + t) * D + j] : 0.0f;
+        Bq = jv ? static_cast<ACC>(bv[(seq + t) * D + j]) : ACC(0);
     }
     for (int s = 1; s < L; ++s) {
         const int t = t0 + s;
         const bool live = t < t1;
         const int tt = live ? t : t0;
-        const float bj = jv ? bv[(seq + tt) * D + j] : 0.0f;
-        float Pn[DP];
-        float Bn;
+        const ACC bj = jv ? static_cast<ACC>(bv[(seq + tt) * D + j]) : ACC(0);
+        ACC Pn[DP];
+        ACC Bn;
         if constexpr (FACT) {
-            const float dj = jv ? dv[(seq + tt) * D + j] : 0.0f;
+            const ACC dj = jv ? static_cast<ACC>(dv[(seq + tt) * D + j]) : ACC(0);
 #pragma unroll
             for (int i = 0; i < DP; ++i) {
-                // keep W in LDS: re-read each row instead of hoisting DP*DP values into registers
-                asm volatile("" ::: "memory");
-                float acc = 0.0f;
+                asm volatile("" ::: "memory");   // keep W in LDS rather than in registers
+                ACC acc = 0;
 #pragma unroll
-                for (int k = 0; k < DP; ++k) acc += Wb[i][k] * P[k];
-                Pn[i] = group_shfl<DP>(dj, gbase, i) * acc;
+                for (int k = 0; k < DP; ++k) acc += static_cast<ACC>(Wb[i][k]) * P[k];
+                Pn[i] = __shfl(dj, gbase + i, 64) * acc;
             }
-            float accb = 0.0f;
+            ACC accb = 0;
 #pragma unroll
-            for (int k = 0; k < DP; ++k) accb += Wr[j][k] * group_shfl<DP>(Bq, gbase, k);
+            for (int k = 0; k < DP; ++k) accb += static_cast<ACC>(Wr[j][k]) * __shfl(Bq, gbase + k, 64);
             Bn = dj * accb + bj;
         } else {
 #pragma unroll
             for (int i = 0; i < DP; ++i) {
                 asm volatile("" ::: "memory");   // bound the loads in flight to one row
-                float acc = 0.0f;
+                ACC acc = 0;
 #pragma unroll
                 for (int k = 0; k < DP; ++k) acc += Aget(tt, i, k) * P[k];
                 Pn[i] = acc;
             }
-            float accb = 0.0f;
+            ACC accb = 0;
 #pragma unroll
-            for (int k = 0; k < DP; ++k) accb += Aget(tt, j, k) * group_shfl<DP>(Bq, gbase, k);
+            for (int k = 0; k < DP; ++k) accb += Aget(tt, j, k) * __shfl(Bq, gbase + k, 64);
             Bn = accb + bj;
         }
         if (live) {
@@ -128,32 +135,207 @@ __global__ __launch_bounds__(kThreads) void dense_agg_kernel(
     }
 }
 
+// ------------------------------------------------ matrix-core aggregates
+// Row of the 32x32 accumulator held in register v by a lane of half hf.
+__device__ __forceinline__ int row32(int v, int hf) { return 8 * (v >> 2) + 4 * hf + (v & 3); }
+
+// D = 32, factored leaves, float32: one 64-lane workgroup per chunk.
+//   A operand (W):      lane l, instruction v holds W[l % 32][row32(v, l / 32)]
+//   B operand (P_old):  lane l, instruction v holds P_old[row32(v, l / 32)][l % 32] = accumulator v
+//   result:             C[i][j] = sum_k W[i][k] P_old[k][j], then row i scaled by d_t[i]
+// The offset B_c advances on VALU with the broadcast of the previous offset.
+__global__ __launch_bounds__(64) void dense_agg_mfma32_kernel(const float *__restrict__ dv, const float *__restrict__ W,
+                                                            const float *__restrict__ bv, const int *__restrict__ skip,
+                                                            const int *__restrict__ all_done, int T, int L, int nchunk,
+                                                            float *__restrict__ Pout, float *__restrict__ Bout)
+{
+    constexpr int D = 32;
+    if (all_done && *all_done) return;
+    __shared__ float ds[64 * D], bs[64 * D];     // the chunk's d_t and b_t rows (L <= 64)
+    const int lane = threadIdx.x, j = lane & 31, hf = lane >> 5;
+    const long long q = blockIdx.x;
+    const int bseq = static_cast<int>(q / nchunk), c = static_cast<int>(q % nchunk);
+    if (skip && skip[bseq]) return;
+    const int t0 = c * L, n = min(L, T - t0);
+    const size_t seq = static_cast<size_t>(bseq) * T;
+    for (int e = lane; e < n * (D / 4); e += 64) {
+        const int r = e / (D / 4), col = (e % (D / 4)) * 4;
+        const size_t g = (seq + t0 + r) * D + col;
+        *reinterpret_cast<v4f *>(ds + r * D + col) = *reinterpret_cast<const v4f *>(dv + g);
+        *reinterpret_cast<v4f *>(bs + r * D + col) = *reinterpret_cast<const v4f *>(bv + g);
+    }
+    float WA[16], Wcol[16], Wrow[D];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        WA[v] = W[j * D + row32(v, hf)];
+        Wcol[v] = W[row32(v, hf) * D + j];
+    }
+#pragma unroll
+    for (int k = 0; k < D; ++k) Wrow[k] = W[j * D + k];
+    __syncthreads();
+
+    v16f P;
+    {
+        const v4f *d0 = reinterpret_cast<const v4f *>(ds);
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+            const v4f dq = d0[2 * qd + hf];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) P[4 * qd + r] = dq[r] * Wcol[4 * qd + r];
+        }
+    }
+    float Bq = bs[j];
+    for (int s = 1; s < n; ++s) {
+        v16f acc = {};
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(WA[v], P[v], acc, 0, 0, 0);
+        const v4f *drow = reinterpret_cast<const v4f *>(ds + s * D);
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+            const v4f dq = drow[2 * qd + hf];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) P[4 * qd + r] = dq[r] * acc[4 * qd + r];
+        }
+        float sum = 0.0f;
+#pragma unroll
+        for (int k = 0; k < D; ++k) sum += Wrow[k] * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Bq), k));
+        Bq = ds[s * D + j] * sum + bs[s * D + j];
+    }
+    float *po = Pout + static_cast<size_t>(q) * D * D;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) po[row32(v, hf) * D + j] = P[v];
+    if (hf == 0) Bout[static_cast<size_t>(q) * D + j] = Bq;
+}
+
+// D = 16, factored leaves, float32 (16x16x4) or float64 (16x16x4 f64).
+// Accumulator v of lane l holds C[row16(v, l / 16)][l % 16]: rows 4 (l / 16) + v
+// for the float32 instruction, l / 16 + 4 v for the float64 one (measured lane
+// layouts).  The running product is fed back as the B operand of the next step,
+// so instruction u contracts over k = row16(u, l / 16):
+//   A operand (W):      lane l, instruction u holds W[l % 16][row16(u, l / 16)]
+//   B operand (P_old):  lane l, instruction u holds P_old[row16(u, l / 16)][l % 16] = accumulator u
+template <class ACC>
+__device__ __forceinline__ int row16(int v, int g)
+{
+    return sizeof(ACC) == 8 ? g + 4 * v : 4 * g + v;
+}
+
+template <class ACC>
+__device__ __forceinline__ void mfma16(ACC a, ACC b, ACC (&acc)[4]);
+
+template <>
+__device__ __forceinline__ void mfma16<float>(float a, float b, float (&acc)[4])
+{
+    v4f c = {acc[0], acc[1], acc[2], acc[3]};
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    acc[0] = c[0]; acc[1] = c[1]; acc[2] = c[2]; acc[3] = c[3];
+}
+
+template <>
+__device__ __forceinline__ void mfma16<double>(double a, double b, double (&acc)[4])
+{
+    v4d c = {acc[0], acc[1], acc[2], acc[3]};
+    c = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+    acc[0] = c[0]; acc[1] = c[1]; acc[2] = c[2]; acc[3] = c[3];
+}
+
+template <class ACC>
+__device__ __forceinline__ ACC lane_bcast(ACC v, int k);
+
+template <>
+__device__ __forceinline__ float lane_bcast<float>(float v, int k)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), k));
+}
+
+template <>
+__device__ __forceinline__ double lane_bcast<double>(double v, int k)
+{
+    const long long bits = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane(static_cast<int>(bits & 0xffffffffll), k);
+    const int hi = __builtin_amdgcn_readlane(static_cast<int>(bits >> 32), k);
+    return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned>(lo));
+}
+
+template <class ACC>
+__global__ __launch_bounds__(64) void dense_agg_mfma16_kernel(const float *__restrict__ dv, const float *__restrict__ W,
+                                                            const float *__restrict__ bv, const int *__restrict__ skip,
+                                                            const int *__restrict__ all_done, int T, int L, int nchunk,
+                                                            ACC *__restrict__ Pout, ACC *__restrict__ Bout)
+{
+    constexpr int D = 16;
+    if (all_done && *all_done) return;
+    __shared__ float ds[64 * D], bs[64 * D];
+    const int lane = threadIdx.x, j = lane & 15, g = lane >> 4;
+    const long long q = blockIdx.x;
+    const int bseq = static_cast<int>(q / nchunk), c = static_cast<int>(q % nchunk);
+    if (skip && skip[bseq]) return;
+    const int t0 = c * L, n = min(L, T - t0);
+    const size_t seq = static_cast<size_t>(bseq) * T;
+    for (int e = lane; e < n * (D / 4); e += 64) {
+        const int r = e / (D / 4), col = (e % (D / 4)) * 4;
+        const size_t gi = (seq + t0 + r) * D + col;
+        *reinterpret_cast<v4f *>(ds + r * D + col) = *reinterpret_cast<const v4f *>(dv + gi);
+        *reinterpret_cast<v4f *>(bs + r * D + col) = *reinterpret_cast<const v4f *>(bv + gi);
+    }
+    ACC WA[4], Wcol[4], Wrow[D];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        WA[u] = static_cast<ACC>(W[j * D + row16<ACC>(u, g)]);
+        Wcol[u] = static_cast<ACC>(W[row16<ACC>(u, g) * D + j]);
+    }
+#pragma unroll
+    for (int k = 0; k < D; ++k) Wrow[k] = static_cast<ACC>(W[j * D + k]);
+    __syncthreads();
+
+    ACC P[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) P[v] = static_cast<ACC>(ds[row16<ACC>(v, g)]) * Wcol[v];
+    ACC Bq = static_cast<ACC>(bs[j]);
+    for (int s = 1; s < n; ++s) {
+        ACC acc[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) mfma16<ACC>(WA[u], P[u], acc);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) P[v] = static_cast<ACC>(ds[s * D + row16<ACC>(v, g)]) * acc[v];
+        ACC sum = 0;
+#pragma unroll
+        for (int k = 0; k < D; ++k) sum += Wrow[k] * lane_bcast<ACC>(Bq, k);
+        Bq = static_cast<ACC>(ds[s * D + j]) * sum + static_cast<ACC>(bs[s * D + j]);
+    }
+    ACC *po = Pout + static_cast<size_t>(q) * D * D;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) po[row16<ACC>(v, g) * D + j] = P[v];
+    if (g == 0) Bout[static_cast<size_t>(q) * D + j] = Bq;
+}
+
+// ------------------------------------------------------------- carry walk
 // One wavefront per sequence walks its chunks in order.
-template <int DP>
+template <int DP, class ACC>
 __global__ __launch_bounds__(kThreads) void dense_carry_kernel(
-    const float *__restrict__ Pagg, const float *__restrict__ Bagg, const float *__restrict__ s0,
+    const ACC *__restrict__ Pagg, const ACC *__restrict__ Bagg, const float *__restrict__ s0,
     const int *__restrict__ skip, const int *__restrict__ all_done, int B, int D, int nchunk,
-    float *__restrict__ carry)
+    ACC *__restrict__ carry)
 {
     if (all_done && *all_done) return;
     const int lane = threadIdx.x & 63;
     const int bseq = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
     if (bseq >= B || (skip && skip[bseq])) return;    // uniform per wavefront
     const bool jv = lane < D;
-    float st = (jv && s0) ? s0[static_cast<size_t>(bseq) * D + lane] : 0.0f;
+    ACC st = (jv && s0) ? static_cast<ACC>(s0[static_cast<size_t>(bseq) * D + lane]) : ACC(0);
     const size_t q0 = static_cast<size_t>(bseq) * nchunk;
-    float row[DP];
+    ACC row[DP];
 #pragma unroll
-    for (int k = 0; k < DP; ++k) row[k] = (jv && k < D) ? Pagg[(q0 * D + lane) * D + k] : 0.0f;
+    for (int k = 0; k < DP; ++k) row[k] = (jv && k < D) ? Pagg[(q0 * D + lane) * D + k] : ACC(0);
     for (int c = 0; c < nchunk; ++c) {
         const size_t q = q0 + c;
         if (jv) carry[q * D + lane] = st;
         if (c == nchunk - 1) break;
-        const float bq = jv ? Bagg[q * D + lane] : 0.0f;
-        float nxt[DP];
+        const ACC bq = jv ? Bagg[q * D + lane] : ACC(0);
+        ACC nxt[DP];
 #pragma unroll
-        for (int k = 0; k < DP; ++k) nxt[k] = (jv && k < D && c + 1 < nchunk) ? Pagg[((q + 1) * D + lane) * D + k] : 0.0f;
-        float acc = 0.0f;
+        for (int k = 0; k < DP; ++k) nxt[k] = (jv && k < D) ? Pagg[((q + 1) * D + lane) * D + k] : ACC(0);
+        ACC acc = 0;
 #pragma unroll
         for (int k = 0; k < DP; ++k) acc += row[k] * __shfl(st, k, 64);
         st = acc + bq;
@@ -162,10 +344,11 @@ __global__ __launch_bounds__(kThreads) void dense_carry_kernel(
     }
 }
 
-template <int DP, bool FACT>
+// ----------------------------------------------------------------- replay
+template <int DP, bool FACT, class ACC>
 __global__ __launch_bounds__(kThreads) void dense_replay_kernel(
     const float *__restrict__ A, const float *__restrict__ dv, const float *__restrict__ W,
-    const float *__restrict__ bv, const float *__restrict__ carry, const int *__restrict__ skip,
+    const float *__restrict__ bv, const ACC *__restrict__ carry, const int *__restrict__ skip,
     const int *__restrict__ all_done, int B, int T, int D, int L, int nchunk, float *out0, float *out1,
     const int *__restrict__ out_sel)
 {
@@ -184,70 +367,98 @@ __global__ __launch_bounds__(kThreads) void dense_replay_kernel(
     const bool jv = j < D;
     float *out = (out_sel && (*out_sel & 1)) ? out1 : out0;
 
-    float wrow[FACT ? DP : 1];
+    ACC wrow[FACT ? DP : 1];
     if constexpr (FACT) {
 #pragma unroll
-        for (int k = 0; k < DP; ++k) wrow[k] = (jv && k < D) ? W[j * D + k] : 0.0f;
+        for (int k = 0; k < DP; ++k) wrow[k] = (jv && k < D) ? static_cast<ACC>(W[j * D + k]) : ACC(0);
     }
-    float st = jv ? carry[static_cast<size_t>(q) * D + j] : 0.0f;
+    ACC st = jv ? carry[static_cast<size_t>(q) * D + j] : ACC(0);
     for (int s = 0; s < L; ++s) {
         const int t = t0 + s;
         const bool live = t < t1;
         const int tt = live ? t : t0;
-        const float bj = jv ? bv[(seq + tt) * D + j] : 0.0f;
-        float acc = 0.0f;
+        const ACC bj = jv ? static_cast<ACC>(bv[(seq + tt) * D + j]) : ACC(0);
+        ACC acc = 0;
         if constexpr (FACT) {
 #pragma unroll
             for (int k = 0; k < DP; ++k) acc += wrow[k] * __shfl(st, gbase + k, 64);
-            const float dj = jv ? dv[(seq + tt) * D + j] : 0.0f;
+            const ACC dj = jv ? static_cast<ACC>(dv[(seq + tt) * D + j]) : ACC(0);
             acc = dj * acc + bj;
         } else {
 #pragma unroll
             for (int k = 0; k < DP; ++k) {
-                const float akj = (jv && k < D) ? A[((seq + tt) * D + j) * D + k] : 0.0f;
+                const ACC akj = (jv && k < D) ? static_cast<ACC>(A[((seq + tt) * D + j) * D + k]) : ACC(0);
                 acc += akj * __shfl(st, gbase + k, 64);
             }
             acc = acc + bj;
         }
         if (live) {
             st = acc;
-            if (act && jv) out[(seq + t) * D + j] = st;
+            if (act && jv) out[(seq + t) * D + j] = static_cast<float>(st);
         }
     }
 }
 
 int pick_dp(int D) { return D <= 4 ? 4 : D <= 8 ? 8 : D <= 16 ? 16 : D <= 32 ? 32 : 64; }
 
-template <int DP>
+template <int DP, class ACC>
 int launch_dense_dp(const float *A, const float *d, const float *W, const float *b, const float *s0, float *out0,
                     float *out1, const int *out_sel, const int *skip, const int *all_done, const DenseScanPlan &pl,
-                    float *Pagg, float *Bagg, float *carry, hipStream_t stream)
+                    ACC *Pagg, ACC *Bagg, ACC *carry, hipStream_t stream)
 {
     constexpr int G = 64 / DP;
     const long long nq = static_cast<long long>(pl.B) * pl.nchunk;
     const long long waves = (nq + G - 1) / G;
     const unsigned blocks = static_cast<unsigned>((waves + 3) / 4);
     const unsigned cblocks = static_cast<unsigned>((pl.B + 3) / 4);
-    if (d) {
-        hipLaunchKernelGGL((dense_agg_kernel<DP, true>), dim3(blocks), dim3(kThreads), 0, stream, A, d, W, b, skip,
+    const bool f64 = sizeof(ACC) == 8;
+    if (d && DP == 32 && pl.D == 32 && !f64) {
+        hipLaunchKernelGGL(dense_agg_mfma32_kernel, dim3(static_cast<unsigned>(nq)), dim3(64), 0, stream, d, W, b, skip,
+                           all_done, pl.T, pl.chunk_len, pl.nchunk, reinterpret_cast<float *>(Pagg),
+                           reinterpret_cast<float *>(Bagg));
+    } else if (d && DP == 16 && pl.D == 16) {
+        hipLaunchKernelGGL((dense_agg_mfma16_kernel<ACC>), dim3(static_cast<unsigned>(nq)), dim3(64), 0, stream, d, W,
+                           b, skip, all_done, pl.T, pl.chunk_len, pl.nchunk, Pagg, Bagg);
+    } else if (d) {
+        hipLaunchKernelGGL((dense_agg_kernel<DP, true, ACC>), dim3(blocks), dim3(kThreads), 0, stream, A, d, W, b, skip,
                            all_done, pl.B, pl.T, pl.D, pl.chunk_len, pl.nchunk, Pagg, Bagg);
     } else {
-        hipLaunchKernelGGL((dense_agg_kernel<DP, false>), dim3(blocks), dim3(kThreads), 0, stream, A, d, W, b, skip,
-                           all_done, pl.B, pl.T, pl.D, pl.chunk_len, pl.nchunk, Pagg, Bagg);
+        hipLaunchKernelGGL((dense_agg_kernel<DP, false, ACC>), dim3(blocks), dim3(kThreads), 0, stream, A, d, W, b,
+                           skip, all_done, pl.B, pl.T, pl.D, pl.chunk_len, pl.nchunk, Pagg, Bagg);
     }
     DEER_HIP(hipGetLastError());
-    hipLaunchKernelGGL((dense_carry_kernel<DP>), dim3(cblocks), dim3(kThreads), 0, stream, Pagg, Bagg, s0, skip,
+    hipLaunchKernelGGL((dense_carry_kernel<DP, ACC>), dim3(cblocks), dim3(kThreads), 0, stream, Pagg, Bagg, s0, skip,
                        all_done, pl.B, pl.D, pl.nchunk, carry);
     DEER_HIP(hipGetLastError());
     if (d) {
-        hipLaunchKernelGGL((dense_replay_kernel<DP, true>), dim3(blocks), dim3(kThreads), 0, stream, A, d, W, b, carry,
-                           skip, all_done, pl.B, pl.T, pl.D, pl.chunk_len, pl.nchunk, out0, out1, out_sel);
+        hipLaunchKernelGGL((dense_replay_kernel<DP, true, ACC>), dim3(blocks), dim3(kThreads), 0, stream, A, d, W, b,
+                           carry, skip, all_done, pl.B, pl.T, pl.D, pl.chunk_len, pl.nchunk, out0, out1, out_sel);
     } else {
-        hipLaunchKernelGGL((dense_replay_kernel<DP, false>), dim3(blocks), dim3(kThreads), 0, stream, A, d, W, b,
+        hipLaunchKernelGGL((dense_replay_kernel<DP, false, ACC>), dim3(blocks), dim3(kThreads), 0, stream, A, d, W, b,
                            carry, skip, all_done, pl.B, pl.T, pl.D, pl.chunk_len, pl.nchunk, out0, out1, out_sel);
     }
     DEER_HIP(hipGetLastError());
     return DEER_OK;
+}
+
+template <class ACC>
+int launch_dense_acc(const float *A, const float *d, const float *W, const float *b, const float *s0, float *out0,
+                     float *out1, const int *out_sel, const int *skip, const int *all_done, const DenseScanPlan &pl,
+                     void *state, hipStream_t stream)
+{
+    const size_t nq = static_cast<size_t>(pl.B) * pl.nchunk;
+    const int D = pl.D;
+    Carve cv(state);
+    ACC *Pagg = cv.take<ACC>(nq * D * D);
+    ACC *Bagg = cv.take<ACC>(nq * D);
+    ACC *carry = cv.take<ACC>(nq * D);
+    switch (pick_dp(D)) {
+    case 4: return launch_dense_dp<4, ACC>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, Pagg, Bagg, carry, stream);
+    case 8: return launch_dense_dp<8, ACC>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, Pagg, Bagg, carry, stream);
+    case 16: return launch_dense_dp<16, ACC>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, Pagg, Bagg, carry, stream);
+    case 32: return launch_dense_dp<32, ACC>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, Pagg, Bagg, carry, stream);
+    default: return launch_dense_dp<64, ACC>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, Pagg, Bagg, carry, stream);
+    }
 }
 
 }  // namespace
@@ -258,7 +469,7 @@ DenseScanPlan dense_scan_plan(int B, int T, int D)
     p.B = B;
     p.T = T;
     p.D = D;
-    // Long chunks amortise the carry walk; short ones give enough chunks to fill the chip.
+    // Long chunks shorten the carry walk; short ones give enough chunks to fill the chip.
     int L = 64;
     while (L > 16 && static_cast<long long>(B) * ((T + L - 1) / L) < 8192) L /= 2;
     p.chunk_len = L;
@@ -266,31 +477,23 @@ DenseScanPlan dense_scan_plan(int B, int T, int D)
     return p;
 }
 
-size_t dense_scan_state_bytes(int B, int T, int D)
+size_t dense_scan_state_bytes(int B, int T, int D, bool f64)
 {
     const DenseScanPlan p = dense_scan_plan(B, T, D);
     const size_t nq = static_cast<size_t>(B) * p.nchunk;
-    return align_up(nq * D * D * sizeof(float)) + 2 * align_up(nq * D * sizeof(float));
+    const size_t w = f64 ? sizeof(double) : sizeof(float);
+    return align_up(nq * D * D * w) + 2 * align_up(nq * D * w);
 }
 
 int launch_dense_scan(const float *A, const float *d, const float *W, const float *b, const float *s0, float *out0,
                       float *out1, const int *out_sel, const int *skip, const int *all_done, int B, int T, int D,
-                      void *state, hipStream_t stream)
+                      bool f64, void *state, hipStream_t stream)
 {
     if (B == 0 || T == 0) return DEER_OK;
     const DenseScanPlan pl = dense_scan_plan(B, T, D);
-    const size_t nq = static_cast<size_t>(B) * pl.nchunk;
-    Carve cv(state);
-    float *Pagg = cv.take<float>(nq * D * D);
-    float *Bagg = cv.take<float>(nq * D);
-    float *carry = cv.take<float>(nq * D);
-    switch (pick_dp(D)) {
-    case 4: return launch_dense_dp<4>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, Pagg, Bagg, carry, stream);
-    case 8: return launch_dense_dp<8>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, Pagg, Bagg, carry, stream);
-    case 16: return launch_dense_dp<16>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, Pagg, Bagg, carry, stream);
-    case 32: return launch_dense_dp<32>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, Pagg, Bagg, carry, stream);
-    default: return launch_dense_dp<64>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, Pagg, Bagg, carry, stream);
-    }
+    if (f64)
+        return launch_dense_acc<double>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, state, stream);
+    return launch_dense_acc<float>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, state, stream);
 }
 
 }  // namespace deer

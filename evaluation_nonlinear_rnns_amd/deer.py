@@ -23,6 +23,8 @@ DEER_CELL_GRU = 1
 MODES = {"dense": DEER_MODE_DENSE, "diag": DEER_MODE_DIAG}
 CELLS = {"tanh": DEER_CELL_TANH, "gru": DEER_CELL_GRU}
 
+DEER_SCAN_F64 = 16   # or-ed into the dense mode: the linear solve accumulates in double
+
 DEER_OK = 0
 DEER_NOT_CONVERGED = 1
 ERRORS = {-1: "DEER_ERR_INVALID", -2: "DEER_ERR_UNSUPPORTED", -3: "DEER_ERR_WORKSPACE",
@@ -143,11 +145,15 @@ class Cell:
 
 # ------------------------------------------------------------- workspaces
 
-def deer_workspace_size(cell: Cell, B: int, T: int, mode: str) -> int:
+def _mode(mode: str, scan_f64: bool) -> int:
+    return MODES[mode] | (DEER_SCAN_F64 if scan_f64 else 0)
+
+
+def deer_workspace_size(cell: Cell, B: int, T: int, mode: str, scan_f64: bool = False) -> int:
     lib = load_library()
     n = ctypes.c_size_t(0)
     p = cell.params()
-    _check(lib.deer_workspace_size(ctypes.byref(p), B, T, MODES[mode], ctypes.byref(n)))
+    _check(lib.deer_workspace_size(ctypes.byref(p), B, T, _mode(mode, scan_f64), ctypes.byref(n)))
     return int(n.value)
 
 
@@ -177,12 +183,13 @@ def deer_workspace_init(ws, stream=None) -> None:
 # ---------------------------------------------------------------- solvers
 
 def deer_solve(cell: Cell, x, s0=None, mode: str = "dense", tol: float = 1e-6, max_iter: int = 100,
-               init_guess=None, out=None, workspace=None, stream=None):
+               init_guess=None, out=None, workspace=None, stream=None, scan_f64: bool = False):
     """Parallel Newton / quasi-Newton solve; returns ``(traj, iters, resid, status, rc)``.
 
     ``traj`` is a ``[B,T,D]`` CUDA tensor; ``iters``, ``status`` are numpy int32
     ``[B]``, ``resid`` numpy float32 ``[B]``; ``rc`` is DEER_OK or
-    DEER_NOT_CONVERGED.
+    DEER_NOT_CONVERGED.  ``scan_f64`` (dense mode) accumulates the linear solve
+    in double precision.
     """
     import numpy as np
     import torch
@@ -195,12 +202,12 @@ def deer_solve(cell: Cell, x, s0=None, mode: str = "dense", tol: float = 1e-6, m
     if out is None:
         out = torch.empty((B, T, D), dtype=torch.float32, device=x.device)
     if workspace is None:
-        workspace = new_workspace(deer_workspace_size(cell, B, T, mode), device=x.device)
+        workspace = new_workspace(deer_workspace_size(cell, B, T, mode, scan_f64), device=x.device)
     iters = np.zeros(B, np.int32)
     resid = np.zeros(B, np.float32)
     status = np.zeros(B, np.int32)
     rc = lib.deer_solve(ctypes.byref(p), _dev(x, "x", shape=(B, T, M)), _dev(s0, "s0", shape=(B, D)), B, T,
-                        MODES[mode], ctypes.c_float(tol), int(max_iter),
+                        _mode(mode, scan_f64), ctypes.c_float(tol), int(max_iter),
                         _dev(init_guess, "init_guess", shape=(B, T, D)), _dev(out, "out", shape=(B, T, D)),
                         iters.ctypes.data_as(ctypes.c_void_p), resid.ctypes.data_as(ctypes.c_void_p),
                         status.ctypes.data_as(ctypes.c_void_p),

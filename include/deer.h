@@ -39,6 +39,18 @@ extern "C" {
 #endif
 
 enum deer_mode { DEER_MODE_DENSE = 0, DEER_MODE_DIAG = 1 };
+
+/*
+ * Flag or-ed into the mode of deer_solve (dense mode only): the linear solve
+ * accumulates its chunk products, offsets and carried states in double
+ * precision (inputs, outputs and the cell evaluation stay float32).  For
+ * unpredictable dynamics, float32 products of many Jacobians grow large enough
+ * that rounding breaks the step-to-step consistency of the solved trajectory at
+ * chunk boundaries and the residual stalls above small tolerances; the pages
+ * note that float32 overflow forced damping for Newton on such systems
+ * ("Parallel Broyden Methods", appendix F.2).
+ */
+#define DEER_SCAN_F64 16
 enum deer_cell { DEER_CELL_TANH = 0, DEER_CELL_GRU = 1 };
 
 enum deer_status {

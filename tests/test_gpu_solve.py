@@ -23,14 +23,14 @@ TOL = 1e-4
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "oracle_full_workloads.json")
 
 
-def _run(orc, p, mode, tol, max_iter, s0=True, check_iters=True, init=None):
+def _run(orc, p, mode, tol, max_iter, s0=True, check_iters=True, init=None, scan_f64=False):
     dev = device()
     cell = deer.cell_from_problem(p, dev)
     x = torch.from_numpy(p["x"]).to(dev)
     s0_t = torch.from_numpy(p["s0"]).to(dev) if s0 else None
     init_t = None if init is None else torch.from_numpy(init).to(dev)
     traj, iters, resid, status, rc = deer.deer_solve(cell, x, s0_t, mode=mode, tol=tol, max_iter=max_iter,
-                                                     init_guess=init_t)
+                                                     init_guess=init_t, scan_f64=scan_f64)
     torch.cuda.synchronize()
     oc = orc.Cell.from_problem(p)
     s0n = p["s0"] if s0 else None
@@ -54,6 +54,17 @@ def test_tanh_solve_matches_oracle(orc, mode, B, T, D, M, gain):
     assert rc == deer.DEER_OK and np.all(status == 0)
     assert np.all(rel_linf(got, ref) <= TOL)
     assert np.all(resid <= 1e-5)
+
+
+@pytest.mark.parametrize("B,T,D,M,gain", [(2, 300, 4, 3, 0.6), (2, 1000, 16, 16, 0.9), (3, 700, 32, 32, 0.7),
+                                          (1, 200, 6, 4, 0.8)])
+def test_tanh_dense_solve_f64_scan_matches_oracle(orc, B, T, D, M, gain):
+    """Dense DEER with the linear solve accumulated in double."""
+    p = I.tanh_problem(550 + T + D, B, T, D, M, gain=gain, bias_std=0.3, s0_std=0.5)
+    log(f"deer_solve tanh dense f64-scan B={B} T={T} D={D} M={M}")
+    got, ref, iters, resid, status, rc, oit = _run(orc, p, "dense", 1e-5, T, scan_f64=True)
+    assert rc == deer.DEER_OK and np.all(status == 0)
+    assert np.all(rel_linf(got, ref) <= TOL)
 
 
 @pytest.mark.parametrize("B,T,D,M", [(2, 100, 4, 3), (3, 1000, 16, 16), (2, 777, 32, 8), (2, 2000, 64, 64),
@@ -115,15 +126,16 @@ def _golden(name, gain=None):
     return g[f"{gain:g}"] if gain is not None else g
 
 
-def _full(orc, name, gain=None, sample=None):
+def _full(orc, name, gain=None, sample=None, scan_f64=False):
     dev = device()
     w = I.WORKLOADS[name]
     gold = _golden(name, gain)
     p = I.workload_problem(name, gain=gain)
-    log(f"deer_solve full workload {name} gain={gain}")
+    log(f"deer_solve full workload {name} gain={gain} scan_f64={scan_f64}")
     cell = deer.cell_from_problem(p, dev)
     x = torch.from_numpy(p["x"]).to(dev)
-    traj, iters, resid, status, rc = deer.deer_solve(cell, x, mode=w.mode, tol=w.tol, max_iter=w.max_iter)
+    traj, iters, resid, status, rc = deer.deer_solve(cell, x, mode=w.mode, tol=w.tol, max_iter=w.max_iter,
+                                                     scan_f64=scan_f64)
     torch.cuda.synchronize()
     seqs = range(w.B) if sample is None else sample
     oc = orc.Cell.from_problem(p)
@@ -166,8 +178,11 @@ def test_full_sweep_gain2_certified(orc):
     """g = 2: float32 and float64 rollouts of the oracle itself part by more than
     1e-4, so no float32 method can meet the literal bound over all of T.  The GPU
     trajectory is certified by its float64 one-step residual and matched up to the
-    horizon where the oracle's own float32 rollout still tracks float64."""
-    w, gold, p, got, ref, iters, status, seqs = _full(orc, "tanh_d16_t4096_sweep", gain=2.0, sample=list(range(8)))
+    horizon where the oracle's own float32 rollout still tracks float64.  The
+    linear solve accumulates in double here: float32 chunk products are too large
+    at this gain for the residual to reach 1e-6."""
+    w, gold, p, got, ref, iters, status, seqs = _full(orc, "tanh_d16_t4096_sweep", gain=2.0, sample=list(range(8)),
+                                                      scan_f64=True)
     assert np.all(status == 0)
     oc = orc.Cell.from_problem(p)
     # the oracle's float64 residual of the GPU trajectory: max_t |s_t - f(s_{t-1})| <= 10 tol

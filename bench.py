@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense-DEER and gain-sweep measurements")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work for the baseline sample")
+    ap.add_argument("--only", choices=("dense", "sweep", "scan"), default=None,
+                    help="run one secondary measurement alone and print its JSON (for profiling)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run a plain 1 GiB device copy (the reference kernel for HBM counter scaling)")
     return ap.parse_args()
@@ -309,6 +311,11 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.only:
+        fn = {"dense": dense_solve, "sweep": gain_sweep, "scan": scan_bandwidth}[args.only]
+        print(json.dumps({args.only: fn(args, dev)}), flush=True)
+        return
 
     w, p, ms_per_step, ms_events, prof, iters = solve_workload(args, dev)
     dom, kernels, roof = roofline_of(w, prof)

@@ -23,6 +23,8 @@
 // states (float, or double for unpredictable dynamics where chunk products
 // grow large enough that float32 rounding breaks the consistency of the
 // solution at chunk boundaries); inputs and outputs are float32.
+#include <algorithm>
+
 #include "internal.h"
 
 namespace deer {
@@ -139,72 +141,124 @@ __global__ __launch_bounds__(kThreads) void dense_agg_kernel(
 // Row of the 32x32 accumulator held in register v by a lane of half hf.
 __device__ __forceinline__ int row32(int v, int hf) { return 8 * (v >> 2) + 4 * hf + (v & 3); }
 
-// D = 32, factored leaves, float32: one 64-lane workgroup per chunk.
-//   A operand (W):      lane l, instruction v holds W[l % 32][row32(v, l / 32)]
-//   B operand (P_old):  lane l, instruction v holds P_old[row32(v, l / 32)][l % 32] = accumulator v
-//   result:             C[i][j] = sum_k W[i][k] P_old[k][j], then row i scaled by d_t[i]
-// The offset B_c advances on VALU with the broadcast of the previous offset.
-__global__ __launch_bounds__(64) void dense_agg_mfma32_kernel(const float *__restrict__ dv, const float *__restrict__ W,
-                                                            const float *__restrict__ bv, const int *__restrict__ skip,
-                                                            const int *__restrict__ all_done, int T, int L, int nchunk,
-                                                            float *__restrict__ Pout, float *__restrict__ Bout)
+// D = 32, factored leaves, float32: one 128-thread workgroup per chunk.  Its
+// first wavefront runs the product chain on the matrix cores, the second the
+// offset chain on VALU; both read the chunk's d_t and b_t from LDS, so the two
+// chains overlap.
+//   A operand (W diag(d_{t-1})):  lane l, instruction v holds W[l % 32][k] d_{t-1}[k], k = row32(v, l / 32)
+//   B operand (Q_old):            lane l, instruction v holds Q_old[row32(v, l / 32)][l % 32] = accumulator v
+constexpr int kAggThreads = 128;
+__global__ __launch_bounds__(kAggThreads) void dense_agg_mfma32_kernel(
+    const float *__restrict__ dv, const float *__restrict__ W, const float *__restrict__ bv,
+    const int *__restrict__ skip, const int *__restrict__ all_done, int T, int L, int nchunk,
+    float *__restrict__ Pout, float *__restrict__ Bout)
 {
     constexpr int D = 32;
+    constexpr int kRows = 64 * D / 4 / kAggThreads;  // float4 rows of d (and of b) per thread, L <= 64
     if (all_done && *all_done) return;
-    __shared__ float ds[64 * D], bs[64 * D];     // the chunk's d_t and b_t rows (L <= 64)
-    const int lane = threadIdx.x, j = lane & 31, hf = lane >> 5;
+    __shared__ float ds[64 * D], bs[64 * D];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int j = lane & 31, hf = lane >> 5;
     const long long q = blockIdx.x;
     const int bseq = static_cast<int>(q / nchunk), c = static_cast<int>(q % nchunk);
     if (skip && skip[bseq]) return;
     const int t0 = c * L, n = min(L, T - t0);
-    const size_t seq = static_cast<size_t>(bseq) * T;
-    for (int e = lane; e < n * (D / 4); e += 64) {
-        const int r = e / (D / 4), col = (e % (D / 4)) * 4;
-        const size_t g = (seq + t0 + r) * D + col;
-        *reinterpret_cast<v4f *>(ds + r * D + col) = *reinterpret_cast<const v4f *>(dv + g);
-        *reinterpret_cast<v4f *>(bs + r * D + col) = *reinterpret_cast<const v4f *>(bv + g);
+    {
+        // all of the chunk's loads in flight at once
+        const size_t base = (static_cast<size_t>(bseq) * T + t0) * D;
+        v4f dreg[kRows], breg[kRows];
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) {
+            const int e = tid + kAggThreads * i;
+            const int ec = e < n * (D / 4) ? e : 0;     // clamped: rows past the chunk are never read
+            dreg[i] = *reinterpret_cast<const v4f *>(dv + base + static_cast<size_t>(ec) * 4);
+            breg[i] = *reinterpret_cast<const v4f *>(bv + base + static_cast<size_t>(ec) * 4);
+        }
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) {
+            const int e = tid + kAggThreads * i;
+            *reinterpret_cast<v4f *>(ds + e * 4) = dreg[i];
+            *reinterpret_cast<v4f *>(bs + e * 4) = breg[i];
+        }
     }
-    float WA[16], Wcol[16], Wrow[D];
+    __syncthreads();
+
+    if (wave == 1) {
+        // offset B_s = d_s (W B_{s-1}) + b_s, B_0 = b_0; lane j < 32 owns row j
+        float Wrow[D];
+#pragma unroll
+        for (int k = 0; k < D; ++k) Wrow[k] = W[j * D + k];
+        float Bq = bs[j];
+        for (int s = 1; s < n; ++s) {
+            float h[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int k = 0; k < D; ++k)
+                h[k & 3] += Wrow[k] * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Bq), k));
+            Bq = ds[s * D + j] * ((h[0] + h[1]) + (h[2] + h[3])) + bs[s * D + j];
+        }
+        if (hf == 0) Bout[static_cast<size_t>(q) * D + j] = Bq;
+        return;
+    }
+
+    // Q_s = W P_{s-1} runs unscaled: Q_0 = W and Q_s = (W diag(d_{s-1})) Q_{s-1}, so
+    // the diagonal lands on the A operand and the accumulator of one step is the
+    // B operand of the next (two accumulators alternate); P = diag(d_last) Q_last.
+    // The scaled A operands of step s+1 are formed while step s runs.
+    float WA[16];
+    v16f qa, qb;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
         WA[v] = W[j * D + row32(v, hf)];
-        Wcol[v] = W[row32(v, hf) * D + j];
+        qa[v] = W[row32(v, hf) * D + j];
     }
-#pragma unroll
-    for (int k = 0; k < D; ++k) Wrow[k] = W[j * D + k];
-    __syncthreads();
-
-    v16f P;
-    {
-        const v4f *d0 = reinterpret_cast<const v4f *>(ds);
+    auto scaled = [&](int s, float (&ws)[16]) {       // W diag(d_{s-1}), this lane's A operands
+        const v4f *dprev = reinterpret_cast<const v4f *>(ds + (min(s, n - 1) - 1) * D);
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
-            const v4f dq = d0[2 * qd + hf];
+            const v4f dq = dprev[2 * qd + hf];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) P[4 * qd + r] = dq[r] * Wcol[4 * qd + r];
+            for (int r = 0; r < 4; ++r) ws[4 * qd + r] = WA[4 * qd + r] * dq[r];
         }
-    }
-    float Bq = bs[j];
-    for (int s = 1; s < n; ++s) {
+    };
+    auto step = [&](const v16f &qin, const float (&ws)[16]) -> v16f {
         v16f acc = {};
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(WA[v], P[v], acc, 0, 0, 0);
-        const v4f *drow = reinterpret_cast<const v4f *>(ds + s * D);
+        for (int v = 0; v < 16; ++v) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(ws[v], qin[v], acc, 0, 0, 0);
+        return acc;
+    };
+    // (rows past the chunk are clamped: a scaled operand formed for a step that
+    // never runs is simply unused, which keeps the loop body free of branches)
+    float wa[16], wb[16];
+    int s = 1;
+    scaled(1, wa);
+    if ((n - 1) & 1) {                                // odd step count: peel one so the pairs end in qa
+        scaled(2, wb);
+        qa = step(qa, wa);
+        s = 2;
 #pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-            const v4f dq = drow[2 * qd + hf];
+        for (int v = 0; v < 16; ++v) wa[v] = wb[v];
+    }
+    for (; s + 1 < n; s += 2) {
+        scaled(s + 1, wb);
+        qb = step(qa, wa);
+        scaled(s + 2, wa);
+        qa = step(qb, wb);
+        // issue order: the pair's LDS reads first, then each MFMA with two VALU ops
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) P[4 * qd + r] = dq[r] * acc[4 * qd + r];
+        for (int g = 0; g < 32; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x8, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x2, 2, 0);
         }
-        float sum = 0.0f;
-#pragma unroll
-        for (int k = 0; k < D; ++k) sum += Wrow[k] * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Bq), k));
-        Bq = ds[s * D + j] * sum + bs[s * D + j];
     }
     float *po = Pout + static_cast<size_t>(q) * D * D;
+    const v4f *dl = reinterpret_cast<const v4f *>(ds + (n - 1) * D);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) po[row32(v, hf) * D + j] = P[v];
-    if (hf == 0) Bout[static_cast<size_t>(q) * D + j] = Bq;
+    for (int qd = 0; qd < 4; ++qd) {
+        const v4f dq = dl[2 * qd + hf];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) po[row32(4 * qd + r, hf) * D + j] = dq[r] * qa[4 * qd + r];
+    }
 }
 
 // D = 16, factored leaves, float32 (16x16x4) or float64 (16x16x4 f64).
@@ -310,41 +364,181 @@ __global__ __launch_bounds__(64) void dense_agg_mfma16_kernel(const float *__res
 }
 
 // ------------------------------------------------------------- carry walk
-// One wavefront per sequence walks its chunks in order.
+// One wavefront per sequence walks its chunks in order: s_in(c+1) = P_c s_in(c) + B_c.
+// The chain through s is the only dependency, so the chunk aggregates are
+// fetched PF chunks ahead into a register ring and load latency stays off the
+// critical path.  Lane (grp, j) holds row j of P_c restricted to the KG
+// columns of its group; s is broadcast with cross-lane shuffles (no LDS and no
+// barrier, whose release fence would wait for the prefetches) and the G
+// partial sums are reduced across groups.
 template <int DP, class ACC>
-__global__ __launch_bounds__(kThreads) void dense_carry_kernel(
+struct CarryGeom {
+    static constexpr int G = (64 / DP < DP) ? 64 / DP : DP;    // lane groups splitting the columns
+    static constexpr int KG = DP / G;                           // columns per lane
+    static constexpr int W = static_cast<int>(sizeof(ACC) / 4); // 32-bit registers per value
+    static constexpr int PFr = 160 / ((KG + 1) * W);            // ring depth within ~160 registers
+    static constexpr int PF = PFr > 16 ? 16 : PFr < 1 ? 1 : PFr;
+    static constexpr int VEC = 16 / static_cast<int>(sizeof(ACC));   // values per 16-byte load
+};
+
+// Row segment of one chunk product: KG columns starting at k0.  Every lane
+// loads (indices clamped into the matrix) so the loads carry no branch and the
+// compiler can keep several chunks of prefetch in flight; columns outside the
+// matrix read as zero.
+template <int KG, class ACC, bool VECP>
+__device__ __forceinline__ void load_row_segment(const ACC *__restrict__ row, int k0, int D, ACC (&r)[KG])
+{
+    if constexpr (VECP) {       // D == DP: the segment is whole and 16-byte aligned
+        constexpr int VEC = 16 / static_cast<int>(sizeof(ACC));
+        typedef ACC vt __attribute__((ext_vector_type(VEC)));
+#pragma unroll
+        for (int i = 0; i < KG; i += VEC) {
+            const vt v = *reinterpret_cast<const vt *>(row + k0 + i);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) r[i + e] = v[e];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < KG; ++i) {
+            const int k = k0 + i;
+            const ACC v = row[k < D ? k : D - 1];
+            r[i] = k < D ? v : ACC(0);
+        }
+    }
+}
+
+template <int DP, class ACC, bool VECP>
+__global__ __launch_bounds__(64) void dense_carry_kernel(
     const ACC *__restrict__ Pagg, const ACC *__restrict__ Bagg, const float *__restrict__ s0,
     const int *__restrict__ skip, const int *__restrict__ all_done, int B, int D, int nchunk,
     ACC *__restrict__ carry)
 {
+    using Gm = CarryGeom<DP, ACC>;
+    constexpr int G = Gm::G, KG = Gm::KG, PF = Gm::PF;
     if (all_done && *all_done) return;
-    const int lane = threadIdx.x & 63;
-    const int bseq = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-    if (bseq >= B || (skip && skip[bseq])) return;    // uniform per wavefront
-    const bool jv = lane < D;
-    ACC st = (jv && s0) ? static_cast<ACC>(s0[static_cast<size_t>(bseq) * D + lane]) : ACC(0);
+    const int bseq = blockIdx.x;
+    if (bseq >= B || (skip && skip[bseq])) return;      // uniform per workgroup
+    const int lane = threadIdx.x;
+    const int grp = lane / DP, j = lane % DP;
+    const bool act = grp < G;
+    const bool jv = act && j < D;
+    const int jr = j < D ? j : D - 1;                   // clamped row for the loads
+    const int k0 = act ? grp * KG : 0;
     const size_t q0 = static_cast<size_t>(bseq) * nchunk;
-    ACC row[DP];
+    const bool writer = grp == 0 && j < D;
+
+    ACC ring[PF][KG], bring[PF];
+    auto fetch = [&](int c, ACC (&r)[KG], ACC &bq) {
+        const size_t q = q0 + static_cast<size_t>(c < nchunk ? c : nchunk - 1);
+        load_row_segment<KG, ACC, VECP>(Pagg + (q * D + jr) * D, k0, D, r);
+        bq = Bagg[q * D + jr];
+    };
 #pragma unroll
-    for (int k = 0; k < DP; ++k) row[k] = (jv && k < D) ? Pagg[(q0 * D + lane) * D + k] : ACC(0);
-    for (int c = 0; c < nchunk; ++c) {
-        const size_t q = q0 + c;
-        if (jv) carry[q * D + lane] = st;
-        if (c == nchunk - 1) break;
-        const ACC bq = jv ? Bagg[q * D + lane] : ACC(0);
-        ACC nxt[DP];
+    for (int u = 0; u < PF; ++u) fetch(u, ring[u], bring[u]);
+
+    ACC st = (jv && s0) ? static_cast<ACC>(s0[static_cast<size_t>(bseq) * D + j]) : ACC(0);
+    auto advance = [&](int c, const ACC (&r)[KG], ACC bq) {
+        if (writer) carry[(q0 + c) * D + j] = st;
+        ACC a0 = 0, a1 = 0;
 #pragma unroll
-        for (int k = 0; k < DP; ++k) nxt[k] = (jv && k < D) ? Pagg[((q + 1) * D + lane) * D + k] : ACC(0);
-        ACC acc = 0;
+        for (int i = 0; i < KG; i += 2) {
+            a0 += r[i] * __shfl(st, k0 + i, 64);
+            if (i + 1 < KG) a1 += r[i + 1] * __shfl(st, k0 + i + 1, 64);
+        }
+        ACC acc = a0 + a1;
 #pragma unroll
-        for (int k = 0; k < DP; ++k) acc += row[k] * __shfl(st, k, 64);
-        st = acc + bq;
+        for (int o = DP; o < G * DP; o <<= 1) acc += __shfl_xor(acc, o, 64);
+        st = jv ? acc + bq : ACC(0);
+    };
+    // whole rounds of PF chunks: straight-line bodies, refills clamped past the end
+    const int nfull = nchunk - nchunk % PF;
+    for (int c0 = 0; c0 < nfull; c0 += PF) {
 #pragma unroll
-        for (int k = 0; k < DP; ++k) row[k] = nxt[k];
+        for (int u = 0; u < PF; ++u) {
+            advance(c0 + u, ring[u], bring[u]);
+            fetch(c0 + u + PF, ring[u], bring[u]);
+        }
     }
+#pragma unroll
+    for (int u = 0; u < PF; ++u)
+        if (nfull + u < nchunk) advance(nfull + u, ring[u], bring[u]);
 }
 
 // ----------------------------------------------------------------- replay
+// Factored leaves: one wavefront per chunk re-runs s_t = d_t * (W s_{t-1}) + b_t
+// from the chunk's carried-in state.  Lane (grp, j) owns row j and the KG
+// columns of its group (the carry walk's split); d_t and b_t are fetched PR
+// steps ahead with unconditional, clamped loads.  When every lane owns a row
+// (D == DP and the groups fill the wavefront) every group writes the
+// (identical) new state and steps past the end of a short last chunk rewrite
+// its final state, so the step body has no branch.
+template <int DP, class ACC, bool FULL>
+__global__ __launch_bounds__(kThreads) void dense_replay_fact_kernel(
+    const float *__restrict__ dv, const float *__restrict__ W, const float *__restrict__ bv,
+    const ACC *__restrict__ carry, const int *__restrict__ skip, const int *__restrict__ all_done, int B, int T,
+    int D, int L, int nchunk, float *out0, float *out1, const int *__restrict__ out_sel)
+{
+    using Gm = CarryGeom<DP, ACC>;
+    constexpr int G = Gm::G, KG = Gm::KG;
+    constexpr int PR = 16;                              // chunk lengths are multiples of PR
+    if (all_done && *all_done) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const long long q = static_cast<long long>(blockIdx.x) * (kThreads / 64) + wave;
+    if (q >= static_cast<long long>(B) * nchunk) return;            // uniform per wavefront
+    const int bseq = static_cast<int>(q / nchunk), c = static_cast<int>(q % nchunk);
+    if (skip && skip[bseq]) return;
+    const int grp = lane / DP, j = lane % DP;
+    const bool act = grp < G;
+    const bool jv = act && j < D;
+    const int jr = j < D ? j : D - 1;
+    const int k0 = act ? grp * KG : 0;
+    const int t0 = c * L, t1 = min(T, t0 + L);
+    const size_t seq = static_cast<size_t>(bseq) * T;
+    float *out = (out_sel && (*out_sel & 1)) ? out1 : out0;
+
+    ACC wseg[KG];
+#pragma unroll
+    for (int i = 0; i < KG; ++i) {
+        const int k = k0 + i;
+        const float w = W[jr * D + (k < D ? k : D - 1)];
+        wseg[i] = (jv && k < D) ? static_cast<ACC>(w) : ACC(0);
+    }
+    ACC st = carry[static_cast<size_t>(q) * D + jr];
+    st = jv ? st : ACC(0);
+    float dr[PR], br[PR];
+    auto fetch = [&](int t, float &dd, float &bb) {
+        const size_t i = (seq + (t < t1 ? t : t1 - 1)) * D + jr;
+        dd = dv[i];
+        bb = bv[i];
+    };
+#pragma unroll
+    for (int u = 0; u < PR; ++u) fetch(t0 + u, dr[u], br[u]);
+    for (int sb = 0; sb < L; sb += PR) {
+#pragma unroll
+        for (int u = 0; u < PR; ++u) {
+            const int t = t0 + sb + u;
+            ACC a0 = 0, a1 = 0;
+#pragma unroll
+            for (int i = 0; i < KG; i += 2) {
+                a0 += wseg[i] * __shfl(st, k0 + i, 64);
+                if (i + 1 < KG) a1 += wseg[i + 1] * __shfl(st, k0 + i + 1, 64);
+            }
+            ACC acc = a0 + a1;
+#pragma unroll
+            for (int o = DP; o < G * DP; o <<= 1) acc += __shfl_xor(acc, o, 64);
+            const ACC y = static_cast<ACC>(dr[u]) * acc + static_cast<ACC>(br[u]);
+            fetch(t + PR, dr[u], br[u]);
+            const bool live = t < t1;
+            st = (live && jv) ? y : st;
+            if constexpr (FULL) {
+                out[(seq + (live ? t : t1 - 1)) * D + j] = static_cast<float>(st);
+            } else {
+                if (grp == 0 && jv && live) out[(seq + t) * D + j] = static_cast<float>(st);
+            }
+        }
+    }
+}
+
 template <int DP, bool FACT, class ACC>
 __global__ __launch_bounds__(kThreads) void dense_replay_kernel(
     const float *__restrict__ A, const float *__restrict__ dv, const float *__restrict__ W,
@@ -373,28 +567,54 @@ __global__ __launch_bounds__(kThreads) void dense_replay_kernel(
         for (int k = 0; k < DP; ++k) wrow[k] = (jv && k < D) ? static_cast<ACC>(W[j * D + k]) : ACC(0);
     }
     ACC st = jv ? carry[static_cast<size_t>(q) * D + j] : ACC(0);
-    for (int s = 0; s < L; ++s) {
-        const int t = t0 + s;
-        const bool live = t < t1;
-        const int tt = live ? t : t0;
-        const ACC bj = jv ? static_cast<ACC>(bv[(seq + tt) * D + j]) : ACC(0);
-        ACC acc = 0;
-        if constexpr (FACT) {
+    if constexpr (FACT) {
+        // d_t and b_t are independent of the chain: fetch them PR steps ahead.
+        // The loads are unconditional (row and step clamped into the chunk), so
+        // the wait before each use leaves the later prefetches in flight.
+        constexpr int PR = 8;                           // chunk lengths are multiples of PR
+        const int jr = jv ? j : 0;
+        float dr[PR], br[PR];
+        auto fetch = [&](int t, float &dd, float &bb) {
+            const size_t i = (seq + (t < t1 ? t : t0)) * D + jr;
+            dd = dv[i];
+            bb = bv[i];
+        };
 #pragma unroll
-            for (int k = 0; k < DP; ++k) acc += wrow[k] * __shfl(st, gbase + k, 64);
-            const ACC dj = jv ? static_cast<ACC>(dv[(seq + tt) * D + j]) : ACC(0);
-            acc = dj * acc + bj;
-        } else {
+        for (int u = 0; u < PR; ++u) fetch(t0 + u, dr[u], br[u]);
+        for (int sb = 0; sb < L; sb += PR) {
+#pragma unroll
+            for (int u = 0; u < PR; ++u) {
+                const int t = t0 + sb + u;
+                ACC a0 = 0, a1 = 0;
+#pragma unroll
+                for (int k = 0; k < DP; k += 2) {
+                    a0 += wrow[k] * __shfl(st, gbase + k, 64);
+                    if (k + 1 < DP) a1 += wrow[k + 1] * __shfl(st, gbase + k + 1, 64);
+                }
+                const ACC acc = static_cast<ACC>(dr[u]) * (a0 + a1) + static_cast<ACC>(br[u]);
+                fetch(t + PR, dr[u], br[u]);
+                const bool live = t < t1;
+                st = live && jv ? acc : st;
+                if (live && act && jv) out[(seq + t) * D + j] = static_cast<float>(st);
+            }
+        }
+    } else {
+        for (int s = 0; s < L; ++s) {
+            const int t = t0 + s;
+            const bool live = t < t1;
+            const int tt = live ? t : t0;
+            const ACC bj = jv ? static_cast<ACC>(bv[(seq + tt) * D + j]) : ACC(0);
+            ACC acc = 0;
 #pragma unroll
             for (int k = 0; k < DP; ++k) {
                 const ACC akj = (jv && k < D) ? static_cast<ACC>(A[((seq + tt) * D + j) * D + k]) : ACC(0);
                 acc += akj * __shfl(st, gbase + k, 64);
             }
             acc = acc + bj;
-        }
-        if (live) {
-            st = acc;
-            if (act && jv) out[(seq + t) * D + j] = static_cast<float>(st);
+            if (live) {
+                st = acc;
+                if (act && jv) out[(seq + t) * D + j] = static_cast<float>(st);
+            }
         }
     }
 }
@@ -410,11 +630,10 @@ int launch_dense_dp(const float *A, const float *d, const float *W, const float 
     const long long nq = static_cast<long long>(pl.B) * pl.nchunk;
     const long long waves = (nq + G - 1) / G;
     const unsigned blocks = static_cast<unsigned>((waves + 3) / 4);
-    const unsigned cblocks = static_cast<unsigned>((pl.B + 3) / 4);
     const bool f64 = sizeof(ACC) == 8;
     if (d && DP == 32 && pl.D == 32 && !f64) {
-        hipLaunchKernelGGL(dense_agg_mfma32_kernel, dim3(static_cast<unsigned>(nq)), dim3(64), 0, stream, d, W, b, skip,
-                           all_done, pl.T, pl.chunk_len, pl.nchunk, reinterpret_cast<float *>(Pagg),
+        hipLaunchKernelGGL(dense_agg_mfma32_kernel, dim3(static_cast<unsigned>(nq)), dim3(kAggThreads), 0, stream, d, W,
+                           b, skip, all_done, pl.T, pl.chunk_len, pl.nchunk, reinterpret_cast<float *>(Pagg),
                            reinterpret_cast<float *>(Bagg));
     } else if (d && DP == 16 && pl.D == 16) {
         hipLaunchKernelGGL((dense_agg_mfma16_kernel<ACC>), dim3(static_cast<unsigned>(nq)), dim3(64), 0, stream, d, W,
@@ -427,12 +646,24 @@ int launch_dense_dp(const float *A, const float *d, const float *W, const float 
                            skip, all_done, pl.B, pl.T, pl.D, pl.chunk_len, pl.nchunk, Pagg, Bagg);
     }
     DEER_HIP(hipGetLastError());
-    hipLaunchKernelGGL((dense_carry_kernel<DP, ACC>), dim3(cblocks), dim3(kThreads), 0, stream, Pagg, Bagg, s0, skip,
-                       all_done, pl.B, pl.D, pl.nchunk, carry);
+    constexpr bool kVecOk = CarryGeom<DP, ACC>::KG % CarryGeom<DP, ACC>::VEC == 0;
+    if (kVecOk && pl.D == DP)
+        hipLaunchKernelGGL((dense_carry_kernel<DP, ACC, kVecOk>), dim3(static_cast<unsigned>(pl.B)), dim3(64), 0, stream,
+                           Pagg, Bagg, s0, skip, all_done, pl.B, pl.D, pl.nchunk, carry);
+    else
+        hipLaunchKernelGGL((dense_carry_kernel<DP, ACC, false>), dim3(static_cast<unsigned>(pl.B)), dim3(64), 0, stream,
+                           Pagg, Bagg, s0, skip, all_done, pl.B, pl.D, pl.nchunk, carry);
     DEER_HIP(hipGetLastError());
     if (d) {
-        hipLaunchKernelGGL((dense_replay_kernel<DP, true, ACC>), dim3(blocks), dim3(kThreads), 0, stream, A, d, W, b,
-                           carry, skip, all_done, pl.B, pl.T, pl.D, pl.chunk_len, pl.nchunk, out0, out1, out_sel);
+        const unsigned rblocks = static_cast<unsigned>((nq + kThreads / 64 - 1) / (kThreads / 64));
+        if (pl.D == DP && CarryGeom<DP, ACC>::G * DP == 64)       // every lane owns a row
+            hipLaunchKernelGGL((dense_replay_fact_kernel<DP, ACC, true>), dim3(rblocks), dim3(kThreads), 0, stream, d,
+                               W, b, carry, skip, all_done, pl.B, pl.T, pl.D, pl.chunk_len, pl.nchunk, out0, out1,
+                               out_sel);
+        else
+            hipLaunchKernelGGL((dense_replay_fact_kernel<DP, ACC, false>), dim3(rblocks), dim3(kThreads), 0, stream, d,
+                               W, b, carry, skip, all_done, pl.B, pl.T, pl.D, pl.chunk_len, pl.nchunk, out0, out1,
+                               out_sel);
     } else {
         hipLaunchKernelGGL((dense_replay_kernel<DP, false, ACC>), dim3(blocks), dim3(kThreads), 0, stream, A, d, W, b,
                            carry, skip, all_done, pl.B, pl.T, pl.D, pl.chunk_len, pl.nchunk, out0, out1, out_sel);
@@ -470,6 +701,7 @@ DenseScanPlan dense_scan_plan(int B, int T, int D)
     p.T = T;
     p.D = D;
     // Long chunks shorten the carry walk; short ones give enough chunks to fill the chip.
+    // L stays a multiple of 16 (the replay's prefetch depth).
     int L = 64;
     while (L > 16 && static_cast<long long>(B) * ((T + L - 1) / L) < 8192) L /= 2;
     p.chunk_len = L;

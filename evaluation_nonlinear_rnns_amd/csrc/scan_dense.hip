@@ -141,6 +141,83 @@ __global__ __launch_bounds__(kThreads) void dense_agg_kernel(
 // Row of the 32x32 accumulator held in register v by a lane of half hf.
 __device__ __forceinline__ int row32(int v, int hf) { return 8 * (v >> 2) + 4 * hf + (v & 3); }
 
+// Offset chain of a D = 32 chunk on one wavefront: B_s = d_s (W B_{s-1}) + b_s
+// from B_0 = b_0, written to out[0..31].  The state is split into two blocks of
+// 16; each 16-lane row holds one block K of the input and contracts the 16 x 16
+// block (I, K) of W against it with row rotations (DPP), so every term is one
+// FMA on registers.  The two rows that share an output block I then add their
+// partial sums with one exchange.  Steps alternate between two row layouts --
+// A: K = r & 1, I = r >> 1, partner lane ^ 16; B: K = r >> 1, I = r & 1,
+// partner lane ^ 32 -- because the output blocks of an A step sit exactly where
+// a B step expects its input blocks, and the other way round.
+template <int K>
+__device__ __forceinline__ int row_ror(int v)   // DPP rotation by K lanes within each row of 16
+{
+    return __builtin_amdgcn_update_dpp(0, v, 0x120 + K, 0xf, 0xf, true);
+}
+
+template <int K>
+struct RowRotations {
+    static __device__ __forceinline__ void sources(int m, int (&src)[16])
+    {
+        src[K] = row_ror<K>(m);
+        RowRotations<K + 1>::sources(m, src);
+    }
+    static __device__ __forceinline__ void contract(float x, const float (&w)[16], float &a0, float &a1)
+    {
+        const float xr = __int_as_float(row_ror<K>(__float_as_int(x)));
+        if (K & 1) a1 += w[K] * xr; else a0 += w[K] * xr;
+        RowRotations<K + 1>::contract(x, w, a0, a1);
+    }
+};
+template <>
+struct RowRotations<16> {
+    static __device__ __forceinline__ void sources(int, int (&)[16]) {}
+    static __device__ __forceinline__ void contract(float, const float (&)[16], float &, float &) {}
+};
+
+__device__ __forceinline__ void offset_chain32(const float *__restrict__ W, const float *ds, const float *bs, int n,
+                                               float *__restrict__ out)
+{
+    constexpr int D = 32;
+    const int lane = threadIdx.x & 63, r = lane >> 4, m = lane & 15;
+    // source lane (within the row) that rotation k delivers to this lane, measured
+    // by rotating the lane indices themselves
+    int src[16];
+    src[0] = m;
+    RowRotations<1>::sources(m, src);
+    const int KA = r & 1, IA = r >> 1, KB = r >> 1, IB = r & 1;
+    float wA[16], wB[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        wA[k] = W[(16 * IA + m) * D + 16 * KA + src[k]];
+        wB[k] = W[(16 * IB + m) * D + 16 * KB + src[k]];
+    }
+    auto contract = [&](float x, const float (&w)[16]) -> float {
+        float a0 = w[0] * x, a1 = 0.0f;
+        RowRotations<1>::contract(x, w, a0, a1);
+        return a0 + a1;
+    };
+    float x = bs[16 * KA + m];                        // B_0 in the A layout
+    int s = 1;
+    for (; s + 1 < n; s += 2) {
+        float y = contract(x, wA);                    // A step: output block IA
+        y += __shfl_xor(y, 16, 64);
+        x = ds[s * D + 16 * IA + m] * y + bs[s * D + 16 * IA + m];
+        y = contract(x, wB);                          // B step: output block IB
+        y += __shfl_xor(y, 32, 64);
+        x = ds[(s + 1) * D + 16 * IB + m] * y + bs[(s + 1) * D + 16 * IB + m];
+    }
+    int I = KA;                                       // block held after an even number of steps (A layout)
+    if (s < n) {
+        float y = contract(x, wA);
+        y += __shfl_xor(y, 16, 64);
+        x = ds[s * D + 16 * IA + m] * y + bs[s * D + 16 * IA + m];
+        I = IA;
+    }
+    out[16 * I + m] = x;                              // rows holding the same block write the same values
+}
+
 // D = 32, factored leaves, float32: one 128-thread workgroup per chunk.  Its
 // first wavefront runs the product chain on the matrix cores, the second the
 // offset chain on VALU; both read the chunk's d_t and b_t from LDS, so the two
@@ -184,19 +261,7 @@ __global__ __launch_bounds__(kAggThreads) void dense_agg_mfma32_kernel(
     __syncthreads();
 
     if (wave == 1) {
-        // offset B_s = d_s (W B_{s-1}) + b_s, B_0 = b_0; lane j < 32 owns row j
-        float Wrow[D];
-#pragma unroll
-        for (int k = 0; k < D; ++k) Wrow[k] = W[j * D + k];
-        float Bq = bs[j];
-        for (int s = 1; s < n; ++s) {
-            float h[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int k = 0; k < D; ++k)
-                h[k & 3] += Wrow[k] * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Bq), k));
-            Bq = ds[s * D + j] * ((h[0] + h[1]) + (h[2] + h[3])) + bs[s * D + j];
-        }
-        if (hf == 0) Bout[static_cast<size_t>(q) * D + j] = Bq;
+        offset_chain32(W, ds, bs, n, Bout + static_cast<size_t>(q) * D);
         return;
     }
 
@@ -465,37 +530,129 @@ __global__ __launch_bounds__(64) void dense_carry_kernel(
 }
 
 // ----------------------------------------------------------------- replay
+// Stage a chunk's d_t and b_t rows ([n][D] each, contiguous at base) into LDS
+// with one wavefront, every load of a round in flight at once.
+__device__ __forceinline__ void stage_chunk64(const float *__restrict__ dv, const float *__restrict__ bv, size_t base,
+                                              int nel, int D, float *dsm, float *bsm)
+{
+    const int lane = threadIdx.x & 63;
+    if ((D & 3) == 0) {
+        constexpr int kU = 8;                           // float4 loads per array per lane per round
+        for (int e0 = 0; e0 < nel / 4; e0 += 64 * kU) {
+            v4f dq[kU], bq[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int e = e0 + lane + 64 * u;
+                const int ec = e < nel / 4 ? e : 0;
+                dq[u] = *reinterpret_cast<const v4f *>(dv + base + static_cast<size_t>(ec) * 4);
+                bq[u] = *reinterpret_cast<const v4f *>(bv + base + static_cast<size_t>(ec) * 4);
+            }
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int e = e0 + lane + 64 * u;
+                if (e < nel / 4) {
+                    *reinterpret_cast<v4f *>(dsm + e * 4) = dq[u];
+                    *reinterpret_cast<v4f *>(bsm + e * 4) = bq[u];
+                }
+            }
+        }
+    } else {
+        for (int e = lane; e < nel; e += 64) {
+            dsm[e] = dv[base + e];
+            bsm[e] = bv[base + e];
+        }
+    }
+}
+
+// D = 32, float32: the replay on the offset chain's row layout (two blocks of
+// 16, DPP row rotations, one exchange per step, alternating A / B layouts);
+// each step's state is written by both rows that hold a block.
+__global__ __launch_bounds__(64) void dense_replay_dpp32_kernel(
+    const float *__restrict__ dv, const float *__restrict__ W, const float *__restrict__ bv,
+    const float *__restrict__ carry, const int *__restrict__ skip, const int *__restrict__ all_done, int T, int L,
+    int nchunk, float *out0, float *out1, const int *__restrict__ out_sel)
+{
+    constexpr int D = 32;
+    __shared__ float dsm[64 * D], bsm[64 * D];
+    if (all_done && *all_done) return;
+    const long long q = blockIdx.x;
+    const int bseq = static_cast<int>(q / nchunk), c = static_cast<int>(q % nchunk);
+    if (skip && skip[bseq]) return;
+    const int t0 = c * L, n = min(L, T - t0);
+    const size_t base = (static_cast<size_t>(bseq) * T + t0) * D;
+    stage_chunk64(dv, bv, base, n * D, D, dsm, bsm);
+    __syncthreads();
+
+    const int lane = threadIdx.x, r = lane >> 4, m = lane & 15;
+    int src[16];
+    src[0] = m;
+    RowRotations<1>::sources(m, src);
+    const int KA = r & 1, IA = r >> 1, KB = r >> 1, IB = r & 1;
+    float wA[16], wB[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        wA[k] = W[(16 * IA + m) * D + 16 * KA + src[k]];
+        wB[k] = W[(16 * IB + m) * D + 16 * KB + src[k]];
+    }
+    auto contract = [&](float x, const float (&w)[16]) -> float {
+        float a0 = w[0] * x, a1 = 0.0f;
+        RowRotations<1>::contract(x, w, a0, a1);
+        return a0 + a1;
+    };
+    float *out = ((out_sel && (*out_sel & 1)) ? out1 : out0) + base;
+    float x = carry[static_cast<size_t>(q) * D + 16 * KA + m];      // carried-in state, A layout
+    int s = 0;
+    for (; s + 1 < n; s += 2) {
+        float y = contract(x, wA);
+        y += __shfl_xor(y, 16, 64);
+        x = dsm[s * D + 16 * IA + m] * y + bsm[s * D + 16 * IA + m];
+        out[s * D + 16 * IA + m] = x;
+        y = contract(x, wB);
+        y += __shfl_xor(y, 32, 64);
+        x = dsm[(s + 1) * D + 16 * IB + m] * y + bsm[(s + 1) * D + 16 * IB + m];
+        out[(s + 1) * D + 16 * IB + m] = x;
+    }
+    if (s < n) {
+        float y = contract(x, wA);
+        y += __shfl_xor(y, 16, 64);
+        x = dsm[s * D + 16 * IA + m] * y + bsm[s * D + 16 * IA + m];
+        out[s * D + 16 * IA + m] = x;
+    }
+}
+
 // Factored leaves: one wavefront per chunk re-runs s_t = d_t * (W s_{t-1}) + b_t
-// from the chunk's carried-in state.  Lane (grp, j) owns row j and the KG
-// columns of its group (the carry walk's split); d_t and b_t are fetched PR
-// steps ahead with unconditional, clamped loads.  When every lane owns a row
-// (D == DP and the groups fill the wavefront) every group writes the
-// (identical) new state and steps past the end of a short last chunk rewrite
-// its final state, so the step body has no branch.
+// from the chunk's carried-in state.  The chunk's d_t and b_t rows are staged
+// in LDS first (every load in flight at once), so the step chain only waits on
+// LDS.  Lane (grp, j) owns row j and the KG columns of its group (the carry
+// walk's split).  When every lane owns a row (D == DP and the groups fill the
+// wavefront) every group writes the (identical) new state, so the step body
+// has no branch.
 template <int DP, class ACC, bool FULL>
-__global__ __launch_bounds__(kThreads) void dense_replay_fact_kernel(
+__global__ __launch_bounds__(64) void dense_replay_fact_kernel(
     const float *__restrict__ dv, const float *__restrict__ W, const float *__restrict__ bv,
     const ACC *__restrict__ carry, const int *__restrict__ skip, const int *__restrict__ all_done, int B, int T,
     int D, int L, int nchunk, float *out0, float *out1, const int *__restrict__ out_sel)
 {
     using Gm = CarryGeom<DP, ACC>;
     constexpr int G = Gm::G, KG = Gm::KG;
-    constexpr int PR = 16;                              // chunk lengths are multiples of PR
+    extern __shared__ float rsm[];                  // d rows [L][D], then b rows [L][D]
     if (all_done && *all_done) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const long long q = static_cast<long long>(blockIdx.x) * (kThreads / 64) + wave;
-    if (q >= static_cast<long long>(B) * nchunk) return;            // uniform per wavefront
+    const long long q = blockIdx.x;
     const int bseq = static_cast<int>(q / nchunk), c = static_cast<int>(q % nchunk);
     if (skip && skip[bseq]) return;
+    const int lane = threadIdx.x;
+    const int t0 = c * L, n = min(L, T - t0);
+    const size_t base = (static_cast<size_t>(bseq) * T + t0) * D;
+    float *dsm = rsm, *bsm = rsm + L * D;
+    stage_chunk64(dv, bv, base, n * D, D, dsm, bsm);
+    __syncthreads();
+
     const int grp = lane / DP, j = lane % DP;
     const bool act = grp < G;
     const bool jv = act && j < D;
     const int jr = j < D ? j : D - 1;
     const int k0 = act ? grp * KG : 0;
-    const int t0 = c * L, t1 = min(T, t0 + L);
-    const size_t seq = static_cast<size_t>(bseq) * T;
     float *out = (out_sel && (*out_sel & 1)) ? out1 : out0;
-
     ACC wseg[KG];
 #pragma unroll
     for (int i = 0; i < KG; ++i) {
@@ -505,36 +662,23 @@ __global__ __launch_bounds__(kThreads) void dense_replay_fact_kernel(
     }
     ACC st = carry[static_cast<size_t>(q) * D + jr];
     st = jv ? st : ACC(0);
-    float dr[PR], br[PR];
-    auto fetch = [&](int t, float &dd, float &bb) {
-        const size_t i = (seq + (t < t1 ? t : t1 - 1)) * D + jr;
-        dd = dv[i];
-        bb = bv[i];
-    };
+    float *orow = out + base + j;
+    for (int s = 0; s < n; ++s) {
+        ACC a0 = 0, a1 = 0;
 #pragma unroll
-    for (int u = 0; u < PR; ++u) fetch(t0 + u, dr[u], br[u]);
-    for (int sb = 0; sb < L; sb += PR) {
+        for (int i = 0; i < KG; i += 2) {
+            a0 += wseg[i] * __shfl(st, k0 + i, 64);
+            if (i + 1 < KG) a1 += wseg[i + 1] * __shfl(st, k0 + i + 1, 64);
+        }
+        ACC acc = a0 + a1;
 #pragma unroll
-        for (int u = 0; u < PR; ++u) {
-            const int t = t0 + sb + u;
-            ACC a0 = 0, a1 = 0;
-#pragma unroll
-            for (int i = 0; i < KG; i += 2) {
-                a0 += wseg[i] * __shfl(st, k0 + i, 64);
-                if (i + 1 < KG) a1 += wseg[i + 1] * __shfl(st, k0 + i + 1, 64);
-            }
-            ACC acc = a0 + a1;
-#pragma unroll
-            for (int o = DP; o < G * DP; o <<= 1) acc += __shfl_xor(acc, o, 64);
-            const ACC y = static_cast<ACC>(dr[u]) * acc + static_cast<ACC>(br[u]);
-            fetch(t + PR, dr[u], br[u]);
-            const bool live = t < t1;
-            st = (live && jv) ? y : st;
-            if constexpr (FULL) {
-                out[(seq + (live ? t : t1 - 1)) * D + j] = static_cast<float>(st);
-            } else {
-                if (grp == 0 && jv && live) out[(seq + t) * D + j] = static_cast<float>(st);
-            }
+        for (int o = DP; o < G * DP; o <<= 1) acc += __shfl_xor(acc, o, 64);
+        const ACC y = static_cast<ACC>(dsm[s * D + jr]) * acc + static_cast<ACC>(bsm[s * D + jr]);
+        st = jv ? y : st;
+        if constexpr (FULL) {
+            orow[static_cast<size_t>(s) * D] = static_cast<float>(st);
+        } else {
+            if (grp == 0 && jv) orow[static_cast<size_t>(s) * D] = static_cast<float>(st);
         }
     }
 }
@@ -654,16 +798,20 @@ int launch_dense_dp(const float *A, const float *d, const float *W, const float 
         hipLaunchKernelGGL((dense_carry_kernel<DP, ACC, false>), dim3(static_cast<unsigned>(pl.B)), dim3(64), 0, stream,
                            Pagg, Bagg, s0, skip, all_done, pl.B, pl.D, pl.nchunk, carry);
     DEER_HIP(hipGetLastError());
-    if (d) {
-        const unsigned rblocks = static_cast<unsigned>((nq + kThreads / 64 - 1) / (kThreads / 64));
+    if (d && DP == 32 && pl.D == 32 && !f64) {
+        hipLaunchKernelGGL(dense_replay_dpp32_kernel, dim3(static_cast<unsigned>(nq)), dim3(64), 0, stream, d, W, b,
+                           reinterpret_cast<const float *>(carry), skip, all_done, pl.T, pl.chunk_len, pl.nchunk, out0,
+                           out1, out_sel);
+    } else if (d) {
+        const size_t lds = static_cast<size_t>(pl.chunk_len) * pl.D * 2 * sizeof(float);
         if (pl.D == DP && CarryGeom<DP, ACC>::G * DP == 64)       // every lane owns a row
-            hipLaunchKernelGGL((dense_replay_fact_kernel<DP, ACC, true>), dim3(rblocks), dim3(kThreads), 0, stream, d,
-                               W, b, carry, skip, all_done, pl.B, pl.T, pl.D, pl.chunk_len, pl.nchunk, out0, out1,
-                               out_sel);
+            hipLaunchKernelGGL((dense_replay_fact_kernel<DP, ACC, true>), dim3(static_cast<unsigned>(nq)), dim3(64), lds,
+                               stream, d, W, b, carry, skip, all_done, pl.B, pl.T, pl.D, pl.chunk_len, pl.nchunk, out0,
+                               out1, out_sel);
         else
-            hipLaunchKernelGGL((dense_replay_fact_kernel<DP, ACC, false>), dim3(rblocks), dim3(kThreads), 0, stream, d,
-                               W, b, carry, skip, all_done, pl.B, pl.T, pl.D, pl.chunk_len, pl.nchunk, out0, out1,
-                               out_sel);
+            hipLaunchKernelGGL((dense_replay_fact_kernel<DP, ACC, false>), dim3(static_cast<unsigned>(nq)), dim3(64), lds,
+                               stream, d, W, b, carry, skip, all_done, pl.B, pl.T, pl.D, pl.chunk_len, pl.nchunk, out0,
+                               out1, out_sel);
     } else {
         hipLaunchKernelGGL((dense_replay_kernel<DP, false, ACC>), dim3(blocks), dim3(kThreads), 0, stream, A, d, W, b,
                            carry, skip, all_done, pl.B, pl.T, pl.D, pl.chunk_len, pl.nchunk, out0, out1, out_sel);
@@ -701,7 +849,6 @@ DenseScanPlan dense_scan_plan(int B, int T, int D)
     p.T = T;
     p.D = D;
     // Long chunks shorten the carry walk; short ones give enough chunks to fill the chip.
-    // L stays a multiple of 16 (the replay's prefetch depth).
     int L = 64;
     while (L > 16 && static_cast<long long>(B) * ((T + L - 1) / L) < 8192) L /= 2;
     p.chunk_len = L;

@@ -34,7 +34,7 @@
 #endif
 
 enum { ORC_CELL_TANH = 0, ORC_CELL_GRU = 1, ORC_CELL_LINEAR = 2 };
-enum { ORC_MODE_DENSE = 0, ORC_MODE_DIAG = 1 };
+enum { ORC_MODE_DENSE = 0, ORC_MODE_DIAG = 1, ORC_MODE_JACOBI = 2, ORC_MODE_PICARD = 3 };
 
 typedef struct {
     int cell;        /* ORC_CELL_* */
@@ -157,11 +157,14 @@ int ORC_CAT(orc_solve_dense, SUF)(const float *A, const float *bv, const float *
 }                                                                                                \
                                                                                                  \
 int ORC_CAT(orc_newton, SUF)(const orc_cell *c, const float *x, const float *s0, int B, int T,   \
-                             int mode, double tol, int max_iter, const float *init, REAL *traj,  \
-                             int *iters, double *resid, int *status, double *hist, int threads)  \
+                             int mode, double damp, double tol, int max_iter, const float *init, \
+                             REAL *traj, int *iters, double *resid, int *status, double *hist,   \
+                             int threads)                                                        \
 {                                                                                                \
     if (!c || !traj || !iters || !resid || !status || B < 0 || T < 0 || c->D <= 0 ||            \
-        max_iter < 0 || (mode != ORC_MODE_DENSE && mode != ORC_MODE_DIAG)) return -1;            \
+        max_iter < 0 || mode < ORC_MODE_DENSE || mode > ORC_MODE_PICARD ||                       \
+        !(damp >= 0.0 && damp <= 1.0) ||                                                         \
+        (damp != 0.0 && mode != ORC_MODE_DENSE && mode != ORC_MODE_DIAG)) return -1;            \
     int err = 0;                                                                                 \
     const int D = c->D;                                                                          \
     const size_t TD = (size_t)T * D;                                                             \
@@ -172,7 +175,8 @@ int ORC_CAT(orc_newton, SUF)(const orc_cell *c, const float *x, const float *s0,
         REAL *work = (REAL *)malloc(sizeof(REAL) * (3 * TD + 7 * (size_t)D + asz));              \
         if (!work) { err |= 1; continue; }                                                       \
         status[b] = ORC_CAT(o_newton_one, SUF)(c, x + (size_t)b * T * c->M,                     \
-                                               s0 ? s0 + (size_t)b * D : NULL, T, mode, tol,     \
+                                               s0 ? s0 + (size_t)b * D : NULL, T, mode, damp,    \
+                                               tol,                                              \
                                                max_iter, init ? init + (size_t)b * TD : NULL,    \
                                                traj + (size_t)b * TD, iters + b, resid + b,      \
                                                hist ? hist + (size_t)b * (max_iter + 1) : NULL,  \

@@ -22,7 +22,7 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _SOURCES = [os.path.join(_HERE, "oracle.c"), os.path.join(_HERE, "orc_impl.h")]
 
 CELLS = {"tanh": 0, "gru": 1, "linear": 2}
-MODES = {"dense": 0, "diag": 1}
+MODES = {"dense": 0, "diag": 1, "jacobi": 2, "picard": 3}
 STATUS = {0: "converged", 1: "not_converged", 2: "nonfinite"}
 
 
@@ -170,8 +170,11 @@ def solve_dense(A, b, s0=None, precision: str = "f64", threads: int = 0) -> np.n
 
 
 def newton(cell: Cell, x, s0=None, mode: str = "dense", tol: float = 1e-6, max_iter: int = 100,
-           precision: str = "f32", init=None, threads: int = 0, history: bool = False):
-    """Parallel Newton (``mode="dense"``) or diagonal quasi-Newton (``"diag"``).
+           precision: str = "f32", init=None, threads: int = 0, history: bool = False, damping: float = 0.0):
+    """Fixed-point iteration of one linearisation: parallel Newton (``"dense"``),
+    diagonal quasi-Newton (``"diag"``), Jacobi (``"jacobi"``, A_t = 0) or Picard
+    (``"picard"``, A_t = I).  ``damping`` k in [0, 1] shrinks the Jacobian (or its
+    diagonal) to ``(1 - k) J`` in the dense and diag modes.
 
     Returns ``(traj [B,T,D], iters [B], resid [B], status [B])`` and, with
     ``history=True``, the residual at every iteration ``[B, max_iter+1]``.
@@ -188,7 +191,7 @@ def newton(cell: Cell, x, s0=None, mode: str = "dense", tol: float = 1e-6, max_i
     status = np.zeros(B, np.int32)
     hist = np.full((B, max_iter + 1), np.nan) if history else None
     rc = getattr(lib(), "orc_newton_" + precision)(
-        cell.ref, _ptr(x), _ptr(s0), B, T, MODES[mode], ctypes.c_double(tol), int(max_iter),
+        cell.ref, _ptr(x), _ptr(s0), B, T, MODES[mode], ctypes.c_double(damping), ctypes.c_double(tol), int(max_iter),
         _ptr(init), _ptr(traj), _ptr(iters), _ptr(resid), _ptr(status), _ptr(hist), threads)
     if rc != 0:
         raise RuntimeError("orc_newton failed")

@@ -125,26 +125,35 @@ static void FN(o_solve_dense_one)(const REAL *A, const REAL *b, const REAL *s0, 
 }
 
 /*
- * Parallel-Newton fixed-point iteration for one sequence, with the linear
- * recurrence solved by sequential forward substitution.
+ * Fixed-point iteration of a chosen linearisation for one sequence, with the
+ * linear recurrence solved by sequential forward substitution.
  *
  * Residual r_t(s) = s_t - f(s_{t-1}, x_t) (the "Predictability Enables
  * Parallelization" page, rebuttal, where it restates its equation 2); the
  * trajectory is its root.  Each iteration i:
- *   f_t, J_t at the current guess s^(i)  (s^(i)_0 := s_0)
+ *   f_t (and J_t where the mode needs it) at the current guess s^(i)  (s^(i)_0 := s_0)
  *   res = max_{t,d} |s^(i)_t - f_t|      (NaN counts as not converged)
  *   stop if res <= tol (iters = i), or if i == max_iter (not converged)
- *   A_t = J_t (dense) or diag(J_t) (diag), b_t = f_t - A_t s^(i)_{t-1}
- *   s^(i+1) solves s_t = A_t s_{t-1} + b_t from s_0
- * ("Parallel Broyden Methods" page, section 2 problem statement and the
- * exact / diagonal quasi-Newton paragraphs.)
+ *   A_t by mode, b_t = f_t - A_t s^(i)_{t-1}, and s^(i+1) solves
+ *   s_t = A_t s_{t-1} + b_t from s_0.
+ * The modes are the approximate linearisations the pages compare (the first
+ * page's thread: every method linearises the dynamics, then evaluates the
+ * linear recurrence in parallel; "Parallel Broyden Methods", section 2):
+ *   dense  : A_t = (1 - k) J_t              (Newton / DEER; k = 0 undamped)
+ *   diag   : A_t = (1 - k) diag(J_t)        (diagonal quasi-Newton)
+ *   jacobi : A_t = 0, so s^(i+1)_t = f_t
+ *   picard : A_t = I, so s^(i+1)_t = s^(i+1)_{t-1} + (f_t - s^(i)_{t-1})
+ * k is the damping of the scale-ELK method: the full Jacobian block shrunk by
+ * the factor 1 - k ("Parallel Broyden Methods", appendix E.4; its Gibbs
+ * appendix damps Newton this way to avoid float32 overflow).  The offsets use
+ * the same A_t, so every mode keeps the trajectory as its fixed point.
  *
  * hist (optional, max_iter+1 entries) receives res at every iteration (NaN
  * after the stop).  Returns the status: 0 converged, 1 not converged within
  * max_iter, 2 the residual is not finite when the cap is reached.
  */
 static int FN(o_newton_one)(const orc_cell *c, const float *x, const float *s0, int T, int mode,
-                              double tol, int max_iter, const float *init,
+                              double damp, double tol, int max_iter, const float *init,
                               REAL *s /*[T,D] in: ignored, out: final iterate*/,
                               int *iters_out, double *resid_out, double *hist,
                               REAL *work)
@@ -163,6 +172,7 @@ static int FN(o_newton_one)(const orc_cell *c, const float *x, const float *s0, 
     if (hist)
         for (int i = 0; i <= max_iter; ++i) hist[i] = NAN;
 
+    const REAL shrink = (REAL)(1.0 - damp);
     for (int it = 0;; ++it) {
         double res = 0.0;
         int nonfinite = 0;
@@ -188,6 +198,29 @@ static int FN(o_newton_one)(const orc_cell *c, const float *x, const float *s0, 
             *iters_out = max_iter;
             *resid_out = res;
             return (res == res && !isinf(res)) ? 1 : 2;
+        }
+        if (mode == ORC_MODE_JACOBI) {          /* A_t = 0: the next iterate is f itself */
+            memcpy(s, f, TD * sizeof(REAL));
+            continue;
+        }
+        if (mode == ORC_MODE_PICARD) {          /* A_t = I: accumulate the one-step corrections */
+            for (int t = 0; t < T; ++t)
+                for (int d = 0; d < D; ++d) {
+                    const REAL prev_old = (t == 0) ? s0r[d] : s[(size_t)(t - 1) * D + d];
+                    bb[(size_t)t * D + d] = f[(size_t)t * D + d] - prev_old;
+                }
+            for (int t = 0; t < T; ++t)
+                for (int d = 0; d < D; ++d) {
+                    const REAL prev_new = (t == 0) ? s0r[d] : sn[(size_t)(t - 1) * D + d];
+                    sn[(size_t)t * D + d] = prev_new + bb[(size_t)t * D + d];
+                }
+            memcpy(s, sn, TD * sizeof(REAL));
+            continue;
+        }
+        /* damping: A_t = (1 - k) J_t (or its diagonal) */
+        {
+            const size_t na = (mode == ORC_MODE_DENSE) ? TD * D : TD;
+            for (size_t e = 0; e < na; ++e) A[e] = shrink * A[e];
         }
         /* offsets b_t = f_t - A_t s_{t-1}, with the same A_t the solve uses */
         for (int t = 0; t < T; ++t) {

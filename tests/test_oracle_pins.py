@@ -460,3 +460,117 @@ def test_stop_rule_edges(orc):
     # the exact prefix before the NaN is untouched
     r64 = orc.rollout(c, p["x"])
     assert np.abs(tr[1, :5] - r64[1, :5]).max() < 1e-6
+
+
+# ------------------------------------------- other linearisations and damping
+
+@pytest.mark.parametrize("mode,damping", [("jacobi", 0.0), ("picard", 0.0), ("dense", 0.5), ("diag", 0.3),
+                                          ("dense", 1.0)])
+def test_finite_step_recovery_other_linearisations(orc, mode, damping):
+    """Finite-step recovery holds for any blocks A_t: after i iterations the first
+    i states are exact ("Parallel Broyden Methods" page, Theorem 1, section 3.2)."""
+    T, D = 10, 3
+    p = I.tanh_problem(91, 2, T, D, D, gain=1.1, bias_std=0.3, s0_std=0.5)
+    c = orc.Cell.from_problem(p)
+    r64 = orc.rollout(c, p["x"], p["s0"])
+    init = np.random.default_rng(9).standard_normal(r64.shape).astype(np.float32)
+    for i in range(1, T + 1):
+        tr, it, _, _ = orc.newton(c, p["x"], p["s0"], mode=mode, tol=-1.0, max_iter=i, precision="f64",
+                                  init=init, damping=damping)
+        assert list(it) == [i, i]
+        assert np.abs(tr[:, :i] - r64[:, :i]).max() < 1e-9, i
+    tr, it, _, st = orc.newton(c, p["x"], p["s0"], mode=mode, tol=1e-12, max_iter=T + 2, precision="f64",
+                               init=init, damping=damping)
+    assert all(st == 0) and all(it <= T)
+    assert np.abs(tr - r64).max() < 1e-11
+
+
+def test_jacobi_when_f_ignores_the_state(orc):
+    """W = 0 makes f_t = tanh(U x_t + b) independent of the state: Jacobi (A_t = 0)
+    lands on it in exactly one iteration, from any start."""
+    p = I.tanh_problem(92, 2, 40, 5, 4, gain=1.0, bias_std=0.4, s0_std=0.5)
+    c = orc.Cell("tanh", np.zeros_like(p["W"]), p["U"], p["b"])
+    want = np.tanh(np.einsum("dm,btm->btd", p["U"].astype(np.float64), p["x"].astype(np.float64))
+                   + p["b"].astype(np.float64))
+    init = np.random.default_rng(3).standard_normal(want.shape).astype(np.float32)
+    tr, it, _, st = orc.newton(c, p["x"], p["s0"], mode="jacobi", tol=1e-12, max_iter=5, precision="f64",
+                               init=init)
+    assert list(it) == [1, 1] and all(st == 0)
+    np.testing.assert_allclose(tr, want, rtol=0, atol=1e-14)
+
+
+def test_picard_is_exact_for_identity_dynamics(orc):
+    """Picard linearises with the identity, which is exact when f(s, x) = s + g(x)
+    (an explicit-Euler accumulation, the case the pages give Picard for): one
+    iteration gives the cumulative sum s_t = s_0 + sum_{tau <= t} g(x_tau)."""
+    D, M, T = 4, 3, 50
+    p = I.tanh_problem(93, 2, T, D, M, gain=1.0, bias_std=0.5, s0_std=0.5)
+    c = orc.Cell("linear", np.eye(D, dtype=np.float32), p["U"], p["b"])
+    g = np.einsum("dm,btm->btd", p["U"].astype(np.float64), p["x"].astype(np.float64)) + p["b"].astype(np.float64)
+    want = p["s0"].astype(np.float64)[:, None, :] + np.cumsum(g, axis=1)
+    tr, it, _, st = orc.newton(c, p["x"], p["s0"], mode="picard", tol=1e-10, max_iter=5, precision="f64")
+    assert list(it) == [1, 1] and all(st == 0)
+    np.testing.assert_allclose(tr, want, rtol=0, atol=1e-12)
+
+
+def test_picard_struggles_on_contractive_dynamics(orc):
+    """With W = 0 the dynamics are as contractive as can be: Jacobi needs one
+    iteration, Picard the full T (the first page: Picard struggles on contractive
+    systems where Newton and Jacobi excel).  Here the Picard error obeys
+    u^(i+1)_t = -sum_{tau < t} u^(i)_tau from u^(0) = -f, a closed form the
+    iterates must follow."""
+    D, M, T = 3, 2, 12
+    p = I.tanh_problem(94, 1, T, D, M, gain=1.0, bias_std=0.4, s0_std=0.0)
+    c = orc.Cell("tanh", np.zeros_like(p["W"]), p["U"], p["b"])
+    f = np.tanh(np.einsum("dm,btm->btd", p["U"].astype(np.float64), p["x"].astype(np.float64))
+                + p["b"].astype(np.float64))
+    u = -f.copy()                                          # error of the zero start
+    for i in range(1, 5):
+        u = -np.concatenate([np.zeros_like(u[:, :1]), np.cumsum(u, axis=1)[:, :-1]], axis=1)
+        tr, _, _, _ = orc.newton(c, p["x"], None, mode="picard", tol=-1.0, max_iter=i, precision="f64")
+        np.testing.assert_allclose(tr - f, u, rtol=0, atol=1e-12)
+    _, itj, _, _ = orc.newton(c, p["x"], None, mode="jacobi", tol=1e-12, max_iter=T + 2, precision="f64")
+    _, itp, _, stp = orc.newton(c, p["x"], None, mode="picard", tol=1e-12, max_iter=T + 2, precision="f64")
+    assert list(itj) == [1] and list(itp) == [T] and list(stp) == [0]
+
+
+@pytest.mark.parametrize("mode", ["dense", "diag"])
+def test_damping_limits(orc, mode):
+    """k = 0 is the undamped iteration and k = 1 shrinks the blocks to zero, which is
+    Jacobi -- both reproduced bit for bit; any k keeps the rollout as the fixed point."""
+    p = I.tanh_problem(95, 2, 60, 5, 4, gain=0.9, bias_std=0.3, s0_std=0.5)
+    c = orc.Cell.from_problem(p)
+    for prec in ("f32", "f64"):
+        for i in (1, 3, 6):
+            a, _, _, _ = orc.newton(c, p["x"], p["s0"], mode=mode, tol=-1.0, max_iter=i, precision=prec)
+            b, _, _, _ = orc.newton(c, p["x"], p["s0"], mode=mode, tol=-1.0, max_iter=i, precision=prec, damping=0.0)
+            j, _, _, _ = orc.newton(c, p["x"], p["s0"], mode="jacobi", tol=-1.0, max_iter=i, precision=prec)
+            k1, _, _, _ = orc.newton(c, p["x"], p["s0"], mode=mode, tol=-1.0, max_iter=i, precision=prec,
+                                     damping=1.0)
+            assert np.array_equal(a, b)
+            assert np.array_equal(j, k1)
+    r64 = orc.rollout(c, p["x"], p["s0"])
+    for k in (0.25, 0.6):
+        tr, _, _, st = orc.newton(c, p["x"], p["s0"], mode=mode, tol=1e-12, max_iter=60, precision="f64", damping=k)
+        assert all(st == 0) and np.abs(tr - r64).max() < 1e-11
+
+
+def test_damping_trades_iterations_for_stability(orc):
+    """Damping slows a predictable Newton solve (the blocks move away from the true
+    Jacobian) and keeps the iteration count between Newton's and Jacobi's."""
+    p = I.tanh_problem(96, 2, 200, 6, 6, gain=0.8, bias_std=0.3, s0_std=0.5)
+    c = orc.Cell.from_problem(p)
+    its = {}
+    for name, mode, k in (("newton", "dense", 0.0), ("damped", "dense", 0.5), ("jacobi", "jacobi", 0.0)):
+        _, it, _, st = orc.newton(c, p["x"], p["s0"], mode=mode, tol=1e-10, max_iter=200, precision="f64", damping=k)
+        assert all(st == 0)
+        its[name] = int(it.max())
+    assert its["newton"] < its["damped"] <= its["jacobi"]
+
+
+def test_damping_argument_checks(orc):
+    p = I.tanh_problem(97, 1, 8, 2, 2, gain=0.5)
+    c = orc.Cell.from_problem(p)
+    for mode, k in (("dense", -0.1), ("diag", 1.5), ("jacobi", 0.5), ("picard", 0.2), ("dense", float("nan"))):
+        with pytest.raises(RuntimeError):
+            orc.newton(c, p["x"], None, mode=mode, tol=1e-6, max_iter=3, precision="f64", damping=k)

@@ -181,14 +181,14 @@ int check_cell(const deer_cell_params_t *p, int mode_flags)
     if (!p) return fail(DEER_ERR_INVALID, "cell parameters: null pointer");
     if (p->cell != DEER_CELL_TANH && p->cell != DEER_CELL_GRU)
         return fail(DEER_ERR_INVALID, "cell parameters: unknown cell " + std::to_string(p->cell));
-    if (mode != DEER_MODE_DENSE && mode != DEER_MODE_DIAG)
+    if (mode < DEER_MODE_DENSE || mode > DEER_MODE_PICARD)
         return fail(DEER_ERR_INVALID, "unknown mode " + std::to_string(mode));
     if (p->D < 1 || p->D > kMaxD)
         return fail(DEER_ERR_UNSUPPORTED, "state size D=" + std::to_string(p->D) + " outside 1..64");
     if (p->M < 1 || p->M > kMaxM)
         return fail(DEER_ERR_UNSUPPORTED, "input size M=" + std::to_string(p->M) + " outside 1..1024");
-    if (p->cell == DEER_CELL_GRU && mode != DEER_MODE_DIAG)
-        return fail(DEER_ERR_UNSUPPORTED, "the GRU cell is supported in diag mode only");
+    if (p->cell == DEER_CELL_GRU && mode == DEER_MODE_DENSE)
+        return fail(DEER_ERR_UNSUPPORTED, "the GRU cell has no dense mode (diag, Jacobi and Picard are supported)");
     if (!p->W || !p->U) return fail(DEER_ERR_INVALID, "cell parameters: W and U are required");
     return DEER_OK;
 }
@@ -201,11 +201,15 @@ int check_sizes(int B, int T)
     return DEER_OK;
 }
 
-// The GRU in diag mode at D = 32 / 64 runs one fused evaluation + scan launch
-// per iteration; everything else runs evaluation and scan as two launches.
+// The diagonal-block modes (diag, Jacobi, Picard) solve with the diagonal scan.
+bool diag_blocks(int mode) { return mode != DEER_MODE_DENSE; }
+
+// The GRU in a diagonal-block mode at D = 32 / 64 runs one fused evaluation +
+// scan launch per iteration; everything else runs evaluation and scan as two
+// launches.
 bool fused_gru_step(const deer_cell_params_t *p, int mode)
 {
-    return p->cell == DEER_CELL_GRU && mode == DEER_MODE_DIAG && gru_fast_path(p->D, p->M);
+    return p->cell == DEER_CELL_GRU && diag_blocks(mode) && gru_fast_path(p->D, p->M);
 }
 
 // Layout of the deer_solve workspace.
@@ -235,7 +239,7 @@ SolveLayout solve_layout(void *ws, const deer_cell_params_t *p, int B, int T, in
     // the scan state comes first so that its header keeps a fixed place
     const bool fused = fused_gru_step(p, mode);
     const size_t scan_bytes = fused ? gru_step_state_bytes(B, T, p->D)
-                              : (mode == DEER_MODE_DIAG) ? diag_scan_state_bytes(B, T, p->D)
+                              : diag_blocks(mode) ? diag_scan_state_bytes(B, T, p->D)
                                                          : dense_scan_state_bytes(B, T, p->D, f64);
     L.scan = c.take<char>(scan_bytes);
     L.ctl = c.take<SolveControl>(1);
@@ -374,13 +378,18 @@ int deer_rollout(const deer_cell_params_t *p, const float *x, const float *s0, i
 }
 
 int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int B, int T, int mode_flags,
-               float tol, int max_iter, const float *init_guess, float *traj_out, int *iters_out, float *resid_out,
-               int *status_out, void *workspace, size_t ws_bytes, void *stream_)
+               float damping, float tol, int max_iter, const float *init_guess, float *traj_out, int *iters_out,
+               float *resid_out, int *status_out, void *workspace, size_t ws_bytes, void *stream_)
 {
     int rc = check_cell(p, mode_flags);
     const int mode = mode_flags & ~DEER_SCAN_F64;
     const bool scan_f64 = (mode_flags & DEER_SCAN_F64) != 0;
     if (rc) return rc;
+    if (!(damping >= 0.0f && damping <= 1.0f)) return fail(DEER_ERR_INVALID, "damping must lie in [0, 1]");
+    if (damping != 0.0f && mode != DEER_MODE_DENSE && mode != DEER_MODE_DIAG)
+        return fail(DEER_ERR_INVALID, "damping applies to the dense and diag modes only");
+    const Linearization lz{mode == DEER_MODE_JACOBI ? kLinZero : mode == DEER_MODE_PICARD ? kLinIdentity : kLinJacobian,
+                           1.0f - damping};
     rc = check_sizes(B, T);
     if (rc) return rc;
     if (max_iter < 0) return fail(DEER_ERR_INVALID, "max_iter must be >= 0");
@@ -437,7 +446,7 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
         if (fused) {
             prof.begin(0);
             r = launch_gru_quasi_step(p->W, p->b2, L.proj, s0, traj_out, L.buf1, L.ctl, L.done, L.iters, L.status,
-                                      L.resid, tol, max_iter, L.res_bits, L.res_tile, B, T, D, zero_start, L.scan,
+                                      L.resid, tol, max_iter, L.res_bits, L.res_tile, B, T, D, zero_start, lz, L.scan,
                                       stream);
             prof.end();
             return r;
@@ -445,10 +454,10 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
         prof.begin(0);
         if (gru)
             r = launch_gru_eval(p->W, p->b2, L.proj, s0, traj_out, L.buf1, sel, L.done, all_done, L.lin, L.bvec,
-                                L.res_bits, B, T, D, p->M, stream);
+                                L.res_bits, B, T, D, p->M, lz, stream);
         else
             r = launch_tanh_eval(p->W, L.proj, s0, traj_out, L.buf1, sel, L.done, all_done, L.lin, L.bvec,
-                                 L.res_bits, B, T, D, mode == DEER_MODE_DENSE, stream);
+                                 L.res_bits, B, T, D, mode == DEER_MODE_DENSE, lz, stream);
         prof.end();
         if (r) return r;
         prof.begin(3);
@@ -457,7 +466,7 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
         prof.end();
         DEER_HIP(hipGetLastError());
         prof.begin(1);
-        if (mode == DEER_MODE_DIAG)
+        if (diag_blocks(mode))
             r = launch_diag_scan(L.lin, L.bvec, s0, traj_out, L.buf1, sel, L.done, all_done, B, T, D, L.scan, stream);
         else
             r = launch_dense_scan(nullptr, L.lin, p->W, L.bvec, s0, traj_out, L.buf1, sel, L.done, all_done, B, T, D,
@@ -515,7 +524,7 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
             hipMemcpyAsync(status_h.data(), L.status, sizeof(int) * B, hipMemcpyDeviceToHost, stream) != hipSuccess)
             rc = fail(DEER_ERR_HIP, "deer_solve: result copy failed");
     }
-    if (rc == DEER_OK && (mode == DEER_MODE_DIAG || fused)) {
+    if (rc == DEER_OK && (diag_blocks(mode) || fused)) {
         if (hipMemcpyAsync(&abort_flag, &static_cast<ScanHeader *>(L.scan)->abort, sizeof(unsigned),
                            hipMemcpyDeviceToHost, stream) != hipSuccess)
             rc = fail(DEER_ERR_HIP, "deer_solve: flag copy failed");

@@ -124,7 +124,8 @@ __global__ __launch_bounds__(kThreads) void gru_eval_mfma_kernel(
     const float *__restrict__ Whh, const float *__restrict__ bhh, const float *__restrict__ pt,
     const float *__restrict__ s0, const float *s_even, const float *s_odd, const int *__restrict__ sel,
     const int *__restrict__ skip, const int *__restrict__ all_done, float *__restrict__ aout,
-    float *__restrict__ bout, unsigned *__restrict__ res_bits, int T, int tiles_per_seq, long long ntiles)
+    float *__restrict__ bout, unsigned *__restrict__ res_bits, int T, int tiles_per_seq, long long ntiles,
+    Linearization lz)
 {
     using G = GruGeom<D>;
     if (all_done && *all_done) return;
@@ -207,8 +208,8 @@ __global__ __launch_bounds__(kThreads) void gru_eval_mfma_kernel(
             const float zg = sigmoid_fast(pc[1][v >> 2][v & 3] + qz);
             const float ng = tanh_fast(pc[2][v >> 2][v & 3] + rg * qn);
             const float f = (1.0f - zg) * ng + zg * h;
-            const float a = zg + (h - ng) * zg * (1.0f - zg) * wz +
-                            (1.0f - zg) * (1.0f - ng * ng) * (rg * wn + rg * (1.0f - rg) * wr * qn);
+            const float a = lin_diag(lz, zg + (h - ng) * zg * (1.0f - zg) * wz +
+                                             (1.0f - zg) * (1.0f - ng * ng) * (rg * wn + rg * (1.0f - rg) * wr * qn));
             const size_t o = (seq + t) * D + c;
             __builtin_nontemporal_store(a, aout + o);
             __builtin_nontemporal_store(f - a * h, bout + o);
@@ -242,7 +243,8 @@ __global__ __launch_bounds__(kThreads, 2) void gru_quasi_step_kernel(
     const float *__restrict__ s0, float *s_even, float *s_odd, SolveControl *ctl, int *done, int *iters,
     int *status, float *resid, float tol, int max_iter, unsigned *res_bits, unsigned *__restrict__ res_tile, int T,
     int tiles_per_seq,
-    int nseq, long long ntiles, int zero_start, ScanHeader *__restrict__ hdr, unsigned long long *__restrict__ desc)
+    int nseq, long long ntiles, int zero_start, Linearization lz, ScanHeader *__restrict__ hdr,
+    unsigned long long *__restrict__ desc)
 {
     using G = GruGeom<D>;
     if (ctl->all_done) return;                   // same value for every workgroup of the launch
@@ -335,8 +337,8 @@ __global__ __launch_bounds__(kThreads, 2) void gru_quasi_step_kernel(
             const float zg = sigmoid_fast(pc[1][v >> 2][v & 3] + qz);
             const float ng = tanh_fast(pc[2][v >> 2][v & 3] + rg * qn);
             const float f = (1.0f - zg) * ng + zg * h;
-            const float a = zg + (h - ng) * zg * (1.0f - zg) * wz +
-                            (1.0f - zg) * (1.0f - ng * ng) * (rg * wn + rg * (1.0f - rg) * wr * qn);
+            const float a = lin_diag(lz, zg + (h - ng) * zg * (1.0f - zg) * wz +
+                                             (1.0f - zg) * (1.0f - ng * ng) * (rg * wn + rg * (1.0f - rg) * wr * qn));
             const bool in = full || t < T;
             la[v] = in ? a : 1.0f;
             lb[v] = in ? f - a * h : 0.0f;
@@ -632,7 +634,7 @@ int capacity_of(K kernel, size_t lds)
 template <int D>
 int launch_gru_mfma(const float *Whh, const float *bhh, const float *p, const float *s0, const float *s_even,
                     const float *s_odd, const int *sel, const int *skip, const int *all_done, float *a, float *bvec,
-                    unsigned *res_bits, int B, int T, hipStream_t stream)
+                    unsigned *res_bits, int B, int T, Linearization lz, hipStream_t stream)
 {
     using G = GruGeom<D>;
     static int cap = 0;
@@ -641,7 +643,7 @@ int launch_gru_mfma(const float *Whh, const float *bhh, const float *p, const fl
     const long long ntiles = static_cast<long long>(B) * tps;
     const unsigned grid = static_cast<unsigned>(std::max<long long>(1, std::min<long long>(ntiles, cap)));
     hipLaunchKernelGGL((gru_eval_mfma_kernel<D>), dim3(grid), dim3(kThreads), 0, stream, Whh, bhh, p, s0, s_even,
-                       s_odd, sel, skip, all_done, a, bvec, res_bits, T, tps, ntiles);
+                       s_odd, sel, skip, all_done, a, bvec, res_bits, T, tps, ntiles, lz);
     DEER_HIP(hipGetLastError());
     return DEER_OK;
 }
@@ -666,8 +668,8 @@ int launch_proj_mfma(const float *x, const float *U, const float *bias, float *p
 template <int D>
 int launch_gru_step(const float *Whh, const float *bhh, const float *pt, const float *s0, float *s_even, float *s_odd,
                     SolveControl *ctl, int *done, int *iters, int *status, float *resid, float tol, int max_iter,
-                    unsigned *res_bits, unsigned *res_tile, int B, int T, bool zero_start, void *state,
-                    hipStream_t stream)
+                    unsigned *res_bits, unsigned *res_tile, int B, int T, bool zero_start, Linearization lz,
+                    void *state, hipStream_t stream)
 {
     using G = GruGeom<D>;
     static int cap = 0;
@@ -679,7 +681,7 @@ int launch_gru_step(const float *Whh, const float *bhh, const float *pt, const f
     auto *desc = reinterpret_cast<unsigned long long *>(static_cast<char *>(state) + sizeof(ScanHeader));
     hipLaunchKernelGGL((gru_quasi_step_kernel<D>), dim3(grid), dim3(kThreads), 0, stream, Whh, bhh, pt, s0, s_even,
                        s_odd, ctl, done, iters, status, resid, tol, max_iter, res_bits, res_tile, T, tps, B, ntiles,
-                       zero_start ? 1 : 0, hdr, desc);
+                       zero_start ? 1 : 0, lz, hdr, desc);
     DEER_HIP(hipGetLastError());
     return DEER_OK;
 }
@@ -690,13 +692,15 @@ bool gru_mfma_supported(int D) { return D == 32 || D == 64; }
 
 int launch_gru_eval_mfma(const float *Whh, const float *bhh, const float *p, const float *s0, const float *s_even,
                          const float *s_odd, const int *sel, const int *skip, const int *all_done, float *a,
-                         float *bvec, unsigned *res_bits, int B, int T, int D, hipStream_t stream)
+                         float *bvec, unsigned *res_bits, int B, int T, int D, Linearization lz, hipStream_t stream)
 {
     if (B == 0 || T == 0) return DEER_OK;
     if (D == 64)
-        return launch_gru_mfma<64>(Whh, bhh, p, s0, s_even, s_odd, sel, skip, all_done, a, bvec, res_bits, B, T, stream);
+        return launch_gru_mfma<64>(Whh, bhh, p, s0, s_even, s_odd, sel, skip, all_done, a, bvec, res_bits, B, T, lz,
+                                   stream);
     if (D == 32)
-        return launch_gru_mfma<32>(Whh, bhh, p, s0, s_even, s_odd, sel, skip, all_done, a, bvec, res_bits, B, T, stream);
+        return launch_gru_mfma<32>(Whh, bhh, p, s0, s_even, s_odd, sel, skip, all_done, a, bvec, res_bits, B, T, lz,
+                                   stream);
     return fail(DEER_ERR_UNSUPPORTED, "GRU matrix-core evaluation needs D = 32 or 64");
 }
 
@@ -736,15 +740,15 @@ size_t gru_step_state_bytes(int B, int T, int D)
 int launch_gru_quasi_step(const float *Whh, const float *bhh, const float *pt, const float *s0, float *s_even,
                           float *s_odd, SolveControl *ctl, int *done, int *iters, int *status, float *resid,
                           float tol, int max_iter, unsigned *res_bits, unsigned *res_tile, int B, int T, int D,
-                          bool zero_start, void *state, hipStream_t stream)
+                          bool zero_start, Linearization lz, void *state, hipStream_t stream)
 {
     if (B == 0 || T == 0) return DEER_OK;
     if (D == 64)
         return launch_gru_step<64>(Whh, bhh, pt, s0, s_even, s_odd, ctl, done, iters, status, resid, tol, max_iter,
-                                   res_bits, res_tile, B, T, zero_start, state, stream);
+                                   res_bits, res_tile, B, T, zero_start, lz, state, stream);
     if (D == 32)
         return launch_gru_step<32>(Whh, bhh, pt, s0, s_even, s_odd, ctl, done, iters, status, resid, tol, max_iter,
-                                   res_bits, res_tile, B, T, zero_start, state, stream);
+                                   res_bits, res_tile, B, T, zero_start, lz, state, stream);
     return fail(DEER_ERR_UNSUPPORTED, "fused GRU step needs D = 32 or 64");
 }
 

@@ -110,14 +110,14 @@ __global__ __launch_bounds__(kThreads) void projection_kernel(const float *__res
 }
 
 // ------------------------------------------------------------- tanh cell
-// f = tanh(W s + p); dense: lin = d = 1 - f^2, b = f - d * (W s)  (A_t = diag(d) W)
-//                    diag:  lin = a = d * W_cc, b = f - a * s_c
+// f = tanh(W s + p); dense: lin = d = shrink (1 - f^2), b = f - d * (W s)  (A_t = diag(d) W)
+//                    other: lin = a = lin_diag((1 - f^2) W_cc), b = f - a * s_c
 template <int DP>
 __global__ __launch_bounds__(kThreads) void tanh_eval_kernel(
     const float *__restrict__ W, const float *__restrict__ p, const float *__restrict__ s0,
     const float *s_even, const float *s_odd, const int *__restrict__ sel, const int *__restrict__ skip,
     const int *__restrict__ all_done, float *__restrict__ lin, float *__restrict__ bout, unsigned *__restrict__ res_bits,
-    int T, int D, int tiles, int dense)
+    int T, int D, int tiles, int dense, Linearization lz)
 {
     if (all_done && *all_done) return;
     const int bseq = blockIdx.x / tiles, tile = blockIdx.x % tiles;
@@ -159,10 +159,11 @@ __global__ __launch_bounds__(kThreads) void tanh_eval_kernel(
         const float f = tanhf(h);
         const float d = 1.0f - f * f;
         if (dense) {
-            lin[o] = d;
-            bout[o] = f - d * ws;
+            const float dd = lz.shrink * d;
+            lin[o] = dd;
+            bout[o] = f - dd * ws;
         } else {
-            const float a = d * wcc;
+            const float a = lin_diag(lz, d * wcc);
             lin[o] = a;
             bout[o] = f - a * srow[r][c];
         }
@@ -181,7 +182,7 @@ __global__ __launch_bounds__(kThreads) void gru_eval_kernel(
     const float *__restrict__ Whh, const float *__restrict__ bhh, const float *__restrict__ p,
     const float *__restrict__ s0, const float *s_even, const float *s_odd, const int *__restrict__ sel,
     const int *__restrict__ skip, const int *__restrict__ all_done, float *__restrict__ aout,
-    float *__restrict__ bout, unsigned *__restrict__ res_bits, int T, int D, int tiles)
+    float *__restrict__ bout, unsigned *__restrict__ res_bits, int T, int D, int tiles, Linearization lz)
 {
     if (all_done && *all_done) return;
     const int bseq = blockIdx.x / tiles, tile = blockIdx.x % tiles;
@@ -233,8 +234,8 @@ __global__ __launch_bounds__(kThreads) void gru_eval_kernel(
         const float ng = tanhf(p[pb + 2 * D + c] + rg * qn);
         const float h = srow[r][c];
         const float f = (1.0f - zg) * ng + zg * h;
-        const float a = zg + (h - ng) * zg * (1.0f - zg) * wz +
-                        (1.0f - zg) * (1.0f - ng * ng) * (rg * wn + rg * (1.0f - rg) * wr * qn);
+        const float a = lin_diag(lz, zg + (h - ng) * zg * (1.0f - zg) * wz +
+                                         (1.0f - zg) * (1.0f - ng * ng) * (rg * wn + rg * (1.0f - rg) * wr * qn));
         const size_t o = (seq + t) * D + c;
         aout[o] = a;
         bout[o] = f - a * h;
@@ -348,12 +349,12 @@ int launch_projection(const float *x, const float *U, const float *bias, float *
 #define DEER_TANH_CASE(DPV)                                                                                     \
     case DPV:                                                                                                   \
         hipLaunchKernelGGL((tanh_eval_kernel<DPV>), dim3(blocks), dim3(kThreads), 0, stream, W, p, s0, s_even,  \
-                           s_odd, sel, skip, all_done, lin, bvec, res_bits, T, D, tiles, dense);                \
+                           s_odd, sel, skip, all_done, lin, bvec, res_bits, T, D, tiles, dense, lz);            \
         break;
 
 int launch_tanh_eval(const float *W, const float *p, const float *s0, const float *s_even, const float *s_odd,
                      const int *sel, const int *skip, const int *all_done, float *lin, float *bvec, unsigned *res_bits,
-                     int B, int T, int D, int dense, hipStream_t stream)
+                     int B, int T, int D, int dense, Linearization lz, hipStream_t stream)
 {
     int tiles;
     const unsigned blocks = eval_blocks(B, T, tiles);
@@ -372,16 +373,16 @@ int launch_tanh_eval(const float *W, const float *p, const float *s0, const floa
 #define DEER_GRU_CASE(DPV)                                                                                      \
     case DPV:                                                                                                   \
         hipLaunchKernelGGL((gru_eval_kernel<DPV>), dim3(blocks), dim3(kThreads), 0, stream, Whh, bhh, p, s0,    \
-                           s_even, s_odd, sel, skip, all_done, a, bvec, res_bits, T, D, tiles);                 \
+                           s_even, s_odd, sel, skip, all_done, a, bvec, res_bits, T, D, tiles, lz);             \
         break;
 
 int launch_gru_eval(const float *Whh, const float *bhh, const float *p, const float *s0, const float *s_even,
                     const float *s_odd, const int *sel, const int *skip, const int *all_done, float *a, float *bvec,
-                    unsigned *res_bits, int B, int T, int D, int M, hipStream_t stream)
+                    unsigned *res_bits, int B, int T, int D, int M, Linearization lz, hipStream_t stream)
 {
     if (gru_fast_path(D, M))
         return launch_gru_eval_mfma(Whh, bhh, p, s0, s_even, s_odd, sel, skip, all_done, a, bvec, res_bits, B, T, D,
-                                    stream);
+                                    lz, stream);
     int tiles;
     const unsigned blocks = eval_blocks(B, T, tiles);
     if (blocks == 0) return DEER_OK;

@@ -164,30 +164,45 @@ int launch_projection(const float *x, const float *U, const float *bias, float *
                       int O, bool tiled, hipStream_t stream);
 size_t projection_floats(int B, int T, int O);
 
+// How an iteration linearises f: the Jacobian (or its diagonal) shrunk by
+// `shrink` = 1 - k, the zero block (Jacobi) or the identity (Picard).
+enum LinKind : int { kLinJacobian = 0, kLinZero = 1, kLinIdentity = 2 };
+struct Linearization {
+    int kind;
+    float shrink;
+};
+
+// The diagonal block entry a mode uses, given the Jacobian's diagonal entry.
+__device__ __forceinline__ float lin_diag(Linearization l, float jdiag)
+{
+    return l.kind == kLinJacobian ? l.shrink * jdiag : (l.kind == kLinZero ? 0.0f : 1.0f);
+}
+
 // tanh cell: f_t = tanh(W s_{t-1} + p_t).  Dense mode writes the factored
-// leaf d_t = 1 - f_t^2 into `lin` and b_t = f_t - d_t * (W s_{t-1}); diag mode
-// writes a_t = d_t * diag(W) into `lin` and b_t = f_t - a_t * s_{t-1}.
+// leaf d_t = shrink (1 - f_t^2) into `lin` and b_t = f_t - d_t * (W s_{t-1});
+// the other modes write a_t = lin_diag(d_t * diag(W)) into `lin` and
+// b_t = f_t - a_t * s_{t-1}.
 // res_bits[b] receives atomic max of |s_t - f_t| (float bits).
 int launch_tanh_eval(const float *W, const float *p, const float *s0, const float *s_even,
                      const float *s_odd, const int *sel, const int *skip, const int *all_done,
                      float *lin, float *bvec, unsigned *res_bits, int B, int T, int D, int dense,
-                     hipStream_t stream);
+                     Linearization lz, hipStream_t stream);
 
-// GRU cell, diagonal Jacobian: writes a_t = diag(d f / d s) and
+// GRU cell, diagonal blocks: writes a_t = lin_diag(diag(d f / d s)) and
 // b_t = f_t - a_t * s_{t-1}.  With gru_fast_path(D, M) the projection is
 // tiled and the evaluation runs on the matrix cores.
 bool gru_fast_path(int D, int M);
 int launch_gru_eval(const float *Whh, const float *bhh, const float *p, const float *s0,
                     const float *s_even, const float *s_odd, const int *sel, const int *skip,
                     const int *all_done, float *a, float *bvec, unsigned *res_bits, int B, int T,
-                    int D, int M, hipStream_t stream);
+                    int D, int M, Linearization lz, hipStream_t stream);
 
 // Matrix-core versions (cell_mfma.hip) for the supported sizes.
 bool gru_mfma_supported(int D);
 int launch_gru_eval_mfma(const float *Whh, const float *bhh, const float *p, const float *s0,
                          const float *s_even, const float *s_odd, const int *sel, const int *skip,
                          const int *all_done, float *a, float *bvec, unsigned *res_bits, int B, int T,
-                         int D, hipStream_t stream);
+                         int D, Linearization lz, hipStream_t stream);
 bool proj_mfma_supported(int M, int O);
 size_t proj_tiled_floats(int B, int T, int O);
 int launch_projection_mfma(const float *x, const float *U, const float *bias, float *p, int B, int T,
@@ -206,7 +221,7 @@ size_t gru_step_state_bytes(int B, int T, int D);
 int launch_gru_quasi_step(const float *Whh, const float *bhh, const float *pt, const float *s0, float *s_even,
                           float *s_odd, SolveControl *ctl, int *done, int *iters, int *status, float *resid,
                           float tol, int max_iter, unsigned *res_bits, unsigned *res_tile, int B, int T, int D,
-                          bool zero_start, void *state, hipStream_t stream);
+                          bool zero_start, Linearization lz, void *state, hipStream_t stream);
 
 int launch_rollout(const deer_cell_params_t *p, const float *x, const float *s0, int B, int T,
                    float *traj, hipStream_t stream);

@@ -18,9 +18,11 @@ LIB_PATH = os.path.join(_HERE, "libdeer.so")
 
 DEER_MODE_DENSE = 0
 DEER_MODE_DIAG = 1
+DEER_MODE_JACOBI = 2
+DEER_MODE_PICARD = 3
 DEER_CELL_TANH = 0
 DEER_CELL_GRU = 1
-MODES = {"dense": DEER_MODE_DENSE, "diag": DEER_MODE_DIAG}
+MODES = {"dense": DEER_MODE_DENSE, "diag": DEER_MODE_DIAG, "jacobi": DEER_MODE_JACOBI, "picard": DEER_MODE_PICARD}
 CELLS = {"tanh": DEER_CELL_TANH, "gru": DEER_CELL_GRU}
 
 DEER_SCAN_F64 = 16   # or-ed into the dense mode: the linear solve accumulates in double
@@ -64,8 +66,8 @@ def load_library():
     sig = {
         "deer_workspace_size": ([ctypes.POINTER(CellParams), c_int, c_int, c_int, ctypes.POINTER(c_size)], c_int),
         "deer_workspace_init": ([vp, c_size, vp], c_int),
-        "deer_solve": ([ctypes.POINTER(CellParams), vp, vp, c_int, c_int, c_int, fp, c_int, vp, vp, vp, vp, vp,
-                        vp, c_size, vp], c_int),
+        "deer_solve": ([ctypes.POINTER(CellParams), vp, vp, c_int, c_int, c_int, fp, fp, c_int, vp, vp, vp, vp,
+                        vp, vp, c_size, vp], c_int),
         "linear_scan_workspace_size": ([c_int, c_int, c_int, c_int, ctypes.POINTER(c_size)], c_int),
         "linear_scan_diag": ([vp, vp, vp, vp, c_int, c_int, c_int, vp, c_size, vp], c_int),
         "linear_scan_dense": ([vp, vp, vp, vp, c_int, c_int, c_int, vp, c_size, vp], c_int),
@@ -183,13 +185,16 @@ def deer_workspace_init(ws, stream=None) -> None:
 # ---------------------------------------------------------------- solvers
 
 def deer_solve(cell: Cell, x, s0=None, mode: str = "dense", tol: float = 1e-6, max_iter: int = 100,
-               init_guess=None, out=None, workspace=None, stream=None, scan_f64: bool = False):
-    """Parallel Newton / quasi-Newton solve; returns ``(traj, iters, resid, status, rc)``.
+               init_guess=None, out=None, workspace=None, stream=None, scan_f64: bool = False,
+               damping: float = 0.0):
+    """Parallel fixed-point solve; returns ``(traj, iters, resid, status, rc)``.
 
-    ``traj`` is a ``[B,T,D]`` CUDA tensor; ``iters``, ``status`` are numpy int32
-    ``[B]``, ``resid`` numpy float32 ``[B]``; ``rc`` is DEER_OK or
-    DEER_NOT_CONVERGED.  ``scan_f64`` (dense mode) accumulates the linear solve
-    in double precision.
+    ``mode``: ``"dense"`` (Newton), ``"diag"`` (diagonal quasi-Newton),
+    ``"jacobi"`` or ``"picard"``; ``damping`` k shrinks the dense / diag blocks
+    to ``(1 - k) J``.  ``traj`` is a ``[B,T,D]`` CUDA tensor; ``iters``,
+    ``status`` are numpy int32 ``[B]``, ``resid`` numpy float32 ``[B]``; ``rc``
+    is DEER_OK or DEER_NOT_CONVERGED.  ``scan_f64`` (dense mode) accumulates
+    the linear solve in double precision.
     """
     import numpy as np
     import torch
@@ -207,7 +212,7 @@ def deer_solve(cell: Cell, x, s0=None, mode: str = "dense", tol: float = 1e-6, m
     resid = np.zeros(B, np.float32)
     status = np.zeros(B, np.int32)
     rc = lib.deer_solve(ctypes.byref(p), _dev(x, "x", shape=(B, T, M)), _dev(s0, "s0", shape=(B, D)), B, T,
-                        _mode(mode, scan_f64), ctypes.c_float(tol), int(max_iter),
+                        _mode(mode, scan_f64), ctypes.c_float(damping), ctypes.c_float(tol), int(max_iter),
                         _dev(init_guess, "init_guess", shape=(B, T, D)), _dev(out, "out", shape=(B, T, D)),
                         iters.ctypes.data_as(ctypes.c_void_p), resid.ctypes.data_as(ctypes.c_void_p),
                         status.ctypes.data_as(ctypes.c_void_p),

@@ -38,7 +38,21 @@
 extern "C" {
 #endif
 
-enum deer_mode { DEER_MODE_DENSE = 0, DEER_MODE_DIAG = 1 };
+/*
+ * Linearisation used by each iteration (the first page's thread: every method
+ * linearises the dynamics, then evaluates the linear recurrence in parallel;
+ * "Parallel Broyden Methods", section 2 and the Picard paragraph of its
+ * diffusion experiment):
+ *   DENSE   A_t = (1 - k) J_t, the full Jacobian   (Newton / DEER)
+ *   DIAG    A_t = (1 - k) diag(J_t)                (diagonal quasi-Newton)
+ *   JACOBI  A_t = 0: the next iterate is f of the current one, shifted by one step
+ *   PICARD  A_t = I: the next iterate accumulates the one-step corrections
+ * with offsets b_t = f_t - A_t s_{t-1}, so every mode keeps the trajectory as
+ * its fixed point and recovers it exactly within T iterations.  k is the
+ * damping argument of deer_solve (scale-ELK: "Parallel Broyden Methods",
+ * appendix E.4).
+ */
+enum deer_mode { DEER_MODE_DENSE = 0, DEER_MODE_DIAG = 1, DEER_MODE_JACOBI = 2, DEER_MODE_PICARD = 3 };
 
 /*
  * Flag or-ed into the mode of deer_solve (dense mode only): the linear solve
@@ -84,8 +98,8 @@ enum deer_seq_status {
  *            f = (1 - z) * n + z * s
  *          (the GRU is only cited on the pages; these are its textbook
  *          equations).
- * Supported: 1 <= D <= 64, 1 <= M <= 1024.  tanh in dense or diag mode, GRU in
- * diag mode.
+ * Supported: 1 <= D <= 64, 1 <= M <= 1024.  tanh in every mode, GRU in the
+ * diag, Jacobi and Picard modes.
  */
 typedef struct {
     int cell;        /* enum deer_cell */
@@ -112,14 +126,18 @@ int deer_workspace_size(const deer_cell_params_t *p, int B, int T, int mode, siz
 int deer_workspace_init(void *workspace, size_t ws_bytes, void *stream);
 
 /*
- * Solve for the trajectory by parallel Newton (mode DEER_MODE_DENSE) or
- * diagonal quasi-Newton (DEER_MODE_DIAG) iterations ("Parallel Broyden
- * Methods", section 2: exact parallel Newton and diagonal quasi-Newton;
- * finite-step recovery, Theorem 1 of section 3.2).
+ * Solve for the trajectory by parallel Newton (mode DEER_MODE_DENSE), diagonal
+ * quasi-Newton (DEER_MODE_DIAG), Jacobi or Picard iterations ("Parallel
+ * Broyden Methods", section 2: exact parallel Newton and diagonal
+ * quasi-Newton; finite-step recovery, Theorem 1 of section 3.2).
  *
  *   p           cell parameters (host struct holding device pointers)
  *   x           device [B,T,M] inputs
  *   s0          device [B,D] initial states, or NULL for zeros
+ *   mode        enum deer_mode, optionally or-ed with DEER_SCAN_F64 (dense only)
+ *   damping     k in [0, 1]: the blocks become (1 - k) J_t (dense) or
+ *               (1 - k) diag(J_t) (diag); must be 0 for Jacobi and Picard.
+ *               k = 0 is the undamped method, k = 1 turns it into Jacobi.
  *   tol         stop when max_{t,d} |s_t - f(s_{t-1}, x_t)| <= tol for a
  *               sequence (absolute L-infinity residual, tested on each iterate
  *               before it is refined; NaN never passes)
@@ -139,7 +157,7 @@ int deer_workspace_init(void *workspace, size_t ws_bytes, void *stream);
  * returns after the outputs are complete.
  */
 int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int B, int T,
-               int mode, float tol, int max_iter, const float *init_guess, float *traj_out,
+               int mode, float damping, float tol, int max_iter, const float *init_guess, float *traj_out,
                int *iters_out, float *resid_out, int *status_out, void *workspace, size_t ws_bytes,
                void *stream);
 

@@ -66,6 +66,12 @@ def test_workspace_size_checks(deer):
     gru = _params(deer, cell="gru")
     assert lib.deer_workspace_size(ctypes.byref(gru), 4, 100, deer.DEER_MODE_DENSE, ctypes.byref(n)) == -2
     assert lib.deer_workspace_size(ctypes.byref(gru), 4, 100, deer.DEER_MODE_DIAG, ctypes.byref(n)) == 0
+    diag = n.value
+    for mode in (deer.DEER_MODE_JACOBI, deer.DEER_MODE_PICARD):      # diagonal-block modes share diag's layout
+        assert lib.deer_workspace_size(ctypes.byref(gru), 4, 100, mode, ctypes.byref(n)) == 0 and n.value == diag
+        assert lib.deer_workspace_size(ctypes.byref(p), 4, 100, mode, ctypes.byref(n)) == 0
+    assert lib.deer_workspace_size(ctypes.byref(p), 4, 100, deer.DEER_MODE_JACOBI | deer.DEER_SCAN_F64,
+                                   ctypes.byref(n)) == -2
     assert lib.deer_workspace_size(ctypes.byref(p), -1, 100, 0, ctypes.byref(n)) == -1
     assert lib.deer_workspace_size(ctypes.byref(p), 4, 100, 7, ctypes.byref(n)) == -1
     assert lib.deer_workspace_size(None, 4, 100, 0, ctypes.byref(n)) == -1
@@ -106,20 +112,25 @@ def test_solve_argument_checks(deer):
     p = _params(deer)
     it = (ctypes.c_int * 4)()
     fake = ctypes.c_void_p(0x1000)
-    args = lambda B, T, mode, tol, mi, ws, wsb: (ctypes.byref(p), fake, None, B, T, mode, ctypes.c_float(tol), mi,  # noqa: E731
-                                                 None, ctypes.c_void_p(0x2000), it, None, None, ws, wsb, None)
+    args = lambda B, T, mode, tol, mi, ws, wsb, k=0.0: (ctypes.byref(p), fake, None, B, T, mode,  # noqa: E731
+                                                        ctypes.c_float(k), ctypes.c_float(tol), mi, None,
+                                                        ctypes.c_void_p(0x2000), it, None, None, ws, wsb, None)
     assert lib.deer_solve(*args(4, 10, 0, 1e-6, -1, fake, 1 << 30)) == -1          # max_iter < 0
     assert lib.deer_solve(*args(4, 10, 0, float("nan"), 5, fake, 1 << 30)) == -1   # tol NaN
     assert lib.deer_solve(*args(4, 10, 0, 1e-6, 5, None, 0)) == -3                 # no workspace
     assert lib.deer_solve(*args(4, 10, 0, 1e-6, 5, ctypes.c_void_p(0x1010), 1 << 30)) == -3  # misaligned
     assert lib.deer_solve(*args(0, 10, 0, 1e-6, 5, None, 0)) == 0                  # empty batch
+    for mode, k in ((0, -0.5), (1, 1.5), (0, float("nan")), (2, 0.5), (3, 0.1)):   # damping range, and
+        assert lib.deer_solve(*args(4, 10, mode, 1e-6, 5, fake, 1 << 30, k)) == -1  # only dense/diag take it
+        assert b"damping" in lib.deer_last_error()
+    assert lib.deer_solve(*args(4, 10, 4, 1e-6, 5, fake, 1 << 30)) == -1          # unknown mode
     # empty trajectories: residual 0 passes any tol >= 0 after zero iterations
     st = (ctypes.c_int * 4)()
-    assert lib.deer_solve(ctypes.byref(p), None, None, 4, 0, 0, ctypes.c_float(1e-6), 5, None, None, it, None, st,
-                          None, 0, None) == 0
+    assert lib.deer_solve(ctypes.byref(p), None, None, 4, 0, 0, ctypes.c_float(0.0), ctypes.c_float(1e-6), 5, None,
+                          None, it, None, st, None, 0, None) == 0
     assert list(it) == [0, 0, 0, 0] and list(st) == [0, 0, 0, 0]
-    assert lib.deer_solve(ctypes.byref(p), None, None, 4, 0, 0, ctypes.c_float(-1.0), 5, None, None, it, None, st,
-                          None, 0, None) == 1
+    assert lib.deer_solve(ctypes.byref(p), None, None, 4, 0, 0, ctypes.c_float(0.0), ctypes.c_float(-1.0), 5, None,
+                          None, it, None, st, None, 0, None) == 1
     assert list(it) == [5, 5, 5, 5] and list(st) == [1, 1, 1, 1]
 
 

@@ -23,20 +23,20 @@ TOL = 1e-4
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "oracle_full_workloads.json")
 
 
-def _run(orc, p, mode, tol, max_iter, s0=True, check_iters=True, init=None, scan_f64=False):
+def _run(orc, p, mode, tol, max_iter, s0=True, check_iters=True, init=None, scan_f64=False, damping=0.0):
     dev = device()
     cell = deer.cell_from_problem(p, dev)
     x = torch.from_numpy(p["x"]).to(dev)
     s0_t = torch.from_numpy(p["s0"]).to(dev) if s0 else None
     init_t = None if init is None else torch.from_numpy(init).to(dev)
     traj, iters, resid, status, rc = deer.deer_solve(cell, x, s0_t, mode=mode, tol=tol, max_iter=max_iter,
-                                                     init_guess=init_t, scan_f64=scan_f64)
+                                                     init_guess=init_t, scan_f64=scan_f64, damping=damping)
     torch.cuda.synchronize()
     oc = orc.Cell.from_problem(p)
     s0n = p["s0"] if s0 else None
     ref = orc.rollout(oc, p["x"], s0n)
     _, oit, ores, ost = orc.newton(oc, p["x"], s0n, mode=mode, tol=tol, max_iter=max_iter, precision="f32",
-                                   init=init)
+                                   init=init, damping=damping)
     got = traj.cpu().numpy()
     if check_iters:
         assert np.all(np.abs(iters - oit) <= 1), (iters, oit)
@@ -75,6 +75,43 @@ def test_gru_solve_matches_oracle(orc, B, T, D, M):
     got, ref, iters, resid, status, rc, oit = _run(orc, p, "diag", 1e-5, 200)
     assert rc == deer.DEER_OK and np.all(status == 0)
     assert np.all(rel_linf(got, ref) <= TOL)
+
+
+@pytest.mark.parametrize("cell,mode,damping,D,T", [
+    ("tanh", "jacobi", 0.0, 8, 300), ("tanh", "picard", 0.0, 4, 60), ("tanh", "dense", 0.3, 16, 500),
+    ("tanh", "diag", 0.5, 32, 400), ("tanh", "dense", 1.0, 8, 200), ("tanh", "picard", 0.0, 32, 40),
+    ("gru", "jacobi", 0.0, 64, 2000), ("gru", "picard", 0.0, 64, 100), ("gru", "diag", 0.3, 64, 3000),
+    ("gru", "jacobi", 0.0, 16, 500), ("gru", "diag", 0.4, 32, 1000), ("gru", "picard", 0.0, 8, 50)])
+def test_linearisations_match_oracle(orc, cell, mode, damping, D, T):
+    """Jacobi (A_t = 0), Picard (A_t = I) and damped Newton / quasi-Newton
+    (A_t = (1 - k) J_t): iteration counts within one of the oracle's float32 run
+    of the same linearisation, trajectory within 1e-4 of the float64 rollout."""
+    B = 2
+    if cell == "tanh":
+        p = I.tanh_problem(800 + T + D, B, T, D, D, gain=0.7, bias_std=0.3, s0_std=0.5)
+    else:
+        p = I.gru_problem(900 + T + D, B, T, D, D, bias_std=0.3, s0_std=0.5)
+    log(f"deer_solve {cell} {mode} damping={damping} B={B} T={T} D={D}")
+    got, ref, iters, resid, status, rc, oit = _run(orc, p, mode, 1e-5, T + 1, damping=damping)
+    assert rc == deer.DEER_OK and np.all(status == 0), (iters, status)
+    assert np.all(rel_linf(got, ref) <= TOL)
+    assert np.all(resid <= 1e-5)
+
+
+def test_damping_one_is_jacobi(orc):
+    """k = 1 shrinks the blocks to zero: the damped quasi-Newton solve takes
+    Jacobi's steps (same counts, same trajectory)."""
+    p = I.gru_problem(951, 2, 1500, 64, 64, bias_std=0.3, s0_std=0.5)
+    dev = device()
+    cell = deer.cell_from_problem(p, dev)
+    x = torch.from_numpy(p["x"]).to(dev)
+    s0 = torch.from_numpy(p["s0"]).to(dev)
+    log("deer_solve gru diag damping=1 vs jacobi")
+    t1, i1, _, st1, _ = deer.deer_solve(cell, x, s0, mode="diag", tol=1e-5, max_iter=400, damping=1.0)
+    t1 = t1.cpu().numpy()
+    t2, i2, _, st2, _ = deer.deer_solve(cell, x, s0, mode="jacobi", tol=1e-5, max_iter=400)
+    assert list(i1) == list(i2) and list(st1) == list(st2) == [0, 0]
+    assert np.array_equal(t1, t2.cpu().numpy())
 
 
 def test_solve_edge_cases(orc):

@@ -13,7 +13,8 @@ workload as a reported baseline, the standalone diagonal linear scan
 (B=32, T=131072, D=256) in GB/s against the HBM peak, the dense-Jacobian DEER
 solve of the tanh RNN (B=64, T=16384, D=32) with its chunk-compose rate on the
 matrix cores, and the gain sweep of the D=16 tanh RNN (B=32, T=4096) against
-the sequential GPU rollout.
+the sequential GPU rollout, and the Jacobi / Picard / damped linearisations
+of the same solver against it.
 """
 import argparse
 import json
@@ -39,9 +40,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-scan", action="store_true", help="skip the standalone scan measurement")
     ap.add_argument("--no-dense", action="store_true",
-                    help="skip the dense-DEER and gain-sweep measurements")
+                    help="skip the dense-DEER, gain-sweep and linearisation measurements")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work for the baseline sample")
-    ap.add_argument("--only", choices=("dense", "sweep", "scan"), default=None,
+    ap.add_argument("--only", choices=("dense", "sweep", "scan", "lin"), default=None,
                     help="run one secondary measurement alone and print its JSON (for profiling)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run a plain 1 GiB device copy (the reference kernel for HBM counter scaling)")
@@ -268,6 +269,52 @@ def gain_sweep(args, dev):
             "crossover_gain": min(slower) if slower else None}
 
 
+def linearizations(args, dev):
+    """The same solver with other linearisations of f: iterations, time per solve
+    and the ratio to the sequential GPU rollout.  On the contractive tanh
+    workload (gain 0.9): Newton, damped Newton (k = 0.5), diagonal quasi-Newton,
+    Jacobi (A_t = 0) and Picard (A_t = I, which needs up to T iterations on
+    contractive dynamics).  On the GRU workload: quasi-Newton, damped
+    quasi-Newton (k = 0.3) and Jacobi."""
+    import torch
+    from evaluation_nonlinear_rnns_amd import deer, inputs as I
+
+    stream = torch.cuda.current_stream()
+    out = {}
+    cases = (("tanh_d16_t4096_sweep", 0.9, (("newton", "dense", 0.0), ("newton_damped_0.5", "dense", 0.5),
+                                             ("quasi_newton", "diag", 0.0), ("jacobi", "jacobi", 0.0),
+                                             ("picard", "picard", 0.0))),
+             ("gru_d64_t65536", None, (("quasi_newton", "diag", 0.0), ("quasi_newton_damped_0.3", "diag", 0.3),
+                                       ("jacobi", "jacobi", 0.0))))
+    for name, gain, runs in cases:
+        w = I.WORKLOADS[name]
+        p = I.workload_problem(name, gain=gain) if gain is not None else I.workload_problem(name)
+        cell = deer.cell_from_problem(p, dev)
+        x = torch.from_numpy(p["x"]).to(dev)
+        del p
+        traj = torch.empty((w.B, w.T, w.D), dtype=torch.float32, device=dev)
+        seq = torch.empty_like(traj)
+        ms_seq, _, _ = _time_solves(lambda: deer.deer_rollout(cell, x, None, out=seq, stream=stream), 2, stream)
+        rows = {}
+        for label, mode, k in runs:
+            ws = deer.new_workspace(deer.deer_workspace_size(cell, w.B, w.T, mode), device=dev)
+            cap = w.T + 1 if mode == "picard" else w.max_iter
+
+            def step():
+                return deer.deer_solve(cell, x, None, mode=mode, tol=w.tol, max_iter=cap, out=traj, workspace=ws,
+                                       stream=stream, damping=k)
+
+            ms, _, res = _time_solves(step, 2, stream)
+            _, iters, _, status, rc = res
+            rows[label] = {"mode": mode, "damping": k, "rc": int(rc), "iterations_max": int(iters.max()),
+                           "ms_per_solve": round(ms, 3), "speedup_vs_rollout": round(ms_seq / ms, 3)}
+            del ws
+        out[name] = {"gain": gain, "B": w.B, "T": w.T, "D": w.D, "tol": w.tol, "rollout_ms": round(ms_seq, 3),
+                     "runs": rows}
+        del traj, seq, x
+    return out
+
+
 def cpu_baseline(args, w, p):
     """The oracle's float32 sequential rollout of the same workload on the host cores."""
     from oracle import oracle as O
@@ -313,7 +360,7 @@ def main():
         del src, dst
 
     if args.only:
-        fn = {"dense": dense_solve, "sweep": gain_sweep, "scan": scan_bandwidth}[args.only]
+        fn = {"dense": dense_solve, "sweep": gain_sweep, "scan": scan_bandwidth, "lin": linearizations}[args.only]
         print(json.dumps({args.only: fn(args, dev)}), flush=True)
         return
 
@@ -346,6 +393,7 @@ def main():
     if not args.no_dense:
         line["dense_deer"] = dense_solve(args, dev)
         line["gain_sweep"] = gain_sweep(args, dev)
+        line["linearizations"] = linearizations(args, dev)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(args, w, p)
     print(json.dumps(line), flush=True)

@@ -229,11 +229,12 @@ __global__ __launch_bounds__(kThreads) void gru_eval_mfma_kernel(
 // later map on the left ("Parallel Broyden Methods", appendix C.2), at four
 // levels: the 4 consecutive positions a lane holds, the 8 position groups of
 // a 32-position sub-tile (exchanged between the lane pair l, l ^ 32), the
-// sub-tiles of the workgroup's tile (LDS), and the tiles of a sequence
-// (decoupled look-back with self-validating 64-bit descriptors, as in the
-// standalone diagonal scan).  Tiles are taken in the strided order blockIdx.x,
-// blockIdx.x + G, ...; with the whole persistent grid resident the smallest
-// waiting tile's predecessor is always in progress.
+// sub-tiles of the workgroup's tile (LDS), and the tiles of a sequence (the
+// deterministic decoupled look-back of the standalone diagonal scan, with
+// self-validating 64-bit descriptors).  Tiles are taken in the
+// strided order blockIdx.x, blockIdx.x + G, ...; with the whole persistent grid
+// resident the smallest waiting tile's predecessors are always done or in
+// progress.
 //
 // The residual of the iterate is reduced per tile into res_tile[tile] (plain
 // stores; the convergence test takes the max over a sequence's tiles).
@@ -391,6 +392,7 @@ __global__ __launch_bounds__(kThreads, 2) void gru_quasi_step_kernel(
                 TB = shA[k][cc] * TB + shB[k][cc];
                 TA = shA[k][cc] * TA;
             }
+            const unsigned long long *base = desc + static_cast<size_t>(bseq) * tiles_per_seq * 3 * D;
             unsigned long long *mine = desc + (static_cast<size_t>(bseq) * tiles_per_seq + tt) * 3 * D;
             float carry;
             if (tt == 0) {
@@ -398,53 +400,10 @@ __global__ __launch_bounds__(kThreads, 2) void gru_quasi_step_kernel(
             } else {
                 store_desc(mine + cc, pack_desc(TA, tag_agg));
                 store_desc(mine + D + cc, pack_desc(TB, tag_agg));
-                // walk back in windows of kWin predecessors whose descriptors are read together
-                float kA = 1.0f, kB = 0.0f;      // maps s_end(j) to s_end(tt - 1)
-                int j = tt - 1;
-                unsigned spins = 0;
-                bool found = false;
-                while (!found) {
-                    unsigned long long wi[kWin], wa[kWin], wb[kWin];
-#pragma unroll
-                    for (int u = 0; u < kWin; ++u) {
-                        const int jj = max(j - u, 0);
-                        const unsigned long long *pj = desc + (static_cast<size_t>(bseq) * tiles_per_seq + jj) * 3 * D;
-                        wi[u] = load_desc(pj + 2 * D + cc);
-                        wa[u] = load_desc(pj + cc);
-                        wb[u] = load_desc(pj + D + cc);
-                    }
-                    bool stalled = false;
-#pragma unroll
-                    for (int u = 0; u < kWin; ++u) {
-                        if (found || stalled || j - u < 0) continue;
-                        if (desc_tag(wi[u]) == tag_inc) {
-                            carry = kA * desc_val(wi[u]) + kB;
-                            found = true;
-                        } else if (desc_tag(wa[u]) == tag_agg && desc_tag(wb[u]) == tag_agg) {
-                            kB = kA * desc_val(wb[u]) + kB;
-                            kA = kA * desc_val(wa[u]);
-                        } else {
-                            stalled = true;
-                            j -= u;              // resume at the first tile not yet published
-                        }
-                    }
-                    if (found) break;
-                    if (!stalled) {
-                        j -= kWin;
-                        continue;
-                    }
-                    ++spins;
-                    if (spins > kDescSpinLimit ||
-                        ((spins & 1023u) == 0u &&
-                         __hip_atomic_load(&hdr->abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
-                        __hip_atomic_store(&hdr->abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        carry = __builtin_nanf("");
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
-                }
+                carry = chained_carry<kWin>(base, 3 * D, cc, D + cc, 2 * D + cc, tt, tag_agg, tag_inc, &hdr->abort,
+                                            kDescSpinLimit);
             }
-            store_desc(mine + 2 * D + cc, pack_desc(TA * carry + TB, tag_inc));
+            store_desc(mine + 2 * D + cc, pack_desc(__builtin_fmaf(TA, carry, TB), tag_inc));
             shC[cc] = carry;
         }
         __syncthreads();

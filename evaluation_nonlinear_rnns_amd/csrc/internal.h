@@ -117,6 +117,94 @@ struct ScanHeader {
 };
 static_assert(sizeof(ScanHeader) == 256, "header is one alignment unit");
 
+// Deterministic look-back of the single-pass scans.  A chain of tiles (one
+// sequence's tiles of the same channels) publishes, per channel, each tile's
+// aggregate pair (A, B) and its inclusive prefix (the state after its last
+// step), always computed as the left-to-right chain
+//     inc_t = fma(A_t, inc_{t-1}, B_t),   inc_0 = fma(A_0, s_0, B_0).
+// A tile walks back, WIN descriptors per round trip, to the nearest earlier
+// tile k whose inclusive prefix is published (every tile in between having
+// published its aggregate), then applies the aggregates k+1 .. t-1 forward with
+// the same fused multiply-adds.  That reproduces the chain's value bit for bit
+// whichever k the timing delivered, so a scan of the same input gives the same
+// bits every time (an iteration that amplifies perturbations, like Picard's,
+// depends on that to keep its exact prefix exact) -- at the cost of the
+// forward pass over (t-1-k) aggregates, which are L2-resident.  A tile waits
+// only on tiles with smaller indices.  Descriptor words are `value | tag << 32`;
+// the wait is bounded by spin_limit, after which the abort flag is raised and
+// NaN returned.
+__device__ __forceinline__ unsigned long long scan_word_load(const unsigned long long *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float scan_word_val(unsigned long long w) { return __uint_as_float(static_cast<unsigned>(w)); }
+
+template <int WIN>
+__device__ inline float chained_carry(const unsigned long long *chain, size_t words_per_tile, int oa, int ob, int oi,
+                                      int t, unsigned tag_agg, unsigned tag_inc, unsigned *abort_flag,
+                                      unsigned spin_limit)
+{
+    // 1. the nearest earlier inclusive prefix, WIN tiles per round trip
+    int j = t - 1, k = -1, uk = 0;
+    float x = 0.0f;
+    unsigned long long wa[WIN], wb[WIN];
+    unsigned spins = 0;
+    while (true) {
+        unsigned long long wi[WIN];
+#pragma unroll
+        for (int u = 0; u < WIN; ++u) {
+            const size_t jj = static_cast<size_t>(max(j - u, 0)) * words_per_tile;
+            wi[u] = scan_word_load(chain + jj + oi);
+            wa[u] = scan_word_load(chain + jj + oa);
+            wb[u] = scan_word_load(chain + jj + ob);
+        }
+        bool stalled = false;
+#pragma unroll
+        for (int u = 0; u < WIN; ++u) {
+            if (k >= 0 || stalled || j - u < 0) continue;
+            if (static_cast<unsigned>(wi[u] >> 32) == tag_inc) {
+                k = j - u;
+                uk = u;
+                x = scan_word_val(wi[u]);
+            } else if (static_cast<unsigned>(wa[u] >> 32) != tag_agg || static_cast<unsigned>(wb[u] >> 32) != tag_agg) {
+                stalled = true;
+                j -= u;                             // resume at the first tile not yet published
+            }
+        }
+        if (k >= 0) break;
+        if (!stalled) {
+            j -= WIN;
+            continue;
+        }
+        ++spins;
+        if (spins > spin_limit ||
+            ((spins & 1023u) == 0u && __hip_atomic_load(abort_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
+            __hip_atomic_store(abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return __builtin_nanf("");
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    // 2. the chain forward from inc_k: tiles k+1 .. j are still in registers
+    //    (window slots uk-1 .. 0), tiles j+1 .. t-1 were passed in earlier rounds
+#pragma unroll
+    for (int u = WIN - 1; u >= 0; --u)
+        if (u < uk) x = __builtin_fmaf(scan_word_val(wa[u]), x, scan_word_val(wb[u]));
+    for (int m0 = j + 1; m0 < t; m0 += WIN) {
+        float A[WIN], Bv[WIN];
+#pragma unroll
+        for (int u = 0; u < WIN; ++u) {
+            const size_t mm = static_cast<size_t>(min(m0 + u, t - 1)) * words_per_tile;
+            A[u] = scan_word_val(scan_word_load(chain + mm + oa));
+            Bv[u] = scan_word_val(scan_word_load(chain + mm + ob));
+        }
+#pragma unroll
+        for (int u = 0; u < WIN; ++u)
+            if (m0 + u < t) x = __builtin_fmaf(A[u], x, Bv[u]);
+    }
+    return x;
+}
+
 // Geometry of one diagonal-scan launch.
 struct DiagScanPlan {
     int B, T, D;

@@ -17,9 +17,10 @@
 //   2. the time slots of the workgroup are combined through LDS (exclusive
 //      prefix per slot, chunk aggregate per channel);
 //   3. the chunk publishes its aggregate, looks back over the earlier chunks
-//      of the same channels (decoupled look-back) until it meets an inclusive
-//      prefix, and publishes its own inclusive prefix (the state at the
-//      chunk's last step);
+//      of the same channels until it meets an inclusive prefix, applies the
+//      aggregates in between forward from it (a decoupled look-back made
+//      deterministic: the carry is always the left-to-right chain's value), and
+//      publishes its own inclusive prefix (the state at its last step);
 //   4. every thread replays its registers from the carried-in state and
 //      streams s out (non-temporal stores).
 // a and b are read once and s written once: 12 bytes per element.  Holding
@@ -32,8 +33,8 @@
 // valid on its own and no fences are needed.  Forward progress: a workgroup
 // only waits on chunks with smaller indices, each workgroup takes its chunks
 // in increasing order, and all workgroups of the persistent grid are resident
-// together, so the smallest waiting chunk's predecessor is always being
-// processed.  The wait is bounded all the same; if the bound is hit the
+// together, so the smallest waiting chunk's predecessors are always done or
+// being processed.  The wait is bounded all the same; if the bound is hit the
 // header's abort flag is set and the chunk's carry becomes NaN.
 #include <algorithm>
 
@@ -162,42 +163,17 @@ __global__ __launch_bounds__(kThreads) void diag_scan_kernel(
                     GB = ak * GB + shB[k][c];
                     GA = ak * GA;
                 }
+                const unsigned long long *base = desc + static_cast<size_t>(chain) * nchunk * 3 * CH;
                 unsigned long long *mine = desc + (static_cast<size_t>(chain) * nchunk + tchunk) * 3 * CH;
                 if (tchunk == 0) {
                     carry = s0 ? s0[static_cast<size_t>(bseq) * D + ch] : 0.0f;
                 } else {
                     store_word(mine + c, pack_word(GA, tag_agg));
                     store_word(mine + CH + c, pack_word(GB, tag_agg));
-                    float accA = 1.0f, accB = 0.0f;   // maps s_end(j) to s_end(tchunk - 1)
-                    int j = tchunk - 1;
-                    unsigned spins = 0;
-                    while (true) {
-                        const unsigned long long *pj = desc + (static_cast<size_t>(chain) * nchunk + j) * 3 * CH;
-                        const unsigned long long wi = load_word(pj + 2 * CH + c);
-                        const unsigned long long wa = load_word(pj + c);
-                        const unsigned long long wb = load_word(pj + CH + c);
-                        if (word_tag(wi) == tag_inc) {
-                            carry = accA * word_val(wi) + accB;
-                            break;
-                        }
-                        if (word_tag(wa) == tag_agg && word_tag(wb) == tag_agg) {
-                            accB = accA * word_val(wb) + accB;
-                            accA = accA * word_val(wa);
-                            --j;
-                            continue;
-                        }
-                        ++spins;
-                        if (spins > kSpinLimit ||
-                            ((spins & 1023u) == 0u &&
-                             __hip_atomic_load(&hdr->abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
-                            __hip_atomic_store(&hdr->abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                            carry = __builtin_nanf("");
-                            break;
-                        }
-                        __builtin_amdgcn_s_sleep(1);
-                    }
+                    carry = chained_carry<4>(base, 3 * CH, c, CH + c, 2 * CH + c, tchunk, tag_agg, tag_inc, &hdr->abort,
+                                             kSpinLimit);
                 }
-                store_word(mine + 2 * CH + c, pack_word(GA * carry + GB, tag_inc));
+                store_word(mine + 2 * CH + c, pack_word(__builtin_fmaf(GA, carry, GB), tag_inc));
             }
             shC[c] = carry;
         }

@@ -90,3 +90,15 @@ def test_linear_scan_dense_matches_sequential_solve(orc, B, T, D):
     ref = orc.solve_dense(p["A"], p["b"], p["s0"])
     err = rel_linf(s.cpu().numpy(), ref)
     assert np.all(err <= TOL), err
+
+
+def test_linear_scan_diag_is_bitwise_reproducible(orc):
+    """Repeated scans of the same input give the same bits (the look-back's carry
+    is always the left-to-right chain's value, whatever the timing)."""
+    dev = device()
+    p = I.diag_scan_problem(77, 3, 200000, 64)
+    a = torch.from_numpy(p["a"]).to(dev)
+    b = torch.from_numpy(p["b"]).to(dev)
+    log("linear_scan_diag x3 B=3 T=200000 D=64")
+    outs = [deer.linear_scan_diag(a, b, None).cpu().numpy() for _ in range(3)]
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])

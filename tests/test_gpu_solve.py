@@ -232,3 +232,35 @@ def test_full_sweep_gain2_certified(orc):
             assert np.abs(got[k, :h] - ref[k, :h]).max() / np.abs(ref[k]).max() <= TOL
     # iteration counts are reported, and stay inside the finite-step bound
     assert np.all(iters <= w.T)
+
+
+def test_solves_are_bitwise_reproducible(orc):
+    """The scans' look-back always yields the left-to-right chain's value, so
+    the same solve gives the same bits whatever the workgroup timing."""
+    dev = device()
+    for cell_kind, mode, D, T in (("gru", "diag", 64, 20000), ("tanh", "diag", 16, 30000), ("tanh", "dense", 32, 5000)):
+        if cell_kind == "gru":
+            p = I.gru_problem(971, 4, T, D, D, bias_std=0.3, s0_std=0.5)
+        else:
+            p = I.tanh_problem(972, 4, T, D, D, gain=0.9, bias_std=0.3, s0_std=0.5)
+        cell = deer.cell_from_problem(p, dev)
+        x = torch.from_numpy(p["x"]).to(dev)
+        log(f"deer_solve twice {cell_kind} {mode} T={T}")
+        runs = [deer.deer_solve(cell, x, None, mode=mode, tol=1e-6, max_iter=100) for _ in range(3)]
+        first = runs[0][0].cpu().numpy()
+        for r in runs[1:]:
+            assert np.array_equal(first, r[0].cpu().numpy())
+            assert list(r[1]) == list(runs[0][1])
+
+
+def test_picard_long_sequence_matches_oracle(orc):
+    """Picard (A_t = I) amplifies any perturbation behind its exact prefix, so it
+    reaches tol on a long contractive sequence only if every scan of the solve is
+    bit-reproducible: it then needs exactly T iterations, like the oracle."""
+    T = 2048
+    p = I.workload_problem("tanh_d16_t4096_sweep", gain=0.9)
+    p = dict(p, x=np.ascontiguousarray(p["x"][:2, :T]), s0=np.ascontiguousarray(p["s0"][:2]), B=2, T=T)
+    log(f"deer_solve tanh picard T={T}")
+    got, ref, iters, resid, status, rc, oit = _run(orc, p, "picard", 1e-6, T + 1)
+    assert rc == deer.DEER_OK and list(iters) == [T, T] and list(oit) == [T, T]
+    assert np.all(rel_linf(got, ref) <= TOL)

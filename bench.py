@@ -231,9 +231,10 @@ def dense_solve(args, dev):
 def gain_sweep(args, dev):
     """Dense DEER against the sequential GPU rollout across the recurrent gain g.
 
-    The gain sets the largest Lyapunov exponent; the sweep locates the g where
-    the parallel solve stops beating the sequential evaluation.  At g = 2 the
-    linear solve accumulates in double (float32 chunk products are too large).
+    The gain sets the largest Lyapunov exponent (estimated on the GPU along the
+    solved trajectory, deer_lle); the sweep locates the g where the parallel
+    solve stops beating the sequential evaluation.  At g = 2 the linear solve
+    accumulates in double (float32 chunk products are too large).
     """
     import torch
     from evaluation_nonlinear_rnns_amd import deer, inputs as I
@@ -261,9 +262,13 @@ def gain_sweep(args, dev):
             return deer.deer_rollout(cell, x, None, out=seq, stream=stream)
 
         ms_seq, _, _ = _time_solves(roll, 3, stream)
+        v0 = torch.from_numpy(I.lle_probe(50, w.B, w.D)).to(dev)
+        lle_out = torch.empty(w.B, dtype=torch.float64, device=dev)
+        ms_lle, _, _ = _time_solves(lambda: deer.deer_lle(cell, x, out, v0, out=lle_out, stream=stream), 3, stream)
         rows.append({"gain": g, "scan_f64": f64, "rc": int(rc), "iterations_max": int(iters.max()),
                      "iterations_median": float(np.median(iters)), "deer_ms": round(ms, 3),
-                     "rollout_ms": round(ms_seq, 3), "speedup_vs_rollout": round(ms_seq / ms, 3)})
+                     "rollout_ms": round(ms_seq, 3), "speedup_vs_rollout": round(ms_seq / ms, 3),
+                     "lle_mean": round(float(lle_out.mean().item()), 4), "lle_ms": round(ms_lle, 3)})
     slower = [r["gain"] for r in rows if r["speedup_vs_rollout"] < 1.0]
     return {"workload": w.name, "B": w.B, "T": w.T, "D": w.D, "rows": rows,
             "crossover_gain": min(slower) if slower else None}
@@ -309,7 +314,11 @@ def linearizations(args, dev):
             rows[label] = {"mode": mode, "damping": k, "rc": int(rc), "iterations_max": int(iters.max()),
                            "ms_per_solve": round(ms, 3), "speedup_vs_rollout": round(ms_seq / ms, 3)}
             del ws
+        v0 = torch.from_numpy(I.lle_probe(60, w.B, w.D)).to(dev)
+        lle_out = torch.empty(w.B, dtype=torch.float64, device=dev)
+        ms_lle, _, _ = _time_solves(lambda: deer.deer_lle(cell, x, seq, v0, out=lle_out, stream=stream), 2, stream)
         out[name] = {"gain": gain, "B": w.B, "T": w.T, "D": w.D, "tol": w.tol, "rollout_ms": round(ms_seq, 3),
+                     "lle_mean_on_rollout": round(float(lle_out.mean().item()), 4), "lle_ms": round(ms_lle, 3),
                      "runs": rows}
         del traj, seq, x
     return out

@@ -377,6 +377,34 @@ int deer_rollout(const deer_cell_params_t *p, const float *x, const float *s0, i
     return launch_rollout(p, x, s0, B, T, traj_out, static_cast<hipStream_t>(stream));
 }
 
+int deer_lle_workspace_size(const deer_cell_params_t *p, int B, int T, size_t *bytes_out)
+{
+    if (!bytes_out) return fail(DEER_ERR_INVALID, "bytes_out: null pointer");
+    int rc = check_cell(p, p && p->cell == DEER_CELL_GRU ? DEER_MODE_DIAG : DEER_MODE_DENSE);
+    if (rc) return rc;
+    rc = check_sizes(B, T);
+    if (rc) return rc;
+    *bytes_out = lle_layout(nullptr, p, B, T).bytes;
+    return DEER_OK;
+}
+
+int deer_lle(const deer_cell_params_t *p, const float *x, const float *s0, const float *traj, const float *v0, int B,
+             int T, double *lle_out, void *workspace, size_t ws_bytes, void *stream)
+{
+    int rc = check_cell(p, p && p->cell == DEER_CELL_GRU ? DEER_MODE_DIAG : DEER_MODE_DENSE);
+    if (rc) return rc;
+    rc = check_sizes(B, T);
+    if (rc) return rc;
+    if (B == 0) return DEER_OK;
+    if (T <= 0) return fail(DEER_ERR_INVALID, "deer_lle: T must be positive");
+    if (!x || !traj || !v0 || !lle_out) return fail(DEER_ERR_INVALID, "deer_lle: x, traj, v0 and lle_out are required");
+    const LleLayout need = lle_layout(nullptr, p, B, T);
+    rc = check_workspace(workspace, ws_bytes, need.bytes, "deer_lle");
+    if (rc) return rc;
+    return launch_lle(p, x, s0, traj, v0, B, T, lle_out, lle_layout(workspace, p, B, T),
+                      static_cast<hipStream_t>(stream));
+}
+
 int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int B, int T, int mode_flags,
                float damping, float tol, int max_iter, const float *init_guess, float *traj_out, int *iters_out,
                float *resid_out, int *status_out, void *workspace, size_t ws_bytes, void *stream_)

@@ -314,4 +314,16 @@ int launch_gru_quasi_step(const float *Whh, const float *bhh, const float *pt, c
 int launch_rollout(const deer_cell_params_t *p, const float *x, const float *s0, int B, int T,
                    float *traj, hipStream_t stream);
 
+// Largest Lyapunov exponent along a trajectory (lle.hip): workspace layout and launch.
+struct LleLayout {
+    float *proj = nullptr;      // input projection [B,T,PD], row-major
+    float *F = nullptr;         // per-step Jacobian factors [B,T,NF,D]
+    float *junk = nullptr;      // offsets the tanh evaluation also writes (unused)
+    unsigned *res_bits = nullptr;
+    size_t bytes = 0;
+};
+LleLayout lle_layout(void *ws, const deer_cell_params_t *p, int B, int T);
+int launch_lle(const deer_cell_params_t *p, const float *x, const float *s0, const float *traj, const float *v0, int B,
+               int T, double *out, const LleLayout &L, hipStream_t stream);
+
 }  // namespace deer

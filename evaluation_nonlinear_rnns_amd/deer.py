@@ -34,8 +34,8 @@ ERRORS = {-1: "DEER_ERR_INVALID", -2: "DEER_ERR_UNSUPPORTED", -3: "DEER_ERR_WORK
 
 # Every symbol include/deer.h declares.
 EXPORTS = ("deer_workspace_size", "deer_workspace_init", "deer_solve", "linear_scan_workspace_size",
-           "linear_scan_diag", "linear_scan_dense", "deer_rollout", "deer_profile_enable",
-           "deer_profile_read", "deer_last_error")
+           "linear_scan_diag", "linear_scan_dense", "deer_rollout", "deer_lle_workspace_size", "deer_lle",
+           "deer_profile_enable", "deer_profile_read", "deer_last_error")
 
 
 class DeerError(RuntimeError):
@@ -72,6 +72,8 @@ def load_library():
         "linear_scan_diag": ([vp, vp, vp, vp, c_int, c_int, c_int, vp, c_size, vp], c_int),
         "linear_scan_dense": ([vp, vp, vp, vp, c_int, c_int, c_int, vp, c_size, vp], c_int),
         "deer_rollout": ([ctypes.POINTER(CellParams), vp, vp, c_int, c_int, vp, vp], c_int),
+        "deer_lle_workspace_size": ([ctypes.POINTER(CellParams), c_int, c_int, ctypes.POINTER(c_size)], c_int),
+        "deer_lle": ([ctypes.POINTER(CellParams), vp, vp, vp, vp, c_int, c_int, vp, vp, c_size, vp], c_int),
         "deer_profile_enable": ([c_int], c_int),
         "deer_profile_read": ([c_int, ctypes.POINTER(ctypes.c_longlong), ctypes.POINTER(ctypes.c_double)], c_int),
         "deer_last_error": ([], ctypes.c_char_p),
@@ -264,6 +266,28 @@ def deer_rollout(cell: Cell, x, s0=None, out=None, stream=None):
         out = torch.empty((B, T, cell.D), dtype=torch.float32, device=x.device)
     _check(lib.deer_rollout(ctypes.byref(p), _dev(x, "x", shape=(B, T, M)), _dev(s0, "s0", shape=(B, cell.D)),
                             B, T, _dev(out, "out", shape=(B, T, cell.D)), _stream(stream)))
+    return out
+
+
+def deer_lle(cell: Cell, x, traj, v0, s0=None, out=None, workspace=None, stream=None):
+    """Largest Lyapunov exponent per sequence along ``traj [B,T,D]``; returns a
+    float64 CUDA tensor ``[B]``.  ``v0 [B,D]`` are the probe vectors."""
+    import torch
+    lib = load_library()
+    B, T, M = (int(v) for v in x.shape)
+    D = cell.D
+    p = cell.params()
+    if out is None:
+        out = torch.empty(B, dtype=torch.float64, device=x.device)
+    if workspace is None:
+        n = ctypes.c_size_t(0)
+        _check(lib.deer_lle_workspace_size(ctypes.byref(p), B, T, ctypes.byref(n)))
+        workspace = new_workspace(n.value, device=x.device)
+    _check(lib.deer_lle(ctypes.byref(p), _dev(x, "x", shape=(B, T, M)), _dev(s0, "s0", shape=(B, D)),
+                        _dev(traj, "traj", shape=(B, T, D)), _dev(v0, "v0", shape=(B, D)), B, T,
+                        _dev(out, "out", dtype=torch.float64, shape=(B,)),
+                        _dev(workspace, "workspace", dtype=workspace.dtype),
+                        workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
 
 

@@ -199,6 +199,27 @@ int deer_rollout(const deer_cell_params_t *p, const float *x, const float *s0, i
                  float *traj_out, void *stream);
 
 /*
+ * Largest Lyapunov exponent of the dynamics along a given trajectory, per
+ * sequence: a probe vector is pushed through the Jacobians J_t = d f / d s at
+ * (s_{t-1}, x_t), renormalised after every step, and the log growth is
+ * averaged over the T steps (natural log, per step, no burn-in).  This is the
+ * estimator of the "Predictability Enables Parallelization" page (rebuttal,
+ * "LLE computation cost"; its appendix's Algorithm 1); a negative value
+ * predicts that parallel Newton converges in few iterations.
+ *   p       cell parameters (any supported cell)
+ *   x       device [B,T,M] inputs;  s0 device [B,D] or NULL (zeros)
+ *   traj    device [B,T,D], the trajectory (traj[t] = state after step t+1)
+ *   v0      device [B,D] probe vectors (need not be normalised; not all zero)
+ *   lle_out device [B] float64
+ *   workspace device, >= deer_lle_workspace_size bytes, 256-byte aligned
+ * T must be positive.  The vector chain is sequential in t (one wavefront per
+ * sequence); the Jacobian factors are evaluated in parallel beforehand.
+ */
+int deer_lle_workspace_size(const deer_cell_params_t *p, int B, int T, size_t *bytes_out);
+int deer_lle(const deer_cell_params_t *p, const float *x, const float *s0, const float *traj, const float *v0,
+             int B, int T, double *lle_out, void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * Per-kernel timing of deer_solve, for measurement.  While enabled, deer_solve
  * records a pair of HIP events on its stream around every launch of the named
  * kernel class and accumulates the elapsed time; reading returns the number of

@@ -142,3 +142,21 @@ def test_profile_counters_read_and_reset(deer):
         assert deer.deer_profile_read(k) == (0, 0.0)
     with pytest.raises(deer.DeerError):
         deer.deer_profile_read(9)
+
+
+def test_lle_argument_checks(deer):
+    lib = deer.load_library()
+    p = _params(deer, D=16, M=8)
+    n = ctypes.c_size_t(0)
+    assert lib.deer_lle_workspace_size(ctypes.byref(p), 4, 100, ctypes.byref(n)) == 0 and n.value > 0
+    gru = _params(deer, cell="gru", D=16, M=8)
+    m = ctypes.c_size_t(0)
+    assert lib.deer_lle_workspace_size(ctypes.byref(gru), 4, 100, ctypes.byref(m)) == 0 and m.value > n.value
+    assert lib.deer_lle_workspace_size(ctypes.byref(_params(deer, D=65)), 4, 100, ctypes.byref(n)) == -2
+    fake = ctypes.c_void_p(0x1000)
+    out = ctypes.c_void_p(0x2000)
+    assert lib.deer_lle(ctypes.byref(p), fake, None, fake, fake, 0, 10, out, None, 0, None) == 0      # empty batch
+    assert lib.deer_lle(ctypes.byref(p), fake, None, fake, fake, 2, 0, out, fake, 1 << 30, None) == -1  # T = 0
+    assert b"T must be positive" in lib.deer_last_error()
+    assert lib.deer_lle(ctypes.byref(p), fake, None, None, fake, 2, 10, out, fake, 1 << 30, None) == -1  # no traj
+    assert lib.deer_lle(ctypes.byref(p), fake, None, fake, fake, 2, 10, out, None, 0, None) == -3        # workspace

@@ -35,6 +35,8 @@ int hip_fail(hipError_t e, const char *what)
 }
 
 // --------------------------------------------------------------- profiling
+thread_local ProfLaunch g_prof_launch;
+
 namespace {
 constexpr int kProfKinds = 4;
 std::atomic<int> g_prof_enabled{0};
@@ -51,22 +53,22 @@ struct ProfScope {
     hipEvent_t open_start = nullptr;
 
     explicit ProfScope(hipStream_t s) : on(g_prof_enabled.load() != 0), stream(s) {}
+    // The launches between begin and end record the pair themselves (DEER_LAUNCH).
     void begin(int kind)
     {
         if (!on) return;
-        hipEvent_t e;
-        if (hipEventCreate(&e) != hipSuccess) { on = false; return; }
-        (void)hipEventRecord(e, stream);
+        hipEvent_t e0, e1;
+        if (hipEventCreate(&e0) != hipSuccess) { on = false; return; }
+        if (hipEventCreate(&e1) != hipSuccess) { (void)hipEventDestroy(e0); on = false; return; }
         open_kind = kind;
-        open_start = e;
+        open_start = e0;
+        g_prof_launch = ProfLaunch{e0, e1};
     }
     void end()
     {
         if (!on || open_kind < 0) return;
-        hipEvent_t e;
-        if (hipEventCreate(&e) != hipSuccess) { on = false; return; }
-        (void)hipEventRecord(e, stream);
-        marks.push_back({open_kind, {open_start, e}});
+        marks.push_back({open_kind, {open_start, g_prof_launch.stop}});
+        g_prof_launch = ProfLaunch{};
         open_kind = -1;
     }
     // Call after the stream has been synchronised.  Only the first limit[k]
@@ -94,7 +96,15 @@ struct ProfScope {
         }
         marks.clear();
     }
-    ~ProfScope() { release(); }
+    ~ProfScope()
+    {
+        if (open_kind >= 0) {                    // a scope left open by an error return
+            (void)hipEventDestroy(open_start);
+            (void)hipEventDestroy(g_prof_launch.stop);
+        }
+        g_prof_launch = ProfLaunch{};
+        release();
+    }
 };
 
 // Pinned host words for polling the device's all-done flag, one set per host thread.
@@ -303,7 +313,7 @@ int deer_workspace_init(void *workspace, size_t ws_bytes, void *stream)
         return fail(DEER_ERR_WORKSPACE, "workspace: not 256-byte aligned");
     const size_t words = ws_bytes / 4;
     if (words == 0) return DEER_OK;
-    hipLaunchKernelGGL(zero_words_kernel, dim3(grid_for(words)), dim3(256), 0, static_cast<hipStream_t>(stream),
+    DEER_LAUNCH(zero_words_kernel, dim3(grid_for(words)), dim3(256), 0, static_cast<hipStream_t>(stream),
                        static_cast<unsigned *>(workspace), words);
     DEER_HIP(hipGetLastError());
     return DEER_OK;
@@ -448,16 +458,16 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
     ProfScope prof(stream);
 
     // per-solve control state and the starting iterate s^(0) in traj_out
-    hipLaunchKernelGGL(init_control_kernel, dim3(grid_for(static_cast<size_t>(B) + 1)), dim3(256), 0, stream, L.ctl,
+    DEER_LAUNCH(init_control_kernel, dim3(grid_for(static_cast<size_t>(B) + 1)), dim3(256), 0, stream, L.ctl,
                        L.done, L.iters, L.status, L.resid, L.res_bits, B);
     DEER_HIP(hipGetLastError());
     const bool fused = fused_gru_step(p, mode);
     const bool zero_start = fused && !init_guess;   // the fused step reads no s^(0) when it is all zeros
     if (init_guess) {
         if (init_guess != traj_out)
-            hipLaunchKernelGGL(copy_kernel, dim3(grid_for(BTD)), dim3(256), 0, stream, traj_out, init_guess, BTD);
+            DEER_LAUNCH(copy_kernel, dim3(grid_for(BTD)), dim3(256), 0, stream, traj_out, init_guess, BTD);
     } else if (!zero_start) {
-        hipLaunchKernelGGL(fill_kernel, dim3(grid_for(BTD)), dim3(256), 0, stream, traj_out, BTD, 0.0f);
+        DEER_LAUNCH(fill_kernel, dim3(grid_for(BTD)), dim3(256), 0, stream, traj_out, BTD, 0.0f);
     }
     DEER_HIP(hipGetLastError());
 
@@ -489,7 +499,7 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
         prof.end();
         if (r) return r;
         prof.begin(3);
-        hipLaunchKernelGGL(check_kernel, dim3(1), dim3(256), 0, stream, L.ctl, L.res_bits, nullptr, 0, L.done, L.iters,
+        DEER_LAUNCH(check_kernel, dim3(1), dim3(256), 0, stream, L.ctl, L.res_bits, nullptr, 0, L.done, L.iters,
                            L.status, L.resid, B, tol, max_iter);
         prof.end();
         DEER_HIP(hipGetLastError());
@@ -540,7 +550,7 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
     }
     if (rc == DEER_OK) {
         const size_t per_seq = static_cast<size_t>(T) * D;
-        hipLaunchKernelGGL(gather_kernel, dim3(grid_for(per_seq, 256, 1024), B), dim3(256), 0, stream, traj_out,
+        DEER_LAUNCH(gather_kernel, dim3(grid_for(per_seq, 256, 1024), B), dim3(256), 0, stream, traj_out,
                            L.buf1, L.iters, per_seq, B, zero_start ? 1 : 0);
         if (hipGetLastError() != hipSuccess) rc = fail(DEER_ERR_HIP, "deer_solve: gather launch failed");
     }

@@ -601,7 +601,7 @@ int launch_gru_mfma(const float *Whh, const float *bhh, const float *p, const fl
     const int tps = (T + G::TP - 1) / G::TP;
     const long long ntiles = static_cast<long long>(B) * tps;
     const unsigned grid = static_cast<unsigned>(std::max<long long>(1, std::min<long long>(ntiles, cap)));
-    hipLaunchKernelGGL((gru_eval_mfma_kernel<D>), dim3(grid), dim3(kThreads), 0, stream, Whh, bhh, p, s0, s_even,
+    DEER_LAUNCH((gru_eval_mfma_kernel<D>), dim3(grid), dim3(kThreads), 0, stream, Whh, bhh, p, s0, s_even,
                        s_odd, sel, skip, all_done, a, bvec, res_bits, T, tps, ntiles, lz);
     DEER_HIP(hipGetLastError());
     return DEER_OK;
@@ -618,7 +618,7 @@ int launch_proj_mfma(const float *x, const float *U, const float *bias, float *p
     const long long nsub = static_cast<long long>(B) * tps32;
     const long long ntiles = (nsub + G::PS - 1) / G::PS;
     const unsigned grid = static_cast<unsigned>(std::max<long long>(1, std::min<long long>(ntiles, cap)));
-    hipLaunchKernelGGL((projection_mfma_kernel<KP, NOB, TILED>), dim3(grid), dim3(kThreads), 0, stream, x, U, bias, p,
+    DEER_LAUNCH((projection_mfma_kernel<KP, NOB, TILED>), dim3(grid), dim3(kThreads), 0, stream, x, U, bias, p,
                        T, M, tps32, nsub);
     DEER_HIP(hipGetLastError());
     return DEER_OK;
@@ -638,7 +638,7 @@ int launch_gru_step(const float *Whh, const float *bhh, const float *pt, const f
     const unsigned grid = static_cast<unsigned>(std::max<long long>(1, std::min<long long>(ntiles, cap)));
     auto *hdr = static_cast<ScanHeader *>(state);
     auto *desc = reinterpret_cast<unsigned long long *>(static_cast<char *>(state) + sizeof(ScanHeader));
-    hipLaunchKernelGGL((gru_quasi_step_kernel<D>), dim3(grid), dim3(kThreads), 0, stream, Whh, bhh, pt, s0, s_even,
+    DEER_LAUNCH((gru_quasi_step_kernel<D>), dim3(grid), dim3(kThreads), 0, stream, Whh, bhh, pt, s0, s_even,
                        s_odd, ctl, done, iters, status, resid, tol, max_iter, res_bits, res_tile, T, tps, B, ntiles,
                        zero_start ? 1 : 0, lz, hdr, desc);
     DEER_HIP(hipGetLastError());

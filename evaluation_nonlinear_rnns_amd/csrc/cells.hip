@@ -337,18 +337,18 @@ int launch_projection(const float *x, const float *U, const float *bias, float *
     const unsigned blocks = static_cast<unsigned>((N + rows_per_block - 1) / rows_per_block);
     const int og = (O + 63) / 64;
     if (og == 1)
-        hipLaunchKernelGGL((projection_kernel<1>), dim3(blocks), dim3(kThreads), 0, stream, x, U, bias, p, N, M, O, row_tiles);
+        DEER_LAUNCH((projection_kernel<1>), dim3(blocks), dim3(kThreads), 0, stream, x, U, bias, p, N, M, O, row_tiles);
     else if (og == 2)
-        hipLaunchKernelGGL((projection_kernel<2>), dim3(blocks), dim3(kThreads), 0, stream, x, U, bias, p, N, M, O, row_tiles);
+        DEER_LAUNCH((projection_kernel<2>), dim3(blocks), dim3(kThreads), 0, stream, x, U, bias, p, N, M, O, row_tiles);
     else
-        hipLaunchKernelGGL((projection_kernel<3>), dim3(blocks), dim3(kThreads), 0, stream, x, U, bias, p, N, M, O, row_tiles);
+        DEER_LAUNCH((projection_kernel<3>), dim3(blocks), dim3(kThreads), 0, stream, x, U, bias, p, N, M, O, row_tiles);
     DEER_HIP(hipGetLastError());
     return DEER_OK;
 }
 
 #define DEER_TANH_CASE(DPV)                                                                                     \
     case DPV:                                                                                                   \
-        hipLaunchKernelGGL((tanh_eval_kernel<DPV>), dim3(blocks), dim3(kThreads), 0, stream, W, p, s0, s_even,  \
+        DEER_LAUNCH((tanh_eval_kernel<DPV>), dim3(blocks), dim3(kThreads), 0, stream, W, p, s0, s_even,  \
                            s_odd, sel, skip, all_done, lin, bvec, res_bits, T, D, tiles, dense, lz);            \
         break;
 
@@ -372,7 +372,7 @@ int launch_tanh_eval(const float *W, const float *p, const float *s0, const floa
 
 #define DEER_GRU_CASE(DPV)                                                                                      \
     case DPV:                                                                                                   \
-        hipLaunchKernelGGL((gru_eval_kernel<DPV>), dim3(blocks), dim3(kThreads), 0, stream, Whh, bhh, p, s0,    \
+        DEER_LAUNCH((gru_eval_kernel<DPV>), dim3(blocks), dim3(kThreads), 0, stream, Whh, bhh, p, s0,    \
                            s_even, s_odd, sel, skip, all_done, a, bvec, res_bits, T, D, tiles, lz);             \
         break;
 
@@ -400,10 +400,10 @@ int launch_gru_eval(const float *Whh, const float *bhh, const float *p, const fl
 #define DEER_ROLL_CASE(DPV)                                                                                      \
     case DPV:                                                                                                    \
         if (gru)                                                                                                 \
-            hipLaunchKernelGGL((rollout_kernel<DPV, true>), dim3(blocks), dim3(kThreads), 0, stream, p->W, p->U, \
+            DEER_LAUNCH((rollout_kernel<DPV, true>), dim3(blocks), dim3(kThreads), 0, stream, p->W, p->U, \
                                p->b, p->b2, x, s0, traj, B, T, p->D, p->M);                                      \
         else                                                                                                     \
-            hipLaunchKernelGGL((rollout_kernel<DPV, false>), dim3(blocks), dim3(kThreads), 0, stream, p->W,      \
+            DEER_LAUNCH((rollout_kernel<DPV, false>), dim3(blocks), dim3(kThreads), 0, stream, p->W,      \
                                p->U, p->b, p->b2, x, s0, traj, B, T, p->D, p->M);                                \
         break;
 

@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <cstddef>
 #include <cstdint>
@@ -43,6 +44,29 @@ struct Carve {
         return p;
     }
 };
+
+// ------------------------------------------------------------ launches
+// Every kernel launch goes through DEER_LAUNCH.  While deer_solve profiles a
+// class of launches it leaves the class's event pair here; the launches then go
+// out through hipExtLaunchKernelGGL, which timestamps the dispatch itself (no
+// separate event packets between kernels).  The first launch of the class takes
+// the start event and every launch the stop event, so the last one stands.
+struct ProfLaunch {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+extern thread_local ProfLaunch g_prof_launch;
+
+#define DEER_LAUNCH(kernel, grid, block, shmem, stream, ...)                                                     \
+    do {                                                                                                      \
+        if (::deer::g_prof_launch.stop) {                                                                     \
+            hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, ::deer::g_prof_launch.start,            \
+                                  ::deer::g_prof_launch.stop, 0, __VA_ARGS__);                                \
+            ::deer::g_prof_launch.start = nullptr;                                                            \
+        } else {                                                                                              \
+            hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                              \
+        }                                                                                                     \
+    } while (0)
 
 // ------------------------------------------------------------ solve control
 // Device-side state of one deer_solve call.

@@ -159,17 +159,17 @@ int launch_lle_dp(const deer_cell_params_t *p, const float *s0, const float *tra
     const int D = p->D;
     if (p->cell == DEER_CELL_GRU) {
         const int tiles = (T + kTP - 1) / kTP;
-        hipLaunchKernelGGL((gru_lle_factor_kernel<DP>), dim3(static_cast<unsigned>(static_cast<long long>(B) * tiles)),
+        DEER_LAUNCH((gru_lle_factor_kernel<DP>), dim3(static_cast<unsigned>(static_cast<long long>(B) * tiles)),
                            dim3(kThreads), 0, stream, p->W, p->b2, proj, s0, traj, F, T, D, tiles);
         DEER_HIP(hipGetLastError());
-        hipLaunchKernelGGL((lle_chain_kernel<DP, 4>), dim3(static_cast<unsigned>(B)), dim3(64), 0, stream, p->W, F, v0,
+        DEER_LAUNCH((lle_chain_kernel<DP, 4>), dim3(static_cast<unsigned>(B)), dim3(64), 0, stream, p->W, F, v0,
                            T, D, out);
     } else {
         // d_t = 1 - f_t^2 is the factored dense leaf the tanh evaluation writes
         const int r = launch_tanh_eval(p->W, proj, s0, traj, traj, nullptr, nullptr, nullptr, F, junk, res_bits, B, T,
                                        D, 1, Linearization{kLinJacobian, 1.0f}, stream);
         if (r) return r;
-        hipLaunchKernelGGL((lle_chain_kernel<DP, 1>), dim3(static_cast<unsigned>(B)), dim3(64), 0, stream, p->W, F, v0,
+        DEER_LAUNCH((lle_chain_kernel<DP, 1>), dim3(static_cast<unsigned>(B)), dim3(64), 0, stream, p->W, F, v0,
                            T, D, out);
     }
     DEER_HIP(hipGetLastError());

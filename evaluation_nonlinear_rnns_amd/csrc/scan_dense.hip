@@ -776,44 +776,44 @@ int launch_dense_dp(const float *A, const float *d, const float *W, const float 
     const unsigned blocks = static_cast<unsigned>((waves + 3) / 4);
     const bool f64 = sizeof(ACC) == 8;
     if (d && DP == 32 && pl.D == 32 && !f64) {
-        hipLaunchKernelGGL(dense_agg_mfma32_kernel, dim3(static_cast<unsigned>(nq)), dim3(kAggThreads), 0, stream, d, W,
+        DEER_LAUNCH(dense_agg_mfma32_kernel, dim3(static_cast<unsigned>(nq)), dim3(kAggThreads), 0, stream, d, W,
                            b, skip, all_done, pl.T, pl.chunk_len, pl.nchunk, reinterpret_cast<float *>(Pagg),
                            reinterpret_cast<float *>(Bagg));
     } else if (d && DP == 16 && pl.D == 16) {
-        hipLaunchKernelGGL((dense_agg_mfma16_kernel<ACC>), dim3(static_cast<unsigned>(nq)), dim3(64), 0, stream, d, W,
+        DEER_LAUNCH((dense_agg_mfma16_kernel<ACC>), dim3(static_cast<unsigned>(nq)), dim3(64), 0, stream, d, W,
                            b, skip, all_done, pl.T, pl.chunk_len, pl.nchunk, Pagg, Bagg);
     } else if (d) {
-        hipLaunchKernelGGL((dense_agg_kernel<DP, true, ACC>), dim3(blocks), dim3(kThreads), 0, stream, A, d, W, b, skip,
+        DEER_LAUNCH((dense_agg_kernel<DP, true, ACC>), dim3(blocks), dim3(kThreads), 0, stream, A, d, W, b, skip,
                            all_done, pl.B, pl.T, pl.D, pl.chunk_len, pl.nchunk, Pagg, Bagg);
     } else {
-        hipLaunchKernelGGL((dense_agg_kernel<DP, false, ACC>), dim3(blocks), dim3(kThreads), 0, stream, A, d, W, b,
+        DEER_LAUNCH((dense_agg_kernel<DP, false, ACC>), dim3(blocks), dim3(kThreads), 0, stream, A, d, W, b,
                            skip, all_done, pl.B, pl.T, pl.D, pl.chunk_len, pl.nchunk, Pagg, Bagg);
     }
     DEER_HIP(hipGetLastError());
     constexpr bool kVecOk = CarryGeom<DP, ACC>::KG % CarryGeom<DP, ACC>::VEC == 0;
     if (kVecOk && pl.D == DP)
-        hipLaunchKernelGGL((dense_carry_kernel<DP, ACC, kVecOk>), dim3(static_cast<unsigned>(pl.B)), dim3(64), 0, stream,
+        DEER_LAUNCH((dense_carry_kernel<DP, ACC, kVecOk>), dim3(static_cast<unsigned>(pl.B)), dim3(64), 0, stream,
                            Pagg, Bagg, s0, skip, all_done, pl.B, pl.D, pl.nchunk, carry);
     else
-        hipLaunchKernelGGL((dense_carry_kernel<DP, ACC, false>), dim3(static_cast<unsigned>(pl.B)), dim3(64), 0, stream,
+        DEER_LAUNCH((dense_carry_kernel<DP, ACC, false>), dim3(static_cast<unsigned>(pl.B)), dim3(64), 0, stream,
                            Pagg, Bagg, s0, skip, all_done, pl.B, pl.D, pl.nchunk, carry);
     DEER_HIP(hipGetLastError());
     if (d && DP == 32 && pl.D == 32 && !f64) {
-        hipLaunchKernelGGL(dense_replay_dpp32_kernel, dim3(static_cast<unsigned>(nq)), dim3(64), 0, stream, d, W, b,
+        DEER_LAUNCH(dense_replay_dpp32_kernel, dim3(static_cast<unsigned>(nq)), dim3(64), 0, stream, d, W, b,
                            reinterpret_cast<const float *>(carry), skip, all_done, pl.T, pl.chunk_len, pl.nchunk, out0,
                            out1, out_sel);
     } else if (d) {
         const size_t lds = static_cast<size_t>(pl.chunk_len) * pl.D * 2 * sizeof(float);
         if (pl.D == DP && CarryGeom<DP, ACC>::G * DP == 64)       // every lane owns a row
-            hipLaunchKernelGGL((dense_replay_fact_kernel<DP, ACC, true>), dim3(static_cast<unsigned>(nq)), dim3(64), lds,
+            DEER_LAUNCH((dense_replay_fact_kernel<DP, ACC, true>), dim3(static_cast<unsigned>(nq)), dim3(64), lds,
                                stream, d, W, b, carry, skip, all_done, pl.B, pl.T, pl.D, pl.chunk_len, pl.nchunk, out0,
                                out1, out_sel);
         else
-            hipLaunchKernelGGL((dense_replay_fact_kernel<DP, ACC, false>), dim3(static_cast<unsigned>(nq)), dim3(64), lds,
+            DEER_LAUNCH((dense_replay_fact_kernel<DP, ACC, false>), dim3(static_cast<unsigned>(nq)), dim3(64), lds,
                                stream, d, W, b, carry, skip, all_done, pl.B, pl.T, pl.D, pl.chunk_len, pl.nchunk, out0,
                                out1, out_sel);
     } else {
-        hipLaunchKernelGGL((dense_replay_kernel<DP, false, ACC>), dim3(blocks), dim3(kThreads), 0, stream, A, d, W, b,
+        DEER_LAUNCH((dense_replay_kernel<DP, false, ACC>), dim3(blocks), dim3(kThreads), 0, stream, A, d, W, b,
                            carry, skip, all_done, pl.B, pl.T, pl.D, pl.chunk_len, pl.nchunk, out0, out1, out_sel);
     }
     DEER_HIP(hipGetLastError());

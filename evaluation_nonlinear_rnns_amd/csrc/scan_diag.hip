@@ -288,13 +288,13 @@ int launch_diag_scan(const float *a, const float *b, const float *s0, float *out
     auto *hdr = static_cast<ScanHeader *>(state);
     auto *desc = reinterpret_cast<unsigned long long *>(static_cast<char *>(state) + sizeof(ScanHeader));
     if (k == kWide)
-        hipLaunchKernelGGL((diag_scan_kernel<4, 256, kLT>), dim3(grid), dim3(kThreads), 0, stream, a, b, s0, out0,
+        DEER_LAUNCH((diag_scan_kernel<4, 256, kLT>), dim3(grid), dim3(kThreads), 0, stream, a, b, s0, out0,
                            out1, out_sel, skip, all_done, T, D, p.groups, p.chains, p.nchunk, hdr, desc);
     else if (k == kNarrow)
-        hipLaunchKernelGGL((diag_scan_kernel<4, 64, kLT>), dim3(grid), dim3(kThreads), 0, stream, a, b, s0, out0,
+        DEER_LAUNCH((diag_scan_kernel<4, 64, kLT>), dim3(grid), dim3(kThreads), 0, stream, a, b, s0, out0,
                            out1, out_sel, skip, all_done, T, D, p.groups, p.chains, p.nchunk, hdr, desc);
     else
-        hipLaunchKernelGGL((diag_scan_kernel<1, 64, kLT>), dim3(grid), dim3(kThreads), 0, stream, a, b, s0, out0,
+        DEER_LAUNCH((diag_scan_kernel<1, 64, kLT>), dim3(grid), dim3(kThreads), 0, stream, a, b, s0, out0,
                            out1, out_sel, skip, all_done, T, D, p.groups, p.chains, p.nchunk, hdr, desc);
     DEER_HIP(hipGetLastError());
     return DEER_OK;

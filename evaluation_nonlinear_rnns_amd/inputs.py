@@ -110,6 +110,31 @@ def tanh_problem(seed: int, B: int, T: int, D: int, M: int, gain: float = 1.0,
             "D": D, "M": M, "B": B, "T": T, "gain": gain}
 
 
+def lowrank_tanh_problem(seed: int, B: int, T: int, D: int, M: int, rank: int = 2, leak: float = 0.5,
+                         gain: float = 0.4) -> dict:
+    """A tanh RNN whose recurrent matrix is a scaled identity plus a rank-``rank``
+    coupling, ``W = leak I + gain P Q^T / D`` with ``P, Q ~ N(0, 1)`` ``[D, rank]``
+    -- a stand-in for the low-rank RNNs of the "Parallel Broyden Methods" page
+    (appendix F.1), whose Jacobian blocks are diagonal plus low rank.  Then
+    ``U ~ N(0, 1/M)``, ``b = 0``, ``x ~ N(0, 1)``, ``s0 = 0``.
+    """
+    rng = np.random.default_rng(seed)
+    P = _normal(rng, (D, rank), 1.0).astype(np.float64)
+    Q = _normal(rng, (D, rank), 1.0).astype(np.float64)
+    W = (leak * np.eye(D) + gain * (P @ Q.T) / D).astype(np.float32)
+    U = _normal(rng, (D, M), 1.0 / np.sqrt(M))
+    x = _normal(rng, (B, T, M), 1.0)
+    return {"cell": "tanh", "W": W, "U": U, "b": np.zeros(D, np.float32), "b2": None, "x": x,
+            "s0": np.zeros((B, D), np.float32), "D": D, "M": M, "B": B, "T": T, "rank": rank,
+            "leak": leak, "gain": gain}
+
+
+def broyden_sketch(seed: int, D: int, rank: int) -> np.ndarray:
+    """The random sketch ``Omega [D, rank] ~ N(0, 1)`` of the compressed scan."""
+    rng = np.random.default_rng(seed)
+    return _normal(rng, (D, rank), 1.0)
+
+
 def gru_problem(seed: int, B: int, T: int, D: int, M: int, w_std: Optional[float] = None,
                 bias_std: float = 0.0, s0_std: float = 0.0) -> dict:
     """Parameters and inputs of a random GRU (gate order r, z, n).

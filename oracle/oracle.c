@@ -18,7 +18,11 @@
  *   - sequential solvers of the linear recurrence s_t = A_t s_{t-1} + b_t in
  *     diagonal and dense form;
  *   - the largest Lyapunov exponent ("Predictability Enables Parallelization"
- *     page, rebuttal "LLE computation cost", Algorithm 1).
+ *     page, rebuttal "LLE computation cost", Algorithm 1);
+ *   - the parallel Broyden iteration with diagonal-plus-low-rank blocks and
+ *     its chunked, randomly compressed scan ("Parallel Broyden Methods" page,
+ *     section 3; its formulas were lost in extraction, so orc_impl.h states
+ *     the reading it implements).
  * Each function is given in double precision (_f64) and in single precision
  * (_f32, the arithmetic a float32 run of the same algorithm performs).
  *
@@ -205,8 +209,85 @@ int ORC_CAT(orc_lle, SUF)(const orc_cell *c, const float *x, const float *s0, co
     return err ? -1 : 0;                                                                         \
 }
 
+#define ORC_BROYDEN_WRAPPERS(REAL, SUF)                                                          \
+int ORC_CAT(orc_broyden, SUF)(const orc_cell *c, const float *x, const float *s0, int B, int T,  \
+                              int rank, int multisecant, double alpha, double damp,              \
+                              double gram_reg, int chunk, const float *sketch, double tol,       \
+                              int max_iter, const float *init, REAL *traj, int *iters,           \
+                              double *resid, int *status, double *hist, int threads)             \
+{                                                                                                \
+    if (!c || !traj || !iters || !resid || !status || B < 0 || T < 0 || c->D <= 0 ||            \
+        max_iter < 0 || rank < 0 || rank > 8 || (rank > 0 && !sketch) || chunk < 1 ||            \
+        !(damp >= 0.0 && damp <= 1.0) || !(gram_reg >= 0.0) || !isfinite(alpha)) return -1;      \
+    int err = 0;                                                                                 \
+    const int D = c->D, m = rank;                                                                \
+    const size_t TD = (size_t)T * D, TMD = (size_t)T * m * D;                                    \
+    const size_t wsz = 5 * TD + 4 * TMD + (size_t)D * m + 9 * (size_t)D                          \
+                     + (4 * (size_t)D + 7 * (size_t)m * D + 2 * (size_t)m * m + (size_t)m);       \
+    const int nt = orc_threads(threads, B);                                                      \
+    _Pragma("omp parallel for num_threads(nt) schedule(dynamic, 1) reduction(|:err)")            \
+    for (int b = 0; b < B; ++b) {                                                                \
+        REAL *work = (REAL *)malloc(sizeof(REAL) * wsz);                                         \
+        if (!work) { err |= 1; continue; }                                                       \
+        status[b] = ORC_CAT(o_broyden_one, SUF)(c, x + (size_t)b * T * c->M,                    \
+                                                s0 ? s0 + (size_t)b * D : NULL, T, rank,         \
+                                                multisecant, alpha, damp, gram_reg, chunk,       \
+                                                sketch, tol, max_iter,                           \
+                                                init ? init + (size_t)b * TD : NULL,             \
+                                                traj + (size_t)b * TD, iters + b, resid + b,     \
+                                                hist ? hist + (size_t)b * (max_iter + 1) : NULL, \
+                                                work);                                           \
+        free(work);                                                                              \
+    }                                                                                            \
+    return err ? -1 : 0;                                                                         \
+}                                                                                                \
+                                                                                                 \
+int ORC_CAT(orc_dplr_scan, SUF)(double alpha, const float *U, const float *V, const float *cvec, \
+                                const float *sketch, int B, int T, int D, int m, int n,          \
+                                int chunk, REAL *delta, int threads)                             \
+{                                                                                                \
+    if (!U || !V || !cvec || !delta || (m > 0 && !sketch) || B < 0 || T < 0 || D <= 0 ||        \
+        m < 0 || m > 8 || n < 0 || n > m || chunk < 1) return -1;                                \
+    int err = 0;                                                                                 \
+    const size_t TD = (size_t)T * D, TMD = (size_t)T * m * D;                                    \
+    const int nt = orc_threads(threads, B);                                                      \
+    _Pragma("omp parallel for num_threads(nt) schedule(dynamic, 1) reduction(|:err)")            \
+    for (int b = 0; b < B; ++b) {                                                                \
+        const size_t wsz = 2 * TMD + TD + (size_t)D * m                                          \
+                         + 3 * (size_t)D + 7 * (size_t)m * D + 2 * (size_t)m * m;                \
+        REAL *buf = (REAL *)malloc(sizeof(REAL) * wsz);                                          \
+        if (!buf) { err |= 1; continue; }                                                        \
+        REAL *Ur = buf, *Vr = buf + TMD, *cr = buf + 2 * TMD, *Om = cr + TD, *w = Om + (size_t)D * m; \
+        for (size_t e = 0; e < TMD; ++e) {                                                       \
+            Ur[e] = (REAL)U[(size_t)b * TMD + e];                                                \
+            Vr[e] = (REAL)V[(size_t)b * TMD + e];                                                \
+        }                                                                                        \
+        for (size_t e = 0; e < TD; ++e) cr[e] = (REAL)cvec[(size_t)b * TD + e];                  \
+        for (size_t e = 0; e < (size_t)D * m; ++e) Om[e] = (REAL)sketch[e];                      \
+        ORC_CAT(o_dplr_scan_one, SUF)((REAL)alpha, Ur, Vr, n, m, cr, T, D, chunk, Om,            \
+                                      delta + (size_t)b * TD, w);                                \
+        free(buf);                                                                               \
+    }                                                                                            \
+    return err ? -1 : 0;                                                                         \
+}                                                                                                \
+                                                                                                 \
+int ORC_CAT(orc_broyden_update, SUF)(int multisecant, double alpha, double gram_reg, int it,     \
+                                     int m, int D, REAL *U, REAL *V, REAL *F, const REAL *ds,    \
+                                     const REAL *df)                                             \
+{                                                                                                \
+    if (!U || !V || !F || !ds || !df || m < 1 || m > 8 || D <= 0 || it < 1) return -1;           \
+    REAL *scr = (REAL *)malloc(sizeof(REAL) * ((size_t)D + 2 * (size_t)m * m + (size_t)m));      \
+    if (!scr) return -1;                                                                         \
+    ORC_CAT(o_broyden_update_one, SUF)(multisecant, (REAL)alpha, (REAL)gram_reg, it, m, D, U, V, \
+                                       F, ds, df, scr);                                          \
+    free(scr);                                                                                   \
+    return 0;                                                                                    \
+}
+
 ORC_WRAPPERS(double, _f64)
 ORC_WRAPPERS(float, _f32)
+ORC_BROYDEN_WRAPPERS(double, _f64)
+ORC_BROYDEN_WRAPPERS(float, _f32)
 
 /* Threads an OpenMP region would use by default (reported with CPU timings). */
 int orc_max_threads(void)

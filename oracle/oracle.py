@@ -53,7 +53,7 @@ def lib():
             build()
         _lib = ctypes.CDLL(_LIB_PATH)
         for name in ("orc_step", "orc_rollout", "orc_solve_diag", "orc_solve_dense", "orc_newton",
-                     "orc_lle"):
+                     "orc_lle", "orc_broyden", "orc_dplr_scan", "orc_broyden_update"):
             for suf in ("_f64", "_f32"):
                 getattr(_lib, name + suf).restype = ctypes.c_int
         _lib.orc_max_threads.restype = ctypes.c_int
@@ -214,3 +214,75 @@ def lle(cell: Cell, x, traj, v0, s0=None, precision: str = "f64", threads: int =
     if rc != 0:
         raise RuntimeError("orc_lle failed")
     return out
+
+
+def broyden(cell: Cell, x, sketch, s0=None, rank: int = 2, multisecant: bool = False, alpha: float = 0.0,
+            damping: float = 0.0, gram_reg: float = 0.0, chunk: int = 32, tol: float = 1e-6,
+            max_iter: int = 100, precision: str = "f32", init=None, threads: int = 0, history: bool = False):
+    """Parallel Broyden iteration with diagonal-plus-low-rank blocks
+    ``alpha I + (1 - damping) U V^T`` (``rank`` columns, rank-one updates with
+    truncation or the multisecant fit with Gram regularisation ``gram_reg``) and
+    the chunked compressed scan (``chunk`` positions, sketch ``[D, rank]``).
+
+    Returns ``(traj, iters, resid, status)`` like :func:`newton` (plus the
+    residual history with ``history=True``).
+    """
+    dt = _dt(precision)
+    x = _f32(x)
+    B, T = x.shape[0], x.shape[1]
+    s0 = None if s0 is None else _f32(s0)
+    init = None if init is None else _f32(init)
+    sk = _f32(sketch).reshape(cell.D, rank) if rank > 0 else np.zeros((cell.D, 1), np.float32)
+    traj = np.empty((B, T, cell.D), dt)
+    iters = np.zeros(B, np.int32)
+    resid = np.zeros(B, np.float64)
+    status = np.zeros(B, np.int32)
+    hist = np.full((B, max_iter + 1), np.nan) if history else None
+    rc = getattr(lib(), "orc_broyden_" + precision)(
+        cell.ref, _ptr(x), _ptr(s0), B, T, int(rank), int(bool(multisecant)), ctypes.c_double(alpha),
+        ctypes.c_double(damping), ctypes.c_double(gram_reg), int(chunk), _ptr(sk), ctypes.c_double(tol),
+        int(max_iter), _ptr(init), _ptr(traj), _ptr(iters), _ptr(resid), _ptr(status), _ptr(hist), threads)
+    if rc != 0:
+        raise RuntimeError("orc_broyden failed")
+    if history:
+        return traj, iters, resid, status, hist
+    return traj, iters, resid, status
+
+
+def dplr_scan(alpha: float, U, V, c, sketch, n: Optional[int] = None, chunk: int = 32,
+              precision: str = "f64", threads: int = 0) -> np.ndarray:
+    """Chunked compressed scan ``delta_t = (alpha I + U_t V_t^T) delta_{t-1} + c_t``,
+    ``delta_0 = 0``.  ``U, V [B, T, m, D]`` (columns), ``c [B, T, D]``; the first
+    ``n`` columns are used (all by default).  Returns ``delta [B, T, D]``."""
+    dt = _dt(precision)
+    U = _f32(U)
+    V = _f32(V)
+    c = _f32(c)
+    B, T, m, D = U.shape
+    n = m if n is None else n
+    sk = _f32(sketch).reshape(D, m) if m > 0 else np.zeros((D, 1), np.float32)
+    out = np.empty((B, T, D), dt)
+    rc = getattr(lib(), "orc_dplr_scan_" + precision)(ctypes.c_double(alpha), _ptr(U), _ptr(V), _ptr(c), _ptr(sk),
+                                                      B, T, D, m, int(n), int(chunk), _ptr(out), threads)
+    if rc != 0:
+        raise RuntimeError("orc_dplr_scan failed")
+    return out
+
+
+def broyden_update(U, V, F, ds, df, it: int, multisecant: bool = False, alpha: float = 0.0,
+                   gram_reg: float = 0.0, precision: str = "f64"):
+    """One block update at iteration ``it >= 1`` (in place on copies): returns
+    the new ``(U, V, F)``, each ``[m, D]``."""
+    dt = _dt(precision)
+    U = np.array(U, dtype=dt, order="C")
+    V = np.array(V, dtype=dt, order="C")
+    F = np.array(F, dtype=dt, order="C")
+    ds = np.ascontiguousarray(ds, dtype=dt)
+    df = np.ascontiguousarray(df, dtype=dt)
+    m, D = U.shape
+    rc = getattr(lib(), "orc_broyden_update_" + precision)(int(bool(multisecant)), ctypes.c_double(alpha),
+                                                           ctypes.c_double(gram_reg), int(it), m, D, _ptr(U),
+                                                           _ptr(V), _ptr(F), _ptr(ds), _ptr(df))
+    if rc != 0:
+        raise RuntimeError("orc_broyden_update failed")
+    return U, V, F

@@ -285,4 +285,337 @@ static double FN(o_lle_one)(const orc_cell *c, const float *x, const float *s0, 
     return sum / (double)T;
 }
 
+
+/*
+ * ---------------------------------------------------------------- Broyden
+ * Parallel Broyden iteration ("Parallel Broyden Methods" page, sections 3.1
+ * and 3.2, appendices E.1-E.4).  The page's formulas did not survive
+ * extraction; what follows is the reading stated with the build's design notes.
+ *
+ * Block approximation at position t: a diagonal-plus-low-rank (DPLR) matrix
+ *     J^_t = alpha I + sum_j u_j v_j^T      (at most m columns)
+ * with the identity-scaled diagonal baseline alpha of appendix H.5 (0 for the
+ * Gibbs appendix, the leak for the RNN appendix).  The solver uses the damped
+ * block A_t = alpha I + (1 - k) sum_j u_j v_j^T (appendix E.4: damping on the
+ * low-rank correction only).
+ *
+ * Secant pair at iteration i >= 1 and position t:
+ *     ds = s^(i)_{t-1} - s^(i-1)_{t-1},   df = f(s^(i)_{t-1}) - f(s^(i-1)_{t-1}).
+ * Column slot of iteration i: (i - 1) mod m; after the update min(i, m)
+ * columns are valid.
+ *   rank-one ("good" Broyden, limited memory by simple truncation, E.1-E.2):
+ *     the column in the slot (the oldest once m are stored) is dropped, then
+ *     u = (df - J^' ds) / (ds.ds), v = ds, so the new block meets the secant
+ *     exactly; a zero ds gives a zero column.
+ *   multisecant (E.3): the slot takes (ds, df); with S, F the valid secant
+ *     columns, G = S^T S + lambda I and
+ *         U = (F - alpha S) G^{-1},  V = S,
+ *     so J^ S = F when lambda = 0.  A failed Cholesky factorisation of G
+ *     (a pivot <= 0 or not finite) leaves U = 0 at that position.
+ *
+ * Linear step in increment form: with c_t = f_t - s_t (minus the residual),
+ *     delta_t = A_t delta_{t-1} + c_t,  delta_0 = 0,   s^(i+1) = s^(i) + delta,
+ * solved by a chunked scan: chunks of L positions are replayed exactly from
+ * their entry value, and the entry of chunk q+1 is the aggregate of chunk q
+ * applied to the entry of chunk q.  The aggregate P = p I + sum_a l_a r_a^T,
+ * with offset Pb, is folded left to right over the chunk,
+ *     A_t P = alpha p I + [alpha l_a + sum_j u~_j (v_j.l_a) | p u~_j] [r_a | v_j]^T,
+ *     Pb   <- A_t Pb + c_t,
+ * and whenever the low-rank part has more than m columns it is re-compressed
+ * to m by the randomized scheme of section 3.2: Y = L (R^T Omega) with the
+ * fixed sketch Omega [D, m], Q an orthonormal basis of Y's columns (modified
+ * Gram-Schmidt; a column whose remaining norm is at most 1e-5 of its original
+ * norm is dropped as zero), then L <- Q, R <- R (L^T Q), i.e. the correction
+ * becomes Q Q^T L R^T.  Exact zeros stay exact: where c_t = 0 on a prefix,
+ * delta_t = 0 there, which keeps finite-step recovery under compression.
+ */
+#define ORC_QR_DROP 1e-5
+
+/* y = alpha x + sum_{j<n} u_j (v_j . x);  u, v: n columns of D */
+static void FN(o_dplr_apply)(REAL alpha, const REAL *u, const REAL *v, int n, int D, const REAL *x, REAL *y)
+{
+    for (int d = 0; d < D; ++d) y[d] = alpha * x[d];
+    for (int j = 0; j < n; ++j) {
+        REAL dot = 0;
+        for (int d = 0; d < D; ++d) dot += v[(size_t)j * D + d] * x[d];
+        for (int d = 0; d < D; ++d) y[d] += u[(size_t)j * D + d] * dot;
+    }
+}
+
+/* Re-compress the K-column correction sum_a Lf_a Rf_a^T to m columns. */
+static void FN(o_compress)(const REAL *Lf, const REAL *Rf, int K, const REAL *Om, int m, int D,
+                             REAL *Lo, REAL *Ro, REAL *scr /* m*K + m*D */)
+{
+    REAL *RtO = scr;                 /* [K][m]: R^T Omega */
+    REAL *Y = scr + (size_t)m * K;   /* [m][D] */
+    for (int a = 0; a < K; ++a)
+        for (int j = 0; j < m; ++j) {
+            REAL acc = 0;
+            for (int d = 0; d < D; ++d) acc += Rf[(size_t)a * D + d] * Om[(size_t)d * m + j];
+            RtO[(size_t)a * m + j] = acc;
+        }
+    for (int j = 0; j < m; ++j)
+        for (int d = 0; d < D; ++d) {
+            REAL acc = 0;
+            for (int a = 0; a < K; ++a) acc += Lf[(size_t)a * D + d] * RtO[(size_t)a * m + j];
+            Y[(size_t)j * D + d] = acc;
+        }
+    /* modified Gram-Schmidt: Q into Lo */
+    for (int j = 0; j < m; ++j) {
+        REAL *q = Lo + (size_t)j * D;
+        REAL ny = 0;
+        for (int d = 0; d < D; ++d) {
+            q[d] = Y[(size_t)j * D + d];
+            ny += q[d] * q[d];
+        }
+        for (int l = 0; l < j; ++l) {
+            const REAL *ql = Lo + (size_t)l * D;
+            REAL cf = 0;
+            for (int d = 0; d < D; ++d) cf += ql[d] * q[d];
+            for (int d = 0; d < D; ++d) q[d] -= cf * ql[d];
+        }
+        REAL nq = 0;
+        for (int d = 0; d < D; ++d) nq += q[d] * q[d];
+        nq = (REAL)sqrt((double)nq);
+        ny = (REAL)sqrt((double)ny);
+        if (!(nq > (REAL)ORC_QR_DROP * ny)) {
+            for (int d = 0; d < D; ++d) q[d] = 0;
+        } else {
+            for (int d = 0; d < D; ++d) q[d] = q[d] / nq;
+        }
+    }
+    /* Ro_j = sum_a Rf_a (Lf_a . Q_j) */
+    for (int j = 0; j < m; ++j) {
+        for (int d = 0; d < D; ++d) Ro[(size_t)j * D + d] = 0;
+        for (int a = 0; a < K; ++a) {
+            REAL cf = 0;
+            for (int d = 0; d < D; ++d) cf += Lf[(size_t)a * D + d] * Lo[(size_t)j * D + d];
+            for (int d = 0; d < D; ++d) Ro[(size_t)j * D + d] += Rf[(size_t)a * D + d] * cf;
+        }
+    }
+}
+
+/*
+ * Chunked compressed scan of delta_t = A_t delta_{t-1} + c_t, delta_0 = 0, for
+ * one sequence.  A_t = alpha I + sum_{j<n} U[t][j] V[t][j]^T (U already damped);
+ * U, V: [T][m][D]; c, delta: [T][D].
+ */
+static void FN(o_dplr_scan_one)(REAL alpha, const REAL *U, const REAL *V, int n, int m, const REAL *c, int T,
+                                  int D, int L, const REAL *Om, REAL *delta, REAL *work)
+{
+    REAL *entry = work;                   /* D */
+    REAL *Pb = entry + D;                 /* D */
+    REAL *tmpv = Pb + D;                  /* D */
+    REAL *PL = tmpv + D;                  /* m*D */
+    REAL *PR = PL + (size_t)m * D;        /* m*D */
+    REAL *Lf = PR + (size_t)m * D;        /* 2m*D */
+    REAL *Rf = Lf + (size_t)2 * m * D;    /* 2m*D */
+    REAL *scr = Rf + (size_t)2 * m * D;   /* 2m*m + m*D */
+    for (int d = 0; d < D; ++d) entry[d] = 0;
+    for (int t0 = 0; t0 < T; t0 += L) {
+        const int t1 = (t0 + L < T) ? t0 + L : T;
+        /* exact replay of the chunk from its entry */
+        for (int t = t0; t < t1; ++t) {
+            const REAL *prev = (t == t0) ? entry : delta + (size_t)(t - 1) * D;
+            FN(o_dplr_apply)(alpha, U + (size_t)t * m * D, V + (size_t)t * m * D, n, D, prev, delta + (size_t)t * D);
+            for (int d = 0; d < D; ++d) delta[(size_t)t * D + d] += c[(size_t)t * D + d];
+        }
+        if (t1 >= T) break;
+        /* aggregate of the chunk, folded left to right */
+        REAL p = 1;
+        int r = 0;
+        for (int d = 0; d < D; ++d) Pb[d] = 0;
+        for (int t = t0; t < t1; ++t) {
+            const REAL *u = U + (size_t)t * m * D, *v = V + (size_t)t * m * D;
+            const int K = r + n;
+            for (int a = 0; a < r; ++a) {
+                FN(o_dplr_apply)(alpha, u, v, n, D, PL + (size_t)a * D, Lf + (size_t)a * D);
+                for (int d = 0; d < D; ++d) Rf[(size_t)a * D + d] = PR[(size_t)a * D + d];
+            }
+            for (int j = 0; j < n; ++j)
+                for (int d = 0; d < D; ++d) {
+                    Lf[(size_t)(r + j) * D + d] = p * u[(size_t)j * D + d];
+                    Rf[(size_t)(r + j) * D + d] = v[(size_t)j * D + d];
+                }
+            p = alpha * p;
+            if (K <= m) {
+                memcpy(PL, Lf, sizeof(REAL) * (size_t)K * D);
+                memcpy(PR, Rf, sizeof(REAL) * (size_t)K * D);
+                r = K;
+            } else {
+                FN(o_compress)(Lf, Rf, K, Om, m, D, PL, PR, scr);
+                r = m;
+            }
+            FN(o_dplr_apply)(alpha, u, v, n, D, Pb, tmpv);
+            for (int d = 0; d < D; ++d) Pb[d] = tmpv[d] + c[(size_t)t * D + d];
+        }
+        /* entry of the next chunk */
+        FN(o_dplr_apply)(p, PL, PR, r, D, entry, tmpv);
+        for (int d = 0; d < D; ++d) entry[d] = tmpv[d] + Pb[d];
+    }
+}
+
+/* Block update of one position at iteration it >= 1 (see above).
+ * U, V (and F for the multisecant variant): [m][D], updated in place. */
+static void FN(o_broyden_update_one)(int multisecant, REAL alpha, REAL lambda, int it, int m, int D,
+                                       REAL *U, REAL *V, REAL *F, const REAL *ds, const REAL *df,
+                                       REAL *scr /* D + 2 m m + m */)
+{
+    if (m <= 0 || it < 1) return;
+    const int slot = (it - 1) % m;
+    if (!multisecant) {
+        const int nb = (it - 1 < m) ? it - 1 : m;     /* valid before the update */
+        REAL *jds = scr;
+        for (int d = 0; d < D; ++d) jds[d] = alpha * ds[d];
+        for (int j = 0; j < nb; ++j) {
+            if (j == slot) continue;
+            REAL dot = 0;
+            for (int d = 0; d < D; ++d) dot += V[(size_t)j * D + d] * ds[d];
+            for (int d = 0; d < D; ++d) jds[d] += U[(size_t)j * D + d] * dot;
+        }
+        REAL ss = 0;
+        for (int d = 0; d < D; ++d) ss += ds[d] * ds[d];
+        for (int d = 0; d < D; ++d) {
+            if (ss > 0) {
+                U[(size_t)slot * D + d] = (df[d] - jds[d]) / ss;
+                V[(size_t)slot * D + d] = ds[d];
+            } else {
+                U[(size_t)slot * D + d] = 0;
+                V[(size_t)slot * D + d] = 0;
+            }
+        }
+        return;
+    }
+    for (int d = 0; d < D; ++d) {
+        V[(size_t)slot * D + d] = ds[d];
+        F[(size_t)slot * D + d] = df[d];
+    }
+    const int n = (it < m) ? it : m;
+    REAL *G = scr, *C = scr + (size_t)m * m, *y = C + (size_t)m * m;
+    for (int a = 0; a < n; ++a)
+        for (int b = 0; b < n; ++b) {
+            REAL acc = 0;
+            for (int d = 0; d < D; ++d) acc += V[(size_t)a * D + d] * V[(size_t)b * D + d];
+            G[(size_t)a * m + b] = acc + ((a == b) ? lambda : (REAL)0);
+        }
+    /* Cholesky G = C C^T (C lower triangular) */
+    int ok = 1;
+    for (int a = 0; a < n && ok; ++a) {
+        for (int b = 0; b <= a; ++b) {
+            REAL acc = G[(size_t)a * m + b];
+            for (int e = 0; e < b; ++e) acc -= C[(size_t)a * m + e] * C[(size_t)b * m + e];
+            if (a == b) {
+                if (!(acc > 0) || isinf((double)acc)) { ok = 0; break; }
+                C[(size_t)a * m + a] = (REAL)sqrt((double)acc);
+            } else {
+                C[(size_t)a * m + b] = acc / C[(size_t)b * m + b];
+            }
+        }
+    }
+    for (int d = 0; d < D; ++d) {
+        if (!ok) {
+            for (int a = 0; a < m; ++a) U[(size_t)a * D + d] = 0;
+            continue;
+        }
+        /* solve G y = F_d - alpha S_d: forward then backward substitution */
+        for (int a = 0; a < n; ++a) {
+            REAL acc = F[(size_t)a * D + d] - alpha * V[(size_t)a * D + d];
+            for (int e = 0; e < a; ++e) acc -= C[(size_t)a * m + e] * y[e];
+            y[a] = acc / C[(size_t)a * m + a];
+        }
+        for (int a = n - 1; a >= 0; --a) {
+            REAL acc = y[a];
+            for (int e = a + 1; e < n; ++e) acc -= C[(size_t)e * m + a] * y[e];
+            y[a] = acc / C[(size_t)a * m + a];
+        }
+        for (int a = 0; a < n; ++a) U[(size_t)a * D + d] = y[a];
+        for (int a = n; a < m; ++a) U[(size_t)a * D + d] = 0;
+    }
+}
+
+/*
+ * The parallel Broyden iteration for one sequence.  Iteration i:
+ *   f_t = f(s^(i)_{t-1}, x_t);  res = max |s^(i)_t - f_t|;  stop as the Newton
+ *   iteration does (converged at res <= tol, iters = i; else at the cap);
+ *   for i >= 1 update every block from the secants against iteration i-1;
+ *   delta from the compressed scan with c_t = f_t - s^(i)_t;  s^(i+1) = s^(i) + delta.
+ * Iteration 0 has no secant yet: A_t = alpha I.
+ */
+static int FN(o_broyden_one)(const orc_cell *c, const float *x, const float *s0, int T, int rank,
+                               int multisecant, double alpha_d, double damp, double lambda_d, int L,
+                               const float *omega, double tol, int max_iter, const float *init,
+                               REAL *s /*[T,D] out*/, int *iters_out, double *resid_out, double *hist,
+                               REAL *work)
+{
+    const int D = c->D, m = rank;
+    const size_t TD = (size_t)T * D, TMD = (size_t)T * m * D;
+    REAL *f = work;                   /* [T,D] */
+    REAL *fp = f + TD;                /* [T,D] previous f */
+    REAL *sp = fp + TD;               /* [T,D] previous iterate */
+    REAL *cc = sp + TD;               /* [T,D] */
+    REAL *dl = cc + TD;               /* [T,D] */
+    REAL *U = dl + TD;                /* [T,m,D] */
+    REAL *V = U + TMD;                /* [T,m,D] */
+    REAL *F = V + TMD;                /* [T,m,D] */
+    REAL *Ud = F + TMD;               /* [T,m,D] damped */
+    REAL *Om = Ud + TMD;              /* [D,m] */
+    REAL *s0r = Om + (size_t)D * m;   /* D */
+    REAL *ds = s0r + D, *df = ds + D; /* D each */
+    REAL *tmp = df + D;               /* 6D */
+    REAL *scr = tmp + 6 * D;          /* scan: 3 D + 7 m D + 2 m m; update: D + 2 m m + m */
+    const REAL alpha = (REAL)alpha_d, lambda = (REAL)lambda_d, shrink = (REAL)(1.0 - damp);
+
+    for (int d = 0; d < D; ++d) s0r[d] = s0 ? (REAL)s0[d] : (REAL)0;
+    for (size_t e = 0; e < (size_t)D * m; ++e) Om[e] = (REAL)omega[e];
+    for (size_t e = 0; e < TD; ++e) s[e] = init ? (REAL)init[e] : (REAL)0;
+    for (size_t e = 0; e < TMD; ++e) U[e] = V[e] = F[e] = Ud[e] = 0;
+    if (hist)
+        for (int i = 0; i <= max_iter; ++i) hist[i] = NAN;
+
+    for (int it = 0;; ++it) {
+        double res = 0.0;
+        int nonfinite = 0;
+        for (int t = 0; t < T; ++t) {
+            const REAL *sprev = (t == 0) ? s0r : s + (size_t)(t - 1) * D;
+            FN(o_step)(c, sprev, x + (size_t)t * c->M, f + (size_t)t * D, NULL, NULL, tmp);
+            for (int d = 0; d < D; ++d) {
+                const double r = fabs((double)(s[(size_t)t * D + d] - f[(size_t)t * D + d]));
+                if (!(r == r) || isinf(r)) nonfinite = 1;
+                if (r > res) res = r;
+            }
+        }
+        if (nonfinite) res = NAN;
+        if (hist) hist[it] = res;
+        if ((REAL)res <= (REAL)tol) {
+            *iters_out = it;
+            *resid_out = res;
+            return 0;
+        }
+        if (it >= max_iter) {
+            *iters_out = max_iter;
+            *resid_out = res;
+            return (res == res && !isinf(res)) ? 1 : 2;
+        }
+        if (it >= 1 && m > 0) {
+            for (int t = 0; t < T; ++t) {
+                for (int d = 0; d < D; ++d) {
+                    const REAL a = (t == 0) ? s0r[d] : s[(size_t)(t - 1) * D + d];
+                    const REAL b = (t == 0) ? s0r[d] : sp[(size_t)(t - 1) * D + d];
+                    ds[d] = a - b;
+                    df[d] = f[(size_t)t * D + d] - fp[(size_t)t * D + d];
+                }
+                FN(o_broyden_update_one)(multisecant, alpha, lambda, it, m, D, U + (size_t)t * m * D,
+                                           V + (size_t)t * m * D, F + (size_t)t * m * D, ds, df, scr);
+            }
+        }
+        const int n = (it < m) ? it : m;
+        for (size_t e = 0; e < TMD; ++e) Ud[e] = shrink * U[e];
+        for (size_t e = 0; e < TD; ++e) cc[e] = f[e] - s[e];
+        FN(o_dplr_scan_one)(alpha, Ud, V, n, m, cc, T, D, L, Om, dl, scr);
+        memcpy(sp, s, TD * sizeof(REAL));
+        memcpy(fp, f, TD * sizeof(REAL));
+        for (size_t e = 0; e < TD; ++e) s[e] = s[e] + dl[e];
+    }
+}
+
 #undef FN

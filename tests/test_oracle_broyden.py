@@ -1,0 +1,311 @@
+"""Pins of the oracle's parallel Broyden iteration and its compressed scan.
+
+The page ("Parallel Broyden Methods", section 3 and appendix E) lost its
+formulas in extraction, so the oracle implements a stated reading; these tests
+tie that reading to facts fixed independently of the oracle: dense forward
+substitution (numpy) where the compressed scan must be exact, the secant
+conditions the Broyden updates are built to meet, numpy's linear solve for the
+regularised multisecant fit, the finite-step recovery the page proves, the
+sequential rollout as the fixed point, and the Picard / Jacobi iterations that
+the rank-0 case reduces to.
+"""
+import numpy as np
+import pytest
+
+from evaluation_nonlinear_rnns_amd import inputs as I
+
+
+def _dense_scan(alpha, U, V, c, n=None):
+    """delta_t = (alpha I + sum_{j<n} U_tj V_tj^T) delta_{t-1} + c_t, in float64 numpy."""
+    U = U.astype(np.float32).astype(np.float64)
+    V = V.astype(np.float32).astype(np.float64)
+    c = c.astype(np.float32).astype(np.float64)
+    B, T, m, D = U.shape
+    n = m if n is None else n
+    out = np.zeros((B, T, D))
+    for b in range(B):
+        prev = np.zeros(D)
+        for t in range(T):
+            A = alpha * np.eye(D) + U[b, t, :n].T @ V[b, t, :n]
+            prev = A @ prev + c[b, t]
+            out[b, t] = prev
+    return out
+
+
+def _blocks(seed, B, T, m, D, scale=0.3):
+    rng = np.random.default_rng(seed)
+    U = (rng.standard_normal((B, T, m, D)) * scale).astype(np.float32)
+    V = (rng.standard_normal((B, T, m, D)) * scale).astype(np.float32)
+    c = rng.standard_normal((B, T, D)).astype(np.float32)
+    return U, V, c
+
+
+# ------------------------------------------------------------ compressed scan
+
+@pytest.mark.parametrize("m", [1, 2, 4])
+def test_dplr_scan_single_chunk_is_exact(orc, m):
+    """One chunk: the scan is the exact replay, equal to dense forward substitution."""
+    U, V, c = _blocks(1 + m, 2, 40, m, 7)
+    sk = I.broyden_sketch(5, 7, m)
+    got = orc.dplr_scan(0.6, U, V, c, sk, chunk=64)
+    np.testing.assert_allclose(got, _dense_scan(0.6, U, V, c), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("m,chunk", [(1, 3), (2, 4), (3, 5)])
+def test_dplr_scan_purely_low_rank_is_exact_across_chunks(orc, m, chunk):
+    """alpha = 0: products of rank-m blocks keep rank m, so re-compression loses
+    nothing and the chunk carries are exact (the page's purely low-rank case)."""
+    U, V, c = _blocks(11 + m, 2, 30, m, 8, scale=0.5)
+    sk = I.broyden_sketch(6, 8, m)
+    got = orc.dplr_scan(0.0, U, V, c, sk, chunk=chunk)
+    ref = _dense_scan(0.0, U, V, c)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-10 * np.abs(ref).max())
+
+
+def test_dplr_scan_shared_column_space_is_exact(orc):
+    """Blocks alpha I + Ub C_t V_t^T with a fixed column space span(Ub): every
+    product's low-rank part stays in that m-dimensional space, so the randomized
+    compression is exact even with a non-zero diagonal."""
+    rng = np.random.default_rng(3)
+    B, T, m, D = 2, 36, 2, 9
+    # small dyadic entries, so U = Ub C is exact in float32 and its columns lie
+    # exactly in span(Ub)
+    Ub = rng.integers(-3, 4, (D, m)).astype(np.float64)
+    C = rng.integers(-4, 5, (B, T, m, m)) / 32.0
+    U = np.einsum("dk,btkj->btjd", Ub, C).astype(np.float32)
+    assert np.array_equal(U.astype(np.float64), np.einsum("dk,btkj->btjd", Ub, C))
+    V = (rng.standard_normal((B, T, m, D)) * 0.4).astype(np.float32)
+    c = rng.standard_normal((B, T, D)).astype(np.float32)
+    sk = I.broyden_sketch(9, D, m)
+    got = orc.dplr_scan(0.8, U, V, c, sk, chunk=5)
+    ref = _dense_scan(0.8, U, V, c)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-10 * np.abs(ref).max())
+
+
+def test_dplr_scan_general_blocks_are_approximate(orc):
+    """General DPLR blocks across chunks: the carries go through compressed
+    aggregates, so the result differs from the exact solve -- slightly."""
+    U, V, c = _blocks(21, 2, 64, 2, 8)
+    sk = I.broyden_sketch(4, 8, 2)
+    got = orc.dplr_scan(0.5, U, V, c, sk, chunk=8)
+    ref = _dense_scan(0.5, U, V, c)
+    err = np.abs(got - ref).max() / np.abs(ref).max()
+    assert 1e-9 < err < 0.05, err
+    # positions of the first chunk never see a compressed carry
+    np.testing.assert_allclose(got[:, :8], ref[:, :8], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("precision", ["f64", "f32"])
+def test_dplr_scan_zero_prefix_stays_exactly_zero(orc, precision):
+    """c_t = 0 on a prefix spanning several chunks gives delta_t = 0 there,
+    bit for bit, whatever the compression does (the mechanism behind
+    finite-step recovery)."""
+    U, V, c = _blocks(31, 2, 50, 3, 6)
+    c[:, :23] = 0.0
+    sk = I.broyden_sketch(7, 6, 3)
+    got = orc.dplr_scan(0.7, U, V, c, sk, chunk=4, precision=precision)
+    assert np.all(got[:, :23] == 0.0)
+    assert np.all(got[:, 23] != 0.0)
+
+
+def test_dplr_scan_rank_zero_is_scalar_recurrence(orc):
+    """n = 0 columns: delta_t = alpha delta_{t-1} + c_t, a first-order IIR filter."""
+    U, V, c = _blocks(41, 1, 40, 2, 5)
+    sk = I.broyden_sketch(8, 5, 2)
+    got = orc.dplr_scan(0.9, U, V, c, sk, n=0, chunk=6)
+    ref = np.zeros((40, 5))
+    prev = np.zeros(5)
+    for t in range(40):
+        prev = 0.9 * prev + c[0, t].astype(np.float64)
+        ref[t] = prev
+    np.testing.assert_allclose(got[0], ref, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------ block updates
+
+def _jhat(alpha, U, V, cols):
+    D = U.shape[1]
+    return alpha * np.eye(D) + sum(np.outer(U[j], V[j]) for j in cols) if cols else alpha * np.eye(D)
+
+
+def test_rank_one_update_meets_the_secant_and_changes_least(orc):
+    """Good Broyden: after dropping the slot's column, J_new ds = df, and
+    J_new w = J' w for every w orthogonal to ds."""
+    rng = np.random.default_rng(5)
+    m, D, alpha = 3, 6, 0.4
+    U = rng.standard_normal((m, D))
+    V = rng.standard_normal((m, D))
+    F = np.zeros((m, D))
+    ds, df = rng.standard_normal(D), rng.standard_normal(D)
+    it = 5                                   # slot (5 - 1) % 3 = 1; all 3 columns valid before
+    U2, V2, _ = orc.broyden_update(U, V, F, ds, df, it, alpha=alpha)
+    J2 = _jhat(alpha, U2, V2, [0, 1, 2])
+    np.testing.assert_allclose(J2 @ ds, df, rtol=0, atol=1e-12)
+    Jp = _jhat(alpha, U, V, [0, 2])
+    w = rng.standard_normal(D)
+    w -= (w @ ds) / (ds @ ds) * ds
+    np.testing.assert_allclose(J2 @ w, Jp @ w, rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(U2[[0, 2]], U[[0, 2]])
+    np.testing.assert_array_equal(V2[1], ds)
+
+
+def test_rank_one_update_fills_slots_in_order_then_truncates(orc):
+    rng = np.random.default_rng(6)
+    m, D = 2, 4
+    U = np.zeros((m, D)); V = np.zeros((m, D)); F = np.zeros((m, D))
+    secants = [(rng.standard_normal(D), rng.standard_normal(D)) for _ in range(3)]
+    for it, (ds, df) in enumerate(secants, start=1):
+        U, V, F = orc.broyden_update(U, V, F, ds, df, it, alpha=0.0)
+    # slots: it 1 -> 0, it 2 -> 1, it 3 -> 0 (the oldest, from it 1, dropped)
+    np.testing.assert_array_equal(V[0], secants[2][0])
+    np.testing.assert_array_equal(V[1], secants[1][0])
+    J = _jhat(0.0, U, V, [0, 1])
+    np.testing.assert_allclose(J @ secants[2][0], secants[2][1], rtol=0, atol=1e-12)
+
+
+def test_rank_one_update_degenerate_secant_gives_zero_column(orc):
+    rng = np.random.default_rng(7)
+    m, D = 2, 5
+    U = rng.standard_normal((m, D)); V = rng.standard_normal((m, D)); F = np.zeros((m, D))
+    U2, V2, _ = orc.broyden_update(U, V, F, np.zeros(D), rng.standard_normal(D), 3, alpha=0.3)
+    assert np.all(U2[0] == 0) and np.all(V2[0] == 0)
+    np.testing.assert_array_equal(U2[1], U[1])
+
+
+@pytest.mark.parametrize("n", [1, 2, 4])
+def test_multisecant_fits_every_secant(orc, n):
+    """lambda = 0: J S = F for the n stored secants and J w = alpha w off span(S)."""
+    rng = np.random.default_rng(8 + n)
+    m, D, alpha = 4, 7, 0.25
+    U = np.zeros((m, D)); V = np.zeros((m, D)); F = np.zeros((m, D))
+    S, Fs = [], []
+    for it in range(1, n + 1):
+        ds, df = rng.standard_normal(D), rng.standard_normal(D)
+        S.append(ds); Fs.append(df)
+        U, V, F = orc.broyden_update(U, V, F, ds, df, it, multisecant=True, alpha=alpha)
+    J = _jhat(alpha, U, V, list(range(n)))
+    for ds, df in zip(S, Fs):
+        np.testing.assert_allclose(J @ ds, df, rtol=0, atol=1e-10)
+    Q, _ = np.linalg.qr(np.array(S).T, mode="complete")
+    w = Q[:, n]
+    np.testing.assert_allclose(J @ w, alpha * w, rtol=0, atol=1e-12)
+
+
+def test_multisecant_regularised_fit_matches_linear_solve(orc):
+    """U = (F - alpha S)(S^T S + lambda I)^{-1}, checked with numpy's solver."""
+    rng = np.random.default_rng(12)
+    m, D, alpha, lam = 3, 6, 0.5, 0.3
+    U = np.zeros((m, D)); V = np.zeros((m, D)); F = np.zeros((m, D))
+    S, Fs = [], []
+    for it in range(1, 6):                   # 5 updates, ring of 3: slots 0,1,2,0,1
+        ds, df = rng.standard_normal(D), rng.standard_normal(D)
+        U, V, F = orc.broyden_update(U, V, F, ds, df, it, multisecant=True, alpha=alpha, gram_reg=lam)
+        S.append(ds); Fs.append(df)
+    Sm = np.array([S[3], S[4], S[2]]).T      # columns in slot order
+    Fm = np.array([Fs[3], Fs[4], Fs[2]]).T
+    ref = np.linalg.solve(Sm.T @ Sm + lam * np.eye(m), (Fm - alpha * Sm).T)   # [m, D]
+    np.testing.assert_allclose(U, ref, rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(V, Sm.T)
+
+
+def test_multisecant_singular_gram_gives_no_correction(orc):
+    m, D = 2, 4
+    U = np.ones((m, D)); V = np.zeros((m, D)); F = np.zeros((m, D))
+    U2, _, _ = orc.broyden_update(U, V, F, np.zeros(D), np.ones(D), 1, multisecant=True, alpha=0.5)
+    assert np.all(U2 == 0)
+
+
+# ------------------------------------------------------------ the iteration
+
+def _lowrank(seed=4, B=2, T=48, D=10):
+    p = I.lowrank_tanh_problem(seed, B, T, D, D, rank=2, leak=0.5, gain=0.6)
+    return p
+
+
+@pytest.mark.parametrize("multisecant", [False, True])
+@pytest.mark.parametrize("k", [1, 2, 5, 9])
+def test_broyden_finite_step_recovery(orc, multisecant, k):
+    """After k iterations the first k positions equal the sequential rollout,
+    even though chunk carries go through compressed aggregates (chunk 4)."""
+    p = _lowrank()
+    c = orc.Cell.from_problem(p)
+    ref = orc.rollout(c, p["x"])
+    sk = I.broyden_sketch(2, p["D"], 2)
+    traj, iters, _, status = orc.broyden(c, p["x"], sk, rank=2, multisecant=multisecant, alpha=0.5,
+                                         gram_reg=1e-9 if multisecant else 0.0, chunk=4, tol=-1.0,
+                                         max_iter=k, precision="f64")
+    assert np.all(iters == k) and np.all(status == 1)
+    np.testing.assert_allclose(traj[:, :k], ref[:, :k], rtol=0, atol=1e-13)
+    assert np.abs(traj[:, k:] - ref[:, k:]).max() > 1e-8
+
+
+@pytest.mark.parametrize("multisecant", [False, True])
+@pytest.mark.parametrize("cell", ["tanh", "gru"])
+def test_broyden_converges_to_the_rollout(orc, multisecant, cell):
+    if cell == "tanh":
+        p = _lowrank(T=200)
+    else:
+        p = I.gru_problem(8, 2, 200, 12, 6, bias_std=0.3)
+    c = orc.Cell.from_problem(p)
+    ref = orc.rollout(c, p["x"])
+    sk = I.broyden_sketch(3, p["D"], 4)
+    traj, iters, resid, status = orc.broyden(c, p["x"], sk, rank=4, multisecant=multisecant, alpha=0.5,
+                                             gram_reg=1e-8 if multisecant else 0.0, chunk=16, tol=1e-10,
+                                             max_iter=200, precision="f64")
+    assert np.all(status == 0), (iters, resid)
+    assert np.all(iters < 100), iters         # well inside the finite-step bound T = 200
+    np.testing.assert_allclose(traj, ref, rtol=0, atol=1e-9)
+
+
+@pytest.mark.parametrize("alpha,mode", [(1.0, "picard"), (0.0, "jacobi")])
+def test_broyden_rank_zero_reduces_to_picard_and_jacobi(orc, alpha, mode):
+    """No low-rank columns: A_t = I is Picard, A_t = 0 is Jacobi."""
+    p = _lowrank(T=60)
+    c = orc.Cell.from_problem(p)
+    sk = I.broyden_sketch(3, p["D"], 1)
+    tb, ib, _, sb = orc.broyden(c, p["x"], sk, rank=0, alpha=alpha, chunk=7, tol=1e-10, max_iter=200,
+                                precision="f64")
+    tn, i_n, _, sn = orc.newton(c, p["x"], mode=mode, tol=1e-10, max_iter=200, precision="f64")
+    np.testing.assert_array_equal(ib, i_n)
+    np.testing.assert_array_equal(sb, sn)
+    np.testing.assert_allclose(tb, tn, rtol=0, atol=1e-12)
+
+
+def test_broyden_full_damping_is_rank_zero(orc):
+    """k = 1 removes the low-rank correction: the iterates are those of rank 0."""
+    p = _lowrank(T=40)
+    c = orc.Cell.from_problem(p)
+    sk = I.broyden_sketch(3, p["D"], 3)
+    ta, ia, _, _ = orc.broyden(c, p["x"], sk, rank=3, alpha=0.5, damping=1.0, chunk=5, tol=-1.0, max_iter=6,
+                               precision="f64")
+    tb, ib, _, _ = orc.broyden(c, p["x"], sk, rank=0, alpha=0.5, chunk=5, tol=-1.0, max_iter=6,
+                               precision="f64")
+    np.testing.assert_array_equal(ta, tb)
+
+
+def test_broyden_beats_picard_on_the_gru(orc):
+    """The page's point: secant blocks without any Jacobian converge in a few
+    tens of iterations where the identity blocks (Picard) crawl."""
+    p = I.gru_problem(2, 1, 256, 16, 16)
+    c = orc.Cell.from_problem(p)
+    sk = I.broyden_sketch(3, 16, 2)
+    _, ib, _, sb = orc.broyden(c, p["x"], sk, rank=2, alpha=0.5, chunk=32, tol=1e-6, max_iter=256,
+                               precision="f64")
+    _, ip, _, _ = orc.newton(c, p["x"], mode="picard", tol=1e-6, max_iter=256, precision="f64")
+    assert sb[0] == 0 and ib[0] < 30 and ip[0] > 4 * ib[0], (ib, ip)
+
+
+def test_broyden_argument_checks(orc):
+    p = _lowrank(T=8)
+    c = orc.Cell.from_problem(p)
+    sk = I.broyden_sketch(3, p["D"], 2)
+    for kw in ({"rank": 9}, {"damping": 1.5}, {"chunk": 0}, {"gram_reg": -1.0}):
+        args = dict(rank=2, alpha=0.5, chunk=4, tol=1e-6, max_iter=4)
+        args.update(kw)
+        if args["rank"] == 9:
+            sk9 = np.zeros((p["D"], 9), np.float32)
+            with pytest.raises(RuntimeError):
+                orc.broyden(c, p["x"], sk9, **args)
+            continue
+        with pytest.raises(RuntimeError):
+            orc.broyden(c, p["x"], sk, **args)

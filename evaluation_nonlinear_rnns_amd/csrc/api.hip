@@ -270,6 +270,126 @@ SolveLayout solve_layout(void *ws, const deer_cell_params_t *p, int B, int T, in
     return L;
 }
 
+// The two polling events of a solve; destroyed when the solve returns, after
+// its final stream synchronisation.
+struct PollEvents {
+    hipEvent_t ev[2] = {nullptr, nullptr};
+    ~PollEvents()
+    {
+        for (auto &e : ev)
+            if (e) (void)hipEventDestroy(e);
+    }
+};
+
+// Enqueue batches of iterations (1, 2, 4, 4, ...) and, while the current batch
+// runs, wait for the copy of the device's all-done flag enqueued after the
+// previous batch; stop enqueueing once it reads set.  Kernels enqueued after
+// convergence exit at once.  `total` caps the evaluations enqueued.
+template <class Enqueue>
+int run_polled(Enqueue &&enqueue_iteration, const int *all_done, long long total, hipStream_t stream,
+               PollEvents &pe, const char *who)
+{
+    int rc = DEER_OK;
+    long long launched = 0;
+    int batch = 1;
+    int slot = 0;
+    for (auto &e : pe.ev)
+        if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess)
+            return fail(DEER_ERR_HIP, std::string(who) + ": event creation failed");
+    bool pending = false;
+    int pending_slot = 0;
+    volatile int *h = g_poll.host;
+    while (launched < total) {
+        const long long n = std::min<long long>(batch, total - launched);
+        for (long long k = 0; k < n && rc == DEER_OK; ++k) rc = enqueue_iteration();
+        if (rc) break;
+        launched += n;
+        h[slot] = 0;
+        if (hipMemcpyAsync(g_poll.host + slot, all_done, sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+            hipEventRecord(pe.ev[slot], stream) != hipSuccess) {
+            rc = fail(DEER_ERR_HIP, std::string(who) + ": polling copy failed");
+            break;
+        }
+        if (pending) {
+            if (hipEventSynchronize(pe.ev[pending_slot]) != hipSuccess) {
+                rc = fail(DEER_ERR_HIP, std::string(who) + ": event wait failed");
+                break;
+            }
+            if (h[pending_slot]) break;
+        }
+        pending = true;
+        pending_slot = slot;
+        slot ^= 1;
+        if (batch < 4) batch *= 2;
+    }
+    return rc;
+}
+
+// Layout of the deer_solve_broyden workspace and of the standalone DPLR scan's.
+struct BroydenLayout {
+    SolveControl *ctl = nullptr;
+    unsigned *res_bits = nullptr;
+    int *done = nullptr, *iters = nullptr, *status = nullptr;
+    float *resid = nullptr;
+    float *buf1 = nullptr;              // second iterate buffer [B,T,D]
+    float *f_even = nullptr, *f_odd = nullptr;   // f^(i) by parity [B,T,D]
+    float *proj = nullptr;              // input projection
+    float *U = nullptr, *V = nullptr, *F = nullptr;   // [B,T,m,D]
+    float *agg_p = nullptr;
+    int *agg_r = nullptr;
+    float *agg_L = nullptr, *agg_R = nullptr, *agg_b = nullptr, *entry = nullptr;
+    size_t bytes = 0;
+};
+
+void carve_dplr_scan(Carve &c, BroydenLayout &L, int B, int T, int D, int m, int chunk)
+{
+    const size_t nch = static_cast<size_t>(B) * ((T + chunk - 1) / chunk);
+    L.agg_p = c.take<float>(nch);
+    L.agg_r = c.take<int>(nch);
+    L.agg_L = c.take<float>(nch * m * D);
+    L.agg_R = c.take<float>(nch * m * D);
+    L.agg_b = c.take<float>(nch * D);
+    L.entry = c.take<float>(nch * D);
+}
+
+BroydenLayout broyden_layout(void *ws, const deer_cell_params_t *p, int B, int T, const deer_broyden_opts_t *o)
+{
+    const size_t BTD = static_cast<size_t>(B) * T * p->D;
+    const int PD = (p->cell == DEER_CELL_GRU) ? 3 * p->D : p->D;
+    Carve c(ws);
+    BroydenLayout L;
+    L.ctl = c.take<SolveControl>(1);
+    L.res_bits = c.take<unsigned>(B);
+    L.done = c.take<int>(B);
+    L.iters = c.take<int>(B);
+    L.status = c.take<int>(B);
+    L.resid = c.take<float>(B);
+    L.buf1 = c.take<float>(BTD);
+    L.f_even = c.take<float>(BTD);
+    L.f_odd = c.take<float>(BTD);
+    L.proj = c.take<float>(projection_floats(B, T, PD));
+    L.U = c.take<float>(BTD * o->rank);
+    L.V = c.take<float>(BTD * o->rank);
+    if (o->multisecant) L.F = c.take<float>(BTD * o->rank);
+    carve_dplr_scan(c, L, B, T, p->D, o->rank, o->chunk);
+    L.bytes = c.off;
+    return L;
+}
+
+int check_broyden_opts(const deer_broyden_opts_t *o, bool need_sketch)
+{
+    if (!o) return fail(DEER_ERR_INVALID, "Broyden options: null pointer");
+    if (o->rank < 0 || o->rank > 8) return fail(DEER_ERR_UNSUPPORTED, "Broyden rank outside 0..8");
+    if (o->chunk < 1 || o->chunk > 4096) return fail(DEER_ERR_INVALID, "Broyden chunk outside 1..4096");
+    if (!std::isfinite(o->alpha)) return fail(DEER_ERR_INVALID, "Broyden alpha not finite");
+    if (!(o->damping >= 0.0f && o->damping <= 1.0f)) return fail(DEER_ERR_INVALID, "Broyden damping outside [0, 1]");
+    if (!(o->gram_reg >= 0.0f) || std::isinf(o->gram_reg))
+        return fail(DEER_ERR_INVALID, "Broyden gram_reg must be finite and >= 0");
+    if (need_sketch && o->rank > 0 && !o->sketch)
+        return fail(DEER_ERR_INVALID, "Broyden sketch required for rank > 0");
+    return DEER_OK;
+}
+
 int check_workspace(void *ws, size_t have, size_t need, const char *who)
 {
     if (!ws || have < need)
@@ -513,41 +633,9 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
         return r;
     };
 
-    // Enqueue batches of iterations and poll the device flag of the previous
-    // batch while the current one runs.  Kernels after convergence exit at once.
     const long long total = static_cast<long long>(max_iter) + 1;   // evaluations needed at most
-    long long launched = 0;
-    int batch = 1;
-    int slot = 0;
-    hipEvent_t ev[2] = {nullptr, nullptr};
-    DEER_HIP(hipEventCreateWithFlags(&ev[0], hipEventDisableTiming));
-    DEER_HIP(hipEventCreateWithFlags(&ev[1], hipEventDisableTiming));
-    bool pending = false;
-    int pending_slot = 0;
-    volatile int *h = g_poll.host;
-    while (launched < total) {
-        const long long n = std::min<long long>(batch, total - launched);
-        for (long long k = 0; k < n && rc == DEER_OK; ++k) rc = enqueue_iteration();
-        if (rc) break;
-        launched += n;
-        h[slot] = 0;
-        if (hipMemcpyAsync(g_poll.host + slot, all_done, sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess ||
-            hipEventRecord(ev[slot], stream) != hipSuccess) {
-            rc = fail(DEER_ERR_HIP, "deer_solve: polling copy failed");
-            break;
-        }
-        if (pending) {
-            if (hipEventSynchronize(ev[pending_slot]) != hipSuccess) {
-                rc = fail(DEER_ERR_HIP, "deer_solve: event wait failed");
-                break;
-            }
-            if (h[pending_slot]) break;
-        }
-        pending = true;
-        pending_slot = slot;
-        slot ^= 1;
-        if (batch < 4) batch *= 2;
-    }
+    PollEvents pe;
+    rc = run_polled(enqueue_iteration, all_done, total, stream, pe, "deer_solve");
     if (rc == DEER_OK) {
         const size_t per_seq = static_cast<size_t>(T) * D;
         DEER_LAUNCH(gather_kernel, dim3(grid_for(per_seq, 256, 1024), B), dim3(256), 0, stream, traj_out,
@@ -568,8 +656,6 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
             rc = fail(DEER_ERR_HIP, "deer_solve: flag copy failed");
     }
     const hipError_t se = hipStreamSynchronize(stream);
-    (void)hipEventDestroy(ev[0]);
-    (void)hipEventDestroy(ev[1]);
     if (se != hipSuccess && rc == DEER_OK) rc = hip_fail(se, "hipStreamSynchronize(deer_solve)");
     if (rc) return rc;
     {
@@ -585,6 +671,183 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
         any_nc |= status_h[b] != DEER_SEQ_CONVERGED;
     }
     return any_nc ? DEER_NOT_CONVERGED : DEER_OK;
+}
+
+int deer_broyden_workspace_size(const deer_cell_params_t *p, int B, int T, const deer_broyden_opts_t *opts,
+                                size_t *bytes_out)
+{
+    if (!bytes_out) return fail(DEER_ERR_INVALID, "deer_broyden_workspace_size: null output");
+    int rc = check_cell(p, DEER_MODE_DIAG);
+    if (rc) return rc;
+    rc = check_broyden_opts(opts, false);
+    if (rc) return rc;
+    rc = check_sizes(B, T);
+    if (rc) return rc;
+    *bytes_out = broyden_layout(nullptr, p, B, T, opts).bytes;
+    return DEER_OK;
+}
+
+int deer_solve_broyden(const deer_cell_params_t *p, const float *x, const float *s0, int B, int T,
+                       const deer_broyden_opts_t *opts, float tol, int max_iter, const float *init_guess,
+                       float *traj_out, int *iters_out, float *resid_out, int *status_out, void *workspace,
+                       size_t ws_bytes, void *stream_)
+{
+    int rc = check_cell(p, DEER_MODE_DIAG);
+    if (rc) return rc;
+    rc = check_broyden_opts(opts, true);
+    if (rc) return rc;
+    rc = check_sizes(B, T);
+    if (rc) return rc;
+    if (max_iter < 0) return fail(DEER_ERR_INVALID, "max_iter must be >= 0");
+    if (std::isnan(tol)) return fail(DEER_ERR_INVALID, "tol is NaN");
+    if (B == 0) return DEER_OK;
+    if (!iters_out) return fail(DEER_ERR_INVALID, "iters_out: null pointer");
+    if (T == 0) {
+        const bool pass = 0.0f <= tol;
+        for (int b = 0; b < B; ++b) {
+            iters_out[b] = pass ? 0 : max_iter;
+            if (resid_out) resid_out[b] = 0.0f;
+            if (status_out) status_out[b] = pass ? DEER_SEQ_CONVERGED : DEER_SEQ_NOT_CONVERGED;
+        }
+        return pass ? DEER_OK : DEER_NOT_CONVERGED;
+    }
+    if (!x || !traj_out) return fail(DEER_ERR_INVALID, "x and traj_out are required");
+    rc = check_workspace(workspace, ws_bytes, broyden_layout(nullptr, p, B, T, opts).bytes, "deer_solve_broyden");
+    if (rc) return rc;
+    if (!g_poll.host) return fail(DEER_ERR_HIP, "deer_solve_broyden: pinned host memory unavailable");
+
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    const BroydenLayout L = broyden_layout(workspace, p, B, T, opts);
+    const int D = p->D;
+    const size_t BTD = static_cast<size_t>(B) * T * D;
+    const bool gru = p->cell == DEER_CELL_GRU;
+    const int PD = gru ? 3 * D : D;
+    const bool tiled = gru && gru_fast_path(D, p->M);
+    ProfScope prof(stream);
+
+    DEER_LAUNCH(init_control_kernel, dim3(grid_for(static_cast<size_t>(B) + 1)), dim3(256), 0, stream, L.ctl,
+                L.done, L.iters, L.status, L.resid, L.res_bits, B);
+    if (init_guess) {
+        if (init_guess != traj_out)
+            DEER_LAUNCH(copy_kernel, dim3(grid_for(BTD)), dim3(256), 0, stream, traj_out, init_guess, BTD);
+    } else {
+        DEER_LAUNCH(fill_kernel, dim3(grid_for(BTD)), dim3(256), 0, stream, traj_out, BTD, 0.0f);
+    }
+    DEER_HIP(hipGetLastError());
+    prof.begin(2);
+    rc = launch_projection(x, p->U, p->b, L.proj, B, T, p->M, PD, tiled, stream);
+    prof.end();
+    if (rc) return rc;
+
+    DplrArgs a;
+    a.B = B; a.T = T; a.D = D; a.m = opts->rank;
+    a.chunk = opts->chunk; a.nchunk = (T + opts->chunk - 1) / opts->chunk;
+    a.alpha = opts->alpha; a.shrink = 1.0f - opts->damping; a.lambda = opts->gram_reg;
+    a.multisecant = opts->multisecant ? 1 : 0;
+    a.omega = opts->sketch;
+    a.U = L.U; a.V = L.V; a.F = L.F;
+    a.s0 = s0; a.s_even = traj_out; a.s_odd = L.buf1; a.f_even = L.f_even; a.f_odd = L.f_odd;
+    a.ctl = L.ctl; a.skip = L.done;
+    a.agg_p = L.agg_p; a.agg_r = L.agg_r; a.agg_L = L.agg_L; a.agg_R = L.agg_R; a.agg_b = L.agg_b;
+    a.entry = L.entry;
+
+    const int *sel = &L.ctl->iter;
+    const int *all_done = &L.ctl->all_done;
+    const Linearization value{kLinValue, 1.0f};
+    auto enqueue_iteration = [&]() -> int {
+        int r;
+        prof.begin(0);
+        if (gru)
+            r = launch_gru_eval(p->W, p->b2, L.proj, s0, traj_out, L.buf1, sel, L.done, all_done, L.f_even,
+                                L.f_odd, L.res_bits, B, T, D, p->M, value, stream);
+        else
+            r = launch_tanh_eval(p->W, L.proj, s0, traj_out, L.buf1, sel, L.done, all_done, L.f_even, L.f_odd,
+                                 L.res_bits, B, T, D, 0, value, stream);
+        prof.end();
+        if (r) return r;
+        prof.begin(3);
+        DEER_LAUNCH(check_kernel, dim3(1), dim3(256), 0, stream, L.ctl, L.res_bits, nullptr, 0, L.done, L.iters,
+                    L.status, L.resid, B, tol, max_iter);
+        prof.end();
+        DEER_HIP(hipGetLastError());
+        prof.begin(1);
+        r = launch_dplr_step(a, stream);
+        prof.end();
+        return r;
+    };
+    const long long total = static_cast<long long>(max_iter) + 1;
+    PollEvents pe;
+    rc = run_polled(enqueue_iteration, all_done, total, stream, pe, "deer_solve_broyden");
+    if (rc == DEER_OK) {
+        const size_t per_seq = static_cast<size_t>(T) * D;
+        DEER_LAUNCH(gather_kernel, dim3(grid_for(per_seq, 256, 1024), B), dim3(256), 0, stream, traj_out, L.buf1,
+                    L.iters, per_seq, B, 0);
+        if (hipGetLastError() != hipSuccess) rc = fail(DEER_ERR_HIP, "deer_solve_broyden: gather launch failed");
+    }
+    std::vector<int> status_h(B, 0);
+    if (rc == DEER_OK) {
+        if (hipMemcpyAsync(iters_out, L.iters, sizeof(int) * B, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+            (resid_out && hipMemcpyAsync(resid_out, L.resid, sizeof(float) * B, hipMemcpyDeviceToHost, stream) != hipSuccess) ||
+            hipMemcpyAsync(status_h.data(), L.status, sizeof(int) * B, hipMemcpyDeviceToHost, stream) != hipSuccess)
+            rc = fail(DEER_ERR_HIP, "deer_solve_broyden: result copy failed");
+    }
+    const hipError_t se = hipStreamSynchronize(stream);
+    if (se != hipSuccess && rc == DEER_OK) rc = hip_fail(se, "hipStreamSynchronize(deer_solve_broyden)");
+    if (rc) return rc;
+    {
+        int last = 0;
+        for (int b = 0; b < B; ++b) last = std::max(last, iters_out[b]);
+        const long long limit[kProfKinds] = {last + 1, last, 1, last + 1};
+        prof.collect(limit);
+    }
+    bool any_nc = false;
+    for (int b = 0; b < B; ++b) {
+        if (status_out) status_out[b] = status_h[b];
+        any_nc |= status_h[b] != DEER_SEQ_CONVERGED;
+    }
+    return any_nc ? DEER_NOT_CONVERGED : DEER_OK;
+}
+
+int linear_scan_dplr_workspace_size(int B, int T, int D, int rank, int chunk, size_t *bytes_out)
+{
+    if (!bytes_out) return fail(DEER_ERR_INVALID, "linear_scan_dplr_workspace_size: null output");
+    int rc = check_sizes(B, T);
+    if (rc) return rc;
+    if (D < 1 || D > kMaxD) return fail(DEER_ERR_UNSUPPORTED, "DPLR scan: D outside 1..64");
+    if (rank < 0 || rank > 8) return fail(DEER_ERR_UNSUPPORTED, "DPLR scan: rank outside 0..8");
+    if (chunk < 1 || chunk > 4096) return fail(DEER_ERR_INVALID, "DPLR scan: chunk outside 1..4096");
+    Carve c(nullptr);
+    BroydenLayout L;
+    carve_dplr_scan(c, L, B, T, D, rank, chunk);
+    *bytes_out = c.off;
+    return DEER_OK;
+}
+
+int linear_scan_dplr(float alpha, const float *U, const float *V, const float *c, const float *sketch, float *delta,
+                     int B, int T, int D, int rank, int chunk, void *workspace, size_t ws_bytes, void *stream)
+{
+    size_t need = 0;
+    int rc = linear_scan_dplr_workspace_size(B, T, D, rank, chunk, &need);
+    if (rc) return rc;
+    if (!std::isfinite(alpha)) return fail(DEER_ERR_INVALID, "DPLR scan: alpha not finite");
+    if (static_cast<long long>(B) * T == 0) return DEER_OK;
+    if (!c || !delta || (rank > 0 && (!U || !V || !sketch)))
+        return fail(DEER_ERR_INVALID, "DPLR scan: c, delta (and U, V, sketch for rank > 0) are required");
+    rc = check_workspace(workspace, ws_bytes, need, "linear_scan_dplr");
+    if (rc) return rc;
+    Carve cv(workspace);
+    BroydenLayout L;
+    carve_dplr_scan(cv, L, B, T, D, rank, chunk);
+    DplrArgs a;
+    a.B = B; a.T = T; a.D = D; a.m = rank; a.n_fixed = rank;
+    a.chunk = chunk; a.nchunk = (T + chunk - 1) / chunk;
+    a.alpha = alpha;
+    a.omega = sketch;
+    a.U = const_cast<float *>(U); a.V = const_cast<float *>(V);
+    a.c = c; a.out = delta;
+    a.agg_p = L.agg_p; a.agg_r = L.agg_r; a.agg_L = L.agg_L; a.agg_R = L.agg_R; a.agg_b = L.agg_b;
+    a.entry = L.entry;
+    return launch_dplr_step(a, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -147,6 +147,7 @@ __global__ __launch_bounds__(kThreads) void gru_eval_mfma_kernel(
     const float wz = Whh[static_cast<size_t>(D + c) * D + c];
     const float wn = Whh[static_cast<size_t>(2 * D + c) * D + c];
     const float *s = (sel && (*sel & 1)) ? s_odd : s_even;
+    float *fdst = (sel && (*sel & 1)) ? bout : aout;   // kLinValue output
 
     const long long tb = ntiles * blockIdx.x / gridDim.x, te = ntiles * (blockIdx.x + 1) / gridDim.x;
     if (tb >= te) return;
@@ -211,8 +212,12 @@ __global__ __launch_bounds__(kThreads) void gru_eval_mfma_kernel(
             const float a = lin_diag(lz, zg + (h - ng) * zg * (1.0f - zg) * wz +
                                              (1.0f - zg) * (1.0f - ng * ng) * (rg * wn + rg * (1.0f - rg) * wr * qn));
             const size_t o = (seq + t) * D + c;
-            __builtin_nontemporal_store(a, aout + o);
-            __builtin_nontemporal_store(f - a * h, bout + o);
+            if (lz.kind == kLinValue) {
+                __builtin_nontemporal_store(f, fdst + o);
+            } else {
+                __builtin_nontemporal_store(a, aout + o);
+                __builtin_nontemporal_store(f - a * h, bout + o);
+            }
             rmax = max(rmax, __float_as_uint(fabsf(st - f)));
         }
     }

@@ -126,6 +126,7 @@ __global__ __launch_bounds__(kThreads) void tanh_eval_kernel(
     __shared__ float Wt[DP][DP + 1];     // Wt[k][c] = W[c][k]
     __shared__ float srow[kTP + 1][DP];  // srow[r] = s_{t0 - 1 + r}
     const float *s = (sel && (*sel & 1)) ? s_odd : s_even;
+    float *fdst = (sel && (*sel & 1)) ? bout : lin;   // kLinValue output
     const int t0 = tile * kTP;
     const size_t seq = static_cast<size_t>(bseq) * T;
     for (int e = threadIdx.x; e < DP * DP; e += kThreads) {
@@ -158,7 +159,9 @@ __global__ __launch_bounds__(kThreads) void tanh_eval_kernel(
         const float h = ws + p[o];
         const float f = tanhf(h);
         const float d = 1.0f - f * f;
-        if (dense) {
+        if (lz.kind == kLinValue) {
+            fdst[o] = f;
+        } else if (dense) {
             const float dd = lz.shrink * d;
             lin[o] = dd;
             bout[o] = f - dd * ws;
@@ -191,6 +194,7 @@ __global__ __launch_bounds__(kThreads) void gru_eval_kernel(
     __shared__ float Wt[DP][3 * DP];     // Wt[k][g*DP + c] = W_hh[g*D + c][k]
     __shared__ float srow[kTP + 1][DP];
     const float *s = (sel && (*sel & 1)) ? s_odd : s_even;
+    float *fdst = (sel && (*sel & 1)) ? bout : aout;  // kLinValue output
     const int t0 = tile * kTP;
     const size_t seq = static_cast<size_t>(bseq) * T;
     for (int e = threadIdx.x; e < 3 * DP * DP; e += kThreads) {
@@ -237,8 +241,12 @@ __global__ __launch_bounds__(kThreads) void gru_eval_kernel(
         const float a = lin_diag(lz, zg + (h - ng) * zg * (1.0f - zg) * wz +
                                          (1.0f - zg) * (1.0f - ng * ng) * (rg * wn + rg * (1.0f - rg) * wr * qn));
         const size_t o = (seq + t) * D + c;
-        aout[o] = a;
-        bout[o] = f - a * h;
+        if (lz.kind == kLinValue) {
+            fdst[o] = f;
+        } else {
+            aout[o] = a;
+            bout[o] = f - a * h;
+        }
         rmax = max(rmax, __float_as_uint(fabsf(srow[r + 1][c] - f)));
     }
     block_max_to(rmax, res_bits + bseq);

@@ -278,7 +278,9 @@ size_t projection_floats(int B, int T, int O);
 
 // How an iteration linearises f: the Jacobian (or its diagonal) shrunk by
 // `shrink` = 1 - k, the zero block (Jacobi) or the identity (Picard).
-enum LinKind : int { kLinJacobian = 0, kLinZero = 1, kLinIdentity = 2 };
+// kLinValue: evaluation only -- the cell value f_t goes to the first output
+// array when the iteration index (*sel) is even, to the second when it is odd.
+enum LinKind : int { kLinJacobian = 0, kLinZero = 1, kLinIdentity = 2, kLinValue = 3 };
 struct Linearization {
     int kind;
     float shrink;
@@ -337,6 +339,36 @@ int launch_gru_quasi_step(const float *Whh, const float *bhh, const float *pt, c
 
 int launch_rollout(const deer_cell_params_t *p, const float *x, const float *s0, int B, int T,
                    float *traj, hipStream_t stream);
+
+// Parallel Broyden (broyden.hip): the block updates and the chunked compressed
+// scan of delta_t = A_t delta_{t-1} + c_t, A_t = alpha I + shrink U_t V_t^T.
+// Solver mode (ctl set): iteration i = ctl->iter - 1 (the convergence check
+// has run); c_t = f^(i)_t - s^(i)_t; blocks are updated from the secants
+// against iteration i - 1 first; s^(i+1) = s^(i) + delta goes to the iterate
+// buffer that does not hold s^(i).  Standalone mode (ctl null): c given, the
+// first n_fixed columns used as they are, delta written to out.
+struct DplrArgs {
+    int B = 0, T = 0, D = 0;
+    int m = 0;                  // columns per block (ring size)
+    int chunk = 32, nchunk = 0;
+    float alpha = 0.0f, shrink = 1.0f, lambda = 0.0f;
+    int multisecant = 0;
+    int n_fixed = 0;
+    const float *omega = nullptr;                     // [D, m]
+    float *U = nullptr, *V = nullptr, *F = nullptr;   // [B, T, m, D]
+    const float *c = nullptr;                         // standalone: [B, T, D]
+    float *out = nullptr;                             // standalone: delta [B, T, D]
+    const float *s0 = nullptr;
+    float *s_even = nullptr, *s_odd = nullptr;        // iterate buffers (solver)
+    const float *f_even = nullptr, *f_odd = nullptr;  // cell values by iteration parity (solver)
+    const SolveControl *ctl = nullptr;
+    const int *skip = nullptr;
+    float *agg_p = nullptr;                           // [B * nchunk]
+    int *agg_r = nullptr;                             // [B * nchunk]
+    float *agg_L = nullptr, *agg_R = nullptr;         // [B * nchunk, m, D]
+    float *agg_b = nullptr, *entry = nullptr;         // [B * nchunk, D]
+};
+int launch_dplr_step(const DplrArgs &a, hipStream_t stream);
 
 // Largest Lyapunov exponent along a trajectory (lle.hip): workspace layout and launch.
 struct LleLayout {

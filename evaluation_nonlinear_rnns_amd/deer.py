@@ -35,13 +35,20 @@ ERRORS = {-1: "DEER_ERR_INVALID", -2: "DEER_ERR_UNSUPPORTED", -3: "DEER_ERR_WORK
 # Every symbol include/deer.h declares.
 EXPORTS = ("deer_workspace_size", "deer_workspace_init", "deer_solve", "linear_scan_workspace_size",
            "linear_scan_diag", "linear_scan_dense", "deer_rollout", "deer_lle_workspace_size", "deer_lle",
-           "deer_profile_enable", "deer_profile_read", "deer_last_error")
+           "deer_broyden_workspace_size", "deer_solve_broyden", "linear_scan_dplr_workspace_size",
+           "linear_scan_dplr", "deer_profile_enable", "deer_profile_read", "deer_last_error")
 
 
 class DeerError(RuntimeError):
     def __init__(self, code: int, msg: str):
         super().__init__(f"{ERRORS.get(code, code)}: {msg}")
         self.code = code
+
+
+class BroydenOpts(ctypes.Structure):
+    _fields_ = [("rank", ctypes.c_int), ("multisecant", ctypes.c_int), ("alpha", ctypes.c_float),
+                ("damping", ctypes.c_float), ("gram_reg", ctypes.c_float), ("chunk", ctypes.c_int),
+                ("sketch", ctypes.c_void_p)]
 
 
 class CellParams(ctypes.Structure):
@@ -74,6 +81,12 @@ def load_library():
         "deer_rollout": ([ctypes.POINTER(CellParams), vp, vp, c_int, c_int, vp, vp], c_int),
         "deer_lle_workspace_size": ([ctypes.POINTER(CellParams), c_int, c_int, ctypes.POINTER(c_size)], c_int),
         "deer_lle": ([ctypes.POINTER(CellParams), vp, vp, vp, vp, c_int, c_int, vp, vp, c_size, vp], c_int),
+        "deer_broyden_workspace_size": ([ctypes.POINTER(CellParams), c_int, c_int, ctypes.POINTER(BroydenOpts),
+                                         ctypes.POINTER(c_size)], c_int),
+        "deer_solve_broyden": ([ctypes.POINTER(CellParams), vp, vp, c_int, c_int, ctypes.POINTER(BroydenOpts), fp,
+                                c_int, vp, vp, vp, vp, vp, vp, c_size, vp], c_int),
+        "linear_scan_dplr_workspace_size": ([c_int, c_int, c_int, c_int, c_int, ctypes.POINTER(c_size)], c_int),
+        "linear_scan_dplr": ([fp, vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, vp, c_size, vp], c_int),
         "deer_profile_enable": ([c_int], c_int),
         "deer_profile_read": ([c_int, ctypes.POINTER(ctypes.c_longlong), ctypes.POINTER(ctypes.c_double)], c_int),
         "deer_last_error": ([], ctypes.c_char_p),
@@ -288,6 +301,84 @@ def deer_lle(cell: Cell, x, traj, v0, s0=None, out=None, workspace=None, stream=
                         _dev(out, "out", dtype=torch.float64, shape=(B,)),
                         _dev(workspace, "workspace", dtype=workspace.dtype),
                         workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def _broyden_opts(rank, multisecant, alpha, damping, gram_reg, chunk, sketch, D):
+    if rank > 0 and sketch is None:
+        raise ValueError("a sketch [D, rank] is required for rank > 0")
+    sk = _dev(sketch, "sketch", shape=(D, rank)) if rank > 0 else None
+    return BroydenOpts(int(rank), int(bool(multisecant)), float(alpha), float(damping), float(gram_reg), int(chunk),
+                       sk)
+
+
+def deer_broyden_workspace_size(cell: Cell, B: int, T: int, rank: int = 2, multisecant: bool = False,
+                                chunk: int = 32) -> int:
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    p = cell.params()
+    o = BroydenOpts(int(rank), int(bool(multisecant)), 0.0, 0.0, 0.0, int(chunk), None)
+    _check(lib.deer_broyden_workspace_size(ctypes.byref(p), B, T, ctypes.byref(o), ctypes.byref(n)))
+    return int(n.value)
+
+
+def deer_solve_broyden(cell: Cell, x, sketch=None, s0=None, rank: int = 2, multisecant: bool = False,
+                       alpha: float = 0.0, damping: float = 0.0, gram_reg: float = 0.0, chunk: int = 32,
+                       tol: float = 1e-6, max_iter: int = 100, init_guess=None, out=None, workspace=None,
+                       stream=None):
+    """Parallel Broyden solve; returns ``(traj, iters, resid, status, rc)`` like
+    :func:`deer_solve`.  ``sketch`` is a ``[D, rank]`` CUDA tensor."""
+    import numpy as np
+    import torch
+    lib = load_library()
+    B, T, M = (int(v) for v in x.shape)
+    D = cell.D
+    if M != cell.M:
+        raise ValueError(f"x has input size {M}, the cell expects {cell.M}")
+    p = cell.params()
+    o = _broyden_opts(rank, multisecant, alpha, damping, gram_reg, chunk, sketch, D)
+    if out is None:
+        out = torch.empty((B, T, D), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = new_workspace(deer_broyden_workspace_size(cell, B, T, rank, multisecant, chunk),
+                                  device=x.device)
+    iters = np.zeros(B, np.int32)
+    resid = np.zeros(B, np.float32)
+    status = np.zeros(B, np.int32)
+    rc = lib.deer_solve_broyden(ctypes.byref(p), _dev(x, "x", shape=(B, T, M)), _dev(s0, "s0", shape=(B, D)), B, T,
+                                ctypes.byref(o), ctypes.c_float(tol), int(max_iter),
+                                _dev(init_guess, "init_guess", shape=(B, T, D)), _dev(out, "out", shape=(B, T, D)),
+                                iters.ctypes.data_as(ctypes.c_void_p), resid.ctypes.data_as(ctypes.c_void_p),
+                                status.ctypes.data_as(ctypes.c_void_p),
+                                _dev(workspace, "workspace", dtype=workspace.dtype),
+                                workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, allow_nc=True)
+    return out, iters, resid, status, rc
+
+
+def linear_scan_dplr_workspace_size(B: int, T: int, D: int, rank: int, chunk: int = 32) -> int:
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    _check(lib.linear_scan_dplr_workspace_size(B, T, D, rank, chunk, ctypes.byref(n)))
+    return int(n.value)
+
+
+def linear_scan_dplr(alpha: float, U, V, c, sketch, chunk: int = 32, out=None, workspace=None, stream=None):
+    """``delta_t = (alpha I + U_t V_t^T) delta_{t-1} + c_t`` with chunk carries
+    re-compressed; ``U, V [B,T,rank,D]``, ``c [B,T,D]``, ``sketch [D, rank]``."""
+    import torch
+    lib = load_library()
+    B, T, D = (int(v) for v in c.shape)
+    rank = int(U.shape[2])
+    if out is None:
+        out = torch.empty_like(c)
+    if workspace is None:
+        workspace = new_workspace(linear_scan_dplr_workspace_size(B, T, D, rank, chunk), device=c.device)
+    _check(lib.linear_scan_dplr(ctypes.c_float(alpha), _dev(U, "U", shape=(B, T, rank, D)),
+                                _dev(V, "V", shape=(B, T, rank, D)), _dev(c, "c"),
+                                _dev(sketch, "sketch", shape=(D, rank)), _dev(out, "out", shape=(B, T, D)),
+                                B, T, D, rank, int(chunk), _dev(workspace, "workspace", dtype=workspace.dtype),
+                                workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
 
 

@@ -220,12 +220,69 @@ int deer_lle(const deer_cell_params_t *p, const float *x, const float *s0, const
              int B, int T, double *lle_out, void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * Parallel Broyden ("Parallel Broyden Methods", sections 3.1-3.2, appendix E):
+ * quasi-Newton blocks built from trajectory secants, no Jacobian evaluated.
+ * Block at position t: A_t = alpha I + (1 - damping) U_t V_t^T with at most
+ * `rank` columns; each iteration i >= 1 folds in the secant pair
+ * (s^(i)_{t-1} - s^(i-1)_{t-1}, f^(i)_t - f^(i-1)_t) into column slot
+ * (i - 1) mod rank, by a rank-one "good Broyden" update after dropping that
+ * slot's column (multisecant = 0) or by refitting all stored secants,
+ * U = (F - alpha S)(S^T S + gram_reg I)^{-1}, V = S (multisecant = 1).  The
+ * linear step solves the increment recurrence delta_t = A_t delta_{t-1} +
+ * (f_t - s_t) by a chunked scan: chunks of `chunk` positions are replayed
+ * exactly; chunk carries go through chunk aggregates whose low-rank part is
+ * re-compressed to `rank` columns with the random sketch (range of
+ * L (R^T sketch), modified Gram-Schmidt).  Exact zeros stay exact, so the
+ * first i positions are exact after i iterations (finite-step recovery).
+ */
+typedef struct {
+    int rank;             /* columns per block, 0..8 (0: A_t = alpha I) */
+    int multisecant;      /* 0: rank-one updates with truncation; 1: multisecant refit */
+    float alpha;          /* diagonal baseline alpha I (finite) */
+    float damping;        /* in [0, 1]: the low-rank correction is scaled by 1 - damping */
+    float gram_reg;       /* >= 0, added to the diagonal of S^T S (multisecant) */
+    int chunk;            /* positions per scan chunk, 1..4096 */
+    const float *sketch;  /* device [D, rank] random sketch; may be NULL when rank = 0 (and for the size query) */
+} deer_broyden_opts_t;
+
+/* Bytes of workspace deer_solve_broyden needs (host output). */
+int deer_broyden_workspace_size(const deer_cell_params_t *p, int B, int T, const deer_broyden_opts_t *opts,
+                                size_t *bytes_out);
+
+/*
+ * Solve for the trajectory with parallel Broyden iterations.  Arguments, the
+ * stopping rule, freezing, outputs and polling are those of deer_solve; the
+ * workspace (>= deer_broyden_workspace_size bytes, 256-byte aligned) needs no
+ * zero fill.  Cells: tanh and GRU.  Iteration 0 uses A_t = alpha I.
+ */
+int deer_solve_broyden(const deer_cell_params_t *p, const float *x, const float *s0, int B, int T,
+                       const deer_broyden_opts_t *opts, float tol, int max_iter, const float *init_guess,
+                       float *traj_out, int *iters_out, float *resid_out, int *status_out, void *workspace,
+                       size_t ws_bytes, void *stream);
+
+/* Bytes of workspace linear_scan_dplr needs (host output). */
+int linear_scan_dplr_workspace_size(int B, int T, int D, int rank, int chunk, size_t *bytes_out);
+
+/*
+ * The chunked compressed scan alone: delta_t = (alpha I + U_t V_t^T) delta_{t-1} + c_t,
+ * delta_{-1} = 0, with the chunk carries re-compressed as deer_solve_broyden does.
+ *   U, V    device [B,T,rank,D] (column j of position t contiguous)
+ *   c       device [B,T,D];  delta device [B,T,D] (aliases none of the inputs)
+ *   sketch  device [D, rank];  1 <= D <= 64, 0 <= rank <= 8, 1 <= chunk <= 4096
+ */
+int linear_scan_dplr(float alpha, const float *U, const float *V, const float *c, const float *sketch,
+                     float *delta, int B, int T, int D, int rank, int chunk, void *workspace, size_t ws_bytes,
+                     void *stream);
+
+/*
  * Per-kernel timing of deer_solve, for measurement.  While enabled, deer_solve
  * records a pair of HIP events on its stream around every launch of the named
  * kernel class and accumulates the elapsed time; reading returns the number of
  * launches timed and their summed milliseconds and resets the counters.
  *   which: 0 = cell evaluation (f and Jacobian), 1 = linear scan,
- *          2 = input projection, 3 = convergence check.
+ *          2 = input projection, 3 = convergence check.  deer_solve_broyden
+ *          times its cell evaluation (0), block updates with the compressed
+ *          scan (1), projection (2) and check (3) the same way.
  */
 int deer_profile_enable(int enable);
 int deer_profile_read(int which, long long *launches, double *milliseconds);

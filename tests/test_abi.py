@@ -160,3 +160,57 @@ def test_lle_argument_checks(deer):
     assert b"T must be positive" in lib.deer_last_error()
     assert lib.deer_lle(ctypes.byref(p), fake, None, None, fake, 2, 10, out, fake, 1 << 30, None) == -1  # no traj
     assert lib.deer_lle(ctypes.byref(p), fake, None, fake, fake, 2, 10, out, None, 0, None) == -3        # workspace
+
+
+def test_broyden_argument_checks(deer):
+    lib = deer.load_library()
+    p = _params(deer, D=16, M=8)
+    fake = ctypes.c_void_p(0x1000)
+    n = ctypes.c_size_t(0)
+
+    def opts(**kw):
+        base = dict(rank=2, multisecant=0, alpha=0.5, damping=0.0, gram_reg=0.0, chunk=32, sketch=fake)
+        base.update(kw)
+        return deer.BroydenOpts(base["rank"], base["multisecant"], base["alpha"], base["damping"],
+                                base["gram_reg"], base["chunk"], base["sketch"])
+
+    o = opts(sketch=None)                        # the size query needs no sketch
+    assert lib.deer_broyden_workspace_size(ctypes.byref(p), 4, 100, ctypes.byref(o), ctypes.byref(n)) == 0
+    r2 = n.value
+    assert r2 > 0 and r2 % 256 == 0
+    o4 = opts(rank=4, sketch=None)
+    assert lib.deer_broyden_workspace_size(ctypes.byref(p), 4, 100, ctypes.byref(o4), ctypes.byref(n)) == 0
+    assert n.value > r2
+    ms = opts(rank=4, multisecant=1, sketch=None)
+    r4 = n.value
+    assert lib.deer_broyden_workspace_size(ctypes.byref(p), 4, 100, ctypes.byref(ms), ctypes.byref(n)) == 0
+    assert n.value > r4                          # the multisecant variant also keeps the df columns
+    for bad, code in ((opts(rank=9), -2), (opts(chunk=0), -1), (opts(chunk=5000), -1), (opts(damping=1.5), -1),
+                      (opts(gram_reg=-1.0), -1), (opts(alpha=float("nan")), -1)):
+        assert lib.deer_broyden_workspace_size(ctypes.byref(p), 4, 100, ctypes.byref(bad), ctypes.byref(n)) == code
+    assert lib.deer_broyden_workspace_size(ctypes.byref(p), 4, 100, None, ctypes.byref(n)) == -1
+    iters = (ctypes.c_int * 2)()
+    # the solve needs the sketch for rank > 0, and a large enough workspace
+    o = opts(sketch=None)
+    assert lib.deer_solve_broyden(ctypes.byref(p), fake, None, 2, 10, ctypes.byref(o), 1e-5, 10, None, fake,
+                                  iters, None, None, fake, 1 << 30, None) == -1
+    o = opts()
+    assert lib.deer_solve_broyden(ctypes.byref(p), fake, None, 2, 10, ctypes.byref(o), 1e-5, 10, None, fake,
+                                  iters, None, None, None, 0, None) == -3
+    assert lib.deer_solve_broyden(ctypes.byref(p), fake, None, 2, 10, ctypes.byref(o), 1e-5, -1, None, fake,
+                                  iters, None, None, fake, 1 << 30, None) == -1
+    assert lib.deer_solve_broyden(ctypes.byref(p), fake, None, 0, 10, ctypes.byref(o), 1e-5, 10, None, fake,
+                                  iters, None, None, None, 0, None) == 0          # empty batch
+    # T = 0: residual 0 passes a tolerance >= 0 at iteration 0
+    st = (ctypes.c_int * 2)()
+    assert lib.deer_solve_broyden(ctypes.byref(p), fake, None, 2, 0, ctypes.byref(o), 1e-5, 10, None, fake,
+                                  iters, None, st, None, 0, None) == 0
+    assert list(iters) == [0, 0] and list(st) == [0, 0]
+    # the standalone scan
+    assert lib.linear_scan_dplr_workspace_size(4, 100, 16, 2, 32, ctypes.byref(n)) == 0 and n.value > 0
+    assert lib.linear_scan_dplr_workspace_size(4, 100, 65, 2, 32, ctypes.byref(n)) == -2
+    assert lib.linear_scan_dplr_workspace_size(4, 100, 16, 9, 32, ctypes.byref(n)) == -2
+    assert lib.linear_scan_dplr(0.5, fake, fake, fake, None, fake, 4, 100, 16, 2, 32, fake, 1 << 30, None) == -1
+    assert lib.linear_scan_dplr(0.5, fake, fake, fake, fake, fake, 4, 100, 16, 2, 32, None, 0, None) == -3
+    assert lib.linear_scan_dplr(float("inf"), fake, fake, fake, fake, fake, 4, 100, 16, 2, 32, fake, 1 << 30,
+                                None) == -1

@@ -1,0 +1,199 @@
+"""GPU parity of the parallel Broyden path (deer_solve_broyden, linear_scan_dplr)
+against the oracle.
+
+Bars: the compressed scan matches the oracle's scan (same chunks, same sketch)
+within 1e-4 normwise relative L-infinity per sequence, exactly where the
+compression is exact it also matches dense forward substitution, and exact
+zeros stay exact; the solver's early iterates match the oracle's float32 run
+of the same algorithm within 1e-4, its converged trajectory matches the
+oracle's float64 rollout within 1e-4, the first k positions are recovered
+after k iterations, and its iteration count is within two of the oracle's
+float32 run (the re-compression's Gram-Schmidt rounds differently in the two
+float32 implementations, which can shift a run by an iteration or two).
+"""
+import numpy as np
+import pytest
+import torch
+
+from evaluation_nonlinear_rnns_amd import deer, inputs as I
+from gpu_util import device, log, rel_linf
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-4
+
+
+def _blocks(seed, B, T, m, D, scale=0.3):
+    rng = np.random.default_rng(seed)
+    U = (rng.standard_normal((B, T, m, D)) * scale).astype(np.float32)
+    V = (rng.standard_normal((B, T, m, D)) * scale).astype(np.float32)
+    c = rng.standard_normal((B, T, D)).astype(np.float32)
+    return U, V, c
+
+
+def _gpu_scan(alpha, U, V, c, sk, chunk):
+    dev = device()
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    out = deer.linear_scan_dplr(alpha, t(U), t(V), t(c), t(sk), chunk=chunk)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("B,T,D,m,chunk,alpha", [(3, 300, 7, 1, 32, 0.5), (2, 1000, 32, 2, 32, 0.6),
+                                                 (2, 777, 64, 4, 64, 0.4), (2, 129, 16, 8, 16, 0.3),
+                                                 (1, 50, 5, 3, 7, 0.9), (2, 64, 12, 2, 64, 0.5)])
+def test_dplr_scan_matches_oracle(orc, B, T, D, m, chunk, alpha):
+    U, V, c = _blocks(100 + T + D + m, B, T, m, D, scale=0.5 / np.sqrt(D) ** 0.5)
+    sk = I.broyden_sketch(7, D, m)
+    log(f"linear_scan_dplr B={B} T={T} D={D} m={m} chunk={chunk}")
+    got = _gpu_scan(alpha, U, V, c, sk, chunk)
+    ref = orc.dplr_scan(alpha, U, V, c, sk, chunk=chunk)
+    assert np.all(rel_linf(got, ref) <= TOL), rel_linf(got, ref)
+
+
+def test_dplr_scan_rank_zero(orc):
+    B, T, D = 2, 333, 9
+    rng = np.random.default_rng(4)
+    c = rng.standard_normal((B, T, D)).astype(np.float32)
+    U = np.zeros((B, T, 0, D), np.float32)
+    log("linear_scan_dplr rank 0")
+    got = _gpu_scan(0.95, U, U, c, np.zeros((D, 0), np.float32), 32)
+    ref = orc.dplr_scan(0.95, U, U, c, np.zeros((D, 0), np.float32), chunk=32)
+    assert np.all(rel_linf(got, ref) <= TOL)
+
+
+def test_dplr_scan_purely_low_rank_is_exact(orc):
+    """alpha = 0: compression exact, so the chunked result is the dense forward substitution."""
+    B, T, D, m = 2, 400, 16, 2
+    U, V, c = _blocks(9, B, T, m, D, scale=0.35)
+    sk = I.broyden_sketch(3, D, m)
+    log("linear_scan_dplr alpha=0")
+    got = _gpu_scan(0.0, U, V, c, sk, 16)
+    ref = np.zeros((B, T, D))
+    for b in range(B):
+        prev = np.zeros(D)
+        for t in range(T):
+            A = U[b, t].T.astype(np.float64) @ V[b, t].astype(np.float64)
+            prev = A @ prev + c[b, t]
+            ref[b, t] = prev
+    assert np.all(rel_linf(got, ref) <= TOL)
+
+
+def test_dplr_scan_zero_prefix_is_exact():
+    B, T, D, m = 2, 500, 24, 3
+    U, V, c = _blocks(13, B, T, m, D)
+    c[:, :200] = 0.0
+    sk = I.broyden_sketch(5, D, m)
+    log("linear_scan_dplr zero prefix")
+    got = _gpu_scan(0.7, U, V, c, sk, 32)
+    assert np.all(got[:, :200] == 0.0)
+    assert np.all(np.abs(got[:, 200]) > 0)
+
+
+# ------------------------------------------------------------------ solver
+
+def _solve(orc, p, rank, multisecant, alpha, tol, max_iter, chunk=32, damping=0.0, gram_reg=0.0, check=True):
+    dev = device()
+    cell = deer.cell_from_problem(p, dev)
+    x = torch.from_numpy(p["x"]).to(dev)
+    s0 = torch.from_numpy(p["s0"]).to(dev)
+    sk_np = I.broyden_sketch(21, p["D"], max(rank, 1))[:, :rank]
+    sk = torch.from_numpy(np.ascontiguousarray(sk_np)).to(dev) if rank > 0 else None
+    traj, iters, resid, status, rc = deer.deer_solve_broyden(cell, x, sk, s0, rank=rank, multisecant=multisecant,
+                                                             alpha=alpha, damping=damping, gram_reg=gram_reg,
+                                                             chunk=chunk, tol=tol, max_iter=max_iter)
+    torch.cuda.synchronize()
+    oc = orc.Cell.from_problem(p)
+    otraj, oit, ores, ost = orc.broyden(oc, p["x"], np.ascontiguousarray(sk_np), p["s0"], rank=rank,
+                                        multisecant=multisecant, alpha=alpha, damping=damping, gram_reg=gram_reg,
+                                        chunk=chunk, tol=tol, max_iter=max_iter, precision="f32")
+    return traj.cpu().numpy(), iters, resid, status, rc, otraj, oit, ost
+
+
+CASES = [("tanh", 2, 300, 10, 2, False, 0.5), ("tanh", 2, 1000, 32, 4, False, 0.5),
+         ("tanh", 2, 700, 16, 4, True, 0.5), ("gru", 2, 500, 16, 2, False, 0.5),
+         ("gru", 2, 1000, 64, 4, False, 0.5), ("gru", 1, 300, 32, 4, True, 0.5)]
+
+
+def _problem(cell, B, T, D):
+    if cell == "tanh":
+        return I.lowrank_tanh_problem(70 + T + D, B, T, D, D, rank=2, leak=0.5, gain=0.6)
+    p = I.gru_problem(80 + T + D, B, T, D, D, bias_std=0.3, s0_std=0.5)
+    return p
+
+
+@pytest.mark.parametrize("cell,B,T,D,rank,ms,alpha", CASES)
+def test_broyden_early_iterates_match_oracle(orc, cell, B, T, D, rank, ms, alpha):
+    """After 1, 2 and 3 iterations (tol < 0 never passes) the GPU iterate is the
+    oracle's float32 iterate of the same algorithm."""
+    p = _problem(cell, B, T, D)
+    for k in (1, 2, 3):
+        log(f"deer_solve_broyden {cell} B={B} T={T} D={D} rank={rank} ms={ms} k={k}")
+        got, iters, _, status, rc, otraj, oit, ost = _solve(orc, p, rank, ms, alpha, -1.0, k,
+                                                             gram_reg=1e-6 if ms else 0.0)
+        assert rc == deer.DEER_NOT_CONVERGED and np.all(iters == k)
+        assert np.all(rel_linf(got, otraj) <= TOL), (k, rel_linf(got, otraj))
+
+
+@pytest.mark.parametrize("cell,B,T,D,rank,ms,alpha", CASES)
+def test_broyden_solve_matches_oracle(orc, cell, B, T, D, rank, ms, alpha):
+    p = _problem(cell, B, T, D)
+    log(f"deer_solve_broyden {cell} B={B} T={T} D={D} rank={rank} ms={ms} converge")
+    got, iters, resid, status, rc, otraj, oit, ost = _solve(orc, p, rank, ms, alpha, 1e-5, 300,
+                                                         gram_reg=1e-6 if ms else 0.0)
+    assert rc == deer.DEER_OK and np.all(status == 0), (iters, resid, status)
+    oc = orc.Cell.from_problem(p)
+    ref = orc.rollout(oc, p["x"], p["s0"])
+    assert np.all(rel_linf(got, ref) <= TOL), rel_linf(got, ref)
+    assert np.all(np.abs(iters - oit) <= 2), (iters, oit)
+    assert np.all(resid <= 1e-5)
+
+
+@pytest.mark.parametrize("multisecant", [False, True])
+def test_broyden_finite_step_recovery(orc, multisecant):
+    p = _problem("tanh", 2, 400, 16)
+    oc = orc.Cell.from_problem(p)
+    ref = orc.rollout(oc, p["x"], p["s0"])
+    for k in (1, 5, 40):
+        log(f"deer_solve_broyden recovery ms={multisecant} k={k}")
+        got, iters, _, _, _, _, _, _ = _solve(orc, p, 3, multisecant, 0.5, -1.0, k, chunk=8,
+                                              gram_reg=1e-6 if multisecant else 0.0)
+        assert np.all(iters == k)
+        assert np.all(rel_linf(got[:, :k], ref[:, :k]) <= 1e-5)
+
+
+def test_broyden_rank_zero_alpha_one_is_picard(orc):
+    """No secant columns and alpha = 1: the Picard iteration, step for step."""
+    dev = device()
+    p = _problem("gru", 2, 300, 16)
+    log("deer_solve_broyden rank 0 vs picard")
+    got, iters, _, status, rc, _, oit, _ = _solve(orc, p, 0, False, 1.0, 1e-5, 400)
+    cell = deer.cell_from_problem(p, dev)
+    x = torch.from_numpy(p["x"]).to(dev)
+    s0 = torch.from_numpy(p["s0"]).to(dev)
+    _, pit, _, _, _ = deer.deer_solve(cell, x, s0, mode="picard", tol=1e-5, max_iter=400)
+    assert np.all(np.abs(iters - pit) <= 1), (iters, pit)
+    assert np.all(np.abs(iters - oit) <= 2), (iters, oit)
+
+
+def test_broyden_damping_and_workspace_reuse(orc):
+    """A caller-owned workspace is reused across calls (no zero fill needed) and
+    damping reaches the solve."""
+    dev = device()
+    p = _problem("tanh", 2, 500, 32)
+    cell = deer.cell_from_problem(p, dev)
+    x = torch.from_numpy(p["x"]).to(dev)
+    sk = torch.from_numpy(I.broyden_sketch(21, 32, 4)).to(dev)
+    ws = deer.new_workspace(deer.deer_broyden_workspace_size(cell, 2, 500, rank=4), device=dev)
+    ws.fill_(0xFF)                               # garbage must not matter
+    oc = orc.Cell.from_problem(p)
+    ref = orc.rollout(oc, p["x"])
+    for damping in (0.0, 0.3, 0.0):
+        log(f"deer_solve_broyden workspace reuse damping={damping}")
+        traj, iters, _, status, rc = deer.deer_solve_broyden(cell, x, sk, rank=4, alpha=0.5, damping=damping,
+                                                             tol=1e-5, max_iter=300, workspace=ws)
+        torch.cuda.synchronize()
+        _, oit, _, _ = orc.broyden(oc, p["x"], I.broyden_sketch(21, 32, 4), rank=4, alpha=0.5, damping=damping,
+                                   tol=1e-5, max_iter=300, precision="f32")
+        assert rc == deer.DEER_OK
+        assert np.all(rel_linf(traj.cpu().numpy(), ref) <= TOL)
+        assert np.all(np.abs(iters - oit) <= 2), (damping, iters, oit)

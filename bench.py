@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense-DEER, gain-sweep and linearisation measurements")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work for the baseline sample")
-    ap.add_argument("--only", choices=("dense", "sweep", "scan", "lin"), default=None,
+    ap.add_argument("--only", choices=("dense", "sweep", "scan", "lin", "broyden"), default=None,
                     help="run one secondary measurement alone and print its JSON (for profiling)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run a plain 1 GiB device copy (the reference kernel for HBM counter scaling)")
@@ -228,6 +228,54 @@ def dense_solve(args, dev):
             "compose_frac_of_fp32_mfma_peak": round(tflops / MFMA_F32_PEAK_TFLOPS, 4)}
 
 
+def broyden_solve(args, dev):
+    """Parallel Broyden (no Jacobian) on the GRU workload (B=16, T=65536, D=64).
+
+    Per iteration: the value-only GRU evaluation (reads s^(i) and the
+    projection, writes f^(i): 5D words per position), then the block update and
+    compressed scan in three launches -- fold (reads s^(i) and s^(i-1) at t-1,
+    f^(i) and f^(i-1), the block's U, V columns; writes the slot's two columns),
+    carry, replay (reads s^(i), f^(i) and the used columns; writes s^(i+1)).
+    Algorithmic bytes of the update + scan per position at rank m, rank-one
+    variant: fold 4D + 2mD read, 2D written; replay 2D + 2mD read, D written:
+    (9 + 4m) D words (the carry's chunk aggregates are O(1/chunk)).  The
+    multisecant variant also reads the m stored df columns and rewrites all m
+    u columns: + 2m D words.
+    """
+    import torch
+    from evaluation_nonlinear_rnns_amd import deer, inputs as I
+
+    w = I.WORKLOADS["gru_d64_t65536"]
+    p = I.workload_problem(w.name)
+    cell = deer.cell_from_problem(p, dev)
+    x = torch.from_numpy(p["x"]).to(dev)
+    out = torch.empty((w.B, w.T, w.D), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    rows = []
+    for rank, ms_, chunk in ((2, False, 32), (2, False, 64), (4, False, 64), (4, True, 64)):
+        sk = torch.from_numpy(I.broyden_sketch(21, w.D, rank)).to(dev)
+        ws = deer.new_workspace(deer.deer_broyden_workspace_size(cell, w.B, w.T, rank, ms_, chunk), device=dev)
+
+        def step():
+            return deer.deer_solve_broyden(cell, x, sk, rank=rank, multisecant=ms_, alpha=0.5,
+                                           gram_reg=1e-6 if ms_ else 0.0, chunk=chunk, tol=w.tol,
+                                           max_iter=w.max_iter, out=out, workspace=ws, stream=stream)
+
+        ms, prof, res = _time_solves(step, 2, stream)
+        _, iters, _, status, rc = res
+        n_s, ms_s = prof[deer.PROFILE_SCAN]
+        n_e, ms_e = prof[deer.PROFILE_EVAL]
+        step_ms = ms_s / max(n_s, 1)
+        nbytes = (9 + 4 * rank + (2 * rank if ms_ else 0)) * w.D * 4 * w.B * w.T
+        rows.append({"rank": rank, "multisecant": ms_, "chunk": chunk, "alpha": 0.5, "rc": int(rc),
+                     "iterations": sorted(set(int(v) for v in iters)), "ms_per_solve": round(ms, 3),
+                     "B*T/s": round(w.B * w.T / (ms * 1e-3), 1), "eval_avg_ms": round(ms_e / max(n_e, 1), 4),
+                     "update_scan_avg_ms": round(step_ms, 4), "update_scan_bytes": nbytes,
+                     "update_scan_GBs": round(nbytes / (step_ms * 1e-3) / 1e9, 1)})
+        del ws
+    return {"workload": w.name, "B": w.B, "T": w.T, "D": w.D, "tol": w.tol, "runs": rows}
+
+
 def gain_sweep(args, dev):
     """Dense DEER against the sequential GPU rollout across the recurrent gain g.
 
@@ -369,7 +417,8 @@ def main():
         del src, dst
 
     if args.only:
-        fn = {"dense": dense_solve, "sweep": gain_sweep, "scan": scan_bandwidth, "lin": linearizations}[args.only]
+        fn = {"dense": dense_solve, "sweep": gain_sweep, "scan": scan_bandwidth, "lin": linearizations,
+              "broyden": broyden_solve}[args.only]
         print(json.dumps({args.only: fn(args, dev)}), flush=True)
         return
 
@@ -403,6 +452,7 @@ def main():
         line["dense_deer"] = dense_solve(args, dev)
         line["gain_sweep"] = gain_sweep(args, dev)
         line["linearizations"] = linearizations(args, dev)
+        line["broyden"] = broyden_solve(args, dev)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(args, w, p)
     print(json.dumps(line), flush=True)

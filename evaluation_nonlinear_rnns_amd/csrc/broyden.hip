@@ -42,11 +42,28 @@ constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / 64;
 constexpr float kQrDrop = 1e-5f;
 
+// DPP move of v; lanes outside ROWMASK (rows of 16 lanes) read 0.
+template <int CTRL, int ROWMASK = 0xF>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWMASK, 0xF,
+                                                                 false));
+}
+
+// Sum over the 64 lanes, the same value on every lane: pairs and quads
+// (quad_perm), halves of a row (row_half_mirror), rows (row_mirror), then the
+// row totals are chained into row 3 (row_bcast:15 into rows 1 and 3,
+// row_bcast:31 into rows 2 and 3) and lane 63's total is broadcast.  The
+// order of the additions is fixed, so every call rounds the same way.
 __device__ __forceinline__ float wsum(float v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+    v += dpp<0xB1>(v);          // quad_perm [1, 0, 3, 2]
+    v += dpp<0x4E>(v);          // quad_perm [2, 3, 0, 1]
+    v += dpp<0x141>(v);         // row_half_mirror
+    v += dpp<0x140>(v);         // row_mirror
+    v += dpp<0x142, 0xA>(v);    // row_bcast:15
+    v += dpp<0x143, 0xC>(v);    // row_bcast:31
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 __device__ __forceinline__ float ld(const float *p, bool ok) { return ok ? *p : 0.0f; }
@@ -185,28 +202,71 @@ __global__ __launch_bounds__(kThreads) void dplr_fold_kernel(DplrArgs a)
 #pragma unroll
     for (int j = 0; j < MR; ++j) PL[j] = PR[j] = 0.0f;
 
-    for (int t = t0; t < t1; ++t) {
-        const size_t pos = seq + t;
+    // inputs of position t, loaded one position ahead of their use (clamped,
+    // always-valid addresses; lanes past D and columns past m read as zero)
+    const int l = min(lane, D - 1);
+    struct In {
         float u[MR], v[MR], fs[MR];
-        float *Up = a.U + pos * m * D + lane, *Vp = a.V + pos * m * D + lane;
-        float *Fp = a.F ? a.F + pos * m * D + lane : nullptr;
+        float sc, fc, fp, sp;       // s^(i)_t, f^(i)_t, f^(i-1)_t, s^(i-1)_{t-1} (or c_t standalone)
+    };
+    auto load_in = [&](int t, In &in) {
+        const size_t pos = seq + min(t, a.T - 1);
 #pragma unroll
         for (int j = 0; j < MR; ++j) {
-            const bool have = row && j < m;
-            u[j] = ld(Up + j * D, have);
-            v[j] = ld(Vp + j * D, have);
-            fs[j] = (Fp && a.multisecant) ? ld(Fp + j * D, have) : 0.0f;
+            in.u[j] = in.v[j] = in.fs[j] = 0.0f;
+            if (m > 0) {
+                const size_t o = (pos * m + min(j, m - 1)) * D + l;
+                const bool have = row && j < m;
+                const float uu = a.U[o], vv = a.V[o];
+                in.u[j] = have ? uu : 0.0f;
+                in.v[j] = have ? vv : 0.0f;
+                if (a.multisecant) {
+                    const float ff = a.F[o];
+                    in.fs[j] = have ? ff : 0.0f;
+                }
+            }
         }
+        if (a.ctl) {
+            const float sc = sv.s_cur[pos * D + l], fc = sv.f_cur[pos * D + l];
+            in.sc = row ? sc : 0.0f;
+            in.fc = row ? fc : 0.0f;
+            in.fp = in.sp = 0.0f;
+            if (sv.update) {
+                const float fp = sv.f_prev[pos * D + l];
+                const float sp = sv.s_prev[(pos - (t > 0 ? 1 : 0)) * D + l];
+                in.fp = row ? fp : 0.0f;
+                in.sp = (row && t > 0) ? sp : 0.0f;
+            }
+        } else {
+            const float cc = a.c[pos * D + l];
+            in.sc = row ? cc : 0.0f;
+            in.fc = in.fp = in.sp = 0.0f;
+        }
+    };
+    // s^(i)_{t0-1}: the first ds of the chunk
+    float s_before = 0.0f;
+    if (a.ctl && sv.update && t0 > 0) {
+        const float v0 = sv.s_cur[(seq + t0 - 1) * D + l];
+        s_before = row ? v0 : 0.0f;
+    }
+    In cur;
+    load_in(t0, cur);
+    for (int t = t0; t < t1; ++t) {
+        const size_t pos = seq + t;
+        In nxt;
+        load_in(t + 1, nxt);                        // clamped past the chunk: harmless extra load
+        float(&u)[MR] = cur.u;
+        float(&v)[MR] = cur.v;
+        float(&fs)[MR] = cur.fs;
         float c;
         if (a.ctl) {
-            const float fc = ld(sv.f_cur + pos * D + lane, row);
-            c = fc - ld(sv.s_cur + pos * D + lane, row);
+            c = cur.fc - cur.sc;
             if (sv.update) {
-                float ds = 0.0f;
-                if (t > 0) ds = ld(sv.s_cur + (pos - 1) * D + lane, row) - ld(sv.s_prev + (pos - 1) * D + lane, row);
-                const float df = fc - ld(sv.f_prev + pos * D + lane, row);
-                block_update<MR>(a, sv.i, ds, df, u, v, fs);
+                const float ds = (t > 0) ? s_before - cur.sp : 0.0f;
+                const float df = cur.fc - cur.fp;
+                block_update<MR>(a, sv.i, ds, df, cur.u, cur.v, cur.fs);
                 if (row) {
+                    float *Up = a.U + pos * m * D + lane, *Vp = a.V + pos * m * D + lane;
                     if (a.multisecant) {
 #pragma unroll
                         for (int j = 0; j < MR; ++j)
@@ -218,14 +278,18 @@ __global__ __launch_bounds__(kThreads) void dplr_fold_kernel(DplrArgs a)
                         if (j == slot) {
                             if (!a.multisecant) Up[j * D] = u[j];
                             Vp[j * D] = v[j];
-                            if (a.multisecant) Fp[j * D] = fs[j];
+                            if (a.multisecant) a.F[pos * m * D + lane + j * D] = fs[j];
                         }
                 }
             }
+            s_before = cur.sc;
         } else {
-            c = ld(a.c + pos * D + lane, row);
+            c = cur.sc;
         }
-        if (last) continue;                         // the last chunk only updates its blocks
+        if (last) {                                 // the last chunk only updates its blocks
+            cur = nxt;
+            continue;
+        }
 #pragma unroll
         for (int j = 0; j < MR; ++j) u[j] *= a.shrink;
 
@@ -293,6 +357,7 @@ __global__ __launch_bounds__(kThreads) void dplr_fold_kernel(DplrArgs a)
             r = m;
         }
         Pb = dplr_apply<MR>(a.alpha, u, v, n, Pb) + c;
+        cur = nxt;
     }
     if (last || !row) return;
     const size_t agg = static_cast<size_t>(bseq) * a.nchunk + q;
@@ -321,22 +386,44 @@ __global__ __launch_bounds__(kThreads) void dplr_carry_kernel(DplrArgs a)
     if (!solver_view(a, bseq, sv)) return;
     const int D = a.D, m = a.m;
     const bool row = lane < D;
-    float e = 0.0f;
-    for (int q = 0; q < a.nchunk; ++q) {
-        const size_t agg = static_cast<size_t>(bseq) * a.nchunk + q;
-        if (row) a.entry[agg * D + lane] = e;
-        if (q == a.nchunk - 1) break;
-        const float p = a.agg_p[agg];
-        const int r = a.agg_r[agg];
-        float ne = p * e;
+    const size_t base = static_cast<size_t>(bseq) * a.nchunk;
+    const int nq = a.nchunk - 1;                 // aggregates in the chain
+    // ring of the next kPF aggregates, loaded ahead of the dependent chain
+    constexpr int kPF = 8;
+    float rl[kPF][MR], rrr[kPF][MR], rb[kPF], rp[kPF];
+    int rk[kPF];
+    auto fetch = [&](int q, float (&L)[MR], float (&R)[MR], float &b, float &p, int &r) {
+        const int qq = min(q, max(nq - 1, 0));   // clamped: always a valid address
+        const size_t agg = base + qq;
+        p = a.agg_p[agg];
+        r = a.agg_r[agg];
+        b = ld(a.agg_b + agg * D + lane, row);
 #pragma unroll
-        for (int j = 0; j < MR; ++j)
-            if (j < r) {
-                const float rj = ld(a.agg_R + (agg * m + j) * D + lane, row);
-                const float lj = ld(a.agg_L + (agg * m + j) * D + lane, row);
-                ne += lj * wsum(rj * e);
-            }
-        e = ne + ld(a.agg_b + agg * D + lane, row);
+        for (int j = 0; j < MR; ++j) {
+            const bool have = row && j < m;
+            L[j] = ld(a.agg_L + (agg * m + j) * D + lane, have);
+            R[j] = ld(a.agg_R + (agg * m + j) * D + lane, have);
+        }
+    };
+    float e = 0.0f;
+    if (nq > 0) {
+#pragma unroll
+        for (int k = 0; k < kPF; ++k) fetch(k, rl[k], rrr[k], rb[k], rp[k], rk[k]);
+    }
+    for (int q0 = 0; q0 <= nq; q0 += kPF) {
+#pragma unroll
+        for (int k = 0; k < kPF; ++k) {
+            const int q = q0 + k;
+            if (q > nq) break;
+            if (row) a.entry[(base + q) * D + lane] = e;
+            if (q == nq) break;
+            float ne = rp[k] * e;
+#pragma unroll
+            for (int j = 0; j < MR; ++j)
+                if (j < rk[k]) ne += rl[k][j] * wsum(rrr[k][j] * e);
+            e = ne + rb[k];
+            fetch(q + kPF, rl[k], rrr[k], rb[k], rp[k], rk[k]);
+        }
     }
 }
 
@@ -355,27 +442,46 @@ __global__ __launch_bounds__(kThreads) void dplr_replay_kernel(DplrArgs a)
     const int t0 = q * a.chunk, t1 = min(t0 + a.chunk, a.T);
     const size_t seq = static_cast<size_t>(bseq) * a.T;
     float dl = ld(a.entry + (static_cast<size_t>(bseq) * a.nchunk + q) * D + lane, row);
-    for (int t = t0; t < t1; ++t) {
-        const size_t pos = seq + t;
+    const int l = min(lane, D - 1);
+    struct In {
         float u[MR], v[MR];
+        float sc, c;
+    };
+    auto load_in = [&](int t, In &in) {
+        const size_t pos = seq + min(t, a.T - 1);
 #pragma unroll
         for (int j = 0; j < MR; ++j) {
-            const bool have = row && j < n;
-            u[j] = ld(a.U + (pos * m + j) * D + lane, have) * a.shrink;
-            v[j] = ld(a.V + (pos * m + j) * D + lane, have);
+            in.u[j] = in.v[j] = 0.0f;
+            if (n > 0) {
+                const size_t o = (pos * m + min(j, n - 1)) * D + l;
+                const bool have = row && j < n;
+                const float uu = a.U[o], vv = a.V[o];
+                in.u[j] = have ? uu * a.shrink : 0.0f;
+                in.v[j] = have ? vv : 0.0f;
+            }
         }
-        float c, sc = 0.0f;
         if (a.ctl) {
-            sc = ld(sv.s_cur + pos * D + lane, row);
-            c = ld(sv.f_cur + pos * D + lane, row) - sc;
+            const float sc = sv.s_cur[pos * D + l], fc = sv.f_cur[pos * D + l];
+            in.sc = row ? sc : 0.0f;
+            in.c = row ? fc - sc : 0.0f;
         } else {
-            c = ld(a.c + pos * D + lane, row);
+            const float cc = a.c[pos * D + l];
+            in.sc = 0.0f;
+            in.c = row ? cc : 0.0f;
         }
-        dl = dplr_apply<MR>(a.alpha, u, v, n, dl) + c;
+    };
+    In cur;
+    load_in(t0, cur);
+    for (int t = t0; t < t1; ++t) {
+        const size_t pos = seq + t;
+        In nxt;
+        load_in(t + 1, nxt);
+        dl = dplr_apply<MR>(a.alpha, cur.u, cur.v, n, dl) + cur.c;
         if (row) {
-            if (a.ctl) sv.s_next[pos * D + lane] = sc + dl;
+            if (a.ctl) sv.s_next[pos * D + lane] = cur.sc + dl;
             else a.out[pos * D + lane] = dl;
         }
+        cur = nxt;
     }
 }
 

@@ -209,39 +209,45 @@ __global__ __launch_bounds__(kThreads) void dplr_fold_kernel(DplrArgs a)
         float u[MR], v[MR], fs[MR];
         float sc, fc, fp, sp;       // s^(i)_t, f^(i)_t, f^(i-1)_t, s^(i-1)_{t-1} (or c_t standalone)
     };
+    // Branch-free loads: every source is a valid [B,T,...] buffer (an unused one
+    // stands in where a mode reads nothing), so the loads stay in flight.
+    const float *src_s = a.ctl ? sv.s_cur : a.c;
+    const float *src_f = a.ctl ? sv.f_cur : a.c;
+    const float *src_fp = a.ctl ? sv.f_prev : a.c;
+    const float *src_sp = a.ctl ? sv.s_prev : a.c;
+    const float *src_u = m > 0 ? a.U : src_s;
+    const float *src_v = m > 0 ? a.V : src_s;
+    const float *src_F = (m > 0 && a.multisecant) ? a.F : src_v;
+    const int mm = max(m, 1);
     auto load_in = [&](int t, In &in) {
         const size_t pos = seq + min(t, a.T - 1);
 #pragma unroll
         for (int j = 0; j < MR; ++j) {
-            in.u[j] = in.v[j] = in.fs[j] = 0.0f;
-            if (m > 0) {
-                const size_t o = (pos * m + min(j, m - 1)) * D + l;
-                const bool have = row && j < m;
-                const float uu = a.U[o], vv = a.V[o];
-                in.u[j] = have ? uu : 0.0f;
-                in.v[j] = have ? vv : 0.0f;
-                if (a.multisecant) {
-                    const float ff = a.F[o];
-                    in.fs[j] = have ? ff : 0.0f;
-                }
-            }
+            const size_t o = m > 0 ? (pos * m + min(j, mm - 1)) * D + l : pos * D + l;
+            in.u[j] = src_u[o];
+            in.v[j] = src_v[o];
+            in.fs[j] = src_F[o];
         }
-        if (a.ctl) {
-            const float sc = sv.s_cur[pos * D + l], fc = sv.f_cur[pos * D + l];
-            in.sc = row ? sc : 0.0f;
-            in.fc = row ? fc : 0.0f;
-            in.fp = in.sp = 0.0f;
-            if (sv.update) {
-                const float fp = sv.f_prev[pos * D + l];
-                const float sp = sv.s_prev[(pos - (t > 0 ? 1 : 0)) * D + l];
-                in.fp = row ? fp : 0.0f;
-                in.sp = (row && t > 0) ? sp : 0.0f;
-            }
-        } else {
-            const float cc = a.c[pos * D + l];
-            in.sc = row ? cc : 0.0f;
-            in.fc = in.fp = in.sp = 0.0f;
+        in.sc = src_s[pos * D + l];
+        in.fc = src_f[pos * D + l];
+        in.fp = src_fp[pos * D + l];
+        in.sp = src_sp[(pos - (t > 0 ? 1 : 0)) * D + l];
+    };
+    // Values are masked when a position is consumed, not when it is loaded, so
+    // the loads of the next position stay in flight: lanes past D and columns
+    // past m become zero.
+    auto mask_in = [&](In &in) {
+#pragma unroll
+        for (int j = 0; j < MR; ++j) {
+            const bool have = row && j < m;
+            in.u[j] = have ? in.u[j] : 0.0f;
+            in.v[j] = have ? in.v[j] : 0.0f;
+            in.fs[j] = have ? in.fs[j] : 0.0f;
         }
+        in.sc = row ? in.sc : 0.0f;
+        in.fc = row ? in.fc : 0.0f;
+        in.fp = row ? in.fp : 0.0f;
+        in.sp = row ? in.sp : 0.0f;
     };
     // s^(i)_{t0-1}: the first ds of the chunk
     float s_before = 0.0f;
@@ -255,6 +261,7 @@ __global__ __launch_bounds__(kThreads) void dplr_fold_kernel(DplrArgs a)
         const size_t pos = seq + t;
         In nxt;
         load_in(t + 1, nxt);                        // clamped past the chunk: harmless extra load
+        mask_in(cur);
         float(&u)[MR] = cur.u;
         float(&v)[MR] = cur.v;
         float(&fs)[MR] = cur.fs;
@@ -392,17 +399,20 @@ __global__ __launch_bounds__(kThreads) void dplr_carry_kernel(DplrArgs a)
     constexpr int kPF = 8;
     float rl[kPF][MR], rrr[kPF][MR], rb[kPF], rp[kPF];
     int rk[kPF];
+    // unconditional loads at clamped, always-valid addresses (a load under a
+    // divergent branch would make every later wait drain the whole ring)
+    const int l = min(lane, D - 1);
     auto fetch = [&](int q, float (&L)[MR], float (&R)[MR], float &b, float &p, int &r) {
-        const int qq = min(q, max(nq - 1, 0));   // clamped: always a valid address
+        const int qq = min(q, max(nq - 1, 0));
         const size_t agg = base + qq;
         p = a.agg_p[agg];
         r = a.agg_r[agg];
-        b = ld(a.agg_b + agg * D + lane, row);
+        b = a.agg_b[agg * D + l];
 #pragma unroll
         for (int j = 0; j < MR; ++j) {
-            const bool have = row && j < m;
-            L[j] = ld(a.agg_L + (agg * m + j) * D + lane, have);
-            R[j] = ld(a.agg_R + (agg * m + j) * D + lane, have);
+            const size_t o = m > 0 ? (agg * m + min(j, m - 1)) * D + l : agg * D + l;
+            L[j] = (m > 0 ? a.agg_L : a.agg_b)[o];
+            R[j] = (m > 0 ? a.agg_R : a.agg_b)[o];
         }
     };
     float e = 0.0f;
@@ -417,11 +427,17 @@ __global__ __launch_bounds__(kThreads) void dplr_carry_kernel(DplrArgs a)
             if (q > nq) break;
             if (row) a.entry[(base + q) * D + lane] = e;
             if (q == nq) break;
+            // lanes past D hold copies of lane D - 1; e is zero there, so they add nothing
+            // every column is computed and the unused ones are selected away (no
+            // branches, so the ring's loads stay in flight across steps)
             float ne = rp[k] * e;
 #pragma unroll
-            for (int j = 0; j < MR; ++j)
-                if (j < rk[k]) ne += rl[k][j] * wsum(rrr[k][j] * e);
-            e = ne + rb[k];
+            for (int j = 0; j < MR; ++j) {
+                const bool use = j < rk[k];
+                const float w = wsum(use ? rrr[k][j] * e : 0.0f);
+                ne += use ? rl[k][j] * w : 0.0f;
+            }
+            e = row ? ne + rb[k] : 0.0f;
             fetch(q + kPF, rl[k], rrr[k], rb[k], rp[k], rk[k]);
         }
     }
@@ -447,28 +463,21 @@ __global__ __launch_bounds__(kThreads) void dplr_replay_kernel(DplrArgs a)
         float u[MR], v[MR];
         float sc, c;
     };
+    const float *src_s = a.ctl ? sv.s_cur : a.c;
+    const float *src_c = a.ctl ? sv.f_cur : a.c;
+    const float *src_u = n > 0 ? a.U : src_s;
+    const float *src_v = n > 0 ? a.V : src_s;
+    const int nn = max(n, 1);
     auto load_in = [&](int t, In &in) {
         const size_t pos = seq + min(t, a.T - 1);
 #pragma unroll
         for (int j = 0; j < MR; ++j) {
-            in.u[j] = in.v[j] = 0.0f;
-            if (n > 0) {
-                const size_t o = (pos * m + min(j, n - 1)) * D + l;
-                const bool have = row && j < n;
-                const float uu = a.U[o], vv = a.V[o];
-                in.u[j] = have ? uu * a.shrink : 0.0f;
-                in.v[j] = have ? vv : 0.0f;
-            }
+            const size_t o = n > 0 ? (pos * m + min(j, nn - 1)) * D + l : pos * D + l;
+            in.u[j] = src_u[o];
+            in.v[j] = src_v[o];
         }
-        if (a.ctl) {
-            const float sc = sv.s_cur[pos * D + l], fc = sv.f_cur[pos * D + l];
-            in.sc = row ? sc : 0.0f;
-            in.c = row ? fc - sc : 0.0f;
-        } else {
-            const float cc = a.c[pos * D + l];
-            in.sc = 0.0f;
-            in.c = row ? cc : 0.0f;
-        }
+        in.sc = src_s[pos * D + l];
+        in.c = src_c[pos * D + l];            // f in the solver; c = f - s once consumed
     };
     In cur;
     load_in(t0, cur);
@@ -476,7 +485,15 @@ __global__ __launch_bounds__(kThreads) void dplr_replay_kernel(DplrArgs a)
         const size_t pos = seq + t;
         In nxt;
         load_in(t + 1, nxt);
-        dl = dplr_apply<MR>(a.alpha, cur.u, cur.v, n, dl) + cur.c;
+#pragma unroll
+        for (int j = 0; j < MR; ++j) {
+            const bool have = row && j < n;
+            cur.u[j] = have ? cur.u[j] * a.shrink : 0.0f;
+            cur.v[j] = have ? cur.v[j] : 0.0f;
+        }
+        const float c = row ? (a.ctl ? cur.c - cur.sc : cur.c) : 0.0f;
+        cur.sc = row ? cur.sc : 0.0f;
+        dl = dplr_apply<MR>(a.alpha, cur.u, cur.v, n, dl) + c;
         if (row) {
             if (a.ctl) sv.s_next[pos * D + lane] = cur.sc + dl;
             else a.out[pos * D + lane] = dl;

@@ -10,7 +10,12 @@ its rebuttal), and the gap between the oracle's float32 and float64 rollouts
 with the predictability horizon (the last step at which that gap stays within
 1e-5).  These full sizes take minutes on a CPU, which is why they are stored.
 
-Usage: python tests/golden/make_golden.py [workload ...]
+The record ``broyden_gru_d64_t65536`` holds the float32 iteration counts of the
+oracle's parallel Broyden run on the GRU workload in the configuration the
+benchmark times (rank 2, rank-one updates, alpha 0.5, chunks of 64 positions,
+sketch seed 21).
+
+Usage: python tests/golden/make_golden.py [workload ... | broyden]
 """
 import json
 import os
@@ -67,6 +72,26 @@ def run_one(name, gain=None):
     return rec
 
 
+BROYDEN = {"rank": 2, "multisecant": False, "alpha": 0.5, "chunk": 64, "sketch_seed": 21}
+
+
+def run_broyden():
+    w = I.WORKLOADS["gru_d64_t65536"]
+    p = I.workload_problem(w.name)
+    c = O.Cell.from_problem(p)
+    sk = I.broyden_sketch(BROYDEN["sketch_seed"], w.D, BROYDEN["rank"])
+    t0 = time.time()
+    _, iters, resid, status = O.broyden(c, p["x"], sk, p["s0"], rank=BROYDEN["rank"],
+                                        multisecant=BROYDEN["multisecant"], alpha=BROYDEN["alpha"],
+                                        chunk=BROYDEN["chunk"], tol=w.tol, max_iter=w.max_iter, precision="f32")
+    t1 = time.time()
+    print(f"broyden {w.name}: iters {min(iters)}..{max(iters)}, status {sorted(set(int(v) for v in status))}, "
+          f"{t1 - t0:.1f}s", flush=True)
+    return dict(BROYDEN, workload=w.name, tol=w.tol, max_iter=w.max_iter, iters_f32=[int(v) for v in iters],
+                resid_f32=[float(v) for v in resid], status_f32=[int(v) for v in status],
+                seconds_broyden_f32=round(t1 - t0, 2))
+
+
 def main(argv):
     names = argv or ["tanh_d4_t1024", "gru_d64_t65536", "tanh_d32_t16384", "tanh_d16_t4096_sweep"]
     data = {}
@@ -76,6 +101,11 @@ def main(argv):
     data["_about"] = ("Oracle reference values for the full-size workloads, written by "
                       "tests/golden/make_golden.py from oracle/ only.")
     for name in names:
+        if name == "broyden":
+            data["broyden_gru_d64_t65536"] = run_broyden()
+            with open(OUT, "w") as f:
+                json.dump(data, f, indent=1)
+            continue
         w = I.WORKLOADS[name]
         if w.gains:
             data[name] = {f"{g:g}": run_one(name, gain=g) for g in w.gains}

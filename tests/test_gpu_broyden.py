@@ -197,3 +197,85 @@ def test_broyden_damping_and_workspace_reuse(orc):
         assert rc == deer.DEER_OK
         assert np.all(rel_linf(traj.cpu().numpy(), ref) <= TOL)
         assert np.all(np.abs(iters - oit) <= 2), (damping, iters, oit)
+
+
+# ------------------------------------------------------------ full size and edges
+
+def test_full_gru_broyden(orc):
+    """The benchmark's configuration on the full GRU workload (B=16, T=65536,
+    D=64): converged; iteration counts within two of the oracle's float32 run
+    (stored by tests/golden/make_golden.py); sampled sequences match the
+    oracle's float64 rollout."""
+    import json
+    import os
+    gold = json.load(open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                                       "oracle_full_workloads.json")))["broyden_gru_d64_t65536"]
+    dev = device()
+    w = I.WORKLOADS["gru_d64_t65536"]
+    p = I.workload_problem(w.name)
+    cell = deer.cell_from_problem(p, dev)
+    x = torch.from_numpy(p["x"]).to(dev)
+    sk = torch.from_numpy(I.broyden_sketch(gold["sketch_seed"], w.D, gold["rank"])).to(dev)
+    log("deer_solve_broyden full gru_d64_t65536")
+    traj, iters, resid, status, rc = deer.deer_solve_broyden(cell, x, sk, rank=gold["rank"],
+                                                             multisecant=gold["multisecant"], alpha=gold["alpha"],
+                                                             chunk=gold["chunk"], tol=w.tol, max_iter=w.max_iter)
+    torch.cuda.synchronize()
+    assert rc == deer.DEER_OK and np.all(status == 0)
+    assert np.all(np.abs(iters - np.asarray(gold["iters_f32"])) <= 2), (iters, gold["iters_f32"])
+    seqs = [0, 7, 15]
+    ref = orc.rollout(orc.Cell.from_problem(p), p["x"][seqs])
+    assert np.all(rel_linf(traj[seqs].cpu().numpy(), ref) <= TOL)
+
+
+@pytest.mark.parametrize("T,D,chunk", [(1, 8, 32), (32, 8, 32), (33, 8, 32), (100, 1, 16), (257, 3, 64)])
+def test_broyden_edge_sizes(orc, T, D, chunk):
+    """One position, exactly one chunk, one more than a chunk, a scalar state,
+    and a ragged last chunk."""
+    p = I.lowrank_tanh_problem(90 + T + D, 2, T, D, D, rank=1, leak=0.5, gain=0.6)
+    for ms in (False, True):
+        log(f"deer_solve_broyden edge T={T} D={D} chunk={chunk} ms={ms}")
+        got, iters, resid, status, rc, otraj, oit, ost = _solve(orc, p, 2, ms, 0.5, 1e-6, 300, chunk=chunk,
+                                                             gram_reg=1e-6 if ms else 0.0)
+        assert rc == deer.DEER_OK and np.all(status == 0)
+        ref = orc.rollout(orc.Cell.from_problem(p), p["x"], p["s0"])
+        assert np.all(rel_linf(got, ref) <= TOL)
+        assert np.all(np.abs(iters - oit) <= 2), (iters, oit)
+        if T == 1:
+            assert np.all(iters == 1)                # one step recovers the only state
+
+
+def test_broyden_rank_eight_and_init_guess(orc):
+    """Rank 8 (the largest), and a start from the converged trajectory, which
+    passes at iteration 0."""
+    dev = device()
+    p = _problem("gru", 2, 600, 32)
+    log("deer_solve_broyden rank 8")
+    got, iters, resid, status, rc, otraj, oit, ost = _solve(orc, p, 8, False, 0.5, 1e-5, 300)
+    assert rc == deer.DEER_OK and np.all(status == 0)
+    assert np.all(np.abs(iters - oit) <= 2), (iters, oit)
+    ref = orc.rollout(orc.Cell.from_problem(p), p["x"], p["s0"])
+    assert np.all(rel_linf(got, ref) <= TOL)
+    cell = deer.cell_from_problem(p, dev)
+    x = torch.from_numpy(p["x"]).to(dev)
+    s0 = torch.from_numpy(p["s0"]).to(dev)
+    sk = torch.from_numpy(I.broyden_sketch(21, 32, 8)).to(dev)
+    init = torch.from_numpy(got).to(dev)
+    log("deer_solve_broyden from the solution")
+    traj, it2, _, st2, rc2 = deer.deer_solve_broyden(cell, x, sk, s0, rank=8, alpha=0.5, tol=1e-5, max_iter=300,
+                                                     init_guess=init)
+    torch.cuda.synchronize()
+    assert rc2 == deer.DEER_OK and np.all(it2 == 0)
+    assert np.array_equal(traj.cpu().numpy(), got)
+
+
+def test_broyden_many_sequences(orc):
+    """More sequences than one workgroup's worth of wavefronts, with sequences
+    stopping at different iterations."""
+    p = I.gru_problem(93, 300, 80, 8, 4, bias_std=0.3, s0_std=0.5)
+    log("deer_solve_broyden B=300")
+    got, iters, resid, status, rc, otraj, oit, ost = _solve(orc, p, 2, False, 0.5, 1e-5, 100, chunk=16)
+    assert rc == deer.DEER_OK and np.all(status == 0)
+    assert np.all(np.abs(iters - oit) <= 2)
+    ref = orc.rollout(orc.Cell.from_problem(p), p["x"], p["s0"])
+    assert np.all(rel_linf(got, ref) <= TOL)

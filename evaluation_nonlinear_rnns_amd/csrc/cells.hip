@@ -326,9 +326,13 @@ unsigned eval_blocks(int B, int T, int &tiles)
 
 }  // namespace
 
+// The matrix-core evaluation kernels read the tiled projection in whole tiles
+// of up to 128 positions (4 blocks of 32 positions x O outputs): the last
+// sequence's last tile may reach 3 blocks past its data, so 3 blocks of slack
+// follow the array (read, never used).
 size_t projection_floats(int B, int T, int O)
 {
-    return std::max(static_cast<size_t>(B) * T * O, proj_tiled_floats(B, T, O));
+    return std::max(static_cast<size_t>(B) * T * O, proj_tiled_floats(B, T, O)) + 3 * 32 * static_cast<size_t>(O);
 }
 
 bool gru_fast_path(int D, int M) { return gru_mfma_supported(D) && proj_mfma_supported(M, 3 * D); }

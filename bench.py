@@ -252,7 +252,7 @@ def broyden_solve(args, dev):
     out = torch.empty((w.B, w.T, w.D), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     rows = []
-    for rank, ms_, chunk in ((2, False, 32), (2, False, 64), (4, False, 64), (4, True, 64)):
+    for rank, ms_, chunk in ((2, False, 64), (2, False, 128), (4, False, 128), (4, True, 128), (8, False, 128)):
         sk = torch.from_numpy(I.broyden_sketch(21, w.D, rank)).to(dev)
         ws = deer.new_workspace(deer.deer_broyden_workspace_size(cell, w.B, w.T, rank, ms_, chunk), device=dev)
 

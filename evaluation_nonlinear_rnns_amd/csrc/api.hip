@@ -335,20 +335,14 @@ struct BroydenLayout {
     float *f_even = nullptr, *f_odd = nullptr;   // f^(i) by parity [B,T,D]
     float *proj = nullptr;              // input projection
     float *U = nullptr, *V = nullptr, *F = nullptr;   // [B,T,m,D]
-    float *agg_p = nullptr;
-    int *agg_r = nullptr;
-    float *agg_L = nullptr, *agg_R = nullptr, *agg_b = nullptr, *entry = nullptr;
+    float *agg = nullptr, *entry = nullptr;   // chunk aggregate records, carried entries
     size_t bytes = 0;
 };
 
 void carve_dplr_scan(Carve &c, BroydenLayout &L, int B, int T, int D, int m, int chunk)
 {
     const size_t nch = static_cast<size_t>(B) * ((T + chunk - 1) / chunk);
-    L.agg_p = c.take<float>(nch);
-    L.agg_r = c.take<int>(nch);
-    L.agg_L = c.take<float>(nch * m * D);
-    L.agg_R = c.take<float>(nch * m * D);
-    L.agg_b = c.take<float>(nch * D);
+    L.agg = c.take<float>(nch * dplr_record_floats(m, D));
     L.entry = c.take<float>(nch * D);
 }
 
@@ -748,7 +742,7 @@ int deer_solve_broyden(const deer_cell_params_t *p, const float *x, const float 
     a.U = L.U; a.V = L.V; a.F = L.F;
     a.s0 = s0; a.s_even = traj_out; a.s_odd = L.buf1; a.f_even = L.f_even; a.f_odd = L.f_odd;
     a.ctl = L.ctl; a.skip = L.done;
-    a.agg_p = L.agg_p; a.agg_r = L.agg_r; a.agg_L = L.agg_L; a.agg_R = L.agg_R; a.agg_b = L.agg_b;
+    a.agg = L.agg;
     a.entry = L.entry;
 
     const int *sel = &L.ctl->iter;
@@ -845,7 +839,7 @@ int linear_scan_dplr(float alpha, const float *U, const float *V, const float *c
     a.omega = sketch;
     a.U = const_cast<float *>(U); a.V = const_cast<float *>(V);
     a.c = c; a.out = delta;
-    a.agg_p = L.agg_p; a.agg_r = L.agg_r; a.agg_L = L.agg_L; a.agg_R = L.agg_R; a.agg_b = L.agg_b;
+    a.agg = L.agg;
     a.entry = L.entry;
     return launch_dplr_step(a, static_cast<hipStream_t>(stream));
 }

@@ -16,21 +16,26 @@
 //
 // Linear step, increment form: delta_t = A_t delta_{t-1} + c_t, delta_0 = 0,
 // c_t = f_t - s_t, s^(i+1) = s^(i) + delta.  Chunks of L positions:
-//   fold   (one wavefront per chunk): block updates, then the chunk aggregate
-//          P = p I + sum_a l_a r_a^T with offset Pb, composed left to right
+//   fold   block updates, then the chunk aggregate P = p I + sum_a l_a r_a^T
+//          with offset Pb, composed left to right
 //          (A_t P = alpha p I + [alpha l_a + sum_j u~_j (v_j.l_a) | p u~_j][r_a | v_j]^T,
 //          Pb <- A_t Pb + c_t) and re-compressed to m columns whenever it has
 //          more: Y = L (R^T Omega), Q = modified Gram-Schmidt basis of Y's
 //          columns (a column left with at most 1e-5 of its norm drops to zero),
 //          L <- Q, R <- R (L^T Q);
-//   carry  (one wavefront per sequence): entry_{q+1} = P_q entry_q + Pb_q;
-//   replay (one wavefront per chunk): the exact recurrence from the chunk's entry.
+//   carry  entry_{q+1} = P_q entry_q + Pb_q along each sequence's chunks;
+//   replay the exact recurrence from each chunk's entry.
 // Exact zeros stay zero, so a converged prefix (c_t = 0) stays exact through
 // compressed carries: finite-step recovery holds.
 //
-// Lane d of a wavefront holds row d of every D-vector (D <= 64); inner
-// products are wavefront sums broadcast from lane 0, so every lane takes the
-// same decisions.
+// Work mapping: the fold and the replay run four chunks per wavefront, one per
+// 16-lane DPP row.  Lane i of a row holds rows i, i + 16, ... of every
+// D-vector (D <= 16 KD), so an inner product is KD local products plus four
+// DPP steps within the row, and every lane of the row ends with the same bits
+// (the additions pair lanes symmetrically); decisions that depend on an inner
+// product (a zero secant, a Cholesky pivot, a dropped Gram-Schmidt column) are
+// per-row selects.  The carry runs one sequence per block from LDS (see
+// dplr_carry_kernel).
 #include <algorithm>
 
 #include "internal.h"
@@ -40,35 +45,58 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / 64;
+constexpr int kRows = 4;                   // chunks (or sequences) per wavefront
 constexpr float kQrDrop = 1e-5f;
 
-// DPP move of v; lanes outside ROWMASK (rows of 16 lanes) read 0.
-template <int CTRL, int ROWMASK = 0xF>
+template <int CTRL>
 __device__ __forceinline__ float dpp(float v)
 {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWMASK, 0xF,
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF,
                                                                  false));
 }
 
-// Sum over the 64 lanes, the same value on every lane: pairs and quads
-// (quad_perm), halves of a row (row_half_mirror), rows (row_mirror), then the
-// row totals are chained into row 3 (row_bcast:15 into rows 1 and 3,
-// row_bcast:31 into rows 2 and 3) and lane 63's total is broadcast.  The
-// order of the additions is fixed, so every call rounds the same way.
-__device__ __forceinline__ float wsum(float v)
+// Sum over the 16 lanes of the lane's DPP row: neighbours, pairs of
+// neighbours (quad_perm), quads (row_half_mirror), halves (row_mirror).  Each
+// step adds two values that the partner lane adds in the other order, so all
+// 16 lanes hold identical bits.
+__device__ __forceinline__ float rsum(float v)
 {
     v += dpp<0xB1>(v);          // quad_perm [1, 0, 3, 2]
     v += dpp<0x4E>(v);          // quad_perm [2, 3, 0, 1]
     v += dpp<0x141>(v);         // row_half_mirror
     v += dpp<0x140>(v);         // row_mirror
-    v += dpp<0x142, 0xA>(v);    // row_bcast:15
-    v += dpp<0x143, 0xC>(v);    // row_bcast:31
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+    return v;
 }
 
-__device__ __forceinline__ float ld(const float *p, bool ok) { return ok ? *p : 0.0f; }
+template <int KD>
+__device__ __forceinline__ float dot(const float (&x)[KD], const float (&y)[KD])
+{
+    float s = x[0] * y[0];
+#pragma unroll
+    for (int k = 1; k < KD; ++k) s += x[k] * y[k];
+    return rsum(s);
+}
 
-// Iteration-dependent view of the buffers (solver) or the fixed inputs (scan).
+// y = alpha x + sum_{j<n} u_j (v_j . x)
+template <int MR, int KD>
+__device__ __forceinline__ void dplr_apply(float alpha, const float (&u)[MR][KD], const float (&v)[MR][KD], int n,
+                                           const float (&x)[KD], float (&y)[KD])
+{
+    float cf[MR];
+#pragma unroll
+    for (int j = 0; j < MR; ++j) cf[j] = (j < n) ? dot<KD>(v[j], x) : 0.0f;
+#pragma unroll
+    for (int k = 0; k < KD; ++k) {
+        float acc = alpha * x[k];
+#pragma unroll
+        for (int j = 0; j < MR; ++j)
+            if (j < n) acc += u[j][k] * cf[j];
+        y[k] = acc;
+    }
+}
+
+// Iteration-dependent view of the buffers (solver) or the fixed inputs (scan);
+// wavefront-uniform.
 struct StepView {
     const float *s_cur = nullptr, *s_prev = nullptr, *f_cur = nullptr, *f_prev = nullptr;
     float *s_next = nullptr;
@@ -77,14 +105,13 @@ struct StepView {
     bool update = false;
 };
 
-__device__ __forceinline__ bool solver_view(const DplrArgs &a, int bseq, StepView &v)
+__device__ __forceinline__ bool step_view(const DplrArgs &a, StepView &v)
 {
     if (!a.ctl) {                                   // standalone scan
         v.n = a.n_fixed;
         return true;
     }
     if (a.ctl->all_done) return false;
-    if (a.skip && a.skip[bseq]) return false;
     v.i = a.ctl->iter - 1;                          // the check of iteration i has set iter = i + 1
     const bool odd = (v.i & 1) != 0;
     v.s_cur = odd ? a.s_odd : a.s_even;
@@ -97,33 +124,44 @@ __device__ __forceinline__ bool solver_view(const DplrArgs &a, int bseq, StepVie
     return true;
 }
 
-// Block update of one position (see the file header); lane d holds row d.
-template <int MR>
-__device__ __forceinline__ void block_update(const DplrArgs &a, int i, float ds, float df, float (&u)[MR],
-                                             float (&v)[MR], float (&fs)[MR])
+// Block update of one position (see the file header) for the lane's rows.
+template <int MR, int KD, bool MS>
+__device__ __forceinline__ void block_update(const DplrArgs &a, int i, const float (&ds)[KD], const float (&df)[KD],
+                                             float (&u)[MR][KD], float (&v)[MR][KD], float (&fs)[MR][KD])
 {
     const int m = a.m;
     const int slot = (i - 1) % m;
-    if (!a.multisecant) {
+    if (!MS) {
         const int nb = min(i - 1, m);
-        float jds = a.alpha * ds;
+        float cf[MR];
 #pragma unroll
-        for (int j = 0; j < MR; ++j)
-            if (j < nb && j != slot) jds += u[j] * wsum(v[j] * ds);
-        const float ss = wsum(ds * ds);
+        for (int j = 0; j < MR; ++j) cf[j] = (j < nb && j != slot) ? dot<KD>(v[j], ds) : 0.0f;
+        const float ss = dot<KD>(ds, ds);
+        const bool ok = ss > 0.0f;
+        const float inv = ok ? 1.0f / ss : 0.0f;
+        // every element is written through a select: a store at the runtime slot
+        // would turn the register arrays into an indexed stack array
 #pragma unroll
-        for (int j = 0; j < MR; ++j)
-            if (j == slot) {
-                u[j] = ss > 0.0f ? (df - jds) / ss : 0.0f;
-                v[j] = ss > 0.0f ? ds : 0.0f;
+        for (int k = 0; k < KD; ++k) {
+            float jds = a.alpha * ds[k];
+#pragma unroll
+            for (int j = 0; j < MR; ++j)
+                if (j < nb && j != slot) jds += u[j][k] * cf[j];
+            const float nu = (df[k] - jds) * inv, nv = ok ? ds[k] : 0.0f;
+#pragma unroll
+            for (int j = 0; j < MR; ++j) {
+                u[j][k] = (j == slot) ? nu : u[j][k];
+                v[j][k] = (j == slot) ? nv : v[j][k];
             }
+        }
         return;
     }
 #pragma unroll
     for (int j = 0; j < MR; ++j)
-        if (j == slot) {
-            v[j] = ds;
-            fs[j] = df;
+#pragma unroll
+        for (int k = 0; k < KD; ++k) {
+            v[j][k] = (j == slot) ? ds[k] : v[j][k];
+            fs[j][k] = (j == slot) ? df[k] : fs[j][k];
         }
     const int n = min(i, m);
     float C[MR][MR];
@@ -132,389 +170,525 @@ __device__ __forceinline__ void block_update(const DplrArgs &a, int i, float ds,
     for (int r = 0; r < MR; ++r)
 #pragma unroll
         for (int c = 0; c <= r; ++c) {
-            if (r >= n || !ok) continue;
-            float acc = wsum(v[r] * v[c]) + (r == c ? a.lambda : 0.0f);
+            C[r][c] = 1.0f;
+            if (r >= n) continue;
+            float acc = dot<KD>(v[r], v[c]) + (r == c ? a.lambda : 0.0f);
 #pragma unroll
             for (int e = 0; e < c; ++e) acc -= C[r][e] * C[c][e];
             if (r == c) {
-                if (!(acc > 0.0f) || __builtin_isinf(acc)) ok = false;
-                else C[r][r] = sqrtf(acc);
+                const bool good = acc > 0.0f && !__builtin_isinf(acc);
+                ok = ok && good;
+                C[r][r] = good ? sqrtf(acc) : 1.0f;
             } else {
                 C[r][c] = acc / C[c][c];
             }
         }
-    float y[MR];
 #pragma unroll
-    for (int r = 0; r < MR; ++r) {
-        if (r >= n) continue;
-        float acc = fs[r] - a.alpha * v[r];
+    for (int k = 0; k < KD; ++k) {
+        float y[MR];
 #pragma unroll
-        for (int e = 0; e < r; ++e) acc -= C[r][e] * y[e];
-        y[r] = ok ? acc / C[r][r] : 0.0f;
+        for (int r = 0; r < MR; ++r) {
+            y[r] = 0.0f;
+            if (r >= n) continue;
+            float acc = fs[r][k] - a.alpha * v[r][k];
+#pragma unroll
+            for (int e = 0; e < r; ++e) acc -= C[r][e] * y[e];
+            y[r] = acc / C[r][r];
+        }
+#pragma unroll
+        for (int r = MR - 1; r >= 0; --r) {
+            if (r >= n) continue;
+            float acc = y[r];
+#pragma unroll
+            for (int e = r + 1; e < MR; ++e)
+                if (e < n) acc -= C[e][r] * y[e];
+            y[r] = acc / C[r][r];
+        }
+#pragma unroll
+        for (int r = 0; r < MR; ++r) u[r][k] = (ok && r < n) ? y[r] : 0.0f;
     }
-#pragma unroll
-    for (int r = MR - 1; r >= 0; --r) {
-        if (r >= n) continue;
-        float acc = y[r];
-#pragma unroll
-        for (int e = r + 1; e < MR; ++e)
-            if (e < n) acc -= C[e][r] * y[e];
-        y[r] = ok ? acc / C[r][r] : 0.0f;
-    }
-#pragma unroll
-    for (int r = 0; r < MR; ++r) u[r] = (ok && r < n) ? y[r] : 0.0f;
-}
-
-// y = alpha x + sum_{j<n} u_j (v_j . x) for the lane's row
-template <int MR>
-__device__ __forceinline__ float dplr_apply(float alpha, const float (&u)[MR], const float (&v)[MR], int n, float x)
-{
-    float y = alpha * x;
-#pragma unroll
-    for (int j = 0; j < MR; ++j)
-        if (j < n) y += u[j] * wsum(v[j] * x);
-    return y;
 }
 
 // ------------------------------------------------------------------ fold
-template <int MR>
+template <int MR, int KD, bool MS>
 __global__ __launch_bounds__(kThreads) void dplr_fold_kernel(DplrArgs a)
 {
-    const int lane = threadIdx.x & 63;
+    const int lane = threadIdx.x & 63, row4 = lane >> 4, li = lane & 15;
     const long long w = static_cast<long long>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
-    if (w >= static_cast<long long>(a.B) * a.nchunk) return;
-    const int bseq = static_cast<int>(w / a.nchunk), q = static_cast<int>(w % a.nchunk);
+    const long long nch = static_cast<long long>(a.B) * a.nchunk;
+    if (w * kRows >= nch) return;
     StepView sv;
-    if (!solver_view(a, bseq, sv)) return;
+    if (!step_view(a, sv)) return;
+    const long long cid0 = w * kRows + row4;
+    const bool rvalid = cid0 < nch;
+    const long long cid = rvalid ? cid0 : nch - 1;  // rows past the end repeat the last chunk, store nothing
+    const int bseq = static_cast<int>(cid / a.nchunk), q = static_cast<int>(cid % a.nchunk);
+    const bool rlive = rvalid && !(a.ctl && a.skip && a.skip[bseq]);
     const int D = a.D, m = a.m, n = sv.n;
-    const bool row = lane < D;
     const int t0 = q * a.chunk, t1 = min(t0 + a.chunk, a.T);
     const bool last = q == a.nchunk - 1;
-    if (last && !sv.update) return;                 // nothing to fold and no carry to produce
+    // does any row of the wavefront produce an aggregate (every chunk but a sequence's last)?
+    bool wave_agg = false;
+    for (int rr = 0; rr < kRows; ++rr) {
+        const long long c2 = w * kRows + rr;
+        wave_agg = wave_agg || (c2 < nch && c2 % a.nchunk != a.nchunk - 1);
+    }
+    if (!wave_agg && !sv.update) return;            // nothing to fold and no carry to produce
     const size_t seq = static_cast<size_t>(bseq) * a.T;
-    float om[MR];
+    bool rowok[KD];
+    int dd[KD];
 #pragma unroll
-    for (int j = 0; j < MR; ++j) om[j] = (row && j < m) ? a.omega[lane * m + j] : 0.0f;
-
-    float p = 1.0f, Pb = 0.0f;
-    int r = 0;
-    float PL[MR], PR[MR];
+    for (int k = 0; k < KD; ++k) {
+        const int d = li + 16 * k;
+        rowok[k] = d < D;
+        dd[k] = min(d, D - 1);
+    }
+    float om[MR][KD];
 #pragma unroll
-    for (int j = 0; j < MR; ++j) PL[j] = PR[j] = 0.0f;
+    for (int j = 0; j < MR; ++j)
+#pragma unroll
+        for (int k = 0; k < KD; ++k) om[j][k] = (rowok[k] && j < m) ? a.omega[dd[k] * m + j] : 0.0f;
 
-    // inputs of position t, loaded one position ahead of their use (clamped,
-    // always-valid addresses; lanes past D and columns past m read as zero)
-    const int l = min(lane, D - 1);
-    struct In {
-        float u[MR], v[MR], fs[MR];
-        float sc, fc, fp, sp;       // s^(i)_t, f^(i)_t, f^(i-1)_t, s^(i-1)_{t-1} (or c_t standalone)
-    };
-    // Branch-free loads: every source is a valid [B,T,...] buffer (an unused one
-    // stands in where a mode reads nothing), so the loads stay in flight.
+    // branch-free loads from always-valid sources (an unused buffer stands in)
     const float *src_s = a.ctl ? sv.s_cur : a.c;
     const float *src_f = a.ctl ? sv.f_cur : a.c;
     const float *src_fp = a.ctl ? sv.f_prev : a.c;
     const float *src_sp = a.ctl ? sv.s_prev : a.c;
     const float *src_u = m > 0 ? a.U : src_s;
     const float *src_v = m > 0 ? a.V : src_s;
-    const float *src_F = (m > 0 && a.multisecant) ? a.F : src_v;
+    const float *src_F = (m > 0 && MS) ? a.F : src_v;
     const int mm = max(m, 1);
-    auto load_in = [&](int t, In &in) {
-        const size_t pos = seq + min(t, a.T - 1);
+
+    float p = 1.0f;
+    int r = 0;
+    float Pb[KD], PL[MR][KD], PR[MR][KD], s_before[KD];
 #pragma unroll
-        for (int j = 0; j < MR; ++j) {
-            const size_t o = m > 0 ? (pos * m + min(j, mm - 1)) * D + l : pos * D + l;
-            in.u[j] = src_u[o];
-            in.v[j] = src_v[o];
-            in.fs[j] = src_F[o];
-        }
-        in.sc = src_s[pos * D + l];
-        in.fc = src_f[pos * D + l];
-        in.fp = src_fp[pos * D + l];
-        in.sp = src_sp[(pos - (t > 0 ? 1 : 0)) * D + l];
-    };
-    // Values are masked when a position is consumed, not when it is loaded, so
-    // the loads of the next position stay in flight: lanes past D and columns
-    // past m become zero.
-    auto mask_in = [&](In &in) {
+    for (int k = 0; k < KD; ++k) {
+        Pb[k] = 0.0f;
+        s_before[k] = 0.0f;
 #pragma unroll
-        for (int j = 0; j < MR; ++j) {
-            const bool have = row && j < m;
-            in.u[j] = have ? in.u[j] : 0.0f;
-            in.v[j] = have ? in.v[j] : 0.0f;
-            in.fs[j] = have ? in.fs[j] : 0.0f;
-        }
-        in.sc = row ? in.sc : 0.0f;
-        in.fc = row ? in.fc : 0.0f;
-        in.fp = row ? in.fp : 0.0f;
-        in.sp = row ? in.sp : 0.0f;
-    };
-    // s^(i)_{t0-1}: the first ds of the chunk
-    float s_before = 0.0f;
-    if (a.ctl && sv.update && t0 > 0) {
-        const float v0 = sv.s_cur[(seq + t0 - 1) * D + l];
-        s_before = row ? v0 : 0.0f;
+        for (int j = 0; j < MR; ++j) PL[j][k] = PR[j][k] = 0.0f;
     }
-    In cur;
-    load_in(t0, cur);
-    for (int t = t0; t < t1; ++t) {
-        const size_t pos = seq + t;
-        In nxt;
-        load_in(t + 1, nxt);                        // clamped past the chunk: harmless extra load
-        mask_in(cur);
-        float(&u)[MR] = cur.u;
-        float(&v)[MR] = cur.v;
-        float(&fs)[MR] = cur.fs;
-        float c;
-        if (a.ctl) {
-            c = cur.fc - cur.sc;
-            if (sv.update) {
-                const float ds = (t > 0) ? s_before - cur.sp : 0.0f;
-                const float df = cur.fc - cur.fp;
-                block_update<MR>(a, sv.i, ds, df, cur.u, cur.v, cur.fs);
-                if (row) {
-                    float *Up = a.U + pos * m * D + lane, *Vp = a.V + pos * m * D + lane;
-                    if (a.multisecant) {
+    if (a.ctl && sv.update && t0 > 0) {
+#pragma unroll
+        for (int k = 0; k < KD; ++k) {
+            const float v0 = src_s[(seq + t0 - 1) * D + dd[k]];
+            s_before[k] = rowok[k] ? v0 : 0.0f;
+        }
+    }
+
+    const int len = min(a.chunk, a.T);             // only a sequence's last chunk can be shorter
+    for (int s = 0; s < len; ++s) {
+        const int t = t0 + s;
+        const bool ract = rlive && t < t1;
+        const size_t pos = seq + min(t, a.T - 1);
+        float u[MR][KD], v[MR][KD], fs[MR][KD], c[KD], sc[KD], ds[KD], df[KD];
+#pragma unroll
+        for (int k = 0; k < KD; ++k) {
+#pragma unroll
+            for (int j = 0; j < MR; ++j) {
+                const size_t o = m > 0 ? (pos * m + min(j, mm - 1)) * D + dd[k] : pos * D + dd[k];
+                const bool have = rowok[k] && j < m;
+                const float uu = src_u[o], vv = src_v[o], ff = src_F[o];
+                u[j][k] = have ? uu : 0.0f;
+                v[j][k] = have ? vv : 0.0f;
+                fs[j][k] = have ? ff : 0.0f;
+            }
+            const float s_ = src_s[pos * D + dd[k]], f_ = src_f[pos * D + dd[k]];
+            const float fp_ = src_fp[pos * D + dd[k]];
+            const float sp_ = src_sp[(pos - (t > 0 ? 1 : 0)) * D + dd[k]];
+            sc[k] = rowok[k] ? s_ : 0.0f;
+            c[k] = rowok[k] ? (a.ctl ? f_ - s_ : s_) : 0.0f;   // standalone: src_s is c
+            ds[k] = (rowok[k] && t > 0) ? s_before[k] - sp_ : 0.0f;
+            df[k] = rowok[k] ? f_ - fp_ : 0.0f;
+        }
+        if (a.ctl && sv.update) {
+            block_update<MR, KD, MS>(a, sv.i, ds, df, u, v, fs);
+            if (ract) {
+                // the slot's column is picked by selects (a runtime index into the
+                // register arrays would move them to the stack)
+                const int slot = (sv.i - 1) % m;
+                const size_t so = (pos * m + slot) * D + li;
+#pragma unroll
+                for (int k = 0; k < KD; ++k) {
+                    if (!rowok[k]) continue;
+                    float su = 0.0f, sv_ = 0.0f, sf = 0.0f;
+#pragma unroll
+                    for (int j = 0; j < MR; ++j) {
+                        su = (j == slot) ? u[j][k] : su;
+                        sv_ = (j == slot) ? v[j][k] : sv_;
+                        sf = (j == slot) ? fs[j][k] : sf;
+                    }
+                    a.V[so + 16 * k] = sv_;
+                    if (MS) {
+                        a.F[so + 16 * k] = sf;
 #pragma unroll
                         for (int j = 0; j < MR; ++j)
-                            if (j < m) Up[j * D] = u[j];
+                            if (j < m) a.U[(pos * m + j) * D + li + 16 * k] = u[j][k];
+                    } else {
+                        a.U[so + 16 * k] = su;
                     }
-                    const int slot = (sv.i - 1) % m;
-#pragma unroll
-                    for (int j = 0; j < MR; ++j)
-                        if (j == slot) {
-                            if (!a.multisecant) Up[j * D] = u[j];
-                            Vp[j * D] = v[j];
-                            if (a.multisecant) a.F[pos * m * D + lane + j * D] = fs[j];
-                        }
                 }
             }
-            s_before = cur.sc;
-        } else {
-            c = cur.sc;
-        }
-        if (last) {                                 // the last chunk only updates its blocks
-            cur = nxt;
-            continue;
-        }
 #pragma unroll
-        for (int j = 0; j < MR; ++j) u[j] *= a.shrink;
+            for (int k = 0; k < KD; ++k) s_before[k] = sc[k];
+        }
+        if (!wave_agg) continue;                    // the rows' last chunks only update their blocks
+#pragma unroll
+        for (int j = 0; j < MR; ++j)
+#pragma unroll
+            for (int k = 0; k < KD; ++k) u[j][k] *= a.shrink;
 
-        // A_t P: the K = r + n column pairs
-        float Lf[2 * MR], Rf[2 * MR];
+        // A_t P: the r aggregate columns, then the n block columns
+        float Lf[2 * MR][KD], Rf[2 * MR][KD];
 #pragma unroll
         for (int e = 0; e < MR; ++e) {
-            Lf[e] = (e < r) ? dplr_apply<MR>(a.alpha, u, v, n, PL[e]) : 0.0f;
-            Rf[e] = (e < r) ? PR[e] : 0.0f;
+            float y[KD];
+            dplr_apply<MR, KD>(a.alpha, u, v, n, PL[e], y);
+#pragma unroll
+            for (int k = 0; k < KD; ++k) {
+                Lf[e][k] = (e < r) ? y[k] : 0.0f;
+                Rf[e][k] = (e < r) ? PR[e][k] : 0.0f;
+            }
         }
 #pragma unroll
-        for (int j = 0; j < MR; ++j) {
-            Lf[MR + j] = p * u[j];
-            Rf[MR + j] = v[j];
-        }
-        // columns in the order of the definition: the r aggregate columns, then the n block columns
+        for (int j = 0; j < MR; ++j)
+#pragma unroll
+            for (int k = 0; k < KD; ++k) {
+                Lf[MR + j][k] = p * u[j][k];
+                Rf[MR + j][k] = v[j][k];
+            }
         auto col_ok = [&](int e) { return e < MR ? e < r : (e - MR) < n; };
         const int K = r + n;
         p = a.alpha * p;
         if (K <= m) {
-            float NL[MR], NR[MR];
-            int k = 0;
+            // column j of the result: aggregate column j for j < r, else block column j - r
+            // (selects on uniform conditions; no runtime array index)
 #pragma unroll
-            for (int e = 0; e < 2 * MR; ++e) {
-                if (!col_ok(e)) continue;
+            for (int j = 0; j < MR; ++j)
 #pragma unroll
-                for (int j = 0; j < MR; ++j)
-                    if (j == k) { NL[j] = Lf[e]; NR[j] = Rf[e]; }
-                ++k;
-            }
+                for (int k = 0; k < KD; ++k) {
+                    float nl = (j < r) ? Lf[j][k] : 0.0f, nr = (j < r) ? Rf[j][k] : 0.0f;
 #pragma unroll
-            for (int j = 0; j < MR; ++j) {
-                PL[j] = j < K ? NL[j] : 0.0f;
-                PR[j] = j < K ? NR[j] : 0.0f;
-            }
+                    for (int jj = 0; jj <= j; ++jj) {
+                        const bool pick = j - r == jj && jj < n;
+                        nl = pick ? Lf[MR + jj][k] : nl;
+                        nr = pick ? Rf[MR + jj][k] : nr;
+                    }
+                    PL[j][k] = nl;
+                    PR[j][k] = nr;
+                }
             r = K;
         } else {
             // Y = L (R^T Omega), then modified Gram-Schmidt
-            float Q[MR];
+            float Q[MR][KD];
 #pragma unroll
             for (int j = 0; j < MR; ++j) {
-                if (j >= m) { Q[j] = 0.0f; continue; }
-                float y = 0.0f;
+                if (j >= m) {
+#pragma unroll
+                    for (int k = 0; k < KD; ++k) Q[j][k] = 0.0f;
+                    continue;
+                }
+                float y[KD];
+#pragma unroll
+                for (int k = 0; k < KD; ++k) y[k] = 0.0f;
+                float rto[2 * MR];
+#pragma unroll
+                for (int e = 0; e < 2 * MR; ++e) rto[e] = col_ok(e) ? dot<KD>(Rf[e], om[j]) : 0.0f;
 #pragma unroll
                 for (int e = 0; e < 2 * MR; ++e)
-                    if (col_ok(e)) y += Lf[e] * wsum(Rf[e] * om[j]);
-                const float ny = sqrtf(wsum(y * y));
+                    if (col_ok(e))
+#pragma unroll
+                        for (int k = 0; k < KD; ++k) y[k] += Lf[e][k] * rto[e];
+                const float ny2 = dot<KD>(y, y);
 #pragma unroll
                 for (int l = 0; l < MR; ++l)
-                    if (l < j) y -= wsum(Q[l] * y) * Q[l];
-                const float nq = sqrtf(wsum(y * y));
-                Q[j] = (nq > kQrDrop * ny) ? y / nq : 0.0f;
+                    if (l < j) {
+                        const float cf = dot<KD>(Q[l], y);
+#pragma unroll
+                        for (int k = 0; k < KD; ++k) y[k] -= cf * Q[l][k];
+                    }
+                // kept iff |y| > kQrDrop |y before orthogonalisation| (compared as squares)
+                const float nq2 = dot<KD>(y, y);
+                const bool keep = nq2 > (kQrDrop * kQrDrop) * ny2;
+                const float inq = 1.0f / sqrtf(nq2);
+#pragma unroll
+                for (int k = 0; k < KD; ++k) Q[j][k] = keep ? y[k] * inq : 0.0f;
             }
 #pragma unroll
             for (int j = 0; j < MR; ++j) {
-                float rr = 0.0f;
-                if (j < m) {
+                float lq[2 * MR];
+#pragma unroll
+                for (int e = 0; e < 2 * MR; ++e) lq[e] = (j < m && col_ok(e)) ? dot<KD>(Lf[e], Q[j]) : 0.0f;
+#pragma unroll
+                for (int k = 0; k < KD; ++k) {
+                    float rr = 0.0f;
 #pragma unroll
                     for (int e = 0; e < 2 * MR; ++e)
-                        if (col_ok(e)) rr += Rf[e] * wsum(Lf[e] * Q[j]);
+                        if (j < m && col_ok(e)) rr += Rf[e][k] * lq[e];
+                    PL[j][k] = Q[j][k];
+                    PR[j][k] = rr;
                 }
-                PL[j] = Q[j];
-                PR[j] = rr;
             }
             r = m;
         }
-        Pb = dplr_apply<MR>(a.alpha, u, v, n, Pb) + c;
-        cur = nxt;
+        float nb[KD];
+        dplr_apply<MR, KD>(a.alpha, u, v, n, Pb, nb);
+#pragma unroll
+        for (int k = 0; k < KD; ++k) Pb[k] = nb[k] + c[k];
     }
-    if (last || !row) return;
-    const size_t agg = static_cast<size_t>(bseq) * a.nchunk + q;
-    if (lane == 0) {
-        a.agg_p[agg] = p;
-        a.agg_r[agg] = r;
+    if (last || !rlive) return;
+    const int Dp = dplr_padded_dim(D);
+    float *rec = a.agg + static_cast<size_t>(cid) * dplr_record_floats(m, D);
+    if (li == 0) {
+        rec[(2 * m + 1) * Dp] = p;
+        reinterpret_cast<int *>(rec)[(2 * m + 1) * Dp + 1] = r;
     }
 #pragma unroll
-    for (int j = 0; j < MR; ++j)
-        if (j < m) {
-            a.agg_L[(agg * m + j) * D + lane] = PL[j];
-            a.agg_R[(agg * m + j) * D + lane] = PR[j];
-        }
-    a.agg_b[agg * D + lane] = Pb;
+    for (int k = 0; k < KD; ++k) {
+        if (!rowok[k]) continue;
+        const int d = li + 16 * k;
+#pragma unroll
+        for (int j = 0; j < MR; ++j)
+            if (j < m) {
+                rec[j * Dp + d] = PL[j][k];
+                rec[(m + j) * Dp + d] = PR[j][k];
+            }
+        rec[2 * m * Dp + d] = Pb[k];
+    }
 }
 
 // ------------------------------------------------------------------ carry
-template <int MR>
-__global__ __launch_bounds__(kThreads) void dplr_carry_kernel(DplrArgs a)
+constexpr int kCarryLdsBytes = 64 * 1024;          // both batch buffers
+inline int carry_batch(int m, int D, int nchunk)
 {
-    const int lane = threadIdx.x & 63;
-    const long long w = static_cast<long long>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
-    if (w >= a.B) return;
-    const int bseq = static_cast<int>(w);
-    StepView sv;
-    if (!solver_view(a, bseq, sv)) return;
-    const int D = a.D, m = a.m;
-    const bool row = lane < D;
-    const size_t base = static_cast<size_t>(bseq) * a.nchunk;
-    const int nq = a.nchunk - 1;                 // aggregates in the chain
-    // ring of the next kPF aggregates, loaded ahead of the dependent chain
-    constexpr int kPF = 8;
-    float rl[kPF][MR], rrr[kPF][MR], rb[kPF], rp[kPF];
-    int rk[kPF];
-    // unconditional loads at clamped, always-valid addresses (a load under a
-    // divergent branch would make every later wait drain the whole ring)
-    const int l = min(lane, D - 1);
-    auto fetch = [&](int q, float (&L)[MR], float (&R)[MR], float &b, float &p, int &r) {
-        const int qq = min(q, max(nq - 1, 0));
-        const size_t agg = base + qq;
-        p = a.agg_p[agg];
-        r = a.agg_r[agg];
-        b = a.agg_b[agg * D + l];
-#pragma unroll
-        for (int j = 0; j < MR; ++j) {
-            const size_t o = m > 0 ? (agg * m + min(j, m - 1)) * D + l : agg * D + l;
-            L[j] = (m > 0 ? a.agg_L : a.agg_b)[o];
-            R[j] = (m > 0 ? a.agg_R : a.agg_b)[o];
-        }
-    };
-    float e = 0.0f;
-    if (nq > 0) {
-#pragma unroll
-        for (int k = 0; k < kPF; ++k) fetch(k, rl[k], rrr[k], rb[k], rp[k], rk[k]);
-    }
-    for (int q0 = 0; q0 <= nq; q0 += kPF) {
-#pragma unroll
-        for (int k = 0; k < kPF; ++k) {
-            const int q = q0 + k;
-            if (q > nq) break;
-            if (row) a.entry[(base + q) * D + lane] = e;
-            if (q == nq) break;
-            // lanes past D hold copies of lane D - 1; e is zero there, so they add nothing
-            // every column is computed and the unused ones are selected away (no
-            // branches, so the ring's loads stay in flight across steps)
-            float ne = rp[k] * e;
-#pragma unroll
-            for (int j = 0; j < MR; ++j) {
-                const bool use = j < rk[k];
-                const float w = wsum(use ? rrr[k][j] * e : 0.0f);
-                ne += use ? rl[k][j] * w : 0.0f;
-            }
-            e = row ? ne + rb[k] : 0.0f;
-            fetch(q + kPF, rl[k], rrr[k], rb[k], rp[k], rk[k]);
-        }
+    const int fit = kCarryLdsBytes / (2 * 4 * dplr_record_floats(m, D));
+    return std::max(1, std::min(std::max(nchunk - 1, 1), fit));
+}
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// KD consecutive floats from LDS (one ds_read of 4, 8 or 16 bytes; p is KD-aligned)
+template <int KD>
+__device__ __forceinline__ void lds_vec(const float *p, float (&o)[KD])
+{
+    if constexpr (KD == 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(p);
+        o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+    } else if constexpr (KD == 2) {
+        const f32x2 v = *reinterpret_cast<const f32x2 *>(p);
+        o[0] = v.x; o[1] = v.y;
+    } else {
+        o[0] = *p;
     }
 }
 
+// One chunk record of the chain, as wavefront 0 reads it from LDS.
+template <int MR, int KD>
+struct CarryRec {
+    float L[MR][KD], R[MR][KD], b[KD];
+    float p;
+    int r;
+};
+
+// One block per sequence.  The chain over the chunk aggregates is serial, so
+// wavefront 0 runs it from LDS while wavefronts 1-3 copy the next batch of
+// records (one contiguous span, all loads of a thread in flight together)
+// into the other buffer.  In wavefront 0 lane i of a DPP row holds rows
+// KD i .. KD i + KD - 1 (one vector LDS read per vector and record); all four
+// rows run the same chain and row 0 stores the entries.  Records are read one
+// step ahead of their use.
+template <int MR, int KD>
+__global__ __launch_bounds__(kThreads) void dplr_carry_kernel(DplrArgs a, int nb)
+{
+    extern __shared__ float carry_lds[];
+    const int bseq = blockIdx.x;
+    StepView sv;
+    if (!step_view(a, sv)) return;
+    if (a.ctl && a.skip && a.skip[bseq]) return;
+    const int D = a.D, m = a.m, Dp = dplr_padded_dim(D);
+    const int RS = dplr_record_floats(m, D);          // a multiple of 4
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, row4 = lane >> 4, li = lane & 15;
+    const size_t base = static_cast<size_t>(bseq) * a.nchunk;
+    const int nq = a.nchunk - 1;                      // aggregates in the chain
+    const int nbatch = (nq + nb - 1) / nb;
+    const int stride = nb * RS;
+    auto stage = [&](int kb, int tid, int nthr) {
+        const int q0 = kb * nb, n4 = min(nb, nq - q0) * RS / 4;
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(a.agg + (base + q0) * RS);
+        f32x4 *dst = reinterpret_cast<f32x4 *>(carry_lds + (kb & 1) * stride);
+        for (int i0 = tid; i0 < n4; i0 += 16 * nthr) {
+            f32x4 v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v[u] = src[min(i0 + u * nthr, n4 - 1)];
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                if (i0 + u * nthr < n4) dst[i0 + u * nthr] = v[u];
+        }
+    };
+    if (nbatch > 0) stage(0, threadIdx.x, kThreads);
+    __syncthreads();
+
+    // lane rows: d = KD li + k; lanes past the padded width read the last vector slot
+    const int d0 = KD * li;
+    const int ro = min(d0, Dp - KD);
+    bool rowok[KD];
+#pragma unroll
+    for (int k = 0; k < KD; ++k) rowok[k] = d0 + k < D;
+    const int mm1 = max(m - 1, 0);
+    auto read_rec = [&](const float *rec, CarryRec<MR, KD> &c) {
+#pragma unroll
+        for (int j = 0; j < MR; ++j) {
+            const int jj = min(j, mm1);
+            lds_vec<KD>(rec + jj * Dp + ro, c.L[j]);
+            lds_vec<KD>(rec + (m + jj) * Dp + ro, c.R[j]);
+        }
+        lds_vec<KD>(rec + 2 * m * Dp + ro, c.b);
+        c.p = rec[(2 * m + 1) * Dp];
+        c.r = reinterpret_cast<const int *>(rec)[(2 * m + 1) * Dp + 1];
+    };
+    const bool storer = wave == 0 && row4 == 0;
+    float e[KD];
+#pragma unroll
+    for (int k = 0; k < KD; ++k) e[k] = 0.0f;
+    for (int kb = 0; kb < nbatch; ++kb) {
+        if (wave != 0) {
+            if (kb + 1 < nbatch) stage(kb + 1, threadIdx.x - 64, kThreads - 64);
+        } else {
+            const float *buf = carry_lds + (kb & 1) * stride;
+            const int q0 = kb * nb, cnt = min(nb, nq - q0);
+            CarryRec<MR, KD> cur;
+            read_rec(buf, cur);
+            for (int qi = 0; qi < cnt; ++qi) {
+                CarryRec<MR, KD> nxt;
+                read_rec(buf + min(qi + 1, cnt - 1) * RS, nxt);
+                if (storer)
+#pragma unroll
+                    for (int k = 0; k < KD; ++k)
+                        if (rowok[k]) a.entry[(base + q0 + qi) * D + d0 + k] = e[k];
+                const int rk = __builtin_amdgcn_readfirstlane(cur.r);
+                float cf[MR];
+#pragma unroll
+                for (int j = 0; j < MR; ++j) {
+                    float rj[KD];
+#pragma unroll
+                    for (int k = 0; k < KD; ++k) rj[k] = (rowok[k] && j < rk) ? cur.R[j][k] : 0.0f;
+                    cf[j] = dot<KD>(rj, e);
+                }
+#pragma unroll
+                for (int k = 0; k < KD; ++k) {
+                    float ne = cur.p * e[k];
+#pragma unroll
+                    for (int j = 0; j < MR; ++j) ne += (j < rk) ? cur.L[j][k] * cf[j] : 0.0f;
+                    e[k] = rowok[k] ? ne + cur.b[k] : 0.0f;
+                }
+                cur = nxt;
+            }
+        }
+        __syncthreads();
+    }
+    if (storer)
+#pragma unroll
+        for (int k = 0; k < KD; ++k)
+            if (rowok[k]) a.entry[(base + nq) * D + d0 + k] = e[k];
+}
+
 // ------------------------------------------------------------------ replay
-template <int MR>
+template <int MR, int KD>
 __global__ __launch_bounds__(kThreads) void dplr_replay_kernel(DplrArgs a)
 {
-    const int lane = threadIdx.x & 63;
+    const int lane = threadIdx.x & 63, row4 = lane >> 4, li = lane & 15;
     const long long w = static_cast<long long>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
-    if (w >= static_cast<long long>(a.B) * a.nchunk) return;
-    const int bseq = static_cast<int>(w / a.nchunk), q = static_cast<int>(w % a.nchunk);
+    const long long nch = static_cast<long long>(a.B) * a.nchunk;
+    if (w * kRows >= nch) return;
     StepView sv;
-    if (!solver_view(a, bseq, sv)) return;
+    if (!step_view(a, sv)) return;
+    const long long cid0 = w * kRows + row4;
+    const bool rvalid = cid0 < nch;
+    const long long cid = rvalid ? cid0 : nch - 1;
+    const int bseq = static_cast<int>(cid / a.nchunk), q = static_cast<int>(cid % a.nchunk);
+    const bool rlive = rvalid && !(a.ctl && a.skip && a.skip[bseq]);
     const int D = a.D, m = a.m, n = sv.n;
-    const bool row = lane < D;
     const int t0 = q * a.chunk, t1 = min(t0 + a.chunk, a.T);
     const size_t seq = static_cast<size_t>(bseq) * a.T;
-    float dl = ld(a.entry + (static_cast<size_t>(bseq) * a.nchunk + q) * D + lane, row);
-    const int l = min(lane, D - 1);
-    struct In {
-        float u[MR], v[MR];
-        float sc, c;
-    };
+    bool rowok[KD];
+    int dd[KD];
+#pragma unroll
+    for (int k = 0; k < KD; ++k) {
+        const int d = li + 16 * k;
+        rowok[k] = d < D;
+        dd[k] = min(d, D - 1);
+    }
     const float *src_s = a.ctl ? sv.s_cur : a.c;
     const float *src_c = a.ctl ? sv.f_cur : a.c;
     const float *src_u = n > 0 ? a.U : src_s;
     const float *src_v = n > 0 ? a.V : src_s;
     const int nn = max(n, 1);
-    auto load_in = [&](int t, In &in) {
-        const size_t pos = seq + min(t, a.T - 1);
+    float dl[KD];
 #pragma unroll
-        for (int j = 0; j < MR; ++j) {
-            const size_t o = n > 0 ? (pos * m + min(j, nn - 1)) * D + l : pos * D + l;
-            in.u[j] = src_u[o];
-            in.v[j] = src_v[o];
-        }
-        in.sc = src_s[pos * D + l];
-        in.c = src_c[pos * D + l];            // f in the solver; c = f - s once consumed
-    };
-    In cur;
-    load_in(t0, cur);
-    for (int t = t0; t < t1; ++t) {
-        const size_t pos = seq + t;
-        In nxt;
-        load_in(t + 1, nxt);
-#pragma unroll
-        for (int j = 0; j < MR; ++j) {
-            const bool have = row && j < n;
-            cur.u[j] = have ? cur.u[j] * a.shrink : 0.0f;
-            cur.v[j] = have ? cur.v[j] : 0.0f;
-        }
-        const float c = row ? (a.ctl ? cur.c - cur.sc : cur.c) : 0.0f;
-        cur.sc = row ? cur.sc : 0.0f;
-        dl = dplr_apply<MR>(a.alpha, cur.u, cur.v, n, dl) + c;
-        if (row) {
-            if (a.ctl) sv.s_next[pos * D + lane] = cur.sc + dl;
-            else a.out[pos * D + lane] = dl;
-        }
-        cur = nxt;
+    for (int k = 0; k < KD; ++k) {
+        const float e0 = a.entry[cid * D + dd[k]];
+        dl[k] = rowok[k] ? e0 : 0.0f;
     }
+    const int len = min(a.chunk, a.T);
+    for (int s = 0; s < len; ++s) {
+        const int t = t0 + s;
+        const bool ract = rlive && t < t1;
+        const size_t pos = seq + min(t, a.T - 1);
+        float u[MR][KD], v[MR][KD], c[KD], sc[KD];
+#pragma unroll
+        for (int k = 0; k < KD; ++k) {
+#pragma unroll
+            for (int j = 0; j < MR; ++j) {
+                const size_t o = n > 0 ? (pos * m + min(j, nn - 1)) * D + dd[k] : pos * D + dd[k];
+                const bool have = rowok[k] && j < n;
+                const float uu = src_u[o], vv = src_v[o];
+                u[j][k] = have ? uu * a.shrink : 0.0f;
+                v[j][k] = have ? vv : 0.0f;
+            }
+            const float s_ = src_s[pos * D + dd[k]], c_ = src_c[pos * D + dd[k]];
+            sc[k] = rowok[k] ? s_ : 0.0f;
+            c[k] = rowok[k] ? (a.ctl ? c_ - s_ : c_) : 0.0f;
+        }
+        float y[KD];
+        dplr_apply<MR, KD>(a.alpha, u, v, n, dl, y);
+#pragma unroll
+        for (int k = 0; k < KD; ++k) {
+            dl[k] = y[k] + c[k];
+            if (ract && rowok[k]) {
+                const size_t o = pos * D + li + 16 * k;
+                if (a.ctl) sv.s_next[o] = sc[k] + dl[k];
+                else a.out[o] = dl[k];
+            }
+        }
+    }
+}
+
+template <int MR, int KD>
+int launch_dplr(const DplrArgs &a, hipStream_t stream)
+{
+    const long long chunks = static_cast<long long>(a.B) * a.nchunk;
+    const long long wc = (chunks + kRows - 1) / kRows;
+    const unsigned gc = static_cast<unsigned>((wc + kWavesPerBlock - 1) / kWavesPerBlock);
+    if (a.multisecant) DEER_LAUNCH((dplr_fold_kernel<MR, KD, true>), dim3(gc), dim3(kThreads), 0, stream, a);
+    else DEER_LAUNCH((dplr_fold_kernel<MR, KD, false>), dim3(gc), dim3(kThreads), 0, stream, a);
+    DEER_HIP(hipGetLastError());
+    const int nb = carry_batch(a.m, a.D, a.nchunk);
+    const size_t lds = 2 * sizeof(float) * static_cast<size_t>(nb) * dplr_record_floats(a.m, a.D);
+    DEER_LAUNCH((dplr_carry_kernel<MR, KD>), dim3(a.B), dim3(kThreads), lds, stream, a, nb);
+    DEER_HIP(hipGetLastError());
+    DEER_LAUNCH((dplr_replay_kernel<MR, KD>), dim3(gc), dim3(kThreads), 0, stream, a);
+    DEER_HIP(hipGetLastError());
+    return DEER_OK;
 }
 
 template <int MR>
 int launch_dplr_mr(const DplrArgs &a, hipStream_t stream)
 {
-    const long long chunks = static_cast<long long>(a.B) * a.nchunk;
-    const unsigned gc = static_cast<unsigned>((chunks + kWavesPerBlock - 1) / kWavesPerBlock);
-    const unsigned gs = static_cast<unsigned>((a.B + kWavesPerBlock - 1) / kWavesPerBlock);
-    DEER_LAUNCH((dplr_fold_kernel<MR>), dim3(gc), dim3(kThreads), 0, stream, a);
-    DEER_HIP(hipGetLastError());
-    DEER_LAUNCH((dplr_carry_kernel<MR>), dim3(gs), dim3(kThreads), 0, stream, a);
-    DEER_HIP(hipGetLastError());
-    DEER_LAUNCH((dplr_replay_kernel<MR>), dim3(gc), dim3(kThreads), 0, stream, a);
-    DEER_HIP(hipGetLastError());
-    return DEER_OK;
+    if (a.D <= 16) return launch_dplr<MR, 1>(a, stream);
+    if (a.D <= 32) return launch_dplr<MR, 2>(a, stream);
+    return launch_dplr<MR, 4>(a, stream);
 }
 
 }  // namespace

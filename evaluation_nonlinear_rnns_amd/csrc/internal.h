@@ -363,12 +363,18 @@ struct DplrArgs {
     const float *f_even = nullptr, *f_odd = nullptr;  // cell values by iteration parity (solver)
     const SolveControl *ctl = nullptr;
     const int *skip = nullptr;
-    float *agg_p = nullptr;                           // [B * nchunk]
-    int *agg_r = nullptr;                             // [B * nchunk]
-    float *agg_L = nullptr, *agg_R = nullptr;         // [B * nchunk, m, D]
-    float *agg_b = nullptr, *entry = nullptr;         // [B * nchunk, D]
+    float *agg = nullptr;                             // [B * nchunk] records (dplr_record_floats)
+    float *entry = nullptr;                           // [B * nchunk, D]
 };
 int launch_dplr_step(const DplrArgs &a, hipStream_t stream);
+
+// Chunk aggregate record, contiguous per chunk so a run of consecutive chunks
+// is one span: with Dp = D rounded up to a multiple of 4, L_j at j Dp, R_j at
+// (m + j) Dp, the offset b at 2m Dp, then p (float) and the column count r
+// (int bits) at (2m + 1) Dp and + 1, two words of padding.  Words d in [D, Dp)
+// of each vector are never written.
+__host__ __device__ inline int dplr_padded_dim(int D) { return (D + 3) & ~3; }
+__host__ __device__ inline int dplr_record_floats(int m, int D) { return (2 * m + 1) * dplr_padded_dim(D) + 4; }
 
 // Largest Lyapunov exponent along a trajectory (lle.hip): workspace layout and launch.
 struct LleLayout {

@@ -120,7 +120,7 @@ __device__ __forceinline__ void gru_fetch(const float *__restrict__ s, const flo
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void gru_eval_mfma_kernel(
+__global__ __launch_bounds__(kThreads, 2) void gru_eval_mfma_kernel(
     const float *__restrict__ Whh, const float *__restrict__ bhh, const float *__restrict__ pt,
     const float *__restrict__ s0, const float *s_even, const float *s_odd, const int *__restrict__ sel,
     const int *__restrict__ skip, const int *__restrict__ all_done, float *__restrict__ aout,

@@ -37,6 +37,7 @@
 // per-row selects.  The carry runs one sequence per block from LDS (see
 // dplr_carry_kernel).
 #include <algorithm>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -47,6 +48,8 @@ constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / 64;
 constexpr int kRows = 4;                   // chunks (or sequences) per wavefront
 constexpr float kQrDrop = 1e-5f;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v)
@@ -126,10 +129,10 @@ __device__ __forceinline__ bool step_view(const DplrArgs &a, StepView &v)
 
 // Block update of one position (see the file header) for the lane's rows.
 template <int MR, int KD, bool MS>
-__device__ __forceinline__ void block_update(const DplrArgs &a, int i, const float (&ds)[KD], const float (&df)[KD],
-                                             float (&u)[MR][KD], float (&v)[MR][KD], float (&fs)[MR][KD])
+__device__ __forceinline__ void block_update(const DplrArgs &a, int m, int i, const float (&ds)[KD],
+                                             const float (&df)[KD], float (&u)[MR][KD], float (&v)[MR][KD],
+                                             float (&fs)[MR][KD])
 {
-    const int m = a.m;
     const int slot = (i - 1) % m;
     if (!MS) {
         const int nb = min(i - 1, m);
@@ -210,11 +213,56 @@ __device__ __forceinline__ void block_update(const DplrArgs &a, int i, const flo
 }
 
 // ------------------------------------------------------------------ fold
-template <int MR, int KD, bool MS>
+// A load from a wavefront-uniform base plus a 32-bit lane byte offset (the
+// global_load form with a scalar base: no 64-bit address arithmetic per load).
+__device__ __forceinline__ float ldu(const float *base, unsigned off)
+{
+    return *reinterpret_cast<const float *>(reinterpret_cast<const char *>(base) + off);
+}
+
+// KD consecutive floats from a uniform base plus a lane byte offset (one
+// 4-, 8- or 16-byte load; the offset is KD-float aligned).
+template <int KD>
+__device__ __forceinline__ void ldv(const float *base, unsigned off, float (&o)[KD])
+{
+    const char *p = reinterpret_cast<const char *>(base) + off;
+    if constexpr (KD == 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(p);
+        o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+    } else if constexpr (KD == 2) {
+        const f32x2 v = *reinterpret_cast<const f32x2 *>(p);
+        o[0] = v.x; o[1] = v.y;
+    } else {
+        o[0] = *reinterpret_cast<const float *>(p);
+    }
+}
+
+// Lane rows: with D = 16 KD (FULL) lane i of a DPP row holds the KD
+// consecutive rows KD i .. KD i + KD - 1 (vector loads, no row masks);
+// otherwise rows i, i + 16, ... with rows past D masked.
+template <int KD, bool FULL>
+__device__ __forceinline__ int lane_row(int li, int k)
+{
+    return FULL ? KD * li + k : li + 16 * k;
+}
+
+// Inputs of one position for the lane's rows, as loaded (masked when used).
+template <int MR, int KD>
+struct FoldIn {
+    float u[MR][KD], v[MR][KD], fs[MR][KD];
+    float s[KD], f[KD], fp[KD], sp[KD];
+};
+
+// Positions are processed in two loops: a general one while the aggregate
+// holds fewer than m columns (or fewer than m block columns exist yet), then,
+// when r = n = m = MR, one whose column counts are compile-time constants
+// (every step then re-compresses 2m columns to m).
+template <int MR, int KD, bool MS, bool FULL>
 __global__ __launch_bounds__(kThreads) void dplr_fold_kernel(DplrArgs a)
 {
     const int lane = threadIdx.x & 63, row4 = lane >> 4, li = lane & 15;
-    const long long w = static_cast<long long>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const long long w = static_cast<long long>(blockIdx.x) * kWavesPerBlock + wv;
     const long long nch = static_cast<long long>(a.B) * a.nchunk;
     if (w * kRows >= nch) return;
     StepView sv;
@@ -237,11 +285,13 @@ __global__ __launch_bounds__(kThreads) void dplr_fold_kernel(DplrArgs a)
     const size_t seq = static_cast<size_t>(bseq) * a.T;
     bool rowok[KD];
     int dd[KD];
+    unsigned ddb[KD];
 #pragma unroll
     for (int k = 0; k < KD; ++k) {
-        const int d = li + 16 * k;
-        rowok[k] = d < D;
-        dd[k] = min(d, D - 1);
+        const int d = lane_row<KD, FULL>(li, k);
+        rowok[k] = FULL || d < D;
+        dd[k] = FULL ? d : min(d, D - 1);
+        ddb[k] = 4u * dd[k];
     }
     float om[MR][KD];
 #pragma unroll
@@ -249,7 +299,10 @@ __global__ __launch_bounds__(kThreads) void dplr_fold_kernel(DplrArgs a)
 #pragma unroll
         for (int k = 0; k < KD; ++k) om[j][k] = (rowok[k] && j < m) ? a.omega[dd[k] * m + j] : 0.0f;
 
-    // branch-free loads from always-valid sources (an unused buffer stands in)
+    // Addressing: position index P = b T + t.  The wavefront's four chunks are
+    // consecutive, so every row's positions lie within 4 chunk lengths of the
+    // first row's first position P0; bases are uniform, lane offsets 32-bit.
+    // Loads are branch-free from always-valid sources (an unused buffer stands in).
     const float *src_s = a.ctl ? sv.s_cur : a.c;
     const float *src_f = a.ctl ? sv.f_cur : a.c;
     const float *src_fp = a.ctl ? sv.f_prev : a.c;
@@ -258,6 +311,57 @@ __global__ __launch_bounds__(kThreads) void dplr_fold_kernel(DplrArgs a)
     const float *src_v = m > 0 ? a.V : src_s;
     const float *src_F = (m > 0 && MS) ? a.F : src_v;
     const int mm = max(m, 1);
+    const long long cw = w * kRows;
+    const size_t P0 = static_cast<size_t>(cw / a.nchunk) * a.T + static_cast<size_t>(cw % a.nchunk) * a.chunk;
+    const int sh = P0 > 0 ? 1 : 0;                 // s^(i-1)_{t-1} may sit one position before P0
+    const int rel0 = static_cast<int>(seq + t0 - P0), relmax = static_cast<int>(seq + a.T - 1 - P0);
+    const float *bs = src_s + P0 * D, *bf = src_f + P0 * D, *bfp = src_fp + P0 * D;
+    const float *bsp = src_sp + (P0 - sh) * D;
+    const float *bu[MR], *bv[MR], *bF[MR];
+#pragma unroll
+    for (int j = 0; j < MR; ++j) {
+        const size_t o = (P0 * m + min(j, mm - 1)) * D;
+        bu[j] = src_u + o;
+        bv[j] = src_v + o;
+        bF[j] = src_F + o;
+    }
+    auto load = [&](int s, FoldIn<MR, KD> &in) {
+        // position clamped to the sequence; s^(i-1) one position earlier unless it is t = 0
+        const int relc = min(rel0 + s, relmax);
+        const int tc = t0 + (relc - rel0);
+        const unsigned osd = 4u * static_cast<unsigned>(relc * D);
+        const unsigned osp = 4u * static_cast<unsigned>((relc + sh - (tc > 0 ? 1 : 0)) * D);
+        const unsigned ouv = 4u * static_cast<unsigned>(relc * m * D);
+        if constexpr (FULL) {
+            ldv<KD>(bs, osd + ddb[0], in.s);
+            ldv<KD>(bf, osd + ddb[0], in.f);
+            ldv<KD>(bfp, osd + ddb[0], in.fp);
+            ldv<KD>(bsp, osp + ddb[0], in.sp);
+#pragma unroll
+            for (int j = 0; j < MR; ++j) {
+                ldv<KD>(bu[j], ouv + ddb[0], in.u[j]);
+                ldv<KD>(bv[j], ouv + ddb[0], in.v[j]);
+                if constexpr (MS) ldv<KD>(bF[j], ouv + ddb[0], in.fs[j]);
+                else
+#pragma unroll
+                    for (int k = 0; k < KD; ++k) in.fs[j][k] = 0.0f;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < KD; ++k) {
+                in.s[k] = ldu(bs, osd + ddb[k]);
+                in.f[k] = ldu(bf, osd + ddb[k]);
+                in.fp[k] = ldu(bfp, osd + ddb[k]);
+                in.sp[k] = ldu(bsp, osp + ddb[k]);
+#pragma unroll
+                for (int j = 0; j < MR; ++j) {
+                    in.u[j][k] = ldu(bu[j], ouv + ddb[k]);
+                    in.v[j][k] = ldu(bv[j], ouv + ddb[k]);
+                    in.fs[j][k] = MS ? ldu(bF[j], ouv + ddb[k]) : 0.0f;
+                }
+            }
+        }
+    };
 
     float p = 1.0f;
     int r = 0;
@@ -277,38 +381,35 @@ __global__ __launch_bounds__(kThreads) void dplr_fold_kernel(DplrArgs a)
         }
     }
 
-    const int len = min(a.chunk, a.T);             // only a sequence's last chunk can be shorter
-    for (int s = 0; s < len; ++s) {
+    // one position; STEADY: r = n = m = MR known at compile time
+    auto step = [&](auto steady, const FoldIn<MR, KD> &in, int s) {
+        constexpr bool S = decltype(steady)::value;
+        const int n_ = S ? MR : n, m_ = S ? MR : m;
         const int t = t0 + s;
         const bool ract = rlive && t < t1;
-        const size_t pos = seq + min(t, a.T - 1);
         float u[MR][KD], v[MR][KD], fs[MR][KD], c[KD], sc[KD], ds[KD], df[KD];
 #pragma unroll
         for (int k = 0; k < KD; ++k) {
 #pragma unroll
             for (int j = 0; j < MR; ++j) {
-                const size_t o = m > 0 ? (pos * m + min(j, mm - 1)) * D + dd[k] : pos * D + dd[k];
-                const bool have = rowok[k] && j < m;
-                const float uu = src_u[o], vv = src_v[o], ff = src_F[o];
-                u[j][k] = have ? uu : 0.0f;
-                v[j][k] = have ? vv : 0.0f;
-                fs[j][k] = have ? ff : 0.0f;
+                const bool have = rowok[k] && j < m_;
+                u[j][k] = have ? in.u[j][k] : 0.0f;
+                v[j][k] = have ? in.v[j][k] : 0.0f;
+                fs[j][k] = have ? in.fs[j][k] : 0.0f;
             }
-            const float s_ = src_s[pos * D + dd[k]], f_ = src_f[pos * D + dd[k]];
-            const float fp_ = src_fp[pos * D + dd[k]];
-            const float sp_ = src_sp[(pos - (t > 0 ? 1 : 0)) * D + dd[k]];
-            sc[k] = rowok[k] ? s_ : 0.0f;
-            c[k] = rowok[k] ? (a.ctl ? f_ - s_ : s_) : 0.0f;   // standalone: src_s is c
-            ds[k] = (rowok[k] && t > 0) ? s_before[k] - sp_ : 0.0f;
-            df[k] = rowok[k] ? f_ - fp_ : 0.0f;
+            sc[k] = rowok[k] ? in.s[k] : 0.0f;
+            c[k] = rowok[k] ? (a.ctl ? in.f[k] - in.s[k] : in.s[k]) : 0.0f;   // standalone: src_s is c
+            ds[k] = (rowok[k] && t > 0) ? s_before[k] - in.sp[k] : 0.0f;
+            df[k] = rowok[k] ? in.f[k] - in.fp[k] : 0.0f;
         }
         if (a.ctl && sv.update) {
-            block_update<MR, KD, MS>(a, sv.i, ds, df, u, v, fs);
+            block_update<MR, KD, MS>(a, m_, sv.i, ds, df, u, v, fs);
             if (ract) {
                 // the slot's column is picked by selects (a runtime index into the
                 // register arrays would move them to the stack)
-                const int slot = (sv.i - 1) % m;
-                const size_t so = (pos * m + slot) * D + li;
+                const int slot = (sv.i - 1) % m_;
+                const size_t pos = seq + t;
+                const size_t so = (pos * m_ + slot) * D;
 #pragma unroll
                 for (int k = 0; k < KD; ++k) {
                     if (!rowok[k]) continue;
@@ -319,36 +420,37 @@ __global__ __launch_bounds__(kThreads) void dplr_fold_kernel(DplrArgs a)
                         sv_ = (j == slot) ? v[j][k] : sv_;
                         sf = (j == slot) ? fs[j][k] : sf;
                     }
-                    a.V[so + 16 * k] = sv_;
+                    a.V[so + dd[k]] = sv_;
                     if (MS) {
-                        a.F[so + 16 * k] = sf;
+                        a.F[so + dd[k]] = sf;
 #pragma unroll
                         for (int j = 0; j < MR; ++j)
-                            if (j < m) a.U[(pos * m + j) * D + li + 16 * k] = u[j][k];
+                            if (j < m_) a.U[(pos * m_ + j) * D + dd[k]] = u[j][k];
                     } else {
-                        a.U[so + 16 * k] = su;
+                        a.U[so + dd[k]] = su;
                     }
                 }
             }
 #pragma unroll
             for (int k = 0; k < KD; ++k) s_before[k] = sc[k];
         }
-        if (!wave_agg) continue;                    // the rows' last chunks only update their blocks
+        if (!wave_agg) return;                      // the rows' last chunks only update their blocks
 #pragma unroll
         for (int j = 0; j < MR; ++j)
 #pragma unroll
             for (int k = 0; k < KD; ++k) u[j][k] *= a.shrink;
 
         // A_t P: the r aggregate columns, then the n block columns
+        const int r_ = S ? MR : r;
         float Lf[2 * MR][KD], Rf[2 * MR][KD];
 #pragma unroll
         for (int e = 0; e < MR; ++e) {
             float y[KD];
-            dplr_apply<MR, KD>(a.alpha, u, v, n, PL[e], y);
+            dplr_apply<MR, KD>(a.alpha, u, v, n_, PL[e], y);
 #pragma unroll
             for (int k = 0; k < KD; ++k) {
-                Lf[e][k] = (e < r) ? y[k] : 0.0f;
-                Rf[e][k] = (e < r) ? PR[e][k] : 0.0f;
+                Lf[e][k] = (e < r_) ? y[k] : 0.0f;
+                Rf[e][k] = (e < r_) ? PR[e][k] : 0.0f;
             }
         }
 #pragma unroll
@@ -358,20 +460,20 @@ __global__ __launch_bounds__(kThreads) void dplr_fold_kernel(DplrArgs a)
                 Lf[MR + j][k] = p * u[j][k];
                 Rf[MR + j][k] = v[j][k];
             }
-        auto col_ok = [&](int e) { return e < MR ? e < r : (e - MR) < n; };
-        const int K = r + n;
+        auto col_ok = [&](int e) { return e < MR ? e < r_ : (e - MR) < n_; };
+        const int K = r_ + n_;
         p = a.alpha * p;
-        if (K <= m) {
+        if (!S && K <= m) {
             // column j of the result: aggregate column j for j < r, else block column j - r
             // (selects on uniform conditions; no runtime array index)
 #pragma unroll
             for (int j = 0; j < MR; ++j)
 #pragma unroll
                 for (int k = 0; k < KD; ++k) {
-                    float nl = (j < r) ? Lf[j][k] : 0.0f, nr = (j < r) ? Rf[j][k] : 0.0f;
+                    float nl = (j < r_) ? Lf[j][k] : 0.0f, nr = (j < r_) ? Rf[j][k] : 0.0f;
 #pragma unroll
                     for (int jj = 0; jj <= j; ++jj) {
-                        const bool pick = j - r == jj && jj < n;
+                        const bool pick = j - r_ == jj && jj < n_;
                         nl = pick ? Lf[MR + jj][k] : nl;
                         nr = pick ? Rf[MR + jj][k] : nr;
                     }
@@ -384,7 +486,7 @@ __global__ __launch_bounds__(kThreads) void dplr_fold_kernel(DplrArgs a)
             float Q[MR][KD];
 #pragma unroll
             for (int j = 0; j < MR; ++j) {
-                if (j >= m) {
+                if (j >= m_) {
 #pragma unroll
                     for (int k = 0; k < KD; ++k) Q[j][k] = 0.0f;
                     continue;
@@ -419,23 +521,41 @@ __global__ __launch_bounds__(kThreads) void dplr_fold_kernel(DplrArgs a)
             for (int j = 0; j < MR; ++j) {
                 float lq[2 * MR];
 #pragma unroll
-                for (int e = 0; e < 2 * MR; ++e) lq[e] = (j < m && col_ok(e)) ? dot<KD>(Lf[e], Q[j]) : 0.0f;
+                for (int e = 0; e < 2 * MR; ++e) lq[e] = (j < m_ && col_ok(e)) ? dot<KD>(Lf[e], Q[j]) : 0.0f;
 #pragma unroll
                 for (int k = 0; k < KD; ++k) {
                     float rr = 0.0f;
 #pragma unroll
                     for (int e = 0; e < 2 * MR; ++e)
-                        if (j < m && col_ok(e)) rr += Rf[e][k] * lq[e];
+                        if (j < m_ && col_ok(e)) rr += Rf[e][k] * lq[e];
                     PL[j][k] = Q[j][k];
                     PR[j][k] = rr;
                 }
             }
-            r = m;
+            r = m_;
         }
         float nb[KD];
-        dplr_apply<MR, KD>(a.alpha, u, v, n, Pb, nb);
+        dplr_apply<MR, KD>(a.alpha, u, v, n_, Pb, nb);
 #pragma unroll
         for (int k = 0; k < KD; ++k) Pb[k] = nb[k] + c[k];
+    };
+
+    const int len = min(a.chunk, a.T);             // only a sequence's last chunk can be shorter
+    const bool steady_ok = n == MR && m == MR;
+    FoldIn<MR, KD> cur;
+    load(0, cur);
+    int s = 0;
+    for (; s < len && !(steady_ok && r == MR); ++s) {
+        FoldIn<MR, KD> nxt;
+        load(s + 1, nxt);                           // clamped past the chunk: a harmless extra load
+        step(std::false_type{}, cur, s);
+        cur = nxt;
+    }
+    for (; s < len; ++s) {                          // reached only with steady_ok and r = MR
+        FoldIn<MR, KD> nxt;
+        load(s + 1, nxt);
+        step(std::true_type{}, cur, s);
+        cur = nxt;
     }
     if (last || !rlive) return;
     const int Dp = dplr_padded_dim(D);
@@ -447,7 +567,7 @@ __global__ __launch_bounds__(kThreads) void dplr_fold_kernel(DplrArgs a)
 #pragma unroll
     for (int k = 0; k < KD; ++k) {
         if (!rowok[k]) continue;
-        const int d = li + 16 * k;
+        const int d = dd[k];
 #pragma unroll
         for (int j = 0; j < MR; ++j)
             if (j < m) {
@@ -465,9 +585,6 @@ inline int carry_batch(int m, int D, int nchunk)
     const int fit = kCarryLdsBytes / (2 * 4 * dplr_record_floats(m, D));
     return std::max(1, std::min(std::max(nchunk - 1, 1), fit));
 }
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // KD consecutive floats from LDS (one ds_read of 4, 8 or 16 bytes; p is KD-aligned)
 template <int KD>
@@ -596,10 +713,19 @@ __global__ __launch_bounds__(kThreads) void dplr_carry_kernel(DplrArgs a, int nb
 
 // ------------------------------------------------------------------ replay
 template <int MR, int KD>
+struct ReplayIn {
+    float u[MR][KD], v[MR][KD], s[KD], c[KD];
+};
+
+// Four chunks per wavefront replay the exact recurrence from their entries.
+// The addressing is the fold's (uniform bases, 32-bit lane offsets); the
+// inputs of positions s + 1 and s + 2 are in flight while position s runs.
+template <int MR, int KD, bool FULL>
 __global__ __launch_bounds__(kThreads) void dplr_replay_kernel(DplrArgs a)
 {
     const int lane = threadIdx.x & 63, row4 = lane >> 4, li = lane & 15;
-    const long long w = static_cast<long long>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const long long w = static_cast<long long>(blockIdx.x) * kWavesPerBlock + wv;
     const long long nch = static_cast<long long>(a.B) * a.nchunk;
     if (w * kRows >= nch) return;
     StepView sv;
@@ -614,17 +740,56 @@ __global__ __launch_bounds__(kThreads) void dplr_replay_kernel(DplrArgs a)
     const size_t seq = static_cast<size_t>(bseq) * a.T;
     bool rowok[KD];
     int dd[KD];
+    unsigned ddb[KD];
 #pragma unroll
     for (int k = 0; k < KD; ++k) {
-        const int d = li + 16 * k;
-        rowok[k] = d < D;
-        dd[k] = min(d, D - 1);
+        const int d = lane_row<KD, FULL>(li, k);
+        rowok[k] = FULL || d < D;
+        dd[k] = FULL ? d : min(d, D - 1);
+        ddb[k] = 4u * dd[k];
     }
     const float *src_s = a.ctl ? sv.s_cur : a.c;
     const float *src_c = a.ctl ? sv.f_cur : a.c;
     const float *src_u = n > 0 ? a.U : src_s;
     const float *src_v = n > 0 ? a.V : src_s;
+    const int mu = n > 0 ? m : 0;                  // column stride of the U/V stand-in
     const int nn = max(n, 1);
+    const long long cw = w * kRows;
+    const size_t P0 = static_cast<size_t>(cw / a.nchunk) * a.T + static_cast<size_t>(cw % a.nchunk) * a.chunk;
+    const int rel0 = static_cast<int>(seq + t0 - P0), relmax = static_cast<int>(seq + a.T - 1 - P0);
+    const float *bs = src_s + P0 * D, *bc = src_c + P0 * D;
+    const float *bu[MR], *bv[MR];
+#pragma unroll
+    for (int j = 0; j < MR; ++j) {
+        const size_t o = (P0 * mu + (n > 0 ? min(j, nn - 1) : 0)) * D;
+        bu[j] = src_u + o;
+        bv[j] = src_v + o;
+    }
+    auto load = [&](int s, ReplayIn<MR, KD> &in) {
+        const int relc = min(rel0 + s, relmax);
+        const unsigned osd = 4u * static_cast<unsigned>(relc * D);
+        const unsigned ouv = 4u * static_cast<unsigned>(relc * mu * D);
+        if constexpr (FULL) {
+            ldv<KD>(bs, osd + ddb[0], in.s);
+            ldv<KD>(bc, osd + ddb[0], in.c);
+#pragma unroll
+            for (int j = 0; j < MR; ++j) {
+                ldv<KD>(bu[j], ouv + ddb[0], in.u[j]);
+                ldv<KD>(bv[j], ouv + ddb[0], in.v[j]);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < KD; ++k) {
+                in.s[k] = ldu(bs, osd + ddb[k]);
+                in.c[k] = ldu(bc, osd + ddb[k]);
+#pragma unroll
+                for (int j = 0; j < MR; ++j) {
+                    in.u[j][k] = ldu(bu[j], ouv + ddb[k]);
+                    in.v[j][k] = ldu(bv[j], ouv + ddb[k]);
+                }
+            }
+        }
+    };
     float dl[KD];
 #pragma unroll
     for (int k = 0; k < KD; ++k) {
@@ -632,7 +797,12 @@ __global__ __launch_bounds__(kThreads) void dplr_replay_kernel(DplrArgs a)
         dl[k] = rowok[k] ? e0 : 0.0f;
     }
     const int len = min(a.chunk, a.T);
+    ReplayIn<MR, KD> in0, in1;
+    load(0, in0);
+    load(1, in1);
     for (int s = 0; s < len; ++s) {
+        ReplayIn<MR, KD> in2;
+        load(s + 2, in2);                           // clamped past the chunk: harmless extra loads
         const int t = t0 + s;
         const bool ract = rlive && t < t1;
         const size_t pos = seq + min(t, a.T - 1);
@@ -641,15 +811,12 @@ __global__ __launch_bounds__(kThreads) void dplr_replay_kernel(DplrArgs a)
         for (int k = 0; k < KD; ++k) {
 #pragma unroll
             for (int j = 0; j < MR; ++j) {
-                const size_t o = n > 0 ? (pos * m + min(j, nn - 1)) * D + dd[k] : pos * D + dd[k];
                 const bool have = rowok[k] && j < n;
-                const float uu = src_u[o], vv = src_v[o];
-                u[j][k] = have ? uu * a.shrink : 0.0f;
-                v[j][k] = have ? vv : 0.0f;
+                u[j][k] = have ? in0.u[j][k] * a.shrink : 0.0f;
+                v[j][k] = have ? in0.v[j][k] : 0.0f;
             }
-            const float s_ = src_s[pos * D + dd[k]], c_ = src_c[pos * D + dd[k]];
-            sc[k] = rowok[k] ? s_ : 0.0f;
-            c[k] = rowok[k] ? (a.ctl ? c_ - s_ : c_) : 0.0f;
+            sc[k] = rowok[k] ? in0.s[k] : 0.0f;
+            c[k] = rowok[k] ? (a.ctl ? in0.c[k] - in0.s[k] : in0.c[k]) : 0.0f;
         }
         float y[KD];
         dplr_apply<MR, KD>(a.alpha, u, v, n, dl, y);
@@ -657,11 +824,13 @@ __global__ __launch_bounds__(kThreads) void dplr_replay_kernel(DplrArgs a)
         for (int k = 0; k < KD; ++k) {
             dl[k] = y[k] + c[k];
             if (ract && rowok[k]) {
-                const size_t o = pos * D + li + 16 * k;
+                const size_t o = pos * D + dd[k];
                 if (a.ctl) sv.s_next[o] = sc[k] + dl[k];
                 else a.out[o] = dl[k];
             }
         }
+        in0 = in1;
+        in1 = in2;
     }
 }
 
@@ -671,14 +840,21 @@ int launch_dplr(const DplrArgs &a, hipStream_t stream)
     const long long chunks = static_cast<long long>(a.B) * a.nchunk;
     const long long wc = (chunks + kRows - 1) / kRows;
     const unsigned gc = static_cast<unsigned>((wc + kWavesPerBlock - 1) / kWavesPerBlock);
-    if (a.multisecant) DEER_LAUNCH((dplr_fold_kernel<MR, KD, true>), dim3(gc), dim3(kThreads), 0, stream, a);
-    else DEER_LAUNCH((dplr_fold_kernel<MR, KD, false>), dim3(gc), dim3(kThreads), 0, stream, a);
+    const bool full = a.D == 16 * KD;
+    if (a.multisecant) {
+        if (full) DEER_LAUNCH((dplr_fold_kernel<MR, KD, true, true>), dim3(gc), dim3(kThreads), 0, stream, a);
+        else DEER_LAUNCH((dplr_fold_kernel<MR, KD, true, false>), dim3(gc), dim3(kThreads), 0, stream, a);
+    } else {
+        if (full) DEER_LAUNCH((dplr_fold_kernel<MR, KD, false, true>), dim3(gc), dim3(kThreads), 0, stream, a);
+        else DEER_LAUNCH((dplr_fold_kernel<MR, KD, false, false>), dim3(gc), dim3(kThreads), 0, stream, a);
+    }
     DEER_HIP(hipGetLastError());
     const int nb = carry_batch(a.m, a.D, a.nchunk);
     const size_t lds = 2 * sizeof(float) * static_cast<size_t>(nb) * dplr_record_floats(a.m, a.D);
     DEER_LAUNCH((dplr_carry_kernel<MR, KD>), dim3(a.B), dim3(kThreads), lds, stream, a, nb);
     DEER_HIP(hipGetLastError());
-    DEER_LAUNCH((dplr_replay_kernel<MR, KD>), dim3(gc), dim3(kThreads), 0, stream, a);
+    if (full) DEER_LAUNCH((dplr_replay_kernel<MR, KD, true>), dim3(gc), dim3(kThreads), 0, stream, a);
+    else DEER_LAUNCH((dplr_replay_kernel<MR, KD, false>), dim3(gc), dim3(kThreads), 0, stream, a);
     DEER_HIP(hipGetLastError());
     return DEER_OK;
 }

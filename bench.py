@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense-DEER, gain-sweep and linearisation measurements")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work for the baseline sample")
-    ap.add_argument("--only", choices=("dense", "sweep", "scan", "lin", "broyden"), default=None,
+    ap.add_argument("--only", choices=("dense", "sweep", "scan", "lin", "broyden", "tiny"), default=None,
                     help="run one secondary measurement alone and print its JSON (for profiling)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run a plain 1 GiB device copy (the reference kernel for HBM counter scaling)")
@@ -226,6 +226,46 @@ def dense_solve(args, dev):
             "linear_solve_avg_ms": round(scan_ms, 4), "eval_avg_ms": round(ms_e / max(n_e, 1), 4),
             "compose_flops_per_launch": flops, "compose_tflops": round(tflops, 2),
             "compose_frac_of_fp32_mfma_peak": round(tflops / MFMA_F32_PEAK_TFLOPS, 4)}
+
+
+def tiny_solve(args, dev):
+    """Dense DEER on the tiny tanh RNN (B=1, T=1024, D=4): everything fits in
+    cache, so the solve is bound by launch and polling latency; reported as
+    absolute time per solve and B*T/s, no roofline."""
+    import torch
+    from evaluation_nonlinear_rnns_amd import deer, inputs as I
+
+    w = I.WORKLOADS["tanh_d4_t1024"]
+    p = I.workload_problem(w.name)
+    cell = deer.cell_from_problem(p, dev)
+    x = torch.from_numpy(p["x"]).to(dev)
+    out = torch.empty((w.B, w.T, w.D), dtype=torch.float32, device=dev)
+    ws = deer.new_workspace(deer.deer_workspace_size(cell, w.B, w.T, w.mode), device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        return deer.deer_solve(cell, x, None, mode=w.mode, tol=w.tol, max_iter=w.max_iter, out=out, workspace=ws,
+                               stream=stream)
+
+    # per-launch times from the HIP events of a profiled pass; the solve time
+    # from a separate pass without them (their cost is comparable to a launch here)
+    _, prof, res = _time_solves(step, 10, stream)
+    _, iters, _, status, rc = res
+    n_s, ms_s = prof[deer.PROFILE_SCAN]
+    n_e, ms_e = prof[deer.PROFILE_EVAL]
+    reps = max(200, args.steps)
+    for _ in range(20):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / reps
+    return {"workload": w.name, "B": w.B, "T": w.T, "D": w.D, "rc": int(rc),
+            "iterations": sorted(set(int(v) for v in iters)), "solves_timed": reps,
+            "ms_per_solve": round(ms, 4), "B*T/s": round(w.B * w.T / (ms * 1e-3), 1),
+            "linear_solve_avg_ms": round(ms_s / max(n_s, 1), 4), "eval_avg_ms": round(ms_e / max(n_e, 1), 4)}
 
 
 def broyden_solve(args, dev):
@@ -418,7 +458,7 @@ def main():
 
     if args.only:
         fn = {"dense": dense_solve, "sweep": gain_sweep, "scan": scan_bandwidth, "lin": linearizations,
-              "broyden": broyden_solve}[args.only]
+              "broyden": broyden_solve, "tiny": tiny_solve}[args.only]
         print(json.dumps({args.only: fn(args, dev)}), flush=True)
         return
 
@@ -450,6 +490,7 @@ def main():
         line["linear_scan"] = scan_bandwidth(args, dev)
     if not args.no_dense:
         line["dense_deer"] = dense_solve(args, dev)
+        line["tiny_dense"] = tiny_solve(args, dev)
         line["gain_sweep"] = gain_sweep(args, dev)
         line["linearizations"] = linearizations(args, dev)
         line["broyden"] = broyden_solve(args, dev)

@@ -118,6 +118,63 @@ struct PollSlots {
 };
 thread_local PollSlots g_poll;
 
+// Pinned staging for the per-sequence results read back at the end of a solve
+// (copies into pageable memory take tens of microseconds each); one buffer
+// per host thread, grown on demand, reused only after the stream has been
+// synchronised.
+struct ResultStage {
+    char *host = nullptr;
+    size_t cap = 0;
+    char *get(size_t bytes)
+    {
+        if (bytes <= cap) return host;
+        if (host) (void)hipHostFree(host);
+        host = nullptr;
+        cap = 0;
+        if (hipHostMalloc(reinterpret_cast<void **>(&host), bytes, hipHostMallocDefault) != hipSuccess) {
+            host = nullptr;
+            return nullptr;
+        }
+        cap = bytes;
+        return host;
+    }
+};
+thread_local ResultStage g_stage;
+
+// Iteration counts, residuals, statuses and (when abort_dev is set) the
+// look-back abort word: enqueued into the pinned stage, one stream
+// synchronisation, then copied to the caller's host arrays.
+int read_results(const int *iters_dev, const int *status_dev, const float *resid_dev, const unsigned *abort_dev,
+                 int B, hipStream_t stream, int *iters_out, float *resid_out, std::vector<int> &status_h,
+                 unsigned &abort_flag, const char *who)
+{
+    const size_t need = (2 * sizeof(int) + sizeof(float)) * static_cast<size_t>(B) + sizeof(unsigned);
+    char *st = g_stage.get(need);
+    if (!st) {
+        (void)hipStreamSynchronize(stream);
+        return fail(DEER_ERR_HIP, std::string(who) + ": pinned host memory unavailable");
+    }
+    int *h_iters = reinterpret_cast<int *>(st);
+    int *h_status = h_iters + B;
+    float *h_resid = reinterpret_cast<float *>(h_status + B);
+    unsigned *h_abort = reinterpret_cast<unsigned *>(h_resid + B);
+    *h_abort = 0u;
+    int rc = DEER_OK;
+    if (hipMemcpyAsync(h_iters, iters_dev, sizeof(int) * B, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipMemcpyAsync(h_status, status_dev, sizeof(int) * B, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        (resid_out && hipMemcpyAsync(h_resid, resid_dev, sizeof(float) * B, hipMemcpyDeviceToHost, stream) != hipSuccess) ||
+        (abort_dev && hipMemcpyAsync(h_abort, abort_dev, sizeof(unsigned), hipMemcpyDeviceToHost, stream) != hipSuccess))
+        rc = fail(DEER_ERR_HIP, std::string(who) + ": result copy failed");
+    const hipError_t se = hipStreamSynchronize(stream);
+    if (se != hipSuccess && rc == DEER_OK) rc = hip_fail(se, (std::string("hipStreamSynchronize(") + who + ")").c_str());
+    if (rc) return rc;
+    std::memcpy(iters_out, h_iters, sizeof(int) * B);
+    if (resid_out) std::memcpy(resid_out, h_resid, sizeof(float) * B);
+    status_h.assign(h_status, h_status + B);
+    abort_flag = *h_abort;
+    return DEER_OK;
+}
+
 // ------------------------------------------------------ small device kernels
 __global__ void init_control_kernel(SolveControl *ctl, int *done, int *iters, int *status, float *resid,
                                     unsigned *res_bits, int B)
@@ -639,18 +696,13 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
     std::vector<int> status_h(B, 0);
     unsigned abort_flag = 0;
     if (rc == DEER_OK) {
-        if (hipMemcpyAsync(iters_out, L.iters, sizeof(int) * B, hipMemcpyDeviceToHost, stream) != hipSuccess ||
-            (resid_out && hipMemcpyAsync(resid_out, L.resid, sizeof(float) * B, hipMemcpyDeviceToHost, stream) != hipSuccess) ||
-            hipMemcpyAsync(status_h.data(), L.status, sizeof(int) * B, hipMemcpyDeviceToHost, stream) != hipSuccess)
-            rc = fail(DEER_ERR_HIP, "deer_solve: result copy failed");
+        const unsigned *abort_dev =
+            (diag_blocks(mode) || fused) ? &static_cast<ScanHeader *>(L.scan)->abort : nullptr;
+        rc = read_results(L.iters, L.status, L.resid, abort_dev, B, stream, iters_out, resid_out, status_h,
+                          abort_flag, "deer_solve");
+    } else {
+        (void)hipStreamSynchronize(stream);
     }
-    if (rc == DEER_OK && (diag_blocks(mode) || fused)) {
-        if (hipMemcpyAsync(&abort_flag, &static_cast<ScanHeader *>(L.scan)->abort, sizeof(unsigned),
-                           hipMemcpyDeviceToHost, stream) != hipSuccess)
-            rc = fail(DEER_ERR_HIP, "deer_solve: flag copy failed");
-    }
-    const hipError_t se = hipStreamSynchronize(stream);
-    if (se != hipSuccess && rc == DEER_OK) rc = hip_fail(se, "hipStreamSynchronize(deer_solve)");
     if (rc) return rc;
     {
         int last = 0;
@@ -779,14 +831,13 @@ int deer_solve_broyden(const deer_cell_params_t *p, const float *x, const float 
         if (hipGetLastError() != hipSuccess) rc = fail(DEER_ERR_HIP, "deer_solve_broyden: gather launch failed");
     }
     std::vector<int> status_h(B, 0);
+    unsigned abort_flag = 0;
     if (rc == DEER_OK) {
-        if (hipMemcpyAsync(iters_out, L.iters, sizeof(int) * B, hipMemcpyDeviceToHost, stream) != hipSuccess ||
-            (resid_out && hipMemcpyAsync(resid_out, L.resid, sizeof(float) * B, hipMemcpyDeviceToHost, stream) != hipSuccess) ||
-            hipMemcpyAsync(status_h.data(), L.status, sizeof(int) * B, hipMemcpyDeviceToHost, stream) != hipSuccess)
-            rc = fail(DEER_ERR_HIP, "deer_solve_broyden: result copy failed");
+        rc = read_results(L.iters, L.status, L.resid, nullptr, B, stream, iters_out, resid_out, status_h, abort_flag,
+                          "deer_solve_broyden");
+    } else {
+        (void)hipStreamSynchronize(stream);
     }
-    const hipError_t se = hipStreamSynchronize(stream);
-    if (se != hipSuccess && rc == DEER_OK) rc = hip_fail(se, "hipStreamSynchronize(deer_solve_broyden)");
     if (rc) return rc;
     {
         int last = 0;

@@ -230,8 +230,10 @@ def dense_solve(args, dev):
 
 def tiny_solve(args, dev):
     """Dense DEER on the tiny tanh RNN (B=1, T=1024, D=4): everything fits in
-    cache, so the solve is bound by launch and polling latency; reported as
-    absolute time per solve and B*T/s, no roofline."""
+    cache and the solve is bound by launch and synchronisation latency, so it
+    runs as one launch (one workgroup per sequence performs every iteration on
+    chip).  Reported as absolute time per solve, next to the multi-launch loop
+    on the same problem; no roofline."""
     import torch
     from evaluation_nonlinear_rnns_amd import deer, inputs as I
 
@@ -243,29 +245,34 @@ def tiny_solve(args, dev):
     ws = deer.new_workspace(deer.deer_workspace_size(cell, w.B, w.T, w.mode), device=dev)
     stream = torch.cuda.current_stream()
 
-    def step():
-        return deer.deer_solve(cell, x, None, mode=w.mode, tol=w.tol, max_iter=w.max_iter, out=out, workspace=ws,
-                               stream=stream)
+    def solver(multi):
+        def step():
+            return deer.deer_solve(cell, x, None, mode=w.mode, tol=w.tol, max_iter=w.max_iter, out=out,
+                                   workspace=ws, stream=stream, multi_launch=multi)
+        return step
 
-    # per-launch times from the HIP events of a profiled pass; the solve time
-    # from a separate pass without them (their cost is comparable to a launch here)
-    _, prof, res = _time_solves(step, 10, stream)
+    # the kernel time from the HIP events of a profiled pass; the solve time
+    # from passes without them (their cost is comparable to a launch here)
+    _, prof, res = _time_solves(solver(False), 10, stream)
     _, iters, _, status, rc = res
-    n_s, ms_s = prof[deer.PROFILE_SCAN]
     n_e, ms_e = prof[deer.PROFILE_EVAL]
     reps = max(200, args.steps)
-    for _ in range(20):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        step()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1000.0 / reps
-    return {"workload": w.name, "B": w.B, "T": w.T, "D": w.D, "rc": int(rc),
+    ms = {}
+    for multi in (False, True):
+        step = solver(multi)
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            step()
+        torch.cuda.synchronize()
+        ms[multi] = (time.perf_counter() - t0) * 1000.0 / reps
+    return {"workload": w.name, "B": w.B, "T": w.T, "D": w.D, "rc": int(rc), "path": "single launch",
             "iterations": sorted(set(int(v) for v in iters)), "solves_timed": reps,
-            "ms_per_solve": round(ms, 4), "B*T/s": round(w.B * w.T / (ms * 1e-3), 1),
-            "linear_solve_avg_ms": round(ms_s / max(n_s, 1), 4), "eval_avg_ms": round(ms_e / max(n_e, 1), 4)}
+            "ms_per_solve": round(ms[False], 4), "B*T/s": round(w.B * w.T / (ms[False] * 1e-3), 1),
+            "solve_kernel_ms": round(ms_e / max(n_e, 1), 4),
+            "multi_launch_ms_per_solve": round(ms[True], 4)}
 
 
 def broyden_solve(args, dev):

@@ -242,7 +242,7 @@ unsigned grid_for(size_t n, unsigned threads = 256, unsigned cap = 8192)
 // ------------------------------------------------------ argument checks
 int check_cell(const deer_cell_params_t *p, int mode_flags)
 {
-    const int mode = mode_flags & ~DEER_SCAN_F64;
+    const int mode = mode_flags & ~(DEER_SCAN_F64 | DEER_MULTI_LAUNCH);
     if ((mode_flags & DEER_SCAN_F64) && mode != DEER_MODE_DENSE)
         return fail(DEER_ERR_UNSUPPORTED, "DEER_SCAN_F64 applies to dense mode only");
     if (!p) return fail(DEER_ERR_INVALID, "cell parameters: null pointer");
@@ -297,7 +297,7 @@ struct SolveLayout {
 
 SolveLayout solve_layout(void *ws, const deer_cell_params_t *p, int B, int T, int mode_flags)
 {
-    const int mode = mode_flags & ~DEER_SCAN_F64;
+    const int mode = mode_flags & ~(DEER_SCAN_F64 | DEER_MULTI_LAUNCH);
     const bool f64 = (mode_flags & DEER_SCAN_F64) != 0;
     const size_t BTD = static_cast<size_t>(B) * T * p->D;
     const int PD = (p->cell == DEER_CELL_GRU) ? 3 * p->D : p->D;
@@ -591,8 +591,9 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
                float *resid_out, int *status_out, void *workspace, size_t ws_bytes, void *stream_)
 {
     int rc = check_cell(p, mode_flags);
-    const int mode = mode_flags & ~DEER_SCAN_F64;
+    const int mode = mode_flags & ~(DEER_SCAN_F64 | DEER_MULTI_LAUNCH);
     const bool scan_f64 = (mode_flags & DEER_SCAN_F64) != 0;
+    const bool multi_launch = (mode_flags & DEER_MULTI_LAUNCH) != 0;
     if (rc) return rc;
     if (!(damping >= 0.0f && damping <= 1.0f)) return fail(DEER_ERR_INVALID, "damping must lie in [0, 1]");
     if (damping != 0.0f && mode != DEER_MODE_DENSE && mode != DEER_MODE_DIAG)
@@ -627,6 +628,33 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
     const bool gru = p->cell == DEER_CELL_GRU;
     const int PD = gru ? 3 * D : D;
     ProfScope prof(stream);
+
+    if (!gru && !scan_f64 && !multi_launch && tiny_solve_fits(D, T)) {
+        // small problem: the whole solve, projection included, in one launch that
+        // writes the per-sequence results straight into the pinned stage
+        char *st = g_stage.get((2 * sizeof(int) + sizeof(float)) * static_cast<size_t>(B));
+        if (!st) return fail(DEER_ERR_HIP, "deer_solve: pinned host memory unavailable");
+        int *h_iters = reinterpret_cast<int *>(st);
+        int *h_status = h_iters + B;
+        float *h_resid = reinterpret_cast<float *>(h_status + B);
+        prof.begin(0);
+        rc = launch_tiny_solve(p->W, p->U, p->b, x, p->M, s0, init_guess, traj_out, B, T, D,
+                               mode == DEER_MODE_DENSE, lz, tol, max_iter, h_iters, h_status, h_resid, stream);
+        prof.end();
+        const hipError_t se = hipStreamSynchronize(stream);
+        if (rc) return rc;
+        if (se != hipSuccess) return hip_fail(se, "hipStreamSynchronize(deer_solve)");
+        const long long limit[kProfKinds] = {1, 0, 0, 0};
+        prof.collect(limit);
+        bool any_nc = false;
+        for (int b = 0; b < B; ++b) {
+            iters_out[b] = h_iters[b];
+            if (resid_out) resid_out[b] = h_resid[b];
+            if (status_out) status_out[b] = h_status[b];
+            any_nc |= h_status[b] != DEER_SEQ_CONVERGED;
+        }
+        return any_nc ? DEER_NOT_CONVERGED : DEER_OK;
+    }
 
     // per-solve control state and the starting iterate s^(0) in traj_out
     DEER_LAUNCH(init_control_kernel, dim3(grid_for(static_cast<size_t>(B) + 1)), dim3(256), 0, stream, L.ctl,

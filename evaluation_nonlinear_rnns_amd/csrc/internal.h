@@ -340,6 +340,16 @@ int launch_gru_quasi_step(const float *Whh, const float *bhh, const float *pt, c
 int launch_rollout(const deer_cell_params_t *p, const float *x, const float *s0, int B, int T,
                    float *traj, hipStream_t stream);
 
+// Whole tanh solves in one launch (tiny.hip): one workgroup per sequence forms
+// its input projection and runs every iteration on chip; for D <= 4 and
+// T <= 1024.  Writes the trajectory, and the iterations, statuses and
+// residuals to `iters`, `status`, `resid` (device-visible host memory is
+// allowed: they are written once per sequence and fenced system-wide).
+bool tiny_solve_fits(int D, int T);
+int launch_tiny_solve(const float *W, const float *U, const float *bias, const float *x, int M, const float *s0,
+                      const float *init, float *traj, int B, int T, int D, bool dense, Linearization lz, float tol,
+                      int max_iter, int *iters, int *status, float *resid, hipStream_t stream);
+
 // Parallel Broyden (broyden.hip): the block updates and the chunked compressed
 // scan of delta_t = A_t delta_{t-1} + c_t, A_t = alpha I + shrink U_t V_t^T.
 // Solver mode (ctl set): iteration i = ctl->iter - 1 (the convergence check

@@ -26,6 +26,7 @@ MODES = {"dense": DEER_MODE_DENSE, "diag": DEER_MODE_DIAG, "jacobi": DEER_MODE_J
 CELLS = {"tanh": DEER_CELL_TANH, "gru": DEER_CELL_GRU}
 
 DEER_SCAN_F64 = 16   # or-ed into the dense mode: the linear solve accumulates in double
+DEER_MULTI_LAUNCH = 32   # or-ed into the mode: never use the single-launch path for small tanh problems
 
 DEER_OK = 0
 DEER_NOT_CONVERGED = 1
@@ -162,8 +163,8 @@ class Cell:
 
 # ------------------------------------------------------------- workspaces
 
-def _mode(mode: str, scan_f64: bool) -> int:
-    return MODES[mode] | (DEER_SCAN_F64 if scan_f64 else 0)
+def _mode(mode: str, scan_f64: bool, multi_launch: bool = False) -> int:
+    return MODES[mode] | (DEER_SCAN_F64 if scan_f64 else 0) | (DEER_MULTI_LAUNCH if multi_launch else 0)
 
 
 def deer_workspace_size(cell: Cell, B: int, T: int, mode: str, scan_f64: bool = False) -> int:
@@ -201,7 +202,7 @@ def deer_workspace_init(ws, stream=None) -> None:
 
 def deer_solve(cell: Cell, x, s0=None, mode: str = "dense", tol: float = 1e-6, max_iter: int = 100,
                init_guess=None, out=None, workspace=None, stream=None, scan_f64: bool = False,
-               damping: float = 0.0):
+               damping: float = 0.0, multi_launch: bool = False):
     """Parallel fixed-point solve; returns ``(traj, iters, resid, status, rc)``.
 
     ``mode``: ``"dense"`` (Newton), ``"diag"`` (diagonal quasi-Newton),
@@ -209,7 +210,9 @@ def deer_solve(cell: Cell, x, s0=None, mode: str = "dense", tol: float = 1e-6, m
     to ``(1 - k) J``.  ``traj`` is a ``[B,T,D]`` CUDA tensor; ``iters``,
     ``status`` are numpy int32 ``[B]``, ``resid`` numpy float32 ``[B]``; ``rc``
     is DEER_OK or DEER_NOT_CONVERGED.  ``scan_f64`` (dense mode) accumulates
-    the linear solve in double precision.
+    the linear solve in double precision.  ``multi_launch`` keeps small tanh
+    problems (D <= 4, T <= 1024) on the multi-launch loop instead of the
+    single-launch path.
     """
     import numpy as np
     import torch
@@ -227,7 +230,8 @@ def deer_solve(cell: Cell, x, s0=None, mode: str = "dense", tol: float = 1e-6, m
     resid = np.zeros(B, np.float32)
     status = np.zeros(B, np.int32)
     rc = lib.deer_solve(ctypes.byref(p), _dev(x, "x", shape=(B, T, M)), _dev(s0, "s0", shape=(B, D)), B, T,
-                        _mode(mode, scan_f64), ctypes.c_float(damping), ctypes.c_float(tol), int(max_iter),
+                        _mode(mode, scan_f64, multi_launch), ctypes.c_float(damping), ctypes.c_float(tol),
+                        int(max_iter),
                         _dev(init_guess, "init_guess", shape=(B, T, D)), _dev(out, "out", shape=(B, T, D)),
                         iters.ctypes.data_as(ctypes.c_void_p), resid.ctypes.data_as(ctypes.c_void_p),
                         status.ctypes.data_as(ctypes.c_void_p),

@@ -65,6 +65,14 @@ enum deer_mode { DEER_MODE_DENSE = 0, DEER_MODE_DIAG = 1, DEER_MODE_JACOBI = 2, 
  * ("Parallel Broyden Methods", appendix F.2).
  */
 #define DEER_SCAN_F64 16
+/*
+ * Flag or-ed into the mode of deer_solve: always run the multi-launch
+ * iteration loop.  Without it, tanh problems with D <= 4 and T <= 1024 (not
+ * DEER_SCAN_F64) run as one launch in which one workgroup per sequence
+ * performs every iteration on chip (same arithmetic and stopping rule; the
+ * scan tree differs, so results differ only by rounding).
+ */
+#define DEER_MULTI_LAUNCH 32
 enum deer_cell { DEER_CELL_TANH = 0, DEER_CELL_GRU = 1 };
 
 enum deer_status {
@@ -135,6 +143,7 @@ int deer_workspace_init(void *workspace, size_t ws_bytes, void *stream);
  *   x           device [B,T,M] inputs
  *   s0          device [B,D] initial states, or NULL for zeros
  *   mode        enum deer_mode, optionally or-ed with DEER_SCAN_F64 (dense only)
+ *               and DEER_MULTI_LAUNCH
  *   damping     k in [0, 1]: the blocks become (1 - k) J_t (dense) or
  *               (1 - k) diag(J_t) (diag); must be 0 for Jacobi and Picard.
  *               k = 0 is the undamped method, k = 1 turns it into Jacobi.

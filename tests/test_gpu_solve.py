@@ -23,14 +23,16 @@ TOL = 1e-4
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "oracle_full_workloads.json")
 
 
-def _run(orc, p, mode, tol, max_iter, s0=True, check_iters=True, init=None, scan_f64=False, damping=0.0):
+def _run(orc, p, mode, tol, max_iter, s0=True, check_iters=True, init=None, scan_f64=False, damping=0.0,
+         multi_launch=False):
     dev = device()
     cell = deer.cell_from_problem(p, dev)
     x = torch.from_numpy(p["x"]).to(dev)
     s0_t = torch.from_numpy(p["s0"]).to(dev) if s0 else None
     init_t = None if init is None else torch.from_numpy(init).to(dev)
     traj, iters, resid, status, rc = deer.deer_solve(cell, x, s0_t, mode=mode, tol=tol, max_iter=max_iter,
-                                                     init_guess=init_t, scan_f64=scan_f64, damping=damping)
+                                                     init_guess=init_t, scan_f64=scan_f64, damping=damping,
+                                                     multi_launch=multi_launch)
     torch.cuda.synchronize()
     oc = orc.Cell.from_problem(p)
     s0n = p["s0"] if s0 else None
@@ -44,13 +46,15 @@ def _run(orc, p, mode, tol, max_iter, s0=True, check_iters=True, init=None, scan
     return got, ref, iters, resid, status, rc, oit
 
 
+@pytest.mark.parametrize("multi_launch", [False, True])
 @pytest.mark.parametrize("mode", ["dense", "diag"])
 @pytest.mark.parametrize("B,T,D,M,gain", [(2, 100, 4, 3, 0.5), (3, 777, 8, 8, 0.8), (2, 1000, 16, 16, 0.9),
-                                          (2, 500, 32, 32, 0.7), (1, 300, 5, 2, 0.6), (2, 200, 64, 64, 0.6)])
-def test_tanh_solve_matches_oracle(orc, mode, B, T, D, M, gain):
+                                          (2, 500, 32, 32, 0.7), (1, 300, 5, 2, 0.6), (2, 200, 64, 64, 0.6),
+                                          (3, 1000, 2, 3, 0.9)])
+def test_tanh_solve_matches_oracle(orc, mode, B, T, D, M, gain, multi_launch):
     p = I.tanh_problem(500 + T + D, B, T, D, M, gain=gain, bias_std=0.3, s0_std=0.5)
-    log(f"deer_solve tanh {mode} B={B} T={T} D={D} M={M}")
-    got, ref, iters, resid, status, rc, oit = _run(orc, p, mode, 1e-5, T)
+    log(f"deer_solve tanh {mode} B={B} T={T} D={D} M={M} multi_launch={multi_launch}")
+    got, ref, iters, resid, status, rc, oit = _run(orc, p, mode, 1e-5, T, multi_launch=multi_launch)
     assert rc == deer.DEER_OK and np.all(status == 0)
     assert np.all(rel_linf(got, ref) <= TOL)
     assert np.all(resid <= 1e-5)
@@ -140,6 +144,66 @@ def test_solve_edge_cases(orc):
     assert list(iters) == [1, 1] and np.all(rel_linf(got, ref) <= TOL)
 
 
+# ------------------------------------------------ single-launch path (D <= 4, T <= 1024)
+
+@pytest.mark.parametrize("mode,damping", [("dense", 0.0), ("diag", 0.0), ("jacobi", 0.0), ("picard", 0.0),
+                                          ("dense", 0.4), ("diag", 0.7)])
+@pytest.mark.parametrize("B,T,D,M", [(1, 1, 4, 4), (2, 2, 1, 2), (3, 255, 3, 5), (2, 256, 4, 4), (2, 257, 4, 1),
+                                     (1, 512, 2, 2), (2, 513, 4, 3), (1, 1000, 1, 1), (2, 1024, 4, 4)])
+def test_single_launch_matches_oracle(orc, mode, damping, B, T, D, M):
+    """Thread blocks of 1, 2 and 4 positions, ragged last thread, every
+    linearisation: counts within one of the oracle's float32 run, trajectory
+    within 1e-4 of the float64 rollout."""
+    p = I.tanh_problem(1200 + T + D, B, T, D, M, gain=0.8, bias_std=0.3, s0_std=0.5)
+    log(f"deer_solve single launch tanh {mode} damping={damping} B={B} T={T} D={D} M={M}")
+    cap = T + 2 if mode in ("jacobi", "picard") else T + 1
+    got, ref, iters, resid, status, rc, oit = _run(orc, p, mode, 1e-5, cap, damping=damping)
+    assert rc == deer.DEER_OK and np.all(status == 0), (iters, status)
+    assert np.all(rel_linf(got, ref) <= TOL)
+    assert np.all(resid <= 1e-5)
+
+
+def test_single_launch_agrees_with_multi_launch(orc):
+    """The one-launch solve and the multi-launch loop take the same number of
+    iterations and agree to rounding."""
+    dev = device()
+    p = I.tanh_problem(1301, 4, 1024, 4, 4, gain=0.9, bias_std=0.3, s0_std=0.5)
+    cell = deer.cell_from_problem(p, dev)
+    x = torch.from_numpy(p["x"]).to(dev)
+    s0 = torch.from_numpy(p["s0"]).to(dev)
+    for mode in ("dense", "diag"):
+        log(f"deer_solve single vs multi launch {mode}")
+        t1, i1, r1, st1, _ = deer.deer_solve(cell, x, s0, mode=mode, tol=1e-6, max_iter=1024)
+        t1 = t1.cpu().numpy()
+        t2, i2, r2, st2, _ = deer.deer_solve(cell, x, s0, mode=mode, tol=1e-6, max_iter=1024, multi_launch=True)
+        assert list(st1) == list(st2) == [0, 0, 0, 0]
+        assert np.all(np.abs(i1 - i2) <= 1), (i1, i2)
+        assert np.abs(t1 - t2.cpu().numpy()).max() <= 1e-5
+
+
+def test_single_launch_edge_cases(orc):
+    dev = device()
+    p = I.tanh_problem(1310, 3, 300, 4, 4, gain=0.7, bias_std=0.2)
+    oc = orc.Cell.from_problem(p)
+    ref32 = orc.rollout(oc, p["x"], precision="f32")
+    log("deer_solve single launch: warm start at the rollout")
+    _, _, iters, _, status, rc, _ = _run(orc, p, "dense", 1e-5, 50, s0=False, init=ref32)
+    assert list(iters) == [0, 0, 0] and rc == deer.DEER_OK
+    log("deer_solve single launch: max_iter=0 and 1")
+    got, _, iters, _, status, rc, _ = _run(orc, p, "dense", 1e-6, 0, s0=False)
+    assert rc == deer.DEER_NOT_CONVERGED and list(status) == [1, 1, 1] and np.all(got == 0)
+    got, _, iters, _, status, rc, _ = _run(orc, p, "diag", 1e-7, 1, s0=False)
+    assert rc == deer.DEER_NOT_CONVERGED and list(iters) == [1, 1, 1] and list(status) == [1, 1, 1]
+    log("deer_solve single launch: NaN input")
+    q = dict(p)
+    q["x"] = p["x"].copy()
+    q["x"][1, 10, 3] = np.nan
+    got, ref, iters, resid, status, rc, _ = _run(orc, q, "diag", 1e-5, 60, s0=False)
+    assert rc == deer.DEER_NOT_CONVERGED and status[1] == 2 and status[0] == 0 and status[2] == 0
+    assert np.isnan(resid[1])
+    assert np.abs(got[1, :10] - ref[1, :10]).max() < 1e-5
+
+
 def test_sequential_rollout_matches_oracle(orc):
     dev = device()
     for kind in ("tanh", "gru"):
@@ -163,7 +227,7 @@ def _golden(name, gain=None):
     return g[f"{gain:g}"] if gain is not None else g
 
 
-def _full(orc, name, gain=None, sample=None, scan_f64=False):
+def _full(orc, name, gain=None, sample=None, scan_f64=False, multi_launch=False):
     dev = device()
     w = I.WORKLOADS[name]
     gold = _golden(name, gain)
@@ -172,7 +236,7 @@ def _full(orc, name, gain=None, sample=None, scan_f64=False):
     cell = deer.cell_from_problem(p, dev)
     x = torch.from_numpy(p["x"]).to(dev)
     traj, iters, resid, status, rc = deer.deer_solve(cell, x, mode=w.mode, tol=w.tol, max_iter=w.max_iter,
-                                                     scan_f64=scan_f64)
+                                                     scan_f64=scan_f64, multi_launch=multi_launch)
     torch.cuda.synchronize()
     seqs = range(w.B) if sample is None else sample
     oc = orc.Cell.from_problem(p)
@@ -181,8 +245,9 @@ def _full(orc, name, gain=None, sample=None, scan_f64=False):
     return w, gold, p, got, ref, np.asarray(iters), status, list(seqs)
 
 
-def test_full_tanh_d4_t1024(orc):
-    w, gold, p, got, ref, iters, status, seqs = _full(orc, "tanh_d4_t1024")
+@pytest.mark.parametrize("multi_launch", [False, True])
+def test_full_tanh_d4_t1024(orc, multi_launch):
+    w, gold, p, got, ref, iters, status, seqs = _full(orc, "tanh_d4_t1024", multi_launch=multi_launch)
     assert np.all(status == 0)
     assert np.all(np.abs(iters - np.asarray(gold["iters_f32"])) <= 1), (iters, gold["iters_f32"])
     assert np.all(rel_linf(got, ref) <= TOL)

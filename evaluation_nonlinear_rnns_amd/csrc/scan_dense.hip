@@ -848,9 +848,12 @@ DenseScanPlan dense_scan_plan(int B, int T, int D)
     p.B = B;
     p.T = T;
     p.D = D;
-    // Long chunks shorten the carry walk; short ones give enough chunks to fill the chip.
-    int L = 64;
-    while (L > 16 && static_cast<long long>(B) * ((T + L - 1) / L) < 8192) L /= 2;
+    // Chunks of 64 steps (the longest the compose kernels stage).  Shorter chunks
+    // give more parallel composes on small problems, but the carry walk, which
+    // is serial per sequence, grows as T / L and dominates there: on B = 32,
+    // T = 4096, D = 16 a solve took 0.72 ms with 16-step chunks and 0.58 ms
+    // with 64-step ones.
+    const int L = 64;
     p.chunk_len = L;
     p.nchunk = (T + L - 1) / L;
     return p;

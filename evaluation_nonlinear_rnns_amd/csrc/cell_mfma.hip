@@ -85,15 +85,15 @@ struct GruTile {
     static constexpr int NH = ((GruGeom<D>::TP + 1) * (D / 4) + kThreads - 1) / kThreads;   // float4 per thread
 };
 
+// Tile coordinates (sequence bseq, first position t0) are passed in: the tile
+// loops track them incrementally, which keeps 64-bit divisions out of the loop.
 template <int D>
 __device__ __forceinline__ void gru_fetch(const float *__restrict__ s, const float *__restrict__ s0,
-                                          const float *__restrict__ pt, int T, int tps, int tps32, long long tile,
+                                          const float *__restrict__ pt, int T, int tps32, int bseq, int t0,
                                           int ps, int hf, int c, v4f (&hv)[GruTile<D>::NH], v4f (&pv)[3][4])
 {
     using G = GruGeom<D>;
     const int tid = threadIdx.x;
-    const int bseq = static_cast<int>(tile / tps);
-    const int t0 = static_cast<int>(tile % tps) * G::TP;
     const size_t seq = static_cast<size_t>(bseq) * T;
 #pragma unroll
     for (int i = 0; i < GruTile<D>::NH; ++i) {
@@ -155,10 +155,13 @@ __global__ __launch_bounds__(kThreads, 2) void gru_eval_mfma_kernel(
     int cur = -1;
     v4f hv[GruTile<D>::NH];
     v4f pv[3][4];
-    gru_fetch<D>(s, s0, pt, T, tiles_per_seq, tps32, tb, ps, hf, c, hv, pv);
+    // the workgroup's contiguous range of sequence-major tiles, coordinates stepped per tile
+    int bseq = static_cast<int>(tb / tiles_per_seq), tt = static_cast<int>(tb % tiles_per_seq);
+    gru_fetch<D>(s, s0, pt, T, tps32, bseq, tt * G::TP, ps, hf, c, hv, pv);
     for (long long tile = tb; tile < te; ++tile) {
-        const int bseq = static_cast<int>(tile / tiles_per_seq);
-        const int t0 = static_cast<int>(tile % tiles_per_seq) * G::TP;
+        const int t0 = tt * G::TP;
+        int nb = bseq, nt = tt + 1;                  // the next tile of the range
+        if (nt == tiles_per_seq) { nt = 0; ++nb; }
         if (bseq != cur) {
             if (cur >= 0) wave_max_atomic(rmax, res_bits + cur);
             rmax = 0u;
@@ -181,7 +184,10 @@ __global__ __launch_bounds__(kThreads, 2) void gru_eval_mfma_kernel(
         for (int g = 0; g < 3; ++g)
 #pragma unroll
             for (int q = 0; q < 4; ++q) pc[g][q] = pv[g][q];
-        if (tile + 1 < te) gru_fetch<D>(s, s0, pt, T, tiles_per_seq, tps32, tile + 1, ps, hf, c, hv, pv);
+        if (tile + 1 < te) gru_fetch<D>(s, s0, pt, T, tps32, nb, nt * G::TP, ps, hf, c, hv, pv);
+        const int this_seq = bseq;
+        bseq = nb;
+        tt = nt;
         if (!live) continue;
 
         v16f accR = {}, accZ = {}, accN = {};
@@ -195,7 +201,7 @@ __global__ __launch_bounds__(kThreads, 2) void gru_eval_mfma_kernel(
             accN = __builtin_amdgcn_mfma_f32_32x32x2f32(av, wrow[2 * D * G::LDH + 2 * kk], accN, 0, 0, 0);
         }
 
-        const size_t seq = static_cast<size_t>(bseq) * T;
+        const size_t seq = static_cast<size_t>(this_seq) * T;
         const bool full = t0 + ps * 32 + 32 <= T;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -287,15 +293,18 @@ __global__ __launch_bounds__(kThreads, 2) void gru_quasi_step_kernel(
 
     v4f hv[GruTile<D>::NH];
     v4f pv[3][4];
-    long long tile = blockIdx.x;
-    // tiles are numbered time-major (k -> sequence k % nseq, tile k / nseq) so that
-    // the tiles in flight at once spread over the sequences and look-back walks stay short
-    auto seq_major = [&](long long k) { return (k % nseq) * tiles_per_seq + k / nseq; };
-    if (tile < ntiles) gru_fetch<D>(s, s0, pt, T, tiles_per_seq, tps32, seq_major(tile), ps, hf, c, hv, pv);
-    for (; tile < ntiles; tile += gridDim.x) {
-        const int bseq = static_cast<int>(tile % nseq);
-        const int tt = static_cast<int>(tile / nseq);
+    // Tiles are numbered time-major (k -> sequence k % nseq, tile k / nseq) so that
+    // the tiles in flight at once spread over the sequences and look-back walks stay
+    // short.  Workgroup g takes k = g, g + G, ...; the coordinates step by
+    // (G % nseq, G / nseq) with a carry, so the loop does no divisions.
+    const int gq = static_cast<int>(gridDim.x) / nseq, gr = static_cast<int>(gridDim.x) % nseq;
+    int bseq = static_cast<int>(blockIdx.x) % nseq, tt = static_cast<int>(blockIdx.x) / nseq;
+    (void)ntiles;
+    if (tt < tiles_per_seq) gru_fetch<D>(s, s0, pt, T, tps32, bseq, tt * G::TP, ps, hf, c, hv, pv);
+    for (; tt < tiles_per_seq;) {
         const int t0 = tt * G::TP;
+        int nb = bseq + gr, nt = tt + gq;         // the workgroup's next tile
+        if (nb >= nseq) { nb -= nseq; ++nt; }
         const bool live = !(skip && skip[bseq]);  // uniform over the workgroup
         __syncthreads();                          // the previous tile is done with H and the exchange arrays
 #pragma unroll
@@ -313,9 +322,12 @@ __global__ __launch_bounds__(kThreads, 2) void gru_quasi_step_kernel(
         for (int g = 0; g < 3; ++g)
 #pragma unroll
             for (int q = 0; q < 4; ++q) pc[g][q] = pv[g][q];
-        const long long next = tile + gridDim.x;
-        if (next < ntiles) gru_fetch<D>(s, s0, pt, T, tiles_per_seq, tps32, seq_major(next), ps, hf, c, hv, pv);
-        if (!live) continue;
+        if (nt < tiles_per_seq) gru_fetch<D>(s, s0, pt, T, tps32, nb, nt * G::TP, ps, hf, c, hv, pv);
+        if (!live) {
+            bseq = nb;
+            tt = nt;
+            continue;
+        }
 
         v16f accR = {}, accZ = {}, accN = {};
         const float *arow = H + (ps * 32 + r32) * G::LDH + hf;
@@ -432,6 +444,8 @@ __global__ __launch_bounds__(kThreads, 2) void gru_quasi_step_kernel(
                 if (full || t < T) __builtin_nontemporal_store(xs, out + (seq + t) * D + c);
             }
         }
+        bseq = nb;
+        tt = nt;
     }
 
     // The last workgroup out resets the done counter, advances the epoch and

@@ -171,14 +171,24 @@ def scan_bandwidth(args, dev):
             "elements_per_s": w.B * w.T * w.D / (ms * 1e-3)}
 
 
-def _time_solves(step, reps, stream):
+def _time_solves(step, reps, stream, profile=True, budget_ms=None):
+    """Mean wall time of `reps` calls after one warm-up call.  With `profile`
+    the library's per-launch HIP events are on during the timed calls (their
+    packets cost a few microseconds per launch, which matters for small
+    problems); the per-kernel totals come back in `prof`.  With `budget_ms`
+    the count drops (to no fewer than 2) so the timed calls take about that
+    long, judged from the warm-up call."""
     import torch
     from evaluation_nonlinear_rnns_amd import deer
+    t0 = time.perf_counter()
     step()
     torch.cuda.synchronize()
+    if budget_ms is not None:
+        warm = (time.perf_counter() - t0) * 1000.0
+        reps = max(2, min(reps, int(budget_ms / max(warm, 1e-3))))
     for k in range(4):
         deer.deer_profile_read(k)
-    deer.deer_profile_enable(True)
+    deer.deer_profile_enable(profile)
     t0 = time.perf_counter()
     out = None
     for _ in range(reps):
@@ -349,17 +359,18 @@ def gain_sweep(args, dev):
             return deer.deer_solve(cell, x, None, mode=w.mode, tol=w.tol, max_iter=w.max_iter, out=out,
                                    workspace=ws, stream=stream, scan_f64=f64)
 
-        ms, _, res = _time_solves(step, 3, stream)
+        ms, _, res = _time_solves(step, 3 if f64 else 20, stream, profile=False)
         _, iters, _, status, rc = res
         seq = torch.empty_like(out)
 
         def roll():
             return deer.deer_rollout(cell, x, None, out=seq, stream=stream)
 
-        ms_seq, _, _ = _time_solves(roll, 3, stream)
+        ms_seq, _, _ = _time_solves(roll, 10, stream, profile=False)
         v0 = torch.from_numpy(I.lle_probe(50, w.B, w.D)).to(dev)
         lle_out = torch.empty(w.B, dtype=torch.float64, device=dev)
-        ms_lle, _, _ = _time_solves(lambda: deer.deer_lle(cell, x, out, v0, out=lle_out, stream=stream), 3, stream)
+        ms_lle, _, _ = _time_solves(lambda: deer.deer_lle(cell, x, out, v0, out=lle_out, stream=stream), 10, stream,
+                                    profile=False)
         rows.append({"gain": g, "scan_f64": f64, "rc": int(rc), "iterations_max": int(iters.max()),
                      "iterations_median": float(np.median(iters)), "deer_ms": round(ms, 3),
                      "rollout_ms": round(ms_seq, 3), "speedup_vs_rollout": round(ms_seq / ms, 3),
@@ -394,7 +405,8 @@ def linearizations(args, dev):
         del p
         traj = torch.empty((w.B, w.T, w.D), dtype=torch.float32, device=dev)
         seq = torch.empty_like(traj)
-        ms_seq, _, _ = _time_solves(lambda: deer.deer_rollout(cell, x, None, out=seq, stream=stream), 2, stream)
+        ms_seq, _, _ = _time_solves(lambda: deer.deer_rollout(cell, x, None, out=seq, stream=stream), 10, stream,
+                                    profile=False)
         rows = {}
         for label, mode, k in runs:
             ws = deer.new_workspace(deer.deer_workspace_size(cell, w.B, w.T, mode), device=dev)
@@ -404,14 +416,15 @@ def linearizations(args, dev):
                 return deer.deer_solve(cell, x, None, mode=mode, tol=w.tol, max_iter=cap, out=traj, workspace=ws,
                                        stream=stream, damping=k)
 
-            ms, _, res = _time_solves(step, 2, stream)
+            ms, _, res = _time_solves(step, 10, stream, profile=False, budget_ms=300.0)
             _, iters, _, status, rc = res
             rows[label] = {"mode": mode, "damping": k, "rc": int(rc), "iterations_max": int(iters.max()),
                            "ms_per_solve": round(ms, 3), "speedup_vs_rollout": round(ms_seq / ms, 3)}
             del ws
         v0 = torch.from_numpy(I.lle_probe(60, w.B, w.D)).to(dev)
         lle_out = torch.empty(w.B, dtype=torch.float64, device=dev)
-        ms_lle, _, _ = _time_solves(lambda: deer.deer_lle(cell, x, seq, v0, out=lle_out, stream=stream), 2, stream)
+        ms_lle, _, _ = _time_solves(lambda: deer.deer_lle(cell, x, seq, v0, out=lle_out, stream=stream), 10, stream,
+                                    profile=False)
         out[name] = {"gain": gain, "B": w.B, "T": w.T, "D": w.D, "tol": w.tol, "rollout_ms": round(ms_seq, 3),
                      "lle_mean_on_rollout": round(float(lle_out.mean().item()), 4), "lle_ms": round(ms_lle, 3),
                      "runs": rows}

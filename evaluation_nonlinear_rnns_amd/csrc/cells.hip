@@ -22,6 +22,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTP = 64;   // steps per workgroup in the evaluation kernels
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float sigmoidf_(float u) { return 1.0f / (1.0f + expf(-u)); }
 
@@ -112,6 +113,12 @@ __global__ __launch_bounds__(kThreads) void projection_kernel(const float *__res
 // ------------------------------------------------------------- tanh cell
 // f = tanh(W s + p); dense: lin = d = shrink (1 - f^2), b = f - d * (W s)  (A_t = diag(d) W)
 //                    other: lin = a = lin_diag((1 - f^2) W_cc), b = f - a * s_c
+//
+// One workgroup per tile of kTP positions.  Every global load of the tile is
+// issued up front at a clamped, in-bounds address (words outside the problem
+// are selected away afterwards), so a workgroup waits for memory once.  Thread
+// (c, ps) keeps row c of W in registers and reads the state rows as 16-byte
+// LDS broadcasts; W s is accumulated with one FMA per column in column order.
 template <int DP>
 __global__ __launch_bounds__(kThreads) void tanh_eval_kernel(
     const float *__restrict__ W, const float *__restrict__ p, const float *__restrict__ s0,
@@ -122,41 +129,83 @@ __global__ __launch_bounds__(kThreads) void tanh_eval_kernel(
     if (all_done && *all_done) return;
     const int bseq = blockIdx.x / tiles, tile = blockIdx.x % tiles;
     if (skip && skip[bseq]) return;
-    constexpr int PPP = kThreads / DP;   // positions per pass
-    __shared__ float Wt[DP][DP + 1];     // Wt[k][c] = W[c][k]
-    __shared__ float srow[kTP + 1][DP];  // srow[r] = s_{t0 - 1 + r}
+    constexpr int PPP = kThreads / DP;                            // positions per pass
+    constexpr int NP = kTP / PPP;                                 // positions per thread
+    constexpr int NS = ((kTP + 1) * DP + kThreads - 1) / kThreads;   // state words per thread
+    constexpr int NW = (DP * DP + kThreads - 1) / kThreads;         // W words per thread
+    constexpr int LW = DP + 4;                                    // W row stride (conflict-free 16-byte reads)
+    constexpr int WR = (NW * kThreads / DP > DP) ? NW * kThreads / DP : DP;   // W rows incl. padding
+    // Both arrays are padded to whole passes of the workgroup, so the staging
+    // stores need no guard (a guarded store lets the compiler sink its load).
+    __shared__ __align__(16) float Wl[WR * LW];                   // Wl[c][k] = W[c][k], zero past D
+    __shared__ __align__(16) float srow[NS * kThreads];           // srow[r][k] = s_{t0 - 1 + r}[k], rows 0..kTP
     const float *s = (sel && (*sel & 1)) ? s_odd : s_even;
     float *fdst = (sel && (*sel & 1)) ? bout : lin;   // kLinValue output
     const int t0 = tile * kTP;
     const size_t seq = static_cast<size_t>(bseq) * T;
-    for (int e = threadIdx.x; e < DP * DP; e += kThreads) {
-        const int k = e / DP, c = e % DP;
-        Wt[k][c] = (k < D && c < D) ? W[c * D + k] : 0.0f;
+    const int tid = threadIdx.x;
+    const int c = tid % DP, ps = tid / DP;
+    const bool cv = c < D;
+    const int cl = min(c, D - 1);
+
+    // issue order: s_0 row, state rows, W, then the projection (needed only after the barrier)
+    const float s0v = (s0 && tid < D) ? s0[static_cast<size_t>(bseq) * D + tid] : 0.0f;
+    float sv[NS], wv[NW], pv[NP];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        const int e = tid + i * kThreads, r = e / DP, k = e % DP;
+        const int t = min(max(t0 - 1 + r, 0), T - 1);
+        sv[i] = s[(seq + t) * D + min(k, D - 1)];
     }
-    for (int e = threadIdx.x; e < (kTP + 1) * DP; e += kThreads) {
-        const int r = e / DP, c = e % DP;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const int e = min(tid + i * kThreads, DP * DP - 1), r = e / DP, k = e % DP;
+        wv[i] = W[min(r, D - 1) * D + min(k, D - 1)];
+    }
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+        const int t = min(t0 + ps + j * PPP, T - 1);
+        pv[j] = p[(seq + t) * D + cl];
+    }
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        const int e = tid + i * kThreads, r = e / DP, k = e % DP;
         const int t = t0 - 1 + r;
-        float v = 0.0f;
-        if (c < D && t < T) {
-            if (t < 0) v = s0 ? s0[static_cast<size_t>(bseq) * D + c] : 0.0f;
-            else v = s[(seq + t) * D + c];
-        }
-        srow[r][c] = v;
+        srow[e] = (k < D && t >= 0 && t < T) ? sv[i] : 0.0f;
+    }
+    if (t0 == 0 && tid < DP) srow[tid] = tid < D ? s0v : 0.0f;   // s_0 enters the first tile
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const int e = tid + i * kThreads, r = e / DP, k = e % DP;
+        Wl[r * LW + k] = (r < D && k < D) ? wv[i] : 0.0f;
     }
     __syncthreads();
-    const int c = threadIdx.x % DP, ps = threadIdx.x / DP;
-    const bool cv = c < D;
-    const float wcc = cv ? Wt[c][c] : 0.0f;
+
+    float wr[DP];
+#pragma unroll
+    for (int k4 = 0; k4 < DP / 4; ++k4) {
+        const v4f w4 = *reinterpret_cast<const v4f *>(&Wl[c * LW + 4 * k4]);
+        wr[4 * k4] = w4[0]; wr[4 * k4 + 1] = w4[1]; wr[4 * k4 + 2] = w4[2]; wr[4 * k4 + 3] = w4[3];
+    }
+    const float wcc = Wl[c * LW + c];
     unsigned rmax = 0u;
-    for (int r = ps; r < kTP; r += PPP) {
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+        const int r = ps + j * PPP;
         const int t = t0 + r;
-        if (t >= T) break;
+        if (!cv || t >= T) continue;
+        const v4f *sr = reinterpret_cast<const v4f *>(&srow[r * DP]);
         float ws = 0.0f;
-#pragma unroll 8
-        for (int k = 0; k < DP; ++k) ws += Wt[k][c] * srow[r][k];
-        if (!cv) continue;
+#pragma unroll
+        for (int k4 = 0; k4 < DP / 4; ++k4) {
+            const v4f x = sr[k4];
+            ws = __builtin_fmaf(wr[4 * k4], x[0], ws);
+            ws = __builtin_fmaf(wr[4 * k4 + 1], x[1], ws);
+            ws = __builtin_fmaf(wr[4 * k4 + 2], x[2], ws);
+            ws = __builtin_fmaf(wr[4 * k4 + 3], x[3], ws);
+        }
         const size_t o = (seq + t) * D + c;
-        const float h = ws + p[o];
+        const float h = ws + pv[j];
         const float f = tanhf(h);
         const float d = 1.0f - f * f;
         if (lz.kind == kLinValue) {
@@ -168,9 +217,9 @@ __global__ __launch_bounds__(kThreads) void tanh_eval_kernel(
         } else {
             const float a = lin_diag(lz, d * wcc);
             lin[o] = a;
-            bout[o] = f - a * srow[r][c];
+            bout[o] = f - a * srow[r * DP + c];
         }
-        rmax = max(rmax, __float_as_uint(fabsf(srow[r + 1][c] - f)));
+        rmax = max(rmax, __float_as_uint(fabsf(srow[(r + 1) * DP + c] - f)));
     }
     block_max_to(rmax, res_bits + bseq);
 }

@@ -44,6 +44,25 @@ std::mutex g_prof_mu;
 long long g_prof_launches[kProfKinds] = {0, 0, 0, 0};
 double g_prof_ms[kProfKinds] = {0, 0, 0, 0};
 
+// Timing events are reused across calls (one pool per host thread): creating
+// and destroying two events per launch cost more host time than the launch.
+thread_local std::vector<hipEvent_t> g_event_pool;
+
+bool pool_event(hipEvent_t *e)
+{
+    if (!g_event_pool.empty()) {
+        *e = g_event_pool.back();
+        g_event_pool.pop_back();
+        return true;
+    }
+    return hipEventCreate(e) == hipSuccess;
+}
+
+void unpool_event(hipEvent_t e)
+{
+    if (e) g_event_pool.push_back(e);
+}
+
 // Event pairs recorded around launches of one deer_solve call.
 struct ProfScope {
     bool on = false;
@@ -58,8 +77,8 @@ struct ProfScope {
     {
         if (!on) return;
         hipEvent_t e0, e1;
-        if (hipEventCreate(&e0) != hipSuccess) { on = false; return; }
-        if (hipEventCreate(&e1) != hipSuccess) { (void)hipEventDestroy(e0); on = false; return; }
+        if (!pool_event(&e0)) { on = false; return; }
+        if (!pool_event(&e1)) { unpool_event(e0); on = false; return; }
         open_kind = kind;
         open_start = e0;
         g_prof_launch = ProfLaunch{e0, e1};
@@ -88,19 +107,23 @@ struct ProfScope {
         }
         release();
     }
+    // Events go back to the pool only once the stream has passed them: after
+    // collect() (stream synchronised) or, on an error path, after a
+    // synchronisation here, so a pooled event is never re-recorded while pending.
     void release()
     {
         for (auto &m : marks) {
-            (void)hipEventDestroy(m.second.first);
-            (void)hipEventDestroy(m.second.second);
+            unpool_event(m.second.first);
+            unpool_event(m.second.second);
         }
         marks.clear();
     }
     ~ProfScope()
     {
+        if (!marks.empty() || open_kind >= 0) (void)hipStreamSynchronize(stream);
         if (open_kind >= 0) {                    // a scope left open by an error return
-            (void)hipEventDestroy(open_start);
-            (void)hipEventDestroy(g_prof_launch.stop);
+            unpool_event(open_start);
+            unpool_event(g_prof_launch.stop);
         }
         g_prof_launch = ProfLaunch{};
         release();

@@ -44,15 +44,26 @@ std::mutex g_prof_mu;
 long long g_prof_launches[kProfKinds] = {0, 0, 0, 0};
 double g_prof_ms[kProfKinds] = {0, 0, 0, 0};
 
-// Timing events are reused across calls (one pool per host thread): creating
-// and destroying two events per launch cost more host time than the launch.
-thread_local std::vector<hipEvent_t> g_event_pool;
+// Timing events are reused across calls (one pool per host thread and
+// device, since an event belongs to the device that was current when it was
+// created): creating and destroying two events per launch cost more host time
+// than the launch.
+constexpr int kPoolDevices = 64;
+thread_local std::vector<hipEvent_t> g_event_pool[kPoolDevices];
+
+std::vector<hipEvent_t> *event_pool()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kPoolDevices) return nullptr;
+    return &g_event_pool[dev];
+}
 
 bool pool_event(hipEvent_t *e)
 {
-    if (!g_event_pool.empty()) {
-        *e = g_event_pool.back();
-        g_event_pool.pop_back();
+    std::vector<hipEvent_t> *pool = event_pool();
+    if (pool && !pool->empty()) {
+        *e = pool->back();
+        pool->pop_back();
         return true;
     }
     return hipEventCreate(e) == hipSuccess;
@@ -60,7 +71,10 @@ bool pool_event(hipEvent_t *e)
 
 void unpool_event(hipEvent_t e)
 {
-    if (e) g_event_pool.push_back(e);
+    if (!e) return;
+    std::vector<hipEvent_t> *pool = event_pool();
+    if (pool) pool->push_back(e);
+    else (void)hipEventDestroy(e);
 }
 
 // Event pairs recorded around launches of one deer_solve call.

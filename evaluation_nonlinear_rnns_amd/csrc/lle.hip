@@ -7,9 +7,9 @@
 // predicts that parallel Newton converges in few iterations.
 //
 // Two launches: the per-step Jacobian factors are evaluated in parallel over
-// all positions (the trajectory is given), then one wavefront per sequence runs
+// all positions (the trajectory is given), then one workgroup per sequence runs
 // the inherently sequential vector chain, which then costs a few matrix-vector
-// products per step:
+// products per step, split over 2-4 lanes per state channel:
 //   tanh:  J_t v = d_t * (W v),                d_t = 1 - f_t^2
 //   GRU:   J_t v = z * v + al * (Wz v) + be * (Wn v) + ga * (Wr v)
 //          al = (s - n) z (1 - z),  be = (1 - z)(1 - n^2) r,
@@ -21,6 +21,7 @@ namespace deer {
 namespace {
 
 constexpr int kThreads = 256;
+typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int kTP = 64;   // positions per workgroup in the factor kernel
 
 __device__ __forceinline__ float sigm(float u) { return 1.0f / (1.0f + expf(-u)); }
@@ -79,34 +80,99 @@ __global__ __launch_bounds__(kThreads) void gru_lle_factor_kernel(
     }
 }
 
-// One wavefront per sequence: v <- J_t v / |J_t v|, lle = mean_t log |J_t v|.
-// NF = 1 (tanh: factor d) or 4 (GRU: z, al, be, ga).  The factors are fetched
-// PF steps ahead with unconditional (clamped) loads; W sits in LDS and v is
-// broadcast with lane reads.
-template <int DP, int NF>
-__global__ __launch_bounds__(64) void lle_chain_kernel(const float *__restrict__ W, const float *__restrict__ F,
-                                                       const float *__restrict__ v0, int T, int D,
-                                                       double *__restrict__ out)
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
 {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF,
+                                                                 false));
+}
+
+// Sum over the 64 lanes of a wavefront, the same bits in every lane: butterflies
+// inside quads and rows (each pair adds the same two values, so all lanes of a
+// row agree), then the four row sums in a fixed order.
+__device__ __forceinline__ float wave_sum(float v)
+{
+    v += dpp<0xB1>(v);          // quad_perm [1, 0, 3, 2]
+    v += dpp<0x4E>(v);          // quad_perm [2, 3, 0, 1]
+    v += dpp<0x141>(v);         // row_half_mirror
+    v += dpp<0x140>(v);         // row_mirror
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+// Chain geometry: KQ lanes share one channel's dot products (each takes DP / KQ
+// of the columns); a wavefront covers 64 / KQ channels and NW wavefronts the
+// padded state.
+template <int DP> struct ChainGeom;
+template <> struct ChainGeom<4>  { static constexpr int KQ = 4; };
+template <> struct ChainGeom<8>  { static constexpr int KQ = 4; };
+template <> struct ChainGeom<16> { static constexpr int KQ = 4; };
+template <> struct ChainGeom<32> { static constexpr int KQ = 2; };
+template <> struct ChainGeom<64> { static constexpr int KQ = 4; };
+
+template <int DP>
+struct Chain {
+    static constexpr int KQ = ChainGeom<DP>::KQ;
+    static constexpr int CW = 64 / KQ;                    // channels per wavefront
+    static constexpr int NW = DP > CW ? DP / CW : 1;      // wavefronts per sequence
+    static constexpr int KS = DP / KQ;                    // columns per lane
+};
+
+// One workgroup per sequence runs the chain w_t = J_t v_{t-1}, v_t = w_t / |w_t|,
+// lle = mean_t log |w_t|.  NF = 1 (tanh: factor d) or 4 (GRU: z, al, be, ga).
+// Lane (channel c, quarter kq) keeps its rows of W for its columns in
+// registers; the unnormalised w of the previous step sits in LDS (two buffers
+// by step parity) and the 1 / |w| scaling is applied to the dot products.  The
+// norm is a deterministic wave sum (plus an LDS exchange between wavefronts
+// when NW > 1); one barrier per step orders the exchange of w.  Factors are fetched PF steps ahead with
+// clamped loads.
+template <int DP, int NF>
+__global__ __launch_bounds__(64 * Chain<DP>::NW) void lle_chain_kernel(const float *__restrict__ W,
+                                                                       const float *__restrict__ F,
+                                                                       const float *__restrict__ v0, int T, int D,
+                                                                       double *__restrict__ out)
+{
+    using C = Chain<DP>;
     constexpr int NG = NF == 1 ? 1 : 3;
     constexpr int PF = 8;
-    __shared__ float Wsh[NG][DP][DP];    // Wsh[g][k][c] = W[g*D + c][k]
-    const int lane = threadIdx.x, bseq = blockIdx.x;
-    for (int e = lane; e < NG * DP * DP; e += 64) {
-        const int g = e / (DP * DP), k = (e / DP) % DP, c = e % DP;
-        Wsh[g][k][c] = (k < D && c < D) ? W[static_cast<size_t>(g * D + c) * D + k] : 0.0f;
-    }
-    __syncthreads();
-    const bool cv = lane < D;
-    const int c = lane < DP ? lane : 0;
-    const int cr = cv ? lane : 0;
-    float v = cv ? v0[static_cast<size_t>(bseq) * D + lane] : 0.0f;
-    {
-        float s2 = v * v;
+    constexpr int KQ = C::KQ, KS = C::KS, NW = C::NW;
+    __shared__ __align__(16) float wbuf[2][DP];
+    __shared__ float part[2][NW];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, bseq = blockIdx.x;
+    const int c = wave * C::CW + lane / KQ, kq = lane % KQ;
+    const bool cv = c < D;
+    const int cr = cv ? c : 0;
+    float wr[NG][KS];
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) s2 += __shfl_xor(s2, o, 64);
-        v = v / sqrtf(s2);
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int j = 0; j < KS; ++j) {
+            const int k = kq * KS + j;
+            wr[g][j] = (cv && k < D) ? W[static_cast<size_t>(g * D + c) * D + k] : 0.0f;
+        }
+    // step 0 input: w = v0 (unnormalised), scale 1 / |v0|
+    const float v0c = cv ? v0[static_cast<size_t>(bseq) * D + c] : 0.0f;
+    if (kq == 0 && c < DP) wbuf[0][c] = v0c;
+    float inv;
+    {
+        const float sq = wave_sum(kq == 0 ? v0c * v0c : 0.0f);
+        if constexpr (NW > 1) {
+            if (lane == 0) part[0][wave] = sq;
+        }
+        __syncthreads();     // also for one wavefront: lanes read what other lanes wrote
+        if constexpr (NW > 1) {
+            float tot = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) tot += part[0][w];
+            inv = 1.0f / sqrtf(tot);
+        } else {
+            inv = 1.0f / sqrtf(sq);
+        }
     }
+
     const size_t fb = static_cast<size_t>(bseq) * T * NF * D;
     float ring[PF][NF];
     auto fetch = [&](int t, float (&f)[NF]) {
@@ -117,26 +183,59 @@ __global__ __launch_bounds__(64) void lle_chain_kernel(const float *__restrict__
 #pragma unroll
     for (int u = 0; u < PF; ++u) fetch(u, ring[u]);
     double sum = 0.0;
+    int cur = 0;
     auto advance = [&](const float (&f)[NF]) {
+        // dot products of this lane's columns with the previous w
+        float xs[KS];
+        if constexpr (KS >= 4) {
+#pragma unroll
+            for (int j4 = 0; j4 < KS / 4; ++j4) {
+                const v4f x = *reinterpret_cast<const v4f *>(&wbuf[cur][kq * KS + 4 * j4]);
+                xs[4 * j4] = x[0]; xs[4 * j4 + 1] = x[1]; xs[4 * j4 + 2] = x[2]; xs[4 * j4 + 3] = x[3];
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < KS; ++j) xs[j] = wbuf[cur][kq * KS + j];
+        }
         float acc[NG];
 #pragma unroll
-        for (int g = 0; g < NG; ++g) acc[g] = 0.0f;
+        for (int g = 0; g < NG; ++g) {
+            float a = 0.0f;
 #pragma unroll
-        for (int k = 0; k < DP; ++k) {
-            const float vk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), k));
-#pragma unroll
-            for (int g = 0; g < NG; ++g) acc[g] += Wsh[g][k][c] * vk;
+            for (int j = 0; j < KS; ++j) a = __builtin_fmaf(wr[g][j], xs[j], a);
+            if constexpr (KQ >= 2) a += dpp<0xB1>(a);
+            if constexpr (KQ >= 4) a += dpp<0x4E>(a);
+            acc[g] = a * inv;
         }
         float w;
-        if constexpr (NF == 1) w = f[0] * acc[0];
-        else w = f[0] * v + f[1] * acc[1] + f[2] * acc[2] + f[3] * acc[0];   // rows: r = 0, z = 1, n = 2
+        if constexpr (NF == 1) {
+            w = f[0] * acc[0];
+        } else {
+            const float vc = wbuf[cur][c < DP ? c : 0] * inv;
+            w = f[0] * vc + f[1] * acc[1] + f[2] * acc[2] + f[3] * acc[0];   // rows: r = 0, z = 1, n = 2
+        }
         w = cv ? w : 0.0f;
-        float s2 = w * w;
+        const int nxt = cur ^ 1;
+        if (kq == 0 && c < DP) wbuf[nxt][c] = w;
+        float tot = wave_sum(kq == 0 ? w * w : 0.0f);
+        if constexpr (NW > 1) {
+            if (lane == 0) part[nxt][wave] = tot;
+        }
+        // The next step's lanes read w written by other lanes: a barrier even
+        // for a single wavefront, or the compiler may treat the LDS exchange as
+        // private to each lane.
+        __syncthreads();
+        if constexpr (NW > 1) {
+            tot = 0.0f;
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) s2 += __shfl_xor(s2, o, 64);
-        const float g = sqrtf(s2);
-        sum += static_cast<double>(logf(g));
-        v = w / g;
+            for (int q = 0; q < NW; ++q) tot += part[nxt][q];
+        }
+        // log |w| = log2(|w|^2) ln 2 / 2: the hardware log2 and reciprocal square
+        // root (about 1 ulp each) keep the chain's latency down; the log2 sum is
+        // accumulated in float64 and scaled once at the end
+        sum += static_cast<double>(__builtin_amdgcn_logf(tot));
+        inv = __builtin_amdgcn_rsqf(tot);
+        cur = nxt;
     };
     const int nfull = T - T % PF;
     for (int t0 = 0; t0 < nfull; t0 += PF) {
@@ -149,7 +248,7 @@ __global__ __launch_bounds__(64) void lle_chain_kernel(const float *__restrict__
 #pragma unroll
     for (int u = 0; u < PF; ++u)
         if (nfull + u < T) advance(ring[u]);
-    if (lane == 0) out[bseq] = sum / static_cast<double>(T);
+    if (tid == 0) out[bseq] = sum * (0.5 * 0.69314718055994530942) / static_cast<double>(T);
 }
 
 template <int DP>
@@ -162,15 +261,15 @@ int launch_lle_dp(const deer_cell_params_t *p, const float *s0, const float *tra
         DEER_LAUNCH((gru_lle_factor_kernel<DP>), dim3(static_cast<unsigned>(static_cast<long long>(B) * tiles)),
                            dim3(kThreads), 0, stream, p->W, p->b2, proj, s0, traj, F, T, D, tiles);
         DEER_HIP(hipGetLastError());
-        DEER_LAUNCH((lle_chain_kernel<DP, 4>), dim3(static_cast<unsigned>(B)), dim3(64), 0, stream, p->W, F, v0,
-                           T, D, out);
+        DEER_LAUNCH((lle_chain_kernel<DP, 4>), dim3(static_cast<unsigned>(B)), dim3(64 * Chain<DP>::NW), 0, stream,
+                    p->W, F, v0, T, D, out);
     } else {
         // d_t = 1 - f_t^2 is the factored dense leaf the tanh evaluation writes
         const int r = launch_tanh_eval(p->W, proj, s0, traj, traj, nullptr, nullptr, nullptr, F, junk, res_bits, B, T,
                                        D, 1, Linearization{kLinJacobian, 1.0f}, stream);
         if (r) return r;
-        DEER_LAUNCH((lle_chain_kernel<DP, 1>), dim3(static_cast<unsigned>(B)), dim3(64), 0, stream, p->W, F, v0,
-                           T, D, out);
+        DEER_LAUNCH((lle_chain_kernel<DP, 1>), dim3(static_cast<unsigned>(B)), dim3(64 * Chain<DP>::NW), 0, stream,
+                    p->W, F, v0, T, D, out);
     }
     DEER_HIP(hipGetLastError());
     return DEER_OK;

@@ -47,6 +47,22 @@ def test_lle_gru_matches_oracle(orc, D, M, T):
     np.testing.assert_allclose(got, want, rtol=1e-4, atol=1e-4)
 
 
+@pytest.mark.parametrize("cell,D,M,T", [("tanh", 1, 1, 1), ("tanh", 3, 2, 7), ("tanh", 33, 8, 9), ("tanh", 12, 5, 8),
+                                         ("gru", 2, 3, 5), ("gru", 1, 1, 1), ("gru", 40, 7, 17), ("gru", 64, 64, 8)])
+def test_lle_edge_shapes(orc, cell, D, M, T):
+    """Sequences shorter than the chain's 8-step factor ring (and exactly one
+    ring), single-step sequences, one-dimensional states and widths that leave
+    padded channels in every chain layout (2 or 4 lanes per channel, one or
+    four wavefronts)."""
+    if cell == "tanh":
+        p = I.tanh_problem(1300 + D + T, 3, T, D, M, gain=0.9, bias_std=0.3, s0_std=0.5)
+    else:
+        p = I.gru_problem(1400 + D + T, 3, T, D, M, bias_std=0.3, s0_std=0.5)
+    log(f"deer_lle edge {cell} D={D} T={T}")
+    got, want = _lle_case(orc, p, 11 + D + T)
+    np.testing.assert_allclose(got, want, rtol=1e-4, atol=1e-4)
+
+
 def test_lle_predicts_dense_deer_iterations(orc):
     """Across the gain sweep the GPU LLE increases with the gain, and so does the
     number of dense DEER iterations (predictability: the "Predictability

@@ -90,20 +90,24 @@ def solve_workload(args, dev):
     return w, p, ms_per_step, start.elapsed_time(stop) / args.steps, prof, np.array(iters_seen)
 
 
-def _source_sha(path):
+def _source_sha(paths):
+    """Hash of the kernel's source files, in the given order."""
     import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def _traffic(kernel, source):
-    """HBM bytes per launch from committed rocprofv3 counters, if they were taken on this source."""
+def _traffic(kernel, sources):
+    """HBM bytes per launch from committed rocprofv3 counters, if they were taken on these sources."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_sha") != _source_sha(source):
+    if rec.get("source_sha") != _source_sha(sources):
         return None                       # the kernel changed since the counters were taken
     return rec.get("bytes_per_launch")
 
@@ -131,7 +135,8 @@ def roofline_of(w, prof):
     sec = k["avg_ms"] * 1e-3
     achieved = k["bytes"] / sec / 1e9
     tflops = k["flops"] / sec / 1e12
-    src = os.path.join(ROOT, "evaluation_nonlinear_rnns_amd", "csrc", "cell_mfma.hip")
+    # the fused kernel's source: its file and the shared device helpers it inlines
+    src = [os.path.join(ROOT, "evaluation_nonlinear_rnns_amd", "csrc", f) for f in ("cell_mfma.hip", "internal.h")]
     return "gru_quasi_step", kernels, {
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": _traffic("gru_quasi_step", src),

@@ -90,6 +90,35 @@ __device__ inline void finalize_iteration(SolveControl *ctl, unsigned *res_bits,
 {
     const int i = ctl->iter;
     int active = 0;
+    if (!res_tile) {
+        // one sequence per thread: the per-sequence words are read and written
+        // in parallel instead of one dependent round trip per sequence
+        for (int b = threadIdx.x; b < B; b += blockDim.x) {
+            if (done[b]) continue;
+            const unsigned m = res_bits[b];
+            const float r = __uint_as_float(m);
+            res_bits[b] = 0u;
+            if (r <= tol) {
+                done[b] = 1;
+                iters[b] = i;
+                status[b] = DEER_SEQ_CONVERGED;
+                resid[b] = r;
+            } else if (i >= max_iter) {
+                done[b] = 1;
+                iters[b] = max_iter;
+                status[b] = __builtin_isfinite(r) ? DEER_SEQ_NOT_CONVERGED : DEER_SEQ_NONFINITE;
+                resid[b] = r;
+            } else {
+                active = 1;
+            }
+        }
+        active = __syncthreads_or(active);
+        if (threadIdx.x == 0) {
+            if (active) ctl->iter = i + 1;
+            else ctl->all_done = 1;
+        }
+        return;
+    }
     for (int b = 0; b < B; ++b) {
         if (done[b]) continue;                    // same for every thread
         unsigned m = 0u;

@@ -547,6 +547,14 @@ __global__ __launch_bounds__(kThreads) void projection_mfma_kernel(const float *
     const long long ntiles = (nsub + G::PS - 1) / G::PS;
     const long long tb = ntiles * blockIdx.x / gridDim.x, te = ntiles * (blockIdx.x + 1) / gridDim.x;
     if (tb >= te) return;
+    // biases of this lane's output column in each (sub-tile, block) pair, read
+    // once: a conditional load inside the tile loop would wait for the prefetch
+    float bov[G::PAIRS];
+#pragma unroll
+    for (int pi = 0; pi < G::PAIRS; ++pi) {
+        const int ob = (wave * G::PAIRS + pi) % NOB;
+        bov[pi] = bias ? bias[ob * 32 + r32] : 0.0f;
+    }
     v4f xv[ProjTile<KP, NOB>::NX];
     proj_fetch<KP, NOB>(x, T, M, tps32, nsub, tb, xv);
     for (long long tile = tb; tile < te; ++tile) {
@@ -575,7 +583,7 @@ __global__ __launch_bounds__(kThreads) void projection_mfma_kernel(const float *
             for (int kk = 0; kk < G::KK; ++kk)
                 acc = __builtin_amdgcn_mfma_f32_32x32x2f32(arow[2 * kk], brow[2 * kk], acc, 0, 0, 0);
             const int o = ob * 32 + r32;
-            const float bo = bias ? bias[o] : 0.0f;
+            const float bo = bov[pi];
             if constexpr (TILED) {
                 const int g = o / DG, cch = o % DG;
                 v4f *dst = reinterpret_cast<v4f *>(out + static_cast<size_t>(u) * (32 * O));

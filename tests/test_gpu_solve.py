@@ -50,7 +50,7 @@ def _run(orc, p, mode, tol, max_iter, s0=True, check_iters=True, init=None, scan
 @pytest.mark.parametrize("mode", ["dense", "diag"])
 @pytest.mark.parametrize("B,T,D,M,gain", [(2, 100, 4, 3, 0.5), (3, 777, 8, 8, 0.8), (2, 1000, 16, 16, 0.9),
                                           (2, 500, 32, 32, 0.7), (1, 300, 5, 2, 0.6), (2, 200, 64, 64, 0.6),
-                                          (3, 1000, 2, 3, 0.9)])
+                                          (3, 1000, 2, 3, 0.9), (2, 300, 32, 7, 0.7), (3, 31, 32, 32, 0.7)])
 def test_tanh_solve_matches_oracle(orc, mode, B, T, D, M, gain, multi_launch):
     p = I.tanh_problem(500 + T + D, B, T, D, M, gain=gain, bias_std=0.3, s0_std=0.5)
     log(f"deer_solve tanh {mode} B={B} T={T} D={D} M={M} multi_launch={multi_launch}")
@@ -72,7 +72,7 @@ def test_tanh_dense_solve_f64_scan_matches_oracle(orc, B, T, D, M, gain):
 
 
 @pytest.mark.parametrize("B,T,D,M", [(2, 100, 4, 3), (3, 1000, 16, 16), (2, 777, 32, 8), (2, 2000, 64, 64),
-                                     (1, 129, 7, 5)])
+                                     (1, 129, 7, 5), (2, 300, 32, 5), (5, 31, 64, 7), (3, 33, 64, 64)])
 def test_gru_solve_matches_oracle(orc, B, T, D, M):
     p = I.gru_problem(600 + T + D, B, T, D, M, bias_std=0.3, s0_std=0.5)
     log(f"deer_solve gru diag B={B} T={T} D={D} M={M}")

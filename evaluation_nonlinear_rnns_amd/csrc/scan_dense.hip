@@ -156,6 +156,23 @@ __device__ __forceinline__ int row_ror(int v)   // DPP rotation by K lanes withi
     return __builtin_amdgcn_update_dpp(0, v, 0x120 + K, 0xf, 0xf, true);
 }
 
+// acc += w * (x rotated right by K lanes within each row of 16) as one
+// v_fmac_f32_dpp (the compiler keeps the rotation as a separate v_mov_b32_dpp).
+// The same fused multiply-add on the same operands, so the same bits.  The
+// first rotation of a contraction waits two cycles: a DPP source written by
+// the VALU just before needs two wait states, and the hazard check does not
+// look inside asm.
+template <int K>
+__device__ __forceinline__ void fmac_row_ror(float &acc, float x, float w)
+{
+    if constexpr (K == 1)
+        asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_ror:%3 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+                     : "+v"(acc) : "v"(x), "v"(w), "n"(K));
+    else
+        asm volatile("v_fmac_f32_dpp %0, %1, %2 row_ror:%3 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+                     : "+v"(acc) : "v"(x), "v"(w), "n"(K));
+}
+
 template <int K>
 struct RowRotations {
     static __device__ __forceinline__ void sources(int m, int (&src)[16])
@@ -165,8 +182,7 @@ struct RowRotations {
     }
     static __device__ __forceinline__ void contract(float x, const float (&w)[16], float &a0, float &a1)
     {
-        const float xr = __int_as_float(row_ror<K>(__float_as_int(x)));
-        if (K & 1) a1 += w[K] * xr; else a0 += w[K] * xr;
+        if (K & 1) fmac_row_ror<K>(a1, x, w[K]); else fmac_row_ror<K>(a0, x, w[K]);
         RowRotations<K + 1>::contract(x, w, a0, a1);
     }
 };

@@ -309,3 +309,90 @@ def test_broyden_argument_checks(orc):
             continue
         with pytest.raises(RuntimeError):
             orc.broyden(c, p["x"], sk, **args)
+
+
+# ------------------------------------------------------------ secant pairing
+
+def _linear_cell(orc, W, seed, B, T):
+    """Linear cell f(s, x) = W s + x (identity input map), inputs ~ N(0, 1)."""
+    D = W.shape[0]
+    c = orc.Cell("linear", np.asarray(W, np.float32), np.eye(D, dtype=np.float32), np.zeros(D, np.float32))
+    x = np.random.default_rng(seed).standard_normal((B, T, D)).astype(np.float32)
+    return c, x
+
+
+@pytest.mark.parametrize("multisecant", [False, True])
+@pytest.mark.parametrize("chunk", [64, 3])
+def test_broyden_scalar_linear_secant_gives_the_exact_slope(orc, multisecant, chunk):
+    """Scalar linear cell f = w s + x: a secant between the iterates entering
+    position t (s^(i)_{t-1}, s^(i-1)_{t-1}) and the values f^(i)_t, f^(i-1)_t
+    it produces has slope exactly w ("finite differences between successive
+    trajectory iterates", "Parallel Broyden Methods" page, section 3.1).  The
+    first update (iteration 1) therefore makes every block that multiplies a
+    non-zero increment equal to w, iteration 1 is an exact Newton step and the
+    iteration stops at exactly 2 -- for alpha far from w.  Pairing the state
+    difference with any other position breaks the slope and the count."""
+    w = np.float32(0.8)
+    c, x = _linear_cell(orc, np.array([[w]]), 31, 3, 50)
+    ref = orc.rollout(c, x)
+    sk = np.ones((1, 1), np.float32)
+    traj, iters, _, status = orc.broyden(c, x, sk, rank=1, multisecant=multisecant, alpha=-0.3, chunk=chunk,
+                                         tol=1e-12, max_iter=50, precision="f64")
+    assert np.all(status == 0) and np.all(iters == 2), iters
+    np.testing.assert_allclose(traj, ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("D", [2, 4])
+@pytest.mark.parametrize("chunk", [64, 3])
+def test_multisecant_linear_cell_recovers_the_jacobian_after_D_secants(orc, D, chunk):
+    """Linear cell f = W s + x with a diagonal-plus-low-rank W = a I + P Q^T / D
+    of full rank: every correct secant pair satisfies df = W ds exactly, so once
+    a position holds D independent secants (iteration D) the multisecant fit is
+    W itself.  Iteration D is then an exact Newton step, and the count is
+    exactly D + 1 (iteration D - 1 still uses D - 1 secants, which do not span
+    the state space).  With m = D columns the chunk re-compression is exact, so
+    the chunk size does not matter."""
+    rng = np.random.default_rng(40 + D)
+    P = rng.standard_normal((D, D))
+    Q = rng.standard_normal((D, D))
+    W = 0.5 * np.eye(D) + 0.4 * (P @ Q.T) / D
+    c, x = _linear_cell(orc, W, 41 + D, 2, 60)
+    ref = orc.rollout(c, x)
+    sk = I.broyden_sketch(12, D, D)
+    traj, iters, _, status = orc.broyden(c, x, sk, rank=D, multisecant=True, alpha=0.5, chunk=chunk,
+                                         tol=1e-10, max_iter=60, precision="f64")
+    assert np.all(status == 0) and np.all(iters == D + 1), iters
+    np.testing.assert_allclose(traj, ref, rtol=0, atol=1e-10)
+
+
+# ------------------------------------------------------------ Gram-Schmidt drop rule
+
+@pytest.mark.parametrize("precision", ["f64", "f32"])
+@pytest.mark.parametrize("eps,kept", [(1e-6, False), (1e-7, False), (1e-4, True), (1e-3, True)])
+def test_dplr_compression_drops_a_numerically_dependent_sketch_column(orc, precision, eps, kept):
+    """The re-compression keeps a Gram-Schmidt column only if its norm after
+    orthogonalisation exceeds 1e-5 of its norm before.  A hand-built chunk
+    aggregate (D = 4, m = 2, alpha = 0, chunks of 2) with
+        L = [e1, e2],  R = [e3, e4]
+    and a sketch that makes Y = L R^T Omega = [e1, e1 + eps e2] (every product
+    exact in float32): for eps below the threshold the second column is
+    dropped and the carried correction is e1 e3^T, so the entry of the third
+    chunk is e1 (R^T (e3 + e4) = (1, 1)); above it the correction stays
+    L R^T and the entry is e1 + e2, the dense product."""
+    D, m, T = 4, 2, 6
+    e = np.eye(D)
+    U = np.zeros((1, T, m, D)); V = np.zeros((1, T, m, D)); cc = np.zeros((1, T, D))
+    cc[0, 1] = e[2] + e[3]                       # entry of chunk 1 = c_1
+    U[0, 2] = [e[0], e[1]]; V[0, 2] = [e[2], e[3]]          # A_2 = e1 e3^T + e2 e4^T
+    for t in (3, 4, 5):                                      # projector onto span(e1, e2)
+        U[0, t] = [e[0], e[1]]; V[0, t] = [e[0], e[1]]
+    sk = np.array([[0.3, -0.7], [0.9, 0.2], [1.0, 1.0], [0.0, eps]], np.float32)
+    got = orc.dplr_scan(0.0, U, V, cc, sk, chunk=2, precision=precision)
+    exact = _dense_scan(0.0, U, V, cc)
+    np.testing.assert_array_equal(exact[0, 4], [1.0, 1.0, 0.0, 0.0])
+    want = [1.0, 1.0, 0.0, 0.0] if kept else [1.0, 0.0, 0.0, 0.0]
+    tol = 1e-12 if precision == "f64" else 1e-5
+    np.testing.assert_allclose(got[0, 4], want, rtol=0, atol=tol)
+    np.testing.assert_allclose(got[0, 5], want, rtol=0, atol=tol)
+    # the first two chunks never see a compressed carry
+    np.testing.assert_allclose(got[0, :4], exact[0, :4], rtol=0, atol=tol)

@@ -418,6 +418,29 @@ def test_lle_tanh_contraction_bound(orc):
         assert np.all(lam <= math.log(abs(float(np.float32(w)))) + 1e-12)
 
 
+def test_lle_scalar_tanh_closed_form_fixes_the_time_index(orc):
+    """Scalar tanh cell s_t = tanh(w s_{t-1} + u x_t + b): the Jacobian of step t,
+    taken at the state entering it, is w (1 - s_t^2) with s_t the state it
+    produces, so over a few steps lambda = (1/T) sum_t ln|w (1 - s_t^2)|
+    exactly (one-dimensional, so the renormalisation cancels).  Evaluating
+    step t's Jacobian at s_t instead of s_{t-1} gives another value."""
+    w, u, b = np.float32(1.3), np.float32(0.9), np.float32(0.2)
+    c = orc.Cell("tanh", np.array([[w]], np.float32), np.array([[u]], np.float32), np.array([b], np.float32))
+    for T in (1, 2, 3):
+        x = np.random.default_rng(30 + T).standard_normal((2, T, 1)).astype(np.float32)
+        s0 = np.array([[0.4], [-0.6]], np.float32)
+        traj = np.zeros((2, T, 1))
+        want = np.zeros(2)
+        for bi in range(2):
+            s = float(s0[bi, 0])
+            for t in range(T):
+                s = math.tanh(float(w) * s + float(u) * float(x[bi, t, 0]) + float(b))
+                traj[bi, t, 0] = s
+                want[bi] += math.log(abs(float(w) * (1.0 - s * s))) / T
+        lam = orc.lle(c, x, traj, np.ones((2, 1), np.float32), s0=s0)
+        np.testing.assert_allclose(lam, want, rtol=0, atol=1e-12)
+
+
 # ----------------------------------------------------------------- regimes
 
 def test_iterations_grow_with_unpredictability(orc):

@@ -487,6 +487,25 @@ int check_workspace(void *ws, size_t have, size_t need, const char *who)
     return DEER_OK;
 }
 
+
+// Arguments shared by linear_scan_diag and linear_scan_diag_noalloc; *empty is
+// set when there is nothing to do.
+int check_diag_scan_args(const float *a, const float *b, const float *s, int B, int T, int D, const char *who,
+                         bool *empty)
+{
+    *empty = false;
+    int rc = check_sizes(B, T);
+    if (rc) return rc;
+    if (D < 1) return fail(DEER_ERR_INVALID, std::string(who) + ": D must be >= 1");
+    if (B == 0 || T == 0) { *empty = true; return DEER_OK; }
+    if (!a || !b || !s) return fail(DEER_ERR_INVALID, std::string(who) + ": null a, b or s");
+    if (s == a || s == b) return fail(DEER_ERR_INVALID, std::string(who) + ": s must not alias a or b");
+    if (D % 4 == 0 && ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b) |
+                        reinterpret_cast<uintptr_t>(s)) % 16 != 0))
+        return fail(DEER_ERR_INVALID, std::string(who) + ": a, b and s must be 16-byte aligned");
+    return DEER_OK;
+}
+
 }  // namespace
 }  // namespace deer
 
@@ -541,18 +560,31 @@ int linear_scan_workspace_size(int B, int T, int D, int dense, size_t *bytes_out
 int linear_scan_diag(const float *a, const float *b, const float *s0, float *s, int B, int T, int D,
                      void *workspace, size_t ws_bytes, void *stream)
 {
-    int rc = check_sizes(B, T);
-    if (rc) return rc;
-    if (D < 1) return fail(DEER_ERR_INVALID, "linear_scan_diag: D must be >= 1");
-    if (B == 0 || T == 0) return DEER_OK;
-    if (!a || !b || !s) return fail(DEER_ERR_INVALID, "linear_scan_diag: null a, b or s");
-    if (s == a || s == b) return fail(DEER_ERR_INVALID, "linear_scan_diag: s must not alias a or b");
-    if (D % 4 == 0 && ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b) |
-                        reinterpret_cast<uintptr_t>(s)) % 16 != 0))
-        return fail(DEER_ERR_INVALID, "linear_scan_diag: a, b and s must be 16-byte aligned");
+    bool empty = false;
+    int rc = check_diag_scan_args(a, b, s, B, T, D, "linear_scan_diag", &empty);
+    if (rc || empty) return rc;
     rc = check_workspace(workspace, ws_bytes, diag_scan_state_bytes(B, T, D), "linear_scan_diag");
     if (rc) return rc;
     return launch_diag_scan(a, b, s0, s, s, nullptr, nullptr, nullptr, B, T, D, workspace,
+                            static_cast<hipStream_t>(stream));
+}
+
+int linear_scan_diag_noalloc(const float *a, const float *b, const float *s0, float *s, int B, int T, int D,
+                             void *stream)
+{
+    bool empty = false;
+    int rc = check_diag_scan_args(a, b, s, B, T, D, "linear_scan_diag_noalloc", &empty);
+    if (rc || empty) return rc;
+    const size_t need = diag_scan_state_bytes(B, T, D);
+    if (need > static_cast<size_t>(DEER_NOALLOC_SCRATCH_BYTES))
+        return fail(DEER_ERR_UNSUPPORTED, "linear_scan_diag_noalloc: this problem needs " + std::to_string(need) +
+                                              " bytes of look-back state, above the static scratch of " +
+                                              std::to_string(static_cast<size_t>(DEER_NOALLOC_SCRATCH_BYTES)) +
+                                              " bytes (use linear_scan_diag with a workspace)");
+    void *state = nullptr;
+    rc = diag_scan_static_state(&state, static_cast<hipStream_t>(stream));
+    if (rc) return rc;
+    return launch_diag_scan(a, b, s0, s, s, nullptr, nullptr, nullptr, B, T, D, state,
                             static_cast<hipStream_t>(stream));
 }
 

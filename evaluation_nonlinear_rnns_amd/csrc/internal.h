@@ -271,6 +271,10 @@ struct DiagScanPlan {
 };
 DiagScanPlan diag_scan_plan(int B, int T, int D);
 size_t diag_scan_state_bytes(int B, int T, int D);
+// Look-back state of the no-allocation diagonal scan: this device's address of
+// the library's static scratch array (DEER_NOALLOC_SCRATCH_BYTES), cleared on
+// the first call on a device (on `stream`, synchronised).
+int diag_scan_static_state(void **state, hipStream_t stream);
 
 // Enqueue the single-pass diagonal scan.  `out_sel` (device int or null)
 // selects out1 when odd, out0 otherwise; `skip` (device int[B] or null)

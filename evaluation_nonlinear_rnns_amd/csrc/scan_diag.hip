@@ -37,6 +37,7 @@
 // being processed.  The wait is bounded all the same; if the bound is hit the
 // header's abort flag is set and the chunk's carry becomes NaN.
 #include <algorithm>
+#include <mutex>
 
 #include "internal.h"
 
@@ -248,10 +249,48 @@ int persistent_capacity(DiagKind k)
     return slot;
 }
 
-constexpr int kLT4 = 16;   // VEC = 4: 16 slots x 16 steps = 256 steps per chunk
-constexpr int kLT1 = 32;   // VEC = 1: 4 slots x 32 steps = 128 steps per chunk
+// Look-back state of linear_scan_diag_noalloc: a file-scope device array
+// instead of a caller workspace.  Each device that loads the library holds its
+// own copy until the process ends.  In host code `scratch` is only a symbol
+// handle; its device address comes from hipGetSymbolAddress (per device).
+static __device__ __align__(256) unsigned char scratch[DEER_NOALLOC_SCRATCH_BYTES];
+
+__global__ void scratch_zero_kernel(unsigned *__restrict__ p, size_t nwords)
+{
+    size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+    for (; i < nwords; i += stride) p[i] = 0u;
+}
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kScratchDevices] = {};
 
 }  // namespace
+
+int diag_scan_static_state(void **state, hipStream_t stream)
+{
+    int dev = 0;
+    DEER_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kScratchDevices)
+        return fail(DEER_ERR_UNSUPPORTED, "linear_scan_diag_noalloc: device index above 63");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        // Once per device: take this device's address of the array and clear it
+        // (a zero header and zero descriptors: no descriptor carries a valid tag,
+        // and every later launch leaves the header ready for the next one).
+        void *ptr = nullptr;
+        DEER_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+        if (!ptr) return fail(DEER_ERR_HIP, "linear_scan_diag_noalloc: no device address for the scratch array");
+        const size_t words = DEER_NOALLOC_SCRATCH_BYTES / 4;
+        hipLaunchKernelGGL(scratch_zero_kernel, dim3(1024), dim3(256), 0, stream, static_cast<unsigned *>(ptr), words);
+        DEER_HIP(hipGetLastError());
+        DEER_HIP(hipStreamSynchronize(stream));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *state = g_scratch_ptr[dev];
+    return DEER_OK;
+}
 
 DiagScanPlan diag_scan_plan(int B, int T, int D)
 {

@@ -35,7 +35,7 @@ ERRORS = {-1: "DEER_ERR_INVALID", -2: "DEER_ERR_UNSUPPORTED", -3: "DEER_ERR_WORK
 
 # Every symbol include/deer.h declares.
 EXPORTS = ("deer_workspace_size", "deer_workspace_init", "deer_solve", "linear_scan_workspace_size",
-           "linear_scan_diag", "linear_scan_dense", "deer_rollout", "deer_lle_workspace_size", "deer_lle",
+           "linear_scan_diag", "linear_scan_diag_noalloc", "linear_scan_dense", "deer_rollout", "deer_lle_workspace_size", "deer_lle",
            "deer_broyden_workspace_size", "deer_solve_broyden", "linear_scan_dplr_workspace_size",
            "linear_scan_dplr", "deer_profile_enable", "deer_profile_read", "deer_last_error")
 
@@ -78,6 +78,7 @@ def load_library():
                         vp, vp, c_size, vp], c_int),
         "linear_scan_workspace_size": ([c_int, c_int, c_int, c_int, ctypes.POINTER(c_size)], c_int),
         "linear_scan_diag": ([vp, vp, vp, vp, c_int, c_int, c_int, vp, c_size, vp], c_int),
+        "linear_scan_diag_noalloc": ([vp, vp, vp, vp, c_int, c_int, c_int, vp], c_int),
         "linear_scan_dense": ([vp, vp, vp, vp, c_int, c_int, c_int, vp, c_size, vp], c_int),
         "deer_rollout": ([ctypes.POINTER(CellParams), vp, vp, c_int, c_int, vp, vp], c_int),
         "deer_lle_workspace_size": ([ctypes.POINTER(CellParams), c_int, c_int, ctypes.POINTER(c_size)], c_int),
@@ -254,6 +255,23 @@ def linear_scan_diag(a, b, s0=None, out=None, workspace=None, stream=None):
                                 _dev(out, "out", shape=(B, T, D)), B, T, D,
                                 _dev(workspace, "workspace", dtype=workspace.dtype),
                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+DEER_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def linear_scan_diag_noalloc(a, b, s0=None, out=None, stream=None):
+    """``linear_scan_diag`` without a workspace: the look-back state lives in the
+    library's static device array (``DEER_NOALLOC_SCRATCH_BYTES``); ``out`` must be
+    given by callers that cannot allocate.  Returns ``s``."""
+    import torch
+    lib = load_library()
+    B, T, D = (int(v) for v in a.shape)
+    if out is None:
+        out = torch.empty_like(a)
+    _check(lib.linear_scan_diag_noalloc(_dev(a, "a"), _dev(b, "b", shape=(B, T, D)), _dev(s0, "s0", shape=(B, D)),
+                                        _dev(out, "out", shape=(B, T, D)), B, T, D, _stream(stream)))
     return out
 
 

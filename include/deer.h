@@ -20,7 +20,8 @@
  *   - `stream` is a hipStream_t (NULL = the legacy default stream).  All work
  *     is enqueued on it; outputs are complete once the stream is synchronised.
  *   - The library never allocates or frees caller memory and keeps no pointer
- *     after a call returns.  Scratch memory comes from the caller's workspace.
+ *     after a call returns.  Scratch memory comes from the caller's workspace
+ *     (linear_scan_diag_noalloc: from a static device array instead).
  *   - Return value: DEER_OK (0) on success, DEER_NOT_CONVERGED (1) when
  *     deer_solve ran to max_iter for at least one sequence (a result, not an
  *     error), a negative DEER_ERR_* code otherwise.  After a negative return
@@ -186,6 +187,27 @@ int linear_scan_workspace_size(int B, int T, int D, int dense, size_t *bytes_out
  */
 int linear_scan_diag(const float *a, const float *b, const float *s0, float *s, int B, int T, int D,
                      void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * linear_scan_diag for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same scan and the same results bit for bit, with the look-back state in
+ * a static device array of DEER_NOALLOC_SCRATCH_BYTES that the library holds
+ * on every device it runs on until the process ends.  Neither this call nor
+ * the kernels it launches allocate anything.
+ *   Arguments as linear_scan_diag, without the workspace.
+ *   Size limit: linear_scan_workspace_size(B, T, D, 0) must not exceed
+ *   DEER_NOALLOC_SCRATCH_BYTES (about 3.5e8 elements for D a multiple of 4,
+ *   a quarter of that otherwise); larger problems return
+ *   DEER_ERR_UNSUPPORTED.
+ *   The first call on a device clears the array and synchronises `stream`
+ *   once.  All calls on one device share the array: calls that may overlap on
+ *   one GPU (different streams or host threads) race and must be serialised
+ *   by the caller.
+ */
+#define DEER_NOALLOC_SCRATCH_BYTES (64u << 20)
+int linear_scan_diag_noalloc(const float *a, const float *b, const float *s0, float *s, int B, int T, int D,
+                             void *stream);
 
 /*
  * Scan of the dense affine recurrence s_t = A_t s_{t-1} + b_t, s_{-1} = s0,

@@ -107,6 +107,25 @@ def test_scan_argument_checks(deer):
     assert lib.linear_scan_dense(fake, fake, None, ctypes.c_void_p(0x2000), 1, 10, 65, fake, 1 << 20, None) == -2
 
 
+def test_noalloc_scan_argument_checks(deer):
+    """The no-allocation scan checks its arguments like linear_scan_diag and
+    refuses, before any device call, a problem whose look-back state exceeds
+    the static array."""
+    lib = deer.load_library()
+    a, b, s = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000)
+    assert lib.linear_scan_diag_noalloc(None, None, None, None, 0, 10, 4, None) == 0
+    assert lib.linear_scan_diag_noalloc(None, b, None, s, 1, 10, 4, None) == -1
+    assert lib.linear_scan_diag_noalloc(a, b, None, a, 1, 10, 4, None) == -1
+    assert lib.linear_scan_diag_noalloc(ctypes.c_void_p(0x1004), b, None, s, 1, 10, 4, None) == -1
+    assert lib.linear_scan_diag_noalloc(a, b, None, s, 1, 10, 0, None) == -1
+    for B, T, D in ((64, 131072, 256), (64, 131072, 37)):
+        assert deer.linear_scan_workspace_size(B, T, D) > deer.DEER_NOALLOC_SCRATCH_BYTES
+        assert lib.linear_scan_diag_noalloc(a, b, None, s, B, T, D, None) == -2
+        assert b"static scratch" in lib.deer_last_error()
+    # the largest problems that fit are far from trivial
+    assert deer.linear_scan_workspace_size(8, 131072, 256) <= deer.DEER_NOALLOC_SCRATCH_BYTES
+
+
 def test_solve_argument_checks(deer):
     lib = deer.load_library()
     p = _params(deer)

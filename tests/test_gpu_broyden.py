@@ -204,7 +204,7 @@ def test_broyden_damping_and_workspace_reuse(orc):
 def test_full_gru_broyden(orc):
     """The benchmark's configuration on the full GRU workload (B=16, T=65536,
     D=64): converged; iteration counts within two of the oracle's float32 run
-    (stored by tests/golden/make_golden.py); sampled sequences match the
+    (stored by tests/golden/make_golden.py); every sequence matches the
     oracle's float64 rollout."""
     import json
     import os
@@ -223,9 +223,8 @@ def test_full_gru_broyden(orc):
     torch.cuda.synchronize()
     assert rc == deer.DEER_OK and np.all(status == 0)
     assert np.all(np.abs(iters - np.asarray(gold["iters_f32"])) <= 2), (iters, gold["iters_f32"])
-    seqs = [0, 7, 15]
-    ref = orc.rollout(orc.Cell.from_problem(p), p["x"][seqs])
-    assert np.all(rel_linf(traj[seqs].cpu().numpy(), ref) <= TOL)
+    ref = orc.rollout(orc.Cell.from_problem(p), p["x"])
+    assert np.all(rel_linf(traj.cpu().numpy(), ref) <= TOL)
 
 
 @pytest.mark.parametrize("T,D,chunk", [(1, 8, 32), (32, 8, 32), (33, 8, 32), (100, 1, 16), (257, 3, 64)])

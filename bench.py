@@ -176,6 +176,53 @@ def scan_bandwidth(args, dev):
             "elements_per_s": w.B * w.T * w.D / (ms * 1e-3)}
 
 
+def host_info():
+    """Host CPU model and the logical CPUs this process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"cpu_model": model, "nproc": int(avail)}
+
+
+def _stats(times_s):
+    t = np.asarray(times_s, dtype=np.float64)
+    return float(np.median(t)), float(np.mean(t))
+
+
+def gpu_rollout_timer(cell, x, B, T, D, dev, stream):
+    """The sequential GPU rollout (deer_rollout) with its buffers allocated once:
+    returns (ms per rollout, trajectory tensor)."""
+    import torch
+    from evaluation_nonlinear_rnns_amd import deer
+    seq = torch.empty((B, T, D), dtype=torch.float32, device=dev)
+    ws = deer.new_workspace(deer.rollout_workspace_size(cell, B, T), device=dev)
+    roll = lambda: deer.deer_rollout(cell, x, None, out=seq, workspace=ws, stream=stream)  # noqa: E731
+    ms, _, _ = _time_solves(roll, 10, stream, profile=False)
+    return ms, seq
+
+
+def cpu_rollout_timed(p, threads, runs=5, steps=None):
+    """The oracle's float32 sequential rollout on the host: one warm-up run,
+    then `runs` timed runs; returns (median s, mean s) per run."""
+    from oracle import oracle as O
+    cell = O.Cell.from_problem(p)
+    xs = p["x"] if steps is None else np.ascontiguousarray(p["x"][:, :steps])
+    O.rollout(cell, xs, precision="f32", threads=threads)
+    times = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        O.rollout(cell, xs, precision="f32", threads=threads)
+        times.append(time.perf_counter() - t0)
+    return _stats(times)
+
+
 def _time_solves(step, reps, stream, profile=True, budget_ms=None):
     """Mean wall time of `reps` calls after one warm-up call.  With `profile`
     the library's per-launch HIP events are on during the timed calls (their
@@ -351,6 +398,7 @@ def gain_sweep(args, dev):
 
     w = I.WORKLOADS["tanh_d16_t4096_sweep"]
     stream = torch.cuda.current_stream()
+    cpu_threads = min(w.B, host_info()["nproc"])
     rows = []
     for g in w.gains:
         p = I.workload_problem(w.name, gain=g)
@@ -366,23 +414,34 @@ def gain_sweep(args, dev):
 
         ms, _, res = _time_solves(step, 3 if f64 else 20, stream, profile=False)
         _, iters, _, status, rc = res
-        seq = torch.empty_like(out)
-
-        def roll():
-            return deer.deer_rollout(cell, x, None, out=seq, stream=stream)
-
-        ms_seq, _, _ = _time_solves(roll, 10, stream, profile=False)
+        ms_seq, _ = gpu_rollout_timer(cell, x, w.B, w.T, w.D, dev, stream)
         v0 = torch.from_numpy(I.lle_probe(50, w.B, w.D)).to(dev)
         lle_out = torch.empty(w.B, dtype=torch.float64, device=dev)
         ms_lle, _, _ = _time_solves(lambda: deer.deer_lle(cell, x, out, v0, out=lle_out, stream=stream), 10, stream,
                                     profile=False)
-        rows.append({"gain": g, "scan_f64": f64, "rc": int(rc), "iterations_max": int(iters.max()),
-                     "iterations_median": float(np.median(iters)), "deer_ms": round(ms, 3),
-                     "rollout_ms": round(ms_seq, 3), "speedup_vs_rollout": round(ms_seq / ms, 3),
-                     "lle_mean": round(float(lle_out.mean().item()), 4), "lle_ms": round(ms_lle, 3)})
-    slower = [r["gain"] for r in rows if r["speedup_vs_rollout"] < 1.0]
-    return {"workload": w.name, "B": w.B, "T": w.T, "D": w.D, "rows": rows,
-            "crossover_gain": min(slower) if slower else None}
+        row = {"gain": g, "scan_f64": f64, "rc": int(rc), "iterations_max": int(iters.max()),
+               "iterations_median": float(np.median(iters)), "deer_ms": round(ms, 3),
+               "gpu_rollout_ms": round(ms_seq, 4), "speedup_vs_gpu_rollout": round(ms_seq / ms, 3),
+               "lle_mean": round(float(lle_out.mean().item()), 4), "lle_ms": round(ms_lle, 3)}
+        if not args.no_cpu:
+            med, mean = cpu_rollout_timed(p, cpu_threads)
+            row.update({"cpu_rollout_ms_median": round(med * 1e3, 3), "cpu_rollout_ms_mean": round(mean * 1e3, 3),
+                        "speedup_vs_cpu_rollout": round(med * 1e3 / ms, 3)})
+        rows.append(row)
+    out = {"workload": w.name, "B": w.B, "T": w.T, "D": w.D, "rows": rows,
+           "crossover_vs_gpu_rollout": _crossover(rows, "speedup_vs_gpu_rollout")}
+    if not args.no_cpu:
+        out["crossover_vs_cpu_rollout"] = _crossover(rows, "speedup_vs_cpu_rollout")
+        out["cpu"] = dict(host_info(), threads=cpu_threads,
+                          timing="oracle float32 rollout of all sequences, median and mean of 5 runs after 1 warm-up")
+    return out
+
+
+def _crossover(rows, key):
+    """The gain bracket (largest swept gain where DEER is faster, smallest where it is slower)."""
+    faster = [r["gain"] for r in rows if r[key] >= 1.0]
+    slower = [r["gain"] for r in rows if r[key] < 1.0]
+    return {"faster_up_to": max(faster) if faster else None, "slower_from": min(slower) if slower else None}
 
 
 def linearizations(args, dev):
@@ -409,9 +468,7 @@ def linearizations(args, dev):
         x = torch.from_numpy(p["x"]).to(dev)
         del p
         traj = torch.empty((w.B, w.T, w.D), dtype=torch.float32, device=dev)
-        seq = torch.empty_like(traj)
-        ms_seq, _, _ = _time_solves(lambda: deer.deer_rollout(cell, x, None, out=seq, stream=stream), 10, stream,
-                                    profile=False)
+        ms_seq, seq = gpu_rollout_timer(cell, x, w.B, w.T, w.D, dev, stream)
         rows = {}
         for label, mode, k in runs:
             ws = deer.new_workspace(deer.deer_workspace_size(cell, w.B, w.T, mode), device=dev)
@@ -424,13 +481,13 @@ def linearizations(args, dev):
             ms, _, res = _time_solves(step, 10, stream, profile=False, budget_ms=300.0)
             _, iters, _, status, rc = res
             rows[label] = {"mode": mode, "damping": k, "rc": int(rc), "iterations_max": int(iters.max()),
-                           "ms_per_solve": round(ms, 3), "speedup_vs_rollout": round(ms_seq / ms, 3)}
+                           "ms_per_solve": round(ms, 3), "speedup_vs_gpu_rollout": round(ms_seq / ms, 3)}
             del ws
         v0 = torch.from_numpy(I.lle_probe(60, w.B, w.D)).to(dev)
         lle_out = torch.empty(w.B, dtype=torch.float64, device=dev)
         ms_lle, _, _ = _time_solves(lambda: deer.deer_lle(cell, x, seq, v0, out=lle_out, stream=stream), 10, stream,
                                     profile=False)
-        out[name] = {"gain": gain, "B": w.B, "T": w.T, "D": w.D, "tol": w.tol, "rollout_ms": round(ms_seq, 3),
+        out[name] = {"gain": gain, "B": w.B, "T": w.T, "D": w.D, "tol": w.tol, "gpu_rollout_ms": round(ms_seq, 3),
                      "lle_mean_on_rollout": round(float(lle_out.mean().item()), 4), "lle_ms": round(ms_lle, 3),
                      "runs": rows}
         del traj, seq, x
@@ -438,27 +495,30 @@ def linearizations(args, dev):
 
 
 def cpu_baseline(args, w, p):
-    """The oracle's float32 sequential rollout of the same workload on the host cores."""
+    """The oracle's float32 sequential rollout of the headline workload on the
+    host cores (one thread per sequence, up to the CPUs available), one warm-up
+    run and five timed runs; if a full run would take longer than the budget, a
+    prefix of every sequence is timed instead.  Also one sequence on one thread."""
     from oracle import oracle as O
 
+    info = host_info()
+    threads = min(w.B, info["nproc"])
     cell = O.Cell.from_problem(p)
-    threads = min(w.B, O.max_threads())
-    # calibrate on a short prefix, then run a bounded sample of about cpu_seconds:
-    # the whole workload repeated, or a prefix of it if one pass is longer
+    # calibrate on a short prefix: the 6 runs should take about cpu_seconds
     Tc = 2048
     t0 = time.perf_counter()
     O.rollout(cell, p["x"][:, :Tc], precision="f32", threads=threads)
     per_step = (time.perf_counter() - t0) / Tc
-    Ts = int(min(w.T, max(Tc, args.cpu_seconds / max(per_step, 1e-9))))
-    reps = max(1, int(round(args.cpu_seconds / max(per_step * Ts, 1e-9)))) if Ts == w.T else 1
-    xs = p["x"][:, :Ts]
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        O.rollout(cell, xs, precision="f32", threads=threads)
-    dt = time.perf_counter() - t0
-    return {"value": round(reps * w.B * Ts / dt, 1), "unit": "B*T/s", "cores": threads, "kind": "oracle",
-            "sample": f"float32 sequential rollout of all {w.B} sequences over {Ts} of {w.T} steps, "
-                      f"{reps} pass(es), {dt:.1f} s, one thread per sequence"}
+    Ts = int(min(w.T, max(Tc, args.cpu_seconds / 6.0 / max(per_step, 1e-9))))
+    med, mean = cpu_rollout_timed(p, threads, runs=5, steps=Ts)
+    one = dict(p, x=np.ascontiguousarray(p["x"][:1]))
+    med1, _ = cpu_rollout_timed(one, 1, runs=3, steps=Ts)
+    return {"value": round(w.B * Ts / med, 1), "unit": "B*T/s", "cores": threads, "kind": "oracle",
+            "sample": f"float32 sequential rollout of all {w.B} sequences over {Ts} of {w.T} steps, one thread "
+                      f"per sequence; median of 5 runs after 1 warm-up ({med:.2f} s per run, mean {mean:.2f} s)",
+            "value_mean": round(w.B * Ts / mean, 1), "cpu_model": info["cpu_model"], "nproc": info["nproc"],
+            "single_thread_value": round(Ts / med1, 1),
+            "single_thread_sample": f"one sequence over {Ts} steps on one thread, median of 3 runs after 1 warm-up"}
 
 
 def main():

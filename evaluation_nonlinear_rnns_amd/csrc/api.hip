@@ -614,8 +614,20 @@ int deer_workspace_size(const deer_cell_params_t *p, int B, int T, int mode_flag
     return DEER_OK;
 }
 
+int deer_rollout_workspace_size(const deer_cell_params_t *p, int B, int T, size_t *bytes_out)
+{
+    if (!bytes_out) return fail(DEER_ERR_INVALID, "deer_rollout_workspace_size: null output");
+    if (!p) return fail(DEER_ERR_INVALID, "cell parameters: null pointer");
+    int rc = check_cell(p, p->cell == DEER_CELL_GRU ? DEER_MODE_DIAG : DEER_MODE_DENSE);
+    if (rc) return rc;
+    rc = check_sizes(B, T);
+    if (rc) return rc;
+    *bytes_out = rollout_workspace_bytes(p, B, T);
+    return DEER_OK;
+}
+
 int deer_rollout(const deer_cell_params_t *p, const float *x, const float *s0, int B, int T, float *traj_out,
-                 void *stream)
+                 void *workspace, size_t ws_bytes, void *stream)
 {
     if (!p) return fail(DEER_ERR_INVALID, "cell parameters: null pointer");
     int rc = check_cell(p, p->cell == DEER_CELL_GRU ? DEER_MODE_DIAG : DEER_MODE_DENSE);
@@ -624,7 +636,9 @@ int deer_rollout(const deer_cell_params_t *p, const float *x, const float *s0, i
     if (rc) return rc;
     if (B == 0 || T == 0) return DEER_OK;
     if (!x || !traj_out) return fail(DEER_ERR_INVALID, "deer_rollout: null x or traj_out");
-    return launch_rollout(p, x, s0, B, T, traj_out, static_cast<hipStream_t>(stream));
+    rc = check_workspace(workspace, ws_bytes, rollout_workspace_bytes(p, B, T), "deer_rollout");
+    if (rc) return rc;
+    return launch_rollout(p, x, s0, B, T, traj_out, workspace, static_cast<hipStream_t>(stream));
 }
 
 int deer_lle_workspace_size(const deer_cell_params_t *p, int B, int T, size_t *bytes_out)

@@ -301,70 +301,6 @@ __global__ __launch_bounds__(kThreads) void gru_eval_kernel(
     block_max_to(rmax, res_bits + bseq);
 }
 
-// ------------------------------------------------------ sequential rollout
-// One wavefront per sequence steps s_t = f(s_{t-1}, x_t) forward; weights in LDS.
-template <int DP, bool GRU>
-__global__ __launch_bounds__(kThreads) void rollout_kernel(const float *__restrict__ W, const float *__restrict__ U,
-                                                           const float *__restrict__ b, const float *__restrict__ b2,
-                                                           const float *__restrict__ x, const float *__restrict__ s0,
-                                                           float *__restrict__ traj, int B, int T, int D, int M)
-{
-    constexpr int NG = GRU ? 3 : 1;
-    __shared__ float Wt[DP][NG * DP];    // Wt[k][g*DP + c] = W[g*D + c][k]
-    __shared__ float Ut[64][NG * DP];    // Ut[j][g*DP + c] = U[g*D + c][j]  (M <= 64)
-    for (int e = threadIdx.x; e < NG * DP * DP; e += kThreads) {
-        const int row = e / DP, k = e % DP, g = row / DP, c = row % DP;
-        Wt[k][row] = (k < D && c < D) ? W[static_cast<size_t>(g * D + c) * D + k] : 0.0f;
-    }
-    for (int e = threadIdx.x; e < NG * DP * 64; e += kThreads) {
-        const int row = e / 64, j = e % 64, g = row / DP, c = row % DP;
-        Ut[j][row] = (j < M && c < D) ? U[static_cast<size_t>(g * D + c) * M + j] : 0.0f;
-    }
-    __syncthreads();
-    const int lane = threadIdx.x & 63;
-    const int bseq = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-    if (bseq >= B) return;
-    const bool cv = lane < D;
-    const int c = lane < DP ? lane : 0;
-    float bi[NG], bh[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-        bi[g] = (cv && b) ? b[g * D + c] : 0.0f;
-        bh[g] = (cv && b2) ? b2[g * D + c] : 0.0f;
-    }
-    float st = (cv && s0) ? s0[static_cast<size_t>(bseq) * D + lane] : 0.0f;
-    const size_t xb = static_cast<size_t>(bseq) * T * M;
-    const size_t ob = static_cast<size_t>(bseq) * T * D;
-    for (int t = 0; t < T; ++t) {
-        const float xl = (lane < M) ? x[xb + static_cast<size_t>(t) * M + lane] : 0.0f;
-        float gi[NG], gh[NG];
-#pragma unroll
-        for (int g = 0; g < NG; ++g) { gi[g] = bi[g]; gh[g] = bh[g]; }
-        for (int j = 0; j < M; ++j) {
-            const float xj = __shfl(xl, j, 64);
-#pragma unroll
-            for (int g = 0; g < NG; ++g) gi[g] += Ut[j][g * DP + c] * xj;
-        }
-#pragma unroll
-        for (int k = 0; k < DP; ++k) {
-            const float sk = __shfl(st, k, 64);
-#pragma unroll
-            for (int g = 0; g < NG; ++g) gh[g] += Wt[k][g * DP + c] * sk;
-        }
-        float f;
-        if constexpr (GRU) {
-            const float rg = sigmoidf_(gi[0] + gh[0]);
-            const float zg = sigmoidf_(gi[1] + gh[1]);
-            const float ng = tanhf(gi[2] + rg * gh[2]);
-            f = (1.0f - zg) * ng + zg * st;
-        } else {
-            f = tanhf(gi[0] + gh[0]);
-        }
-        st = cv ? f : 0.0f;
-        if (cv) traj[ob + static_cast<size_t>(t) * D + lane] = st;
-    }
-}
-
 int pick_dp(int D) { return D <= 4 ? 4 : D <= 8 ? 8 : D <= 16 ? 16 : D <= 32 ? 32 : 64; }
 
 unsigned eval_blocks(int B, int T, int &tiles)
@@ -453,33 +389,6 @@ int launch_gru_eval(const float *Whh, const float *bhh, const float *p, const fl
         DEER_GRU_CASE(16)
         DEER_GRU_CASE(32)
         DEER_GRU_CASE(64)
-    }
-    DEER_HIP(hipGetLastError());
-    return DEER_OK;
-}
-
-#define DEER_ROLL_CASE(DPV)                                                                                      \
-    case DPV:                                                                                                    \
-        if (gru)                                                                                                 \
-            DEER_LAUNCH((rollout_kernel<DPV, true>), dim3(blocks), dim3(kThreads), 0, stream, p->W, p->U, \
-                               p->b, p->b2, x, s0, traj, B, T, p->D, p->M);                                      \
-        else                                                                                                     \
-            DEER_LAUNCH((rollout_kernel<DPV, false>), dim3(blocks), dim3(kThreads), 0, stream, p->W,      \
-                               p->U, p->b, p->b2, x, s0, traj, B, T, p->D, p->M);                                \
-        break;
-
-int launch_rollout(const deer_cell_params_t *p, const float *x, const float *s0, int B, int T, float *traj,
-                   hipStream_t stream)
-{
-    if (p->M > 64) return fail(DEER_ERR_UNSUPPORTED, "deer_rollout: input size above 64");
-    const bool gru = p->cell == DEER_CELL_GRU;
-    const unsigned blocks = static_cast<unsigned>((B + 3) / 4);
-    switch (pick_dp(p->D)) {
-        DEER_ROLL_CASE(4)
-        DEER_ROLL_CASE(8)
-        DEER_ROLL_CASE(16)
-        DEER_ROLL_CASE(32)
-        DEER_ROLL_CASE(64)
     }
     DEER_HIP(hipGetLastError());
     return DEER_OK;

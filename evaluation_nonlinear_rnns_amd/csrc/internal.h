@@ -370,8 +370,11 @@ int launch_gru_quasi_step(const float *Whh, const float *bhh, const float *pt, c
                           float tol, int max_iter, unsigned *res_bits, unsigned *res_tile, int B, int T, int D,
                           bool zero_start, Linearization lz, void *state, hipStream_t stream);
 
+// Sequential rollout (rollout.hip): the projection into `workspace`
+// (rollout_workspace_bytes), then one workgroup per sequence.
+size_t rollout_workspace_bytes(const deer_cell_params_t *p, int B, int T);
 int launch_rollout(const deer_cell_params_t *p, const float *x, const float *s0, int B, int T,
-                   float *traj, hipStream_t stream);
+                   float *traj, void *workspace, hipStream_t stream);
 
 // Whole tanh solves in one launch (tiny.hip): one workgroup per sequence forms
 // its input projection and runs every iteration on chip; for D <= 4 and

@@ -35,7 +35,8 @@ ERRORS = {-1: "DEER_ERR_INVALID", -2: "DEER_ERR_UNSUPPORTED", -3: "DEER_ERR_WORK
 
 # Every symbol include/deer.h declares.
 EXPORTS = ("deer_workspace_size", "deer_workspace_init", "deer_solve", "linear_scan_workspace_size",
-           "linear_scan_diag", "linear_scan_diag_noalloc", "linear_scan_dense", "deer_rollout", "deer_lle_workspace_size", "deer_lle",
+           "linear_scan_diag", "linear_scan_diag_noalloc", "linear_scan_dense", "deer_rollout_workspace_size",
+           "deer_rollout", "deer_lle_workspace_size", "deer_lle",
            "deer_broyden_workspace_size", "deer_solve_broyden", "linear_scan_dplr_workspace_size",
            "linear_scan_dplr", "deer_profile_enable", "deer_profile_read", "deer_last_error")
 
@@ -80,7 +81,8 @@ def load_library():
         "linear_scan_diag": ([vp, vp, vp, vp, c_int, c_int, c_int, vp, c_size, vp], c_int),
         "linear_scan_diag_noalloc": ([vp, vp, vp, vp, c_int, c_int, c_int, vp], c_int),
         "linear_scan_dense": ([vp, vp, vp, vp, c_int, c_int, c_int, vp, c_size, vp], c_int),
-        "deer_rollout": ([ctypes.POINTER(CellParams), vp, vp, c_int, c_int, vp, vp], c_int),
+        "deer_rollout_workspace_size": ([ctypes.POINTER(CellParams), c_int, c_int, ctypes.POINTER(c_size)], c_int),
+        "deer_rollout": ([ctypes.POINTER(CellParams), vp, vp, c_int, c_int, vp, vp, c_size, vp], c_int),
         "deer_lle_workspace_size": ([ctypes.POINTER(CellParams), c_int, c_int, ctypes.POINTER(c_size)], c_int),
         "deer_lle": ([ctypes.POINTER(CellParams), vp, vp, vp, vp, c_int, c_int, vp, vp, c_size, vp], c_int),
         "deer_broyden_workspace_size": ([ctypes.POINTER(CellParams), c_int, c_int, ctypes.POINTER(BroydenOpts),
@@ -291,7 +293,15 @@ def linear_scan_dense(A, b, s0=None, out=None, workspace=None, stream=None):
     return out
 
 
-def deer_rollout(cell: Cell, x, s0=None, out=None, stream=None):
+def rollout_workspace_size(cell: Cell, B: int, T: int) -> int:
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    p = cell.params()
+    _check(lib.deer_rollout_workspace_size(ctypes.byref(p), B, T, ctypes.byref(n)))
+    return int(n.value)
+
+
+def deer_rollout(cell: Cell, x, s0=None, out=None, workspace=None, stream=None):
     """Sequential rollout on the GPU; returns ``traj [B,T,D]``."""
     import torch
     lib = load_library()
@@ -299,8 +309,12 @@ def deer_rollout(cell: Cell, x, s0=None, out=None, stream=None):
     p = cell.params()
     if out is None:
         out = torch.empty((B, T, cell.D), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = new_workspace(rollout_workspace_size(cell, B, T), device=x.device)
     _check(lib.deer_rollout(ctypes.byref(p), _dev(x, "x", shape=(B, T, M)), _dev(s0, "s0", shape=(B, cell.D)),
-                            B, T, _dev(out, "out", shape=(B, T, cell.D)), _stream(stream)))
+                            B, T, _dev(out, "out", shape=(B, T, cell.D)),
+                            _dev(workspace, "workspace", dtype=workspace.dtype),
+                            workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
 
 

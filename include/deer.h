@@ -223,11 +223,17 @@ int linear_scan_dense(const float *A, const float *b, const float *s0, float *s,
 /*
  * Sequential rollout s_t = f(s_{t-1}, x_t) on the GPU, one step after the
  * other (the evaluation the parallel methods are timed against on the
- * "Predictability" page, rebuttal "Comparison with sequential speed").
+ * "Predictability" page, rebuttal "Comparison with sequential speed").  The
+ * input projection U x_t + b runs first over all positions at once (it does
+ * not depend on the state); then one workgroup per sequence steps the
+ * recurrence.
  *   x device [B,T,M];  s0 device [B,D] or NULL;  traj_out device [B,T,D].
+ *   workspace device, >= deer_rollout_workspace_size bytes, 256-byte aligned
+ *   (no zero fill needed).
  */
+int deer_rollout_workspace_size(const deer_cell_params_t *p, int B, int T, size_t *bytes_out);
 int deer_rollout(const deer_cell_params_t *p, const float *x, const float *s0, int B, int T,
-                 float *traj_out, void *stream);
+                 float *traj_out, void *workspace, size_t ws_bytes, void *stream);
 
 /*
  * Largest Lyapunov exponent of the dynamics along a given trajectory, per

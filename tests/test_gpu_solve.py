@@ -227,19 +227,25 @@ def test_single_launch_edge_cases(orc):
     assert np.abs(got[1, :10] - ref[1, :10]).max() < 1e-5
 
 
-def test_sequential_rollout_matches_oracle(orc):
+@pytest.mark.parametrize("kind,B,T,D,M", [("tanh", 3, 500, 16, 16), ("gru", 3, 500, 64, 64), ("tanh", 2, 1, 4, 4),
+                                          ("tanh", 2, 7, 3, 5), ("gru", 1, 9, 5, 2), ("tanh", 2, 333, 8, 100),
+                                          ("tanh", 3, 1000, 32, 32), ("gru", 2, 777, 32, 7), ("gru", 2, 300, 16, 16),
+                                          ("tanh", 1, 2000, 64, 64), ("gru", 5, 129, 40, 40)])
+def test_sequential_rollout_matches_oracle(orc, kind, B, T, D, M):
+    """The GPU rollout (projection, then one workgroup per sequence): every
+    lane geometry (D up to 4, 8, 16, 32, 64), lengths below, at and past the
+    8-step prefetch ring, inputs wider than 64."""
     dev = device()
-    for kind in ("tanh", "gru"):
-        if kind == "tanh":
-            p = I.tanh_problem(800, 3, 500, 16, 16, gain=0.9, bias_std=0.2, s0_std=0.3)
-        else:
-            p = I.gru_problem(801, 3, 500, 64, 64, bias_std=0.2, s0_std=0.3)
-        log(f"deer_rollout {kind}")
-        cell = deer.cell_from_problem(p, dev)
-        traj = deer.deer_rollout(cell, torch.from_numpy(p["x"]).to(dev), torch.from_numpy(p["s0"]).to(dev))
-        torch.cuda.synchronize()
-        ref = orc.rollout(orc.Cell.from_problem(p), p["x"], p["s0"])
-        assert np.all(rel_linf(traj.cpu().numpy(), ref) <= TOL)
+    if kind == "tanh":
+        p = I.tanh_problem(800 + T + D, B, T, D, M, gain=0.9, bias_std=0.2, s0_std=0.3)
+    else:
+        p = I.gru_problem(801 + T + D, B, T, D, M, bias_std=0.2, s0_std=0.3)
+    log(f"deer_rollout {kind} B={B} T={T} D={D} M={M}")
+    cell = deer.cell_from_problem(p, dev)
+    traj = deer.deer_rollout(cell, torch.from_numpy(p["x"]).to(dev), torch.from_numpy(p["s0"]).to(dev))
+    torch.cuda.synchronize()
+    ref = orc.rollout(orc.Cell.from_problem(p), p["x"], p["s0"])
+    assert np.all(rel_linf(traj.cpu().numpy(), ref) <= TOL)
 
 
 # ------------------------------------------------------------- full workloads

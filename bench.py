@@ -386,12 +386,16 @@ def broyden_solve(args, dev):
 
 
 def gain_sweep(args, dev):
-    """Dense DEER against the sequential GPU rollout across the recurrent gain g.
+    """Dense DEER against the sequential rollout (GPU and the oracle's on the
+    host) across the recurrent gain g.
 
     The gain sets the largest Lyapunov exponent (estimated on the GPU along the
     solved trajectory, deer_lle); the sweep locates the g where the parallel
-    solve stops beating the sequential evaluation.  At g = 2 the linear solve
-    accumulates in double (float32 chunk products are too large).
+    solve stops beating the sequential evaluation.  Every gain runs with the
+    default options (float32; a stall of the finite-step progress switches the
+    linear solve to double accumulation).  At g = 2 the variants are reported
+    too: float32 without escalation (the stall), damped Newton k = 0.3 in
+    float32, and double accumulation from the start.
     """
     import torch
     from evaluation_nonlinear_rnns_amd import deer, inputs as I
@@ -400,26 +404,41 @@ def gain_sweep(args, dev):
     stream = torch.cuda.current_stream()
     cpu_threads = min(w.B, host_info()["nproc"])
     rows = []
+    g2 = None
     for g in w.gains:
         p = I.workload_problem(w.name, gain=g)
         cell = deer.cell_from_problem(p, dev)
         x = torch.from_numpy(p["x"]).to(dev)
-        f64 = g >= 2.0
         out = torch.empty((w.B, w.T, w.D), dtype=torch.float32, device=dev)
-        ws = deer.new_workspace(deer.deer_workspace_size(cell, w.B, w.T, w.mode, scan_f64=f64), device=dev)
+        ws = deer.new_workspace(deer.deer_workspace_size(cell, w.B, w.T, w.mode), device=dev)
 
-        def step():
-            return deer.deer_solve(cell, x, None, mode=w.mode, tol=w.tol, max_iter=w.max_iter, out=out,
-                                   workspace=ws, stream=stream, scan_f64=f64)
+        def solver(**kw):
+            def step():
+                return deer.deer_solve(cell, x, None, mode=w.mode, tol=w.tol, max_iter=w.max_iter, out=out,
+                                       workspace=ws, stream=stream, **kw)
+            return step
 
-        ms, _, res = _time_solves(step, 3 if f64 else 20, stream, profile=False)
+        # default options: float32, finite-step check, escalation to double accumulation on a stall
+        ms, _, res = _time_solves(solver(), 20, stream, profile=False, budget_ms=1500.0)
         _, iters, _, status, rc = res
+        if g >= 2.0:
+            g2 = {}
+            for label, kw in (("float32_no_escalation", {"stall_escalate": False}),
+                              ("damped_0.3_float32", {"damping": 0.3, "stall_escalate": False}),
+                              ("double_accumulation_from_start", {"scan_f64": True})):
+                ms2, _, res2 = _time_solves(solver(**kw), 3, stream, profile=False, budget_ms=1500.0)
+                _, it2, _, st2, rc2 = res2
+                g2[label] = {"options": kw, "rc": int(rc2), "iterations": [int(v) for v in it2],
+                             "status_counts": {str(k): int(v) for k, v in zip(*np.unique(st2, return_counts=True))},
+                             "ms_per_solve": round(ms2, 3)}
         ms_seq, _ = gpu_rollout_timer(cell, x, w.B, w.T, w.D, dev, stream)
         v0 = torch.from_numpy(I.lle_probe(50, w.B, w.D)).to(dev)
         lle_out = torch.empty(w.B, dtype=torch.float64, device=dev)
         ms_lle, _, _ = _time_solves(lambda: deer.deer_lle(cell, x, out, v0, out=lle_out, stream=stream), 10, stream,
                                     profile=False)
-        row = {"gain": g, "scan_f64": f64, "rc": int(rc), "iterations_max": int(iters.max()),
+        row = {"gain": g, "options": "default (float32, stall check, escalation)", "rc": int(rc),
+               "status_counts": {str(k): int(v) for k, v in zip(*np.unique(status, return_counts=True))},
+               "iterations_max": int(iters.max()),
                "iterations_median": float(np.median(iters)), "deer_ms": round(ms, 3),
                "gpu_rollout_ms": round(ms_seq, 4), "speedup_vs_gpu_rollout": round(ms_seq / ms, 3),
                "lle_mean": round(float(lle_out.mean().item()), 4), "lle_ms": round(ms_lle, 3)}
@@ -430,6 +449,8 @@ def gain_sweep(args, dev):
         rows.append(row)
     out = {"workload": w.name, "B": w.B, "T": w.T, "D": w.D, "rows": rows,
            "crossover_vs_gpu_rollout": _crossover(rows, "speedup_vs_gpu_rollout")}
+    if g2 is not None:
+        out["gain_2_variants"] = g2
     if not args.no_cpu:
         out["crossover_vs_cpu_rollout"] = _crossover(rows, "speedup_vs_cpu_rollout")
         out["cpu"] = dict(host_info(), threads=cpu_threads,

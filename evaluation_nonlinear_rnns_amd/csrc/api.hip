@@ -183,9 +183,9 @@ thread_local ResultStage g_stage;
 // synchronisation, then copied to the caller's host arrays.
 int read_results(const int *iters_dev, const int *status_dev, const float *resid_dev, const unsigned *abort_dev,
                  int B, hipStream_t stream, int *iters_out, float *resid_out, std::vector<int> &status_h,
-                 unsigned &abort_flag, const char *who)
+                 unsigned &abort_flag, const char *who, const float *rms_dev = nullptr, float *rms_out = nullptr)
 {
-    const size_t need = (2 * sizeof(int) + sizeof(float)) * static_cast<size_t>(B) + sizeof(unsigned);
+    const size_t need = (2 * sizeof(int) + 2 * sizeof(float)) * static_cast<size_t>(B) + sizeof(unsigned);
     char *st = g_stage.get(need);
     if (!st) {
         (void)hipStreamSynchronize(stream);
@@ -194,12 +194,15 @@ int read_results(const int *iters_dev, const int *status_dev, const float *resid
     int *h_iters = reinterpret_cast<int *>(st);
     int *h_status = h_iters + B;
     float *h_resid = reinterpret_cast<float *>(h_status + B);
-    unsigned *h_abort = reinterpret_cast<unsigned *>(h_resid + B);
+    float *h_rms = h_resid + B;
+    unsigned *h_abort = reinterpret_cast<unsigned *>(h_rms + B);
     *h_abort = 0u;
     int rc = DEER_OK;
     if (hipMemcpyAsync(h_iters, iters_dev, sizeof(int) * B, hipMemcpyDeviceToHost, stream) != hipSuccess ||
         hipMemcpyAsync(h_status, status_dev, sizeof(int) * B, hipMemcpyDeviceToHost, stream) != hipSuccess ||
         (resid_out && hipMemcpyAsync(h_resid, resid_dev, sizeof(float) * B, hipMemcpyDeviceToHost, stream) != hipSuccess) ||
+        (rms_out && rms_dev &&
+         hipMemcpyAsync(h_rms, rms_dev, sizeof(float) * B, hipMemcpyDeviceToHost, stream) != hipSuccess) ||
         (abort_dev && hipMemcpyAsync(h_abort, abort_dev, sizeof(unsigned), hipMemcpyDeviceToHost, stream) != hipSuccess))
         rc = fail(DEER_ERR_HIP, std::string(who) + ": result copy failed");
     const hipError_t se = hipStreamSynchronize(stream);
@@ -207,6 +210,7 @@ int read_results(const int *iters_dev, const int *status_dev, const float *resid
     if (rc) return rc;
     std::memcpy(iters_out, h_iters, sizeof(int) * B);
     if (resid_out) std::memcpy(resid_out, h_resid, sizeof(float) * B);
+    if (rms_out && rms_dev) std::memcpy(rms_out, h_rms, sizeof(float) * B);
     status_h.assign(h_status, h_status + B);
     abort_flag = *h_abort;
     return DEER_OK;
@@ -214,11 +218,51 @@ int read_results(const int *iters_dev, const int *status_dev, const float *resid
 
 // ------------------------------------------------------ small device kernels
 __global__ void init_control_kernel(SolveControl *ctl, int *done, int *iters, int *status, float *resid,
-                                    unsigned *res_bits, int B)
+                                    unsigned *res_bits, StallCheck sc, int B)
 {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i == 0) { ctl->iter = 0; ctl->all_done = 0; }
-    if (i < B) { done[i] = 0; iters[i] = 0; status[i] = 0; resid[i] = 0.0f; res_bits[i] = 0u; }
+    if (i == 0) { ctl->iter = 0; ctl->all_done = 0; ctl->escalate = 0; }
+    if (i < B) {
+        done[i] = 0; iters[i] = 0; status[i] = 0; resid[i] = 0.0f; res_bits[i] = 0u;
+        if (sc.front) { sc.front[i] = kNoFront; sc.best[i] = -1; sc.last_adv[i] = 0; }
+    }
+}
+
+// Root-mean-square residual ||s - f||_2 / sqrt(T D) per sequence, from the
+// trajectory and the value-only evaluation f of it: per (sequence, chunk)
+// partial sums in double (each thread in index order, then a fixed tree), then
+// the chunks in order -- the same bits every time.
+constexpr int kRmsChunk = 16384;
+__global__ void rms_partial_kernel(const float *__restrict__ s, const float *__restrict__ f, size_t per_seq,
+                                   int nchunk, double *__restrict__ part)
+{
+    __shared__ double red[256];
+    const int b = blockIdx.y, ch = blockIdx.x;
+    const size_t base = static_cast<size_t>(b) * per_seq;
+    const size_t e0 = static_cast<size_t>(ch) * kRmsChunk;
+    const size_t e1 = e0 + kRmsChunk < per_seq ? e0 + kRmsChunk : per_seq;
+    double acc = 0.0;
+    for (size_t e = e0 + threadIdx.x; e < e1; e += blockDim.x) {
+        const double d = static_cast<double>(s[base + e]) - static_cast<double>(f[base + e]);
+        acc += d * d;
+    }
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if (static_cast<int>(threadIdx.x) < o) red[threadIdx.x] += red[threadIdx.x + o];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) part[static_cast<size_t>(b) * nchunk + ch] = red[0];
+}
+
+__global__ void rms_final_kernel(const double *__restrict__ part, int nchunk, size_t per_seq, int B,
+                                 float *__restrict__ rms)
+{
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= B) return;
+    double acc = 0.0;
+    for (int ch = 0; ch < nchunk; ++ch) acc += part[static_cast<size_t>(b) * nchunk + ch];
+    rms[b] = static_cast<float>(sqrt(acc / static_cast<double>(per_seq)));
 }
 
 __global__ void fill_kernel(float *__restrict__ p, size_t n, float v)
@@ -244,11 +288,11 @@ __global__ void zero_words_kernel(unsigned *__restrict__ p, size_t nwords)
 
 // Convergence test of the current iteration (see finalize_iteration).
 __global__ void check_kernel(SolveControl *ctl, unsigned *res_bits, const unsigned *res_tile, int tps, int *done,
-                             int *iters, int *status, float *resid, int B, float tol, int max_iter)
+                             int *iters, int *status, float *resid, int B, float tol, int max_iter, StallCheck sc)
 {
     __shared__ unsigned red[256 / 64];
     if (ctl->all_done) return;
-    finalize_iteration(ctl, res_bits, res_tile, tps, done, iters, status, resid, B, tol, max_iter, red);
+    finalize_iteration(ctl, res_bits, res_tile, tps, done, iters, status, resid, B, tol, max_iter, red, sc);
 }
 
 // Sequences whose final iterate sits in the second buffer are copied out.  With
@@ -277,11 +321,8 @@ unsigned grid_for(size_t n, unsigned threads = 256, unsigned cap = 8192)
 }
 
 // ------------------------------------------------------ argument checks
-int check_cell(const deer_cell_params_t *p, int mode_flags)
+int check_cell(const deer_cell_params_t *p, int mode)
 {
-    const int mode = mode_flags & ~(DEER_SCAN_F64 | DEER_MULTI_LAUNCH);
-    if ((mode_flags & DEER_SCAN_F64) && mode != DEER_MODE_DENSE)
-        return fail(DEER_ERR_UNSUPPORTED, "DEER_SCAN_F64 applies to dense mode only");
     if (!p) return fail(DEER_ERR_INVALID, "cell parameters: null pointer");
     if (p->cell != DEER_CELL_TANH && p->cell != DEER_CELL_GRU)
         return fail(DEER_ERR_INVALID, "cell parameters: unknown cell " + std::to_string(p->cell));
@@ -308,6 +349,29 @@ int check_sizes(int B, int T)
 // The diagonal-block modes (diag, Jacobi, Picard) solve with the diagonal scan.
 bool diag_blocks(int mode) { return mode != DEER_MODE_DENSE; }
 
+deer_solve_opts_t solve_opts(const deer_solve_opts_t *o)
+{
+    const deer_solve_opts_t def = DEER_SOLVE_OPTS_DEFAULT;
+    return o ? *o : def;
+}
+
+int check_solve_opts(const deer_solve_opts_t &o, int mode)
+{
+    if (!(o.damping >= 0.0f && o.damping <= 1.0f)) return fail(DEER_ERR_INVALID, "damping must lie in [0, 1]");
+    if (o.damping != 0.0f && mode != DEER_MODE_DENSE && mode != DEER_MODE_DIAG)
+        return fail(DEER_ERR_INVALID, "damping applies to the dense and diag modes only");
+    if (o.scan_f64 && mode != DEER_MODE_DENSE)
+        return fail(DEER_ERR_UNSUPPORTED, "scan_f64 applies to dense mode only");
+    if (o.stall_window < 0) return fail(DEER_ERR_INVALID, "stall_window must be >= 0");
+    return DEER_OK;
+}
+
+// The dense linear solve may run in double: from the start, or after a stall.
+bool may_use_f64(const deer_solve_opts_t &o, int mode)
+{
+    return mode == DEER_MODE_DENSE && (o.scan_f64 || (o.stall_window > 0 && o.stall_escalate));
+}
+
 // The GRU in a diagonal-block mode at D = 32 / 64 runs one fused evaluation +
 // scan launch per iteration; everything else runs evaluation and scan as two
 // launches.
@@ -325,6 +389,10 @@ struct SolveLayout {
     int tps = 0;                   // tiles per sequence for res_tile
     int *done = nullptr, *iters = nullptr, *status = nullptr;
     float *resid = nullptr;
+    float *rms = nullptr;       // root-mean-square residual of the returned iterate [B]
+    double *rms_part = nullptr; // its partial sums [B, chunks]
+    unsigned *front = nullptr;  // finite-step check: front, best front, iteration of its last advance [B]
+    int *best = nullptr, *last_adv = nullptr;
     float *buf1 = nullptr;      // second trajectory buffer [B,T,D]
     float *lin = nullptr;       // a_t (diag) or d_t (dense, factored leaf) [B,T,D]
     float *bvec = nullptr;      // b_t [B,T,D]
@@ -332,10 +400,9 @@ struct SolveLayout {
     size_t bytes = 0;
 };
 
-SolveLayout solve_layout(void *ws, const deer_cell_params_t *p, int B, int T, int mode_flags)
+SolveLayout solve_layout(void *ws, const deer_cell_params_t *p, int B, int T, int mode, const deer_solve_opts_t &o)
 {
-    const int mode = mode_flags & ~(DEER_SCAN_F64 | DEER_MULTI_LAUNCH);
-    const bool f64 = (mode_flags & DEER_SCAN_F64) != 0;
+    const bool f64 = may_use_f64(o, mode);
     const size_t BTD = static_cast<size_t>(B) * T * p->D;
     const int PD = (p->cell == DEER_CELL_GRU) ? 3 * p->D : p->D;
     Carve c(ws);
@@ -356,6 +423,11 @@ SolveLayout solve_layout(void *ws, const deer_cell_params_t *p, int B, int T, in
     L.iters = c.take<int>(B);
     L.status = c.take<int>(B);
     L.resid = c.take<float>(B);
+    L.rms = c.take<float>(B);
+    L.rms_part = c.take<double>(static_cast<size_t>(B) * ((static_cast<size_t>(T) * p->D + kRmsChunk - 1) / kRmsChunk));
+    L.front = c.take<unsigned>(B);
+    L.best = c.take<int>(B);
+    L.last_adv = c.take<int>(B);
     L.buf1 = c.take<float>(BTD);
     L.lin = c.take<float>(BTD);
     L.bvec = c.take<float>(BTD);
@@ -376,12 +448,13 @@ struct PollEvents {
 };
 
 // Enqueue batches of iterations (1, 2, 4, 4, ...) and, while the current batch
-// runs, wait for the copy of the device's all-done flag enqueued after the
-// previous batch; stop enqueueing once it reads set.  Kernels enqueued after
-// convergence exit at once.  `total` caps the evaluations enqueued.
-template <class Enqueue>
-int run_polled(Enqueue &&enqueue_iteration, const int *all_done, long long total, hipStream_t stream,
-               PollEvents &pe, const char *who)
+// runs, wait for the copy of the device's all-done and escalate words enqueued
+// after the previous batch; stop enqueueing once all-done reads set, and call
+// on_escalate() while escalate does.  Kernels enqueued after convergence exit
+// at once.  `total` caps the evaluations enqueued.
+template <class Enqueue, class OnEscalate>
+int run_polled(Enqueue &&enqueue_iteration, SolveControl *ctl, long long total, hipStream_t stream, PollEvents &pe,
+               const char *who, OnEscalate &&on_escalate)
 {
     int rc = DEER_OK;
     long long launched = 0;
@@ -393,13 +466,16 @@ int run_polled(Enqueue &&enqueue_iteration, const int *all_done, long long total
     bool pending = false;
     int pending_slot = 0;
     volatile int *h = g_poll.host;
+    // each slot holds the two adjacent control words (all_done, escalate)
     while (launched < total) {
         const long long n = std::min<long long>(batch, total - launched);
         for (long long k = 0; k < n && rc == DEER_OK; ++k) rc = enqueue_iteration();
         if (rc) break;
         launched += n;
-        h[slot] = 0;
-        if (hipMemcpyAsync(g_poll.host + slot, all_done, sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        h[2 * slot] = 0;
+        h[2 * slot + 1] = 0;
+        if (hipMemcpyAsync(g_poll.host + 2 * slot, &ctl->all_done, 2 * sizeof(int), hipMemcpyDeviceToHost, stream) !=
+                hipSuccess ||
             hipEventRecord(pe.ev[slot], stream) != hipSuccess) {
             rc = fail(DEER_ERR_HIP, std::string(who) + ": polling copy failed");
             break;
@@ -409,7 +485,8 @@ int run_polled(Enqueue &&enqueue_iteration, const int *all_done, long long total
                 rc = fail(DEER_ERR_HIP, std::string(who) + ": event wait failed");
                 break;
             }
-            if (h[pending_slot]) break;
+            if (h[2 * pending_slot]) break;
+            if (h[2 * pending_slot + 1]) on_escalate();
         }
         pending = true;
         pending_slot = slot;
@@ -425,6 +502,8 @@ struct BroydenLayout {
     unsigned *res_bits = nullptr;
     int *done = nullptr, *iters = nullptr, *status = nullptr;
     float *resid = nullptr;
+    unsigned *front = nullptr;          // finite-step check [B]
+    int *best = nullptr, *last_adv = nullptr;
     float *buf1 = nullptr;              // second iterate buffer [B,T,D]
     float *f_even = nullptr, *f_odd = nullptr;   // f^(i) by parity [B,T,D]
     float *proj = nullptr;              // input projection
@@ -452,6 +531,9 @@ BroydenLayout broyden_layout(void *ws, const deer_cell_params_t *p, int B, int T
     L.iters = c.take<int>(B);
     L.status = c.take<int>(B);
     L.resid = c.take<float>(B);
+    L.front = c.take<unsigned>(B);
+    L.best = c.take<int>(B);
+    L.last_adv = c.take<int>(B);
     L.buf1 = c.take<float>(BTD);
     L.f_even = c.take<float>(BTD);
     L.f_odd = c.take<float>(BTD);
@@ -475,6 +557,7 @@ int check_broyden_opts(const deer_broyden_opts_t *o, bool need_sketch)
         return fail(DEER_ERR_INVALID, "Broyden gram_reg must be finite and >= 0");
     if (need_sketch && o->rank > 0 && !o->sketch)
         return fail(DEER_ERR_INVALID, "Broyden sketch required for rank > 0");
+    if (o->stall_window < 0) return fail(DEER_ERR_INVALID, "Broyden stall_window must be >= 0");
     return DEER_OK;
 }
 
@@ -603,14 +686,18 @@ int linear_scan_dense(const float *A, const float *b, const float *s0, float *s,
                              static_cast<hipStream_t>(stream));
 }
 
-int deer_workspace_size(const deer_cell_params_t *p, int B, int T, int mode_flags, size_t *bytes_out)
+int deer_workspace_size(const deer_cell_params_t *p, int B, int T, int mode, const deer_solve_opts_t *opts,
+                        size_t *bytes_out)
 {
     if (!bytes_out) return fail(DEER_ERR_INVALID, "deer_workspace_size: null output");
-    int rc = check_cell(p, mode_flags);
+    int rc = check_cell(p, mode);
+    if (rc) return rc;
+    const deer_solve_opts_t o = solve_opts(opts);
+    rc = check_solve_opts(o, mode);
     if (rc) return rc;
     rc = check_sizes(B, T);
     if (rc) return rc;
-    *bytes_out = solve_layout(nullptr, p, B, T, mode_flags).bytes;
+    *bytes_out = solve_layout(nullptr, p, B, T, mode, o).bytes;
     return DEER_OK;
 }
 
@@ -669,20 +756,17 @@ int deer_lle(const deer_cell_params_t *p, const float *x, const float *s0, const
                       static_cast<hipStream_t>(stream));
 }
 
-int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int B, int T, int mode_flags,
-               float damping, float tol, int max_iter, const float *init_guess, float *traj_out, int *iters_out,
-               float *resid_out, int *status_out, void *workspace, size_t ws_bytes, void *stream_)
+int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int B, int T, int mode, float tol,
+               int max_iter, const deer_solve_opts_t *opts, const float *init_guess, float *traj_out, int *iters_out,
+               float *resid_out, float *rms_out, int *status_out, void *workspace, size_t ws_bytes, void *stream_)
 {
-    int rc = check_cell(p, mode_flags);
-    const int mode = mode_flags & ~(DEER_SCAN_F64 | DEER_MULTI_LAUNCH);
-    const bool scan_f64 = (mode_flags & DEER_SCAN_F64) != 0;
-    const bool multi_launch = (mode_flags & DEER_MULTI_LAUNCH) != 0;
+    int rc = check_cell(p, mode);
     if (rc) return rc;
-    if (!(damping >= 0.0f && damping <= 1.0f)) return fail(DEER_ERR_INVALID, "damping must lie in [0, 1]");
-    if (damping != 0.0f && mode != DEER_MODE_DENSE && mode != DEER_MODE_DIAG)
-        return fail(DEER_ERR_INVALID, "damping applies to the dense and diag modes only");
+    const deer_solve_opts_t o = solve_opts(opts);
+    rc = check_solve_opts(o, mode);
+    if (rc) return rc;
     const Linearization lz{mode == DEER_MODE_JACOBI ? kLinZero : mode == DEER_MODE_PICARD ? kLinIdentity : kLinJacobian,
-                           1.0f - damping};
+                           1.0f - o.damping};
     rc = check_sizes(B, T);
     if (rc) return rc;
     if (max_iter < 0) return fail(DEER_ERR_INVALID, "max_iter must be >= 0");
@@ -695,53 +779,108 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
         for (int b = 0; b < B; ++b) {
             iters_out[b] = pass ? 0 : max_iter;
             if (resid_out) resid_out[b] = 0.0f;
+            if (rms_out) rms_out[b] = 0.0f;
             if (status_out) status_out[b] = pass ? DEER_SEQ_CONVERGED : DEER_SEQ_NOT_CONVERGED;
         }
         return pass ? DEER_OK : DEER_NOT_CONVERGED;
     }
     if (!x || !traj_out) return fail(DEER_ERR_INVALID, "x and traj_out are required");
-    rc = check_workspace(workspace, ws_bytes, solve_layout(nullptr, p, B, T, mode_flags).bytes, "deer_solve");
+    rc = check_workspace(workspace, ws_bytes, solve_layout(nullptr, p, B, T, mode, o).bytes, "deer_solve");
     if (rc) return rc;
     if (!g_poll.host) return fail(DEER_ERR_HIP, "deer_solve: pinned host memory unavailable");
 
     hipStream_t stream = static_cast<hipStream_t>(stream_);
-    const SolveLayout L = solve_layout(workspace, p, B, T, mode_flags);
+    const SolveLayout L = solve_layout(workspace, p, B, T, mode, o);
     const int D = p->D;
     const size_t BTD = static_cast<size_t>(B) * T * D;
+    const size_t per_seq = static_cast<size_t>(T) * D;
     const bool gru = p->cell == DEER_CELL_GRU;
+    const bool dense = mode == DEER_MODE_DENSE;
     const int PD = gru ? 3 * D : D;
+    const bool tiled = gru && gru_fast_path(D, p->M);
     ProfScope prof(stream);
 
-    if (!gru && !scan_f64 && !multi_launch && tiny_solve_fits(D, T)) {
+    // Root-mean-square residual of the returned trajectories (after the solve,
+    // only when asked): the projection (if the solve did not leave one), the
+    // value-only evaluation of traj_out into `lin`, and the reduction.
+    auto residual_rms = [&](bool have_proj) -> int {
+        int r = DEER_OK;
+        if (!have_proj) r = launch_projection(x, p->U, p->b, L.proj, B, T, p->M, PD, tiled, stream);
+        if (r) return r;
+        const Linearization value{kLinValue, 1.0f};
+        if (gru)
+            r = launch_gru_eval(p->W, p->b2, L.proj, s0, traj_out, traj_out, nullptr, nullptr, nullptr, L.lin, L.bvec,
+                                L.res_bits, B, T, D, p->M, value, FrontOut{}, stream);
+        else
+            r = launch_tanh_eval(p->W, L.proj, s0, traj_out, traj_out, nullptr, nullptr, nullptr, L.lin, L.bvec,
+                                 L.res_bits, B, T, D, 0, value, FrontOut{}, stream);
+        if (r) return r;
+        const int nchunk = static_cast<int>((per_seq + kRmsChunk - 1) / kRmsChunk);
+        DEER_LAUNCH(rms_partial_kernel, dim3(static_cast<unsigned>(nchunk), static_cast<unsigned>(B)), dim3(256), 0,
+                    stream, traj_out, L.lin, per_seq, nchunk, L.rms_part);
+        DEER_LAUNCH(rms_final_kernel, dim3(grid_for(static_cast<size_t>(B))), dim3(256), 0, stream, L.rms_part,
+                    nchunk, per_seq, B, L.rms);
+        DEER_HIP(hipGetLastError());
+        return DEER_OK;
+    };
+
+    if (!gru && !o.scan_f64 && !o.multi_launch && tiny_solve_fits(D, T)) {
         // small problem: the whole solve, projection included, in one launch that
         // writes the per-sequence results straight into the pinned stage
-        char *st = g_stage.get((2 * sizeof(int) + sizeof(float)) * static_cast<size_t>(B));
+        char *st = g_stage.get((2 * sizeof(int) + 2 * sizeof(float)) * static_cast<size_t>(B));
         if (!st) return fail(DEER_ERR_HIP, "deer_solve: pinned host memory unavailable");
         int *h_iters = reinterpret_cast<int *>(st);
         int *h_status = h_iters + B;
         float *h_resid = reinterpret_cast<float *>(h_status + B);
+        float *h_rms = h_resid + B;
         prof.begin(0);
-        rc = launch_tiny_solve(p->W, p->U, p->b, x, p->M, s0, init_guess, traj_out, B, T, D,
-                               mode == DEER_MODE_DENSE, lz, tol, max_iter, h_iters, h_status, h_resid, stream);
+        rc = launch_tiny_solve(p->W, p->U, p->b, x, p->M, s0, init_guess, traj_out, B, T, D, dense, lz, tol,
+                               max_iter, tol >= 0.0f ? o.stall_window : 0, h_iters, h_status, h_resid, stream);
         prof.end();
+        if (rc == DEER_OK && rms_out) {
+            rc = residual_rms(false);
+            if (rc == DEER_OK && hipMemcpyAsync(h_rms, L.rms, sizeof(float) * B, hipMemcpyDeviceToHost, stream) !=
+                                     hipSuccess)
+                rc = fail(DEER_ERR_HIP, "deer_solve: result copy failed");
+        }
         const hipError_t se = hipStreamSynchronize(stream);
         if (rc) return rc;
         if (se != hipSuccess) return hip_fail(se, "hipStreamSynchronize(deer_solve)");
         const long long limit[kProfKinds] = {1, 0, 0, 0};
         prof.collect(limit);
-        bool any_nc = false;
+        bool any_nc = false, any_stall = false;
+        for (int b = 0; b < B; ++b) {
+            any_nc |= h_status[b] != DEER_SEQ_CONVERGED;
+            any_stall |= h_status[b] == DEER_SEQ_STALLED;
+        }
+        if (any_stall && dense && o.stall_escalate) {
+            // the single launch has no double-precision scan: solve again on the
+            // multi-launch path with double accumulation from the start
+            deer_solve_opts_t again = o;
+            again.scan_f64 = 1;
+            again.multi_launch = 1;
+            return deer_solve(p, x, s0, B, T, mode, tol, max_iter, &again, init_guess, traj_out, iters_out, resid_out,
+                              rms_out, status_out, workspace, ws_bytes, stream_);
+        }
         for (int b = 0; b < B; ++b) {
             iters_out[b] = h_iters[b];
             if (resid_out) resid_out[b] = h_resid[b];
+            if (rms_out) rms_out[b] = h_rms[b];
             if (status_out) status_out[b] = h_status[b];
-            any_nc |= h_status[b] != DEER_SEQ_CONVERGED;
         }
         return any_nc ? DEER_NOT_CONVERGED : DEER_OK;
     }
 
     // per-solve control state and the starting iterate s^(0) in traj_out
+    StallCheck sc;
+    if (o.stall_window > 0 && tol >= 0.0f) {     // tol < 0 never passes: exactly max_iter iterations
+        sc.front = L.front;
+        sc.best = L.best;
+        sc.last_adv = L.last_adv;
+        sc.window = o.stall_window;
+    }
     DEER_LAUNCH(init_control_kernel, dim3(grid_for(static_cast<size_t>(B) + 1)), dim3(256), 0, stream, L.ctl,
-                       L.done, L.iters, L.status, L.resid, L.res_bits, B);
+                       L.done, L.iters, L.status, L.resid, L.res_bits, sc, B);
     DEER_HIP(hipGetLastError());
     const bool fused = fused_gru_step(p, mode);
     const bool zero_start = fused && !init_guess;   // the fused step reads no s^(0) when it is all zeros
@@ -755,34 +894,40 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
 
     // iteration-invariant input projection (W_ih x + b_ih for the GRU, U x + b for tanh)
     prof.begin(2);
-    rc = launch_projection(x, p->U, p->b, L.proj, B, T, p->M, PD, gru && gru_fast_path(D, p->M), stream);
+    rc = launch_projection(x, p->U, p->b, L.proj, B, T, p->M, PD, tiled, stream);
     prof.end();
     if (rc) return rc;
 
+    // a stall in dense mode may switch the linear solve to double accumulation
+    bool scan_f64 = o.scan_f64 != 0;
+    const bool can_escalate = dense && o.stall_window > 0 && o.stall_escalate && !scan_f64;
     const int *sel = &L.ctl->iter;
     const int *all_done = &L.ctl->all_done;
+    const FrontOut fo{sc.front, tol};
     auto enqueue_iteration = [&]() -> int {
         int r;
+        StallCheck sci = sc;
+        sci.escalate = (can_escalate && !scan_f64) ? 1 : 0;
         if (fused) {
             prof.begin(0);
             r = launch_gru_quasi_step(p->W, p->b2, L.proj, s0, traj_out, L.buf1, L.ctl, L.done, L.iters, L.status,
-                                      L.resid, tol, max_iter, L.res_bits, L.res_tile, B, T, D, zero_start, lz, L.scan,
-                                      stream);
+                                      L.resid, tol, max_iter, L.res_bits, L.res_tile, B, T, D, zero_start, lz, sci,
+                                      L.scan, stream);
             prof.end();
             return r;
         }
         prof.begin(0);
         if (gru)
             r = launch_gru_eval(p->W, p->b2, L.proj, s0, traj_out, L.buf1, sel, L.done, all_done, L.lin, L.bvec,
-                                L.res_bits, B, T, D, p->M, lz, stream);
+                                L.res_bits, B, T, D, p->M, lz, fo, stream);
         else
             r = launch_tanh_eval(p->W, L.proj, s0, traj_out, L.buf1, sel, L.done, all_done, L.lin, L.bvec,
-                                 L.res_bits, B, T, D, mode == DEER_MODE_DENSE, lz, stream);
+                                 L.res_bits, B, T, D, dense, lz, fo, stream);
         prof.end();
         if (r) return r;
         prof.begin(3);
         DEER_LAUNCH(check_kernel, dim3(1), dim3(256), 0, stream, L.ctl, L.res_bits, nullptr, 0, L.done, L.iters,
-                           L.status, L.resid, B, tol, max_iter);
+                           L.status, L.resid, B, tol, max_iter, sci);
         prof.end();
         DEER_HIP(hipGetLastError());
         prof.begin(1);
@@ -797,20 +942,22 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
 
     const long long total = static_cast<long long>(max_iter) + 1;   // evaluations needed at most
     PollEvents pe;
-    rc = run_polled(enqueue_iteration, all_done, total, stream, pe, "deer_solve");
+    rc = run_polled(enqueue_iteration, L.ctl, total, stream, pe, "deer_solve", [&]() {
+        if (can_escalate) scan_f64 = true;
+    });
     if (rc == DEER_OK) {
-        const size_t per_seq = static_cast<size_t>(T) * D;
         DEER_LAUNCH(gather_kernel, dim3(grid_for(per_seq, 256, 1024), B), dim3(256), 0, stream, traj_out,
                            L.buf1, L.iters, per_seq, B, zero_start ? 1 : 0);
         if (hipGetLastError() != hipSuccess) rc = fail(DEER_ERR_HIP, "deer_solve: gather launch failed");
     }
+    if (rc == DEER_OK && rms_out) rc = residual_rms(true);
     std::vector<int> status_h(B, 0);
     unsigned abort_flag = 0;
     if (rc == DEER_OK) {
         const unsigned *abort_dev =
             (diag_blocks(mode) || fused) ? &static_cast<ScanHeader *>(L.scan)->abort : nullptr;
         rc = read_results(L.iters, L.status, L.resid, abort_dev, B, stream, iters_out, resid_out, status_h,
-                          abort_flag, "deer_solve");
+                          abort_flag, "deer_solve", L.rms, rms_out);
     } else {
         (void)hipStreamSynchronize(stream);
     }
@@ -882,8 +1029,15 @@ int deer_solve_broyden(const deer_cell_params_t *p, const float *x, const float 
     const bool tiled = gru && gru_fast_path(D, p->M);
     ProfScope prof(stream);
 
+    StallCheck sc;
+    if (opts->stall_window > 0 && tol >= 0.0f) {
+        sc.front = L.front;
+        sc.best = L.best;
+        sc.last_adv = L.last_adv;
+        sc.window = opts->stall_window;
+    }
     DEER_LAUNCH(init_control_kernel, dim3(grid_for(static_cast<size_t>(B) + 1)), dim3(256), 0, stream, L.ctl,
-                L.done, L.iters, L.status, L.resid, L.res_bits, B);
+                L.done, L.iters, L.status, L.resid, L.res_bits, sc, B);
     if (init_guess) {
         if (init_guess != traj_out)
             DEER_LAUNCH(copy_kernel, dim3(grid_for(BTD)), dim3(256), 0, stream, traj_out, init_guess, BTD);
@@ -911,20 +1065,21 @@ int deer_solve_broyden(const deer_cell_params_t *p, const float *x, const float 
     const int *sel = &L.ctl->iter;
     const int *all_done = &L.ctl->all_done;
     const Linearization value{kLinValue, 1.0f};
+    const FrontOut fo{sc.front, tol};
     auto enqueue_iteration = [&]() -> int {
         int r;
         prof.begin(0);
         if (gru)
             r = launch_gru_eval(p->W, p->b2, L.proj, s0, traj_out, L.buf1, sel, L.done, all_done, L.f_even,
-                                L.f_odd, L.res_bits, B, T, D, p->M, value, stream);
+                                L.f_odd, L.res_bits, B, T, D, p->M, value, fo, stream);
         else
             r = launch_tanh_eval(p->W, L.proj, s0, traj_out, L.buf1, sel, L.done, all_done, L.f_even, L.f_odd,
-                                 L.res_bits, B, T, D, 0, value, stream);
+                                 L.res_bits, B, T, D, 0, value, fo, stream);
         prof.end();
         if (r) return r;
         prof.begin(3);
         DEER_LAUNCH(check_kernel, dim3(1), dim3(256), 0, stream, L.ctl, L.res_bits, nullptr, 0, L.done, L.iters,
-                    L.status, L.resid, B, tol, max_iter);
+                    L.status, L.resid, B, tol, max_iter, sc);
         prof.end();
         DEER_HIP(hipGetLastError());
         prof.begin(1);
@@ -934,7 +1089,7 @@ int deer_solve_broyden(const deer_cell_params_t *p, const float *x, const float 
     };
     const long long total = static_cast<long long>(max_iter) + 1;
     PollEvents pe;
-    rc = run_polled(enqueue_iteration, all_done, total, stream, pe, "deer_solve_broyden");
+    rc = run_polled(enqueue_iteration, L.ctl, total, stream, pe, "deer_solve_broyden", []() {});
     if (rc == DEER_OK) {
         const size_t per_seq = static_cast<size_t>(T) * D;
         DEER_LAUNCH(gather_kernel, dim3(grid_for(per_seq, 256, 1024), B), dim3(256), 0, stream, traj_out, L.buf1,

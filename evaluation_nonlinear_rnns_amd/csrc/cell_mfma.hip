@@ -40,6 +40,11 @@ __device__ __forceinline__ void wave_max_atomic(unsigned v, unsigned *dst)
     for (int o = 32; o > 0; o >>= 1) v = max(v, static_cast<unsigned>(__shfl_xor(static_cast<int>(v), o, 64)));
     if ((threadIdx.x & 63) == 0 && v != 0u) atomicMax(dst, v);
 }
+__device__ __forceinline__ void wave_min_atomic(unsigned v, unsigned *dst)
+{
+    v = wave_min_u32(v);
+    if ((threadIdx.x & 63) == 0 && v != kNoFront) atomicMin(dst, v);
+}
 
 // Self-validating look-back descriptor words: float value | 32-bit tag.
 constexpr unsigned kDescSpinLimit = 1u << 22;
@@ -125,7 +130,7 @@ __global__ __launch_bounds__(kThreads, 2) void gru_eval_mfma_kernel(
     const float *__restrict__ s0, const float *s_even, const float *s_odd, const int *__restrict__ sel,
     const int *__restrict__ skip, const int *__restrict__ all_done, float *__restrict__ aout,
     float *__restrict__ bout, unsigned *__restrict__ res_bits, int T, int tiles_per_seq, long long ntiles,
-    Linearization lz)
+    Linearization lz, FrontOut fo)
 {
     using G = GruGeom<D>;
     if (all_done && *all_done) return;
@@ -151,7 +156,7 @@ __global__ __launch_bounds__(kThreads, 2) void gru_eval_mfma_kernel(
 
     const long long tb = ntiles * blockIdx.x / gridDim.x, te = ntiles * (blockIdx.x + 1) / gridDim.x;
     if (tb >= te) return;
-    unsigned rmax = 0u;
+    unsigned rmax = 0u, fmin = kNoFront;
     int cur = -1;
     v4f hv[GruTile<D>::NH];
     v4f pv[3][4];
@@ -163,8 +168,12 @@ __global__ __launch_bounds__(kThreads, 2) void gru_eval_mfma_kernel(
         int nb = bseq, nt = tt + 1;                  // the next tile of the range
         if (nt == tiles_per_seq) { nt = 0; ++nb; }
         if (bseq != cur) {
-            if (cur >= 0) wave_max_atomic(rmax, res_bits + cur);
+            if (cur >= 0) {
+                wave_max_atomic(rmax, res_bits + cur);
+                if (fo.front) wave_min_atomic(fmin, fo.front + cur);
+            }
             rmax = 0u;
+            fmin = kNoFront;
             cur = bseq;
         }
         const bool live = !(skip && skip[bseq]);  // uniform over the workgroup
@@ -224,10 +233,15 @@ __global__ __launch_bounds__(kThreads, 2) void gru_eval_mfma_kernel(
                 __builtin_nontemporal_store(a, aout + o);
                 __builtin_nontemporal_store(f - a * h, bout + o);
             }
-            rmax = max(rmax, __float_as_uint(fabsf(st - f)));
+            const float ra = fabsf(st - f);
+            rmax = max(rmax, __float_as_uint(ra));
+            fmin = min(fmin, front_of(ra, fo.tol, t));
         }
     }
-    if (cur >= 0) wave_max_atomic(rmax, res_bits + cur);
+    if (cur >= 0) {
+        wave_max_atomic(rmax, res_bits + cur);
+        if (fo.front) wave_min_atomic(fmin, fo.front + cur);
+    }
 }
 
 // ------------------------------------------------- fused quasi-DEER GRU step
@@ -255,7 +269,7 @@ __global__ __launch_bounds__(kThreads, 2) void gru_quasi_step_kernel(
     const float *__restrict__ s0, float *s_even, float *s_odd, SolveControl *ctl, int *done, int *iters,
     int *status, float *resid, float tol, int max_iter, unsigned *res_bits, unsigned *__restrict__ res_tile, int T,
     int tiles_per_seq,
-    int nseq, long long ntiles, int zero_start, Linearization lz, ScanHeader *__restrict__ hdr,
+    int nseq, long long ntiles, int zero_start, Linearization lz, StallCheck sc, ScanHeader *__restrict__ hdr,
     unsigned long long *__restrict__ desc)
 {
     using G = GruGeom<D>;
@@ -400,6 +414,11 @@ __global__ __launch_bounds__(kThreads, 2) void gru_quasi_step_kernel(
             for (int w = 1; w < kThreads / 64; ++w) m = max(m, red[w]);
             if (per_seq) seqmax[bseq] = max(seqmax[bseq], m);
             else res_tile[static_cast<size_t>(bseq) * tiles_per_seq + tt] = m;
+            // finite-step front at tile granularity: the tile's last position
+            // bounds the first violating one from above, so a stall read from it
+            // is never a false one (it is seen up to one tile later)
+            if (sc.front && !(__uint_as_float(m) <= tol))
+                atomicMin(sc.front + bseq, static_cast<unsigned>(min(t0 + G::TP, T) - 1));
         }
         if (tid < D) {
             const int cc = tid;
@@ -468,9 +487,10 @@ __global__ __launch_bounds__(kThreads, 2) void gru_quasi_step_kernel(
         __hip_atomic_store(&hdr->epoch, epoch + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (per_seq)
-        finalize_iteration(ctl, res_bits, nullptr, 0, done, iters, status, resid, nseq, tol, max_iter, red);
+        finalize_iteration(ctl, res_bits, nullptr, 0, done, iters, status, resid, nseq, tol, max_iter, red, sc);
     else
-        finalize_iteration(ctl, nullptr, res_tile, tiles_per_seq, done, iters, status, resid, nseq, tol, max_iter, red);
+        finalize_iteration(ctl, nullptr, res_tile, tiles_per_seq, done, iters, status, resid, nseq, tol, max_iter, red,
+                           sc);
 }
 
 // ------------------------------------------------------------ input projection
@@ -606,30 +626,35 @@ __global__ __launch_bounds__(kThreads) void projection_mfma_kernel(const float *
     }
 }
 
+// Resident workgroups of `kernel` on the current device (compute units times
+// workgroups per unit), cached per device in `cache`.
+constexpr int kCapDevices = 64;
 template <class K>
-int capacity_of(K kernel, size_t lds)
+int capacity_of(int (&cache)[kCapDevices], K kernel, size_t lds)
 {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev >= 0 && dev < kCapDevices && cache[dev] > 0) return cache[dev];
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, lds) != hipSuccess || per_cu < 1)
         per_cu = 1;
+    if (dev >= 0 && dev < kCapDevices) cache[dev] = cus * per_cu;
     return cus * per_cu;
 }
 
 template <int D>
 int launch_gru_mfma(const float *Whh, const float *bhh, const float *p, const float *s0, const float *s_even,
                     const float *s_odd, const int *sel, const int *skip, const int *all_done, float *a, float *bvec,
-                    unsigned *res_bits, int B, int T, Linearization lz, hipStream_t stream)
+                    unsigned *res_bits, int B, int T, Linearization lz, FrontOut fo, hipStream_t stream)
 {
     using G = GruGeom<D>;
-    static int cap = 0;
-    if (cap == 0) cap = capacity_of(gru_eval_mfma_kernel<D>, 0);
+    static int caps[kCapDevices] = {};
+    const int cap = capacity_of(caps, gru_eval_mfma_kernel<D>, 0);
     const int tps = (T + G::TP - 1) / G::TP;
     const long long ntiles = static_cast<long long>(B) * tps;
     const unsigned grid = static_cast<unsigned>(std::max<long long>(1, std::min<long long>(ntiles, cap)));
     DEER_LAUNCH((gru_eval_mfma_kernel<D>), dim3(grid), dim3(kThreads), 0, stream, Whh, bhh, p, s0, s_even,
-                       s_odd, sel, skip, all_done, a, bvec, res_bits, T, tps, ntiles, lz);
+                       s_odd, sel, skip, all_done, a, bvec, res_bits, T, tps, ntiles, lz, fo);
     DEER_HIP(hipGetLastError());
     return DEER_OK;
 }
@@ -639,8 +664,8 @@ int launch_proj_mfma(const float *x, const float *U, const float *bias, float *p
                      hipStream_t stream)
 {
     using G = ProjGeom<KP, NOB>;
-    static int cap = 0;
-    if (cap == 0) cap = capacity_of(projection_mfma_kernel<KP, NOB, TILED>, 0);
+    static int caps[kCapDevices] = {};
+    const int cap = capacity_of(caps, projection_mfma_kernel<KP, NOB, TILED>, 0);
     const int tps32 = (T + 31) / 32;
     const long long nsub = static_cast<long long>(B) * tps32;
     const long long ntiles = (nsub + G::PS - 1) / G::PS;
@@ -655,11 +680,11 @@ template <int D>
 int launch_gru_step(const float *Whh, const float *bhh, const float *pt, const float *s0, float *s_even, float *s_odd,
                     SolveControl *ctl, int *done, int *iters, int *status, float *resid, float tol, int max_iter,
                     unsigned *res_bits, unsigned *res_tile, int B, int T, bool zero_start, Linearization lz,
-                    void *state, hipStream_t stream)
+                    const StallCheck &sc, void *state, hipStream_t stream)
 {
     using G = GruGeom<D>;
-    static int cap = 0;
-    if (cap == 0) cap = capacity_of(gru_quasi_step_kernel<D>, 0);
+    static int caps[kCapDevices] = {};
+    const int cap = capacity_of(caps, gru_quasi_step_kernel<D>, 0);
     const int tps = (T + G::TP - 1) / G::TP;
     const long long ntiles = static_cast<long long>(B) * tps;
     const unsigned grid = static_cast<unsigned>(std::max<long long>(1, std::min<long long>(ntiles, cap)));
@@ -667,7 +692,7 @@ int launch_gru_step(const float *Whh, const float *bhh, const float *pt, const f
     auto *desc = reinterpret_cast<unsigned long long *>(static_cast<char *>(state) + sizeof(ScanHeader));
     DEER_LAUNCH((gru_quasi_step_kernel<D>), dim3(grid), dim3(kThreads), 0, stream, Whh, bhh, pt, s0, s_even,
                        s_odd, ctl, done, iters, status, resid, tol, max_iter, res_bits, res_tile, T, tps, B, ntiles,
-                       zero_start ? 1 : 0, lz, hdr, desc);
+                       zero_start ? 1 : 0, lz, sc, hdr, desc);
     DEER_HIP(hipGetLastError());
     return DEER_OK;
 }
@@ -678,15 +703,16 @@ bool gru_mfma_supported(int D) { return D == 32 || D == 64; }
 
 int launch_gru_eval_mfma(const float *Whh, const float *bhh, const float *p, const float *s0, const float *s_even,
                          const float *s_odd, const int *sel, const int *skip, const int *all_done, float *a,
-                         float *bvec, unsigned *res_bits, int B, int T, int D, Linearization lz, hipStream_t stream)
+                         float *bvec, unsigned *res_bits, int B, int T, int D, Linearization lz, FrontOut fo,
+                         hipStream_t stream)
 {
     if (B == 0 || T == 0) return DEER_OK;
     if (D == 64)
         return launch_gru_mfma<64>(Whh, bhh, p, s0, s_even, s_odd, sel, skip, all_done, a, bvec, res_bits, B, T, lz,
-                                   stream);
+                                   fo, stream);
     if (D == 32)
         return launch_gru_mfma<32>(Whh, bhh, p, s0, s_even, s_odd, sel, skip, all_done, a, bvec, res_bits, B, T, lz,
-                                   stream);
+                                   fo, stream);
     return fail(DEER_ERR_UNSUPPORTED, "GRU matrix-core evaluation needs D = 32 or 64");
 }
 
@@ -726,15 +752,15 @@ size_t gru_step_state_bytes(int B, int T, int D)
 int launch_gru_quasi_step(const float *Whh, const float *bhh, const float *pt, const float *s0, float *s_even,
                           float *s_odd, SolveControl *ctl, int *done, int *iters, int *status, float *resid,
                           float tol, int max_iter, unsigned *res_bits, unsigned *res_tile, int B, int T, int D,
-                          bool zero_start, Linearization lz, void *state, hipStream_t stream)
+                          bool zero_start, Linearization lz, const StallCheck &sc, void *state, hipStream_t stream)
 {
     if (B == 0 || T == 0) return DEER_OK;
     if (D == 64)
         return launch_gru_step<64>(Whh, bhh, pt, s0, s_even, s_odd, ctl, done, iters, status, resid, tol, max_iter,
-                                   res_bits, res_tile, B, T, zero_start, lz, state, stream);
+                                   res_bits, res_tile, B, T, zero_start, lz, sc, state, stream);
     if (D == 32)
         return launch_gru_step<32>(Whh, bhh, pt, s0, s_even, s_odd, ctl, done, iters, status, resid, tol, max_iter,
-                                   res_bits, res_tile, B, T, zero_start, lz, state, stream);
+                                   res_bits, res_tile, B, T, zero_start, lz, sc, state, stream);
     return fail(DEER_ERR_UNSUPPORTED, "fused GRU step needs D = 32 or 64");
 }
 

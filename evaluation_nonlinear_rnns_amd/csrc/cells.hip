@@ -41,6 +41,20 @@ __device__ __forceinline__ void block_max_to(unsigned v, unsigned *dst)
     }
 }
 
+// minimum over the workgroup of violating positions, one atomic per workgroup
+__device__ __forceinline__ void block_min_to(unsigned v, unsigned *dst)
+{
+    __shared__ unsigned red[kThreads / 64];
+    v = wave_min_u32(v);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        unsigned m = red[0];
+        for (int w = 1; w < kThreads / 64; ++w) m = min(m, red[w]);
+        if (m != kNoFront) atomicMin(dst, m);
+    }
+}
+
 // ------------------------------------------------------------- projection
 // out[n][o] = sum_j U[o][j] x[n][j] + bias[o], for OG groups of 64 outputs.
 template <int OG>
@@ -124,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void tanh_eval_kernel(
     const float *__restrict__ W, const float *__restrict__ p, const float *__restrict__ s0,
     const float *s_even, const float *s_odd, const int *__restrict__ sel, const int *__restrict__ skip,
     const int *__restrict__ all_done, float *__restrict__ lin, float *__restrict__ bout, unsigned *__restrict__ res_bits,
-    int T, int D, int tiles, int dense, Linearization lz)
+    int T, int D, int tiles, int dense, Linearization lz, FrontOut fo)
 {
     if (all_done && *all_done) return;
     const int bseq = blockIdx.x / tiles, tile = blockIdx.x % tiles;
@@ -188,7 +202,7 @@ __global__ __launch_bounds__(kThreads) void tanh_eval_kernel(
         wr[4 * k4] = w4[0]; wr[4 * k4 + 1] = w4[1]; wr[4 * k4 + 2] = w4[2]; wr[4 * k4 + 3] = w4[3];
     }
     const float wcc = Wl[c * LW + c];
-    unsigned rmax = 0u;
+    unsigned rmax = 0u, fmin = kNoFront;
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
         const int r = ps + j * PPP;
@@ -219,9 +233,12 @@ __global__ __launch_bounds__(kThreads) void tanh_eval_kernel(
             lin[o] = a;
             bout[o] = f - a * srow[r * DP + c];
         }
-        rmax = max(rmax, __float_as_uint(fabsf(srow[(r + 1) * DP + c] - f)));
+        const float ra = fabsf(srow[(r + 1) * DP + c] - f);
+        rmax = max(rmax, __float_as_uint(ra));
+        fmin = min(fmin, front_of(ra, fo.tol, t));
     }
     block_max_to(rmax, res_bits + bseq);
+    if (fo.front) block_min_to(fmin, fo.front + bseq);
 }
 
 // -------------------------------------------------------------- GRU cell
@@ -234,7 +251,7 @@ __global__ __launch_bounds__(kThreads) void gru_eval_kernel(
     const float *__restrict__ Whh, const float *__restrict__ bhh, const float *__restrict__ p,
     const float *__restrict__ s0, const float *s_even, const float *s_odd, const int *__restrict__ sel,
     const int *__restrict__ skip, const int *__restrict__ all_done, float *__restrict__ aout,
-    float *__restrict__ bout, unsigned *__restrict__ res_bits, int T, int D, int tiles, Linearization lz)
+    float *__restrict__ bout, unsigned *__restrict__ res_bits, int T, int D, int tiles, Linearization lz, FrontOut fo)
 {
     if (all_done && *all_done) return;
     const int bseq = blockIdx.x / tiles, tile = blockIdx.x % tiles;
@@ -268,7 +285,7 @@ __global__ __launch_bounds__(kThreads) void gru_eval_kernel(
     const float br = (cv && bhh) ? bhh[c] : 0.0f;
     const float bz = (cv && bhh) ? bhh[D + c] : 0.0f;
     const float bn = (cv && bhh) ? bhh[2 * D + c] : 0.0f;
-    unsigned rmax = 0u;
+    unsigned rmax = 0u, fmin = kNoFront;
     for (int r = ps; r < kTP; r += PPP) {
         const int t = t0 + r;
         if (t >= T) break;
@@ -296,9 +313,12 @@ __global__ __launch_bounds__(kThreads) void gru_eval_kernel(
             aout[o] = a;
             bout[o] = f - a * h;
         }
-        rmax = max(rmax, __float_as_uint(fabsf(srow[r + 1][c] - f)));
+        const float ra = fabsf(srow[r + 1][c] - f);
+        rmax = max(rmax, __float_as_uint(ra));
+        fmin = min(fmin, front_of(ra, fo.tol, t));
     }
     block_max_to(rmax, res_bits + bseq);
+    if (fo.front) block_min_to(fmin, fo.front + bseq);
 }
 
 int pick_dp(int D) { return D <= 4 ? 4 : D <= 8 ? 8 : D <= 16 ? 16 : D <= 32 ? 32 : 64; }
@@ -346,12 +366,12 @@ int launch_projection(const float *x, const float *U, const float *bias, float *
 #define DEER_TANH_CASE(DPV)                                                                                     \
     case DPV:                                                                                                   \
         DEER_LAUNCH((tanh_eval_kernel<DPV>), dim3(blocks), dim3(kThreads), 0, stream, W, p, s0, s_even,  \
-                           s_odd, sel, skip, all_done, lin, bvec, res_bits, T, D, tiles, dense, lz);            \
+                           s_odd, sel, skip, all_done, lin, bvec, res_bits, T, D, tiles, dense, lz, fo);        \
         break;
 
 int launch_tanh_eval(const float *W, const float *p, const float *s0, const float *s_even, const float *s_odd,
                      const int *sel, const int *skip, const int *all_done, float *lin, float *bvec, unsigned *res_bits,
-                     int B, int T, int D, int dense, Linearization lz, hipStream_t stream)
+                     int B, int T, int D, int dense, Linearization lz, FrontOut fo, hipStream_t stream)
 {
     int tiles;
     const unsigned blocks = eval_blocks(B, T, tiles);
@@ -370,16 +390,16 @@ int launch_tanh_eval(const float *W, const float *p, const float *s0, const floa
 #define DEER_GRU_CASE(DPV)                                                                                      \
     case DPV:                                                                                                   \
         DEER_LAUNCH((gru_eval_kernel<DPV>), dim3(blocks), dim3(kThreads), 0, stream, Whh, bhh, p, s0,    \
-                           s_even, s_odd, sel, skip, all_done, a, bvec, res_bits, T, D, tiles, lz);             \
+                           s_even, s_odd, sel, skip, all_done, a, bvec, res_bits, T, D, tiles, lz, fo);         \
         break;
 
 int launch_gru_eval(const float *Whh, const float *bhh, const float *p, const float *s0, const float *s_even,
                     const float *s_odd, const int *sel, const int *skip, const int *all_done, float *a, float *bvec,
-                    unsigned *res_bits, int B, int T, int D, int M, Linearization lz, hipStream_t stream)
+                    unsigned *res_bits, int B, int T, int D, int M, Linearization lz, FrontOut fo, hipStream_t stream)
 {
     if (gru_fast_path(D, M))
         return launch_gru_eval_mfma(Whh, bhh, p, s0, s_even, s_odd, sel, skip, all_done, a, bvec, res_bits, B, T, D,
-                                    lz, stream);
+                                    lz, fo, stream);
     int tiles;
     const unsigned blocks = eval_blocks(B, T, tiles);
     if (blocks == 0) return DEER_OK;

@@ -73,8 +73,69 @@ extern thread_local ProfLaunch g_prof_launch;
 struct SolveControl {
     int iter;       // current iteration index i (iterate s^(i) lives in buffer i % 2)
     int all_done;   // 1 once every sequence has stopped
-    int pad[62];
+    int escalate;   // 1 once a stall asked for double accumulation (read by the host's poll)
+    int pad[61];
 };
+
+// Finite-step check.  After i iterations the first i states are exact in
+// exact arithmetic ("Parallel Broyden Methods", Theorem 1), so the front --
+// the first position whose residual exceeds tol (or is not finite) -- is never
+// below i.  The evaluation kernels take the front's minimum per sequence into
+// front[] (atomic min; no violation leaves ~0u); finalize_iteration keeps the
+// best front and the iteration it last advanced, and calls a sequence stalled
+// when its best front is below i and has not advanced for `window`
+// iterations.  A stall then either stops the sequence (DEER_SEQ_STALLED) or,
+// with `escalate`, raises ctl->escalate for the host and lets it go on.
+struct StallCheck {
+    unsigned *front = nullptr;   // [B]; nullptr: no check
+    int *best = nullptr;         // [B]
+    int *last_adv = nullptr;     // [B]
+    int window = 0;
+    int escalate = 0;
+};
+constexpr unsigned kNoFront = 0xFFFFFFFFu;
+
+// Where an evaluation kernel takes the front: front[b] (atomic min), or nowhere.
+struct FrontOut {
+    unsigned *front = nullptr;
+    float tol = 0.0f;
+};
+
+// Minimum of a per-lane violating position over the wavefront.
+__device__ __forceinline__ unsigned wave_min_u32(unsigned v)
+{
+    for (int o = 32; o > 0; o >>= 1) v = min(v, static_cast<unsigned>(__shfl_xor(static_cast<int>(v), o, 64)));
+    return v;
+}
+
+// Position t counts toward the front when its residual is not <= tol.
+__device__ __forceinline__ unsigned front_of(float r_abs, float tol, int t)
+{
+    return (r_abs <= tol) ? kNoFront : static_cast<unsigned>(t);
+}
+
+// One sequence's stall bookkeeping at iteration i (the residual did not pass
+// and the cap is not reached).  Returns true when the sequence is to stop as
+// stalled.
+__device__ inline bool stall_step(const StallCheck &sc, SolveControl *ctl, int b, int i)
+{
+    if (!sc.front) return false;
+    const unsigned fr = sc.front[b];
+    sc.front[b] = kNoFront;                     // ready for the next evaluation
+    if (sc.window <= 0) return false;
+    const int f = fr > 0x7FFFFFFFu ? 0x7FFFFFFF : static_cast<int>(fr);
+    if (f > sc.best[b]) {
+        sc.best[b] = f;
+        sc.last_adv[b] = i;
+        return false;
+    }
+    if (sc.best[b] < i && i - sc.last_adv[b] >= sc.window) {
+        if (!sc.escalate) return true;
+        ctl->escalate = 1;
+        sc.last_adv[b] = i;                     // a fresh window after the switch
+    }
+    return false;
+}
 
 // Convergence test of iteration i = ctl->iter for every sequence, run by one
 // whole workgroup (blockDim.x a multiple of 64, at most 1024; `red` is a
@@ -86,7 +147,7 @@ struct SolveControl {
 // bit patterns and NaN patterns sit above +Inf, so maxima are taken on bits.
 __device__ inline void finalize_iteration(SolveControl *ctl, unsigned *res_bits, const unsigned *res_tile, int tps,
                                           int *done, int *iters, int *status, float *resid, int B, float tol,
-                                          int max_iter, unsigned *red)
+                                          int max_iter, unsigned *red, const StallCheck &sc)
 {
     const int i = ctl->iter;
     int active = 0;
@@ -107,6 +168,11 @@ __device__ inline void finalize_iteration(SolveControl *ctl, unsigned *res_bits,
                 done[b] = 1;
                 iters[b] = max_iter;
                 status[b] = __builtin_isfinite(r) ? DEER_SEQ_NOT_CONVERGED : DEER_SEQ_NONFINITE;
+                resid[b] = r;
+            } else if (stall_step(sc, ctl, b, i)) {
+                done[b] = 1;
+                iters[b] = i;
+                status[b] = DEER_SEQ_STALLED;
                 resid[b] = r;
             } else {
                 active = 1;
@@ -145,6 +211,11 @@ __device__ inline void finalize_iteration(SolveControl *ctl, unsigned *res_bits,
                 done[b] = 1;
                 iters[b] = max_iter;
                 status[b] = __builtin_isfinite(r) ? DEER_SEQ_NOT_CONVERGED : DEER_SEQ_NONFINITE;
+                resid[b] = r;
+            } else if (stall_step(sc, ctl, b, i)) {
+                done[b] = 1;
+                iters[b] = i;
+                status[b] = DEER_SEQ_STALLED;
                 resid[b] = r;
             } else {
                 active = 1;
@@ -333,7 +404,7 @@ __device__ __forceinline__ float lin_diag(Linearization l, float jdiag)
 int launch_tanh_eval(const float *W, const float *p, const float *s0, const float *s_even,
                      const float *s_odd, const int *sel, const int *skip, const int *all_done,
                      float *lin, float *bvec, unsigned *res_bits, int B, int T, int D, int dense,
-                     Linearization lz, hipStream_t stream);
+                     Linearization lz, FrontOut fo, hipStream_t stream);
 
 // GRU cell, diagonal blocks: writes a_t = lin_diag(diag(d f / d s)) and
 // b_t = f_t - a_t * s_{t-1}.  With gru_fast_path(D, M) the projection is
@@ -342,14 +413,14 @@ bool gru_fast_path(int D, int M);
 int launch_gru_eval(const float *Whh, const float *bhh, const float *p, const float *s0,
                     const float *s_even, const float *s_odd, const int *sel, const int *skip,
                     const int *all_done, float *a, float *bvec, unsigned *res_bits, int B, int T,
-                    int D, int M, Linearization lz, hipStream_t stream);
+                    int D, int M, Linearization lz, FrontOut fo, hipStream_t stream);
 
 // Matrix-core versions (cell_mfma.hip) for the supported sizes.
 bool gru_mfma_supported(int D);
 int launch_gru_eval_mfma(const float *Whh, const float *bhh, const float *p, const float *s0,
                          const float *s_even, const float *s_odd, const int *sel, const int *skip,
                          const int *all_done, float *a, float *bvec, unsigned *res_bits, int B, int T,
-                         int D, Linearization lz, hipStream_t stream);
+                         int D, Linearization lz, FrontOut fo, hipStream_t stream);
 bool proj_mfma_supported(int M, int O);
 size_t proj_tiled_floats(int B, int T, int O);
 int launch_projection_mfma(const float *x, const float *U, const float *bias, float *p, int B, int T,
@@ -368,7 +439,7 @@ size_t gru_step_state_bytes(int B, int T, int D);
 int launch_gru_quasi_step(const float *Whh, const float *bhh, const float *pt, const float *s0, float *s_even,
                           float *s_odd, SolveControl *ctl, int *done, int *iters, int *status, float *resid,
                           float tol, int max_iter, unsigned *res_bits, unsigned *res_tile, int B, int T, int D,
-                          bool zero_start, Linearization lz, void *state, hipStream_t stream);
+                          bool zero_start, Linearization lz, const StallCheck &sc, void *state, hipStream_t stream);
 
 // Sequential rollout (rollout.hip): the projection into `workspace`
 // (rollout_workspace_bytes), then one workgroup per sequence.
@@ -384,7 +455,7 @@ int launch_rollout(const deer_cell_params_t *p, const float *x, const float *s0,
 bool tiny_solve_fits(int D, int T);
 int launch_tiny_solve(const float *W, const float *U, const float *bias, const float *x, int M, const float *s0,
                       const float *init, float *traj, int B, int T, int D, bool dense, Linearization lz, float tol,
-                      int max_iter, int *iters, int *status, float *resid, hipStream_t stream);
+                      int max_iter, int stall_window, int *iters, int *status, float *resid, hipStream_t stream);
 
 // Parallel Broyden (broyden.hip): the block updates and the chunked compressed
 // scan of delta_t = A_t delta_{t-1} + c_t, A_t = alpha I + shrink U_t V_t^T.

@@ -266,7 +266,7 @@ int launch_lle_dp(const deer_cell_params_t *p, const float *s0, const float *tra
     } else {
         // d_t = 1 - f_t^2 is the factored dense leaf the tanh evaluation writes
         const int r = launch_tanh_eval(p->W, proj, s0, traj, traj, nullptr, nullptr, nullptr, F, junk, res_bits, B, T,
-                                       D, 1, Linearization{kLinJacobian, 1.0f}, stream);
+                                       D, 1, Linearization{kLinJacobian, 1.0f}, FrontOut{}, stream);
         if (r) return r;
         DEER_LAUNCH((lle_chain_kernel<DP, 1>), dim3(static_cast<unsigned>(B)), dim3(64 * Chain<DP>::NW), 0, stream,
                     p->W, F, v0, T, D, out);

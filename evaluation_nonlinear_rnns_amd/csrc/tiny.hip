@@ -92,12 +92,13 @@ __global__ __launch_bounds__(kTinyThreads) void tiny_solve_kernel(const float *_
                                                                   const float *__restrict__ s0,
                                                                   const float *init, float *traj, int T, int D,
                                                                   int dense, Linearization lz, float tol,
-                                                                  int max_iter, int *iters, int *status,
-                                                                  float *resid)
+                                                                  int max_iter, int stall_window, int *iters,
+                                                                  int *status, float *resid)
 {
     __shared__ float S[kTinyThreads * P * kTinyD];   // the iterate s^(i), rows padded to 4
     __shared__ float agg[kTinyThreads * kAffWords];  // inclusive prefixes of the thread maps
     __shared__ unsigned red[kTinyThreads / 64];
+    __shared__ unsigned fred[kTinyThreads / 64];
     const int b = blockIdx.x, tid = threadIdx.x;
     const size_t seq = static_cast<size_t>(b) * T;
 
@@ -131,10 +132,12 @@ __global__ __launch_bounds__(kTinyThreads) void tiny_solve_kernel(const float *_
 
     int it = 0;
     float r = 0.0f;
+    bool stalled = false;
+    int best = -1, last_adv = 0;        // finite-step front bookkeeping (same in every thread)
     for (;; ++it) {
         // blocks and offsets at the thread's positions, composed left to right
         Aff m[P];
-        unsigned rm = 0u;
+        unsigned rm = 0u, fm = kNoFront;
 #pragma unroll
         for (int q = 0; q < P; ++q) {
             const int t = tid * P + q;
@@ -149,7 +152,11 @@ __global__ __launch_bounds__(kTinyThreads) void tiny_solve_kernel(const float *_
 #pragma unroll
                 for (int j = 0; j < kTinyD; ++j) h += w[i][j] * sp[j];
                 f[i] = (i < D) ? tanhf(h) : 0.0f;
-                if (i < D) rm = max(rm, __float_as_uint(fabsf(S[t * kTinyD + i] - f[i])));
+                if (i < D) {
+                    const float ra = fabsf(S[t * kTinyD + i] - f[i]);
+                    rm = max(rm, __float_as_uint(ra));
+                    fm = min(fm, front_of(ra, tol, t));
+                }
             }
 #pragma unroll
             for (int i = 0; i < kTinyD; ++i) {
@@ -172,13 +179,31 @@ __global__ __launch_bounds__(kTinyThreads) void tiny_solve_kernel(const float *_
         }
         // residual of s^(i): maximum over the workgroup on the float bits
         for (int o = 32; o > 0; o >>= 1) rm = max(rm, static_cast<unsigned>(__shfl_xor(static_cast<int>(rm), o, 64)));
-        if ((tid & 63) == 0) red[tid >> 6] = rm;
+        fm = wave_min_u32(fm);
+        if ((tid & 63) == 0) {
+            red[tid >> 6] = rm;
+            fred[tid >> 6] = fm;
+        }
         __syncthreads();
-        unsigned rb = red[0];
+        unsigned rb = red[0], fb = fred[0];
 #pragma unroll
-        for (int k = 1; k < kTinyThreads / 64; ++k) rb = max(rb, red[k]);
+        for (int k = 1; k < kTinyThreads / 64; ++k) {
+            rb = max(rb, red[k]);
+            fb = min(fb, fred[k]);
+        }
         r = __uint_as_float(rb);
         if (r <= tol || it >= max_iter) break;       // same decision in every thread
+        if (stall_window > 0) {
+            // the first `it` states are exact in exact arithmetic, so the front is never below it
+            const int f = fb > 0x7FFFFFFFu ? 0x7FFFFFFF : static_cast<int>(fb);
+            if (f > best) {
+                best = f;
+                last_adv = it;
+            } else if (best < it && it - last_adv >= stall_window) {
+                stalled = true;
+                break;
+            }
+        }
 
         // linear step: thread map, then the inclusive scan over the threads
         Aff loc = m[0];
@@ -238,7 +263,9 @@ __global__ __launch_bounds__(kTinyThreads) void tiny_solve_kernel(const float *_
     }
     if (tid == 0) {
         iters[b] = it;
-        status[b] = (r <= tol) ? DEER_SEQ_CONVERGED : (__builtin_isfinite(r) ? DEER_SEQ_NOT_CONVERGED : DEER_SEQ_NONFINITE);
+        status[b] = (r <= tol) ? DEER_SEQ_CONVERGED
+                    : stalled      ? DEER_SEQ_STALLED
+                                   : (__builtin_isfinite(r) ? DEER_SEQ_NOT_CONVERGED : DEER_SEQ_NONFINITE);
         resid[b] = r;
         __threadfence_system();
     }
@@ -250,20 +277,20 @@ bool tiny_solve_fits(int D, int T) { return D >= 1 && D <= kTinyD && T >= 1 && T
 
 int launch_tiny_solve(const float *W, const float *U, const float *bias, const float *x, int M, const float *s0,
                       const float *init, float *traj, int B, int T, int D, bool dense, Linearization lz, float tol,
-                      int max_iter, int *iters, int *status, float *resid, hipStream_t stream)
+                      int max_iter, int stall_window, int *iters, int *status, float *resid, hipStream_t stream)
 {
     if (B == 0) return DEER_OK;
     const int P = (T + kTinyThreads - 1) / kTinyThreads;
     const int dn = dense ? 1 : 0;
     if (P <= 1)
         DEER_LAUNCH(tiny_solve_kernel<1>, dim3(B), dim3(kTinyThreads), 0, stream, W, U, bias, x, M, s0, init, traj, T,
-                    D, dn, lz, tol, max_iter, iters, status, resid);
+                    D, dn, lz, tol, max_iter, stall_window, iters, status, resid);
     else if (P <= 2)
         DEER_LAUNCH(tiny_solve_kernel<2>, dim3(B), dim3(kTinyThreads), 0, stream, W, U, bias, x, M, s0, init, traj, T,
-                    D, dn, lz, tol, max_iter, iters, status, resid);
+                    D, dn, lz, tol, max_iter, stall_window, iters, status, resid);
     else
         DEER_LAUNCH(tiny_solve_kernel<4>, dim3(B), dim3(kTinyThreads), 0, stream, W, U, bias, x, M, s0, init, traj, T,
-                    D, dn, lz, tol, max_iter, iters, status, resid);
+                    D, dn, lz, tol, max_iter, stall_window, iters, status, resid);
     DEER_HIP(hipGetLastError());
     return DEER_OK;
 }

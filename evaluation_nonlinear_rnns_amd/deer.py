@@ -25,11 +25,9 @@ DEER_CELL_GRU = 1
 MODES = {"dense": DEER_MODE_DENSE, "diag": DEER_MODE_DIAG, "jacobi": DEER_MODE_JACOBI, "picard": DEER_MODE_PICARD}
 CELLS = {"tanh": DEER_CELL_TANH, "gru": DEER_CELL_GRU}
 
-DEER_SCAN_F64 = 16   # or-ed into the dense mode: the linear solve accumulates in double
-DEER_MULTI_LAUNCH = 32   # or-ed into the mode: never use the single-launch path for small tanh problems
-
 DEER_OK = 0
 DEER_NOT_CONVERGED = 1
+SEQ_CONVERGED, SEQ_NOT_CONVERGED, SEQ_NONFINITE, SEQ_STALLED = 0, 1, 2, 3
 ERRORS = {-1: "DEER_ERR_INVALID", -2: "DEER_ERR_UNSUPPORTED", -3: "DEER_ERR_WORKSPACE",
           -4: "DEER_ERR_HIP", -5: "DEER_ERR_DEVICE"}
 
@@ -50,7 +48,22 @@ class DeerError(RuntimeError):
 class BroydenOpts(ctypes.Structure):
     _fields_ = [("rank", ctypes.c_int), ("multisecant", ctypes.c_int), ("alpha", ctypes.c_float),
                 ("damping", ctypes.c_float), ("gram_reg", ctypes.c_float), ("chunk", ctypes.c_int),
-                ("sketch", ctypes.c_void_p)]
+                ("sketch", ctypes.c_void_p), ("stall_window", ctypes.c_int)]
+
+
+class SolveOpts(ctypes.Structure):
+    """deer_solve_opts_t; the defaults are DEER_SOLVE_OPTS_DEFAULT."""
+    _fields_ = [("damping", ctypes.c_float), ("scan_f64", ctypes.c_int), ("multi_launch", ctypes.c_int),
+                ("stall_window", ctypes.c_int), ("stall_escalate", ctypes.c_int)]
+
+
+STALL_WINDOW_DEFAULT = 16
+
+
+def solve_opts(damping: float = 0.0, scan_f64: bool = False, multi_launch: bool = False,
+               stall_window: int = STALL_WINDOW_DEFAULT, stall_escalate: bool = True) -> SolveOpts:
+    return SolveOpts(float(damping), int(bool(scan_f64)), int(bool(multi_launch)), int(stall_window),
+                     int(bool(stall_escalate)))
 
 
 class CellParams(ctypes.Structure):
@@ -73,10 +86,11 @@ def load_library():
     lib = ctypes.CDLL(LIB_PATH)
     c_int, c_size, vp, fp = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
     sig = {
-        "deer_workspace_size": ([ctypes.POINTER(CellParams), c_int, c_int, c_int, ctypes.POINTER(c_size)], c_int),
+        "deer_workspace_size": ([ctypes.POINTER(CellParams), c_int, c_int, c_int, ctypes.POINTER(SolveOpts),
+                                 ctypes.POINTER(c_size)], c_int),
         "deer_workspace_init": ([vp, c_size, vp], c_int),
-        "deer_solve": ([ctypes.POINTER(CellParams), vp, vp, c_int, c_int, c_int, fp, fp, c_int, vp, vp, vp, vp,
-                        vp, vp, c_size, vp], c_int),
+        "deer_solve": ([ctypes.POINTER(CellParams), vp, vp, c_int, c_int, c_int, fp, c_int, ctypes.POINTER(SolveOpts),
+                        vp, vp, vp, vp, vp, vp, vp, c_size, vp], c_int),
         "linear_scan_workspace_size": ([c_int, c_int, c_int, c_int, ctypes.POINTER(c_size)], c_int),
         "linear_scan_diag": ([vp, vp, vp, vp, c_int, c_int, c_int, vp, c_size, vp], c_int),
         "linear_scan_diag_noalloc": ([vp, vp, vp, vp, c_int, c_int, c_int, vp], c_int),
@@ -166,15 +180,13 @@ class Cell:
 
 # ------------------------------------------------------------- workspaces
 
-def _mode(mode: str, scan_f64: bool, multi_launch: bool = False) -> int:
-    return MODES[mode] | (DEER_SCAN_F64 if scan_f64 else 0) | (DEER_MULTI_LAUNCH if multi_launch else 0)
-
-
-def deer_workspace_size(cell: Cell, B: int, T: int, mode: str, scan_f64: bool = False) -> int:
+def deer_workspace_size(cell: Cell, B: int, T: int, mode: str, scan_f64: bool = False,
+                        stall_window: int = STALL_WINDOW_DEFAULT, stall_escalate: bool = True) -> int:
     lib = load_library()
     n = ctypes.c_size_t(0)
     p = cell.params()
-    _check(lib.deer_workspace_size(ctypes.byref(p), B, T, _mode(mode, scan_f64), ctypes.byref(n)))
+    o = solve_opts(scan_f64=scan_f64, stall_window=stall_window, stall_escalate=stall_escalate)
+    _check(lib.deer_workspace_size(ctypes.byref(p), B, T, MODES[mode], ctypes.byref(o), ctypes.byref(n)))
     return int(n.value)
 
 
@@ -205,17 +217,20 @@ def deer_workspace_init(ws, stream=None) -> None:
 
 def deer_solve(cell: Cell, x, s0=None, mode: str = "dense", tol: float = 1e-6, max_iter: int = 100,
                init_guess=None, out=None, workspace=None, stream=None, scan_f64: bool = False,
-               damping: float = 0.0, multi_launch: bool = False):
-    """Parallel fixed-point solve; returns ``(traj, iters, resid, status, rc)``.
+               damping: float = 0.0, multi_launch: bool = False, stall_window: int = STALL_WINDOW_DEFAULT,
+               stall_escalate: bool = True, rms: bool = False):
+    """Parallel fixed-point solve; returns ``(traj, iters, resid, status, rc)``,
+    plus the per-sequence root-mean-square residual with ``rms=True``.
 
     ``mode``: ``"dense"`` (Newton), ``"diag"`` (diagonal quasi-Newton),
     ``"jacobi"`` or ``"picard"``; ``damping`` k shrinks the dense / diag blocks
     to ``(1 - k) J``.  ``traj`` is a ``[B,T,D]`` CUDA tensor; ``iters``,
     ``status`` are numpy int32 ``[B]``, ``resid`` numpy float32 ``[B]``; ``rc``
     is DEER_OK or DEER_NOT_CONVERGED.  ``scan_f64`` (dense mode) accumulates
-    the linear solve in double precision.  ``multi_launch`` keeps small tanh
-    problems (D <= 4, T <= 1024) on the multi-launch loop instead of the
-    single-launch path.
+    the linear solve in double precision from the start.  ``multi_launch``
+    keeps small tanh problems (D <= 4, T <= 1024) on the multi-launch loop
+    instead of the single-launch path.  ``stall_window`` / ``stall_escalate``:
+    the finite-step check of ``deer_solve_opts_t`` (0 turns it off).
     """
     import numpy as np
     import torch
@@ -225,22 +240,27 @@ def deer_solve(cell: Cell, x, s0=None, mode: str = "dense", tol: float = 1e-6, m
     if M != cell.M:
         raise ValueError(f"x has input size {M}, the cell expects {cell.M}")
     p = cell.params()
+    o = solve_opts(damping, scan_f64, multi_launch, stall_window, stall_escalate)
     if out is None:
         out = torch.empty((B, T, D), dtype=torch.float32, device=x.device)
     if workspace is None:
-        workspace = new_workspace(deer_workspace_size(cell, B, T, mode, scan_f64), device=x.device)
+        workspace = new_workspace(deer_workspace_size(cell, B, T, mode, scan_f64, stall_window, stall_escalate),
+                                  device=x.device)
     iters = np.zeros(B, np.int32)
     resid = np.zeros(B, np.float32)
+    rms_a = np.zeros(B, np.float32)
     status = np.zeros(B, np.int32)
     rc = lib.deer_solve(ctypes.byref(p), _dev(x, "x", shape=(B, T, M)), _dev(s0, "s0", shape=(B, D)), B, T,
-                        _mode(mode, scan_f64, multi_launch), ctypes.c_float(damping), ctypes.c_float(tol),
-                        int(max_iter),
+                        MODES[mode], ctypes.c_float(tol), int(max_iter), ctypes.byref(o),
                         _dev(init_guess, "init_guess", shape=(B, T, D)), _dev(out, "out", shape=(B, T, D)),
                         iters.ctypes.data_as(ctypes.c_void_p), resid.ctypes.data_as(ctypes.c_void_p),
+                        rms_a.ctypes.data_as(ctypes.c_void_p) if rms else None,
                         status.ctypes.data_as(ctypes.c_void_p),
                         _dev(workspace, "workspace", dtype=workspace.dtype),
                         workspace.numel() * workspace.element_size(), _stream(stream))
     _check(rc, allow_nc=True)
+    if rms:
+        return out, iters, resid, status, rc, rms_a
     return out, iters, resid, status, rc
 
 
@@ -340,12 +360,12 @@ def deer_lle(cell: Cell, x, traj, v0, s0=None, out=None, workspace=None, stream=
     return out
 
 
-def _broyden_opts(rank, multisecant, alpha, damping, gram_reg, chunk, sketch, D):
+def _broyden_opts(rank, multisecant, alpha, damping, gram_reg, chunk, sketch, D, stall_window):
     if rank > 0 and sketch is None:
         raise ValueError("a sketch [D, rank] is required for rank > 0")
     sk = _dev(sketch, "sketch", shape=(D, rank)) if rank > 0 else None
     return BroydenOpts(int(rank), int(bool(multisecant)), float(alpha), float(damping), float(gram_reg), int(chunk),
-                       sk)
+                       sk, int(stall_window))
 
 
 def deer_broyden_workspace_size(cell: Cell, B: int, T: int, rank: int = 2, multisecant: bool = False,
@@ -353,7 +373,7 @@ def deer_broyden_workspace_size(cell: Cell, B: int, T: int, rank: int = 2, multi
     lib = load_library()
     n = ctypes.c_size_t(0)
     p = cell.params()
-    o = BroydenOpts(int(rank), int(bool(multisecant)), 0.0, 0.0, 0.0, int(chunk), None)
+    o = BroydenOpts(int(rank), int(bool(multisecant)), 0.0, 0.0, 0.0, int(chunk), None, 0)
     _check(lib.deer_broyden_workspace_size(ctypes.byref(p), B, T, ctypes.byref(o), ctypes.byref(n)))
     return int(n.value)
 
@@ -361,7 +381,7 @@ def deer_broyden_workspace_size(cell: Cell, B: int, T: int, rank: int = 2, multi
 def deer_solve_broyden(cell: Cell, x, sketch=None, s0=None, rank: int = 2, multisecant: bool = False,
                        alpha: float = 0.0, damping: float = 0.0, gram_reg: float = 0.0, chunk: int = 32,
                        tol: float = 1e-6, max_iter: int = 100, init_guess=None, out=None, workspace=None,
-                       stream=None):
+                       stream=None, stall_window: int = STALL_WINDOW_DEFAULT):
     """Parallel Broyden solve; returns ``(traj, iters, resid, status, rc)`` like
     :func:`deer_solve`.  ``sketch`` is a ``[D, rank]`` CUDA tensor."""
     import numpy as np
@@ -372,7 +392,7 @@ def deer_solve_broyden(cell: Cell, x, sketch=None, s0=None, rank: int = 2, multi
     if M != cell.M:
         raise ValueError(f"x has input size {M}, the cell expects {cell.M}")
     p = cell.params()
-    o = _broyden_opts(rank, multisecant, alpha, damping, gram_reg, chunk, sketch, D)
+    o = _broyden_opts(rank, multisecant, alpha, damping, gram_reg, chunk, sketch, D, stall_window)
     if out is None:
         out = torch.empty((B, T, D), dtype=torch.float32, device=x.device)
     if workspace is None:

@@ -23,8 +23,9 @@
  *     after a call returns.  Scratch memory comes from the caller's workspace
  *     (linear_scan_diag_noalloc: from a static device array instead).
  *   - Return value: DEER_OK (0) on success, DEER_NOT_CONVERGED (1) when
- *     deer_solve ran to max_iter for at least one sequence (a result, not an
- *     error), a negative DEER_ERR_* code otherwise.  After a negative return
+ *     deer_solve or deer_solve_broyden stopped at least one sequence without
+ *     converging (a result, not an error), a negative DEER_ERR_* code
+ *     otherwise.  After a negative return
  *     deer_last_error() describes the problem.  Nothing is thrown across the
  *     interface.
  *   - One workspace must not be used by two calls that may run at the same
@@ -50,30 +51,11 @@ extern "C" {
  *   PICARD  A_t = I: the next iterate accumulates the one-step corrections
  * with offsets b_t = f_t - A_t s_{t-1}, so every mode keeps the trajectory as
  * its fixed point and recovers it exactly within T iterations.  k is the
- * damping argument of deer_solve (scale-ELK: "Parallel Broyden Methods",
+ * damping option of deer_solve (scale-ELK: "Parallel Broyden Methods",
  * appendix E.4).
  */
 enum deer_mode { DEER_MODE_DENSE = 0, DEER_MODE_DIAG = 1, DEER_MODE_JACOBI = 2, DEER_MODE_PICARD = 3 };
 
-/*
- * Flag or-ed into the mode of deer_solve (dense mode only): the linear solve
- * accumulates its chunk products, offsets and carried states in double
- * precision (inputs, outputs and the cell evaluation stay float32).  For
- * unpredictable dynamics, float32 products of many Jacobians grow large enough
- * that rounding breaks the step-to-step consistency of the solved trajectory at
- * chunk boundaries and the residual stalls above small tolerances; the pages
- * note that float32 overflow forced damping for Newton on such systems
- * ("Parallel Broyden Methods", appendix F.2).
- */
-#define DEER_SCAN_F64 16
-/*
- * Flag or-ed into the mode of deer_solve: always run the multi-launch
- * iteration loop.  Without it, tanh problems with D <= 4 and T <= 1024 (not
- * DEER_SCAN_F64) run as one launch in which one workgroup per sequence
- * performs every iteration on chip (same arithmetic and stopping rule; the
- * scan tree differs, so results differ only by rounding).
- */
-#define DEER_MULTI_LAUNCH 32
 enum deer_cell { DEER_CELL_TANH = 0, DEER_CELL_GRU = 1 };
 
 enum deer_status {
@@ -90,7 +72,8 @@ enum deer_status {
 enum deer_seq_status {
     DEER_SEQ_CONVERGED = 0,      /* residual <= tol after iters_out[b] iterations */
     DEER_SEQ_NOT_CONVERGED = 1,  /* max_iter reached with a finite residual */
-    DEER_SEQ_NONFINITE = 2       /* max_iter reached with a NaN / Inf residual */
+    DEER_SEQ_NONFINITE = 2,      /* max_iter reached with a NaN / Inf residual */
+    DEER_SEQ_STALLED = 3         /* rounding stopped the finite-step progress (see deer_solve_opts_t) */
 };
 
 /*
@@ -121,10 +104,55 @@ typedef struct {
 } deer_cell_params_t;
 
 /*
- * Bytes of device workspace deer_solve needs for this problem (host output).
- * Returns DEER_OK, or an error for an unsupported problem.
+ * Options of deer_solve.  Passing NULL means DEER_SOLVE_OPTS_DEFAULT.
+ *
+ *   damping         k in [0, 1]: the blocks become (1 - k) J_t (dense) or
+ *                   (1 - k) diag(J_t) (diag); must be 0 for Jacobi and Picard.
+ *                   k = 0 is the undamped method, k = 1 turns it into Jacobi.
+ *                   Damping keeps Newton's float32 iterates finite on
+ *                   unpredictable dynamics ("Parallel Broyden Methods",
+ *                   appendix E.4 and its full-rank RNN experiment).
+ *   scan_f64        dense mode only: the linear solve accumulates its chunk
+ *                   products, offsets and carried states in double precision
+ *                   from the first iteration (inputs, outputs and the cell
+ *                   evaluation stay float32).
+ *   multi_launch    1: always run the multi-launch iteration loop.  Otherwise
+ *                   tanh problems with D <= 4 and T <= 1024 run as one launch in
+ *                   which one workgroup per sequence performs every iteration on
+ *                   chip (same arithmetic and stopping rule; the scan tree
+ *                   differs, so results differ only by rounding).
+ *   stall_window    the finite-step check, 0 = off.  After i iterations the
+ *                   first i states are exact in exact arithmetic ("Parallel
+ *                   Broyden Methods", Theorem 1), so the first position whose
+ *                   residual exceeds tol (the front) is never below i.  When a
+ *                   sequence's best front stays below i and has not advanced for
+ *                   stall_window iterations, rounding has stopped its progress:
+ *                   it is stopped with DEER_SEQ_STALLED, unless escalation applies.
+ *                   The check is off when tol < 0 (nothing passes; the call runs
+ *                   exactly max_iter iterations).
+ *   stall_escalate  dense mode, 1: the first stall switches the whole solve's
+ *                   linear solve to double accumulation (as scan_f64) and the
+ *                   stalled sequences go on; a stall after that stops them.  With
+ *                   float32 products of many Jacobians of unpredictable dynamics,
+ *                   rounding breaks the step-to-step consistency of the solved
+ *                   trajectory at chunk boundaries; this is the stall it repairs.
  */
-int deer_workspace_size(const deer_cell_params_t *p, int B, int T, int mode, size_t *bytes_out);
+typedef struct {
+    float damping;
+    int scan_f64;
+    int multi_launch;
+    int stall_window;
+    int stall_escalate;
+} deer_solve_opts_t;
+#define DEER_SOLVE_OPTS_DEFAULT {0.0f, 0, 0, 16, 1}
+
+/*
+ * Bytes of device workspace deer_solve needs for this problem and options
+ * (opts may be NULL; host output).  Returns DEER_OK, or an error for an
+ * unsupported problem.
+ */
+int deer_workspace_size(const deer_cell_params_t *p, int B, int T, int mode, const deer_solve_opts_t *opts,
+                        size_t *bytes_out);
 
 /*
  * Zero-fill a workspace on `stream`.  Every workspace (for deer_solve,
@@ -143,32 +171,40 @@ int deer_workspace_init(void *workspace, size_t ws_bytes, void *stream);
  *   p           cell parameters (host struct holding device pointers)
  *   x           device [B,T,M] inputs
  *   s0          device [B,D] initial states, or NULL for zeros
- *   mode        enum deer_mode, optionally or-ed with DEER_SCAN_F64 (dense only)
- *               and DEER_MULTI_LAUNCH
- *   damping     k in [0, 1]: the blocks become (1 - k) J_t (dense) or
- *               (1 - k) diag(J_t) (diag); must be 0 for Jacobi and Picard.
- *               k = 0 is the undamped method, k = 1 turns it into Jacobi.
+ *   mode        enum deer_mode
  *   tol         stop when max_{t,d} |s_t - f(s_{t-1}, x_t)| <= tol for a
  *               sequence (absolute L-infinity residual, tested on each iterate
  *               before it is refined; NaN never passes)
  *   max_iter    iteration cap (>= 0); at most T iterations are ever needed in
  *               exact arithmetic
+ *   opts        deer_solve_opts_t, or NULL for the defaults
  *   init_guess  device [B,T,D] starting trajectory, or NULL for zeros
  *   traj_out    device [B,T,D]: per sequence the first iterate that passed the
- *               test, or the iterate after max_iter iterations
+ *               test, or the iterate after max_iter iterations (or at the stall)
  *   iters_out   host [B]: iterations (linearise + solve steps) applied
- *   resid_out   host [B] or NULL: the residual of the returned iterate
+ *   resid_out   host [B] or NULL: the L-infinity residual of the returned iterate
+ *   rms_out     host [B] or NULL: its root-mean-square residual
+ *               ||r||_2 / sqrt(T D) ("Parallel Broyden Methods", appendix D.2),
+ *               computed by one more evaluation after the solve (only when asked)
  *   status_out  host [B] or NULL: enum deer_seq_status per sequence
  *   workspace   device, >= deer_workspace_size bytes, 256-byte aligned,
  *               zero-filled before its first use (deer_workspace_init)
  * Sequences are independent: each stops on its own and is frozen there.
  * The call enqueues its kernels on `stream`, polls a convergence flag on the
  * device once per batch of iterations (no per-iteration host sync), and
- * returns after the outputs are complete.
+ * returns after the outputs are complete.  Returns DEER_NOT_CONVERGED when any
+ * sequence did not converge (status 1, 2 or 3).
+ *
+ * The diagonal-block modes and the GRU's fused iteration run a single-pass
+ * scan whose tiles wait on earlier tiles (a decoupled look-back over a
+ * persistent grid sized to the device's resident capacity).  That assumes the
+ * whole grid is resident at once: another kernel occupying compute units on a
+ * concurrent stream can delay it; the wait is bounded, and if the bound is hit
+ * the call returns DEER_ERR_DEVICE.
  */
-int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int B, int T,
-               int mode, float damping, float tol, int max_iter, const float *init_guess, float *traj_out,
-               int *iters_out, float *resid_out, int *status_out, void *workspace, size_t ws_bytes,
+int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int B, int T, int mode, float tol,
+               int max_iter, const deer_solve_opts_t *opts, const float *init_guess, float *traj_out,
+               int *iters_out, float *resid_out, float *rms_out, int *status_out, void *workspace, size_t ws_bytes,
                void *stream);
 
 /*
@@ -184,6 +220,10 @@ int linear_scan_workspace_size(int B, int T, int D, int dense, size_t *bytes_out
  *   a, b   device [B,T,D];  s0 device [B,D] or NULL (zeros);  s device [B,T,D]
  *   (s may alias neither a nor b).  One pass: reads a and b once, writes s once.
  *   Any B, T >= 0, 1 <= D.
+ * Tiles wait on earlier tiles (decoupled look-back) over a persistent grid
+ * sized to the device's resident capacity; a kernel occupying compute units
+ * on a concurrent stream can delay it, and if the bounded wait gives up the
+ * affected outputs are NaN.
  */
 int linear_scan_diag(const float *a, const float *b, const float *s0, float *s, int B, int T, int D,
                      void *workspace, size_t ws_bytes, void *stream);
@@ -280,6 +320,7 @@ typedef struct {
     float gram_reg;       /* >= 0, added to the diagonal of S^T S (multisecant) */
     int chunk;            /* positions per scan chunk, 1..4096 */
     const float *sketch;  /* device [D, rank] random sketch; may be NULL when rank = 0 (and for the size query) */
+    int stall_window;     /* finite-step check as in deer_solve_opts_t (0 = off); a stall stops the sequence */
 } deer_broyden_opts_t;
 
 /* Bytes of workspace deer_solve_broyden needs (host output). */

@@ -17,6 +17,7 @@
  *     sequential forward substitution");
  *   - sequential solvers of the linear recurrence s_t = A_t s_{t-1} + b_t in
  *     diagonal and dense form;
+ *   - the residual r_t = s_t - f(s_{t-1}) of a given trajectory;
  *   - the largest Lyapunov exponent ("Predictability Enables Parallelization"
  *     page, rebuttal "LLE computation cost", Algorithm 1);
  *   - the parallel Broyden iteration with diagonal-plus-low-rank blocks and
@@ -112,6 +113,34 @@ int ORC_CAT(orc_rollout, SUF)(const orc_cell *c, const float *x, const float *s0
         ORC_CAT(o_rollout_one, SUF)(c, x + (size_t)b * T * c->M, s0 ? s0 + (size_t)b * c->D : NULL, \
                                     T, out + (size_t)b * T * c->D, tmp);                         \
         free(tmp);                                                                               \
+    }                                                                                            \
+    return err ? -1 : 0;                                                                         \
+}                                                                                                \
+                                                                                                 \
+/* Residual r_t = s_t - f(s_{t-1}, x_t) of a given trajectory (s_{-1} = s0),   \
+ * the quantity the parallel methods drive to zero ("Predictability" page,     \
+ * rebuttal, restating its equation 2).  traj, r: [B,T,D]. */                   \
+int ORC_CAT(orc_residual, SUF)(const orc_cell *c, const float *x, const float *s0, const REAL *traj, \
+                               int B, int T, REAL *r, int threads)                               \
+{                                                                                                \
+    if (!c || !traj || !r || B < 0 || T < 0 || c->D <= 0) return -1;                             \
+    int err = 0;                                                                                 \
+    const int D = c->D;                                                                          \
+    const int nt = orc_threads(threads, B);                                                      \
+    _Pragma("omp parallel for num_threads(nt) schedule(dynamic, 1) reduction(|:err)")            \
+    for (int b = 0; b < B; ++b) {                                                                \
+        REAL *buf = (REAL *)malloc(sizeof(REAL) * 8 * (size_t)D);                                \
+        if (!buf) { err |= 1; continue; }                                                        \
+        REAL *sp0 = buf, *f = buf + D, *tmp = buf + 2 * D;                                       \
+        for (int d = 0; d < D; ++d) sp0[d] = s0 ? (REAL)s0[(size_t)b * D + d] : (REAL)0;         \
+        const REAL *sb = traj + (size_t)b * T * D;                                               \
+        for (int t = 0; t < T; ++t) {                                                            \
+            const REAL *sp = (t == 0) ? sp0 : sb + (size_t)(t - 1) * D;                          \
+            ORC_CAT(o_step, SUF)(c, sp, x + ((size_t)b * T + t) * c->M, f, NULL, NULL, tmp);     \
+            for (int d = 0; d < D; ++d)                                                          \
+                r[((size_t)b * T + t) * D + d] = sb[(size_t)t * D + d] - f[d];                   \
+        }                                                                                        \
+        free(buf);                                                                               \
     }                                                                                            \
     return err ? -1 : 0;                                                                         \
 }                                                                                                \

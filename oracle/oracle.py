@@ -52,7 +52,7 @@ def lib():
         if not os.path.exists(_LIB_PATH):
             build()
         _lib = ctypes.CDLL(_LIB_PATH)
-        for name in ("orc_step", "orc_rollout", "orc_solve_diag", "orc_solve_dense", "orc_newton",
+        for name in ("orc_step", "orc_rollout", "orc_residual", "orc_solve_diag", "orc_solve_dense", "orc_newton",
                      "orc_lle", "orc_broyden", "orc_dplr_scan", "orc_broyden_update"):
             for suf in ("_f64", "_f32"):
                 getattr(_lib, name + suf).restype = ctypes.c_int
@@ -136,6 +136,21 @@ def rollout(cell: Cell, x, s0=None, precision: str = "f64", threads: int = 0) ->
                                                     threads)
     if rc != 0:
         raise RuntimeError("orc_rollout failed")
+    return out
+
+
+def residual(cell: Cell, x, traj, s0=None, precision: str = "f64", threads: int = 0) -> np.ndarray:
+    """Residual ``r_t = s_t - f(s_{t-1}, x_t)`` of a trajectory ``[B, T, D]``."""
+    dt = _dt(precision)
+    x = _f32(x)
+    B, T = x.shape[0], x.shape[1]
+    traj = np.ascontiguousarray(traj, dtype=dt)
+    s0 = None if s0 is None else _f32(s0)
+    out = np.empty((B, T, cell.D), dt)
+    rc = getattr(lib(), "orc_residual_" + precision)(cell.ref, _ptr(x), _ptr(s0), _ptr(traj), B, T, _ptr(out),
+                                                     threads)
+    if rc != 0:
+        raise RuntimeError("orc_residual failed")
     return out
 
 

@@ -55,28 +55,38 @@ def test_workspace_size_checks(deer):
     lib = deer.load_library()
     n = ctypes.c_size_t(0)
     p = _params(deer)
-    assert lib.deer_workspace_size(ctypes.byref(p), 4, 100, deer.DEER_MODE_DENSE, ctypes.byref(n)) == 0
+    ws = lambda prm, B, T, mode, o=None: lib.deer_workspace_size(ctypes.byref(prm), B, T, mode,  # noqa: E731
+                                                                  None if o is None else ctypes.byref(o),
+                                                                  ctypes.byref(n))
+    assert ws(p, 4, 100, deer.DEER_MODE_DENSE) == 0
     dense = n.value
     assert dense > 0 and dense % 256 == 0
-    assert lib.deer_workspace_size(ctypes.byref(p), 4, 100, deer.DEER_MODE_DIAG, ctypes.byref(n)) == 0
+    # float32-only options (no double accumulation, no escalation) need less
+    assert ws(p, 4, 100, deer.DEER_MODE_DENSE, deer.solve_opts(stall_escalate=False)) == 0 and n.value < dense
+    assert ws(p, 4, 100, deer.DEER_MODE_DENSE, deer.solve_opts(scan_f64=True, stall_window=0)) == 0
+    assert n.value == dense
+    assert ws(p, 4, 100, deer.DEER_MODE_DIAG) == 0
     assert n.value > 0
     big = _params(deer, D=65)
-    assert lib.deer_workspace_size(ctypes.byref(big), 4, 100, 0, ctypes.byref(n)) == -2
+    assert ws(big, 4, 100, 0) == -2
     assert b"outside 1..64" in lib.deer_last_error()
     gru = _params(deer, cell="gru")
-    assert lib.deer_workspace_size(ctypes.byref(gru), 4, 100, deer.DEER_MODE_DENSE, ctypes.byref(n)) == -2
-    assert lib.deer_workspace_size(ctypes.byref(gru), 4, 100, deer.DEER_MODE_DIAG, ctypes.byref(n)) == 0
+    assert ws(gru, 4, 100, deer.DEER_MODE_DENSE) == -2
+    assert ws(gru, 4, 100, deer.DEER_MODE_DIAG) == 0
     diag = n.value
     for mode in (deer.DEER_MODE_JACOBI, deer.DEER_MODE_PICARD):      # diagonal-block modes share diag's layout
-        assert lib.deer_workspace_size(ctypes.byref(gru), 4, 100, mode, ctypes.byref(n)) == 0 and n.value == diag
-        assert lib.deer_workspace_size(ctypes.byref(p), 4, 100, mode, ctypes.byref(n)) == 0
-    assert lib.deer_workspace_size(ctypes.byref(p), 4, 100, deer.DEER_MODE_JACOBI | deer.DEER_SCAN_F64,
-                                   ctypes.byref(n)) == -2
-    assert lib.deer_workspace_size(ctypes.byref(p), -1, 100, 0, ctypes.byref(n)) == -1
-    assert lib.deer_workspace_size(ctypes.byref(p), 4, 100, 7, ctypes.byref(n)) == -1
-    assert lib.deer_workspace_size(None, 4, 100, 0, ctypes.byref(n)) == -1
+        assert ws(gru, 4, 100, mode) == 0 and n.value == diag
+        assert ws(p, 4, 100, mode) == 0
+    assert ws(p, 4, 100, deer.DEER_MODE_JACOBI, deer.solve_opts(scan_f64=True)) == -2    # dense only
+    assert b"scan_f64" in lib.deer_last_error()
+    assert ws(p, 4, 100, deer.DEER_MODE_DIAG, deer.solve_opts(stall_window=-1)) == -1
+    assert ws(p, 4, 100, deer.DEER_MODE_DIAG, deer.solve_opts(damping=1.5)) == -1
+    assert ws(p, -1, 100, 0) == -1
+    assert ws(p, 4, 100, 7) == -1
+    assert ws(p, 4, 100, 16) == -1                                    # flags are no longer or-ed into the mode
+    assert lib.deer_workspace_size(None, 4, 100, 0, None, ctypes.byref(n)) == -1
     bad = deer.CellParams(5, 8, 8, ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1000), None, None)
-    assert lib.deer_workspace_size(ctypes.byref(bad), 4, 100, 0, ctypes.byref(n)) == -1
+    assert ws(bad, 4, 100, 0) == -1
 
 
 def test_workspace_grows_with_problem(deer):
@@ -131,9 +141,12 @@ def test_solve_argument_checks(deer):
     p = _params(deer)
     it = (ctypes.c_int * 4)()
     fake = ctypes.c_void_p(0x1000)
-    args = lambda B, T, mode, tol, mi, ws, wsb, k=0.0: (ctypes.byref(p), fake, None, B, T, mode,  # noqa: E731
-                                                        ctypes.c_float(k), ctypes.c_float(tol), mi, None,
-                                                        ctypes.c_void_p(0x2000), it, None, None, ws, wsb, None)
+
+    def args(B, T, mode, tol, mi, ws, wsb, k=0.0, **kw):
+        o = deer.solve_opts(damping=k, **kw)
+        return (ctypes.byref(p), fake, None, B, T, mode, ctypes.c_float(tol), mi, ctypes.byref(o), None,
+                ctypes.c_void_p(0x2000), it, None, None, None, ws, wsb, None)
+
     assert lib.deer_solve(*args(4, 10, 0, 1e-6, -1, fake, 1 << 30)) == -1          # max_iter < 0
     assert lib.deer_solve(*args(4, 10, 0, float("nan"), 5, fake, 1 << 30)) == -1   # tol NaN
     assert lib.deer_solve(*args(4, 10, 0, 1e-6, 5, None, 0)) == -3                 # no workspace
@@ -143,13 +156,16 @@ def test_solve_argument_checks(deer):
         assert lib.deer_solve(*args(4, 10, mode, 1e-6, 5, fake, 1 << 30, k)) == -1  # only dense/diag take it
         assert b"damping" in lib.deer_last_error()
     assert lib.deer_solve(*args(4, 10, 4, 1e-6, 5, fake, 1 << 30)) == -1          # unknown mode
+    assert lib.deer_solve(*args(4, 10, 1, 1e-6, 5, fake, 1 << 30, scan_f64=True)) == -2   # double scan: dense only
+    assert lib.deer_solve(*args(4, 10, 0, 1e-6, 5, fake, 1 << 30, stall_window=-3)) == -1
     # empty trajectories: residual 0 passes any tol >= 0 after zero iterations
     st = (ctypes.c_int * 4)()
-    assert lib.deer_solve(ctypes.byref(p), None, None, 4, 0, 0, ctypes.c_float(0.0), ctypes.c_float(1e-6), 5, None,
-                          None, it, None, st, None, 0, None) == 0
-    assert list(it) == [0, 0, 0, 0] and list(st) == [0, 0, 0, 0]
-    assert lib.deer_solve(ctypes.byref(p), None, None, 4, 0, 0, ctypes.c_float(0.0), ctypes.c_float(-1.0), 5, None,
-                          None, it, None, st, None, 0, None) == 1
+    rms = (ctypes.c_float * 4)(9, 9, 9, 9)
+    assert lib.deer_solve(ctypes.byref(p), None, None, 4, 0, 0, ctypes.c_float(1e-6), 5, None, None, None, it, None,
+                          rms, st, None, 0, None) == 0
+    assert list(it) == [0, 0, 0, 0] and list(st) == [0, 0, 0, 0] and list(rms) == [0, 0, 0, 0]
+    assert lib.deer_solve(ctypes.byref(p), None, None, 4, 0, 0, ctypes.c_float(-1.0), 5, None, None, None, it, None,
+                          None, st, None, 0, None) == 1
     assert list(it) == [5, 5, 5, 5] and list(st) == [1, 1, 1, 1]
 
 

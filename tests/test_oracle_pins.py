@@ -381,6 +381,32 @@ def test_newton_local_rate_is_quadratic_and_quasi_is_linear(orc):
     assert np.all(ratios > 1e-3) and np.all(ratios < 0.9), q
 
 
+@pytest.mark.parametrize("cell", ["tanh", "gru"])
+def test_residual_of_a_perturbed_rollout(orc, cell):
+    """r_t = s_t - f(s_{t-1}): zero along the rollout; moving one state s_k by
+    eps makes r_k = eps exactly and r_{k+1} = f(s_k) - f(s_k + eps) (the next
+    step feels it), every other entry stays zero (the residual is local in
+    time, "Predictability" page, rebuttal, its equation 2)."""
+    p = (I.tanh_problem(41, 2, 30, 5, 3, gain=0.9, bias_std=0.3, s0_std=0.5) if cell == "tanh"
+         else I.gru_problem(42, 2, 30, 5, 3, bias_std=0.3, s0_std=0.5))
+    c = orc.Cell.from_problem(p)
+    s = orc.rollout(c, p["x"], p["s0"])
+    r = orc.residual(c, p["x"], s, p["s0"])
+    assert np.abs(r).max() < 1e-15
+    k, eps = 11, 0.25
+    q = s.copy()
+    q[1, k, 2] += eps
+    r = orc.residual(c, p["x"], q, p["s0"])
+    assert r[1, k, 2] == pytest.approx(eps, abs=1e-15)
+    f_next, _, _ = orc.step(c, q[1, k], p["x"][1, k + 1])
+    np.testing.assert_allclose(r[1, k + 1], s[1, k + 1] - f_next, rtol=0, atol=1e-15)
+    assert np.abs(r[1, k + 1]).max() > 1e-3
+    mask = np.ones(r.shape, bool)
+    mask[1, k, 2] = False
+    mask[1, k + 1] = False
+    assert np.abs(r[mask]).max() < 1e-15
+
+
 # -------------------------------------------------------- Lyapunov exponent
 
 def test_lle_linear_scalar_closed_form(orc):

@@ -144,49 +144,74 @@ struct ProfScope {
     }
 };
 
-// Pinned host words for polling the device's all-done flag, one set per host thread.
-struct PollSlots {
-    int *host = nullptr;
-    PollSlots()
-    {
-        if (hipHostMalloc(reinterpret_cast<void **>(&host), 64 * sizeof(int), hipHostMallocDefault) != hipSuccess)
-            host = nullptr;
-    }
-};
-thread_local PollSlots g_poll;
-
-// Pinned staging for the per-sequence results read back at the end of a solve
-// (copies into pageable memory take tens of microseconds each); one buffer
-// per host thread, grown on demand, reused only after the stream has been
-// synchronised.
-struct ResultStage {
-    char *host = nullptr;
+// Pinned host memory of one solve call: the polling words (all-done and
+// escalate, two slots) and the staging buffer for the per-sequence results
+// read back at the end (copies into pageable memory take tens of microseconds
+// each), grown on demand.  Calls lease a set from a process-wide pool and give
+// it back on return, so the pool holds as many sets as calls have run at the
+// same time, whatever the number of host threads.
+struct HostStage {
+    int *poll = nullptr;
+    char *stage = nullptr;
     size_t cap = 0;
     char *get(size_t bytes)
     {
-        if (bytes <= cap) return host;
-        if (host) (void)hipHostFree(host);
-        host = nullptr;
+        if (bytes <= cap) return stage;
+        if (stage) (void)hipHostFree(stage);
+        stage = nullptr;
         cap = 0;
-        if (hipHostMalloc(reinterpret_cast<void **>(&host), bytes, hipHostMallocDefault) != hipSuccess) {
-            host = nullptr;
+        if (hipHostMalloc(reinterpret_cast<void **>(&stage), bytes, hipHostMallocDefault) != hipSuccess) {
+            stage = nullptr;
             return nullptr;
         }
         cap = bytes;
-        return host;
+        return stage;
     }
 };
-thread_local ResultStage g_stage;
+
+std::mutex g_host_mu;
+std::vector<HostStage *> g_host_free;
+
+class HostLease {
+public:
+    HostLease()
+    {
+        {
+            std::lock_guard<std::mutex> lock(g_host_mu);
+            if (!g_host_free.empty()) {
+                h_ = g_host_free.back();
+                g_host_free.pop_back();
+            }
+        }
+        if (!h_) h_ = new HostStage();
+        if (!h_->poll &&
+            hipHostMalloc(reinterpret_cast<void **>(&h_->poll), 4 * sizeof(int), hipHostMallocDefault) != hipSuccess)
+            h_->poll = nullptr;
+    }
+    ~HostLease()
+    {
+        std::lock_guard<std::mutex> lock(g_host_mu);
+        g_host_free.push_back(h_);
+    }
+    HostLease(const HostLease &) = delete;
+    HostLease &operator=(const HostLease &) = delete;
+    HostStage &operator*() const { return *h_; }
+    HostStage *operator->() const { return h_; }
+
+private:
+    HostStage *h_ = nullptr;
+};
 
 // Iteration counts, residuals, statuses and (when abort_dev is set) the
 // look-back abort word: enqueued into the pinned stage, one stream
 // synchronisation, then copied to the caller's host arrays.
-int read_results(const int *iters_dev, const int *status_dev, const float *resid_dev, const unsigned *abort_dev,
-                 int B, hipStream_t stream, int *iters_out, float *resid_out, std::vector<int> &status_h,
-                 unsigned &abort_flag, const char *who, const float *rms_dev = nullptr, float *rms_out = nullptr)
+int read_results(HostStage &hs, const int *iters_dev, const int *status_dev, const float *resid_dev,
+                 const unsigned *abort_dev, int B, hipStream_t stream, int *iters_out, float *resid_out,
+                 std::vector<int> &status_h, unsigned &abort_flag, const char *who, const float *rms_dev = nullptr,
+                 float *rms_out = nullptr)
 {
     const size_t need = (2 * sizeof(int) + 2 * sizeof(float)) * static_cast<size_t>(B) + sizeof(unsigned);
-    char *st = g_stage.get(need);
+    char *st = hs.get(need);
     if (!st) {
         (void)hipStreamSynchronize(stream);
         return fail(DEER_ERR_HIP, std::string(who) + ": pinned host memory unavailable");
@@ -454,7 +479,7 @@ struct PollEvents {
 // at once.  `total` caps the evaluations enqueued.
 template <class Enqueue, class OnEscalate>
 int run_polled(Enqueue &&enqueue_iteration, SolveControl *ctl, long long total, hipStream_t stream, PollEvents &pe,
-               const char *who, OnEscalate &&on_escalate)
+               HostStage &hs, const char *who, OnEscalate &&on_escalate)
 {
     int rc = DEER_OK;
     long long launched = 0;
@@ -465,7 +490,7 @@ int run_polled(Enqueue &&enqueue_iteration, SolveControl *ctl, long long total, 
             return fail(DEER_ERR_HIP, std::string(who) + ": event creation failed");
     bool pending = false;
     int pending_slot = 0;
-    volatile int *h = g_poll.host;
+    volatile int *h = hs.poll;
     // each slot holds the two adjacent control words (all_done, escalate)
     while (launched < total) {
         const long long n = std::min<long long>(batch, total - launched);
@@ -474,7 +499,7 @@ int run_polled(Enqueue &&enqueue_iteration, SolveControl *ctl, long long total, 
         launched += n;
         h[2 * slot] = 0;
         h[2 * slot + 1] = 0;
-        if (hipMemcpyAsync(g_poll.host + 2 * slot, &ctl->all_done, 2 * sizeof(int), hipMemcpyDeviceToHost, stream) !=
+        if (hipMemcpyAsync(hs.poll + 2 * slot, &ctl->all_done, 2 * sizeof(int), hipMemcpyDeviceToHost, stream) !=
                 hipSuccess ||
             hipEventRecord(pe.ev[slot], stream) != hipSuccess) {
             rc = fail(DEER_ERR_HIP, std::string(who) + ": polling copy failed");
@@ -787,7 +812,8 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
     if (!x || !traj_out) return fail(DEER_ERR_INVALID, "x and traj_out are required");
     rc = check_workspace(workspace, ws_bytes, solve_layout(nullptr, p, B, T, mode, o).bytes, "deer_solve");
     if (rc) return rc;
-    if (!g_poll.host) return fail(DEER_ERR_HIP, "deer_solve: pinned host memory unavailable");
+    HostLease host;
+    if (!host->poll) return fail(DEER_ERR_HIP, "deer_solve: pinned host memory unavailable");
 
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     const SolveLayout L = solve_layout(workspace, p, B, T, mode, o);
@@ -827,7 +853,7 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
     if (!gru && !o.scan_f64 && !o.multi_launch && tiny_solve_fits(D, T)) {
         // small problem: the whole solve, projection included, in one launch that
         // writes the per-sequence results straight into the pinned stage
-        char *st = g_stage.get((2 * sizeof(int) + 2 * sizeof(float)) * static_cast<size_t>(B));
+        char *st = host->get((2 * sizeof(int) + 2 * sizeof(float)) * static_cast<size_t>(B));
         if (!st) return fail(DEER_ERR_HIP, "deer_solve: pinned host memory unavailable");
         int *h_iters = reinterpret_cast<int *>(st);
         int *h_status = h_iters + B;
@@ -942,7 +968,7 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
 
     const long long total = static_cast<long long>(max_iter) + 1;   // evaluations needed at most
     PollEvents pe;
-    rc = run_polled(enqueue_iteration, L.ctl, total, stream, pe, "deer_solve", [&]() {
+    rc = run_polled(enqueue_iteration, L.ctl, total, stream, pe, *host, "deer_solve", [&]() {
         if (can_escalate) scan_f64 = true;
     });
     if (rc == DEER_OK) {
@@ -956,7 +982,7 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
     if (rc == DEER_OK) {
         const unsigned *abort_dev =
             (diag_blocks(mode) || fused) ? &static_cast<ScanHeader *>(L.scan)->abort : nullptr;
-        rc = read_results(L.iters, L.status, L.resid, abort_dev, B, stream, iters_out, resid_out, status_h,
+        rc = read_results(*host, L.iters, L.status, L.resid, abort_dev, B, stream, iters_out, resid_out, status_h,
                           abort_flag, "deer_solve", L.rms, rms_out);
     } else {
         (void)hipStreamSynchronize(stream);
@@ -1018,7 +1044,8 @@ int deer_solve_broyden(const deer_cell_params_t *p, const float *x, const float 
     if (!x || !traj_out) return fail(DEER_ERR_INVALID, "x and traj_out are required");
     rc = check_workspace(workspace, ws_bytes, broyden_layout(nullptr, p, B, T, opts).bytes, "deer_solve_broyden");
     if (rc) return rc;
-    if (!g_poll.host) return fail(DEER_ERR_HIP, "deer_solve_broyden: pinned host memory unavailable");
+    HostLease host;
+    if (!host->poll) return fail(DEER_ERR_HIP, "deer_solve_broyden: pinned host memory unavailable");
 
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     const BroydenLayout L = broyden_layout(workspace, p, B, T, opts);
@@ -1089,7 +1116,7 @@ int deer_solve_broyden(const deer_cell_params_t *p, const float *x, const float 
     };
     const long long total = static_cast<long long>(max_iter) + 1;
     PollEvents pe;
-    rc = run_polled(enqueue_iteration, L.ctl, total, stream, pe, "deer_solve_broyden", []() {});
+    rc = run_polled(enqueue_iteration, L.ctl, total, stream, pe, *host, "deer_solve_broyden", []() {});
     if (rc == DEER_OK) {
         const size_t per_seq = static_cast<size_t>(T) * D;
         DEER_LAUNCH(gather_kernel, dim3(grid_for(per_seq, 256, 1024), B), dim3(256), 0, stream, traj_out, L.buf1,
@@ -1099,8 +1126,8 @@ int deer_solve_broyden(const deer_cell_params_t *p, const float *x, const float 
     std::vector<int> status_h(B, 0);
     unsigned abort_flag = 0;
     if (rc == DEER_OK) {
-        rc = read_results(L.iters, L.status, L.resid, nullptr, B, stream, iters_out, resid_out, status_h, abort_flag,
-                          "deer_solve_broyden");
+        rc = read_results(*host, L.iters, L.status, L.resid, nullptr, B, stream, iters_out, resid_out, status_h,
+                          abort_flag, "deer_solve_broyden");
     } else {
         (void)hipStreamSynchronize(stream);
     }

@@ -156,40 +156,45 @@ __device__ __forceinline__ int row_ror(int v)   // DPP rotation by K lanes withi
     return __builtin_amdgcn_update_dpp(0, v, 0x120 + K, 0xf, 0xf, true);
 }
 
-// acc += w * (x rotated right by K lanes within each row of 16) as one
-// v_fmac_f32_dpp (the compiler keeps the rotation as a separate v_mov_b32_dpp).
-// The same fused multiply-add on the same operands, so the same bits.  The
-// first rotation of a contraction waits two cycles: a DPP source written by
-// the VALU just before needs two wait states, and the hazard check does not
-// look inside asm.
-template <int K>
-__device__ __forceinline__ void fmac_row_ror(float &acc, float x, float w)
-{
-    if constexpr (K == 1)
-        asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_ror:%3 row_mask:0xf bank_mask:0xf bound_ctrl:1"
-                     : "+v"(acc) : "v"(x), "v"(w), "n"(K));
-    else
-        asm volatile("v_fmac_f32_dpp %0, %1, %2 row_ror:%3 row_mask:0xf bank_mask:0xf bound_ctrl:1"
-                     : "+v"(acc) : "v"(x), "v"(w), "n"(K));
-}
-
-template <int K>
+// The 15 rotated products of a row contraction: a0 (even k) and a1 (odd k)
+// accumulate w[k] * (x rotated right by k lanes within each row of 16), each
+// as one v_fmac_f32_dpp (the compiler would keep every rotation as a separate
+// v_mov_b32_dpp next to the FMA).  The same fused multiply-adds on the same
+// operands in the same order, so the same bits.  A DPP source written by the
+// VALU just before needs two wait states and the hazard check does not look
+// inside asm, so the chain is one asm statement that opens with them: no
+// compiler instruction can come between the wait and the DPP reads of x.
 struct RowRotations {
     static __device__ __forceinline__ void sources(int m, int (&src)[16])
     {
-        src[K] = row_ror<K>(m);
-        RowRotations<K + 1>::sources(m, src);
+        src[1] = row_ror<1>(m); src[2] = row_ror<2>(m); src[3] = row_ror<3>(m); src[4] = row_ror<4>(m);
+        src[5] = row_ror<5>(m); src[6] = row_ror<6>(m); src[7] = row_ror<7>(m); src[8] = row_ror<8>(m);
+        src[9] = row_ror<9>(m); src[10] = row_ror<10>(m); src[11] = row_ror<11>(m); src[12] = row_ror<12>(m);
+        src[13] = row_ror<13>(m); src[14] = row_ror<14>(m); src[15] = row_ror<15>(m);
     }
     static __device__ __forceinline__ void contract(float x, const float (&w)[16], float &a0, float &a1)
     {
-        if (K & 1) fmac_row_ror<K>(a1, x, w[K]); else fmac_row_ror<K>(a0, x, w[K]);
-        RowRotations<K + 1>::contract(x, w, a0, a1);
+        asm volatile(
+        "s_nop 1\n\t"
+        "v_fmac_f32_dpp %1, %2, %3 row_ror:1 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %0, %2, %4 row_ror:2 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %1, %2, %5 row_ror:3 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %0, %2, %6 row_ror:4 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %1, %2, %7 row_ror:5 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %0, %2, %8 row_ror:6 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %1, %2, %9 row_ror:7 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %0, %2, %10 row_ror:8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %1, %2, %11 row_ror:9 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %0, %2, %12 row_ror:10 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %1, %2, %13 row_ror:11 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %0, %2, %14 row_ror:12 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %1, %2, %15 row_ror:13 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %0, %2, %16 row_ror:14 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %1, %2, %17 row_ror:15 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+            : "+v"(a0), "+v"(a1)
+            : "v"(x), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(w[4]), "v"(w[5]), "v"(w[6]), "v"(w[7]), "v"(w[8]),
+              "v"(w[9]), "v"(w[10]), "v"(w[11]), "v"(w[12]), "v"(w[13]), "v"(w[14]), "v"(w[15]));
     }
-};
-template <>
-struct RowRotations<16> {
-    static __device__ __forceinline__ void sources(int, int (&)[16]) {}
-    static __device__ __forceinline__ void contract(float, const float (&)[16], float &, float &) {}
 };
 
 __device__ __forceinline__ void offset_chain32(const float *__restrict__ W, const float *ds, const float *bs, int n,
@@ -201,7 +206,7 @@ __device__ __forceinline__ void offset_chain32(const float *__restrict__ W, cons
     // by rotating the lane indices themselves
     int src[16];
     src[0] = m;
-    RowRotations<1>::sources(m, src);
+    RowRotations::sources(m, src);
     const int KA = r & 1, IA = r >> 1, KB = r >> 1, IB = r & 1;
     float wA[16], wB[16];
 #pragma unroll
@@ -211,7 +216,7 @@ __device__ __forceinline__ void offset_chain32(const float *__restrict__ W, cons
     }
     auto contract = [&](float x, const float (&w)[16]) -> float {
         float a0 = w[0] * x, a1 = 0.0f;
-        RowRotations<1>::contract(x, w, a0, a1);
+        RowRotations::contract(x, w, a0, a1);
         return a0 + a1;
     };
     float x = bs[16 * KA + m];                        // B_0 in the A layout
@@ -602,7 +607,7 @@ __global__ __launch_bounds__(64) void dense_replay_dpp32_kernel(
     const int lane = threadIdx.x, r = lane >> 4, m = lane & 15;
     int src[16];
     src[0] = m;
-    RowRotations<1>::sources(m, src);
+    RowRotations::sources(m, src);
     const int KA = r & 1, IA = r >> 1, KB = r >> 1, IB = r & 1;
     float wA[16], wB[16];
 #pragma unroll
@@ -612,7 +617,7 @@ __global__ __launch_bounds__(64) void dense_replay_dpp32_kernel(
     }
     auto contract = [&](float x, const float (&w)[16]) -> float {
         float a0 = w[0] * x, a1 = 0.0f;
-        RowRotations<1>::contract(x, w, a0, a1);
+        RowRotations::contract(x, w, a0, a1);
         return a0 + a1;
     };
     float *out = ((out_sel && (*out_sel & 1)) ? out1 : out0) + base;

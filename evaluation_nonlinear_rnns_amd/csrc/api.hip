@@ -425,6 +425,14 @@ struct SolveLayout {
     size_t bytes = 0;
 };
 
+// The persistent dense solve's state, for the shapes it may take (dense tanh,
+// D <= 16); its own checks decide at solve time whether it runs.
+size_t persist_state_bytes(const deer_cell_params_t *p, int B, int T, int mode, bool f64)
+{
+    if (p->cell != DEER_CELL_TANH || mode != DEER_MODE_DENSE || p->D > 16 || T < 1 || T > 8192) return 0;
+    return dense_persist_state_bytes(B, T, f64);
+}
+
 SolveLayout solve_layout(void *ws, const deer_cell_params_t *p, int B, int T, int mode, const deer_solve_opts_t &o)
 {
     const bool f64 = may_use_f64(o, mode);
@@ -436,7 +444,8 @@ SolveLayout solve_layout(void *ws, const deer_cell_params_t *p, int B, int T, in
     const bool fused = fused_gru_step(p, mode);
     const size_t scan_bytes = fused ? gru_step_state_bytes(B, T, p->D)
                               : diag_blocks(mode) ? diag_scan_state_bytes(B, T, p->D)
-                                                         : dense_scan_state_bytes(B, T, p->D, f64);
+                                                  : std::max(dense_scan_state_bytes(B, T, p->D, f64),
+                                                             persist_state_bytes(p, B, T, mode, f64));
     L.scan = c.take<char>(scan_bytes);
     L.ctl = c.take<SolveControl>(1);
     L.res_bits = c.take<unsigned>(B);
@@ -893,6 +902,56 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
             if (resid_out) resid_out[b] = h_resid[b];
             if (rms_out) rms_out[b] = h_rms[b];
             if (status_out) status_out[b] = h_status[b];
+        }
+        return any_nc ? DEER_NOT_CONVERGED : DEER_OK;
+    }
+
+    // Dense tanh problems the device holds at once: the whole solve in one
+    // launch (a second, double-precision one continues stalled sequences).
+    const bool can_escalate_once = dense && o.stall_window > 0 && o.stall_escalate && !o.scan_f64 && tol >= 0.0f;
+    const bool state_f64 = may_use_f64(o, mode);   // as solve_layout sized it
+    if (!gru && dense && !o.multi_launch && dense_persist_fits(B, D, T, o.scan_f64 != 0) &&
+        (!can_escalate_once || dense_persist_fits(B, D, T, true))) {
+        if (init_guess) {
+            if (init_guess != traj_out)
+                DEER_LAUNCH(copy_kernel, dim3(grid_for(BTD)), dim3(256), 0, stream, traj_out, init_guess, BTD);
+        } else {
+            DEER_LAUNCH(fill_kernel, dim3(grid_for(BTD)), dim3(256), 0, stream, traj_out, BTD, 0.0f);
+        }
+        DEER_HIP(hipGetLastError());
+        prof.begin(2);
+        rc = launch_projection(x, p->U, p->b, L.proj, B, T, p->M, PD, false, stream);
+        prof.end();
+        if (rc) return rc;
+        const int window = tol >= 0.0f ? o.stall_window : 0;   // tol < 0 never passes: exactly max_iter iterations
+        prof.begin(0);
+        rc = launch_dense_persist(p->W, L.proj, s0, traj_out, B, T, D, lz.shrink, tol, max_iter, window,
+                                  o.scan_f64 != 0, can_escalate_once, false, L.iters, L.status, L.resid, L.scan,
+                                  state_f64, stream);
+        prof.end();
+        if (rc == DEER_OK && can_escalate_once) {
+            prof.begin(1);
+            rc = launch_dense_persist(p->W, L.proj, s0, traj_out, B, T, D, lz.shrink, tol, max_iter, window, true,
+                                      false, true, L.iters, L.status, L.resid, L.scan, state_f64, stream);
+            prof.end();
+        }
+        if (rc == DEER_OK && rms_out) rc = residual_rms(true);
+        std::vector<int> status_h(B, 0);
+        unsigned abort_flag = 0;
+        if (rc == DEER_OK) {
+            rc = read_results(*host, L.iters, L.status, L.resid, dense_persist_abort_word(L.scan, B, T, state_f64), B, stream,
+                              iters_out, resid_out, status_h, abort_flag, "deer_solve", L.rms, rms_out);
+        } else {
+            (void)hipStreamSynchronize(stream);
+        }
+        if (rc) return rc;
+        const long long limit[kProfKinds] = {1, can_escalate_once ? 1 : 0, 1, 0};
+        prof.collect(limit);
+        if (abort_flag) return fail(DEER_ERR_DEVICE, "deer_solve: a wait of the one-launch solve hit its bound");
+        bool any_nc = false;
+        for (int b = 0; b < B; ++b) {
+            if (status_out) status_out[b] = status_h[b];
+            any_nc |= status_h[b] != DEER_SEQ_CONVERGED;
         }
         return any_nc ? DEER_NOT_CONVERGED : DEER_OK;
     }

@@ -68,6 +68,55 @@ extern thread_local ProfLaunch g_prof_launch;
         }                                                                                                     \
     } while (0)
 
+// ------------------------------------------------------ row contractions
+// DPP rotation by K lanes within each row of 16 lanes.
+template <int K>
+__device__ __forceinline__ int row_ror(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, 0x120 + K, 0xf, 0xf, true);
+}
+
+// The 15 rotated products of a row contraction: a0 (even k) and a1 (odd k)
+// accumulate w[k] * (x rotated right by k lanes within each row of 16), each
+// as one v_fmac_f32_dpp (the compiler would keep every rotation as a separate
+// v_mov_b32_dpp next to the FMA).  The same fused multiply-adds on the same
+// operands in the same order, so the same bits.  A DPP source written by the
+// VALU just before needs two wait states and the hazard check does not look
+// inside asm, so the chain is one asm statement that opens with them: no
+// compiler instruction can come between the wait and the DPP reads of x.
+struct RowRotations {
+    static __device__ __forceinline__ void sources(int m, int (&src)[16])
+    {
+        src[1] = row_ror<1>(m); src[2] = row_ror<2>(m); src[3] = row_ror<3>(m); src[4] = row_ror<4>(m);
+        src[5] = row_ror<5>(m); src[6] = row_ror<6>(m); src[7] = row_ror<7>(m); src[8] = row_ror<8>(m);
+        src[9] = row_ror<9>(m); src[10] = row_ror<10>(m); src[11] = row_ror<11>(m); src[12] = row_ror<12>(m);
+        src[13] = row_ror<13>(m); src[14] = row_ror<14>(m); src[15] = row_ror<15>(m);
+    }
+    static __device__ __forceinline__ void contract(float x, const float (&w)[16], float &a0, float &a1)
+    {
+        asm volatile(
+        "s_nop 1\n\t"
+        "v_fmac_f32_dpp %1, %2, %3 row_ror:1 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %0, %2, %4 row_ror:2 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %1, %2, %5 row_ror:3 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %0, %2, %6 row_ror:4 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %1, %2, %7 row_ror:5 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %0, %2, %8 row_ror:6 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %1, %2, %9 row_ror:7 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %0, %2, %10 row_ror:8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %1, %2, %11 row_ror:9 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %0, %2, %12 row_ror:10 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %1, %2, %13 row_ror:11 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %0, %2, %14 row_ror:12 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %1, %2, %15 row_ror:13 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %0, %2, %16 row_ror:14 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+        "v_fmac_f32_dpp %1, %2, %17 row_ror:15 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+            : "+v"(a0), "+v"(a1)
+            : "v"(x), "v"(w[1]), "v"(w[2]), "v"(w[3]), "v"(w[4]), "v"(w[5]), "v"(w[6]), "v"(w[7]), "v"(w[8]),
+              "v"(w[9]), "v"(w[10]), "v"(w[11]), "v"(w[12]), "v"(w[13]), "v"(w[14]), "v"(w[15]));
+    }
+};
+
 // ------------------------------------------------------------ solve control
 // Device-side state of one deer_solve call.
 struct SolveControl {
@@ -456,6 +505,26 @@ bool tiny_solve_fits(int D, int T);
 int launch_tiny_solve(const float *W, const float *U, const float *bias, const float *x, int M, const float *s0,
                       const float *init, float *traj, int B, int T, int D, bool dense, Linearization lz, float tol,
                       int max_iter, int stall_window, int *iters, int *status, float *resid, hipStream_t stream);
+
+// Whole dense tanh solves in one launch (dense_solve.hip): each sequence gets a
+// group of workgroups that synchronise among themselves, one group barrier per
+// iteration; for D <= 16, T <= 8192 and grids the device holds at once (f64:
+// double accumulation).  `proj` is the input projection; `traj` holds s^(0)
+// on entry and, on exit, the iterate each sequence stopped at.  `state` holds
+// dense_persist_state_bytes and is set up by each launch; iters, status and
+// resid are device arrays.  With `escalate`, a stalled sequence is handed over
+// (an internal status) instead of stopped; a launch with `resume` and f64
+// continues exactly those sequences and leaves the others alone.  state_f64:
+// the state was sized with f64 (needed by any double-precision launch).
+bool dense_persist_fits(int B, int D, int T, bool f64);
+size_t dense_persist_state_bytes(int B, int T, bool f64);
+int launch_dense_persist(const float *W, const float *proj, const float *s0, float *traj, int B, int T, int D,
+                         float shrink, float tol, int max_iter, int stall_window, bool f64, bool escalate,
+                         bool resume, int *iters, int *status, float *resid, void *state, bool state_f64,
+                         hipStream_t stream);
+// Set (non-zero) when a bounded wait of the launches since the last
+// non-resumed one hit its bound.
+unsigned *dense_persist_abort_word(void *state, int B, int T, bool state_f64);
 
 // Parallel Broyden (broyden.hip): the block updates and the chunked compressed
 // scan of delta_t = A_t delta_{t-1} + c_t, A_t = alpha I + shrink U_t V_t^T.

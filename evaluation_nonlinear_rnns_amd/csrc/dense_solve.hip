@@ -180,7 +180,9 @@ struct PersistArgs {
     unsigned long long *slot;   // [2][B][G]: residual maximum, front and tag of each workgroup, by parity
     unsigned long long *agg;    // [2][B][G][AGGW]: workgroup aggregates, by parity
     unsigned long long *xch;    // [B][G][16]: last state of each workgroup's range
-    int *keep;             // [B] best finite-step front of a sequence handed over
+    int *keep;             // [B][2] best finite-step front and iteration of its last advance, of a
+                           // sequence handed over
+    unsigned *esc_flag;    // set once a sequence stalled (with `escalate`): every sequence hands over
     unsigned *abort_flag;
     int escalate;          // a stall hands the sequence over instead of stopping it
     int resume;            // continue the handed-over sequences, skip the rest
@@ -192,9 +194,10 @@ struct PersistArgs {
 // sees the expected tag has the value of that iteration, so no fence or flag
 // has to order the words (each word validates itself).  Float words: value in
 // the low half, tag i + 1 in the high half; a double takes two words.  Residual
-// slots: maximum |r| bits in the low half, then the front (16 bits, 0xFFFF for
-// none; positions are below 8192) and a 16-bit tag in 1..65535.  The buffers
-// are zeroed at launch, and zero is never an expected tag.
+// slots: maximum |r| bits in the low half, then the front (15 bits, 0x7FFF for
+// none; positions are below 8192), a bit that asks for the hand-over to double
+// precision, and a 16-bit tag in 1..65535.  The buffers are zeroed at launch,
+// and zero is never an expected tag.
 __device__ __forceinline__ unsigned tag32(int i) { return static_cast<unsigned>(i) + 1u; }
 __device__ __forceinline__ unsigned tag16(int i) { return static_cast<unsigned>(i + 1) % 0xFFFFu + 1u; }
 __device__ __forceinline__ void put_word(unsigned long long *p, unsigned bits, unsigned tag)
@@ -206,9 +209,9 @@ __device__ __forceinline__ unsigned long long get_word(const unsigned long long 
 {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ unsigned long long slot_word(unsigned rmax, unsigned front, int i)
+__device__ __forceinline__ unsigned long long slot_word(unsigned rmax, unsigned front, unsigned esc, int i)
 {
-    const unsigned f16 = front == kNoFront ? 0xFFFFu : front;
+    const unsigned f16 = (front == kNoFront ? 0x7FFFu : front) | (esc ? 0x8000u : 0u);
     return (static_cast<unsigned long long>((f16 << 16) | tag16(i)) << 32) | rmax;
 }
 
@@ -270,7 +273,7 @@ struct PersistLds {
     ACC Wg[(kMaxGroup - 1) * (kDP * kDP + kDP)];        // earlier workgroups' aggregates
     __align__(16) ACC line[kNC][kDP];                   // per-wavefront line of the quarter-row contractions
     unsigned red[2][kNC];                               // per-wavefront residual maximum and front
-    unsigned dec_r, dec_f;                              // the group's residual maximum and front
+    unsigned dec_r, dec_f, dec_esc;                     // the group's residual maximum, front, hand-over
     int abort_now;                                      // a wait gave up (from wavefront 0)
 };
 
@@ -299,8 +302,8 @@ __global__ __launch_bounds__(kThreads) void dense_persist_kernel(PersistArgs a)
     if (a.resume) {                                      // a resumed sequence keeps its best front and
         if (a.status[bseq] != kPendingEscalation) return;   // starts a fresh window where it stopped
         i0 = a.iters[bseq];
-        best = a.keep[bseq];
-        last_adv = i0;
+        best = a.keep[2 * bseq];
+        last_adv = a.keep[2 * bseq + 1];
     }
 
     // W in the layouts the phases need (zero past D)
@@ -388,6 +391,9 @@ __global__ __launch_bounds__(kThreads) void dense_persist_kernel(PersistArgs a)
     unsigned target = 0;
     for (int i = i0;; ++i) {
         const int slot = i % 3;
+        // whether some sequence has asked for the hand-over (read early, used in the slot)
+        unsigned esc_seen = 0u;
+        if (a.escalate && tid == 0) esc_seen = __hip_atomic_load(a.esc_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         // ---- 1. evaluation of the wavefront's chunk; wavefront 0 takes its first
         // 16 positions last, once the state before the range is in (from the left
         // neighbour's replay; the state rows hold it at the first iteration)
@@ -502,7 +508,7 @@ __global__ __launch_bounds__(kThreads) void dense_persist_kernel(PersistArgs a)
         if (tid == 0) {
             unsigned m = sh.red[0][0], f = sh.red[1][0];
             for (int q = 1; q < kNC; ++q) { m = max(m, sh.red[0][q]); f = min(f, sh.red[1][q]); }
-            __hip_atomic_store(slot0 + (i & 1) * slots + w, slot_word(m, f, i), __ATOMIC_RELAXED,
+            __hip_atomic_store(slot0 + (i & 1) * slots + w, slot_word(m, f, esc_seen, i), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         }
 
@@ -522,14 +528,17 @@ __global__ __launch_bounds__(kThreads) void dense_persist_kernel(PersistArgs a)
                 if (poll_step(spins, a.abort_flag)) { ab = 1; break; }
             }
             unsigned m = lane < a.G ? static_cast<unsigned>(v) : 0u;
-            unsigned f = lane < a.G ? static_cast<unsigned>(v >> 48) : 0xFFFFu;
+            unsigned f = lane < a.G ? static_cast<unsigned>(v >> 48) & 0x7FFFu : 0x7FFFu;
+            const bool esc = lane < a.G && ((v >> 63) & 1ull);
             for (int o = 32; o > 0; o >>= 1) {
                 m = max(m, static_cast<unsigned>(__shfl_xor(static_cast<int>(m), o, 64)));
                 f = min(f, static_cast<unsigned>(__shfl_xor(static_cast<int>(f), o, 64)));
             }
+            const bool esc_any = __any(esc);
             if (lane == 0) {
                 sh.dec_r = m;
-                sh.dec_f = f == 0xFFFFu ? kNoFront : f;
+                sh.dec_f = f == 0x7FFFu ? kNoFront : f;
+                sh.dec_esc = esc_any ? 1u : 0u;
                 sh.abort_now = __builtin_amdgcn_readfirstlane(ab);
             }
         }
@@ -544,13 +553,24 @@ __global__ __launch_bounds__(kThreads) void dense_persist_kernel(PersistArgs a)
             stop = DEER_SEQ_CONVERGED;
         } else if (i >= a.max_iter) {
             stop = __builtin_isfinite(r) ? DEER_SEQ_NOT_CONVERGED : DEER_SEQ_NONFINITE;
-        } else if (a.stall_window > 0) {
-            const int f = fr > 0x7FFFFFFFu ? 0x7FFFFFFF : static_cast<int>(fr);
-            if (f > best) {
-                best = f;
-                last_adv = i;
-            } else if (best < i && i - last_adv >= a.stall_window) {
-                stop = a.escalate ? kPendingEscalation : DEER_SEQ_STALLED;
+        } else {
+            bool stalled = false;
+            if (a.stall_window > 0) {
+                const int f = fr > 0x7FFFFFFFu ? 0x7FFFFFFF : static_cast<int>(fr);
+                if (f > best) {
+                    best = f;
+                    last_adv = i;
+                } else if (best < i && i - last_adv >= a.stall_window) {
+                    stalled = true;
+                }
+            }
+            if (stalled && !a.escalate) {
+                stop = DEER_SEQ_STALLED;
+            } else if (stalled || (a.escalate && sh.dec_esc)) {
+                // handed over to double precision at this iteration; a stalled
+                // sequence starts a fresh window there, the others keep theirs
+                stop = kPendingEscalation;
+                if (stalled) last_adv = i;
             }
         }
         if (stop >= 0) {
@@ -563,7 +583,11 @@ __global__ __launch_bounds__(kThreads) void dense_persist_kernel(PersistArgs a)
                 a.iters[bseq] = i;
                 a.status[bseq] = stop;
                 a.resid[bseq] = r;
-                if (stop == kPendingEscalation) a.keep[bseq] = best;
+                if (stop == kPendingEscalation) {
+                    a.keep[2 * bseq] = best;
+                    a.keep[2 * bseq + 1] = last_adv;
+                    __hip_atomic_store(a.esc_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
             }
             break;
         }
@@ -647,11 +671,14 @@ __global__ __launch_bounds__(kThreads) void dense_persist_kernel(PersistArgs a)
 
 // Zeroes the tagged-word buffers of a launch (zero is never an expected tag)
 // and, unless the launch resumes another one, the abort word.
-__global__ void persist_init_kernel(unsigned long long *words, size_t n, unsigned *abort_flag)
+__global__ void persist_init_kernel(unsigned long long *words, size_t n, unsigned *esc_flag, unsigned *abort_flag)
 {
     const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
     for (size_t e = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < n; e += stride) words[e] = 0ull;
-    if (blockIdx.x == 0 && threadIdx.x == 0 && abort_flag) *abort_flag = 0u;
+    if (blockIdx.x == 0 && threadIdx.x == 0 && abort_flag) {
+        *abort_flag = 0u;
+        *esc_flag = 0u;
+    }
 }
 
 template <class ACC>
@@ -694,7 +721,7 @@ bool persist_resident(int B, int T, bool f64)
 // double when a double-precision launch may run, exchange rows) in one block,
 // then the kept fronts and the abort word.
 struct PersistState {
-    size_t slot, agg, xch, words_end, keep, abort_off, bytes;
+    size_t slot, agg, xch, words_end, keep, esc_off, abort_off, bytes;
 };
 PersistState persist_state(int B, int T, bool f64)
 {
@@ -706,7 +733,8 @@ PersistState persist_state(int B, int T, bool f64)
     st.xch = st.agg + 2 * BG * aggw * sizeof(unsigned long long);
     st.words_end = st.xch + BG * kDP * sizeof(unsigned long long);
     st.keep = align_up(st.words_end);
-    st.abort_off = st.keep + align_up(static_cast<size_t>(B) * sizeof(int));
+    st.esc_off = st.keep + align_up(2 * static_cast<size_t>(B) * sizeof(int));
+    st.abort_off = st.esc_off + align_up(sizeof(unsigned));
     st.bytes = st.abort_off + align_up(sizeof(unsigned));
     return st;
 }
@@ -747,14 +775,15 @@ int launch_dense_persist(const float *W, const float *proj, const float *s0, flo
     a.agg = reinterpret_cast<unsigned long long *>(st + ps.agg);
     a.xch = reinterpret_cast<unsigned long long *>(st + ps.xch);
     a.keep = reinterpret_cast<int *>(st + ps.keep);
+    a.esc_flag = reinterpret_cast<unsigned *>(st + ps.esc_off);
     a.abort_flag = reinterpret_cast<unsigned *>(st + ps.abort_off);
     a.escalate = escalate ? 1 : 0;
     a.resume = resume ? 1 : 0;
     // every tagged word of the launch's layout starts at zero; a resumed launch
-    // keeps the abort word and the kept fronts of the launch before it
+    // keeps the abort and hand-over words and the kept fronts of the launch before it
     const size_t nwords = ps.words_end / sizeof(unsigned long long);
     DEER_LAUNCH(persist_init_kernel, dim3(static_cast<unsigned>(std::min<size_t>((nwords + 255) / 256, 2048))),
-                dim3(256), 0, stream, reinterpret_cast<unsigned long long *>(st), nwords,
+                dim3(256), 0, stream, reinterpret_cast<unsigned long long *>(st), nwords, a.esc_flag,
                 resume ? nullptr : a.abort_flag);
     DEER_HIP(hipGetLastError());
     return f64 ? launch_persist<double>(a, stream) : launch_persist<float>(a, stream);

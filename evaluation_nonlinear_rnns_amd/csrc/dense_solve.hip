@@ -42,6 +42,7 @@
 // workgroup resident or about to be; all waits are bounded all the same (the
 // abort word then reports a device error).
 #include <algorithm>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -51,6 +52,8 @@ namespace {
 constexpr int kNC = 8;          // chunks per workgroup, one wavefront each
 constexpr int kThreads = 64 * kNC;
 constexpr int kL = 64;          // positions per chunk
+constexpr int kSub = 16;        // positions per sub-chunk (one row of 16 lanes each)
+constexpr int kNS = kL / kSub;  // sub-chunks per chunk
 constexpr int kDP = 16;         // padded state size
 constexpr int kMaxGroup = 16;   // workgroups per sequence
 constexpr unsigned kBarrierSpin = 1u << 22;   // polls of a barrier wait (seconds)
@@ -167,6 +170,37 @@ __device__ __forceinline__ ACC lds_quad_dot(const ACC *M, ACC x, ACC *line, int 
     return quad_dot<ACC>(x, wq, line, j, g);
 }
 
+// y_j = sum_k W[j][k] x_k with each row of 16 lanes holding its own 16-vector
+// (x_j in lane j of the row) and contracting it alone: float by the DPP row
+// rotations (w in rotation order), double through the row's own LDS line
+// (w in natural order).
+template <class ACC>
+__device__ __forceinline__ ACC row_dot16(ACC x, const float (&w)[kDP], ACC *row_line, int j);
+template <>
+__device__ __forceinline__ float row_dot16<float>(float x, const float (&w)[kDP], float *, int)
+{
+    return row_dot<float>(x, w);
+}
+template <>
+__device__ __forceinline__ double row_dot16<double>(double x, const float (&w)[kDP], double *rl, int j)
+{
+    rl[j] = x;
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    typedef double v2d __attribute__((ext_vector_type(2)));
+    const v2d *p = reinterpret_cast<const v2d *>(rl);
+    double a0 = 0.0, a1 = 0.0;
+#pragma unroll
+    for (int k2 = 0; k2 < kDP / 2; ++k2) {
+        const v2d v = p[k2];
+        a0 = __builtin_fma(static_cast<double>(w[2 * k2]), v[0], a0);
+        a1 = __builtin_fma(static_cast<double>(w[2 * k2 + 1]), v[1], a1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    return a0 + a1;
+}
+
 struct PersistArgs {
     const float *W;        // [D, D]
     const float *proj;     // [B, T, D]: U x_t + b
@@ -272,6 +306,7 @@ struct PersistLds {
     ACC ent[kNC * kDP];                                 // states entering the chunks
     ACC Wg[(kMaxGroup - 1) * (kDP * kDP + kDP)];        // earlier workgroups' aggregates
     __align__(16) ACC line[kNC][kDP];                   // per-wavefront line of the quarter-row contractions
+    __align__(16) ACC line4[kNC][kNS][kDP];             // per-row lines of the double row contractions
     unsigned red[2][kNC];                               // per-wavefront residual maximum and front
     unsigned dec_r, dec_f, dec_esc;                     // the group's residual maximum, front, hand-over
     int abort_now;                                      // a wait gave up (from wavefront 0)
@@ -320,13 +355,15 @@ __global__ __launch_bounds__(kThreads) void dense_persist_kernel(PersistArgs a)
     int src[kDP];                                        // column of W that row rotation k brings to lane j
     src[0] = j;
     RowRotations::sources(j, src);
-    float Wr[kDP];                                       // row j of W in rotation order (float replay)
+    float Wrow[kDP];                                     // row j of W in the order row_dot16 reads it
 #pragma unroll
-    for (int k = 0; k < kDP; ++k) Wr[k] = (j < D && src[k] < D) ? a.W[j * D + src[k]] : 0.0f;
-    ACC Wq[4];                                           // columns 4 g .. 4 g + 3 of row j of W
-#pragma unroll
-    for (int m = 0; m < 4; ++m) Wq[m] = static_cast<ACC>((j < D && 4 * g + m < D) ? a.W[j * D + 4 * g + m] : 0.0f);
-    ACC *line = sh.line[wave];
+    for (int k = 0; k < kDP; ++k) {
+        const int c = sizeof(ACC) == 4 ? src[k] : k;
+        Wrow[k] = (j < D && c < D) ? a.W[j * D + c] : 0.0f;
+    }
+    ACC *line = sh.line[wave];                           // per-wavefront line of the quarter-row contractions
+    ACC *row_line = sh.line4[wave][g];                   // per-row line of the row contractions
+    ACC *scratch = sh.Wg + wave * kDP * kDP;             // per-wavefront 16 x 16 matrix (compose, replay)
     const ACC xs0 = static_cast<ACC>((a.s0 && j < D) ? a.s0[static_cast<size_t>(bseq) * D + j] : 0.0f);
 
     // the input projection at the lane's evaluation outputs (position r0 + 16 q + j,
@@ -427,58 +464,115 @@ __global__ __launch_bounds__(kThreads) void dense_persist_kernel(PersistArgs a)
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         __builtin_amdgcn_wave_barrier();
 
-        // ---- 2. chunk aggregates: wavefront q composes chunk q.  The product runs
-        // as Q_0 = W, Q_s = (W diag(d_{s-1})) Q_{s-1}, P = diag(d_{n-1}) Q_{n-1}: the
-        // diagonal scales the A operand (formed a step ahead, off the chain), and
-        // each step's accumulators are the next step's B operands, so the matrix
-        // cores chain without VALU work between them.  Each step's d and b are read
-        // one step ahead, in two alternating register sets.
+        // ---- 2. chunk aggregates: wavefront q composes chunk q as four
+        // sub-chunks of 16 positions.  Sub-chunk k's product runs as Q_0 = W,
+        // Q_s = (W diag(d_{s-1})) Q_{s-1}, P_k = diag(d_last) Q_last: the diagonal
+        // scales the A operand, each step's accumulators are the next step's B
+        // operands, and the four chains interleave on the matrix cores.  Row k of
+        // lanes runs sub-chunk k's offset chain B <- d_s (W B) + b_s.  Then the
+        // chunk aggregate is P_3 P_2 P_1 P_0 with B folded the same way; P_0..P_2
+        // and B_0..B_2 stay in registers for the replay's sub-chunk entries.
+        ACC Pk[kNS - 1][4] = {}, Bk[kNS - 1] = {};
         if (wave < nch) {
             const float *dq = sh.d + r0 * kDP, *bq = sh.b + r0 * kDP;
-            ACC Q[4];
+            int nk[kNS];                                   // positions of sub-chunk k
 #pragma unroll
-            for (int v = 0; v < 4; ++v) Q[v] = Wcol[v];
-            ACC Bq = static_cast<ACC>(bq[j]);
-            struct Row { float d[4], dj, bj; };
-            auto load = [&](Row &R, int st) {
+            for (int k = 0; k < kNS; ++k) nk[k] = min(max(n - kSub * k, 0), kSub);
+            ACC Q[kNS][4];
 #pragma unroll
-                for (int v = 0; v < 4; ++v) R.d[v] = dq[st * kDP + row16<ACC>(v, g)];
-                R.dj = dq[st * kDP + j];
-                R.bj = bq[st * kDP + j];
+            for (int k = 0; k < kNS; ++k)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) Q[k][v] = Wcol[v];
+            // step st of every sub-chunk's chain: the four chains' instructions
+            // interleave, so no MFMA waits on the one before it.  A chain past its
+            // sub-chunk's end keeps its product (uniform selects; full chunks, the
+            // common case, take the loop without them).
+            auto chain_step = [&](int st, auto full) {
+                ACC acc[kNS][4];
+#pragma unroll
+                for (int k = 0; k < kNS; ++k)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) acc[k][v] = 0;
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int k = 0; k < kNS; ++k) {
+                        const float dv = dq[(kSub * k + st - 1) * kDP + row16<ACC>(u, g)];
+                        mfma16<ACC>(WA[u] * static_cast<ACC>(dv), Q[k][u], acc[k]);
+                    }
+#pragma unroll
+                for (int k = 0; k < kNS; ++k) {
+                    const bool live = decltype(full)::value || st < nk[k];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) Q[k][v] = live ? acc[k][v] : Q[k][v];
+                }
             };
-            // step st (1..n-1): Q <- (W diag(d_{st-1})) Q with `prev` = row st - 1,
-            // and the offset B <- d_st (W B) + b_st with `cur` = row st
-            auto step = [&](const Row &prev, const Row &cur) {
-                ACC A[4];
+            if (n == kL) {
+                for (int st = 1; st < kSub; ++st) chain_step(st, std::true_type{});
+            } else {
+                for (int st = 1; st < kSub; ++st) chain_step(st, std::false_type{});
+            }
+            // offset chains, row g of lanes for sub-chunk g
+            const int ng = nk[0] * (g == 0) + nk[1] * (g == 1) + nk[2] * (g == 2) + nk[3] * (g == 3);
+            const float *dg = dq + kSub * g * kDP, *bg = bq + kSub * g * kDP;
+            ACC x = ng > 0 ? static_cast<ACC>(bg[j]) : static_cast<ACC>(0);
+            for (int st = 1; st < kSub; ++st) {
+                const float dc = dg[st * kDP + j], bc = bg[st * kDP + j];   // padding rows past the chunk
+                const ACC y = row_dot16<ACC>(x, Wrow, row_line, j);
+                const ACC xn = static_cast<ACC>(dc) * y + static_cast<ACC>(bc);
+                x = st < ng ? xn : x;
+            }
+            // the chunk aggregate: P = P_{K-1} ... P_0, B = P_{K-1}(... (P_1 B_0 + B_1) ...) + B_{K-1}
+            ACC *scr = scratch;                               // this wavefront's 16 x 16 matrix
+            ACC Pc[4], Bc;
+            auto sub_P = [&](int k, ACC (&Pm)[4]) {           // P_k in accumulator layout
+                const float *dl = dq + (kSub * k + nk[k] - 1) * kDP;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) A[u] = WA[u] * static_cast<ACC>(prev.d[u]);
-                ACC acc[4] = {0, 0, 0, 0};
-#pragma unroll
-                for (int u = 0; u < 4; ++u) mfma16<ACC>(A[u], Q[u], acc);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) Q[v] = acc[v];
-                const ACC sum = quad_dot<ACC>(Bq, Wq, line, j, g);
-                Bq = static_cast<ACC>(cur.dj) * sum + static_cast<ACC>(cur.bj);
+                for (int v = 0; v < 4; ++v) Pm[v] = static_cast<ACC>(dl[row16<ACC>(v, g)]) * Q[k][v];
             };
-            Row R0, R1;
-            load(R0, 0);
-            int st = 1;
-            for (; st + 1 < n; st += 2) {
-                load(R1, st);
-                step(R0, R1);
-                load(R0, st + 1);
-                step(R1, R0);
-            }
-            if (st < n) {
-                load(R1, st);
-                step(R0, R1);
-                R0 = R1;
-            }
-            // R0 is row n - 1 now
+            auto row_bcast = [&](ACC val, int k) -> ACC {     // row k's value in every row
+                if (g == k) line[j] = val;
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                const ACC r = line[j];
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                return r;
+            };
+            sub_P(0, Pc);
+            Bc = row_bcast(x, 0);
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-                sh.P[wave * kDP * kDP + row16<ACC>(v, g) * kDP + j] = static_cast<ACC>(R0.d[v]) * Q[v];
-            if (g == 0) sh.Bc[wave * kDP + j] = Bq;
+            for (int v = 0; v < 4; ++v) Pk[0][v] = Pc[v];
+            Bk[0] = Bc;
+#pragma unroll
+            for (int k = 1; k < kNS; ++k) {
+                if (nk[k] > 0) {
+                    ACC Pm[4];
+                    sub_P(k, Pm);
+                    const ACC bk = row_bcast(x, k);
+                    if (k < kNS - 1) {
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) Pk[k][v] = Pm[v];
+                        Bk[k] = bk;
+                    }
+                    // P_k to the scratch row-major, then Pc <- P_k Pc, Bc <- P_k Bc + B_k
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) scr[row16<ACC>(v, g) * kDP + j] = Pm[v];
+                    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                    ACC acc[4] = {0, 0, 0, 0};
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) mfma16<ACC>(scr[j * kDP + row16<ACC>(u, g)], Pc[u], acc);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) Pc[v] = acc[v];
+                    Bc = lds_quad_dot<ACC>(scr, Bc, line, j, g) + bk;
+                    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                }
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) sh.P[wave * kDP * kDP + row16<ACC>(v, g) * kDP + j] = Pc[v];
+            if (g == 0) sh.Bc[wave * kDP + j] = Bc;
         }
         __syncthreads();
         if (sh.abort_now) break;
@@ -639,31 +733,41 @@ __global__ __launch_bounds__(kThreads) void dense_persist_kernel(PersistArgs a)
         if (sh.abort_now) break;
 
         // ---- 5. replay of chunk `wave` from its entry: s_t = d_t (W s_{t-1}) + b_t,
-        // into the state rows (every row of lanes writes the same value); the
-        // range's last state also goes to the right neighbour
+        // row g of lanes for sub-chunk g (entries from the kept sub-chunk
+        // aggregates), into the state rows; the range's last state also goes to
+        // the right neighbour
         if (wave < nch) {
-            ACC x = sh.ent[wave * kDP + j];
             const float *dq = sh.d + r0 * kDP, *bq = sh.b + r0 * kDP;
-            float *Sq = sh.S + (r0 + 1) * kDP;
-            auto step = [&](float dc, float bc, int st) {
-                ACC y;
-                if constexpr (sizeof(ACC) == 4) y = row_dot<float>(x, Wr);   // DPP rotations: no LDS on the chain
-                else y = quad_dot<ACC>(x, Wq, line, j, g);
-                x = static_cast<ACC>(dc) * y + static_cast<ACC>(bc);
-                Sq[st * kDP + j] = static_cast<float>(x);
-            };
-            float dA = dq[j], bA = bq[j], dB, bB;
-            int st = 0;
-            for (; st + 1 < n; st += 2) {
-                dB = dq[(st + 1) * kDP + j];
-                bB = bq[(st + 1) * kDP + j];
-                step(dA, bA, st);
-                dA = dq[(st + 2) * kDP + j];
-                bA = bq[(st + 2) * kDP + j];
-                step(dB, bB, st + 1);
+            const int ng = min(max(n - kSub * g, 0), kSub);
+            const int K = (n + kSub - 1) / kSub;
+            ACC *scr = scratch;
+            ACC e = sh.ent[wave * kDP + j];
+            ACC x = e;                                        // row 0's entry
+#pragma unroll
+            for (int k = 0; k + 1 < kNS; ++k) {
+                if (k + 1 < K) {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) scr[row16<ACC>(v, g) * kDP + j] = Pk[k][v];
+                    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                    e = lds_quad_dot<ACC>(scr, e, line, j, g) + Bk[k];
+                    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                    x = g == k + 1 ? e : x;
+                }
             }
-            if (st < n) step(dA, bA, st);
-            if (wave == nch - 1 && w + 1 < a.G && g == 0) Words<float>::put(xout + j, static_cast<float>(x), tag32(i));
+            const float *dg = dq + kSub * g * kDP, *bg = bq + kSub * g * kDP;
+            float *Sg = sh.S + (r0 + kSub * g + 1) * kDP;
+            for (int st = 0; st < kSub; ++st) {
+                const float dc = dg[st * kDP + j], bc = bg[st * kDP + j];   // padding rows past the chunk
+                const ACC y = row_dot16<ACC>(x, Wrow, row_line, j);
+                const ACC xn = static_cast<ACC>(dc) * y + static_cast<ACC>(bc);
+                if (st < ng) {
+                    x = xn;
+                    Sg[st * kDP + j] = static_cast<float>(xn);
+                }
+            }
+            if (wave == nch - 1 && w + 1 < a.G && g == K - 1) Words<float>::put(xout + j, static_cast<float>(x), tag32(i));
         }
         __syncthreads();
     }

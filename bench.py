@@ -176,6 +176,32 @@ def scan_bandwidth(args, dev):
             "elements_per_s": w.B * w.T * w.D / (ms * 1e-3)}
 
 
+def copy_ceiling(dev, reps=10):
+    """Measured HBM ceiling of a plain copy on this machine: a 1 GiB device-to-device
+    copy (dst.copy_(src), the runtime's copy kernel), read + write bytes over
+    its mean duration (HIP events).  Reported next to the datasheet peak."""
+    import torch
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        dst.copy_(src)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    del src, dst
+    torch.cuda.empty_cache()
+    gbs = 2 * 4 * n / (ms * 1e-3) / 1e9
+    return {"GBs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "method": "1 GiB device-to-device copy (dst.copy_(src)), read + write bytes, mean of 10 after 2 warm-ups"}
+
+
 def host_info():
     """Host CPU model and the logical CPUs this process may use."""
     model = "unknown"
@@ -592,8 +618,12 @@ def main():
                     for k, v in kernels.items()},
         "ms_per_step_hip_events": round(ms_events, 4),
     }
+    ceil = copy_ceiling(dev)
+    line["copy_ceiling"] = ceil
+    roof["frac_of_copy_ceiling"] = round(roof["achieved"] / ceil["GBs"], 4)
     if not args.no_scan:
         line["linear_scan"] = scan_bandwidth(args, dev)
+        line["linear_scan"]["frac_of_copy_ceiling"] = round(line["linear_scan"]["achieved_GBs"] / ceil["GBs"], 4)
     if not args.no_dense:
         line["dense_deer"] = dense_solve(args, dev)
         line["tiny_dense"] = tiny_solve(args, dev)

@@ -36,7 +36,7 @@ EXPORTS = ("deer_workspace_size", "deer_workspace_init", "deer_solve", "linear_s
            "linear_scan_diag", "linear_scan_diag_noalloc", "linear_scan_dense", "deer_rollout_workspace_size",
            "deer_rollout", "deer_lle_workspace_size", "deer_lle",
            "deer_broyden_workspace_size", "deer_solve_broyden", "linear_scan_dplr_workspace_size",
-           "linear_scan_dplr", "deer_profile_enable", "deer_profile_read", "deer_last_error")
+           "linear_scan_dplr", "deer_profile_enable", "deer_profile_read", "deer_bandwidth_probe", "deer_last_error")
 
 
 class DeerError(RuntimeError):
@@ -107,6 +107,7 @@ def load_library():
         "linear_scan_dplr": ([fp, vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, vp, c_size, vp], c_int),
         "deer_profile_enable": ([c_int], c_int),
         "deer_profile_read": ([c_int, ctypes.POINTER(ctypes.c_longlong), ctypes.POINTER(ctypes.c_double)], c_int),
+        "deer_bandwidth_probe": ([vp, c_size, vp, c_size, vp], c_int),
         "deer_last_error": ([], ctypes.c_char_p),
     }
     for name, (args, res) in sig.items():
@@ -451,6 +452,18 @@ def deer_profile_read(which: int) -> Tuple[int, float]:
 
 
 PROFILE_EVAL, PROFILE_SCAN, PROFILE_PROJECTION, PROFILE_CHECK = 0, 1, 2, 3
+
+
+def bandwidth_probe(src, dst, stream=None) -> None:
+    """Stream all of ``src`` into ``dst`` (contiguous CUDA tensors; ``src``
+    1, 2, 4 or 8 times the bytes of ``dst``) with the library's probe kernel:
+    output vector i is the XOR of the input vectors i, i + n, ... (a bandwidth
+    reference; a copy when the sizes are equal)."""
+    import torch
+    st = stream if stream is not None else torch.cuda.current_stream()
+    _check(load_library().deer_bandwidth_probe(ctypes.c_void_p(src.data_ptr()), src.numel() * src.element_size(),
+                                               ctypes.c_void_p(dst.data_ptr()), dst.numel() * dst.element_size(),
+                                               ctypes.c_void_p(st.cuda_stream)))
 
 
 def cell_from_problem(p: dict, device="cuda") -> Cell:

@@ -360,10 +360,27 @@ int linear_scan_dplr(float alpha, const float *U, const float *V, const float *c
  *   which: 0 = cell evaluation (f and Jacobian), 1 = linear scan,
  *          2 = input projection, 3 = convergence check.  deer_solve_broyden
  *          times its cell evaluation (0), block updates with the compressed
- *          scan (1), projection (2) and check (3) the same way.
+ *          scan (1), projection (2) and check (3) the same way.  Solves that
+ *          run in one launch count it as 0 (the dense one-launch solve its
+ *          double-precision continuation as 1).
  */
 int deer_profile_enable(int enable);
 int deer_profile_read(int which, long long *launches, double *milliseconds);
+
+/*
+ * Measurement utility, not part of the method: the HBM rate a plain streaming
+ * kernel reaches on this device for a given read / write mix (the bench
+ * reports its kernels against it next to the datasheet peak).  Reads all of
+ * src and writes all of dst once, both as contiguous streams of 16-byte
+ * non-temporal accesses: with k = src_bytes / dst_bytes, output vector
+ * 64 g + l (16 bytes) is the XOR of input vectors 64 (k g + j) + l, j < k
+ * (a last partial group of r < 64 outputs: input vectors
+ * 64 k G + r j + l, G full groups); k = 1 is a copy.
+ * Device pointers; dst_bytes and the addresses multiples of 16, k in
+ * {1, 2, 4, 8}, buffers not overlapping (DEER_ERR_INVALID otherwise).
+ * Asynchronous on the stream.
+ */
+int deer_bandwidth_probe(const void *src, size_t src_bytes, void *dst, size_t dst_bytes, void *stream);
 
 /* Thread-local description of the last failure (never NULL). */
 const char *deer_last_error(void);

@@ -249,3 +249,17 @@ def test_broyden_argument_checks(deer):
     assert lib.linear_scan_dplr(0.5, fake, fake, fake, fake, fake, 4, 100, 16, 2, 32, None, 0, None) == -3
     assert lib.linear_scan_dplr(float("inf"), fake, fake, fake, fake, fake, 4, 100, 16, 2, 32, fake, 1 << 30,
                                 None) == -1
+
+
+def test_bandwidth_probe_argument_checks(deer):
+    lib = deer.load_library()
+    vp = ctypes.c_void_p
+    assert lib.deer_bandwidth_probe(None, 0, None, 0, None) == 0            # nothing to stream
+    assert lib.deer_bandwidth_probe(None, 16, None, 16, None) == -1
+    assert b"null pointer" in lib.deer_last_error()
+    assert lib.deer_bandwidth_probe(vp(4096), 24, vp(1 << 20), 24, None) == -1
+    assert b"multiples of 16" in lib.deer_last_error()
+    assert lib.deer_bandwidth_probe(vp(4096), 48, vp(1 << 20), 16, None) == -1       # k = 3
+    assert b"1, 2, 4 or 8" in lib.deer_last_error()
+    assert lib.deer_bandwidth_probe(vp(4096), 64, vp(4096 + 16), 64, None) == -1
+    assert b"overlap" in lib.deer_last_error()

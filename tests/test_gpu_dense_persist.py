@@ -186,3 +186,28 @@ def test_grid_beyond_the_device_takes_the_loop(orc):
     seqs = [0, 17, 39]
     ref = orc.rollout(orc.Cell.from_problem(p), p["x"][seqs], p["s0"][seqs])
     assert np.all(rel_linf(traj.cpu().numpy()[seqs], ref) <= TOL)
+
+
+@pytest.mark.parametrize("scan_f64", [False, True])
+def test_one_launch_largest_groups_at_full_occupancy(orc, scan_f64):
+    """T = 8192: sixteen workgroups per sequence (the largest group, each
+    staging up to fifteen earlier aggregates), 16 sequences filling the 256
+    workgroups the device holds at once; float and double accumulation."""
+    dev = device()
+    B, T, D, M = 16, 8192, 16, 16
+    p = _problem(2309, B, T, D, M, 0.9)
+    cell = deer.cell_from_problem(p, dev)
+    x = torch.from_numpy(p["x"]).to(dev)
+    s0 = torch.from_numpy(p["s0"]).to(dev)
+    tol = 1e-6 if scan_f64 else 1e-5
+    log(f"one-launch dense solve B={B} T={T} D={D} scan_f64={scan_f64}")
+    (traj, iters, resid, status, rc), n1 = _solve_counted(cell, x, s0, mode="dense", tol=tol, max_iter=T,
+                                                          scan_f64=scan_f64)
+    assert n1 == 1
+    assert rc == deer.DEER_OK and np.all(status == 0)
+    seqs = [0, 7, 15]
+    oc = orc.Cell.from_problem(p)
+    ref = orc.rollout(oc, p["x"][seqs], p["s0"][seqs])
+    _, oit, _, _ = orc.newton(oc, p["x"][seqs], p["s0"][seqs], mode="dense", tol=tol, max_iter=T, precision="f32")
+    assert np.all(np.abs(iters[seqs] - oit) <= 1), (iters[seqs], oit)
+    assert np.all(rel_linf(traj.cpu().numpy()[seqs], ref) <= TOL)

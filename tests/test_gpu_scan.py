@@ -103,3 +103,30 @@ def test_linear_scan_diag_is_bitwise_reproducible(orc):
     log("linear_scan_diag x3 B=3 T=200000 D=64")
     outs = [deer.linear_scan_diag(a, b, None).cpu().numpy() for _ in range(3)]
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("k", [1, 2, 4, 8])
+@pytest.mark.parametrize("nbytes", [16, 4096 + 48, (1 << 24) + 16 * 37])
+def test_bandwidth_probe_streams(k, nbytes):
+    """The bandwidth reference writes the XOR of its k input streams (k = 1: a
+    copy), for sizes below, at and past one grid of four vectors per thread."""
+    dev = device()
+    log(f"deer_bandwidth_probe k={k} {nbytes} bytes out")
+    n = nbytes // 16                                   # 16-byte vectors out
+    src = torch.randint(-2**31, 2**31 - 1, (k * n, 4), dtype=torch.int32, device=dev)
+    dst = torch.zeros((n, 4), dtype=torch.int32, device=dev)
+    deer.bandwidth_probe(src, dst)
+    torch.cuda.synchronize()
+    G, r = n // 64, n % 64
+    full = src[:k * 64 * G].reshape(G, k, 64, 4)
+    ref = full[:, 0].clone()
+    for j in range(1, k):
+        ref ^= full[:, j]
+    ref = ref.reshape(G * 64, 4)
+    if r:
+        tail = src[k * 64 * G:].reshape(k, r, 4)
+        t = tail[0].clone()
+        for j in range(1, k):
+            t ^= tail[j]
+        ref = torch.cat([ref, t])
+    assert torch.equal(dst, ref)

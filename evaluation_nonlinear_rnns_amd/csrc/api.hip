@@ -425,11 +425,11 @@ struct SolveLayout {
     size_t bytes = 0;
 };
 
-// The persistent dense solve's state, for the shapes it may take (dense tanh,
-// D <= 16); its own checks decide at solve time whether it runs.
-size_t persist_state_bytes(const deer_cell_params_t *p, int B, int T, int mode, bool f64)
+// The one-launch solves' state, for the shapes they may take (tanh, D <= 16,
+// every mode); their own checks decide at solve time whether they run.
+size_t persist_state_bytes(const deer_cell_params_t *p, int B, int T, bool f64)
 {
-    if (p->cell != DEER_CELL_TANH || mode != DEER_MODE_DENSE || p->D > 16 || T < 1 || T > 8192) return 0;
+    if (p->cell != DEER_CELL_TANH || p->D > 16 || T < 1 || T > 8192) return 0;
     return dense_persist_state_bytes(B, T, f64);
 }
 
@@ -443,9 +443,9 @@ SolveLayout solve_layout(void *ws, const deer_cell_params_t *p, int B, int T, in
     // the scan state comes first so that its header keeps a fixed place
     const bool fused = fused_gru_step(p, mode);
     const size_t scan_bytes = fused ? gru_step_state_bytes(B, T, p->D)
-                              : diag_blocks(mode) ? diag_scan_state_bytes(B, T, p->D)
-                                                  : std::max(dense_scan_state_bytes(B, T, p->D, f64),
-                                                             persist_state_bytes(p, B, T, mode, f64));
+                              : std::max(diag_blocks(mode) ? diag_scan_state_bytes(B, T, p->D)
+                                                           : dense_scan_state_bytes(B, T, p->D, f64),
+                                         persist_state_bytes(p, B, T, f64));
     L.scan = c.take<char>(scan_bytes);
     L.ctl = c.take<SolveControl>(1);
     L.res_bits = c.take<unsigned>(B);
@@ -906,12 +906,14 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
         return any_nc ? DEER_NOT_CONVERGED : DEER_OK;
     }
 
-    // Dense tanh problems the device holds at once: the whole solve in one
-    // launch (a second, double-precision one continues stalled sequences).
+    // Tanh problems the device holds at once: the whole solve in one launch (in
+    // dense mode a second, double-precision one continues stalled sequences).
     const bool can_escalate_once = dense && o.stall_window > 0 && o.stall_escalate && !o.scan_f64 && tol >= 0.0f;
     const bool state_f64 = may_use_f64(o, mode);   // as solve_layout sized it
-    if (!gru && dense && !o.multi_launch && dense_persist_fits(B, D, T, o.scan_f64 != 0) &&
-        (!can_escalate_once || dense_persist_fits(B, D, T, true))) {
+    const bool one_launch =
+        dense ? dense_persist_fits(B, D, T, o.scan_f64 != 0) && (!can_escalate_once || dense_persist_fits(B, D, T, true))
+              : diag_persist_fits(B, D, T);
+    if (!gru && !o.multi_launch && one_launch) {
         if (init_guess) {
             if (init_guess != traj_out)
                 DEER_LAUNCH(copy_kernel, dim3(grid_for(BTD)), dim3(256), 0, stream, traj_out, init_guess, BTD);
@@ -925,9 +927,13 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
         if (rc) return rc;
         const int window = tol >= 0.0f ? o.stall_window : 0;   // tol < 0 never passes: exactly max_iter iterations
         prof.begin(0);
-        rc = launch_dense_persist(p->W, L.proj, s0, traj_out, B, T, D, lz.shrink, tol, max_iter, window,
-                                  o.scan_f64 != 0, can_escalate_once, false, L.iters, L.status, L.resid, L.scan,
-                                  state_f64, stream);
+        if (dense)
+            rc = launch_dense_persist(p->W, L.proj, s0, traj_out, B, T, D, lz.shrink, tol, max_iter, window,
+                                      o.scan_f64 != 0, can_escalate_once, false, L.iters, L.status, L.resid, L.scan,
+                                      state_f64, stream);
+        else
+            rc = launch_diag_persist(p->W, L.proj, s0, traj_out, B, T, D, lz, tol, max_iter, window, L.iters,
+                                     L.status, L.resid, L.scan, stream);
         prof.end();
         if (rc == DEER_OK && can_escalate_once) {
             prof.begin(1);

@@ -208,11 +208,13 @@ struct PersistArgs {
     float *traj;           // [B, T, D]: s^(i0) on entry, the iterate a sequence stops at on exit
     int B, T, D, nchunk, G, max_iter, stall_window;
     float tol, shrink;
+    int lin_kind;          // diagonal kernel: the linearisation (LinKind)
     int *iters, *status;   // [B]
     float *resid;          // [B]
     // Exchanged between the workgroups of a group as tagged words (below):
     unsigned long long *slot;   // [2][B][G]: residual maximum, front and tag of each workgroup, by parity
-    unsigned long long *agg;    // [2][B][G][AGGW]: workgroup aggregates, by parity
+    unsigned long long *agg;    // [2][B][G][AGGW]: workgroup aggregates, by parity (the diagonal
+                                //   kernel uses the first 2 x 16 words of each)
     unsigned long long *xch;    // [B][G][16]: last state of each workgroup's range
     int *keep;             // [B][2] best finite-step front and iteration of its last advance, of a
                            // sequence handed over
@@ -773,6 +775,316 @@ __global__ __launch_bounds__(kThreads) void dense_persist_kernel(PersistArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// The diagonal linearisations in one launch: quasi-Newton (A_t the damped
+// diagonal of the Jacobian), Jacobi (A_t = 0) and Picard (A_t = I) ("Parallel
+// Broyden Methods", section 2 and its Picard paragraph).  The groups, the
+// evaluation, the tagged-word exchange and the stopping rule are those of the
+// dense kernel above.  A diagonal block stays diagonal under composition, so
+// every fold is element-wise: lane (j, g) of a wavefront folds channel j of
+// sub-chunk g, and a workgroup aggregate is 2 x 16 floats (the products and
+// the offsets of its channels).  Accumulation in float, as the multi-launch
+// diagonal scan.
+
+struct DiagLds {
+    static constexpr int NP = kNC * kL;
+    __align__(16) float S[(NP + 1) * kDP];     // S[r] = s_{tb - 1 + r} of the current iterate
+    __align__(16) float a[NP * kDP];           // a_t, b_t at local position r
+    __align__(16) float b[NP * kDP];
+    float sub[kNC][2][kNS][kDP];               // per wavefront: sub-chunk products and offsets
+    float ch[2][kNC][kDP];                     // chunk products and offsets
+    float ent[kNC][kDP];                       // states entering the chunks
+    float Wg[(kMaxGroup - 1) * 2 * kDP];       // earlier workgroups' aggregates
+    unsigned red[2][kNC];                      // per-wavefront residual maximum and front
+    unsigned dec_r, dec_f;                     // the group's residual maximum and front
+    int abort_now;                             // a wait gave up
+};
+
+__global__ __launch_bounds__(kThreads) void diag_persist_kernel(PersistArgs a)
+{
+    __shared__ DiagLds sh;
+    constexpr int AGG = 2 * kDP;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int bseq = blockIdx.x / a.G, w = blockIdx.x % a.G;
+    const int c0 = w * kNC;
+    const int nch = min(kNC, a.nchunk - c0);             // >= 1
+    const int tb = c0 * kL, te = min(a.T, (c0 + nch) * kL), np = te - tb;
+    const int D = a.D;
+    const size_t seq = static_cast<size_t>(bseq) * a.T;
+    const size_t aggs = static_cast<size_t>(a.B) * a.G * AGG;
+    const size_t slots = static_cast<size_t>(a.B) * a.G;
+    unsigned long long *agg0 = a.agg + static_cast<size_t>(bseq) * a.G * AGG;
+    unsigned long long *slot0 = a.slot + static_cast<size_t>(bseq) * a.G;
+    const unsigned long long *xin = a.xch + (static_cast<size_t>(bseq) * a.G + (w > 0 ? w - 1 : 0)) * kDP;
+    unsigned long long *xout = a.xch + (static_cast<size_t>(bseq) * a.G + w) * kDP;
+    const Linearization lz{a.lin_kind, a.shrink};
+    int best = -1, last_adv = 0;                         // finite-step check (the same in every workgroup)
+
+    const int j = lane & 15, g = lane >> 4;
+    float WE[4], wcc[4];                                 // A operand of the evaluation; W_cc of channel 4 g + u
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int c = 4 * g + u;
+        WE[u] = (j < D && c < D) ? a.W[j * D + c] : 0.0f;
+        wcc[u] = c < D ? a.W[c * D + c] : 0.0f;
+    }
+    const float xs0 = (a.s0 && j < D) ? a.s0[static_cast<size_t>(bseq) * D + j] : 0.0f;
+    const int r0 = wave * kL, n = wave < nch ? min(kL, np - r0) : 0;
+    float pr[4][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int r = min(r0 + 16 * q + j, np - 1);
+            const int c = min(4 * g + v, D - 1);
+            pr[q][v] = a.proj[(seq + tb + r) * D + c];
+        }
+    for (int e = tid; e < (np + 1) * kDP; e += kThreads) {
+        const int r = e / kDP, k = e % kDP;
+        const int t = tb - 1 + r;
+        const int kc = k < D ? k : D - 1;
+        const float *src_p = (t < 0) ? (a.s0 ? a.s0 + static_cast<size_t>(bseq) * D + kc : a.W)
+                                     : a.traj + (seq + t) * D + kc;
+        const float v = *src_p;
+        sh.S[e] = (k < D && (t >= 0 || a.s0)) ? v : 0.0f;
+    }
+    if (tid == 0) sh.abort_now = 0;
+    __syncthreads();
+
+    // evaluation of positions r0 + 16 q + j, channels 4 g .. 4 g + 3 (sv holds
+    // s_{t-1} at exactly those channels): a_t = lin(diag of the Jacobian),
+    // b_t = f_t - a_t s_{t-1}
+    auto eval16 = [&](int q, unsigned &rmax, unsigned &fmin) {
+        const int p = 16 * q + j, r = r0 + p;
+        const bool pv = p < n;
+        const int rr = pv ? r : r0;
+        const v4f sv = *reinterpret_cast<const v4f *>(&sh.S[rr * kDP + 4 * g]);
+        v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(WE[u], sv[u], acc, 0, 0, 0);
+        const v4f nx = *reinterpret_cast<const v4f *>(&sh.S[(rr + 1) * kDP + 4 * g]);
+        v4f av, bv;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int c = 4 * g + v;
+            const float f = tanhf(acc[v] + pr[q][v]);
+            const float al = lin_diag(lz, (1.0f - f * f) * wcc[v]);
+            const bool cv = c < D;
+            av[v] = cv ? al : 0.0f;
+            bv[v] = cv ? f - al * sv[v] : 0.0f;
+            if (cv && pv) {
+                const float ra = fabsf(nx[v] - f);
+                rmax = max(rmax, __float_as_uint(ra));
+                fmin = min(fmin, front_of(ra, a.tol, tb + r));
+            }
+        }
+        if (pv) {
+            *reinterpret_cast<v4f *>(&sh.a[r * kDP + 4 * g]) = av;
+            *reinterpret_cast<v4f *>(&sh.b[r * kDP + 4 * g]) = bv;
+        }
+    };
+
+    for (int i = 0;; ++i) {
+        // ---- 1. evaluation; wavefront 0 takes its first 16 positions last, once
+        // the left neighbour's last state is in
+        unsigned rmax = 0u, fmin = kNoFront;
+        if (wave < nch) {
+            eval16(3, rmax, fmin);
+            eval16(2, rmax, fmin);
+            eval16(1, rmax, fmin);
+            if (wave == 0 && w > 0 && i > 0) {
+                float v = 0.0f;
+                bool ok = lane >= kDP;
+                unsigned spins = 0;
+                int ab = 0;
+                for (;;) {
+                    if (!ok) ok = Words<float>::get(xin + lane, tag32(i - 1), v);
+                    if (__all(ok)) break;
+                    if (poll_step(spins, a.abort_flag)) { ab = 1; break; }
+                }
+                if (lane < kDP) sh.S[lane] = v;
+                if (__builtin_amdgcn_readfirstlane(ab) && lane == 0) sh.abort_now = 1;
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+            }
+            eval16(0, rmax, fmin);
+        }
+        for (int o = 32; o > 0; o >>= 1) rmax = max(rmax, static_cast<unsigned>(__shfl_xor(static_cast<int>(rmax), o, 64)));
+        fmin = wave_min_u32(fmin);
+        if (lane == 0) { sh.red[0][wave] = rmax; sh.red[1][wave] = fmin; }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+
+        // ---- 2. sub-chunk aggregates (lane (j, g): channel j of sub-chunk g;
+        // positions past the chunk are identities), then the chunk aggregate
+        if (wave < nch) {
+            const int ng = min(max(n - kSub * g, 0), kSub);
+            const float *ag = sh.a + (r0 + kSub * g) * kDP + j, *bg = sh.b + (r0 + kSub * g) * kDP + j;
+            float A = 1.0f, Bv = 0.0f;
+#pragma unroll
+            for (int st = 0; st < kSub; ++st) {
+                const float as = ag[st * kDP], bs = bg[st * kDP];   // rows past the chunk stay in the array
+                const float Bn = __builtin_fmaf(as, Bv, bs), An = as * A;
+                Bv = st < ng ? Bn : Bv;
+                A = st < ng ? An : A;
+            }
+            sh.sub[wave][0][g][j] = A;
+            sh.sub[wave][1][g][j] = Bv;
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            if (g == 0) {
+                float Ac = 1.0f, Bc = 0.0f;
+#pragma unroll
+                for (int k = 0; k < kNS; ++k) {
+                    const float Ak = sh.sub[wave][0][k][j], Bk = sh.sub[wave][1][k][j];
+                    Bc = __builtin_fmaf(Ak, Bc, Bk);
+                    Ac = Ak * Ac;
+                }
+                sh.ch[0][wave][j] = Ac;
+                sh.ch[1][wave][j] = Bc;
+            }
+        }
+        __syncthreads();
+        if (sh.abort_now) break;
+        // the workgroup aggregate for the later workgroups
+        unsigned long long *agg = agg0 + (i & 1) * aggs;
+        if (wave == 0 && w + 1 < a.G && lane < kDP) {
+            float Aw = sh.ch[0][0][lane], Bw = sh.ch[1][0][lane];
+            for (int q = 1; q < nch; ++q) {
+                const float Aq = sh.ch[0][q][lane], Bq = sh.ch[1][q][lane];
+                Bw = __builtin_fmaf(Aq, Bw, Bq);
+                Aw = Aq * Aw;
+            }
+            unsigned long long *dst = agg + static_cast<size_t>(w) * AGG;
+            Words<float>::put(dst + lane, Aw, tag32(i));
+            Words<float>::put(dst + kDP + lane, Bw, tag32(i));
+        }
+        if (tid == 0) {
+            unsigned m = sh.red[0][0], f = sh.red[1][0];
+            for (int q = 1; q < kNC; ++q) { m = max(m, sh.red[0][q]); f = min(f, sh.red[1][q]); }
+            __hip_atomic_store(slot0 + (i & 1) * slots + w, slot_word(m, f, 0u, i), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+
+        // ---- group barrier: every workgroup's residual slot of this iteration
+        if (wave == 0) {
+            unsigned long long v = 0;
+            bool ok = lane >= a.G;
+            unsigned spins = 0;
+            int ab = 0;
+            for (;;) {
+                if (!ok) {
+                    v = get_word(slot0 + (i & 1) * slots + lane);
+                    ok = (static_cast<unsigned>(v >> 32) & 0xFFFFu) == tag16(i);
+                }
+                if (__all(ok)) break;
+                if (poll_step(spins, a.abort_flag)) { ab = 1; break; }
+            }
+            unsigned m = lane < a.G ? static_cast<unsigned>(v) : 0u;
+            unsigned f = lane < a.G ? static_cast<unsigned>(v >> 48) & 0x7FFFu : 0x7FFFu;
+            for (int o = 32; o > 0; o >>= 1) {
+                m = max(m, static_cast<unsigned>(__shfl_xor(static_cast<int>(m), o, 64)));
+                f = min(f, static_cast<unsigned>(__shfl_xor(static_cast<int>(f), o, 64)));
+            }
+            if (lane == 0) {
+                sh.dec_r = m;
+                sh.dec_f = f == 0x7FFFu ? kNoFront : f;
+                sh.abort_now = __builtin_amdgcn_readfirstlane(ab);
+            }
+        }
+        __syncthreads();
+        if (sh.abort_now) break;
+
+        // ---- 3. the stopping decision
+        const float r = __uint_as_float(sh.dec_r);
+        int stop = -1;
+        if (r <= a.tol) {
+            stop = DEER_SEQ_CONVERGED;
+        } else if (i >= a.max_iter) {
+            stop = __builtin_isfinite(r) ? DEER_SEQ_NOT_CONVERGED : DEER_SEQ_NONFINITE;
+        } else if (a.stall_window > 0) {
+            const unsigned fr = sh.dec_f;
+            const int f = fr > 0x7FFFFFFFu ? 0x7FFFFFFF : static_cast<int>(fr);
+            if (f > best) {
+                best = f;
+                last_adv = i;
+            } else if (best < i && i - last_adv >= a.stall_window) {
+                stop = DEER_SEQ_STALLED;
+            }
+        }
+        if (stop >= 0) {
+            for (int e = tid; e < np * kDP; e += kThreads) {
+                const int k = e % kDP;
+                if (k < D) a.traj[(seq + tb + e / kDP) * D + k] = sh.S[kDP + e];
+            }
+            if (w == 0 && tid == 0) {
+                a.iters[bseq] = i;
+                a.status[bseq] = stop;
+                a.resid[bseq] = r;
+            }
+            break;
+        }
+
+        // ---- 4. the earlier workgroups' aggregates (one value per thread, the
+        // stale ones read again), then the states entering the chunks
+        {
+            static_assert((kMaxGroup - 1) * AGG <= kThreads, "one staged value per thread");
+            const unsigned t = tag32(i);
+            bool need = tid < w * AGG;
+            unsigned spins = 0;
+            for (;;) {
+                if (need) {
+                    float v;
+                    if (Words<float>::get(agg + tid, t, v)) {
+                        sh.Wg[tid] = v;
+                        need = false;
+                    }
+                }
+                if (!__syncthreads_or(need)) break;
+                if (__syncthreads_or(poll_step(spins, a.abort_flag))) {
+                    if (tid == 0) sh.abort_now = 1;
+                    break;
+                }
+            }
+        }
+        __syncthreads();
+        if (wave == 0 && lane < kDP) {
+            float x = xs0;
+            for (int v = 0; v < w; ++v) x = __builtin_fmaf(sh.Wg[v * AGG + lane], x, sh.Wg[v * AGG + kDP + lane]);
+            for (int q = 0; q < nch; ++q) {
+                sh.ent[q][lane] = x;
+                x = __builtin_fmaf(sh.ch[0][q][lane], x, sh.ch[1][q][lane]);
+            }
+        }
+        __syncthreads();
+        if (sh.abort_now) break;
+
+        // ---- 5. replay: lane (j, g) runs channel j of sub-chunk g from its entry
+        // (the chunk's entry through the earlier sub-chunks) into the state rows;
+        // the range's last state also goes to the right neighbour
+        if (wave < nch) {
+            const int ng = min(max(n - kSub * g, 0), kSub);
+            const int K = (n + kSub - 1) / kSub;
+            float x = sh.ent[wave][j];
+#pragma unroll
+            for (int k = 0; k + 1 < kNS; ++k)
+                if (k < g) x = __builtin_fmaf(sh.sub[wave][0][k][j], x, sh.sub[wave][1][k][j]);
+            const float *ag = sh.a + (r0 + kSub * g) * kDP + j, *bg = sh.b + (r0 + kSub * g) * kDP + j;
+            float *Sg = sh.S + (r0 + kSub * g + 1) * kDP + j;
+#pragma unroll
+            for (int st = 0; st < kSub; ++st) {
+                const float xn = __builtin_fmaf(ag[st * kDP], x, bg[st * kDP]);
+                if (st < ng) {
+                    x = xn;
+                    Sg[st * kDP] = xn;
+                }
+            }
+            if (wave == nch - 1 && w + 1 < a.G && g == K - 1) Words<float>::put(xout + j, x, tag32(i));
+        }
+        __syncthreads();
+    }
+}
+
 // Zeroes the tagged-word buffers of a launch (zero is never an expected tag)
 // and, unless the launch resumes another one, the abort word.
 __global__ void persist_init_kernel(unsigned long long *words, size_t n, unsigned *esc_flag, unsigned *abort_flag)
@@ -793,23 +1105,32 @@ int launch_persist(const PersistArgs &a, hipStream_t stream)
     return DEER_OK;
 }
 
-// Workgroups of dense_persist_kernel<ACC> resident at once on the current
-// device (compute units times workgroups per unit), cached per device.
-template <class ACC>
-int persist_capacity()
+// Workgroups of `kernel` (kThreads threads each) resident at once on the
+// current device (compute units times workgroups per unit), cached per device
+// in `cache`.
+template <class F>
+int capacity_of(F kernel, int (&cache)[64])
 {
-    static int cache[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
     if (cache[dev] == 0) {
         int cus = 0, per_cu = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, dense_persist_kernel<ACC>, kThreads, 0) !=
-                hipSuccess)
-            per_cu = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess) per_cu = 0;
         cache[dev] = cus * per_cu > 0 ? cus * per_cu : -1;
     }
     return cache[dev];
+}
+template <class ACC>
+int persist_capacity()
+{
+    static int cache[64] = {};
+    return capacity_of(dense_persist_kernel<ACC>, cache);
+}
+int diag_persist_capacity()
+{
+    static int cache[64] = {};
+    return capacity_of(diag_persist_kernel, cache);
 }
 
 int groups_of(int T) { return (T + kNC * kL - 1) / (kNC * kL); }
@@ -820,6 +1141,8 @@ bool persist_resident(int B, int T, bool f64)
     const int cap = f64 ? persist_capacity<double>() : persist_capacity<float>();
     return cap > 0 && static_cast<long long>(B) * groups_of(T) <= cap;
 }
+
+bool persist_shape(int B, int D, int T) { return D >= 1 && D <= kDP && T >= 1 && T <= kNC * kL * kMaxGroup && B >= 1; }
 
 // Layout of the state: the tagged words (residual slots, aggregates sized for
 // double when a double-precision launch may run, exchange rows) in one block,
@@ -845,9 +1168,13 @@ PersistState persist_state(int B, int T, bool f64)
 
 }  // namespace
 
-bool dense_persist_fits(int B, int D, int T, bool f64)
+bool dense_persist_fits(int B, int D, int T, bool f64) { return persist_shape(B, D, T) && persist_resident(B, T, f64); }
+
+bool diag_persist_fits(int B, int D, int T)
 {
-    return D >= 1 && D <= kDP && T >= 1 && T <= kNC * kL * kMaxGroup && B >= 1 && persist_resident(B, T, f64);
+    if (!persist_shape(B, D, T)) return false;
+    const int cap = diag_persist_capacity();
+    return cap > 0 && static_cast<long long>(B) * groups_of(T) <= cap;
 }
 
 size_t dense_persist_state_bytes(int B, int T, bool f64) { return persist_state(B, T, f64).bytes; }
@@ -891,6 +1218,40 @@ int launch_dense_persist(const float *W, const float *proj, const float *s0, flo
                 resume ? nullptr : a.abort_flag);
     DEER_HIP(hipGetLastError());
     return f64 ? launch_persist<double>(a, stream) : launch_persist<float>(a, stream);
+}
+
+int launch_diag_persist(const float *W, const float *proj, const float *s0, float *traj, int B, int T, int D,
+                        Linearization lz, float tol, int max_iter, int stall_window, int *iters, int *status,
+                        float *resid, void *state, hipStream_t stream)
+{
+    if (B == 0) return DEER_OK;
+    if (lz.kind != kLinJacobian && lz.kind != kLinZero && lz.kind != kLinIdentity)
+        return fail(DEER_ERR_INVALID, "persistent diagonal solve: not a linearisation");
+    if (!diag_persist_fits(B, D, T))
+        return fail(DEER_ERR_UNSUPPORTED, "persistent diagonal solve: problem does not fit the device at once");
+    PersistArgs a{};
+    a.W = W; a.proj = proj; a.s0 = s0; a.traj = traj;
+    a.B = B; a.T = T; a.D = D;
+    a.nchunk = (T + kL - 1) / kL;
+    a.G = groups_of(T);
+    a.max_iter = max_iter; a.stall_window = stall_window; a.tol = tol; a.shrink = lz.shrink;
+    a.lin_kind = lz.kind;
+    a.iters = iters; a.status = status; a.resid = resid;
+    const PersistState ps = persist_state(B, T, false);
+    char *st = static_cast<char *>(state);
+    a.slot = reinterpret_cast<unsigned long long *>(st + ps.slot);
+    a.agg = reinterpret_cast<unsigned long long *>(st + ps.agg);
+    a.xch = reinterpret_cast<unsigned long long *>(st + ps.xch);
+    a.keep = reinterpret_cast<int *>(st + ps.keep);
+    a.esc_flag = reinterpret_cast<unsigned *>(st + ps.esc_off);
+    a.abort_flag = reinterpret_cast<unsigned *>(st + ps.abort_off);
+    const size_t nwords = ps.words_end / sizeof(unsigned long long);
+    DEER_LAUNCH(persist_init_kernel, dim3(static_cast<unsigned>(std::min<size_t>((nwords + 255) / 256, 2048))),
+                dim3(256), 0, stream, reinterpret_cast<unsigned long long *>(st), nwords, a.esc_flag, a.abort_flag);
+    DEER_HIP(hipGetLastError());
+    DEER_LAUNCH(diag_persist_kernel, dim3(static_cast<unsigned>(B) * a.G), dim3(kThreads), 0, stream, a);
+    DEER_HIP(hipGetLastError());
+    return DEER_OK;
 }
 
 }  // namespace deer

@@ -525,6 +525,13 @@ int launch_dense_persist(const float *W, const float *proj, const float *s0, flo
 // Set (non-zero) when a bounded wait of the launches since the last
 // non-resumed one hit its bound.
 unsigned *dense_persist_abort_word(void *state, int B, int T, bool state_f64);
+// The diagonal linearisations (quasi-Newton, Jacobi, Picard) of the same
+// problems in one launch, with the same groups and the same state
+// (dense_persist_state_bytes(B, T, false), abort word included); no hand-over.
+bool diag_persist_fits(int B, int D, int T);
+int launch_diag_persist(const float *W, const float *proj, const float *s0, float *traj, int B, int T, int D,
+                        Linearization lz, float tol, int max_iter, int stall_window, int *iters, int *status,
+                        float *resid, void *state, hipStream_t stream);
 
 // Parallel Broyden (broyden.hip): the block updates and the chunked compressed
 // scan of delta_t = A_t delta_{t-1} + c_t, A_t = alpha I + shrink U_t V_t^T.

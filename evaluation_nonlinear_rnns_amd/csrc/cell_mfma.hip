@@ -19,6 +19,7 @@
 // Positions are staged in LDS with a row stride of K + 2 words, which makes the
 // A-operand reads (32 rows x 2 columns per instruction) bank-conflict free.
 #include <algorithm>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -93,9 +94,8 @@ struct GruTile {
 // Tile coordinates (sequence bseq, first position t0) are passed in: the tile
 // loops track them incrementally, which keeps 64-bit divisions out of the loop.
 template <int D>
-__device__ __forceinline__ void gru_fetch(const float *__restrict__ s, const float *__restrict__ s0,
-                                          const float *__restrict__ pt, int T, int tps32, int bseq, int t0,
-                                          int ps, int hf, int c, v4f (&hv)[GruTile<D>::NH], v4f (&pv)[3][4])
+__device__ __forceinline__ void gru_fetch_rows(const float *__restrict__ s, const float *__restrict__ s0, int T,
+                                               int bseq, int t0, v4f (&hv)[GruTile<D>::NH])
 {
     using G = GruGeom<D>;
     const int tid = threadIdx.x;
@@ -115,13 +115,33 @@ __device__ __forceinline__ void gru_fetch(const float *__restrict__ s, const flo
         }
         hv[i] = v;
     }
-    // tiled projection: 32-position block, gate g, quad q, half hf, channel c, 4 positions
+}
+
+// Tiled projection of the lane's 16 positions: 32-position block, gate g,
+// quad q, half hf, channel c, 4 positions per 16-byte access (load u = 4 g + q).
+template <int D>
+__device__ __forceinline__ const v4f *gru_proj_base(const float *__restrict__ pt, int tps32, int bseq, int t0, int ps)
+{
     const size_t blk = static_cast<size_t>(bseq) * tps32 + (t0 >> 5) + ps;
-    const v4f *base = reinterpret_cast<const v4f *>(pt + blk * (96 * static_cast<size_t>(D)));
+    return reinterpret_cast<const v4f *>(pt + blk * (96 * static_cast<size_t>(D)));
+}
+template <int D>
+__device__ __forceinline__ v4f gru_proj_load(const v4f *base, int u, int hf, int c)
+{
+    return __builtin_nontemporal_load(base + (u * 2 + hf) * D + c);
+}
+
+template <int D>
+__device__ __forceinline__ void gru_fetch(const float *__restrict__ s, const float *__restrict__ s0,
+                                          const float *__restrict__ pt, int T, int tps32, int bseq, int t0,
+                                          int ps, int hf, int c, v4f (&hv)[GruTile<D>::NH], v4f (&pv)[3][4])
+{
+    gru_fetch_rows<D>(s, s0, T, bseq, t0, hv);
+    const v4f *base = gru_proj_base<D>(pt, tps32, bseq, t0, ps);
 #pragma unroll
     for (int g = 0; g < 3; ++g)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) pv[g][q] = __builtin_nontemporal_load(base + ((g * 4 + q) * 2 + hf) * D + c);
+        for (int q = 0; q < 4; ++q) pv[g][q] = gru_proj_load<D>(base, 4 * g + q, hf, c);
 }
 
 template <int D>
@@ -336,23 +356,87 @@ __global__ __launch_bounds__(kThreads, 2) void gru_quasi_step_kernel(
         for (int g = 0; g < 3; ++g)
 #pragma unroll
             for (int q = 0; q < 4; ++q) pc[g][q] = pv[g][q];
-        if (nt < tiles_per_seq) gru_fetch<D>(s, s0, pt, T, tps32, nb, nt * G::TP, ps, hf, c, hv, pv);
+        if (nt < tiles_per_seq) gru_fetch_rows<D>(s, s0, T, nb, nt * G::TP, hv);
         if (!live) {
+            if (nt < tiles_per_seq) {
+                const v4f *nbase = gru_proj_base<D>(pt, tps32, nb, nt * G::TP, ps);
+#pragma unroll
+                for (int u = 0; u < 12; ++u) pv[u / 4][u % 4] = gru_proj_load<D>(nbase, u, hf, c);
+            }
+            // a skipped tile waits for its loads here, so that the live path never
+            // enters with loads pending into registers it reuses (which would put
+            // waits for them into its MFMA phase)
+#pragma unroll
+            for (int g = 0; g < 3; ++g)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) asm volatile("" ::"v"(pv[g][q]));
+#pragma unroll
+            for (int i = 0; i < GruTile<D>::NH; ++i) asm volatile("" ::"v"(hv[i]));
             bseq = nb;
             tt = nt;
             continue;
         }
 
+        // W_hh s on the matrix cores, one pair of k-steps (6 MFMAs) per fenced
+        // segment, with the pair's LDS operands read one segment ahead and the
+        // next tile's 12 projection loads spread over the segments: spreading
+        // them lets the memory stream run under the MFMA phase instead of
+        // arriving as one burst per tile.  The workgroup's last tile runs the
+        // same segments without loads.
         v16f accR = {}, accZ = {}, accN = {};
         const float *arow = H + (ps * 32 + r32) * G::LDH + hf;
         const float *wrow = Ws + c * G::LDH + hf;
+        auto mfma_phase = [&](auto prefetch) {
+            constexpr int NPAIR = G::KK / 2;
+            const v4f *nbase = gru_proj_base<D>(pt, tps32, nb, nt * G::TP, ps);
+            float oa[2], orr[2], oz[2], on[2];
 #pragma unroll
-        for (int kk = 0; kk < G::KK; ++kk) {
-            const float av = arow[2 * kk];
-            accR = __builtin_amdgcn_mfma_f32_32x32x2f32(av, wrow[2 * kk], accR, 0, 0, 0);
-            accZ = __builtin_amdgcn_mfma_f32_32x32x2f32(av, wrow[D * G::LDH + 2 * kk], accZ, 0, 0, 0);
-            accN = __builtin_amdgcn_mfma_f32_32x32x2f32(av, wrow[2 * D * G::LDH + 2 * kk], accN, 0, 0, 0);
-        }
+            for (int h = 0; h < 2; ++h) {
+                oa[h] = arow[2 * h];
+                orr[h] = wrow[2 * h];
+                oz[h] = wrow[D * G::LDH + 2 * h];
+                on[h] = wrow[2 * D * G::LDH + 2 * h];
+            }
+#pragma unroll
+            for (int kp = 0; kp < NPAIR; ++kp) {
+                float na[2], nr[2], nz[2], nn[2];
+                if (kp + 1 < NPAIR) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int k2 = 2 * (2 * (kp + 1) + h);
+                        na[h] = arow[k2];
+                        nr[h] = wrow[k2];
+                        nz[h] = wrow[D * G::LDH + k2];
+                        nn[h] = wrow[2 * D * G::LDH + k2];
+                    }
+                }
+                if (decltype(prefetch)::value) {
+#pragma unroll
+                    for (int u = kp * 12 / NPAIR; u < (kp + 1) * 12 / NPAIR; ++u)
+                        pv[u / 4][u % 4] = gru_proj_load<D>(nbase, u, hf, c);
+                }
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    accR = __builtin_amdgcn_mfma_f32_32x32x2f32(oa[h], orr[h], accR, 0, 0, 0);
+                    accZ = __builtin_amdgcn_mfma_f32_32x32x2f32(oa[h], oz[h], accZ, 0, 0, 0);
+                    accN = __builtin_amdgcn_mfma_f32_32x32x2f32(oa[h], on[h], accN, 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (kp + 1 < NPAIR) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        oa[h] = na[h];
+                        orr[h] = nr[h];
+                        oz[h] = nz[h];
+                        on[h] = nn[h];
+                    }
+                }
+            }
+        };
+        if (nt < tiles_per_seq)
+            mfma_phase(std::true_type{});
+        else
+            mfma_phase(std::false_type{});
 
         // gates, Jacobian diagonal and offsets at the lane's 16 positions
         const bool full = t0 + ps * 32 + 32 <= T;

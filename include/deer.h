@@ -197,10 +197,12 @@ int deer_workspace_init(void *workspace, size_t ws_bytes, void *stream);
  *
  * The diagonal-block modes and the GRU's fused iteration run a single-pass
  * scan whose tiles wait on earlier tiles (a decoupled look-back over a
- * persistent grid sized to the device's resident capacity).  That assumes the
- * whole grid is resident at once: another kernel occupying compute units on a
- * concurrent stream can delay it; the wait is bounded, and if the bound is hit
- * the call returns DEER_ERR_DEVICE.
+ * persistent grid sized to the device's resident capacity), and tanh problems
+ * with D <= 16 and T <= 8192 whose grid the device holds at once run the whole
+ * solve in one launch whose workgroups wait on each other once per iteration.
+ * Both assume the whole grid is resident at once: another kernel occupying
+ * compute units on a concurrent stream can delay it; the waits are bounded,
+ * and if a bound is hit the call returns DEER_ERR_DEVICE.
  */
 int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int B, int T, int mode, float tol,
                int max_iter, const deer_solve_opts_t *opts, const float *init_guess, float *traj_out,

@@ -503,6 +503,227 @@ __global__ __launch_bounds__(64) void dense_carry_kernel(
         if (nfull + u < nchunk) advance(nfull + u, ring[u], bring[u]);
 }
 
+// ------------------------------------------------------- two-level carry walk
+// Float D = 32 with many chunks: a sequence's chunks form kTlGroups
+// consecutive groups.
+//   1. dense_group_tl32_kernel, one workgroup per group: the product P_g of
+//      the group's chunk products on the matrix cores (the running product
+//      stays in the accumulators, as in the compose kernel: P <- P_c P with P_c
+//      as the A operands; wavefront 0) and the group offset B_g by the
+//      matrix-vector chain B <- P_c B + B_c (wavefront 1);
+//   2. dense_carry_tl32_kernel, one workgroup per sequence: wavefront 0 walks
+//      the groups from s0 (the state entering each group), then every
+//      wavefront walks one group's chunks from that state and writes the chunk
+//      carries.
+// The serial chain shrinks from nchunk steps to kTlGroups + nchunk / kTlGroups,
+// and the group products (one D^3 product per chunk, 1/64 of the compose
+// work) run over the whole device.  Pairs of affine maps merge as in the rest
+// of the scan (the later on the left); any grouping gives the same result
+// under exact composition ("Parallel Broyden Methods", appendix B.4), so only
+// rounding differs from the one-level walk.  A group product out of range
+// (non-finite, or above kTlLimit in magnitude: strongly expanding dynamics,
+// where P_g x + B_g would cancel huge terms or overflow) makes its sequence
+// take the one-level walk instead, on wavefront 0.
+constexpr int kTlGroups = 16;
+constexpr int kTlPF = 4;                 // chunks fetched ahead by each walk
+constexpr float kTlLimit = 1e18f;
+constexpr int kTlMinChunks = 32;         // fewer chunks: the one-level walk is short already
+
+__host__ __device__ __forceinline__ int tl_group_size(int nchunk) { return (nchunk + kTlGroups - 1) / kTlGroups; }
+bool tl_carry_shape(int D, int nchunk) { return D == 32 && nchunk >= kTlMinChunks; }
+
+struct TlChunk {
+    v4f a[4];                            // row i of the matrix, columns 8 u + 4 hf .. + 3 (A operand layout)
+    float b;                             // offset entry i
+};
+
+// Matrix q of a [.][32][32] array and its offset, clamped to index < qend:
+// refills past the end load a valid entry that is never used.
+__device__ __forceinline__ void tl_fetch(const float *__restrict__ P, const float *__restrict__ Bv, size_t q,
+                                         size_t qend, int i, int hf, TlChunk &k)
+{
+    const size_t qq = q < qend ? q : qend - 1;
+    const float *row = P + (qq * 32 + i) * 32 + 4 * hf;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) k.a[u] = *reinterpret_cast<const v4f *>(row + 8 * u);
+    k.b = Bv[qq * 32 + i];
+}
+
+// x <- M x + b for the state held in `line` (LDS, 32 floats); every lane
+// returns entry i, and the line holds the new state on return.
+__device__ __forceinline__ float tl_advance(const TlChunk &k, float *line, int i, int hf)
+{
+    float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const v4f xv = *reinterpret_cast<const v4f *>(line + 8 * u + 4 * hf);
+        a0 = __builtin_fmaf(k.a[u][0], xv[0], a0);
+        a1 = __builtin_fmaf(k.a[u][1], xv[1], a1);
+        a0 = __builtin_fmaf(k.a[u][2], xv[2], a0);
+        a1 = __builtin_fmaf(k.a[u][3], xv[3], a1);
+    }
+    float y = a0 + a1;
+    y += __shfl_xor(y, 32, 64);
+    const float x = y + k.b;
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    if (hf == 0) line[i] = x;
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    return x;
+}
+
+__device__ __forceinline__ void tl_set_line(float *line, float x, int i, int hf)
+{
+    if (hf == 0) line[i] = x;
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Walk matrices [cb, ce) of (P, Bv) from the state x, calling at(c, x) with
+// the state before each; whole rounds of kTlPF run as straight-line bodies (a
+// branch inside a round would make the compiler wait for every load in flight).
+template <int PF, class At>
+__device__ __forceinline__ float tl_walk(const float *__restrict__ P, const float *__restrict__ Bv, size_t cb,
+                                         size_t ce, float x, float *line, int i, int hf, At &&at)
+{
+    tl_set_line(line, x, i, hf);
+    TlChunk ring[PF];
+#pragma unroll
+    for (int u = 0; u < PF; ++u) tl_fetch(P, Bv, cb + u, ce, i, hf, ring[u]);
+    const size_t n = ce - cb, nfull = cb + n - n % PF;
+    for (size_t c0 = cb; c0 < nfull; c0 += PF) {
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+            at(c0 + u, x);
+            x = tl_advance(ring[u], line, i, hf);
+            tl_fetch(P, Bv, c0 + u + PF, ce, i, hf, ring[u]);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+        if (nfull + u < ce) {
+            at(nfull + u, x);
+            x = tl_advance(ring[u], line, i, hf);
+        }
+    }
+    return x;
+}
+
+// Group products and offsets: one 128-thread workgroup per (sequence, group).
+// Writes Pg [B][kTlGroups][32][32] (row-major) and Bg [B][kTlGroups][32];
+// groups past the last chunk are left alone.
+__global__ __launch_bounds__(128) void dense_group_tl32_kernel(
+    const float *__restrict__ Pagg, const float *__restrict__ Bagg, const int *__restrict__ skip,
+    const int *__restrict__ all_done, int nchunk, float *__restrict__ Pg, float *__restrict__ Bg)
+{
+    constexpr int D = 32;
+    if (all_done && *all_done) return;
+    const int bseq = blockIdx.x / kTlGroups, g = blockIdx.x % kTlGroups;
+    if (skip && skip[bseq]) return;
+    const int GS = tl_group_size(nchunk);
+    const int cb = g * GS, ce = min(nchunk, cb + GS);
+    if (cb >= ce) return;
+    __shared__ __align__(16) float line[D];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int i = lane & 31, hf = lane >> 5;
+    const size_t q0 = static_cast<size_t>(bseq) * nchunk;
+    const size_t qg = static_cast<size_t>(bseq) * kTlGroups + g;
+    if (wave == 1) {
+        // the offset: the state the group's chunks reach from a zero start
+        const float x = tl_walk<kTlPF>(Pagg, Bagg, q0 + cb + 1, q0 + ce, Bagg[(q0 + cb) * D + i], line, i, hf,
+                                       [](size_t, float) {});
+        if (hf == 0) Bg[qg * D + i] = x;
+        return;
+    }
+    // the product, accumulators in the B operand layout: register v holds P[row32(v, hf)][i]
+    const float *Pf = Pagg + (q0 + cb) * D * D;
+    v16f P;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) P[v] = Pf[row32(v, hf) * D + i];
+    TlChunk ring[kTlPF];
+#pragma unroll
+    for (int u = 0; u < kTlPF; ++u) tl_fetch(Pagg, Bagg, q0 + cb + 1 + u, q0 + ce, i, hf, ring[u]);
+    auto compose = [&](const TlChunk &k) {
+        v16f acc = {};
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(k.a[v >> 2][v & 3], P[v], acc, 0, 0, 0);
+        P = acc;
+    };
+    const int n = ce - cb - 1, nfull = cb + 1 + n - n % kTlPF;
+    for (int c0 = cb + 1; c0 < nfull; c0 += kTlPF) {
+#pragma unroll
+        for (int u = 0; u < kTlPF; ++u) {
+            compose(ring[u]);
+            tl_fetch(Pagg, Bagg, q0 + c0 + u + kTlPF, q0 + ce, i, hf, ring[u]);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kTlPF; ++u)
+        if (nfull + u < ce) compose(ring[u]);
+    float *po = Pg + qg * D * D;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) po[row32(v, hf) * D + i] = P[v];
+}
+
+// Carries from the group products: one workgroup of kTlWalkers wavefronts per
+// sequence, each walking kTlGroups / kTlWalkers consecutive groups; with two
+// wavefronts per SIMD the walks keep kTlWalkPF chunks of loads in flight.
+constexpr int kTlWalkers = 8;
+constexpr int kTlWalkPF = 10;
+__global__ __launch_bounds__(64 * kTlWalkers) void dense_carry_tl32_kernel(
+    const float *__restrict__ Pagg, const float *__restrict__ Bagg, const float *__restrict__ Pg,
+    const float *__restrict__ Bg, const float *__restrict__ s0, const int *__restrict__ skip,
+    const int *__restrict__ all_done, int B, int nchunk, float *__restrict__ carry)
+{
+    constexpr int D = 32, GPW = kTlGroups / kTlWalkers;
+    if (all_done && *all_done) return;
+    const int bseq = blockIdx.x;
+    if (bseq >= B || (skip && skip[bseq])) return;      // uniform per workgroup
+    __shared__ float gent[kTlWalkers][D];               // states entering each walker's first group
+    __shared__ __align__(16) float xl[kTlWalkers][D];   // per-wavefront state line
+    __shared__ int bad;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int i = lane & 31, hf = lane >> 5;
+    const int GS = tl_group_size(nchunk);
+    const int ngroups = (nchunk + GS - 1) / GS;
+    const size_t q0 = static_cast<size_t>(bseq) * nchunk;
+    const size_t g0 = static_cast<size_t>(bseq) * kTlGroups;
+    float *line = xl[wave];
+    const float x0 = s0 ? s0[static_cast<size_t>(bseq) * D + i] : 0.0f;
+    auto write_carry = [&](size_t q, float x) {
+        if (hf == 0) carry[q * D + i] = x;
+    };
+
+    // group products in range?
+    if (tid == 0) bad = 0;
+    __syncthreads();
+    bool out_of_range = false;
+    for (int g = wave; g < ngroups; g += kTlWalkers) {
+        const float *pg = Pg + (g0 + g) * D * D;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) out_of_range |= !(__builtin_fabsf(pg[u * 64 + lane]) <= kTlLimit);
+    }
+    if (__any(out_of_range) && lane == 0) bad = 1;
+    __syncthreads();
+    if (bad) {
+        if (wave == 0) tl_walk<kTlWalkPF>(Pagg, Bagg, q0, q0 + nchunk, x0, line, i, hf, write_carry);
+        return;
+    }
+
+    // the states entering the groups (kept for each walker's first group)
+    if (wave == 0)
+        tl_walk<kTlWalkPF>(Pg, Bg, g0, g0 + ngroups, x0, line, i, hf, [&](size_t q, float x) {
+            const int g = static_cast<int>(q - g0);
+            if (hf == 0 && g % GPW == 0) gent[g / GPW][i] = x;
+        });
+    __syncthreads();
+
+    // every walker's groups from the state entering the first of them
+    const int cb = wave * GPW * GS, ce = min(nchunk, cb + GPW * GS);
+    if (cb < ce) tl_walk<kTlWalkPF>(Pagg, Bagg, q0 + cb, q0 + ce, gent[wave][i], line, i, hf, write_carry);
+}
+
 // ----------------------------------------------------------------- replay
 // Stage a chunk's d_t and b_t rows ([n][D] each, contiguous at base) into LDS
 // with one wavefront, every load of a round in flight at once.
@@ -742,7 +963,7 @@ int pick_dp(int D) { return D <= 4 ? 4 : D <= 8 ? 8 : D <= 16 ? 16 : D <= 32 ? 3
 template <int DP, class ACC>
 int launch_dense_dp(const float *A, const float *d, const float *W, const float *b, const float *s0, float *out0,
                     float *out1, const int *out_sel, const int *skip, const int *all_done, const DenseScanPlan &pl,
-                    ACC *Pagg, ACC *Bagg, ACC *carry, hipStream_t stream)
+                    ACC *Pagg, ACC *Bagg, ACC *carry, float *Pgrp, float *Bgrp, hipStream_t stream)
 {
     constexpr int G = 64 / DP;
     const long long nq = static_cast<long long>(pl.B) * pl.nchunk;
@@ -765,7 +986,14 @@ int launch_dense_dp(const float *A, const float *d, const float *W, const float 
     }
     DEER_HIP(hipGetLastError());
     constexpr bool kVecOk = CarryGeom<DP, ACC>::KG % CarryGeom<DP, ACC>::VEC == 0;
-    if (kVecOk && pl.D == DP)
+    if (DP == 32 && pl.D == 32 && !f64 && pl.nchunk >= kTlMinChunks) {
+        const float *Pf = reinterpret_cast<const float *>(Pagg), *Bf = reinterpret_cast<const float *>(Bagg);
+        DEER_LAUNCH(dense_group_tl32_kernel, dim3(static_cast<unsigned>(pl.B) * kTlGroups), dim3(128), 0, stream, Pf,
+                    Bf, skip, all_done, pl.nchunk, Pgrp, Bgrp);
+        DEER_HIP(hipGetLastError());
+        DEER_LAUNCH(dense_carry_tl32_kernel, dim3(static_cast<unsigned>(pl.B)), dim3(64 * kTlWalkers), 0, stream, Pf,
+                    Bf, Pgrp, Bgrp, s0, skip, all_done, pl.B, pl.nchunk, reinterpret_cast<float *>(carry));
+    } else if (kVecOk && pl.D == DP)
         DEER_LAUNCH((dense_carry_kernel<DP, ACC, kVecOk>), dim3(static_cast<unsigned>(pl.B)), dim3(64), 0, stream,
                            Pagg, Bagg, s0, skip, all_done, pl.B, pl.D, pl.nchunk, carry);
     else
@@ -805,12 +1033,17 @@ int launch_dense_acc(const float *A, const float *d, const float *W, const float
     ACC *Pagg = cv.take<ACC>(nq * D * D);
     ACC *Bagg = cv.take<ACC>(nq * D);
     ACC *carry = cv.take<ACC>(nq * D);
+    float *Pgrp = nullptr, *Bgrp = nullptr;             // two-level carry (float, D = 32, many chunks)
+    if (tl_carry_shape(D, pl.nchunk)) {
+        Pgrp = cv.take<float>(static_cast<size_t>(pl.B) * kTlGroups * D * D);
+        Bgrp = cv.take<float>(static_cast<size_t>(pl.B) * kTlGroups * D);
+    }
     switch (pick_dp(D)) {
-    case 4: return launch_dense_dp<4, ACC>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, Pagg, Bagg, carry, stream);
-    case 8: return launch_dense_dp<8, ACC>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, Pagg, Bagg, carry, stream);
-    case 16: return launch_dense_dp<16, ACC>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, Pagg, Bagg, carry, stream);
-    case 32: return launch_dense_dp<32, ACC>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, Pagg, Bagg, carry, stream);
-    default: return launch_dense_dp<64, ACC>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, Pagg, Bagg, carry, stream);
+    case 4: return launch_dense_dp<4, ACC>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, Pagg, Bagg, carry, Pgrp, Bgrp, stream);
+    case 8: return launch_dense_dp<8, ACC>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, Pagg, Bagg, carry, Pgrp, Bgrp, stream);
+    case 16: return launch_dense_dp<16, ACC>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, Pagg, Bagg, carry, Pgrp, Bgrp, stream);
+    case 32: return launch_dense_dp<32, ACC>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, Pagg, Bagg, carry, Pgrp, Bgrp, stream);
+    default: return launch_dense_dp<64, ACC>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, Pagg, Bagg, carry, Pgrp, Bgrp, stream);
     }
 }
 
@@ -838,7 +1071,11 @@ size_t dense_scan_state_bytes(int B, int T, int D, bool f64)
     const DenseScanPlan p = dense_scan_plan(B, T, D);
     const size_t nq = static_cast<size_t>(B) * p.nchunk;
     const size_t w = f64 ? sizeof(double) : sizeof(float);
-    return align_up(nq * D * D * w) + 2 * align_up(nq * D * w);
+    size_t bytes = align_up(nq * D * D * w) + 2 * align_up(nq * D * w);
+    if (tl_carry_shape(D, p.nchunk))
+        bytes += align_up(static_cast<size_t>(B) * kTlGroups * D * D * sizeof(float)) +
+                 align_up(static_cast<size_t>(B) * kTlGroups * D * sizeof(float));
+    return bytes;
 }
 
 int launch_dense_scan(const float *A, const float *d, const float *W, const float *b, const float *s0, float *out0,

@@ -78,8 +78,11 @@ def test_linear_scan_diag_full_size_every_channel(orc):
 
 
 @pytest.mark.parametrize("B,T,D", [(1, 1, 4), (2, 100, 3), (2, 300, 16), (1, 257, 32), (2, 70, 64), (3, 1500, 4),
-                                   (1, 1000, 32)])
+                                   (1, 1000, 32), (2, 2048, 32), (1, 2113, 32), (1, 5000, 32), (2, 2047, 32)])
 def test_linear_scan_dense_matches_sequential_solve(orc, B, T, D):
+    """Includes D = 32 with 32 chunks or more (the two-level carry: 16 groups
+    of 2, 12 groups of 3 with a last group of one chunk, 16 groups of 5 with a
+    last group of 4) and 31 chunks (the one-level walk)."""
     dev = device()
     p = I.dense_scan_problem(400 + T + D, B, T, D, scale=0.9)
     log(f"linear_scan_dense B={B} T={T} D={D}")
@@ -91,6 +94,30 @@ def test_linear_scan_dense_matches_sequential_solve(orc, B, T, D):
     ref = orc.solve_dense(p["A"], p["b"], p["s0"])
     err = rel_linf(s.cpu().numpy(), ref)
     assert np.all(err <= TOL), err
+
+
+def test_linear_scan_dense_expanding_products_take_the_one_level_walk(orc):
+    """Sequence 1 has expanding blocks (spectral radius about 3), b = 0 and
+    s0 = 0: its exact solution is zero, but its group products (128 steps and
+    more) overflow float32, where the two-level carry would turn 0 * inf into
+    NaN; the kernel sees the out-of-range product and walks that sequence's
+    chunks one by one, giving exact zeros.  Sequence 0 (contractive) keeps the
+    two-level carry and matches the oracle."""
+    dev = device()
+    B, T, D = 2, 2048, 32
+    p = I.dense_scan_problem(4242, B, T, D, scale=0.9)
+    q = I.dense_scan_problem(4243, 1, T, D, scale=3.0)
+    p["A"][1] = q["A"][0]
+    p["b"][1] = 0.0
+    p["s0"][1] = 0.0
+    log("linear_scan_dense B=2 T=2048 D=32, sequence 1 expanding with a zero solution")
+    A = torch.from_numpy(p["A"]).to(dev)
+    b = torch.from_numpy(p["b"]).to(dev)
+    s0 = torch.from_numpy(p["s0"]).to(dev)
+    s = deer.linear_scan_dense(A, b, s0).cpu().numpy()
+    assert np.all(s[1] == 0.0), np.abs(s[1]).max()
+    ref = orc.solve_dense(p["A"][[0]], p["b"][[0]], p["s0"][[0]])
+    assert rel_linf(s[[0]], ref)[0] <= TOL
 
 
 def test_linear_scan_diag_is_bitwise_reproducible(orc):

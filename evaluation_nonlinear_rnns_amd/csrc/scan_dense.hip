@@ -506,16 +506,15 @@ __global__ __launch_bounds__(64) void dense_carry_kernel(
 // ------------------------------------------------------- two-level carry walk
 // Float D = 32 with many chunks: a sequence's chunks form kTlGroups
 // consecutive groups.
-//   1. dense_group_tl32_kernel, one workgroup per group: the product P_g of
+//   1. dense_group_tl32_kernel, one wavefront per group: the product P_g of
 //      the group's chunk products on the matrix cores (the running product
 //      stays in the accumulators, as in the compose kernel: P <- P_c P with P_c
-//      as the A operands; wavefront 0) and the group offset B_g by the
-//      matrix-vector chain B <- P_c B + B_c (wavefront 1);
-//   2. dense_carry_tl32_kernel, one workgroup per sequence: wavefront 0 walks
-//      the groups from s0 (the state entering each group), then every
-//      wavefront walks one group's chunks from that state and writes the chunk
-//      carries.
-// The serial chain shrinks from nchunk steps to kTlGroups + nchunk / kTlGroups,
+//      as the A operands) and the group offset B_g by the matrix-vector chain
+//      B <- P_c B + B_c from the same operands;
+//   2. dense_carry_tl32_kernel, eight single-wavefront walkers per sequence:
+//      each pushes s0 through the maps of the groups before its own, then walks
+//      its two groups' chunks and writes the chunk carries.
+// The serial chain shrinks from nchunk steps to at most kTlGroups + 2 nchunk / kTlGroups,
 // and the group products (one D^3 product per chunk, 1/64 of the compose
 // work) run over the whole device.  Pairs of affine maps merge as in the rest
 // of the scan (the later on the left); any grouping gives the same result
@@ -523,9 +522,9 @@ __global__ __launch_bounds__(64) void dense_carry_kernel(
 // rounding differs from the one-level walk.  A group product out of range
 // (non-finite, or above kTlLimit in magnitude: strongly expanding dynamics,
 // where P_g x + B_g would cancel huge terms or overflow) makes its sequence
-// take the one-level walk instead, on wavefront 0.
+// take the one-level walk instead, on its first walker.
 constexpr int kTlGroups = 16;
-constexpr int kTlPF = 4;                 // chunks fetched ahead by each walk
+constexpr int kTlPF = 8;                 // chunks fetched ahead by the group kernel's chains
 constexpr float kTlLimit = 1e18f;
 constexpr int kTlMinChunks = 32;         // fewer chunks: the one-level walk is short already
 
@@ -581,12 +580,13 @@ __device__ __forceinline__ void tl_set_line(float *line, float x, int i, int hf)
 }
 
 // Walk matrices [cb, ce) of (P, Bv) from the state x, calling at(c, x) with
-// the state before each; whole rounds of kTlPF run as straight-line bodies (a
+// the state before each; whole rounds of PF run as straight-line bodies (a
 // branch inside a round would make the compiler wait for every load in flight).
 template <int PF, class At>
 __device__ __forceinline__ float tl_walk(const float *__restrict__ P, const float *__restrict__ Bv, size_t cb,
                                          size_t ce, float x, float *line, int i, int hf, At &&at)
 {
+    if (ce <= cb) return x;                              // nothing to walk (and nothing to fetch)
     tl_set_line(line, x, i, hf);
     TlChunk ring[PF];
 #pragma unroll
@@ -610,10 +610,12 @@ __device__ __forceinline__ float tl_walk(const float *__restrict__ P, const floa
     return x;
 }
 
-// Group products and offsets: one 128-thread workgroup per (sequence, group).
-// Writes Pg [B][kTlGroups][32][32] (row-major) and Bg [B][kTlGroups][32];
-// groups past the last chunk are left alone.
-__global__ __launch_bounds__(128) void dense_group_tl32_kernel(
+// Group products and offsets: one wavefront per (sequence, group).  Writes
+// Pg [B][kTlGroups][32][32] (row-major) and Bg [B][kTlGroups][32]; groups past
+// the last chunk are left alone.  Each step issues the product's 16 MFMAs and
+// then the offset's matrix-vector step from the same operands, which runs
+// while the matrix cores work.
+__global__ __launch_bounds__(64) void dense_group_tl32_kernel(
     const float *__restrict__ Pagg, const float *__restrict__ Bagg, const int *__restrict__ skip,
     const int *__restrict__ all_done, int nchunk, float *__restrict__ Pg, float *__restrict__ Bg)
 {
@@ -625,103 +627,89 @@ __global__ __launch_bounds__(128) void dense_group_tl32_kernel(
     const int cb = g * GS, ce = min(nchunk, cb + GS);
     if (cb >= ce) return;
     __shared__ __align__(16) float line[D];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lane = threadIdx.x;
     const int i = lane & 31, hf = lane >> 5;
     const size_t q0 = static_cast<size_t>(bseq) * nchunk;
     const size_t qg = static_cast<size_t>(bseq) * kTlGroups + g;
-    if (wave == 1) {
-        // the offset: the state the group's chunks reach from a zero start
-        const float x = tl_walk<kTlPF>(Pagg, Bagg, q0 + cb + 1, q0 + ce, Bagg[(q0 + cb) * D + i], line, i, hf,
-                                       [](size_t, float) {});
-        if (hf == 0) Bg[qg * D + i] = x;
-        return;
-    }
-    // the product, accumulators in the B operand layout: register v holds P[row32(v, hf)][i]
+    // the product, accumulators in the B operand layout: register v holds P[row32(v, hf)][i];
+    // the offset: the state the group's chunks reach from a zero start
     const float *Pf = Pagg + (q0 + cb) * D * D;
     v16f P;
 #pragma unroll
     for (int v = 0; v < 16; ++v) P[v] = Pf[row32(v, hf) * D + i];
+    float x = Bagg[(q0 + cb) * D + i];
+    tl_set_line(line, x, i, hf);
     TlChunk ring[kTlPF];
 #pragma unroll
     for (int u = 0; u < kTlPF; ++u) tl_fetch(Pagg, Bagg, q0 + cb + 1 + u, q0 + ce, i, hf, ring[u]);
-    auto compose = [&](const TlChunk &k) {
+    auto step = [&](const TlChunk &k) {
         v16f acc = {};
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(k.a[v >> 2][v & 3], P[v], acc, 0, 0, 0);
+        x = tl_advance(k, line, i, hf);
         P = acc;
     };
     const int n = ce - cb - 1, nfull = cb + 1 + n - n % kTlPF;
     for (int c0 = cb + 1; c0 < nfull; c0 += kTlPF) {
 #pragma unroll
         for (int u = 0; u < kTlPF; ++u) {
-            compose(ring[u]);
+            step(ring[u]);
             tl_fetch(Pagg, Bagg, q0 + c0 + u + kTlPF, q0 + ce, i, hf, ring[u]);
         }
     }
 #pragma unroll
     for (int u = 0; u < kTlPF; ++u)
-        if (nfull + u < ce) compose(ring[u]);
+        if (nfull + u < ce) step(ring[u]);
     float *po = Pg + qg * D * D;
 #pragma unroll
     for (int v = 0; v < 16; ++v) po[row32(v, hf) * D + i] = P[v];
+    if (hf == 0) Bg[qg * D + i] = x;
 }
 
-// Carries from the group products: one workgroup of kTlWalkers wavefronts per
-// sequence, each walking kTlGroups / kTlWalkers consecutive groups; with two
-// wavefronts per SIMD the walks keep kTlWalkPF chunks of loads in flight.
+// Carries from the group products: kTlWalkers single-wavefront workgroups per
+// sequence, spread over the device (a compute unit keeps only so many cache
+// lines in flight, and eight walkers sharing one ran at a third of the speed).
+// Walker w pushes s0 through the maps of the groups before its own (at most
+// kTlGroups - 2 steps, the same bits in every walker), then walks its
+// kTlGroups / kTlWalkers groups' chunks from there, kTlWalkPF chunks of loads
+// in flight.
 constexpr int kTlWalkers = 8;
 constexpr int kTlWalkPF = 10;
-__global__ __launch_bounds__(64 * kTlWalkers) void dense_carry_tl32_kernel(
+__global__ __launch_bounds__(64) void dense_carry_tl32_kernel(
     const float *__restrict__ Pagg, const float *__restrict__ Bagg, const float *__restrict__ Pg,
     const float *__restrict__ Bg, const float *__restrict__ s0, const int *__restrict__ skip,
     const int *__restrict__ all_done, int B, int nchunk, float *__restrict__ carry)
 {
     constexpr int D = 32, GPW = kTlGroups / kTlWalkers;
     if (all_done && *all_done) return;
-    const int bseq = blockIdx.x;
+    const int bseq = blockIdx.x / kTlWalkers, w = blockIdx.x % kTlWalkers;
     if (bseq >= B || (skip && skip[bseq])) return;      // uniform per workgroup
-    __shared__ float gent[kTlWalkers][D];               // states entering each walker's first group
-    __shared__ __align__(16) float xl[kTlWalkers][D];   // per-wavefront state line
-    __shared__ int bad;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __shared__ __align__(16) float line[D];
+    const int lane = threadIdx.x;
     const int i = lane & 31, hf = lane >> 5;
     const int GS = tl_group_size(nchunk);
     const int ngroups = (nchunk + GS - 1) / GS;
+    const int cb = w * GPW * GS, ce = min(nchunk, cb + GPW * GS);
     const size_t q0 = static_cast<size_t>(bseq) * nchunk;
     const size_t g0 = static_cast<size_t>(bseq) * kTlGroups;
-    float *line = xl[wave];
     const float x0 = s0 ? s0[static_cast<size_t>(bseq) * D + i] : 0.0f;
     auto write_carry = [&](size_t q, float x) {
         if (hf == 0) carry[q * D + i] = x;
     };
-
-    // group products in range?
-    if (tid == 0) bad = 0;
-    __syncthreads();
+    // every group product of the sequence in range? (the same answer in every walker)
     bool out_of_range = false;
-    for (int g = wave; g < ngroups; g += kTlWalkers) {
+    for (int g = 0; g < ngroups; ++g) {
         const float *pg = Pg + (g0 + g) * D * D;
 #pragma unroll
         for (int u = 0; u < 16; ++u) out_of_range |= !(__builtin_fabsf(pg[u * 64 + lane]) <= kTlLimit);
     }
-    if (__any(out_of_range) && lane == 0) bad = 1;
-    __syncthreads();
-    if (bad) {
-        if (wave == 0) tl_walk<kTlWalkPF>(Pagg, Bagg, q0, q0 + nchunk, x0, line, i, hf, write_carry);
+    if (__any(out_of_range)) {
+        if (w == 0) tl_walk<kTlWalkPF>(Pagg, Bagg, q0, q0 + nchunk, x0, line, i, hf, write_carry);
         return;
     }
-
-    // the states entering the groups (kept for each walker's first group)
-    if (wave == 0)
-        tl_walk<kTlWalkPF>(Pg, Bg, g0, g0 + ngroups, x0, line, i, hf, [&](size_t q, float x) {
-            const int g = static_cast<int>(q - g0);
-            if (hf == 0 && g % GPW == 0) gent[g / GPW][i] = x;
-        });
-    __syncthreads();
-
-    // every walker's groups from the state entering the first of them
-    const int cb = wave * GPW * GS, ce = min(nchunk, cb + GPW * GS);
-    if (cb < ce) tl_walk<kTlWalkPF>(Pagg, Bagg, q0 + cb, q0 + ce, gent[wave][i], line, i, hf, write_carry);
+    if (cb >= ce) return;
+    const float xe = tl_walk<kTlWalkPF>(Pg, Bg, g0, g0 + w * GPW, x0, line, i, hf, [](size_t, float) {});
+    tl_walk<kTlWalkPF>(Pagg, Bagg, q0 + cb, q0 + ce, xe, line, i, hf, write_carry);
 }
 
 // ----------------------------------------------------------------- replay
@@ -988,10 +976,10 @@ int launch_dense_dp(const float *A, const float *d, const float *W, const float 
     constexpr bool kVecOk = CarryGeom<DP, ACC>::KG % CarryGeom<DP, ACC>::VEC == 0;
     if (DP == 32 && pl.D == 32 && !f64 && pl.nchunk >= kTlMinChunks) {
         const float *Pf = reinterpret_cast<const float *>(Pagg), *Bf = reinterpret_cast<const float *>(Bagg);
-        DEER_LAUNCH(dense_group_tl32_kernel, dim3(static_cast<unsigned>(pl.B) * kTlGroups), dim3(128), 0, stream, Pf,
+        DEER_LAUNCH(dense_group_tl32_kernel, dim3(static_cast<unsigned>(pl.B) * kTlGroups), dim3(64), 0, stream, Pf,
                     Bf, skip, all_done, pl.nchunk, Pgrp, Bgrp);
         DEER_HIP(hipGetLastError());
-        DEER_LAUNCH(dense_carry_tl32_kernel, dim3(static_cast<unsigned>(pl.B)), dim3(64 * kTlWalkers), 0, stream, Pf,
+        DEER_LAUNCH(dense_carry_tl32_kernel, dim3(static_cast<unsigned>(pl.B) * kTlWalkers), dim3(64), 0, stream, Pf,
                     Bf, Pgrp, Bgrp, s0, skip, all_done, pl.B, pl.nchunk, reinterpret_cast<float *>(carry));
     } else if (kVecOk && pl.D == DP)
         DEER_LAUNCH((dense_carry_kernel<DP, ACC, kVecOk>), dim3(static_cast<unsigned>(pl.B)), dim3(64), 0, stream,

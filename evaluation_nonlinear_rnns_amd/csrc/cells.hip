@@ -56,6 +56,79 @@ __device__ __forceinline__ void block_min_to(unsigned v, unsigned *dst)
 }
 
 // ------------------------------------------------------------- projection
+// Narrow projections (O <= 64 outputs, M <= 64 inputs): out[n][o] =
+// sum_j U[o][j] x[n][j] + bias[o].  Thread (o, rp) keeps row o of U (padded
+// with zeros to MP) in registers and computes output o of rows rp, rp + RPP,
+// ... of each 64-row tile, reading the rows of x from LDS as 16-byte
+// broadcasts.  A tile's rows are contiguous in x and in out, so both stream
+// coalesced.  The grid is a few workgroups per CU striding over the tiles
+// (thousands of short workgroups were bound by their dispatch), each fetching
+// its next tile into registers while it computes the current one.  The sum
+// runs in column order, one FMA per column.
+template <int OP, int MP>
+__global__ __launch_bounds__(kThreads) void projection_rows_kernel(const float *__restrict__ x,
+                                                                   const float *__restrict__ U,
+                                                                   const float *__restrict__ bias,
+                                                                   float *__restrict__ out, long long N, int M, int O)
+{
+    constexpr int TR = 64;                   // rows per tile
+    constexpr int RPP = kThreads / OP;       // rows per pass
+    constexpr int LX = MP + 4;               // LDS row stride (16-byte aligned rows)
+    constexpr int NX = TR * MP / kThreads;   // x words per thread per tile
+    __shared__ __align__(16) float xs[TR * LX];
+    const int tid = threadIdx.x;
+    const int o = tid % OP, rp = tid / OP;
+    const long long tiles = (N + TR - 1) / TR;
+    float u[MP];
+    const bool ov = o < O;
+#pragma unroll
+    for (int k = 0; k < MP; ++k) u[k] = (ov && k < M) ? U[static_cast<size_t>(o) * M + k] : 0.0f;
+    const float bo = (bias && ov) ? bias[o] : 0.0f;
+    // x words of tile t owned by this thread: e = tid + j kThreads -> row e / MP, column e % MP
+    float xv[NX];
+    auto fetch = [&](long long t) {
+        const long long n0 = t * TR;
+#pragma unroll
+        for (int j = 0; j < NX; ++j) {
+            const int e = tid + j * kThreads, r = e / MP, k = e % MP;
+            const long long n = n0 + r;
+            const bool ok = t < tiles && n < N && k < M;
+            const long long idx = ok ? n * M + k : 0;     // clamped: the load stays unconditional
+            const float v = x[idx];
+            xv[j] = ok ? v : 0.0f;
+        }
+    };
+    long long t = blockIdx.x;
+    fetch(t);
+    for (; t < tiles; t += gridDim.x) {
+        __syncthreads();                     // the previous tile is done with xs
+#pragma unroll
+        for (int j = 0; j < NX; ++j) {
+            const int e = tid + j * kThreads;
+            xs[(e / MP) * LX + e % MP] = xv[j];
+        }
+        __syncthreads();
+        fetch(t + gridDim.x);
+        const long long n0 = t * TR;
+        const int nr = static_cast<int>(min(static_cast<long long>(TR), N - n0));
+#pragma unroll
+        for (int jr = 0; jr < TR / RPP; ++jr) {
+            const int r = rp + jr * RPP;
+            const v4f *xr = reinterpret_cast<const v4f *>(xs + r * LX);
+            float acc = 0.0f;
+#pragma unroll
+            for (int k4 = 0; k4 < MP / 4; ++k4) {
+                const v4f q = xr[k4];
+                acc = __builtin_fmaf(u[4 * k4], q[0], acc);
+                acc = __builtin_fmaf(u[4 * k4 + 1], q[1], acc);
+                acc = __builtin_fmaf(u[4 * k4 + 2], q[2], acc);
+                acc = __builtin_fmaf(u[4 * k4 + 3], q[3], acc);
+            }
+            if (ov && r < nr) out[(n0 + r) * O + o] = acc + bo;
+        }
+    }
+}
+
 // out[n][o] = sum_j U[o][j] x[n][j] + bias[o], for OG groups of 64 outputs.
 template <int OG>
 __global__ __launch_bounds__(kThreads) void projection_kernel(const float *__restrict__ x, const float *__restrict__ U,
@@ -323,6 +396,20 @@ __global__ __launch_bounds__(kThreads) void gru_eval_kernel(
 
 int pick_dp(int D) { return D <= 4 ? 4 : D <= 8 ? 8 : D <= 16 ? 16 : D <= 32 ? 32 : 64; }
 
+// Compute units of the current device (cached per device; 256 if the query fails).
+int device_cus()
+{
+    static int cache[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+        cache[dev] = cus;
+    }
+    return cache[dev];
+}
+
 unsigned eval_blocks(int B, int T, int &tiles)
 {
     tiles = (T + kTP - 1) / kTP;
@@ -348,6 +435,26 @@ int launch_projection(const float *x, const float *U, const float *bias, float *
     if (B == 0 || T == 0) return DEER_OK;
     if (tiled || proj_mfma_supported(M, O)) return launch_projection_mfma(x, U, bias, p, B, T, M, O, tiled, stream);
     if (O > 192) return fail(DEER_ERR_UNSUPPORTED, "projection: more than 192 outputs");
+    if (O <= 64 && M <= 64) {
+        const long long NN = static_cast<long long>(B) * T;
+        const unsigned tiles = static_cast<unsigned>(std::min<long long>((NN + 63) / 64, 4ll * device_cus()));
+        const int op = pick_dp(O), mp = M <= 16 ? 16 : M <= 32 ? 32 : 64;
+#define DEER_PROJ_ROWS(OPV, MPV)                                                                               \
+    if (op == OPV && mp == MPV) {                                                                              \
+        DEER_LAUNCH((projection_rows_kernel<OPV, MPV>), dim3(tiles), dim3(kThreads), 0, stream, x, U, bias, p, \
+                    NN, M, O);                                                                                 \
+        DEER_HIP(hipGetLastError());                                                                           \
+        return DEER_OK;                                                                                        \
+    }
+#define DEER_PROJ_ROWS_M(OPV) DEER_PROJ_ROWS(OPV, 16) DEER_PROJ_ROWS(OPV, 32) DEER_PROJ_ROWS(OPV, 64)
+        DEER_PROJ_ROWS_M(4)
+        DEER_PROJ_ROWS_M(8)
+        DEER_PROJ_ROWS_M(16)
+        DEER_PROJ_ROWS_M(32)
+        DEER_PROJ_ROWS_M(64)
+#undef DEER_PROJ_ROWS_M
+#undef DEER_PROJ_ROWS
+    }
     const int N = B * T;
     const int row_tiles = 4;
     const long long rows_per_block = 32ll * row_tiles;

@@ -914,13 +914,8 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
         dense ? dense_persist_fits(B, D, T, o.scan_f64 != 0) && (!can_escalate_once || dense_persist_fits(B, D, T, true))
               : diag_persist_fits(B, D, T);
     if (!gru && !o.multi_launch && one_launch) {
-        if (init_guess) {
-            if (init_guess != traj_out)
-                DEER_LAUNCH(copy_kernel, dim3(grid_for(BTD)), dim3(256), 0, stream, traj_out, init_guess, BTD);
-        } else {
-            DEER_LAUNCH(fill_kernel, dim3(grid_for(BTD)), dim3(256), 0, stream, traj_out, BTD, 0.0f);
-        }
-        DEER_HIP(hipGetLastError());
+        // the launch reads the starting iterate itself (zeros without init_guess)
+        // and writes every position of traj_out when its sequence stops
         prof.begin(2);
         rc = launch_projection(x, p->U, p->b, L.proj, B, T, p->M, PD, false, stream);
         prof.end();
@@ -928,17 +923,18 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
         const int window = tol >= 0.0f ? o.stall_window : 0;   // tol < 0 never passes: exactly max_iter iterations
         prof.begin(0);
         if (dense)
-            rc = launch_dense_persist(p->W, L.proj, s0, traj_out, B, T, D, lz.shrink, tol, max_iter, window,
-                                      o.scan_f64 != 0, can_escalate_once, false, L.iters, L.status, L.resid, L.scan,
-                                      state_f64, stream);
+            rc = launch_dense_persist(p->W, L.proj, s0, init_guess, traj_out, B, T, D, lz.shrink, tol, max_iter,
+                                      window, o.scan_f64 != 0, can_escalate_once, false, L.iters, L.status, L.resid,
+                                      L.scan, state_f64, stream);
         else
-            rc = launch_diag_persist(p->W, L.proj, s0, traj_out, B, T, D, lz, tol, max_iter, window, L.iters,
-                                     L.status, L.resid, L.scan, stream);
+            rc = launch_diag_persist(p->W, L.proj, s0, init_guess, traj_out, B, T, D, lz, tol, max_iter, window,
+                                     L.iters, L.status, L.resid, L.scan, stream);
         prof.end();
         if (rc == DEER_OK && can_escalate_once) {
             prof.begin(1);
-            rc = launch_dense_persist(p->W, L.proj, s0, traj_out, B, T, D, lz.shrink, tol, max_iter, window, true,
-                                      false, true, L.iters, L.status, L.resid, L.scan, state_f64, stream);
+            rc = launch_dense_persist(p->W, L.proj, s0, traj_out, traj_out, B, T, D, lz.shrink, tol, max_iter,
+                                      window, true, false, true, L.iters, L.status, L.resid, L.scan, state_f64,
+                                      stream);
             prof.end();
         }
         if (rc == DEER_OK && rms_out) rc = residual_rms(true);

@@ -205,7 +205,8 @@ struct PersistArgs {
     const float *W;        // [D, D]
     const float *proj;     // [B, T, D]: U x_t + b
     const float *s0;       // [B, D] or null
-    float *traj;           // [B, T, D]: s^(i0) on entry, the iterate a sequence stops at on exit
+    const float *init;     // [B, T, D]: the starting iterate s^(i0), or null for zeros (may alias traj)
+    float *traj;           // [B, T, D]: the iterate a sequence stops at, on exit
     int B, T, D, nchunk, G, max_iter, stall_window;
     float tol, shrink;
     int lin_kind;          // diagonal kernel: the linearisation (LinKind)
@@ -380,15 +381,17 @@ __global__ __launch_bounds__(kThreads) void dense_persist_kernel(PersistArgs a)
             const int c = min(4 * g + v, D - 1);
             pr[q][v] = a.proj[(seq + tb + r) * D + c];
         }
-    // the iterate s^(i0) with the state before the range (s0 or the left neighbour's last)
+    // the iterate s^(i0) with the state before the range (s0 or the left neighbour's last); a
+    // range read here is written back only after the group's first barrier, which this
+    // workgroup's slot holds up, so `init` may alias `traj`
     for (int e = tid; e < (np + 1) * kDP; e += kThreads) {
         const int r = e / kDP, k = e % kDP;
         const int t = tb - 1 + r;
         const int kc = k < D ? k : D - 1;
         const float *src_p = (t < 0) ? (a.s0 ? a.s0 + static_cast<size_t>(bseq) * D + kc : a.W)
-                                     : a.traj + (seq + t) * D + kc;
+                                     : (a.init ? a.init + (seq + t) * D + kc : a.W);
         const float v = *src_p;
-        sh.S[e] = (k < D && (t >= 0 || a.s0)) ? v : 0.0f;
+        sh.S[e] = (k < D && (t < 0 ? a.s0 != nullptr : a.init != nullptr)) ? v : 0.0f;
     }
     if (tid == 0) sh.abort_now = 0;
     __syncthreads();
@@ -844,9 +847,9 @@ __global__ __launch_bounds__(kThreads) void diag_persist_kernel(PersistArgs a)
         const int t = tb - 1 + r;
         const int kc = k < D ? k : D - 1;
         const float *src_p = (t < 0) ? (a.s0 ? a.s0 + static_cast<size_t>(bseq) * D + kc : a.W)
-                                     : a.traj + (seq + t) * D + kc;
+                                     : (a.init ? a.init + (seq + t) * D + kc : a.W);
         const float v = *src_p;
-        sh.S[e] = (k < D && (t >= 0 || a.s0)) ? v : 0.0f;
+        sh.S[e] = (k < D && (t < 0 ? a.s0 != nullptr : a.init != nullptr)) ? v : 0.0f;
     }
     if (tid == 0) sh.abort_now = 0;
     __syncthreads();
@@ -1184,17 +1187,17 @@ unsigned *dense_persist_abort_word(void *state, int B, int T, bool f64)
     return reinterpret_cast<unsigned *>(static_cast<char *>(state) + persist_state(B, T, f64).abort_off);
 }
 
-int launch_dense_persist(const float *W, const float *proj, const float *s0, float *traj, int B, int T, int D,
-                         float shrink, float tol, int max_iter, int stall_window, bool f64, bool escalate,
-                         bool resume, int *iters, int *status, float *resid, void *state, bool state_f64,
-                         hipStream_t stream)
+int launch_dense_persist(const float *W, const float *proj, const float *s0, const float *init, float *traj, int B,
+                         int T, int D, float shrink, float tol, int max_iter, int stall_window, bool f64,
+                         bool escalate, bool resume, int *iters, int *status, float *resid, void *state,
+                         bool state_f64, hipStream_t stream)
 {
     if (B == 0) return DEER_OK;
     if (f64 && !state_f64) return fail(DEER_ERR_INVALID, "persistent dense solve: state sized for float32");
     if (!dense_persist_fits(B, D, T, f64))
         return fail(DEER_ERR_UNSUPPORTED, "persistent dense solve: problem does not fit the device at once");
     PersistArgs a{};
-    a.W = W; a.proj = proj; a.s0 = s0; a.traj = traj;
+    a.W = W; a.proj = proj; a.s0 = s0; a.init = init; a.traj = traj;
     a.B = B; a.T = T; a.D = D;
     a.nchunk = (T + kL - 1) / kL;
     a.G = groups_of(T);
@@ -1220,9 +1223,9 @@ int launch_dense_persist(const float *W, const float *proj, const float *s0, flo
     return f64 ? launch_persist<double>(a, stream) : launch_persist<float>(a, stream);
 }
 
-int launch_diag_persist(const float *W, const float *proj, const float *s0, float *traj, int B, int T, int D,
-                        Linearization lz, float tol, int max_iter, int stall_window, int *iters, int *status,
-                        float *resid, void *state, hipStream_t stream)
+int launch_diag_persist(const float *W, const float *proj, const float *s0, const float *init, float *traj, int B,
+                        int T, int D, Linearization lz, float tol, int max_iter, int stall_window, int *iters,
+                        int *status, float *resid, void *state, hipStream_t stream)
 {
     if (B == 0) return DEER_OK;
     if (lz.kind != kLinJacobian && lz.kind != kLinZero && lz.kind != kLinIdentity)
@@ -1230,7 +1233,7 @@ int launch_diag_persist(const float *W, const float *proj, const float *s0, floa
     if (!diag_persist_fits(B, D, T))
         return fail(DEER_ERR_UNSUPPORTED, "persistent diagonal solve: problem does not fit the device at once");
     PersistArgs a{};
-    a.W = W; a.proj = proj; a.s0 = s0; a.traj = traj;
+    a.W = W; a.proj = proj; a.s0 = s0; a.init = init; a.traj = traj;
     a.B = B; a.T = T; a.D = D;
     a.nchunk = (T + kL - 1) / kL;
     a.G = groups_of(T);

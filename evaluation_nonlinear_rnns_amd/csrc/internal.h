@@ -509,8 +509,9 @@ int launch_tiny_solve(const float *W, const float *U, const float *bias, const f
 // Whole dense tanh solves in one launch (dense_solve.hip): each sequence gets a
 // group of workgroups that synchronise among themselves, one group barrier per
 // iteration; for D <= 16, T <= 8192 and grids the device holds at once (f64:
-// double accumulation).  `proj` is the input projection; `traj` holds s^(0)
-// on entry and, on exit, the iterate each sequence stopped at.  `state` holds
+// double accumulation).  `proj` is the input projection; `init` is the starting
+// iterate (null: zeros; it may alias `traj`), `traj` receives the iterate each
+// sequence stopped at.  `state` holds
 // dense_persist_state_bytes and is set up by each launch; iters, status and
 // resid are device arrays.  With `escalate`, a stalled sequence is handed over
 // (an internal status) instead of stopped; a launch with `resume` and f64
@@ -518,10 +519,10 @@ int launch_tiny_solve(const float *W, const float *U, const float *bias, const f
 // the state was sized with f64 (needed by any double-precision launch).
 bool dense_persist_fits(int B, int D, int T, bool f64);
 size_t dense_persist_state_bytes(int B, int T, bool f64);
-int launch_dense_persist(const float *W, const float *proj, const float *s0, float *traj, int B, int T, int D,
-                         float shrink, float tol, int max_iter, int stall_window, bool f64, bool escalate,
-                         bool resume, int *iters, int *status, float *resid, void *state, bool state_f64,
-                         hipStream_t stream);
+int launch_dense_persist(const float *W, const float *proj, const float *s0, const float *init, float *traj, int B,
+                         int T, int D, float shrink, float tol, int max_iter, int stall_window, bool f64,
+                         bool escalate, bool resume, int *iters, int *status, float *resid, void *state,
+                         bool state_f64, hipStream_t stream);
 // Set (non-zero) when a bounded wait of the launches since the last
 // non-resumed one hit its bound.
 unsigned *dense_persist_abort_word(void *state, int B, int T, bool state_f64);
@@ -529,9 +530,9 @@ unsigned *dense_persist_abort_word(void *state, int B, int T, bool state_f64);
 // problems in one launch, with the same groups and the same state
 // (dense_persist_state_bytes(B, T, false), abort word included); no hand-over.
 bool diag_persist_fits(int B, int D, int T);
-int launch_diag_persist(const float *W, const float *proj, const float *s0, float *traj, int B, int T, int D,
-                        Linearization lz, float tol, int max_iter, int stall_window, int *iters, int *status,
-                        float *resid, void *state, hipStream_t stream);
+int launch_diag_persist(const float *W, const float *proj, const float *s0, const float *init, float *traj, int B,
+                        int T, int D, Linearization lz, float tol, int max_iter, int stall_window, int *iters,
+                        int *status, float *resid, void *state, hipStream_t stream);
 
 // Parallel Broyden (broyden.hip): the block updates and the chunked compressed
 // scan of delta_t = A_t delta_{t-1} + c_t, A_t = alpha I + shrink U_t V_t^T.

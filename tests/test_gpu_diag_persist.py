@@ -122,6 +122,31 @@ def test_one_launch_iteration_cap_and_start(orc, mode):
     assert torch.equal(traj, init)
 
 
+@pytest.mark.parametrize("mode", ["dense", "diag", "picard"])
+def test_one_launch_initial_guess_aliasing_the_output(orc, mode):
+    """init_guess and out are the same tensor: every workgroup reads its range
+    of the guess before any workgroup of its group can stop and write there,
+    so the result equals a solve from a separate copy of the same guess."""
+    B, T, D, M = 3, 1700, 16, 16
+    p = _problem(2777, B, T, D, M, 0.9)
+    cell, x, s0 = _setup(p)
+    oc = orc.Cell.from_problem(p)
+    guess = (0.5 * orc.rollout(oc, p["x"], p["s0"])).astype(np.float32)
+    g = torch.from_numpy(guess).to(x.device)
+    log(f"one-launch {mode} solve, init_guess aliasing out")
+    (ref_traj, ref_iters, _, ref_status, _), n1 = _solve_counted(cell, x, s0, mode=mode, tol=1e-5, max_iter=T + 1,
+                                                                 init_guess=g.clone())
+    assert n1 == 1
+    buf = g.clone()
+    (traj, iters, _, status, rc), n2 = _solve_counted(cell, x, s0, mode=mode, tol=1e-5, max_iter=T + 1,
+                                                      init_guess=buf, out=buf)
+    assert n2 == 1
+    assert traj.data_ptr() == buf.data_ptr()
+    assert rc == deer.DEER_OK and np.all(status == 0)
+    assert np.array_equal(iters, ref_iters)
+    assert torch.equal(traj, ref_traj)
+
+
 def test_one_launch_nan_input_stalls(orc):
     """A NaN input at t = 5 of sequence 1: the states before it converge, the
     front stays at 5 and the check stops that sequence one window later; the

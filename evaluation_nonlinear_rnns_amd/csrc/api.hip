@@ -971,6 +971,9 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
     DEER_HIP(hipGetLastError());
     const bool fused = fused_gru_step(p, mode);
     const bool zero_start = fused && !init_guess;   // the fused step reads no s^(0) when it is all zeros
+    // from a zero start with inputs as wide as the state, the first fused step
+    // computes the input projection itself (no separate projection launch)
+    const bool proj_in_step = zero_start && p->M == D;
     if (init_guess) {
         if (init_guess != traj_out)
             DEER_LAUNCH(copy_kernel, dim3(grid_for(BTD)), dim3(256), 0, stream, traj_out, init_guess, BTD);
@@ -980,10 +983,12 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
     DEER_HIP(hipGetLastError());
 
     // iteration-invariant input projection (W_ih x + b_ih for the GRU, U x + b for tanh)
-    prof.begin(2);
-    rc = launch_projection(x, p->U, p->b, L.proj, B, T, p->M, PD, tiled, stream);
-    prof.end();
-    if (rc) return rc;
+    if (!proj_in_step) {
+        prof.begin(2);
+        rc = launch_projection(x, p->U, p->b, L.proj, B, T, p->M, PD, tiled, stream);
+        prof.end();
+        if (rc) return rc;
+    }
 
     // a stall in dense mode may switch the linear solve to double accumulation
     bool scan_f64 = o.scan_f64 != 0;
@@ -991,15 +996,18 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
     const int *sel = &L.ctl->iter;
     const int *all_done = &L.ctl->all_done;
     const FrontOut fo{sc.front, tol};
+    bool first_step = true;
     auto enqueue_iteration = [&]() -> int {
         int r;
         StallCheck sci = sc;
         sci.escalate = (can_escalate && !scan_f64) ? 1 : 0;
         if (fused) {
+            const bool project = proj_in_step && first_step;
+            first_step = false;
             prof.begin(0);
             r = launch_gru_quasi_step(p->W, p->b2, L.proj, s0, traj_out, L.buf1, L.ctl, L.done, L.iters, L.status,
                                       L.resid, tol, max_iter, L.res_bits, L.res_tile, B, T, D, zero_start, lz, sci,
-                                      L.scan, stream);
+                                      L.scan, project ? x : nullptr, p->U, p->b, p->M, stream);
             prof.end();
             return r;
         }

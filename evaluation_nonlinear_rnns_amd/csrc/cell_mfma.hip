@@ -117,6 +117,28 @@ __device__ __forceinline__ void gru_fetch_rows(const float *__restrict__ s, cons
     }
 }
 
+// Rows x_{t0} .. x_{t0+TP-1} of the inputs (M = D columns) into the row
+// registers, zero past T: the A operands of the first iteration's projection.
+template <int D>
+__device__ __forceinline__ void gru_fetch_xrows(const float *__restrict__ x, int T, int bseq, int t0,
+                                                v4f (&hv)[GruTile<D>::NH])
+{
+    using G = GruGeom<D>;
+    const int tid = threadIdx.x;
+    const size_t seq = static_cast<size_t>(bseq) * T;
+#pragma unroll
+    for (int i = 0; i < GruTile<D>::NH; ++i) {
+        const int e = tid + i * kThreads;
+        v4f v = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (e < G::TP * (D / 4)) {
+            const int r = e / (D / 4), q = (e % (D / 4)) * 4;
+            const int t = t0 + r;
+            if (t < T) v = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(x + (seq + t) * D + q));
+        }
+        hv[i] = v;
+    }
+}
+
 // Tiled projection of the lane's 16 positions: 32-position block, gate g,
 // quad q, half hf, channel c, 4 positions per 16-byte access (load u = 4 g + q).
 template <int D>
@@ -283,14 +305,25 @@ __global__ __launch_bounds__(kThreads, 2) void gru_eval_mfma_kernel(
 //
 // The residual of the iterate is reduced per tile into res_tile[tile] (plain
 // stores; the convergence test takes the max over a sequence's tiles).
-template <int D>
+//
+// FIRST: the first iteration from a zero start, with the input projection
+// computed here instead of by a separate launch (inputs of width M = D).  The
+// iterate is zero, so W_hh s vanishes and the matrix cores compute the
+// projection W_ih x_t of the tile instead (W_ih as the B operands, the rows of
+// x as the A operands); the lane adds b_ih, writes its values to the tiled
+// projection that the later iterations read, and evaluates the gates with
+// q = b_hh and h = 0.  This reads x (D words per position) and writes the
+// projection once, where the separate launch read x and wrote the projection
+// and this iteration then read it back.
+template <int D, bool FIRST>
 __global__ __launch_bounds__(kThreads, 2) void gru_quasi_step_kernel(
     const float *__restrict__ Whh, const float *__restrict__ bhh, const float *__restrict__ pt,
     const float *__restrict__ s0, float *s_even, float *s_odd, SolveControl *ctl, int *done, int *iters,
     int *status, float *resid, float tol, int max_iter, unsigned *res_bits, unsigned *__restrict__ res_tile, int T,
     int tiles_per_seq,
     int nseq, long long ntiles, int zero_start, Linearization lz, StallCheck sc, ScanHeader *__restrict__ hdr,
-    unsigned long long *__restrict__ desc)
+    unsigned long long *__restrict__ desc, const float *__restrict__ xin, const float *__restrict__ Wih,
+    const float *__restrict__ bih, float *pt_out)
 {
     using G = GruGeom<D>;
     if (ctl->all_done) return;                   // same value for every workgroup of the launch
@@ -310,11 +343,18 @@ __global__ __launch_bounds__(kThreads, 2) void gru_quasi_step_kernel(
     const bool per_seq = nseq <= kSeqLds;        // else per-tile maxima go to res_tile
     for (int b = tid; b < kSeqLds; b += kThreads) seqmax[b] = 0u;
 
+    const float *Wop = FIRST ? Wih : Whh;       // B operands of the matrix-core phase
     for (int e = tid; e < 3 * D * D; e += kThreads) {
         const int o = e / D, k = e % D;
-        Ws[o * G::LDH + k] = Whh[e];
+        Ws[o * G::LDH + k] = Wop[e];
     }
     const float br = bhh ? bhh[c] : 0.0f, bz = bhh ? bhh[D + c] : 0.0f, bn = bhh ? bhh[2 * D + c] : 0.0f;
+    float pb[3] = {0.0f, 0.0f, 0.0f};           // b_ih of the lane's channel (first iteration)
+    if (FIRST && bih) {
+        pb[0] = bih[c];
+        pb[1] = bih[D + c];
+        pb[2] = bih[2 * D + c];
+    }
     const float wr = Whh[static_cast<size_t>(c) * D + c];
     const float wz = Whh[static_cast<size_t>(D + c) * D + c];
     const float wn = Whh[static_cast<size_t>(2 * D + c) * D + c];
@@ -334,7 +374,15 @@ __global__ __launch_bounds__(kThreads, 2) void gru_quasi_step_kernel(
     const int gq = static_cast<int>(gridDim.x) / nseq, gr = static_cast<int>(gridDim.x) % nseq;
     int bseq = static_cast<int>(blockIdx.x) % nseq, tt = static_cast<int>(blockIdx.x) / nseq;
     (void)ntiles;
-    if (tt < tiles_per_seq) gru_fetch<D>(s, s0, pt, T, tps32, bseq, tt * G::TP, ps, hf, c, hv, pv);
+    if (FIRST) {
+#pragma unroll
+        for (int g = 0; g < 3; ++g)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) pv[g][q] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        if (tt < tiles_per_seq) gru_fetch_xrows<D>(xin, T, bseq, tt * G::TP, hv);
+    } else if (tt < tiles_per_seq) {
+        gru_fetch<D>(s, s0, pt, T, tps32, bseq, tt * G::TP, ps, hf, c, hv, pv);
+    }
     for (; tt < tiles_per_seq;) {
         const int t0 = tt * G::TP;
         int nb = bseq + gr, nt = tt + gq;         // the workgroup's next tile
@@ -356,9 +404,14 @@ __global__ __launch_bounds__(kThreads, 2) void gru_quasi_step_kernel(
         for (int g = 0; g < 3; ++g)
 #pragma unroll
             for (int q = 0; q < 4; ++q) pc[g][q] = pv[g][q];
-        if (nt < tiles_per_seq) gru_fetch_rows<D>(s, s0, T, nb, nt * G::TP, hv);
+        if (nt < tiles_per_seq) {
+            if (FIRST)
+                gru_fetch_xrows<D>(xin, T, nb, nt * G::TP, hv);
+            else
+                gru_fetch_rows<D>(s, s0, T, nb, nt * G::TP, hv);
+        }
         if (!live) {
-            if (nt < tiles_per_seq) {
+            if (!FIRST && nt < tiles_per_seq) {
                 const v4f *nbase = gru_proj_base<D>(pt, tps32, nb, nt * G::TP, ps);
 #pragma unroll
                 for (int u = 0; u < 12; ++u) pv[u / 4][u % 4] = gru_proj_load<D>(nbase, u, hf, c);
@@ -433,10 +486,31 @@ __global__ __launch_bounds__(kThreads, 2) void gru_quasi_step_kernel(
                 }
             }
         };
-        if (nt < tiles_per_seq)
+        if (!FIRST && nt < tiles_per_seq)
             mfma_phase(std::true_type{});
         else
             mfma_phase(std::false_type{});
+
+        if (FIRST) {
+            // the accumulators hold W_ih x_t: the projection of this tile, written
+            // out for the later iterations (sub-tiles past the sequence's last
+            // 32-position block are not its own), and W_hh s = 0 for the gates
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                pc[0][v >> 2][v & 3] = accR[v] + pb[0];
+                pc[1][v >> 2][v & 3] = accZ[v] + pb[1];
+                pc[2][v >> 2][v & 3] = accN[v] + pb[2];
+                accR[v] = 0.0f;
+                accZ[v] = 0.0f;
+                accN[v] = 0.0f;
+            }
+            if (t0 + ps * 32 < T) {
+                v4f *pbase = const_cast<v4f *>(gru_proj_base<D>(pt_out, tps32, bseq, t0, ps));
+#pragma unroll
+                for (int u = 0; u < 12; ++u)
+                    __builtin_nontemporal_store(pc[u / 4][u % 4], pbase + (u * 2 + hf) * D + c);
+            }
+        }
 
         // gates, Jacobian diagonal and offsets at the lane's 16 positions
         const bool full = t0 + ps * 32 + 32 <= T;
@@ -447,8 +521,8 @@ __global__ __launch_bounds__(kThreads, 2) void gru_quasi_step_kernel(
             const int pos = ps * 32 + acc_row(v, hf);
             const int t = t0 + pos;
             const float qr = accR[v] + br, qz = accZ[v] + bz, qn = accN[v] + bn;
-            const float h = H[pos * G::LDH + c];
-            const float st = H[(pos + 1) * G::LDH + c];
+            const float h = FIRST ? 0.0f : H[pos * G::LDH + c];          // the first iterate is zero
+            const float st = FIRST ? 0.0f : H[(pos + 1) * G::LDH + c];
             const float rg = sigmoid_fast(pc[0][v >> 2][v & 3] + qr);
             const float zg = sigmoid_fast(pc[1][v >> 2][v & 3] + qz);
             const float ng = tanh_fast(pc[2][v >> 2][v & 3] + rg * qn);
@@ -760,23 +834,24 @@ int launch_proj_mfma(const float *x, const float *U, const float *bias, float *p
     return DEER_OK;
 }
 
-template <int D>
+template <int D, bool FIRST>
 int launch_gru_step(const float *Whh, const float *bhh, const float *pt, const float *s0, float *s_even, float *s_odd,
                     SolveControl *ctl, int *done, int *iters, int *status, float *resid, float tol, int max_iter,
                     unsigned *res_bits, unsigned *res_tile, int B, int T, bool zero_start, Linearization lz,
-                    const StallCheck &sc, void *state, hipStream_t stream)
+                    const StallCheck &sc, void *state, const float *x, const float *Wih, const float *bih,
+                    float *pt_out, hipStream_t stream)
 {
     using G = GruGeom<D>;
     static int caps[kCapDevices] = {};
-    const int cap = capacity_of(caps, gru_quasi_step_kernel<D>, 0);
+    const int cap = capacity_of(caps, gru_quasi_step_kernel<D, FIRST>, 0);
     const int tps = (T + G::TP - 1) / G::TP;
     const long long ntiles = static_cast<long long>(B) * tps;
     const unsigned grid = static_cast<unsigned>(std::max<long long>(1, std::min<long long>(ntiles, cap)));
     auto *hdr = static_cast<ScanHeader *>(state);
     auto *desc = reinterpret_cast<unsigned long long *>(static_cast<char *>(state) + sizeof(ScanHeader));
-    DEER_LAUNCH((gru_quasi_step_kernel<D>), dim3(grid), dim3(kThreads), 0, stream, Whh, bhh, pt, s0, s_even,
-                       s_odd, ctl, done, iters, status, resid, tol, max_iter, res_bits, res_tile, T, tps, B, ntiles,
-                       zero_start ? 1 : 0, lz, sc, hdr, desc);
+    DEER_LAUNCH((gru_quasi_step_kernel<D, FIRST>), dim3(grid), dim3(kThreads), 0, stream, Whh, bhh, pt, s0, s_even,
+                s_odd, ctl, done, iters, status, resid, tol, max_iter, res_bits, res_tile, T, tps, B, ntiles,
+                zero_start ? 1 : 0, lz, sc, hdr, desc, x, Wih, bih, pt_out);
     DEER_HIP(hipGetLastError());
     return DEER_OK;
 }
@@ -833,18 +908,27 @@ size_t gru_step_state_bytes(int B, int T, int D)
     return sizeof(ScanHeader) + align_up(static_cast<size_t>(B) * tps * 3 * D * sizeof(unsigned long long));
 }
 
-int launch_gru_quasi_step(const float *Whh, const float *bhh, const float *pt, const float *s0, float *s_even,
+int launch_gru_quasi_step(const float *Whh, const float *bhh, float *pt, const float *s0, float *s_even,
                           float *s_odd, SolveControl *ctl, int *done, int *iters, int *status, float *resid,
                           float tol, int max_iter, unsigned *res_bits, unsigned *res_tile, int B, int T, int D,
-                          bool zero_start, Linearization lz, const StallCheck &sc, void *state, hipStream_t stream)
+                          bool zero_start, Linearization lz, const StallCheck &sc, void *state, const float *x,
+                          const float *Wih, const float *bih, int M, hipStream_t stream)
 {
     if (B == 0 || T == 0) return DEER_OK;
-    if (D == 64)
-        return launch_gru_step<64>(Whh, bhh, pt, s0, s_even, s_odd, ctl, done, iters, status, resid, tol, max_iter,
-                                   res_bits, res_tile, B, T, zero_start, lz, sc, state, stream);
-    if (D == 32)
-        return launch_gru_step<32>(Whh, bhh, pt, s0, s_even, s_odd, ctl, done, iters, status, resid, tol, max_iter,
-                                   res_bits, res_tile, B, T, zero_start, lz, sc, state, stream);
+    const bool first = x != nullptr;
+    if (first && (!zero_start || M != D || !Wih))
+        return fail(DEER_ERR_INVALID, "fused GRU step: the projecting first iteration needs a zero start and M = D");
+#define DEER_GRU_STEP(DV)                                                                                         \
+    if (D == DV)                                                                                                  \
+        return first ? launch_gru_step<DV, true>(Whh, bhh, pt, s0, s_even, s_odd, ctl, done, iters, status, resid, \
+                                                 tol, max_iter, res_bits, res_tile, B, T, zero_start, lz, sc,       \
+                                                 state, x, Wih, bih, pt, stream)                                    \
+                     : launch_gru_step<DV, false>(Whh, bhh, pt, s0, s_even, s_odd, ctl, done, iters, status,      \
+                                                  resid, tol, max_iter, res_bits, res_tile, B, T, zero_start, lz,   \
+                                                  sc, state, nullptr, nullptr, nullptr, nullptr, stream);
+    DEER_GRU_STEP(64)
+    DEER_GRU_STEP(32)
+#undef DEER_GRU_STEP
     return fail(DEER_ERR_UNSUPPORTED, "fused GRU step needs D = 32 or 64");
 }
 

@@ -971,9 +971,10 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
     DEER_HIP(hipGetLastError());
     const bool fused = fused_gru_step(p, mode);
     const bool zero_start = fused && !init_guess;   // the fused step reads no s^(0) when it is all zeros
-    // from a zero start with inputs as wide as the state, the first fused step
-    // computes the input projection itself (no separate projection launch)
-    const bool proj_in_step = zero_start && p->M == D;
+    // from a zero start and a zero initial state with inputs as wide as the
+    // state, the first fused step computes the input projection itself (no
+    // separate projection launch): every state it reads is zero there
+    const bool proj_in_step = zero_start && !s0 && p->M == D;
     if (init_guess) {
         if (init_guess != traj_out)
             DEER_LAUNCH(copy_kernel, dim3(grid_for(BTD)), dim3(256), 0, stream, traj_out, init_guess, BTD);

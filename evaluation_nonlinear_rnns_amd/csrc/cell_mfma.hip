@@ -306,9 +306,9 @@ __global__ __launch_bounds__(kThreads, 2) void gru_eval_mfma_kernel(
 // The residual of the iterate is reduced per tile into res_tile[tile] (plain
 // stores; the convergence test takes the max over a sequence's tiles).
 //
-// FIRST: the first iteration from a zero start, with the input projection
-// computed here instead of by a separate launch (inputs of width M = D).  The
-// iterate is zero, so W_hh s vanishes and the matrix cores compute the
+// FIRST: the first iteration from a zero start and a zero initial state, with
+// the input projection computed here instead of by a separate launch (inputs of
+// width M = D).  Every state read is zero (s_0 included), so W_hh s vanishes and the matrix cores compute the
 // projection W_ih x_t of the tile instead (W_ih as the B operands, the rows of
 // x as the A operands); the lane adds b_ih, writes its values to the tiled
 // projection that the later iterations read, and evaluates the gates with
@@ -916,8 +916,9 @@ int launch_gru_quasi_step(const float *Whh, const float *bhh, float *pt, const f
 {
     if (B == 0 || T == 0) return DEER_OK;
     const bool first = x != nullptr;
-    if (first && (!zero_start || M != D || !Wih))
-        return fail(DEER_ERR_INVALID, "fused GRU step: the projecting first iteration needs a zero start and M = D");
+    if (first && (!zero_start || s0 || M != D || !Wih))
+        return fail(DEER_ERR_INVALID,
+                    "fused GRU step: the projecting first iteration needs a zero start, no s0 and M = D");
 #define DEER_GRU_STEP(DV)                                                                                         \
     if (D == DV)                                                                                                  \
         return first ? launch_gru_step<DV, true>(Whh, bhh, pt, s0, s_even, s_odd, ctl, done, iters, status, resid, \

@@ -484,8 +484,8 @@ size_t gru_step_state_bytes(int B, int T, int D);
 // The workgroup that finishes last also runs finalize_iteration(), so one
 // launch is a whole iteration.  Residual maxima go to res_bits (one word per
 // sequence, zero on entry) for up to 256 sequences, else to res_tile.  zero_start: the iterate s^(0) is all zeros and
-// is not read from memory at iteration 0.  With x non-null (zero_start, inputs of
-// width M = D, the first iteration only) the launch computes the tiled input
+// is not read from memory at iteration 0.  With x non-null (zero_start, s0 null,
+// inputs of width M = D, the first iteration only) the launch computes the tiled input
 // projection W_ih x + b_ih itself, writes it to `pt`, and evaluates the first
 // iterate from it; otherwise `pt` holds the projection already.
 int launch_gru_quasi_step(const float *Whh, const float *bhh, float *pt, const float *s0, float *s_even,

@@ -92,6 +92,32 @@ def test_gru_solve_matches_oracle(orc, B, T, D, M):
     assert np.all(rel_linf(got, ref) <= TOL)
 
 
+@pytest.mark.parametrize("with_s0", [False, True])
+@pytest.mark.parametrize("B,T,D", [(2, 300, 64), (3, 150, 32), (2, 65, 64)])
+def test_gru_fused_first_iterates_match_oracle(orc, B, T, D, with_s0):
+    """tol < 0 runs exactly max_iter = 0, 1, 2, 3 iterations of the fused GRU
+    step (inputs as wide as the state): the returned iterate is the oracle's
+    float32 iterate after as many steps.  Without s0 the first launch also
+    computes the input projection; with s0 (the state before position 0 is not
+    zero) the projection is a launch of its own."""
+    p = I.gru_problem(1400 + T + D, B, T, D, D, bias_std=0.3, s0_std=0.5)
+    dev = device()
+    cell = deer.cell_from_problem(p, dev)
+    x = torch.from_numpy(p["x"]).to(dev)
+    s0n = p["s0"] if with_s0 else None
+    s0 = torch.from_numpy(p["s0"]).to(dev) if with_s0 else None
+    oc = orc.Cell.from_problem(p)
+    for k in (0, 1, 2, 3):
+        log(f"deer_solve gru diag B={B} T={T} D={D} s0={with_s0} tol<0 max_iter={k}")
+        traj, iters, resid, status, rc = deer.deer_solve(cell, x, s0, mode="diag", tol=-1.0, max_iter=k)
+        torch.cuda.synchronize()
+        otraj, _, ores, _ = orc.newton(oc, p["x"], s0n, mode="diag", tol=-1.0, max_iter=k, precision="f32")
+        assert np.all(iters == k) and rc == deer.DEER_NOT_CONVERGED
+        got = traj.cpu().numpy()
+        assert np.abs(got - otraj).max() <= 1e-4 * max(1.0, np.abs(otraj).max()), (k, np.abs(got - otraj).max())
+        assert np.allclose(resid, ores, rtol=1e-3, atol=1e-6), (k, resid, ores)
+
+
 @pytest.mark.parametrize("cell,mode,damping,D,T", [
     ("tanh", "jacobi", 0.0, 8, 300), ("tanh", "picard", 0.0, 4, 60), ("tanh", "dense", 0.3, 16, 500),
     ("tanh", "diag", 0.5, 32, 400), ("tanh", "dense", 1.0, 8, 200), ("tanh", "picard", 0.0, 32, 40),

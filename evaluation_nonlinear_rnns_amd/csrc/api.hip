@@ -38,11 +38,11 @@ int hip_fail(hipError_t e, const char *what)
 thread_local ProfLaunch g_prof_launch;
 
 namespace {
-constexpr int kProfKinds = 4;
+constexpr int kProfKinds = 5;
 std::atomic<int> g_prof_enabled{0};
 std::mutex g_prof_mu;
-long long g_prof_launches[kProfKinds] = {0, 0, 0, 0};
-double g_prof_ms[kProfKinds] = {0, 0, 0, 0};
+long long g_prof_launches[kProfKinds] = {0, 0, 0, 0, 0};
+double g_prof_ms[kProfKinds] = {0, 0, 0, 0, 0};
 
 // Timing events are reused across calls (one pool per host thread and
 // device, since an event belongs to the device that was current when it was
@@ -77,15 +77,23 @@ void unpool_event(hipEvent_t e)
     else (void)hipEventDestroy(e);
 }
 
-// Event pairs recorded around launches of one deer_solve call.
+// Event pairs recorded around launches of one deer_solve call.  A sub-timing
+// (mark_next) shares its scope's start event, which only the scope's own mark
+// owns and returns to the pool.
 struct ProfScope {
+    struct Mark {
+        int kind;
+        hipEvent_t start, stop;
+        bool own_start;
+    };
     bool on = false;
     hipStream_t stream = nullptr;
-    std::vector<std::pair<int, std::pair<hipEvent_t, hipEvent_t>>> marks;
+    std::vector<Mark> marks;
     int open_kind = -1;
     hipEvent_t open_start = nullptr;
+    static thread_local ProfScope *current;
 
-    explicit ProfScope(hipStream_t s) : on(g_prof_enabled.load() != 0), stream(s) {}
+    explicit ProfScope(hipStream_t s) : on(g_prof_enabled.load() != 0), stream(s) { current = this; }
     // The launches between begin and end record the pair themselves (DEER_LAUNCH).
     void begin(int kind)
     {
@@ -95,14 +103,23 @@ struct ProfScope {
         if (!pool_event(&e1)) { unpool_event(e0); on = false; return; }
         open_kind = kind;
         open_start = e0;
-        g_prof_launch = ProfLaunch{e0, e1};
+        g_prof_launch = ProfLaunch{e0, e1, nullptr};
     }
     void end()
     {
         if (!on || open_kind < 0) return;
-        marks.push_back({open_kind, {open_start, g_prof_launch.stop}});
-        g_prof_launch = ProfLaunch{};
+        marks.push_back({open_kind, open_start, g_prof_launch.stop, true});
+        g_prof_launch = ProfLaunch{};             // also drops a sub-timing no launch consumed
         open_kind = -1;
+    }
+    // From the open scope's start to the end of its next launch, as `kind`.
+    void mark_next(int kind)
+    {
+        if (!on || open_kind < 0 || !g_prof_launch.start || g_prof_launch.mark) return;
+        hipEvent_t e;
+        if (!pool_event(&e)) return;
+        g_prof_launch.mark = e;
+        marks.push_back({kind, open_start, e, false});
     }
     // Call after the stream has been synchronised.  Only the first limit[k]
     // launches of each kind did work; launches enqueued after convergence exit
@@ -110,13 +127,13 @@ struct ProfScope {
     void collect(const long long limit[kProfKinds])
     {
         std::lock_guard<std::mutex> lock(g_prof_mu);
-        long long seen[kProfKinds] = {0, 0, 0, 0};
+        long long seen[kProfKinds] = {0, 0, 0, 0, 0};
         for (auto &m : marks) {
-            if (seen[m.first]++ >= limit[m.first]) continue;
+            if (seen[m.kind]++ >= limit[m.kind]) continue;
             float ms = 0.0f;
-            if (hipEventElapsedTime(&ms, m.second.first, m.second.second) == hipSuccess) {
-                g_prof_launches[m.first] += 1;
-                g_prof_ms[m.first] += ms;
+            if (hipEventElapsedTime(&ms, m.start, m.stop) == hipSuccess) {
+                g_prof_launches[m.kind] += 1;
+                g_prof_ms[m.kind] += ms;
             }
         }
         release();
@@ -127,8 +144,8 @@ struct ProfScope {
     void release()
     {
         for (auto &m : marks) {
-            unpool_event(m.second.first);
-            unpool_event(m.second.second);
+            if (m.own_start) unpool_event(m.start);
+            unpool_event(m.stop);
         }
         marks.clear();
     }
@@ -141,8 +158,10 @@ struct ProfScope {
         }
         g_prof_launch = ProfLaunch{};
         release();
+        if (current == this) current = nullptr;
     }
 };
+thread_local ProfScope *ProfScope::current = nullptr;
 
 // Pinned host memory of one solve call: the polling words (all-done and
 // escalate, two slots) and the staging buffer for the per-sequence results
@@ -624,6 +643,12 @@ int check_diag_scan_args(const float *a, const float *b, const float *s, int B, 
 }
 
 }  // namespace
+
+void prof_mark_next(int kind)
+{
+    if (ProfScope::current) ProfScope::current->mark_next(kind);
+}
+
 }  // namespace deer
 
 using namespace deer;
@@ -881,7 +906,7 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
         const hipError_t se = hipStreamSynchronize(stream);
         if (rc) return rc;
         if (se != hipSuccess) return hip_fail(se, "hipStreamSynchronize(deer_solve)");
-        const long long limit[kProfKinds] = {1, 0, 0, 0};
+        const long long limit[kProfKinds] = {1, 0, 0, 0, 0};
         prof.collect(limit);
         bool any_nc = false, any_stall = false;
         for (int b = 0; b < B; ++b) {
@@ -947,7 +972,7 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
             (void)hipStreamSynchronize(stream);
         }
         if (rc) return rc;
-        const long long limit[kProfKinds] = {1, can_escalate_once ? 1 : 0, 1, 0};
+        const long long limit[kProfKinds] = {1, can_escalate_once ? 1 : 0, 1, 0, 0};
         prof.collect(limit);
         if (abort_flag) return fail(DEER_ERR_DEVICE, "deer_solve: a wait of the one-launch solve hit its bound");
         bool any_nc = false;
@@ -998,6 +1023,17 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
     const int *all_done = &L.ctl->all_done;
     const FrontOut fo{sc.front, tol};
     bool first_step = true;
+    // dense tanh at D = 32 in float: the replay of iteration i evaluates the
+    // cell on s^(i+1), so iteration i + 1 starts at its convergence test
+    bool evaluated = false;
+    ReplayEval rev;
+    rev.p = L.proj;
+    rev.lin = L.lin;
+    rev.bout = L.bvec;
+    rev.res_bits = L.res_bits;
+    rev.front = fo.front;
+    rev.tol = tol;
+    rev.shrink = lz.shrink;
     auto enqueue_iteration = [&]() -> int {
         int r;
         StallCheck sci = sc;
@@ -1012,15 +1048,17 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
             prof.end();
             return r;
         }
-        prof.begin(0);
-        if (gru)
-            r = launch_gru_eval(p->W, p->b2, L.proj, s0, traj_out, L.buf1, sel, L.done, all_done, L.lin, L.bvec,
-                                L.res_bits, B, T, D, p->M, lz, fo, stream);
-        else
-            r = launch_tanh_eval(p->W, L.proj, s0, traj_out, L.buf1, sel, L.done, all_done, L.lin, L.bvec,
-                                 L.res_bits, B, T, D, dense, lz, fo, stream);
-        prof.end();
-        if (r) return r;
+        if (!evaluated) {
+            prof.begin(0);
+            if (gru)
+                r = launch_gru_eval(p->W, p->b2, L.proj, s0, traj_out, L.buf1, sel, L.done, all_done, L.lin,
+                                    L.bvec, L.res_bits, B, T, D, p->M, lz, fo, stream);
+            else
+                r = launch_tanh_eval(p->W, L.proj, s0, traj_out, L.buf1, sel, L.done, all_done, L.lin, L.bvec,
+                                     L.res_bits, B, T, D, dense, lz, fo, stream);
+            prof.end();
+            if (r) return r;
+        }
         prof.begin(3);
         DEER_LAUNCH(check_kernel, dim3(1), dim3(256), 0, stream, L.ctl, L.res_bits, nullptr, 0, L.done, L.iters,
                            L.status, L.resid, B, tol, max_iter, sci);
@@ -1029,9 +1067,11 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
         prof.begin(1);
         if (diag_blocks(mode))
             r = launch_diag_scan(L.lin, L.bvec, s0, traj_out, L.buf1, sel, L.done, all_done, B, T, D, L.scan, stream);
-        else
+        else {
+            evaluated = !gru && dense_scan_evaluates(D, scan_f64);
             r = launch_dense_scan(nullptr, L.lin, p->W, L.bvec, s0, traj_out, L.buf1, sel, L.done, all_done, B, T, D,
-                                  scan_f64, L.scan, stream);
+                                  scan_f64, L.scan, stream, evaluated ? &rev : nullptr);
+        }
         prof.end();
         return r;
     };
@@ -1061,7 +1101,7 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
     {
         int last = 0;
         for (int b = 0; b < B; ++b) last = std::max(last, iters_out[b]);
-        const long long limit[kProfKinds] = {last + 1, last, 1, last + 1};
+        const long long limit[kProfKinds] = {last + 1, last, 1, last + 1, last};
         prof.collect(limit);
     }
     if (abort_flag) return fail(DEER_ERR_DEVICE, "deer_solve: the scan look-back wait hit its bound");
@@ -1205,7 +1245,7 @@ int deer_solve_broyden(const deer_cell_params_t *p, const float *x, const float 
     {
         int last = 0;
         for (int b = 0; b < B; ++b) last = std::max(last, iters_out[b]);
-        const long long limit[kProfKinds] = {last + 1, last, 1, last + 1};
+        const long long limit[kProfKinds] = {last + 1, last, 1, last + 1, last};
         prof.collect(limit);
     }
     bool any_nc = false;

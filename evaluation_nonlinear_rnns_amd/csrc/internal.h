@@ -54,15 +54,23 @@ struct Carve {
 struct ProfLaunch {
     hipEvent_t start = nullptr;
     hipEvent_t stop = nullptr;
+    hipEvent_t mark = nullptr;   // when set: the next launch records this stop event instead (a sub-timing)
 };
 extern thread_local ProfLaunch g_prof_launch;
+// Times the next launch of the open profiling scope as kernel class `kind`
+// too (from the scope's start, so it must be the scope's first launch).
+void prof_mark_next(int kind);
+constexpr int kProfCompose = 4;   // the dense scan's chunk-compose launch
 
 #define DEER_LAUNCH(kernel, grid, block, shmem, stream, ...)                                                     \
     do {                                                                                                      \
         if (::deer::g_prof_launch.stop) {                                                                     \
             hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, ::deer::g_prof_launch.start,            \
-                                  ::deer::g_prof_launch.stop, 0, __VA_ARGS__);                                \
+                                  ::deer::g_prof_launch.mark ? ::deer::g_prof_launch.mark                     \
+                                                             : ::deer::g_prof_launch.stop,                    \
+                                  0, __VA_ARGS__);                                                            \
             ::deer::g_prof_launch.start = nullptr;                                                            \
+            ::deer::g_prof_launch.mark = nullptr;                                                             \
         } else {                                                                                              \
             hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                              \
         }                                                                                                     \
@@ -416,10 +424,29 @@ size_t dense_scan_state_bytes(int B, int T, int D, bool f64 = false);
 // Dense scan s_t = A_t s_{t-1} + b_t.  Either A (materialised [B,T,D,D]) or
 // the factored form A_t = diag(d_t) W (d [B,T,D], W [D,D]) is given.  f64:
 // products, offsets, carries and replayed states accumulate in double.
+//
+// `ev` (factored form only; null: none) also evaluates the tanh cell
+// f_t = tanh(W s_{t-1} + p_t) on the solved trajectory while the replay
+// forms W s_{t-1}: the next iteration's d_t = shrink (1 - f_t^2) and
+// b_t = f_t - d_t (W s_{t-1}) overwrite d and b in place, and the residual
+// |s_t - f_t| goes to res_bits (per-sequence max on float bits) and, with
+// front, the first violating position (atomic min).  dense_scan_evaluates()
+// says whether a shape takes that path; otherwise `ev` is ignored and the
+// caller runs the evaluation itself.
+struct ReplayEval {
+    const float *p = nullptr;       // [B,T,D] input projection U x_t + b
+    float *lin = nullptr;           // = d
+    float *bout = nullptr;          // = b
+    unsigned *res_bits = nullptr;   // [B]
+    unsigned *front = nullptr;      // [B] or null
+    float tol = 0.0f;
+    float shrink = 1.0f;
+};
+bool dense_scan_evaluates(int D, bool f64);
 int launch_dense_scan(const float *A, const float *d, const float *W, const float *b,
                       const float *s0, float *out0, float *out1, const int *out_sel,
                       const int *skip, const int *all_done, int B, int T, int D, bool f64, void *state,
-                      hipStream_t stream);
+                      hipStream_t stream, const ReplayEval *ev = nullptr);
 
 // ---------------------------------------------------------- cell kernels
 // p = U x + bias for every position, O outputs.  `tiled` writes the layout

@@ -750,12 +750,25 @@ __device__ __forceinline__ void stage_chunk64(const float *__restrict__ dv, cons
 // D = 32, float32: the replay on the offset chain's row layout (two blocks of
 // 16, DPP row rotations, one exchange per step, alternating A / B layouts);
 // each step's state is written by both rows that hold a block.
+//
+// EVAL: each step's y = W s_{t-1} is also the tanh cell's pre-activation less
+// the projection, so the next iteration's evaluation rides along: f_t =
+// tanh(y + p_t), d_t = shrink (1 - f_t^2) and b_t = f_t - d_t y overwrite the
+// chunk's d and b rows (already staged in LDS; no other workgroup reads them),
+// and |s_t - f_t| feeds the residual maximum and the front.  Each block of a
+// step sits in two rows, so the four (step, block) results of a pair of steps
+// are spread over the four rows -- row 1: (A step, block 0), row 2: (A step,
+// block 1), row 0: (B step, block 0), row 3: (B step, block 1) -- and every
+// lane evaluates once per pair.  The projection of the lane's (step, channel)
+// is fetched four pairs ahead into a register ring.
+template <bool EVAL>
 __global__ __launch_bounds__(64) void dense_replay_dpp32_kernel(
-    const float *__restrict__ dv, const float *__restrict__ W, const float *__restrict__ bv,
-    const float *__restrict__ carry, const int *__restrict__ skip, const int *__restrict__ all_done, int T, int L,
-    int nchunk, float *out0, float *out1, const int *__restrict__ out_sel)
+    const float *dv, const float *__restrict__ W, const float *bv, const float *__restrict__ carry,
+    const int *__restrict__ skip, const int *__restrict__ all_done, int T, int L, int nchunk, float *out0,
+    float *out1, const int *__restrict__ out_sel, ReplayEval ev)
 {
     constexpr int D = 32;
+    constexpr int RP = 4;                                            // projection ring depth (pairs of steps)
     __shared__ float dsm[64 * D], bsm[64 * D];
     if (all_done && *all_done) return;
     const long long q = blockIdx.x;
@@ -764,13 +777,23 @@ __global__ __launch_bounds__(64) void dense_replay_dpp32_kernel(
     const int t0 = c * L, n = min(L, T - t0);
     const size_t base = (static_cast<size_t>(bseq) * T + t0) * D;
     stage_chunk64(dv, bv, base, n * D, D, dsm, bsm);
-    __syncthreads();
 
     const int lane = threadIdx.x, r = lane >> 4, m = lane & 15;
+    const int KA = r & 1, IA = r >> 1, KB = r >> 1, IB = r & 1;
+    const bool useB = r == 0 || r == 3;                              // evaluates the B step of each pair
+    const int ech = useB ? 16 * IB + m : 16 * IA + m;                // its channel
+    const int eofs = useB ? 1 : 0;                                   // its step within the pair
+    const float *pc = EVAL ? ev.p + base : nullptr;
+    float pr[RP];
+    if (EVAL) {
+#pragma unroll
+        for (int k = 0; k < RP; ++k) pr[k] = pc[min(2 * k + eofs, n - 1) * D + ech];
+    }
+    __syncthreads();
+
     int src[16];
     src[0] = m;
     RowRotations::sources(m, src);
-    const int KA = r & 1, IA = r >> 1, KB = r >> 1, IB = r & 1;
     float wA[16], wB[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
@@ -784,22 +807,68 @@ __global__ __launch_bounds__(64) void dense_replay_dpp32_kernel(
     };
     float *out = ((out_sel && (*out_sel & 1)) ? out1 : out0) + base;
     float x = carry[static_cast<size_t>(q) * D + 16 * KA + m];      // carried-in state, A layout
+    // step s (A layout when even, B when odd): y = W s_{t-1} on the lane's
+    // output channel, then s_t into x; returns y
+    auto step = [&](int s, bool odd) -> float {
+        float y = contract(x, odd ? wB : wA);
+        y += __shfl_xor(y, odd ? 32 : 16, 64);
+        const int ch = odd ? 16 * IB + m : 16 * IA + m;
+        x = dsm[s * D + ch] * y + bsm[s * D + ch];
+        out[s * D + ch] = x;
+        return y;
+    };
     int s = 0;
-    for (; s + 1 < n; s += 2) {
-        float y = contract(x, wA);
-        y += __shfl_xor(y, 16, 64);
-        x = dsm[s * D + 16 * IA + m] * y + bsm[s * D + 16 * IA + m];
-        out[s * D + 16 * IA + m] = x;
-        y = contract(x, wB);
-        y += __shfl_xor(y, 32, 64);
-        x = dsm[(s + 1) * D + 16 * IB + m] * y + bsm[(s + 1) * D + 16 * IB + m];
-        out[(s + 1) * D + 16 * IB + m] = x;
-    }
-    if (s < n) {
-        float y = contract(x, wA);
-        y += __shfl_xor(y, 16, 64);
-        x = dsm[s * D + 16 * IA + m] * y + bsm[s * D + 16 * IA + m];
-        out[s * D + 16 * IA + m] = x;
+    if (EVAL) {
+        float *lout = ev.lin + base, *bout = ev.bout + base;
+        unsigned rmax = 0u, fmin = kNoFront;
+        auto evaluate = [&](float y, float st, float pv, int se) {
+            const float f = tanhf(y + pv);
+            const float dd = ev.shrink * (1.0f - f * f);
+            lout[se * D + ech] = dd;
+            bout[se * D + ech] = f - dd * y;
+            const float ra = fabsf(st - f);
+            rmax = max(rmax, __float_as_uint(ra));
+            fmin = min(fmin, front_of(ra, ev.tol, t0 + se));
+        };
+        for (; s + 2 * RP <= n; s += 2 * RP) {
+#pragma unroll
+            for (int k = 0; k < RP; ++k) {
+                const int sa = s + 2 * k;
+                const float ya = step(sa, false);
+                const float xa = x;
+                const float yb = step(sa + 1, true);
+                evaluate(useB ? yb : ya, useB ? x : xa, pr[k], sa + eofs);
+                // refill the slot with the same pair of the next ring round (clamped in bounds)
+                pr[k] = pc[min(sa + 2 * RP + eofs, n - 1) * D + ech];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < RP; ++k) {
+            const int sa = s + 2 * k;
+            if (sa + 1 < n) {
+                const float ya = step(sa, false);
+                const float xa = x;
+                const float yb = step(sa + 1, true);
+                evaluate(useB ? yb : ya, useB ? x : xa, pr[k], sa + eofs);
+            } else if (sa < n) {                                     // a last lone A step
+                const float ya = step(sa, false);
+                if (!useB) evaluate(ya, x, pr[k], sa);
+            }
+        }
+        for (int o = 32; o > 0; o >>= 1) {
+            rmax = max(rmax, static_cast<unsigned>(__shfl_xor(static_cast<int>(rmax), o, 64)));
+            fmin = min(fmin, static_cast<unsigned>(__shfl_xor(static_cast<int>(fmin), o, 64)));
+        }
+        if (lane == 0) {
+            if (rmax) atomicMax(ev.res_bits + bseq, rmax);
+            if (ev.front && fmin != kNoFront) atomicMin(ev.front + bseq, fmin);
+        }
+    } else {
+        for (; s + 1 < n; s += 2) {
+            step(s, false);
+            step(s + 1, true);
+        }
+        if (s < n) step(s, false);
     }
 }
 
@@ -951,13 +1020,15 @@ int pick_dp(int D) { return D <= 4 ? 4 : D <= 8 ? 8 : D <= 16 ? 16 : D <= 32 ? 3
 template <int DP, class ACC>
 int launch_dense_dp(const float *A, const float *d, const float *W, const float *b, const float *s0, float *out0,
                     float *out1, const int *out_sel, const int *skip, const int *all_done, const DenseScanPlan &pl,
-                    ACC *Pagg, ACC *Bagg, ACC *carry, float *Pgrp, float *Bgrp, hipStream_t stream)
+                    ACC *Pagg, ACC *Bagg, ACC *carry, float *Pgrp, float *Bgrp, hipStream_t stream,
+                    const ReplayEval *ev)
 {
     constexpr int G = 64 / DP;
     const long long nq = static_cast<long long>(pl.B) * pl.nchunk;
     const long long waves = (nq + G - 1) / G;
     const unsigned blocks = static_cast<unsigned>((waves + 3) / 4);
     const bool f64 = sizeof(ACC) == 8;
+    prof_mark_next(kProfCompose);
     if (d && DP == 32 && pl.D == 32 && !f64) {
         DEER_LAUNCH(dense_agg_mfma32_kernel, dim3(static_cast<unsigned>(nq)), dim3(kAggThreads), 0, stream, d, W,
                            b, skip, all_done, pl.T, pl.chunk_len, pl.nchunk, reinterpret_cast<float *>(Pagg),
@@ -989,9 +1060,14 @@ int launch_dense_dp(const float *A, const float *d, const float *W, const float 
                            Pagg, Bagg, s0, skip, all_done, pl.B, pl.D, pl.nchunk, carry);
     DEER_HIP(hipGetLastError());
     if (d && DP == 32 && pl.D == 32 && !f64) {
-        DEER_LAUNCH(dense_replay_dpp32_kernel, dim3(static_cast<unsigned>(nq)), dim3(64), 0, stream, d, W, b,
-                           reinterpret_cast<const float *>(carry), skip, all_done, pl.T, pl.chunk_len, pl.nchunk, out0,
-                           out1, out_sel);
+        if (ev)
+            DEER_LAUNCH(dense_replay_dpp32_kernel<true>, dim3(static_cast<unsigned>(nq)), dim3(64), 0, stream, d,
+                        W, b, reinterpret_cast<const float *>(carry), skip, all_done, pl.T, pl.chunk_len, pl.nchunk,
+                        out0, out1, out_sel, *ev);
+        else
+            DEER_LAUNCH(dense_replay_dpp32_kernel<false>, dim3(static_cast<unsigned>(nq)), dim3(64), 0, stream, d,
+                        W, b, reinterpret_cast<const float *>(carry), skip, all_done, pl.T, pl.chunk_len, pl.nchunk,
+                        out0, out1, out_sel, ReplayEval{});
     } else if (d) {
         const size_t lds = static_cast<size_t>(pl.chunk_len) * pl.D * 2 * sizeof(float);
         if (pl.D == DP && CarryGeom<DP, ACC>::G * DP == 64)       // every lane owns a row
@@ -1013,7 +1089,7 @@ int launch_dense_dp(const float *A, const float *d, const float *W, const float 
 template <class ACC>
 int launch_dense_acc(const float *A, const float *d, const float *W, const float *b, const float *s0, float *out0,
                      float *out1, const int *out_sel, const int *skip, const int *all_done, const DenseScanPlan &pl,
-                     void *state, hipStream_t stream)
+                     void *state, hipStream_t stream, const ReplayEval *ev)
 {
     const size_t nq = static_cast<size_t>(pl.B) * pl.nchunk;
     const int D = pl.D;
@@ -1027,11 +1103,11 @@ int launch_dense_acc(const float *A, const float *d, const float *W, const float
         Bgrp = cv.take<float>(static_cast<size_t>(pl.B) * kTlGroups * D);
     }
     switch (pick_dp(D)) {
-    case 4: return launch_dense_dp<4, ACC>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, Pagg, Bagg, carry, Pgrp, Bgrp, stream);
-    case 8: return launch_dense_dp<8, ACC>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, Pagg, Bagg, carry, Pgrp, Bgrp, stream);
-    case 16: return launch_dense_dp<16, ACC>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, Pagg, Bagg, carry, Pgrp, Bgrp, stream);
-    case 32: return launch_dense_dp<32, ACC>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, Pagg, Bagg, carry, Pgrp, Bgrp, stream);
-    default: return launch_dense_dp<64, ACC>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, Pagg, Bagg, carry, Pgrp, Bgrp, stream);
+    case 4: return launch_dense_dp<4, ACC>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, Pagg, Bagg, carry, Pgrp, Bgrp, stream, ev);
+    case 8: return launch_dense_dp<8, ACC>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, Pagg, Bagg, carry, Pgrp, Bgrp, stream, ev);
+    case 16: return launch_dense_dp<16, ACC>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, Pagg, Bagg, carry, Pgrp, Bgrp, stream, ev);
+    case 32: return launch_dense_dp<32, ACC>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, Pagg, Bagg, carry, Pgrp, Bgrp, stream, ev);
+    default: return launch_dense_dp<64, ACC>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, Pagg, Bagg, carry, Pgrp, Bgrp, stream, ev);
     }
 }
 
@@ -1068,13 +1144,18 @@ size_t dense_scan_state_bytes(int B, int T, int D, bool f64)
 
 int launch_dense_scan(const float *A, const float *d, const float *W, const float *b, const float *s0, float *out0,
                       float *out1, const int *out_sel, const int *skip, const int *all_done, int B, int T, int D,
-                      bool f64, void *state, hipStream_t stream)
+                      bool f64, void *state, hipStream_t stream, const ReplayEval *ev)
 {
     if (B == 0 || T == 0) return DEER_OK;
     const DenseScanPlan pl = dense_scan_plan(B, T, D);
+    if (!d || !dense_scan_evaluates(D, f64)) ev = nullptr;
     if (f64)
-        return launch_dense_acc<double>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, state, stream);
-    return launch_dense_acc<float>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, state, stream);
+        return launch_dense_acc<double>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, state, stream,
+                                        nullptr);
+    return launch_dense_acc<float>(A, d, W, b, s0, out0, out1, out_sel, skip, all_done, pl, state, stream, ev);
 }
+
+// the replay kernels that evaluate the cell on the fly (factored leaves only)
+bool dense_scan_evaluates(int D, bool f64) { return D == 32 && !f64; }
 
 }  // namespace deer

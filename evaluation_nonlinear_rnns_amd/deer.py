@@ -451,7 +451,7 @@ def deer_profile_read(which: int) -> Tuple[int, float]:
     return int(n.value), float(ms.value)
 
 
-PROFILE_EVAL, PROFILE_SCAN, PROFILE_PROJECTION, PROFILE_CHECK = 0, 1, 2, 3
+PROFILE_EVAL, PROFILE_SCAN, PROFILE_PROJECTION, PROFILE_CHECK, PROFILE_COMPOSE = 0, 1, 2, 3, 4
 
 
 def bandwidth_probe(src, dst, stream=None) -> None:

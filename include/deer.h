@@ -360,7 +360,10 @@ int linear_scan_dplr(float alpha, const float *U, const float *V, const float *c
  * kernel class and accumulates the elapsed time; reading returns the number of
  * launches timed and their summed milliseconds and resets the counters.
  *   which: 0 = cell evaluation (f and Jacobian), 1 = linear scan,
- *          2 = input projection, 3 = convergence check.  deer_solve_broyden
+ *          2 = input projection, 3 = convergence check, 4 = the dense
+ *          scan's chunk compose alone (a part of 1; dense tanh at D = 32 in
+ *          float also evaluates the cell for the next iteration inside 1,
+ *          so 0 counts only the first evaluation there).  deer_solve_broyden
  *          times its cell evaluation (0), block updates with the compressed
  *          scan (1), projection (2) and check (3) the same way.  Solves that
  *          run in one launch count it as 0 (the dense one-launch solve its

@@ -171,7 +171,7 @@ def test_solve_argument_checks(deer):
 
 def test_profile_counters_read_and_reset(deer):
     deer.deer_profile_enable(False)
-    for k in range(4):
+    for k in range(5):
         n, ms = deer.deer_profile_read(k)
         assert n >= 0 and ms >= 0.0
         assert deer.deer_profile_read(k) == (0, 0.0)

@@ -22,7 +22,7 @@ TOL = 1e-4
 def _solve_counted(cell, x, s0, **kw):
     """deer_solve, and how many launches of the solve kernel (counter 0) it made."""
     deer.deer_profile_enable(True)
-    for k in range(4):
+    for k in range(5):
         deer.deer_profile_read(k)
     try:
         res = deer.deer_solve(cell, x, s0, **kw)

@@ -61,7 +61,8 @@ def _run(orc, p, mode, tol, max_iter, s0=True, check_iters=True, init=None, scan
 @pytest.mark.parametrize("mode", ["dense", "diag"])
 @pytest.mark.parametrize("B,T,D,M,gain", [(2, 100, 4, 3, 0.5), (3, 777, 8, 8, 0.8), (2, 1000, 16, 16, 0.9),
                                           (2, 500, 32, 32, 0.7), (1, 300, 5, 2, 0.6), (2, 200, 64, 64, 0.6),
-                                          (3, 1000, 2, 3, 0.9), (2, 300, 32, 7, 0.7), (3, 31, 32, 32, 0.7)])
+                                          (3, 1000, 2, 3, 0.9), (2, 300, 32, 7, 0.7), (3, 31, 32, 32, 0.7),
+                                          (2, 195, 32, 32, 0.7), (2, 64, 32, 32, 0.8), (3, 5, 32, 32, 0.7)])
 def test_tanh_solve_matches_oracle(orc, mode, B, T, D, M, gain, multi_launch):
     p = I.tanh_problem(500 + T + D, B, T, D, M, gain=gain, bias_std=0.3, s0_std=0.5)
     log(f"deer_solve tanh {mode} B={B} T={T} D={D} M={M} multi_launch={multi_launch}")
@@ -501,6 +502,24 @@ def test_gain2_float32_stall_then_escalation(orc):
     print(f"float32 + escalation: iters {i2.tolist()} status {st2.tolist()}")
     assert rc2 == deer.DEER_OK and np.all(st2 == 0)
     assert np.all(_certify(orc, p, t2.cpu().numpy(), w.tol))
+
+
+def test_dense_d32_gain2_escalation_certified(orc):
+    """Dense DEER at D = 32 (the replay evaluates the cell for the next
+    iteration) at gain 2 in float32 with a short stall window: whether or not
+    a stall hands the solve to double accumulation part-way (after which the
+    evaluation runs as its own launch again), every sequence converges to a
+    trajectory the oracle certifies."""
+    p = I.tanh_problem(4242, 2, 1500, 32, 32, gain=2.0)
+    dev = device()
+    cell = deer.cell_from_problem(p, dev)
+    x = torch.from_numpy(p["x"]).to(dev)
+    log("deer_solve tanh dense D=32 gain 2 float32, stall window 4")
+    traj, iters, resid, status, rc = deer.deer_solve(cell, x, None, mode="dense", tol=1e-5, max_iter=1500,
+                                                     stall_window=4)
+    print(f"D=32 gain 2: iters {iters.tolist()} status {status.tolist()}")
+    assert rc == deer.DEER_OK and np.all(status == 0)
+    assert np.all(_certify(orc, p, traj.cpu().numpy(), 1e-5))
 
 
 def test_gain2_damped_float32_converges_certified(orc):

@@ -289,12 +289,14 @@ __device__ inline void finalize_iteration(SolveControl *ctl, unsigned *res_bits,
 // ------------------------------------------------------ diagonal scan state
 // Look-back state kept in a workspace between launches.  Zero-filled once by
 // the caller; every launch leaves done = 0 and advances epoch.
+constexpr int kTicketGroups = 8;   // one tile counter per group of workgroups (see the scans)
 struct ScanHeader {
-    unsigned reserved;
     unsigned done;     // workgroups finished in the current launch
     unsigned epoch;    // tags descriptors of the current launch
     unsigned abort;    // set if a bounded wait gave up (should never happen)
-    unsigned pad[60];
+    unsigned pad0;
+    unsigned ticket[kTicketGroups];   // next tile of each group to hand out in the current launch
+    unsigned pad[52];
 };
 static_assert(sizeof(ScanHeader) == 256, "header is one alignment unit");
 

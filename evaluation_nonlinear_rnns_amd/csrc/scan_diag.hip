@@ -7,9 +7,14 @@
 // the later map acting on the left (same page, appendix C.2).
 //
 // Layout [B, T, D], D fastest.  The grid is persistent: one workgroup per
-// compute unit (more if occupancy allows), each walking the chunks
-// blockIdx.x, blockIdx.x + G, ... in order.  A chunk is a tile of CH
-// channels x L time steps of one sequence:
+// compute unit (more if occupancy allows).  The chains (one sequence's CH
+// channels) are split into ngrp groups (chain c in group c % ngrp), and so are
+// the workgroups (workgroup g in group g % ngrp, which keeps a group on one XCD
+// when ngrp divides the XCD count).  A group's chunks are numbered time-major
+// over its chains and handed out in index order from the group's counter in
+// the header, each workgroup drawing its next chunk while it works on the
+// current one.  A chunk is a tile of CH channels x L time steps of one
+// sequence:
 //   1. every thread loads LT consecutive steps of VEC channels into registers
 //      (non-temporal 16-byte loads; a wavefront reads whole contiguous row
 //      segments, 1 KB for 256-channel tiles) and folds them into one affine
@@ -25,17 +30,18 @@
 //      streams s out (non-temporal stores).
 // a and b are read once and s written once: 12 bytes per element.  Holding
 // 32 steps per thread keeps about 1 KB of loads in flight per thread, which
-// is what it takes to approach the HBM roofline on this part; with one
-// workgroup per compute unit there are no per-chunk atomics at all.
+// is what it takes to approach the HBM roofline on this part.
 //
 // Look-back descriptors are 64-bit words holding a float and a 32-bit tag
 // (epoch * 4 + kind), written and read with agent-scope atomics, so a word is
-// valid on its own and no fences are needed.  Forward progress: a workgroup
-// only waits on chunks with smaller indices, each workgroup takes its chunks
-// in increasing order, and all workgroups of the persistent grid are resident
-// together, so the smallest waiting chunk's predecessors are always done or
-// being processed.  The wait is bounded all the same; if the bound is hit the
-// header's abort flag is set and the chunk's carry becomes NaN.
+// valid on its own and no fences are needed.  Forward progress does not
+// depend on how many workgroups are resident: a chunk only waits on earlier
+// chunks of its chain (smaller indices of the same group), and a group's
+// chunks are handed out in index order, only to workgroups of the group
+// already running, which take theirs in increasing order.  So a group's
+// smallest unfinished chunk is being processed by its holder and waits on
+// finished chunks only.  The wait is bounded all the same; if the bound is
+// hit the header's abort flag is set and the chunk's carry becomes NaN.
 #include <algorithm>
 #include <mutex>
 
@@ -73,7 +79,7 @@ template <int VEC, int CH, int LT>
 __global__ __launch_bounds__(kThreads) void diag_scan_kernel(
     const float *__restrict__ a, const float *__restrict__ b, const float *__restrict__ s0,
     float *out0, float *out1, const int *__restrict__ out_sel, const int *__restrict__ skip,
-    const int *__restrict__ all_done, int T, int D, int groups, int chains, int nchunk,
+    const int *__restrict__ all_done, int T, int D, int groups, int chains, int nchunk, int ngrp,
     ScanHeader *__restrict__ hdr, unsigned long long *__restrict__ desc)
 {
     using G = DiagGeom<VEC, CH, LT>;
@@ -84,6 +90,7 @@ __global__ __launch_bounds__(kThreads) void diag_scan_kernel(
     __shared__ float shA[NS][CH];
     __shared__ float shB[NS][CH];
     __shared__ float shC[CH];
+    __shared__ long long sh_ticket;
 
     const int tid = threadIdx.x;
     const unsigned epoch = __hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -91,14 +98,30 @@ __global__ __launch_bounds__(kThreads) void diag_scan_kernel(
     float *out = (out_sel && (*out_sel & 1)) ? out1 : out0;
     const int slot = tid / LD;
     const int lc = (tid % LD) * VEC;              // channel offset inside the tile
-    const long long total = static_cast<long long>(chains) * nchunk;
+    const int gid = static_cast<int>(blockIdx.x) % ngrp;
+    const long long nc = (chains - gid + ngrp - 1) / ngrp;          // chains of the group
+    const long long total = nc * nchunk;                            // chunks of the group
+    unsigned *ticket = &hdr->ticket[gid];
 
-    for (long long cidx = blockIdx.x; cidx < total; cidx += gridDim.x) {
-        const int tchunk = static_cast<int>(cidx / chains);
-        const int chain = static_cast<int>(cidx % chains);
+    if (tid == 0) sh_ticket = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    long long cidx = sh_ticket;
+    for (; cidx < total;) {
+        // the next chunk is drawn now and read back after the look-back, so the
+        // round trip overlaps this chunk's loads
+        unsigned next = 0u;
+        if (tid == 0) next = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int tchunk = static_cast<int>(cidx / nc);
+        const int chain = gid + ngrp * static_cast<int>(cidx % nc);
         const int bseq = chain / groups;
         const int grp = chain % groups;
-        if (skip && skip[bseq]) continue;         // uniform over the workgroup
+        if (skip && skip[bseq]) {                 // uniform over the workgroup
+            __syncthreads();                      // every thread has read sh_ticket
+            if (tid == 0) sh_ticket = next;
+            __syncthreads();
+            cidx = sh_ticket;
+            continue;
+        }
         const int c0 = grp * CH + lc;             // first channel of this thread
         const bool cvalid = c0 < D;               // VEC == 4 implies D % 4 == 0
         const int t0 = tchunk * L + slot * LT;
@@ -178,7 +201,9 @@ __global__ __launch_bounds__(kThreads) void diag_scan_kernel(
             }
             shC[c] = carry;
         }
+        if (tid == 0) sh_ticket = next;           // every thread read the current one before the syncs above
         __syncthreads();
+        cidx = sh_ticket;
 
         float st[VEC];
 #pragma unroll
@@ -201,12 +226,15 @@ __global__ __launch_bounds__(kThreads) void diag_scan_kernel(
         }
     }
 
-    // Last workgroup out resets the done counter and advances the epoch.
+    // Last workgroup out resets the done and ticket counters (every workgroup
+    // has drawn its last ticket by then) and advances the epoch.
     __syncthreads();
     if (tid == 0) {
         const unsigned prev = __hip_atomic_fetch_add(&hdr->done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
         if (prev == gridDim.x - 1) {
             __hip_atomic_store(&hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int g = 0; g < ngrp; ++g)
+                __hip_atomic_store(&hdr->ticket[g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(&hdr->epoch, epoch + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
@@ -324,17 +352,20 @@ int launch_diag_scan(const float *a, const float *b, const float *s0, float *out
     const long long total = static_cast<long long>(p.chains) * p.nchunk;
     const DiagKind k = diag_kind(D);
     const unsigned grid = static_cast<unsigned>(std::min<long long>(total, persistent_capacity(k)));
+    if (total + 2LL * grid >= (1LL << 32))       // tickets are 32-bit
+        return fail(DEER_ERR_UNSUPPORTED, "diagonal scan: too many chunks (above 2^31)");
+    const int ngrp = static_cast<int>(std::min<long long>({kTicketGroups, p.chains, grid}));
     auto *hdr = static_cast<ScanHeader *>(state);
     auto *desc = reinterpret_cast<unsigned long long *>(static_cast<char *>(state) + sizeof(ScanHeader));
     if (k == kWide)
         DEER_LAUNCH((diag_scan_kernel<4, 256, kLT>), dim3(grid), dim3(kThreads), 0, stream, a, b, s0, out0,
-                           out1, out_sel, skip, all_done, T, D, p.groups, p.chains, p.nchunk, hdr, desc);
+                           out1, out_sel, skip, all_done, T, D, p.groups, p.chains, p.nchunk, ngrp, hdr, desc);
     else if (k == kNarrow)
         DEER_LAUNCH((diag_scan_kernel<4, 64, kLT>), dim3(grid), dim3(kThreads), 0, stream, a, b, s0, out0,
-                           out1, out_sel, skip, all_done, T, D, p.groups, p.chains, p.nchunk, hdr, desc);
+                           out1, out_sel, skip, all_done, T, D, p.groups, p.chains, p.nchunk, ngrp, hdr, desc);
     else
         DEER_LAUNCH((diag_scan_kernel<1, 64, kLT>), dim3(grid), dim3(kThreads), 0, stream, a, b, s0, out0,
-                           out1, out_sel, skip, all_done, T, D, p.groups, p.chains, p.nchunk, hdr, desc);
+                           out1, out_sel, skip, all_done, T, D, p.groups, p.chains, p.nchunk, ngrp, hdr, desc);
     DEER_HIP(hipGetLastError());
     return DEER_OK;
 }

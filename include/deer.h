@@ -195,14 +195,16 @@ int deer_workspace_init(void *workspace, size_t ws_bytes, void *stream);
  * returns after the outputs are complete.  Returns DEER_NOT_CONVERGED when any
  * sequence did not converge (status 1, 2 or 3).
  *
- * The diagonal-block modes and the GRU's fused iteration run a single-pass
- * scan whose tiles wait on earlier tiles (a decoupled look-back over a
- * persistent grid sized to the device's resident capacity), and tanh problems
- * with D <= 16 and T <= 8192 whose grid the device holds at once run the whole
- * solve in one launch whose workgroups wait on each other once per iteration.
- * Both assume the whole grid is resident at once: another kernel occupying
- * compute units on a concurrent stream can delay it; the waits are bounded,
- * and if a bound is hit the call returns DEER_ERR_DEVICE.
+ * The diagonal-block modes run the single-pass scan of linear_scan_diag,
+ * whose progress does not depend on how much of its grid is resident (see
+ * there).  The GRU's fused iteration (D = 32, 64) runs a single-pass scan over
+ * a persistent grid sized to the device's resident capacity with a fixed tile
+ * stride per workgroup, and tanh problems with D <= 16 and T <= 8192 whose
+ * grid the device holds at once run the whole solve in one launch whose
+ * workgroups wait on each other once per iteration.  Those two assume the
+ * whole grid is resident at once: another kernel occupying compute units on a
+ * concurrent stream can delay them; the waits are bounded, and if a bound is
+ * hit the call returns DEER_ERR_DEVICE.
  */
 int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int B, int T, int mode, float tol,
                int max_iter, const deer_solve_opts_t *opts, const float *init_guess, float *traj_out,
@@ -222,10 +224,13 @@ int linear_scan_workspace_size(int B, int T, int D, int dense, size_t *bytes_out
  *   a, b   device [B,T,D];  s0 device [B,D] or NULL (zeros);  s device [B,T,D]
  *   (s may alias neither a nor b).  One pass: reads a and b once, writes s once.
  *   Any B, T >= 0, 1 <= D.
- * Tiles wait on earlier tiles (decoupled look-back) over a persistent grid
- * sized to the device's resident capacity; a kernel occupying compute units
- * on a concurrent stream can delay it, and if the bounded wait gives up the
- * affected outputs are NaN.
+ * Tiles wait on earlier tiles of their channels (decoupled look-back) over a
+ * persistent grid sized to the device's resident capacity.  Tiles are handed
+ * out in index order from counters in the workspace, and only to running
+ * workgroups, so every tile a workgroup waits on is held by a running one:
+ * the scan completes whatever part of its grid is resident (a kernel
+ * occupying compute units on a concurrent stream only slows it).  The waits
+ * are bounded all the same; if a bound is hit the affected outputs are NaN.
  */
 int linear_scan_diag(const float *a, const float *b, const float *s0, float *s, int B, int T, int D,
                      void *workspace, size_t ws_bytes, void *stream);

@@ -30,7 +30,7 @@ def build(force: bool = True) -> str:
     """Compile ``liboracle.so`` with gcc (no fast-math, no FMA contraction)."""
     if not force and os.path.exists(_LIB_PATH):
         return _LIB_PATH
-    cmd = ["gcc", "-O2", "-std=gnu11", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
+    cmd = ["gcc", "-O3", "-std=gnu11", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
            "-Wall", "-o", _LIB_PATH + ".tmp", _SOURCES[0], "-lm"]
     subprocess.run(cmd, check=True, cwd=_HERE)
     os.replace(_LIB_PATH + ".tmp", _LIB_PATH)

@@ -369,7 +369,8 @@ def test_multisecant_linear_cell_recovers_the_jacobian_after_D_secants(orc, D, c
 
 @pytest.mark.parametrize("precision", ["f64", "f32"])
 @pytest.mark.parametrize("eps,kept", [(1e-6, False), (1e-7, False), (1e-4, True), (1e-3, True)])
-def test_dplr_compression_drops_a_numerically_dependent_sketch_column(orc, precision, eps, kept):
+@pytest.mark.parametrize("scale", [1.0, 2.0 ** -14, 2.0 ** 14])
+def test_dplr_compression_drops_a_numerically_dependent_sketch_column(orc, precision, eps, kept, scale):
     """The re-compression keeps a Gram-Schmidt column only if its norm after
     orthogonalisation exceeds 1e-5 of its norm before.  A hand-built chunk
     aggregate (D = 4, m = 2, alpha = 0, chunks of 2) with
@@ -378,7 +379,9 @@ def test_dplr_compression_drops_a_numerically_dependent_sketch_column(orc, preci
     exact in float32): for eps below the threshold the second column is
     dropped and the carried correction is e1 e3^T, so the entry of the third
     chunk is e1 (R^T (e3 + e4) = (1, 1)); above it the correction stays
-    L R^T and the entry is e1 + e2, the dense product."""
+    L R^T and the entry is e1 + e2, the dense product.  The threshold is
+    relative: scaling the sketch by a power of two (exact) scales Y and
+    leaves every decision unchanged."""
     D, m, T = 4, 2, 6
     e = np.eye(D)
     U = np.zeros((1, T, m, D)); V = np.zeros((1, T, m, D)); cc = np.zeros((1, T, D))
@@ -386,7 +389,7 @@ def test_dplr_compression_drops_a_numerically_dependent_sketch_column(orc, preci
     U[0, 2] = [e[0], e[1]]; V[0, 2] = [e[2], e[3]]          # A_2 = e1 e3^T + e2 e4^T
     for t in (3, 4, 5):                                      # projector onto span(e1, e2)
         U[0, t] = [e[0], e[1]]; V[0, t] = [e[0], e[1]]
-    sk = np.array([[0.3, -0.7], [0.9, 0.2], [1.0, 1.0], [0.0, eps]], np.float32)
+    sk = (np.array([[0.3, -0.7], [0.9, 0.2], [1.0, 1.0], [0.0, eps]], np.float32) * np.float32(scale))
     got = orc.dplr_scan(0.0, U, V, cc, sk, chunk=2, precision=precision)
     exact = _dense_scan(0.0, U, V, cc)
     np.testing.assert_array_equal(exact[0, 4], [1.0, 1.0, 0.0, 0.0])

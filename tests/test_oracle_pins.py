@@ -419,6 +419,10 @@ def test_lle_linear_scalar_closed_form(orc):
         traj = orc.rollout(c, x)
         lam = orc.lle(c, x, traj, np.ones((2, 1), np.float32))
         np.testing.assert_allclose(lam, math.log(abs(float(np.float32(a)))), rtol=0, atol=1e-12)
+        # the start vector is normalised before the first step, so its length
+        # never enters the average (without that, 3.0 would add ln 3 / T)
+        lam3 = orc.lle(c, x, traj, np.full((2, 1), 3.0, np.float32))
+        np.testing.assert_allclose(lam3, math.log(abs(float(np.float32(a)))), rtol=0, atol=1e-12)
 
 
 def test_lle_diagonal_linear_picks_the_largest_rate(orc):
@@ -509,6 +513,26 @@ def test_stop_rule_edges(orc):
     # the exact prefix before the NaN is untouched
     r64 = orc.rollout(c, p["x"])
     assert np.abs(tr[1, :5] - r64[1, :5]).max() < 1e-6
+
+
+def test_stop_rule_accepts_a_residual_equal_to_tol(orc):
+    """The test is `residual <= tol`: a scalar linear cell from a zero start has
+    the residual max_t |u x_t| (b = 0: one product per position, formed the
+    same way here in the oracle's precision).  With tol equal to it the start
+    already passes (0 iterations); one ulp below, one Newton step is taken."""
+    u = np.float32(0.75)
+    c = orc.Cell("linear", np.array([[0.5]], np.float32), np.array([[u]], np.float32), np.zeros(1, np.float32))
+    x = np.random.default_rng(95).standard_normal((1, 20, 1)).astype(np.float32)
+    for prec, dt in (("f64", np.float64), ("f32", np.float32)):
+        r0 = dt(np.abs(dt(u) * x[0, :, 0].astype(dt)).max())
+        _, it, _, st = orc.newton(c, x, None, mode="dense", tol=float(r0), max_iter=5, precision=prec)
+        assert it[0] == 0 and st[0] == 0
+        _, it, _, st = orc.newton(c, x, None, mode="dense", tol=float(np.nextafter(r0, dt(0))),
+                                  max_iter=5, precision=prec)
+        assert it[0] == 1 and st[0] == 0
+        sk = np.ones((1, 1), np.float32)
+        _, it, _, st = orc.broyden(c, x, sk, rank=1, tol=float(r0), max_iter=5, precision=prec)
+        assert it[0] == 0 and st[0] == 0
 
 
 # ------------------------------------------- other linearisations and damping

@@ -261,11 +261,20 @@ int read_results(HostStage &hs, const int *iters_dev, const int *status_dev, con
 }
 
 // ------------------------------------------------------ small device kernels
+// allow_flip: the solve's kernels place iterate i in buffer (i ^ flip) % 2 and
+// the gather honours it (the fused GRU step from a zero start).  The flip is the
+// parity of the iteration that ended the workspace's previous solve, so that a
+// solve taking as many iterations modulo 2 leaves its result in the caller's
+// trajectory buffer (buffer 0) and the gather copies nothing.  Any flip gives
+// the same result; a wrong guess costs the copy, as without the hint.
 __global__ void init_control_kernel(SolveControl *ctl, int *done, int *iters, int *status, float *resid,
-                                    unsigned *res_bits, StallCheck sc, int B)
+                                    unsigned *res_bits, StallCheck sc, int B, int allow_flip)
 {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i == 0) { ctl->iter = 0; ctl->all_done = 0; ctl->escalate = 0; }
+    if (i == 0) {
+        ctl->iter = 0; ctl->all_done = 0; ctl->escalate = 0;
+        ctl->flip = allow_flip ? (ctl->last_parity & 1) : 0;
+    }
     if (i < B) {
         done[i] = 0; iters[i] = 0; status[i] = 0; resid[i] = 0.0f; res_bits[i] = 0u;
         if (sc.front) { sc.front[i] = kNoFront; sc.best[i] = -1; sc.last_adv[i] = 0; }
@@ -343,17 +352,18 @@ __global__ void check_kernel(SolveControl *ctl, unsigned *res_bits, const unsign
 // zero_start, traj was never written for sequences that stopped at iteration
 // 0; their iterate is the all-zero start.
 __global__ void gather_kernel(float *__restrict__ traj, const float *__restrict__ buf1, const int *__restrict__ iters,
-                              size_t per_seq, int B, int zero_start)
+                              size_t per_seq, int B, int zero_start, const SolveControl *ctl)
 {
     const int bseq = blockIdx.y;
     if (bseq >= B) return;
     const int it = iters[bseq];
-    const bool copy = (it & 1) != 0, zero = zero_start && it == 0;
+    const int flip = ctl ? ctl->flip : 0;
+    const bool copy = ((it ^ flip) & 1) != 0, zero = zero_start && it == 0;
     if (!copy && !zero) return;
     const size_t base = static_cast<size_t>(bseq) * per_seq;
     for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < per_seq;
          i += static_cast<size_t>(gridDim.x) * blockDim.x)
-        traj[base + i] = copy ? buf1[base + i] : 0.0f;
+        traj[base + i] = zero ? 0.0f : buf1[base + i];
 }
 
 unsigned grid_for(size_t n, unsigned threads = 256, unsigned cap = 8192)
@@ -991,11 +1001,12 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
         sc.last_adv = L.last_adv;
         sc.window = o.stall_window;
     }
-    DEER_LAUNCH(init_control_kernel, dim3(grid_for(static_cast<size_t>(B) + 1)), dim3(256), 0, stream, L.ctl,
-                       L.done, L.iters, L.status, L.resid, L.res_bits, sc, B);
-    DEER_HIP(hipGetLastError());
     const bool fused = fused_gru_step(p, mode);
     const bool zero_start = fused && !init_guess;   // the fused step reads no s^(0) when it is all zeros
+    // the fused step alone runs such a solve, and it honours the buffer flip
+    DEER_LAUNCH(init_control_kernel, dim3(grid_for(static_cast<size_t>(B) + 1)), dim3(256), 0, stream, L.ctl,
+                       L.done, L.iters, L.status, L.resid, L.res_bits, sc, B, zero_start ? 1 : 0);
+    DEER_HIP(hipGetLastError());
     // from a zero start and a zero initial state with inputs as wide as the
     // state, the first fused step computes the input projection itself (no
     // separate projection launch): every state it reads is zero there
@@ -1083,7 +1094,7 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
     });
     if (rc == DEER_OK) {
         DEER_LAUNCH(gather_kernel, dim3(grid_for(per_seq, 256, 1024), B), dim3(256), 0, stream, traj_out,
-                           L.buf1, L.iters, per_seq, B, zero_start ? 1 : 0);
+                           L.buf1, L.iters, per_seq, B, zero_start ? 1 : 0, L.ctl);
         if (hipGetLastError() != hipSuccess) rc = fail(DEER_ERR_HIP, "deer_solve: gather launch failed");
     }
     if (rc == DEER_OK && rms_out) rc = residual_rms(true);
@@ -1174,7 +1185,7 @@ int deer_solve_broyden(const deer_cell_params_t *p, const float *x, const float 
         sc.window = opts->stall_window;
     }
     DEER_LAUNCH(init_control_kernel, dim3(grid_for(static_cast<size_t>(B) + 1)), dim3(256), 0, stream, L.ctl,
-                L.done, L.iters, L.status, L.resid, L.res_bits, sc, B);
+                L.done, L.iters, L.status, L.resid, L.res_bits, sc, B, 0);
     if (init_guess) {
         if (init_guess != traj_out)
             DEER_LAUNCH(copy_kernel, dim3(grid_for(BTD)), dim3(256), 0, stream, traj_out, init_guess, BTD);
@@ -1230,7 +1241,7 @@ int deer_solve_broyden(const deer_cell_params_t *p, const float *x, const float 
     if (rc == DEER_OK) {
         const size_t per_seq = static_cast<size_t>(T) * D;
         DEER_LAUNCH(gather_kernel, dim3(grid_for(per_seq, 256, 1024), B), dim3(256), 0, stream, traj_out, L.buf1,
-                    L.iters, per_seq, B, 0);
+                    L.iters, per_seq, B, 0, nullptr);
         if (hipGetLastError() != hipSuccess) rc = fail(DEER_ERR_HIP, "deer_solve_broyden: gather launch failed");
     }
     std::vector<int> status_h(B, 0);

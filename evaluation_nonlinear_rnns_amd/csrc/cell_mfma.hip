@@ -359,7 +359,7 @@ __global__ __launch_bounds__(kThreads, 2) void gru_quasi_step_kernel(
     const float wz = Whh[static_cast<size_t>(D + c) * D + c];
     const float wn = Whh[static_cast<size_t>(2 * D + c) * D + c];
     const int iter = *sel;
-    const bool odd = (iter & 1) != 0;
+    const bool odd = ((iter ^ ctl->flip) & 1) != 0;   // s^(i) lives in buffer (i ^ flip) % 2
     const float *s = (zero_start && iter == 0) ? nullptr : (odd ? s_odd : s_even);   // the iterate s^(i)
     float *out = odd ? s_even : s_odd;           // s^(i+1)
     const unsigned epoch = __hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -128,10 +128,12 @@ struct RowRotations {
 // ------------------------------------------------------------ solve control
 // Device-side state of one deer_solve call.
 struct SolveControl {
-    int iter;       // current iteration index i (iterate s^(i) lives in buffer i % 2)
-    int all_done;   // 1 once every sequence has stopped
-    int escalate;   // 1 once a stall asked for double accumulation (read by the host's poll)
-    int pad[61];
+    int iter;         // current iteration index i (iterate s^(i) lives in buffer (i ^ flip) % 2)
+    int all_done;     // 1 once every sequence has stopped
+    int escalate;     // 1 once a stall asked for double accumulation (read by the host's poll)
+    int flip;         // buffer parity of this solve (0 unless the path supports it, see init_control_kernel)
+    int last_parity;  // parity of the iteration that ended the workspace's last solve (kept across solves)
+    int pad[59];
 };
 
 // Finite-step check.  After i iterations the first i states are exact in
@@ -238,7 +240,7 @@ __device__ inline void finalize_iteration(SolveControl *ctl, unsigned *res_bits,
         active = __syncthreads_or(active);
         if (threadIdx.x == 0) {
             if (active) ctl->iter = i + 1;
-            else ctl->all_done = 1;
+            else { ctl->all_done = 1; ctl->last_parity = i & 1; }
         }
         return;
     }
@@ -282,7 +284,7 @@ __device__ inline void finalize_iteration(SolveControl *ctl, unsigned *res_bits,
     active = __syncthreads_or(active);
     if (threadIdx.x == 0) {
         if (active) ctl->iter = i + 1;
-        else ctl->all_done = 1;
+        else { ctl->all_done = 1; ctl->last_parity = i & 1; }
     }
 }
 

@@ -377,6 +377,44 @@ def test_full_sweep_gain2_certified(orc):
     assert np.all(iters <= w.T)
 
 
+def test_gru_fused_buffer_parity_hint(orc):
+    """The fused GRU solve from a zero start places its iterates by the parity
+    of the iteration that ended the workspace's previous solve, so that a solve
+    with the same parity leaves its result in the trajectory buffer.  Solves in
+    a row on one workspace, with iteration counts of both parities (exactly
+    max_iter iterations at tol < 0, including 0), give the same bits as the same
+    solve on a fresh workspace, and a converging solve repeated gives the same
+    bits and counts."""
+    dev = device()
+    B, T, D = 3, 700, 64
+    p = I.gru_problem(977, B, T, D, D, bias_std=0.3, s0_std=0.5)
+    cell = deer.cell_from_problem(p, dev)
+    x = torch.from_numpy(p["x"]).to(dev)
+    ws = deer.new_workspace(deer.deer_workspace_size(cell, B, T, "diag"), device=dev)
+    out = torch.empty((B, T, D), dtype=torch.float32, device=dev)
+    for k in (3, 3, 2, 1, 1, 0, 4, 0, 5):
+        log(f"deer_solve gru diag B={B} T={T} tol<0 max_iter={k} on a reused workspace")
+        got, iters, _, _, _ = deer.deer_solve(cell, x, None, mode="diag", tol=-1.0, max_iter=k, out=out,
+                                              workspace=ws)
+        ref, riters, _, _, _ = deer.deer_solve(cell, x, None, mode="diag", tol=-1.0, max_iter=k)
+        torch.cuda.synchronize()
+        assert np.all(iters == k) and np.all(riters == k)
+        assert np.array_equal(got.cpu().numpy(), ref.cpu().numpy()), k
+        if k == 0:
+            assert not got.any()
+    runs = []
+    for _ in range(3):
+        log(f"deer_solve gru diag B={B} T={T} tol=1e-5 on a reused workspace")
+        t, it, _, st, rc = deer.deer_solve(cell, x, None, mode="diag", tol=1e-5, max_iter=100, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        runs.append((t.cpu().numpy(), it.copy()))
+        assert rc == deer.DEER_OK and np.all(st == 0)
+    for t, it in runs[1:]:
+        assert np.array_equal(t, runs[0][0]) and list(it) == list(runs[0][1])
+    ref = orc.rollout(orc.Cell.from_problem(p), p["x"])
+    assert rel_linf(runs[0][0], ref).max() <= TOL
+
+
 def test_solves_are_bitwise_reproducible(orc):
     """The scans' look-back always yields the left-to-right chain's value, so
     the same solve gives the same bits whatever the workgroup timing."""

@@ -510,11 +510,18 @@ struct PollEvents {
     }
 };
 
-// Enqueue batches of iterations (1, 2, 4, 4, ...) and, while the current batch
-// runs, wait for the copy of the device's all-done and escalate words enqueued
-// after the previous batch; stop enqueueing once all-done reads set, and call
+// Enqueue batches of iterations and, while the current batch runs, wait for
+// the copy of the device's all-done and escalate words enqueued after the
+// previous batch; stop enqueueing once all-done reads set, and call
 // on_escalate() while escalate does.  Kernels enqueued after convergence exit
-// at once.  `total` caps the evaluations enqueued.
+// at once, but each still costs a dispatch (a no-op compose over every chunk
+// is a full grid), so batches start at one iteration and double only when the
+// previous batch had already finished by the time the host polled it: then the
+// device may run dry before the host's next enqueue.  Long iterations keep one
+// iteration per batch and stop within a batch of convergence; short ones grow
+// their batches until the host keeps ahead.  `total` caps the evaluations
+// enqueued.
+constexpr int kMaxPollBatch = 4;
 template <class Enqueue, class OnEscalate>
 int run_polled(Enqueue &&enqueue_iteration, SolveControl *ctl, long long total, hipStream_t stream, PollEvents &pe,
                HostStage &hs, const char *who, OnEscalate &&on_escalate)
@@ -544,17 +551,20 @@ int run_polled(Enqueue &&enqueue_iteration, SolveControl *ctl, long long total, 
             break;
         }
         if (pending) {
+            // finished before the host looked: the device is about to drain the
+            // one batch queued behind it
+            const bool behind = hipEventQuery(pe.ev[pending_slot]) == hipSuccess;
             if (hipEventSynchronize(pe.ev[pending_slot]) != hipSuccess) {
                 rc = fail(DEER_ERR_HIP, std::string(who) + ": event wait failed");
                 break;
             }
             if (h[2 * pending_slot]) break;
             if (h[2 * pending_slot + 1]) on_escalate();
+            if (behind && batch < kMaxPollBatch) batch *= 2;
         }
         pending = true;
         pending_slot = slot;
         slot ^= 1;
-        if (batch < 4) batch *= 2;
     }
     return rc;
 }

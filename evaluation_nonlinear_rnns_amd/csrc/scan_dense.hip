@@ -761,6 +761,12 @@ __device__ __forceinline__ void stage_chunk64(const float *__restrict__ dv, cons
 // block 1), row 0: (B step, block 0), row 3: (B step, block 1) -- and every
 // lane evaluates once per pair.  The projection of the lane's (step, channel)
 // is fetched four pairs ahead into a register ring.
+//
+// The chunk's d and b rows pass through LDS sixteen steps at a time: the rows
+// of the next sixteen steps are requested into registers while the current
+// ones replay, then written over them.  Staging the whole chunk at once took
+// 16 KB of LDS per wavefront and held a compute unit to ten of these
+// latency-bound wavefronts; 4 KB leaves the register file as the limit.
 template <bool EVAL>
 __global__ __launch_bounds__(64) void dense_replay_dpp32_kernel(
     const float *dv, const float *__restrict__ W, const float *bv, const float *__restrict__ carry,
@@ -769,14 +775,41 @@ __global__ __launch_bounds__(64) void dense_replay_dpp32_kernel(
 {
     constexpr int D = 32;
     constexpr int RP = 4;                                            // projection ring depth (pairs of steps)
-    __shared__ float dsm[64 * D], bsm[64 * D];
+    constexpr int kSt = 16;                                          // steps per LDS stage (a multiple of 2 RP)
+    constexpr int kSv = kSt * D / 4 / 64;                            // float4 rows of d (and of b) per lane per stage
+    __shared__ float dsm[kSt * D], bsm[kSt * D];
     if (all_done && *all_done) return;
     const long long q = blockIdx.x;
     const int bseq = static_cast<int>(q / nchunk), c = static_cast<int>(q % nchunk);
     if (skip && skip[bseq]) return;
     const int t0 = c * L, n = min(L, T - t0);
     const size_t base = (static_cast<size_t>(bseq) * T + t0) * D;
-    stage_chunk64(dv, bv, base, n * D, D, dsm, bsm);
+    const int nst = (n + kSt - 1) / kSt;
+    v4f dq[kSv], bq[kSv];
+    // rows of stage st into registers (clamped: rows past the chunk are never read)
+    auto fetch = [&](int st) {
+#pragma unroll
+        for (int u = 0; u < kSv; ++u) {
+            const int e = st * (kSt * D / 4) + static_cast<int>(threadIdx.x) + 64 * u;
+            const int ec = e < n * (D / 4) ? e : 0;
+            dq[u] = *reinterpret_cast<const v4f *>(dv + base + static_cast<size_t>(ec) * 4);
+            bq[u] = *reinterpret_cast<const v4f *>(bv + base + static_cast<size_t>(ec) * 4);
+        }
+    };
+    // stage st into LDS once every lane is done with the previous one, then
+    // request the next
+    auto stage_in = [&](int st) {
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kSv; ++u) {
+            const int e = static_cast<int>(threadIdx.x) + 64 * u;
+            *reinterpret_cast<v4f *>(dsm + e * 4) = dq[u];
+            *reinterpret_cast<v4f *>(bsm + e * 4) = bq[u];
+        }
+        __syncthreads();
+        if (st + 1 < nst) fetch(st + 1);
+    };
+    fetch(0);
 
     const int lane = threadIdx.x, r = lane >> 4, m = lane & 15;
     const int KA = r & 1, IA = r >> 1, KB = r >> 1, IB = r & 1;
@@ -789,7 +822,6 @@ __global__ __launch_bounds__(64) void dense_replay_dpp32_kernel(
 #pragma unroll
         for (int k = 0; k < RP; ++k) pr[k] = pc[min(2 * k + eofs, n - 1) * D + ech];
     }
-    __syncthreads();
 
     int src[16];
     src[0] = m;
@@ -813,7 +845,8 @@ __global__ __launch_bounds__(64) void dense_replay_dpp32_kernel(
         float y = contract(x, odd ? wB : wA);
         y += __shfl_xor(y, odd ? 32 : 16, 64);
         const int ch = odd ? 16 * IB + m : 16 * IA + m;
-        x = dsm[s * D + ch] * y + bsm[s * D + ch];
+        const int ls = (s & (kSt - 1)) * D + ch;
+        x = dsm[ls] * y + bsm[ls];
         out[s * D + ch] = x;
         return y;
     };
@@ -831,6 +864,7 @@ __global__ __launch_bounds__(64) void dense_replay_dpp32_kernel(
             fmin = min(fmin, front_of(ra, ev.tol, t0 + se));
         };
         for (; s + 2 * RP <= n; s += 2 * RP) {
+            if ((s & (kSt - 1)) == 0) stage_in(s / kSt);
 #pragma unroll
             for (int k = 0; k < RP; ++k) {
                 const int sa = s + 2 * k;
@@ -842,6 +876,7 @@ __global__ __launch_bounds__(64) void dense_replay_dpp32_kernel(
                 pr[k] = pc[min(sa + 2 * RP + eofs, n - 1) * D + ech];
             }
         }
+        if (s < n && (s & (kSt - 1)) == 0) stage_in(s / kSt);    // the tail lies in one stage
 #pragma unroll
         for (int k = 0; k < RP; ++k) {
             const int sa = s + 2 * k;
@@ -865,10 +900,14 @@ __global__ __launch_bounds__(64) void dense_replay_dpp32_kernel(
         }
     } else {
         for (; s + 1 < n; s += 2) {
+            if ((s & (kSt - 1)) == 0) stage_in(s / kSt);
             step(s, false);
             step(s + 1, true);
         }
-        if (s < n) step(s, false);
+        if (s < n) {
+            if ((s & (kSt - 1)) == 0) stage_in(s / kSt);
+            step(s, false);
+        }
     }
 }
 

@@ -553,7 +553,9 @@ int run_polled(Enqueue &&enqueue_iteration, SolveControl *ctl, long long total, 
         if (pending) {
             // finished before the host looked: the device is about to drain the
             // one batch queued behind it
-            const bool behind = hipEventQuery(pe.ev[pending_slot]) == hipSuccess;
+            const hipError_t q = hipEventQuery(pe.ev[pending_slot]);
+            const bool behind = q == hipSuccess;
+            if (q == hipErrorNotReady) (void)hipGetLastError();   // a pending event is no error
             if (hipEventSynchronize(pe.ev[pending_slot]) != hipSuccess) {
                 rc = fail(DEER_ERR_HIP, std::string(who) + ": event wait failed");
                 break;

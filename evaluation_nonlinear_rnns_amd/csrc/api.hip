@@ -1014,15 +1014,19 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
         sc.window = o.stall_window;
     }
     const bool fused = fused_gru_step(p, mode);
-    const bool zero_start = fused && !init_guess;   // the fused step reads no s^(0) when it is all zeros
+    // Without an initial guess s^(0) is all zeros and is never stored: the fused
+    // GRU step and the first tanh evaluation read no iterate then, and a
+    // sequence that stops at iteration 0 gets zeros from the gather.  (The
+    // unfused GRU evaluation reads s^(0) from traj_out, which is filled.)
+    const bool zero_start = !init_guess && (fused || !gru);
     // the fused step alone runs such a solve, and it honours the buffer flip
     DEER_LAUNCH(init_control_kernel, dim3(grid_for(static_cast<size_t>(B) + 1)), dim3(256), 0, stream, L.ctl,
-                       L.done, L.iters, L.status, L.resid, L.res_bits, sc, B, zero_start ? 1 : 0);
+                       L.done, L.iters, L.status, L.resid, L.res_bits, sc, B, (fused && zero_start) ? 1 : 0);
     DEER_HIP(hipGetLastError());
     // from a zero start and a zero initial state with inputs as wide as the
     // state, the first fused step computes the input projection itself (no
     // separate projection launch): every state it reads is zero there
-    const bool proj_in_step = zero_start && !s0 && p->M == D;
+    const bool proj_in_step = fused && zero_start && !s0 && p->M == D;
     if (init_guess) {
         if (init_guess != traj_out)
             DEER_LAUNCH(copy_kernel, dim3(grid_for(BTD)), dim3(256), 0, stream, traj_out, init_guess, BTD);
@@ -1076,10 +1080,12 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
             if (gru)
                 r = launch_gru_eval(p->W, p->b2, L.proj, s0, traj_out, L.buf1, sel, L.done, all_done, L.lin,
                                     L.bvec, L.res_bits, B, T, D, p->M, lz, fo, stream);
-            else
-                r = launch_tanh_eval(p->W, L.proj, s0, traj_out, L.buf1, sel, L.done, all_done, L.lin, L.bvec,
-                                     L.res_bits, B, T, D, dense, lz, fo, stream);
+            else   // the first evaluation of a zero start reads no iterate (nullptr: all zeros)
+                r = launch_tanh_eval(p->W, L.proj, s0, (zero_start && first_step) ? nullptr : traj_out, L.buf1,
+                                     sel, L.done, all_done, L.lin, L.bvec, L.res_bits, B, T, D, dense, lz, fo,
+                                     stream);
             prof.end();
+            first_step = false;
             if (r) return r;
         }
         prof.begin(3);

@@ -238,11 +238,16 @@ __global__ __launch_bounds__(kThreads) void tanh_eval_kernel(
     // issue order: s_0 row, state rows, W, then the projection (needed only after the barrier)
     const float s0v = (s0 && tid < D) ? s0[static_cast<size_t>(bseq) * D + tid] : 0.0f;
     float sv[NS], wv[NW], pv[NP];
+    if (s) {
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
-        const int e = tid + i * kThreads, r = e / DP, k = e % DP;
-        const int t = min(max(t0 - 1 + r, 0), T - 1);
-        sv[i] = s[(seq + t) * D + min(k, D - 1)];
+        for (int i = 0; i < NS; ++i) {
+            const int e = tid + i * kThreads, r = e / DP, k = e % DP;
+            const int t = min(max(t0 - 1 + r, 0), T - 1);
+            sv[i] = s[(seq + t) * D + min(k, D - 1)];
+        }
+    } else {                                                      // the all-zero start, never stored
+#pragma unroll
+        for (int i = 0; i < NS; ++i) sv[i] = 0.0f;
     }
 #pragma unroll
     for (int i = 0; i < NW; ++i) {

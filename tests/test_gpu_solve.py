@@ -215,6 +215,37 @@ def test_solve_edge_cases(orc):
     assert list(iters) == [1, 1] and np.all(rel_linf(got, ref) <= TOL)
 
 
+@pytest.mark.parametrize("mode", ["dense", "diag"])
+def test_zero_start_is_never_stored(orc, mode):
+    """Without an initial guess the multi-launch loop neither fills the
+    trajectory buffer with the zero start nor reads it: the first evaluation
+    takes the iterate as zeros, and a sequence that stops at iteration 0 gets
+    zeros from the final gather, whatever the buffer held before."""
+    dev = device()
+    B, T, D = 3, 200, 32
+    p = I.tanh_problem(702, B, T, D, D, gain=0.7)           # b = 0
+    p["x"][1] = 0.0                                         # f(0) = 0: sequence 1 passes at iteration 0
+    cell = deer.cell_from_problem(p, dev)
+    x = torch.from_numpy(p["x"]).to(dev)
+    out = torch.full((B, T, D), float("nan"), dtype=torch.float32, device=dev)
+    log(f"deer_solve tanh {mode} zero start, max_iter=0, output prefilled with NaN")
+    got, iters, _, status, rc = deer.deer_solve(cell, x, None, mode=mode, tol=1e-6, max_iter=0, out=out)
+    torch.cuda.synchronize()
+    assert list(iters) == [0, 0, 0] and list(status) == [1, 0, 1] and not got.cpu().numpy().any()
+    out.fill_(float("nan"))
+    log(f"deer_solve tanh {mode} zero start, one sequence passing at iteration 0")
+    got, iters, _, status, rc = deer.deer_solve(cell, x, None, mode=mode, tol=1e-6, max_iter=100, out=out)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    _, oit, _, ost = orc.newton(orc.Cell.from_problem(p), p["x"], None, mode=mode, tol=1e-6, max_iter=100,
+                                precision="f32")
+    ref = orc.rollout(orc.Cell.from_problem(p), p["x"])
+    assert rc == deer.DEER_OK and np.all(status == 0) and iters[1] == 0 and oit[1] == 0
+    assert np.all(np.abs(iters - oit) <= 1), (iters, oit)
+    assert not got[1].any()
+    assert rel_linf(got[[0, 2]], ref[[0, 2]]).max() <= TOL
+
+
 # ------------------------------------------------ single-launch path (D <= 4, T <= 1024)
 
 @pytest.mark.parametrize("mode,damping", [("dense", 0.0), ("diag", 0.0), ("jacobi", 0.0), ("picard", 0.0),

@@ -164,13 +164,15 @@ struct ProfScope {
 thread_local ProfScope *ProfScope::current = nullptr;
 
 // Pinned host memory of one solve call: the polling words (all-done and
-// escalate, two slots) and the staging buffer for the per-sequence results
+// escalate, two slots, written by the device's convergence test; poll_dev is
+// their device address) and the staging buffer for the per-sequence results
 // read back at the end (copies into pageable memory take tens of microseconds
 // each), grown on demand.  Calls lease a set from a process-wide pool and give
 // it back on return, so the pool holds as many sets as calls have run at the
 // same time, whatever the number of host threads.
 struct HostStage {
     int *poll = nullptr;
+    int *poll_dev = nullptr;
     char *stage = nullptr;
     size_t cap = 0;
     char *get(size_t bytes)
@@ -203,9 +205,15 @@ public:
             }
         }
         if (!h_) h_ = new HostStage();
-        if (!h_->poll &&
-            hipHostMalloc(reinterpret_cast<void **>(&h_->poll), 4 * sizeof(int), hipHostMallocDefault) != hipSuccess)
-            h_->poll = nullptr;
+        if (!h_->poll) {
+            if (hipHostMalloc(reinterpret_cast<void **>(&h_->poll), 4 * sizeof(int), hipHostMallocDefault) !=
+                    hipSuccess ||
+                hipHostGetDevicePointer(reinterpret_cast<void **>(&h_->poll_dev), h_->poll, 0) != hipSuccess) {
+                if (h_->poll) (void)hipHostFree(h_->poll);
+                h_->poll = nullptr;
+                h_->poll_dev = nullptr;
+            }
+        }
     }
     ~HostLease()
     {
@@ -341,11 +349,12 @@ __global__ void zero_words_kernel(unsigned *__restrict__ p, size_t nwords)
 
 // Convergence test of the current iteration (see finalize_iteration).
 __global__ void check_kernel(SolveControl *ctl, unsigned *res_bits, const unsigned *res_tile, int tps, int *done,
-                             int *iters, int *status, float *resid, int B, float tol, int max_iter, StallCheck sc)
+                             int *iters, int *status, float *resid, int B, float tol, int max_iter, StallCheck sc,
+                             int *poll)
 {
     __shared__ unsigned red[256 / 64];
     if (ctl->all_done) return;
-    finalize_iteration(ctl, res_bits, res_tile, tps, done, iters, status, resid, B, tol, max_iter, red, sc);
+    finalize_iteration(ctl, res_bits, res_tile, tps, done, iters, status, resid, B, tol, max_iter, red, sc, poll);
 }
 
 // Sequences whose final iterate sits in the second buffer are copied out.  With
@@ -511,9 +520,11 @@ struct PollEvents {
 };
 
 // Enqueue batches of iterations and, while the current batch runs, wait for
-// the copy of the device's all-done and escalate words enqueued after the
-// previous batch; stop enqueueing once all-done reads set, and call
-// on_escalate() while escalate does.  Kernels enqueued after convergence exit
+// the previous batch's event and read the all-done and escalate words its
+// convergence tests wrote into that batch's pinned slot (a device-to-host
+// copy per poll cost a copy dispatch and about 15 us of queue gaps); stop
+// enqueueing once all-done reads set, and call on_escalate() while escalate
+// does.  Kernels enqueued after convergence exit
 // at once, but each still costs a dispatch (a no-op compose over every chunk
 // is a full grid), so batches start at one iteration and double only when the
 // previous batch had already finished by the time the host polled it: then the
@@ -523,7 +534,7 @@ struct PollEvents {
 // enqueued.
 constexpr int kMaxPollBatch = 4;
 template <class Enqueue, class OnEscalate>
-int run_polled(Enqueue &&enqueue_iteration, SolveControl *ctl, long long total, hipStream_t stream, PollEvents &pe,
+int run_polled(Enqueue &&enqueue_iteration, long long total, hipStream_t stream, PollEvents &pe,
                HostStage &hs, const char *who, OnEscalate &&on_escalate)
 {
     int rc = DEER_OK;
@@ -539,15 +550,14 @@ int run_polled(Enqueue &&enqueue_iteration, SolveControl *ctl, long long total, 
     // each slot holds the two adjacent control words (all_done, escalate)
     while (launched < total) {
         const long long n = std::min<long long>(batch, total - launched);
-        for (long long k = 0; k < n && rc == DEER_OK; ++k) rc = enqueue_iteration();
-        if (rc) break;
-        launched += n;
+        // the batch's convergence tests write all-done and escalate into this slot
         h[2 * slot] = 0;
         h[2 * slot + 1] = 0;
-        if (hipMemcpyAsync(hs.poll + 2 * slot, &ctl->all_done, 2 * sizeof(int), hipMemcpyDeviceToHost, stream) !=
-                hipSuccess ||
-            hipEventRecord(pe.ev[slot], stream) != hipSuccess) {
-            rc = fail(DEER_ERR_HIP, std::string(who) + ": polling copy failed");
+        for (long long k = 0; k < n && rc == DEER_OK; ++k) rc = enqueue_iteration(hs.poll_dev + 2 * slot);
+        if (rc) break;
+        launched += n;
+        if (hipEventRecord(pe.ev[slot], stream) != hipSuccess) {
+            rc = fail(DEER_ERR_HIP, std::string(who) + ": polling event failed");
             break;
         }
         if (pending) {
@@ -1061,7 +1071,7 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
     rev.front = fo.front;
     rev.tol = tol;
     rev.shrink = lz.shrink;
-    auto enqueue_iteration = [&]() -> int {
+    auto enqueue_iteration = [&](int *poll) -> int {
         int r;
         StallCheck sci = sc;
         sci.escalate = (can_escalate && !scan_f64) ? 1 : 0;
@@ -1071,7 +1081,7 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
             prof.begin(0);
             r = launch_gru_quasi_step(p->W, p->b2, L.proj, s0, traj_out, L.buf1, L.ctl, L.done, L.iters, L.status,
                                       L.resid, tol, max_iter, L.res_bits, L.res_tile, B, T, D, zero_start, lz, sci,
-                                      L.scan, project ? x : nullptr, p->U, p->b, p->M, stream);
+                                      L.scan, project ? x : nullptr, p->U, p->b, p->M, poll, stream);
             prof.end();
             return r;
         }
@@ -1090,7 +1100,7 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
         }
         prof.begin(3);
         DEER_LAUNCH(check_kernel, dim3(1), dim3(256), 0, stream, L.ctl, L.res_bits, nullptr, 0, L.done, L.iters,
-                           L.status, L.resid, B, tol, max_iter, sci);
+                           L.status, L.resid, B, tol, max_iter, sci, poll);
         prof.end();
         DEER_HIP(hipGetLastError());
         prof.begin(1);
@@ -1107,7 +1117,7 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
 
     const long long total = static_cast<long long>(max_iter) + 1;   // evaluations needed at most
     PollEvents pe;
-    rc = run_polled(enqueue_iteration, L.ctl, total, stream, pe, *host, "deer_solve", [&]() {
+    rc = run_polled(enqueue_iteration, total, stream, pe, *host, "deer_solve", [&]() {
         if (can_escalate) scan_f64 = true;
     });
     if (rc == DEER_OK) {
@@ -1232,7 +1242,7 @@ int deer_solve_broyden(const deer_cell_params_t *p, const float *x, const float 
     const int *all_done = &L.ctl->all_done;
     const Linearization value{kLinValue, 1.0f};
     const FrontOut fo{sc.front, tol};
-    auto enqueue_iteration = [&]() -> int {
+    auto enqueue_iteration = [&](int *poll) -> int {
         int r;
         prof.begin(0);
         if (gru)
@@ -1245,7 +1255,7 @@ int deer_solve_broyden(const deer_cell_params_t *p, const float *x, const float 
         if (r) return r;
         prof.begin(3);
         DEER_LAUNCH(check_kernel, dim3(1), dim3(256), 0, stream, L.ctl, L.res_bits, nullptr, 0, L.done, L.iters,
-                    L.status, L.resid, B, tol, max_iter, sc);
+                    L.status, L.resid, B, tol, max_iter, sc, poll);
         prof.end();
         DEER_HIP(hipGetLastError());
         prof.begin(1);
@@ -1255,7 +1265,7 @@ int deer_solve_broyden(const deer_cell_params_t *p, const float *x, const float 
     };
     const long long total = static_cast<long long>(max_iter) + 1;
     PollEvents pe;
-    rc = run_polled(enqueue_iteration, L.ctl, total, stream, pe, *host, "deer_solve_broyden", []() {});
+    rc = run_polled(enqueue_iteration, total, stream, pe, *host, "deer_solve_broyden", []() {});
     if (rc == DEER_OK) {
         const size_t per_seq = static_cast<size_t>(T) * D;
         DEER_LAUNCH(gather_kernel, dim3(grid_for(per_seq, 256, 1024), B), dim3(256), 0, stream, traj_out, L.buf1,

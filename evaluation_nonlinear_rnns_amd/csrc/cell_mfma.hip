@@ -323,7 +323,7 @@ __global__ __launch_bounds__(kThreads, 2) void gru_quasi_step_kernel(
     int tiles_per_seq,
     int nseq, long long ntiles, int zero_start, Linearization lz, StallCheck sc, ScanHeader *__restrict__ hdr,
     unsigned long long *__restrict__ desc, const float *__restrict__ xin, const float *__restrict__ Wih,
-    const float *__restrict__ bih, float *pt_out)
+    const float *__restrict__ bih, float *pt_out, int *poll)
 {
     using G = GruGeom<D>;
     if (ctl->all_done) return;                   // same value for every workgroup of the launch
@@ -645,10 +645,10 @@ __global__ __launch_bounds__(kThreads, 2) void gru_quasi_step_kernel(
         __hip_atomic_store(&hdr->epoch, epoch + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (per_seq)
-        finalize_iteration(ctl, res_bits, nullptr, 0, done, iters, status, resid, nseq, tol, max_iter, red, sc);
+        finalize_iteration(ctl, res_bits, nullptr, 0, done, iters, status, resid, nseq, tol, max_iter, red, sc, poll);
     else
         finalize_iteration(ctl, nullptr, res_tile, tiles_per_seq, done, iters, status, resid, nseq, tol, max_iter, red,
-                           sc);
+                           sc, poll);
 }
 
 // ------------------------------------------------------------ input projection
@@ -839,7 +839,7 @@ int launch_gru_step(const float *Whh, const float *bhh, const float *pt, const f
                     SolveControl *ctl, int *done, int *iters, int *status, float *resid, float tol, int max_iter,
                     unsigned *res_bits, unsigned *res_tile, int B, int T, bool zero_start, Linearization lz,
                     const StallCheck &sc, void *state, const float *x, const float *Wih, const float *bih,
-                    float *pt_out, hipStream_t stream)
+                    float *pt_out, int *poll, hipStream_t stream)
 {
     using G = GruGeom<D>;
     static int caps[kCapDevices] = {};
@@ -851,7 +851,7 @@ int launch_gru_step(const float *Whh, const float *bhh, const float *pt, const f
     auto *desc = reinterpret_cast<unsigned long long *>(static_cast<char *>(state) + sizeof(ScanHeader));
     DEER_LAUNCH((gru_quasi_step_kernel<D, FIRST>), dim3(grid), dim3(kThreads), 0, stream, Whh, bhh, pt, s0, s_even,
                 s_odd, ctl, done, iters, status, resid, tol, max_iter, res_bits, res_tile, T, tps, B, ntiles,
-                zero_start ? 1 : 0, lz, sc, hdr, desc, x, Wih, bih, pt_out);
+                zero_start ? 1 : 0, lz, sc, hdr, desc, x, Wih, bih, pt_out, poll);
     DEER_HIP(hipGetLastError());
     return DEER_OK;
 }
@@ -912,7 +912,7 @@ int launch_gru_quasi_step(const float *Whh, const float *bhh, float *pt, const f
                           float *s_odd, SolveControl *ctl, int *done, int *iters, int *status, float *resid,
                           float tol, int max_iter, unsigned *res_bits, unsigned *res_tile, int B, int T, int D,
                           bool zero_start, Linearization lz, const StallCheck &sc, void *state, const float *x,
-                          const float *Wih, const float *bih, int M, hipStream_t stream)
+                          const float *Wih, const float *bih, int M, int *poll, hipStream_t stream)
 {
     if (B == 0 || T == 0) return DEER_OK;
     const bool first = x != nullptr;
@@ -923,10 +923,10 @@ int launch_gru_quasi_step(const float *Whh, const float *bhh, float *pt, const f
     if (D == DV)                                                                                                  \
         return first ? launch_gru_step<DV, true>(Whh, bhh, pt, s0, s_even, s_odd, ctl, done, iters, status, resid, \
                                                  tol, max_iter, res_bits, res_tile, B, T, zero_start, lz, sc,       \
-                                                 state, x, Wih, bih, pt, stream)                                    \
+                                                 state, x, Wih, bih, pt, poll, stream)                              \
                      : launch_gru_step<DV, false>(Whh, bhh, pt, s0, s_even, s_odd, ctl, done, iters, status,      \
                                                   resid, tol, max_iter, res_bits, res_tile, B, T, zero_start, lz,   \
-                                                  sc, state, nullptr, nullptr, nullptr, nullptr, stream);
+                                                  sc, state, nullptr, nullptr, nullptr, nullptr, poll, stream);
     DEER_GRU_STEP(64)
     DEER_GRU_STEP(32)
 #undef DEER_GRU_STEP

@@ -204,9 +204,20 @@ __device__ inline bool stall_step(const StallCheck &sc, SolveControl *ctl, int b
 // residual is one word per sequence (res_bits, reset here) or per-tile maxima
 // (res_tile, tps words per sequence).  Non-negative floats order like their
 // bit patterns and NaN patterns sit above +Inf, so maxima are taken on bits.
+// poll (pinned host memory, or null) receives all_done and escalate, so the
+// host's loop reads them once the launch is done, without a copy.
+__device__ inline void publish_poll(const SolveControl *ctl, int *poll)
+{
+    if (!poll) return;
+    const int ad = __hip_atomic_load(&ctl->all_done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int es = __hip_atomic_load(&ctl->escalate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(poll, ad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(poll + 1, es, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 __device__ inline void finalize_iteration(SolveControl *ctl, unsigned *res_bits, const unsigned *res_tile, int tps,
                                           int *done, int *iters, int *status, float *resid, int B, float tol,
-                                          int max_iter, unsigned *red, const StallCheck &sc)
+                                          int max_iter, unsigned *red, const StallCheck &sc, int *poll)
 {
     const int i = ctl->iter;
     int active = 0;
@@ -241,6 +252,7 @@ __device__ inline void finalize_iteration(SolveControl *ctl, unsigned *res_bits,
         if (threadIdx.x == 0) {
             if (active) ctl->iter = i + 1;
             else { ctl->all_done = 1; ctl->last_parity = i & 1; }
+            publish_poll(ctl, poll);
         }
         return;
     }
@@ -285,6 +297,7 @@ __device__ inline void finalize_iteration(SolveControl *ctl, unsigned *res_bits,
     if (threadIdx.x == 0) {
         if (active) ctl->iter = i + 1;
         else { ctl->all_done = 1; ctl->last_parity = i & 1; }
+        publish_poll(ctl, poll);
     }
 }
 
@@ -523,7 +536,7 @@ int launch_gru_quasi_step(const float *Whh, const float *bhh, float *pt, const f
                           float *s_odd, SolveControl *ctl, int *done, int *iters, int *status, float *resid,
                           float tol, int max_iter, unsigned *res_bits, unsigned *res_tile, int B, int T, int D,
                           bool zero_start, Linearization lz, const StallCheck &sc, void *state, const float *x,
-                          const float *Wih, const float *bih, int M, hipStream_t stream);
+                          const float *Wih, const float *bih, int M, int *poll, hipStream_t stream);
 
 // Sequential rollout (rollout.hip): the projection into `workspace`
 // (rollout_workspace_bytes), then one workgroup per sequence.

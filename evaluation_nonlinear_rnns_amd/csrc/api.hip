@@ -232,6 +232,24 @@ private:
 // Iteration counts, residuals, statuses and (when abort_dev is set) the
 // look-back abort word: enqueued into the pinned stage, one stream
 // synchronisation, then copied to the caller's host arrays.
+// The per-sequence results into the pinned stage in one launch (system-scope
+// stores, visible to the host once the stream has synchronised); separate
+// device-to-host copies cost a copy dispatch and about 10 us of queue gaps each.
+__global__ void pack_results_kernel(const int *__restrict__ iters, const int *__restrict__ status,
+                                    const float *__restrict__ resid, const float *__restrict__ rms,
+                                    const unsigned *__restrict__ abort_word, int B, int *h_iters, int *h_status,
+                                    float *h_resid, float *h_rms, unsigned *h_abort)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    for (int b = i; b < B; b += gridDim.x * blockDim.x) {
+        __hip_atomic_store(h_iters + b, iters[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        __hip_atomic_store(h_status + b, status[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        if (resid) __hip_atomic_store(h_resid + b, resid[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        if (rms) __hip_atomic_store(h_rms + b, rms[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+    if (i == 0) __hip_atomic_store(h_abort, abort_word ? *abort_word : 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 int read_results(HostStage &hs, const int *iters_dev, const int *status_dev, const float *resid_dev,
                  const unsigned *abort_dev, int B, hipStream_t stream, int *iters_out, float *resid_out,
                  std::vector<int> &status_h, unsigned &abort_flag, const char *who, const float *rms_dev = nullptr,
@@ -248,15 +266,11 @@ int read_results(HostStage &hs, const int *iters_dev, const int *status_dev, con
     float *h_resid = reinterpret_cast<float *>(h_status + B);
     float *h_rms = h_resid + B;
     unsigned *h_abort = reinterpret_cast<unsigned *>(h_rms + B);
-    *h_abort = 0u;
     int rc = DEER_OK;
-    if (hipMemcpyAsync(h_iters, iters_dev, sizeof(int) * B, hipMemcpyDeviceToHost, stream) != hipSuccess ||
-        hipMemcpyAsync(h_status, status_dev, sizeof(int) * B, hipMemcpyDeviceToHost, stream) != hipSuccess ||
-        (resid_out && hipMemcpyAsync(h_resid, resid_dev, sizeof(float) * B, hipMemcpyDeviceToHost, stream) != hipSuccess) ||
-        (rms_out && rms_dev &&
-         hipMemcpyAsync(h_rms, rms_dev, sizeof(float) * B, hipMemcpyDeviceToHost, stream) != hipSuccess) ||
-        (abort_dev && hipMemcpyAsync(h_abort, abort_dev, sizeof(unsigned), hipMemcpyDeviceToHost, stream) != hipSuccess))
-        rc = fail(DEER_ERR_HIP, std::string(who) + ": result copy failed");
+    DEER_LAUNCH(pack_results_kernel, dim3(static_cast<unsigned>(std::max(1, (B + 255) / 256))), dim3(256), 0, stream,
+                iters_dev, status_dev, resid_out ? resid_dev : nullptr, (rms_out && rms_dev) ? rms_dev : nullptr,
+                abort_dev, B, h_iters, h_status, h_resid, h_rms, h_abort);
+    if (hipGetLastError() != hipSuccess) rc = fail(DEER_ERR_HIP, std::string(who) + ": result read-back failed");
     const hipError_t se = hipStreamSynchronize(stream);
     if (se != hipSuccess && rc == DEER_OK) rc = hip_fail(se, (std::string("hipStreamSynchronize(") + who + ")").c_str());
     if (rc) return rc;

@@ -173,6 +173,8 @@ thread_local ProfScope *ProfScope::current = nullptr;
 struct HostStage {
     int *poll = nullptr;
     int *poll_dev = nullptr;
+    hipEvent_t ev[2] = {nullptr, nullptr};   // the poll's batch events, created on device ev_dev
+    int ev_dev = -1;
     char *stage = nullptr;
     size_t cap = 0;
     char *get(size_t bytes)
@@ -524,15 +526,6 @@ SolveLayout solve_layout(void *ws, const deer_cell_params_t *p, int B, int T, in
 
 // The two polling events of a solve; destroyed when the solve returns, after
 // its final stream synchronisation.
-struct PollEvents {
-    hipEvent_t ev[2] = {nullptr, nullptr};
-    ~PollEvents()
-    {
-        for (auto &e : ev)
-            if (e) (void)hipEventDestroy(e);
-    }
-};
-
 // Enqueue batches of iterations and, while the current batch runs, wait for
 // the previous batch's event and read the all-done and escalate words its
 // convergence tests wrote into that batch's pinned slot (a device-to-host
@@ -548,16 +541,28 @@ struct PollEvents {
 // enqueued.
 constexpr int kMaxPollBatch = 4;
 template <class Enqueue, class OnEscalate>
-int run_polled(Enqueue &&enqueue_iteration, long long total, hipStream_t stream, PollEvents &pe,
-               HostStage &hs, const char *who, OnEscalate &&on_escalate)
+int run_polled(Enqueue &&enqueue_iteration, long long total, hipStream_t stream, HostStage &hs, const char *who,
+               OnEscalate &&on_escalate)
 {
     int rc = DEER_OK;
     long long launched = 0;
     int batch = 1;
     int slot = 0;
-    for (auto &e : pe.ev)
-        if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess)
-            return fail(DEER_ERR_HIP, std::string(who) + ": event creation failed");
+    // the leased stage keeps its events from call to call (creating two per call
+    // kept the device idle for several microseconds at every solve's start)
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(DEER_ERR_HIP, std::string(who) + ": no current device");
+    if (hs.ev_dev != dev) {
+        for (auto &e : hs.ev) {
+            if (e) (void)hipEventDestroy(e);
+            e = nullptr;
+        }
+        hs.ev_dev = -1;
+        for (auto &e : hs.ev)
+            if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess)
+                return fail(DEER_ERR_HIP, std::string(who) + ": event creation failed");
+        hs.ev_dev = dev;
+    }
     bool pending = false;
     int pending_slot = 0;
     volatile int *h = hs.poll;
@@ -570,17 +575,17 @@ int run_polled(Enqueue &&enqueue_iteration, long long total, hipStream_t stream,
         for (long long k = 0; k < n && rc == DEER_OK; ++k) rc = enqueue_iteration(hs.poll_dev + 2 * slot);
         if (rc) break;
         launched += n;
-        if (hipEventRecord(pe.ev[slot], stream) != hipSuccess) {
+        if (hipEventRecord(hs.ev[slot], stream) != hipSuccess) {
             rc = fail(DEER_ERR_HIP, std::string(who) + ": polling event failed");
             break;
         }
         if (pending) {
             // finished before the host looked: the device is about to drain the
             // one batch queued behind it
-            const hipError_t q = hipEventQuery(pe.ev[pending_slot]);
+            const hipError_t q = hipEventQuery(hs.ev[pending_slot]);
             const bool behind = q == hipSuccess;
             if (q == hipErrorNotReady) (void)hipGetLastError();   // a pending event is no error
-            if (hipEventSynchronize(pe.ev[pending_slot]) != hipSuccess) {
+            if (hipEventSynchronize(hs.ev[pending_slot]) != hipSuccess) {
                 rc = fail(DEER_ERR_HIP, std::string(who) + ": event wait failed");
                 break;
             }
@@ -1130,8 +1135,7 @@ int deer_solve(const deer_cell_params_t *p, const float *x, const float *s0, int
     };
 
     const long long total = static_cast<long long>(max_iter) + 1;   // evaluations needed at most
-    PollEvents pe;
-    rc = run_polled(enqueue_iteration, total, stream, pe, *host, "deer_solve", [&]() {
+    rc = run_polled(enqueue_iteration, total, stream, *host, "deer_solve", [&]() {
         if (can_escalate) scan_f64 = true;
     });
     if (rc == DEER_OK) {
@@ -1278,8 +1282,7 @@ int deer_solve_broyden(const deer_cell_params_t *p, const float *x, const float 
         return r;
     };
     const long long total = static_cast<long long>(max_iter) + 1;
-    PollEvents pe;
-    rc = run_polled(enqueue_iteration, total, stream, pe, *host, "deer_solve_broyden", []() {});
+    rc = run_polled(enqueue_iteration, total, stream, *host, "deer_solve_broyden", []() {});
     if (rc == DEER_OK) {
         const size_t per_seq = static_cast<size_t>(T) * D;
         DEER_LAUNCH(gather_kernel, dim3(grid_for(per_seq, 256, 1024), B), dim3(256), 0, stream, traj_out, L.buf1,
